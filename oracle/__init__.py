@@ -1,0 +1,183 @@
+"""ORACLE -- test infrastructure only.
+
+A plain double-precision CPU implementation of exact softmax attention
+(``oracle.c``), used to check the HIP library. Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+it. The library (``long_context_decode_kv_amd``) never imports it and shares no
+code with it.
+
+Everything here is argument marshalling around ``oracle.c``; the arithmetic and
+its citations live in that file.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+F32, BF16, E4M3 = 0, 1, 2
+_DTYPE_OF_NUMPY = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): E4M3}
+
+
+def build():
+    """Compile ``oracle.c`` with plain gcc (no fast-math, no contraction)."""
+    src = os.path.join(_HERE, "oracle.c")
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-o", _LIB_PATH, src,
+           "-lm", "-lpthread"]
+    subprocess.check_call(cmd)
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    src = os.path.join(_HERE, "oracle.c")
+    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
+        build()
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+    common = [vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, i32]
+    lib.oracle_attention.argtypes = common + [vp, i64, vp, vp, i32]
+    lib.oracle_attention.restype = i32
+    lib.oracle_partial.argtypes = common + [i32, i32, i32, i64, i64, vp, vp, vp]
+    lib.oracle_partial.restype = i32
+    lib.oracle_energy.argtypes = common + [i32, i32, i32, vp]
+    lib.oracle_energy.restype = dbl
+    lib.oracle_merge.argtypes = [vp, dbl, dbl, vp, dbl, dbl, i32, vp, vp, vp]
+    lib.oracle_finalize.argtypes = [vp, dbl, dbl, i32, vp, vp]
+    lib.oracle_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.oracle_combine.restype = i32
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = dbl
+    lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f64.restype = dbl
+    _lib = lib
+    return lib
+
+
+def _threads():
+    return max(1, min(os.cpu_count() or 1, 64))
+
+
+def _p(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+class Problem:
+    """Inputs of one attention call, exactly as stored for the GPU.
+
+    q: [B,Hq,Lq,d] float32 / uint16 (bf16 bits); k, v: [B,Hkv,Lcap,d] float32 /
+    uint16 (bf16) / uint8 (e4m3 codes); k_scale, v_scale: float32 [B*Hkv] for
+    e4m3; kv_lens: int32 [B] or None.
+    """
+
+    def __init__(self, q, k, v, k_scale=None, v_scale=None, kv_lens=None, scale=None, causal=False):
+        self.q = np.ascontiguousarray(q)
+        self.k = np.ascontiguousarray(k)
+        self.v = np.ascontiguousarray(v)
+        assert self.k.dtype == self.v.dtype and self.k.shape == self.v.shape
+        self.B, self.Hq, self.Lq, self.d = self.q.shape
+        _, self.Hkv, self.Lcap, _ = self.k.shape
+        self.q_dtype = _DTYPE_OF_NUMPY[self.q.dtype]
+        self.kv_dtype = _DTYPE_OF_NUMPY[self.k.dtype]
+        self.k_scale = None if k_scale is None else np.ascontiguousarray(k_scale, dtype=np.float32).ravel()
+        self.v_scale = None if v_scale is None else np.ascontiguousarray(v_scale, dtype=np.float32).ravel()
+        self.kv_lens = None if kv_lens is None else np.ascontiguousarray(kv_lens, dtype=np.int32)
+        self.scale = float(scale) if scale is not None else 1.0 / np.sqrt(self.d)
+        self.causal = int(bool(causal))
+
+    def _common(self):
+        return [_p(self.q), self.q_dtype, _p(self.k), _p(self.v), self.kv_dtype, _p(self.k_scale),
+                _p(self.v_scale), _p(self.kv_lens), self.B, self.Hq, self.Hkv, self.Lq, self.Lcap, self.d,
+                self.scale, self.causal]
+
+
+def attention(prob, rows=None, nthreads=None):
+    """Exact attention. Returns (out [nrows,d] f64, lse [nrows] f64); rows are
+    flat ids (b*Hq + h)*Lq + i, or every row in that order when None."""
+    lib = _load()
+    if rows is None:
+        n = prob.B * prob.Hq * prob.Lq
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows_arr.size
+    out = np.zeros((n, prob.d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    rc = lib.oracle_attention(*prob._common(), _p(rows_arr), n, _p(out), _p(lse), nthreads or _threads())
+    if rc != 0:
+        raise ValueError("oracle_attention: bad arguments")
+    return out, lse
+
+
+def partial(prob, b, h, i, j0, j1):
+    """Partial (o, m, l) of one row over keys [j0, j1)."""
+    lib = _load()
+    o = np.zeros(prob.d, dtype=np.float64)
+    m = ctypes.c_double()
+    l = ctypes.c_double()
+    rc = lib.oracle_partial(*prob._common(), b, h, i, j0, j1, _p(o), ctypes.byref(m), ctypes.byref(l))
+    if rc != 0:
+        raise ValueError("oracle_partial: bad arguments")
+    return o, m.value, l.value
+
+
+def merge(a, b):
+    lib = _load()
+    oa, ma, la = a
+    ob, mb, lb = b
+    oa = np.ascontiguousarray(oa, dtype=np.float64)
+    ob = np.ascontiguousarray(ob, dtype=np.float64)
+    o = np.zeros_like(oa)
+    m = ctypes.c_double()
+    l = ctypes.c_double()
+    lib.oracle_merge(_p(oa), ma, la, _p(ob), mb, lb, oa.size, _p(o), ctypes.byref(m), ctypes.byref(l))
+    return o, m.value, l.value
+
+
+def finalize(part):
+    lib = _load()
+    o, m, l = part
+    o = np.ascontiguousarray(o, dtype=np.float64)
+    out = np.zeros_like(o)
+    lse = ctypes.c_double()
+    lib.oracle_finalize(_p(o), m, l, o.size, _p(out), ctypes.byref(lse))
+    return out, lse.value
+
+
+def combine(o_part, m_part, l_part, count=None):
+    """Normalised output of fp32 partials o [R,S,d], m [R,S], l [R,S]."""
+    lib = _load()
+    o_part = np.ascontiguousarray(o_part, dtype=np.float32)
+    m_part = np.ascontiguousarray(m_part, dtype=np.float32)
+    l_part = np.ascontiguousarray(l_part, dtype=np.float32)
+    R, S, d = o_part.shape
+    cnt = None if count is None else np.ascontiguousarray(count, dtype=np.int32)
+    out = np.zeros((R, d), dtype=np.float64)
+    lse = np.zeros(R, dtype=np.float64)
+    rc = lib.oracle_combine(_p(o_part), _p(m_part), _p(l_part), R, S, d, _p(cnt), _p(out), _p(lse))
+    if rc != 0:
+        raise ValueError("oracle_combine: bad arguments")
+    return out, lse
+
+
+def energy(prob, b, h, i, zeta):
+    lib = _load()
+    z = np.ascontiguousarray(zeta, dtype=np.float64)
+    return lib.oracle_energy(*prob._common(), b, h, i, _p(z))
+
+
+def bf16_to_f64(bits):
+    lib = _load()
+    bits = np.asarray(bits, dtype=np.uint16)
+    return np.array([lib.oracle_bf16_to_f64(int(b)) for b in bits.ravel()]).reshape(bits.shape)
+
+
+def e4m3_to_f64(codes):
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e4m3_to_f64(int(c)) for c in codes.ravel()]).reshape(codes.shape)

@@ -1,0 +1,355 @@
+/*
+ * ORACLE -- test infrastructure only. Plain, slow, double-precision CPU
+ * attention used to check the HIP library. Only the tests, the smoke check and
+ * the benchmark's CPU-baseline leg may load it; the library never calls it and
+ * shares no code with it.
+ *
+ * What it computes is the plain definition of exact softmax attention
+ * ("Attention" glossary page, section on Query/Key/Value: each query is dotted
+ * with every key, the scores are normalised by a softmax, and the values are
+ * averaged with those weights; the Tree Attention explainer, section 2, stresses
+ * that the tree method is exact, not an approximation, so the oracle is that
+ * definition written out). The softmax subtracts the row maximum before
+ * exponentiating, the stability step the Grayskull explainer names in its
+ * section 3. Everything is evaluated in double precision from the exact values
+ * the GPU reads (fp32, bf16 bit patterns, or fp8-e4m3 codes times their fp32
+ * per-head scale), decoded here from the format definitions.
+ *
+ * Readings where the pages are silent (all pages give no formula):
+ *  - score scale sigma is an argument (1/sqrt(d) by default in the callers);
+ *  - grouped KV heads: query head h reads KV head floor(h / (Hq/Hkv));
+ *  - causal mask is aligned bottom-right: with n keys and Lq queries, query i
+ *    sits at absolute position n - Lq + i and sees keys j <= n - Lq + i;
+ *  - a row that sees no key returns O = 0 and lse = -inf.
+ *
+ * The partial / merge / combine / energy functions restate the Tree Attention
+ * explainer's section 3 (attention written as the gradient of a scalar energy
+ * function, evaluated by an associative reduction along the sequence axis):
+ *  partial over a key set J: (o = sum_J e^{s_j - m} v_j, m = max_J s_j,
+ *                             l = sum_J e^{s_j - m});
+ *  merge(a, b): m = max(m_a, m_b), o = e^{m_a-m} o_a + e^{m_b-m} o_b,
+ *               l = e^{m_a-m} l_a + e^{m_b-m} l_b; identity (0, -inf, 0);
+ *  finalise: O = o / l, lse = m + ln l;
+ *  energy F(zeta) = ln sum_J exp(s_j + zeta . v_j), so F(0) = lse and the
+ *  gradient of F at 0 is O.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OR_F32 0
+#define OR_BF16 1
+#define OR_E4M3 2
+
+/* bf16: the upper 16 bits of an IEEE-754 binary32. */
+double oracle_bf16_to_f64(uint16_t bits) {
+    uint32_t w = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &w, 4);
+    return (double)f;
+}
+
+/* OCP FP8 E4M3 (e4m3fn): 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+ * exponent field 0: subnormal, value m/8 * 2^(1-7); exponent 15 with mantissa 7
+ * is NaN (there is no infinity); otherwise (1 + m/8) * 2^(e-7). */
+double oracle_e4m3_to_f64(uint8_t code) {
+    int s = (code >> 7) & 1;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m / 8.0, 1 - 7);
+    else v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+typedef struct {
+    const void* q;
+    int q_dtype;
+    const void* k;
+    const void* v;
+    int kv_dtype;
+    const float* k_scale;
+    const float* v_scale;
+    const int32_t* kv_lens;
+    int B, Hq, Hkv, Lq, Lcap, d;
+    double scale;
+    int causal;
+} problem;
+
+static double elem(const void* base, int dtype, int64_t idx) {
+    switch (dtype) {
+    case OR_F32: return (double)((const float*)base)[idx];
+    case OR_BF16: return oracle_bf16_to_f64(((const uint16_t*)base)[idx]);
+    case OR_E4M3: return oracle_e4m3_to_f64(((const uint8_t*)base)[idx]);
+    default: return NAN;
+    }
+}
+
+/* Decoded key or value row j of (b, g), multiplied by its fp8 scale if any. */
+static void load_kv_row(const problem* p, const void* base, const float* scales, int b, int g, int64_t j,
+                        double* dst) {
+    int64_t off = (((int64_t)b * p->Hkv + g) * p->Lcap + j) * p->d;
+    double sc = scales ? (double)scales[(int64_t)b * p->Hkv + g] : 1.0;
+    for (int c = 0; c < p->d; ++c) dst[c] = elem(base, p->kv_dtype, off + c) * sc;
+}
+
+static int64_t seq_len(const problem* p, int b) {
+    int64_t n = p->kv_lens ? (int64_t)p->kv_lens[b] : (int64_t)p->Lcap;
+    if (n < 0) n = 0;
+    if (n > p->Lcap) n = p->Lcap;
+    return n;
+}
+
+/* Keys visible to query i of sequence b: [0, hi). */
+static int64_t visible_end(const problem* p, int b, int i) {
+    int64_t n = seq_len(p, b);
+    if (!p->causal) return n;
+    int64_t hi = n - p->Lq + i + 1;
+    if (hi < 0) hi = 0;
+    if (hi > n) hi = n;
+    return hi;
+}
+
+static void load_q_row(const problem* p, int b, int h, int i, double* dst) {
+    int64_t off = (((int64_t)b * p->Hq + h) * p->Lq + i) * p->d;
+    for (int c = 0; c < p->d; ++c) dst[c] = elem(p->q, p->q_dtype, off + c);
+}
+
+static double score(const problem* p, const double* q, const double* krow) {
+    double acc = 0.0;
+    for (int c = 0; c < p->d; ++c) acc += q[c] * krow[c];
+    return p->scale * acc;
+}
+
+/* One output row by the definition: scores, max, weights, weighted mean. */
+static void attend_row(const problem* p, int b, int h, int i, double* s, double* tmp, double* qd, double* out,
+                       double* lse) {
+    int g = h / (p->Hq / p->Hkv);
+    int64_t hi = visible_end(p, b, i);
+    for (int c = 0; c < p->d; ++c) out[c] = 0.0;
+    if (hi <= 0) {
+        *lse = -INFINITY;
+        return;
+    }
+    load_q_row(p, b, h, i, qd);
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < hi; ++j) {
+        load_kv_row(p, p->k, p->k_scale, b, g, j, tmp);
+        s[j] = score(p, qd, tmp);
+        if (s[j] > mx) mx = s[j];
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < hi; ++j) {
+        double w = exp(s[j] - mx);
+        z += w;
+        load_kv_row(p, p->v, p->v_scale, b, g, j, tmp);
+        for (int c = 0; c < p->d; ++c) out[c] += w * tmp[c];
+    }
+    for (int c = 0; c < p->d; ++c) out[c] /= z;
+    *lse = mx + log(z);
+}
+
+typedef struct {
+    const problem* p;
+    const int64_t* rows;
+    int64_t nrows;
+    int tid, nthreads;
+    double* out;
+    double* lse;
+} row_job;
+
+static void* row_worker(void* arg) {
+    row_job* j = (row_job*)arg;
+    const problem* p = j->p;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(p->Lcap > 0 ? p->Lcap : 1));
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)p->d);
+    double* qd = (double*)malloc(sizeof(double) * (size_t)p->d);
+    for (int64_t r = j->tid; r < j->nrows; r += j->nthreads) {
+        int64_t flat = j->rows ? j->rows[r] : r;
+        int i = (int)(flat % p->Lq);
+        int h = (int)((flat / p->Lq) % p->Hq);
+        int b = (int)(flat / ((int64_t)p->Lq * p->Hq));
+        attend_row(p, b, h, i, s, tmp, qd, j->out + r * p->d, j->lse + r);
+    }
+    free(s);
+    free(tmp);
+    free(qd);
+    return NULL;
+}
+
+static int check_problem(const problem* p) {
+    if (p->B <= 0 || p->Hq <= 0 || p->Hkv <= 0 || p->Lq <= 0 || p->Lcap < 0 || p->d <= 0) return 1;
+    if (p->Hq % p->Hkv) return 1;
+    if (p->kv_dtype == OR_E4M3 && (!p->k_scale || !p->v_scale)) return 1;
+    return 0;
+}
+
+/*
+ * Exact attention for the listed rows (flat row id r = (b*Hq + h)*Lq + i), or for
+ * every row when rows == NULL. Layouts are contiguous: q [B,Hq,Lq,d],
+ * k/v [B,Hkv,Lcap,d], fp8 scales [B*Hkv], kv_lens [B] (NULL = all Lcap).
+ * out [nrows, d] and lse [nrows] are double. Returns 0, or 1 on a bad argument.
+ */
+int oracle_attention(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                     const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv,
+                     int Lq, int Lcap, int d, double scale, int causal, const int64_t* rows, int64_t nrows,
+                     double* out, double* lse, int nthreads) {
+    problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, kv_lens, B, Hq, Hkv, Lq, Lcap, d, scale, causal};
+    if (check_problem(&p)) return 1;
+    if (!rows) nrows = (int64_t)B * Hq * Lq;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > nrows) nthreads = (int)(nrows > 0 ? nrows : 1);
+    pthread_t th[256];
+    row_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (row_job){&p, rows, nrows, t, nthreads, out, lse};
+        pthread_create(&th[t], NULL, row_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* Partial (o, m, l) of row (b, h, i) over keys [j0, j1) intersected with the
+ * keys the row may see. An empty set gives the identity (0, -inf, 0). */
+int oracle_partial(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype, const float* k_scale,
+                   const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int Lq, int Lcap, int d,
+                   double scale, int causal, int b, int h, int i, int64_t j0, int64_t j1, double* o, double* m,
+                   double* l) {
+    problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, kv_lens, B, Hq, Hkv, Lq, Lcap, d, scale, causal};
+    if (check_problem(&p)) return 1;
+    int g = h / (Hq / Hkv);
+    int64_t hi = visible_end(&p, b, i);
+    if (j1 > hi) j1 = hi;
+    if (j0 < 0) j0 = 0;
+    for (int c = 0; c < d; ++c) o[c] = 0.0;
+    *m = -INFINITY;
+    *l = 0.0;
+    if (j1 <= j0) return 0;
+    double* qd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+    double* s = (double*)malloc(sizeof(double) * (size_t)(j1 - j0));
+    load_q_row(&p, b, h, i, qd);
+    double mx = -INFINITY;
+    for (int64_t j = j0; j < j1; ++j) {
+        load_kv_row(&p, k, k_scale, b, g, j, tmp);
+        s[j - j0] = score(&p, qd, tmp);
+        if (s[j - j0] > mx) mx = s[j - j0];
+    }
+    double z = 0.0;
+    for (int64_t j = j0; j < j1; ++j) {
+        double w = exp(s[j - j0] - mx);
+        z += w;
+        load_kv_row(&p, v, v_scale, b, g, j, tmp);
+        for (int c = 0; c < d; ++c) o[c] += w * tmp[c];
+    }
+    *m = mx;
+    *l = z;
+    free(qd);
+    free(tmp);
+    free(s);
+    return 0;
+}
+
+/* Associative merge of two partials (the reduction step of the tree). */
+void oracle_merge(const double* oa, double ma, double la, const double* ob, double mb, double lb, int d, double* o,
+                  double* m, double* l) {
+    double mm = ma > mb ? ma : mb;
+    if (mm == -INFINITY) {
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        *m = -INFINITY;
+        *l = 0.0;
+        return;
+    }
+    double a = exp(ma - mm), bb = exp(mb - mm);
+    for (int c = 0; c < d; ++c) o[c] = a * oa[c] + bb * ob[c];
+    *m = mm;
+    *l = a * la + bb * lb;
+}
+
+void oracle_finalize(const double* o, double m, double l, int d, double* out, double* lse) {
+    if (l <= 0.0 || m == -INFINITY) {
+        for (int c = 0; c < d; ++c) out[c] = 0.0;
+        *lse = -INFINITY;
+        return;
+    }
+    for (int c = 0; c < d; ++c) out[c] = o[c] / l;
+    *lse = m + log(l);
+}
+
+/*
+ * Combine S fp32 partials per row into the normalised output, by the plain
+ * definition of the merged result: m = max_s m_s, w_s = e^{m_s - m},
+ * O = sum_s w_s o_s / sum_s w_s l_s, lse = m + ln sum_s w_s l_s.
+ * o_part [R,S,d], m_part/l_part [R,S]; count [R] (NULL = S) limits the partials
+ * read per row. out [R,d], lse [R] double.
+ */
+int oracle_combine(const float* o_part, const float* m_part, const float* l_part, int R, int S, int d,
+                   const int32_t* count, double* out, double* lse) {
+    if (R < 0 || S < 0 || d <= 0) return 1;
+    for (int64_t r = 0; r < R; ++r) {
+        int n = count ? count[r] : S;
+        if (n > S) n = S;
+        double mx = -INFINITY;
+        for (int s = 0; s < n; ++s) {
+            double ms = (double)m_part[r * S + s];
+            if (ms > mx) mx = ms;
+        }
+        double* o = out + r * d;
+        for (int c = 0; c < d; ++c) o[c] = 0.0;
+        if (mx == -INFINITY) {
+            lse[r] = -INFINITY;
+            continue;
+        }
+        double z = 0.0;
+        for (int s = 0; s < n; ++s) {
+            double ms = (double)m_part[r * S + s];
+            if (ms == -INFINITY) continue;
+            double w = exp(ms - mx);
+            z += w * (double)l_part[r * S + s];
+            for (int c = 0; c < d; ++c) o[c] += w * (double)o_part[((int64_t)r * S + s) * d + c];
+        }
+        if (z <= 0.0) {
+            for (int c = 0; c < d; ++c) o[c] = 0.0;
+            lse[r] = -INFINITY;
+            continue;
+        }
+        for (int c = 0; c < d; ++c) o[c] /= z;
+        lse[r] = mx + log(z);
+    }
+    return 0;
+}
+
+/* Energy of row (b, h, i) at zeta: F = ln sum_{visible j} exp(s_j + zeta . v_j). */
+double oracle_energy(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype, const float* k_scale,
+                     const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int Lq, int Lcap, int d,
+                     double scale, int causal, int b, int h, int i, const double* zeta) {
+    problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, kv_lens, B, Hq, Hkv, Lq, Lcap, d, scale, causal};
+    if (check_problem(&p)) return NAN;
+    int g = h / (Hq / Hkv);
+    int64_t hi = visible_end(&p, b, i);
+    if (hi <= 0) return -INFINITY;
+    double* qd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+    double* e = (double*)malloc(sizeof(double) * (size_t)hi);
+    load_q_row(&p, b, h, i, qd);
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < hi; ++j) {
+        load_kv_row(&p, k, k_scale, b, g, j, tmp);
+        double sj = score(&p, qd, tmp);
+        load_kv_row(&p, v, v_scale, b, g, j, tmp);
+        double zv = 0.0;
+        for (int c = 0; c < d; ++c) zv += zeta[c] * tmp[c];
+        e[j] = sj + zv;
+        if (e[j] > mx) mx = e[j];
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < hi; ++j) z += exp(e[j] - mx);
+    free(qd);
+    free(tmp);
+    free(e);
+    return mx + log(z);
+}

@@ -1,0 +1,362 @@
+"""Pins for the double-precision oracle, independent of the oracle itself.
+
+Each test ties the oracle to something it does not compute the same way:
+brute force without the max shift, closed forms, special cases, invariants of
+exact attention and of its tree reduction, the energy-gradient identity, and
+the format definitions as implemented by torch's own dtypes.
+
+Sources: exact softmax attention as the glossary page "Attention" describes it
+(section on Query/Key/Value); the tree reduction along the sequence axis and its
+exactness ("Tree Attention: Topology-aware Decoding for Long-Context Attention
+on GPU Clusters", explainer sections 1-3); max subtraction for stability
+("Attention in SRAM on Tenstorrent Grayskull", explainer section 3).
+"""
+import math
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+RNG = np.random.default_rng(12345)
+
+
+def rand_f32(*shape, scale=1.0):
+    return (RNG.standard_normal(shape) * scale).astype(np.float32)
+
+
+def brute_row(qrow, krows, vrows, scale):
+    """Textbook softmax with no max shift, in plain Python floats."""
+    s = [scale * math.fsum(float(a) * float(b) for a, b in zip(qrow, k)) for k in krows]
+    e = [math.exp(x) for x in s]
+    z = math.fsum(e)
+    d = len(qrow)
+    out = [math.fsum(e[j] * float(vrows[j][c]) for j in range(len(krows))) / z for c in range(d)]
+    return np.array(out), math.log(z)
+
+
+def run(prob):
+    out, lse = oracle.attention(prob)
+    return out.reshape(prob.B, prob.Hq, prob.Lq, prob.d), lse.reshape(prob.B, prob.Hq, prob.Lq)
+
+
+# ---------------------------------------------------------------- brute force
+
+def test_bruteforce_mha_noncausal():
+    B, H, Lq, L, d = 2, 3, 2, 7, 5
+    q, k, v = rand_f32(B, H, Lq, d), rand_f32(B, H, L, d), rand_f32(B, H, L, d)
+    prob = oracle.Problem(q, k, v, scale=0.37)
+    out, lse = run(prob)
+    for b in range(B):
+        for h in range(H):
+            for i in range(Lq):
+                o_ref, lse_ref = brute_row(q[b, h, i], k[b, h], v[b, h], 0.37)
+                np.testing.assert_allclose(out[b, h, i], o_ref, rtol=1e-12, atol=1e-14)
+                assert abs(lse[b, h, i] - lse_ref) < 1e-12
+
+
+def test_default_scale_is_inverse_sqrt_d():
+    q, k, v = rand_f32(1, 1, 1, 16), rand_f32(1, 1, 9, 16), rand_f32(1, 1, 9, 16)
+    out, lse = run(oracle.Problem(q, k, v))
+    o_ref, lse_ref = brute_row(q[0, 0, 0], k[0, 0], v[0, 0], 0.25)
+    np.testing.assert_allclose(out[0, 0, 0], o_ref, rtol=1e-12, atol=1e-14)
+    assert abs(lse[0, 0, 0] - lse_ref) < 1e-12
+
+
+# ---------------------------------------------------------------- closed forms
+
+def test_two_keys_closed_form():
+    # O = logistic(s1 - s2) v1 + logistic(s2 - s1) v2, lse = ln(e^s1 + e^s2)
+    q = np.array([[[[1.0, -2.0, 0.5]]]], dtype=np.float32)
+    k = np.array([[[[0.5, 0.25, 2.0], [-1.0, 1.0, 0.0]]]], dtype=np.float32)
+    v = np.array([[[[1.0, 2.0, 3.0], [-4.0, 0.5, 8.0]]]], dtype=np.float32)
+    out, lse = run(oracle.Problem(q, k, v, scale=1.0))
+    s1, s2 = 0.5 - 0.5 + 1.0, -1.0 - 2.0
+    w1 = 1.0 / (1.0 + math.exp(-(s1 - s2)))
+    w2 = 1.0 / (1.0 + math.exp(-(s2 - s1)))
+    np.testing.assert_allclose(out[0, 0, 0], w1 * v[0, 0, 0].astype(np.float64) + w2 * v[0, 0, 1].astype(np.float64), rtol=1e-14)
+    assert abs(lse[0, 0, 0] - math.log(math.exp(s1) + math.exp(s2))) < 1e-14
+
+
+def test_single_key_returns_its_value():
+    q, k, v = rand_f32(1, 2, 1, 8), rand_f32(1, 2, 1, 8), rand_f32(1, 2, 1, 8)
+    out, lse = run(oracle.Problem(q, k, v, scale=0.5))
+    for h in range(2):
+        np.testing.assert_array_equal(out[0, h, 0], v[0, h, 0].astype(np.float64))
+        s0 = 0.5 * float(np.dot(q[0, h, 0].astype(np.float64), k[0, h, 0].astype(np.float64)))
+        assert abs(lse[0, h, 0] - s0) < 1e-14
+
+
+def test_uniform_scores_give_mean_of_v():
+    n, d = 37, 6
+    v = rand_f32(1, 1, n, d)
+    # zero query: every score is 0
+    out, lse = run(oracle.Problem(np.zeros((1, 1, 1, d), np.float32), rand_f32(1, 1, n, d), v))
+    np.testing.assert_allclose(out[0, 0, 0], v[0, 0].astype(np.float64).mean(axis=0), rtol=1e-13, atol=1e-15)
+    assert abs(lse[0, 0, 0] - math.log(n)) < 1e-13
+    # all keys equal: every score equals s
+    krow = rand_f32(d)
+    k = np.broadcast_to(krow, (1, 1, n, d)).copy()
+    q = rand_f32(1, 1, 1, d)
+    out, lse = run(oracle.Problem(q, k, v, scale=0.3))
+    s = 0.3 * float(np.dot(q[0, 0, 0].astype(np.float64), krow.astype(np.float64)))
+    np.testing.assert_allclose(out[0, 0, 0], v[0, 0].astype(np.float64).mean(axis=0), rtol=1e-13, atol=1e-15)
+    assert abs(lse[0, 0, 0] - (s + math.log(n))) < 1e-12
+
+
+def test_huge_scores_stay_finite():
+    # Scores around 1e4: exp without the max shift overflows; the oracle must not.
+    d, n = 4, 9
+    q = np.array([[[[100.0, 0.0, 0.0, 0.0]]]], dtype=np.float32)
+    k = np.zeros((1, 1, n, d), np.float32)
+    k[0, 0, :, 0] = np.arange(n, dtype=np.float32) * 10.0 + 50.0  # scores 5000 .. 13000, spaced by 1000
+    v = rand_f32(1, 1, n, d)
+    out, lse = run(oracle.Problem(q, k, v, scale=1.0))
+    assert np.all(np.isfinite(out)) and np.isfinite(lse).all()
+    np.testing.assert_array_equal(out[0, 0, 0], v[0, 0, n - 1].astype(np.float64))
+    assert lse[0, 0, 0] == pytest.approx(100.0 * (50.0 + 10.0 * (n - 1)), rel=1e-15)
+    # two tied maxima: the mean of their values
+    k[0, 0, 3, 0] = k[0, 0, n - 1, 0]
+    out, lse = run(oracle.Problem(q, k, v, scale=1.0))
+    np.testing.assert_allclose(out[0, 0, 0], 0.5 * (v[0, 0, 3].astype(np.float64) + v[0, 0, n - 1]), rtol=1e-15)
+    assert lse[0, 0, 0] == pytest.approx(13000.0 + math.log(2.0), rel=1e-15)
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_weights_sum_to_one():
+    q, k = rand_f32(2, 2, 3, 8, scale=3.0), rand_f32(2, 2, 50, 8, scale=3.0)
+    out, _ = run(oracle.Problem(q, k, np.ones((2, 2, 50, 8), np.float32)))
+    np.testing.assert_allclose(out, 1.0, rtol=0, atol=1e-13)
+
+
+def test_linear_in_v():
+    q, k = rand_f32(1, 2, 2, 8), rand_f32(1, 2, 20, 8)
+    v1, v2 = rand_f32(1, 2, 20, 8), rand_f32(1, 2, 20, 8)
+    o1, _ = run(oracle.Problem(q, k, v1))
+    o2, _ = run(oracle.Problem(q, k, v2))
+    o3, _ = run(oracle.Problem(q, k, (2.0 * v1 - 0.5 * v2).astype(np.float32)))
+    # 2 v1 - 0.5 v2 is exact in fp32 for these magnitudes only up to rounding; compare in f64 terms
+    v3 = (2.0 * v1 - 0.5 * v2).astype(np.float32).astype(np.float64)
+    o3_ref, _ = run(oracle.Problem(q, k, v3.astype(np.float32)))
+    np.testing.assert_allclose(o3, o3_ref, rtol=0, atol=0)
+    np.testing.assert_allclose(o3, 2.0 * o1 - 0.5 * o2, rtol=0, atol=2e-6)
+
+
+def test_key_permutation_invariance():
+    q, k, v = rand_f32(1, 1, 2, 8), rand_f32(1, 1, 31, 8), rand_f32(1, 1, 31, 8)
+    perm = RNG.permutation(31)
+    o1, l1 = run(oracle.Problem(q, k, v))
+    o2, l2 = run(oracle.Problem(q, k[:, :, perm].copy(), v[:, :, perm].copy()))
+    np.testing.assert_allclose(o1, o2, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(l1, l2, rtol=1e-14)
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    B, Hq, Hkv, Lq, L, d = 2, 8, 2, 3, 19, 8
+    q, k, v = rand_f32(B, Hq, Lq, d), rand_f32(B, Hkv, L, d), rand_f32(B, Hkv, L, d)
+    G = Hq // Hkv
+    o1, l1 = run(oracle.Problem(q, k, v))
+    o2, l2 = run(oracle.Problem(q, np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+    # and a mapping h -> h % Hkv would differ
+    o3, _ = run(oracle.Problem(q, np.tile(k, (1, G, 1, 1)), np.tile(v, (1, G, 1, 1))))
+    assert not np.allclose(o1, o3)
+
+
+@pytest.mark.parametrize("Lq,L", [(6, 6), (3, 10), (1, 9)])
+def test_causal_row_equals_its_prefix(Lq, L):
+    B, H, d = 1, 2, 8
+    q, k, v = rand_f32(B, H, Lq, d), rand_f32(B, H, L, d), rand_f32(B, H, L, d)
+    out, lse = run(oracle.Problem(q, k, v, causal=True))
+    for h in range(H):
+        for i in range(Lq):
+            n = L - Lq + i + 1  # bottom-right alignment, self included
+            o_ref, lse_ref = brute_row(q[0, h, i], k[0, h, :n], v[0, h, :n], 1 / math.sqrt(d))
+            np.testing.assert_allclose(out[0, h, i], o_ref, rtol=1e-12, atol=1e-14)
+            assert abs(lse[0, h, i] - lse_ref) < 1e-12
+
+
+def test_ragged_row_equals_sequence_alone():
+    B, Hq, Hkv, Lcap, d = 3, 4, 2, 16, 8
+    q, k, v = rand_f32(B, Hq, 1, d), rand_f32(B, Hkv, Lcap, d), rand_f32(B, Hkv, Lcap, d)
+    lens = np.array([16, 5, 0], np.int32)
+    out, lse = run(oracle.Problem(q, k, v, kv_lens=lens, causal=True))
+    for b in range(2):
+        n = int(lens[b])
+        o_ref, l_ref = run(oracle.Problem(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n]))
+        np.testing.assert_array_equal(out[b], o_ref[0])
+        np.testing.assert_array_equal(lse[b], l_ref[0])
+    # an empty sequence: O = 0, lse = -inf
+    assert np.all(out[2] == 0.0) and np.all(np.isneginf(lse[2]))
+
+
+# ---------------------------------------------------------------- tree reduction
+
+def _chunks(n, S):
+    bounds = [n * s // S for s in range(S + 1)]
+    return list(zip(bounds[:-1], bounds[1:]))
+
+
+def _reduce(parts, shape, rnd):
+    if shape == "left":
+        acc = parts[0]
+        for p in parts[1:]:
+            acc = oracle.merge(acc, p)
+        return acc
+    if shape == "right":
+        acc = parts[-1]
+        for p in reversed(parts[:-1]):
+            acc = oracle.merge(p, acc)
+        return acc
+    if shape == "balanced":
+        level = list(parts)
+        while len(level) > 1:
+            nxt = [oracle.merge(level[i], level[i + 1]) for i in range(0, len(level) - 1, 2)]
+            if len(level) % 2:
+                nxt.append(level[-1])
+            level = nxt
+        return level[0]
+    # random tree: merge random neighbours (any order: merge is commutative too)
+    level = list(parts)
+    while len(level) > 1:
+        i = rnd.randrange(len(level) - 1)
+        a, b = level[i], level[i + 1]
+        m = oracle.merge(b, a) if rnd.random() < 0.5 else oracle.merge(a, b)
+        level[i:i + 2] = [m]
+    return level[0]
+
+
+@pytest.mark.parametrize("shape", ["left", "right", "balanced", "random"])
+def test_tree_combine_equals_single_pass_for_every_split(shape):
+    n, d = 13, 6
+    q, k, v = rand_f32(1, 2, 1, d, scale=2.0), rand_f32(1, 2, n, d), rand_f32(1, 2, n, d)
+    prob = oracle.Problem(q, k, v)
+    out, lse = run(prob)
+    rnd = random.Random(7)
+    for h in range(2):
+        for S in range(1, n + 1):
+            parts = [oracle.partial(prob, 0, h, 0, a, b) for a, b in _chunks(n, S)]
+            o, lse_t = oracle.finalize(_reduce(parts, shape, rnd))
+            np.testing.assert_allclose(o, out[0, h, 0], rtol=1e-12, atol=1e-14)
+            assert abs(lse_t - lse[0, h, 0]) < 1e-12
+
+
+def test_tree_with_empty_chunks_and_identity():
+    n, d = 8, 4
+    q, k, v = rand_f32(1, 1, 1, d), rand_f32(1, 1, n, d), rand_f32(1, 1, n, d)
+    prob = oracle.Problem(q, k, v)
+    out, lse = run(prob)
+    ident = (np.zeros(d), -math.inf, 0.0)
+    parts = [ident, oracle.partial(prob, 0, 0, 0, 0, 3), oracle.partial(prob, 0, 0, 0, 3, 3), ident,
+             oracle.partial(prob, 0, 0, 0, 3, 8), ident]
+    o, l = oracle.finalize(_reduce(parts, "balanced", None))
+    np.testing.assert_allclose(o, out[0, 0, 0], rtol=1e-12)
+    assert abs(l - lse[0, 0, 0]) < 1e-12
+    o, l = oracle.finalize(oracle.merge(ident, ident))
+    assert np.all(o == 0) and l == -math.inf
+
+
+def test_combine_of_fp32_partials_matches_single_pass():
+    R, n, d, S = 3, 40, 8, 6
+    q, k, v = rand_f32(1, R, 1, d), rand_f32(1, R, n, d), rand_f32(1, R, n, d)
+    prob = oracle.Problem(q, k, v)
+    out, lse = run(prob)
+    o_p = np.zeros((R, S, d), np.float32)
+    m_p = np.full((R, S), -np.inf, np.float32)
+    l_p = np.zeros((R, S), np.float32)
+    for r in range(R):
+        for s, (a, b) in enumerate(_chunks(n, S)):
+            o, m, l = oracle.partial(prob, 0, r, 0, a, b)
+            o_p[r, s], m_p[r, s], l_p[r, s] = o, m, l
+    o_c, lse_c = oracle.combine(o_p, m_p, l_p)
+    np.testing.assert_allclose(o_c, out[0, :, 0], rtol=0, atol=1e-6)
+    np.testing.assert_allclose(lse_c, lse[0, :, 0], rtol=0, atol=1e-6)
+    # a normalised (O, lse) pair is the partial (O, lse, 1)
+    o_n, l_n = oracle.combine(out[0, :, 0][:, None, :].astype(np.float32), lse[0, :, 0][:, None].astype(np.float32),
+                              np.ones((R, 1), np.float32))
+    np.testing.assert_allclose(o_n, out[0, :, 0], rtol=0, atol=1e-6)
+    # counts limit what is read; zero partials -> O = 0, lse = -inf
+    o_z, l_z = oracle.combine(o_p, m_p, l_p, count=np.array([0, 1, S], np.int32))
+    assert np.all(o_z[0] == 0) and np.isneginf(l_z[0])
+    np.testing.assert_allclose(o_z[1], o_p[1, 0] / l_p[1, 0], rtol=1e-6)
+
+
+# ---------------------------------------------------------------- energy view
+
+def test_output_is_gradient_of_energy():
+    d, n = 6, 25
+    q, k, v = rand_f32(1, 1, 1, d), rand_f32(1, 1, n, d), rand_f32(1, 1, n, d)
+    prob = oracle.Problem(q, k, v)
+    out, lse = run(prob)
+    assert abs(oracle.energy(prob, 0, 0, 0, np.zeros(d)) - lse[0, 0, 0]) < 1e-13
+    h = 1e-5
+    grad = np.zeros(d)
+    for c in range(d):
+        e = np.zeros(d)
+        e[c] = h
+        grad[c] = (oracle.energy(prob, 0, 0, 0, e) - oracle.energy(prob, 0, 0, 0, -e)) / (2 * h)
+    np.testing.assert_allclose(grad, out[0, 0, 0], rtol=0, atol=1e-8)
+
+
+def test_energy_of_union_is_logsumexp():
+    d, n = 4, 10
+    q, k, v = rand_f32(1, 1, 1, d), rand_f32(1, 1, n, d), rand_f32(1, 1, n, d)
+    zeta = rand_f32(d).astype(np.float64) * 0.1
+    full = oracle.energy(oracle.Problem(q, k, v), 0, 0, 0, zeta)
+    fa = oracle.energy(oracle.Problem(q, k[:, :, :4].copy(), v[:, :, :4].copy()), 0, 0, 0, zeta)
+    fb = oracle.energy(oracle.Problem(q, k[:, :, 4:].copy(), v[:, :, 4:].copy()), 0, 0, 0, zeta)
+    assert abs(full - np.logaddexp(fa, fb)) < 1e-13
+
+
+# ---------------------------------------------------------------- storage formats
+
+def test_bf16_decoder_matches_torch_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint16)
+    ours = oracle.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+
+
+def test_e4m3_decoder_matches_torch_for_every_code():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(ours), nan)
+    np.testing.assert_array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_bf16_inputs_match_bruteforce_on_decoded_values():
+    B, Hq, Hkv, L, d = 1, 4, 2, 11, 8
+    tq = torch.randn(B, Hq, 1, d, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16)
+    tk = torch.randn(B, Hkv, L, d, generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    tv = torch.randn(B, Hkv, L, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    bits = lambda t: t.view(torch.int16).numpy().view(np.uint16)
+    out, lse = run(oracle.Problem(bits(tq), bits(tk), bits(tv)))
+    qd, kd, vd = (t.to(torch.float64).numpy() for t in (tq, tk, tv))
+    for h in range(Hq):
+        o_ref, l_ref = brute_row(qd[0, h, 0], kd[0, h // 2], vd[0, h // 2], 1 / math.sqrt(d))
+        np.testing.assert_allclose(out[0, h, 0], o_ref, rtol=1e-12, atol=1e-14)
+        assert abs(lse[0, h, 0] - l_ref) < 1e-12
+
+
+def test_e4m3_inputs_apply_their_scale():
+    B, Hq, Hkv, L, d = 1, 2, 1, 9, 8
+    q = rand_f32(B, Hq, 1, d)
+    kc = RNG.integers(0, 0x7E, size=(B, Hkv, L, d), dtype=np.uint8) | (RNG.integers(0, 2, size=(B, Hkv, L, d), dtype=np.uint8) << 7)
+    vc = RNG.integers(0, 0x7E, size=(B, Hkv, L, d), dtype=np.uint8)
+    ks, vs = np.array([0.0125], np.float32), np.array([3.5], np.float32)
+    out, lse = run(oracle.Problem(q, kc, vc, k_scale=ks, v_scale=vs))
+    kd = torch.from_numpy(kc).view(torch.float8_e4m3fn).to(torch.float64).numpy() * float(ks[0])
+    vd = torch.from_numpy(vc).view(torch.float8_e4m3fn).to(torch.float64).numpy() * float(vs[0])
+    for h in range(Hq):
+        o_ref, l_ref = brute_row(q[0, h, 0], kd[0, 0], vd[0, 0], 1 / math.sqrt(d))
+        np.testing.assert_allclose(out[0, h, 0], o_ref, rtol=1e-12, atol=1e-14)
+        assert abs(lse[0, h, 0] - l_ref) < 1e-12
