@@ -1,0 +1,63 @@
+"""The five synthetic workloads: shapes and input recipes (no arithmetic of the
+method). Shapes follow Llama-3.1-8B's attention (32 query heads, 8 KV heads,
+head dim 128), the model the Tree Attention explainer evaluates on (section 4);
+no weights, prompts or datasets are involved -- every tensor is drawn from the
+seeded generator.
+
+Recipe: seed = workload number; tensor ids Q=0, K=1, V=2, lengths=3. Values are
+N(0,1) * mul rounded to the storage format; fp8 tensors get one amax/448 scale
+per (batch, KV head).
+"""
+import numpy as np
+
+from . import TID_K, TID_LENS, TID_Q, TID_V, normal_bf16_bits, normal_e4m3, normal_f32, uniform_int
+
+WORKLOADS = {
+    1: dict(name="single-head decode, fp32, L=1024, d=64, 4 splits", kind="decode", B=1, Hq=1, Hkv=1, d=64,
+            L=1024, q="f32", kv="f32", mul=1.0, causal=False, splits=4),
+    2: dict(name="GQA decode, bf16, L=131072, 32q/8kv, d=128", kind="decode", B=1, Hq=32, Hkv=8, d=128,
+            L=131072, q="bf16", kv="bf16", mul=0.5, causal=False, splits=(64, 128, 256)),
+    3: dict(name="batched ragged GQA decode, bf16, B=16, L_b~U[4096,65536]", kind="decode", B=16, Hq=32, Hkv=8,
+            d=128, L=65536, lens=(4096, 65536), q="bf16", kv="bf16", mul=0.5, causal=True, splits=0),
+    4: dict(name="causal prefill, bf16, L=16384, 32q/8kv, d=128", kind="prefill", B=1, Hq=32, Hkv=8, d=128,
+            L=16384, q="bf16", kv="bf16", mul=1.0, causal=True),
+    5: dict(name="fp8-e4m3 KV decode, L=1048576, 32q/8kv, d=128", kind="decode", B=1, Hq=32, Hkv=8, d=128,
+            L=1048576, q="bf16", kv="e4m3", mul=1.0, causal=False, splits=1024),
+}
+
+
+def _draw(fmt, seed, tid, shape, mul):
+    if fmt == "f32":
+        return normal_f32(seed, tid, shape, mul), None
+    if fmt == "bf16":
+        return normal_bf16_bits(seed, tid, shape, mul), None
+    if fmt == "e4m3":
+        return normal_e4m3(seed, tid, shape, mul)
+    raise ValueError(fmt)
+
+
+def make_inputs(wl, seed=None, B=None, Hq=None, Hkv=None, d=None, L=None, Lq=None, mul=None, q_mul=None,
+                lens=None):
+    """Host inputs of a workload (any field overridable for smaller variants).
+
+    Returns dict(q, k, v, k_scale, v_scale, kv_lens) as numpy arrays: bf16 as
+    uint16 bit patterns, e4m3 as uint8 codes, kv_lens int32 or None."""
+    cfg = WORKLOADS[wl] if isinstance(wl, int) else wl
+    seed = cfg.get("seed", wl if isinstance(wl, int) else 0) if seed is None else seed
+    B = B or cfg["B"]
+    Hq = Hq or cfg["Hq"]
+    Hkv = Hkv or cfg["Hkv"]
+    d = d or cfg["d"]
+    L = L or cfg["L"]
+    mul = cfg["mul"] if mul is None else mul
+    if Lq is None:
+        Lq = L if cfg["kind"] == "prefill" else 1
+    q, _ = _draw(cfg["q"], seed, TID_Q, (B, Hq, Lq, d), mul if q_mul is None else q_mul)
+    k, ks = _draw(cfg["kv"], seed, TID_K, (B, Hkv, L, d), mul)
+    v, vs = _draw(cfg["kv"], seed, TID_V, (B, Hkv, L, d), mul)
+    kv_lens = None
+    rng = lens if lens is not None else cfg.get("lens")
+    if rng is not None:
+        kv_lens = uniform_int(seed, TID_LENS, B, int(rng[0]), int(min(rng[1], L)))
+    return dict(q=q, k=k, v=v, k_scale=None if ks is None else ks.ravel(),
+                v_scale=None if vs is None else vs.ravel(), kv_lens=kv_lens)

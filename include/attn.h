@@ -1,0 +1,198 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact scaled-dot-product softmax attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ *   O = softmax(sigma * Q K^T + mask) V,  sigma = 1/sqrt(d) unless given.
+ *
+ * What is computed, and where the pages define it:
+ *  - Attention itself: every query is dotted with every key, the scores are
+ *    normalised by a softmax and used to average the values (glossary page
+ *    "Attention", section on Query/Key/Value). The result is exact, not an
+ *    approximation (explainer of "Tree Attention: Topology-aware Decoding for
+ *    Long-Context Attention on GPU Clusters", section 2).
+ *  - Decode splits the key/value sequence into chunks; each chunk yields a
+ *    partial result that a reduction along the sequence axis merges into the
+ *    exact answer (same Tree Attention explainer, sections 1 and 3). On one GPU
+ *    the chunks are workgroups and the reduction is a two-level tree: LDS inside
+ *    a workgroup, then global memory across workgroups.
+ *  - Score scaling and softmax are fused with the matrix products so that the
+ *    score matrix never travels to DRAM ("Attention in SRAM on Tenstorrent
+ *    Grayskull" explainer, sections 1 and 3), and the softmax subtracts the
+ *    running maximum for stability (same explainer, section 3).
+ *  - Decode reads a KV cache (glossary page, section on memory bandwidth and
+ *    VRAM) and is bound by memory bandwidth (same section); prefill is the
+ *    O(n^2) compute-bound case (glossary page, section on Self-Attention and
+ *    Transformers).
+ *
+ * Conventions (readings where the pages are silent):
+ *  - Tensors are [batch, heads, sequence, head_dim]. Strides are in ELEMENTS and
+ *    the last dimension is contiguous. Head dimension d is 64 or 128.
+ *  - Grouped KV heads: query head h reads KV head h / (Hq / Hkv).
+ *  - Causal masking is aligned bottom-right: with Lkv keys and Lq queries, query
+ *    i sits at position Lkv - Lq + i and sees keys 0 .. Lkv - Lq + i. For a
+ *    single decode query this means "all keys of the sequence".
+ *  - Partials use natural-log units: m = max scaled score, l = sum exp(s - m),
+ *    o = sum exp(s - m) v (unnormalised). The identity is (o=0, m=-inf, l=0).
+ *    A normalised (O, lse) pair is the partial (O, lse, 1).
+ *  - lse (log-sum-exp of the scaled scores, natural log) is fp32; a row that
+ *    sees no key gets O = 0 and lse = -inf.
+ *  - fp8 is OCP E4M3 (bias 7, max 448, no infinity); the real value is
+ *    code * scale with one fp32 scale per (batch, KV head), separately for K
+ *    and V.
+ *
+ * Ownership and errors:
+ *  - Every data pointer is device memory owned by the caller. The library
+ *    allocates nothing and keeps no state between calls; it is thread-safe.
+ *  - Arguments are validated on the host before any launch; a bad argument
+ *    returns an error code and launches nothing. Launches are asynchronous on
+ *    `stream` (a hipStream_t; NULL = the null stream). A launch failure returns
+ *    ATTN_ERR_HIP. attn_last_error() gives a message for the calling thread's
+ *    most recent failure.
+ *  - Determinism: same inputs, same num_splits, same device => bit-identical
+ *    outputs. No floating-point atomics are used.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_API __attribute__((visibility("default")))
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
+    ATTN_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+    ATTN_ERR_HIP = 4          /* the HIP runtime reported an error */
+} attn_status;
+
+typedef enum attn_dtype {
+    ATTN_F32 = 0,
+    ATTN_BF16 = 1,
+    ATTN_FP8_E4M3 = 2
+} attn_dtype;
+
+/* A strided 4-D view [batch, heads, sequence, d]; strides in elements. */
+typedef struct attn_tensor {
+    void* data;
+    int32_t dtype; /* attn_dtype */
+    int64_t stride_b, stride_h, stride_s;
+} attn_tensor;
+
+/* Human-readable name of a status code (static string). */
+ATTN_API const char* attn_status_string(attn_status status);
+
+/* Message describing the calling thread's most recent failed call ("" if none). */
+ATTN_API const char* attn_last_error(void);
+
+/*
+ * Split count that attn_decode uses when num_splits == 0: a pure function of
+ * the shapes, the KV storage type and the compute-unit count of the current
+ * device. Returns >= 1, or 0 on a bad argument or when the device cannot be
+ * queried.
+ */
+ATTN_API int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype);
+
+/*
+ * Bytes of device workspace attn_decode needs for `num_splits` splits (>= 1):
+ * fp32 partials o [B*Hq, S, d], m [B*Hq, S], l [B*Hq, S]. 0 on a bad argument.
+ */
+ATTN_API size_t attn_decode_workspace_size(int B, int Hq, int d, int num_splits);
+
+/*
+ * Split plan of attn_decode / attn_decode_partials for a capacity of L_cap keys
+ * and `num_splits` requested splits (>= 1): chunk = roundup(ceil(L_cap /
+ * num_splits), 64) keys per split; returns the number of splits actually used,
+ * S = ceil(L_cap / chunk) <= num_splits (the partials' row stride), and stores
+ * chunk in *chunk if it is not NULL. 0 on a bad argument.
+ */
+ATTN_API int attn_decode_plan(int L_cap, int num_splits, int* chunk);
+
+/*
+ * Single-query decode over a KV cache (one new token per sequence).
+ *
+ * q        [B, Hq, 1, d]      ATTN_F32 or ATTN_BF16
+ * k, v     [B, Hkv, L_cap, d] same dtype as q, or ATTN_FP8_E4M3 with bf16 q
+ * k_scale, v_scale  device float [B*Hkv] (index b*Hkv + g); required for fp8,
+ *          must be NULL otherwise
+ * kv_lens  device int32 [B]: valid keys per sequence (values are clamped to
+ *          [0, L_cap]); NULL means every sequence has L_cap keys
+ * softmax_scale  <= 0 selects 1/sqrt(d)
+ * causal   accepted for either value; with one query aligned bottom-right the
+ *          query sees every valid key, so it does not change the result
+ * num_splits  0 = attn_decode_auto_splits(); otherwise >= 1. The sequence is
+ *          cut into chunks of roundup(ceil(L_cap/num_splits), 64) keys; a
+ *          sequence of L_b keys uses ceil(L_b/chunk) of them.
+ * out      [B, Hq, 1, d] same dtype as q (bf16 output is rounded to nearest even)
+ * lse      device float [B*Hq] or NULL
+ * workspace  device memory of at least attn_decode_workspace_size(B, Hq, d, S)
+ *          bytes for the split count S in use, 16-byte aligned
+ *
+ * q, k and v need 16-byte aligned data and strides that are multiples of 16
+ * bytes. Supported: d in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
+ * bf16 or fp8 KV with Hq/Hkv == 4 and d == 128 (grouped-query decode of
+ * Llama-style models) runs on MFMA; everything else on the vector ALUs.
+ */
+ATTN_API attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                 const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B,
+                                 int Hq, int Hkv, int d, int L_cap, float softmax_scale, int causal,
+                                 int num_splits, attn_tensor* out, float* lse, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * The first level of attn_decode on its own: the per-chunk partials, merged
+ * inside each workgroup but not across chunks -- what one device contributes
+ * before the cross-device reduction of the Tree Attention explainer (sections
+ * 1 and 3). Arguments as for attn_decode, except the outputs:
+ *   o_part [B*Hq, S, d], m_part [B*Hq, S], l_part [B*Hq, S]: contiguous device
+ *   fp32, row r = b*Hq + h, S = attn_decode_plan(L_cap, num_splits, NULL)
+ *   (num_splits = 0 selects attn_decode_auto_splits()). Splits past the end of
+ *   a shorter sequence hold the identity (0, -inf, 0). *splits_used (host
+ *   pointer, may be NULL) receives S.
+ * attn_combine_partials(o_part, m_part, l_part, B*Hq, S, d, ...) on the result
+ * gives exactly the output of attn_decode.
+ */
+ATTN_API attn_status attn_decode_partials(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                          const float* k_scale, const float* v_scale, const int32_t* kv_lens,
+                                          int B, int Hq, int Hkv, int d, int L_cap, float softmax_scale,
+                                          int causal, int num_splits, float* o_part, float* m_part,
+                                          float* l_part, int* splits_used, void* stream);
+
+/*
+ * Prefill: attention of Lq queries over Lkv keys (causal or not), fused so the
+ * Lq x Lkv score matrix never reaches memory.
+ *
+ * q [B, Hq, Lq, d], k and v [B, Hkv, Lkv, d], out [B, Hq, Lq, d]: ATTN_BF16,
+ * 16-byte aligned data and strides.
+ * lse: device float [B, Hq, Lq] (contiguous) or NULL.
+ * causal with Lq > Lkv is rejected (queries with no visible key).
+ * Supported: d == 128, Hq % Hkv == 0.
+ */
+ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B,
+                                  int Hq, int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal,
+                                  attn_tensor* out, float* lse, void* stream);
+
+/*
+ * Merge S partials per row into the exact normalised result (the reduction
+ * step of the Tree Attention explainer, section 3, on one device): with
+ * m = max_s m_s and w_s = exp(m_s - m), O = sum_s w_s o_s / sum_s w_s l_s and
+ * lse = m + ln sum_s w_s l_s, summed in a fixed balanced order.
+ *
+ * o_part [R, S, d], m_part [R, S], l_part [R, S]: contiguous device fp32.
+ * out: row r of d elements at out->data + r * out->stride_s (F32 or BF16);
+ * stride_b and stride_h are ignored. lse: device float [R] or NULL.
+ * Rows whose partials are all the identity get O = 0 and lse = -inf.
+ */
+ATTN_API attn_status attn_combine_partials(const float* o_part, const float* m_part, const float* l_part, int R,
+                                           int S, int d, attn_tensor* out, float* lse, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

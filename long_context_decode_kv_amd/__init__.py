@@ -1,0 +1,219 @@
+"""Python binding of libattn.so (exact attention for MI355X / gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/attn.h``. torch provides device
+memory (outputs and the decode workspace are allocated here as torch tensors
+when the caller does not pass them) and the current HIP stream.
+
+There is no fallback: if ``libattn.so`` is missing the calls raise.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_FP8_E4M3", "library_path", "load_library",
+    "attn_status_string", "attn_decode_auto_splits", "attn_decode_workspace_size", "attn_decode_plan",
+    "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials",
+]
+
+ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+_STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
+           4: "ATTN_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libattn.so")
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), message))
+        self.status = status
+
+
+class attn_tensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_s", ctypes.c_int64)]
+
+
+def load_library():
+    """Load libattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError("libattn.so not found at %s; build it with __graft_entry__.build()" % library_path)
+    lib = ctypes.CDLL(library_path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    tp = ctypes.POINTER(attn_tensor)
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_last_error.argtypes = []
+    lib.attn_last_error.restype = ctypes.c_char_p
+    lib.attn_decode_auto_splits.argtypes = [i32, i32, i32, i32]
+    lib.attn_decode_auto_splits.restype = i32
+    lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_decode.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, tp, vp, vp,
+                                ctypes.c_size_t, vp]
+    lib.attn_decode.restype = i32
+    lib.attn_decode_plan.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int)]
+    lib.attn_decode_plan.restype = i32
+    lib.attn_decode_partials.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp,
+                                         ctypes.POINTER(ctypes.c_int), vp]
+    lib.attn_decode_partials.restype = i32
+    lib.attn_prefill.argtypes = [tp, tp, tp, i32, i32, i32, i32, i32, i32, f32, i32, tp, vp, vp]
+    lib.attn_prefill.restype = i32
+    lib.attn_combine_partials.argtypes = [vp, vp, vp, i32, i32, i32, tp, vp, vp]
+    lib.attn_combine_partials.restype = i32
+    _lib = lib
+    return lib
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return ATTN_FP8_E4M3
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _tensor(t):
+    if t.dim() != 4:
+        raise ValueError("expected a 4-D [batch, heads, seq, d] tensor, got shape %s" % (tuple(t.shape),))
+    if t.stride(3) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    return attn_tensor(t.data_ptr(), _dtype_code(t), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _check(status):
+    if status != 0:
+        raise AttnError(status, load_library().attn_last_error().decode())
+
+
+def attn_status_string(status):
+    return load_library().attn_status_string(int(status)).decode()
+
+
+def attn_decode_auto_splits(B, Hkv, L_cap, kv_dtype=ATTN_BF16):
+    return load_library().attn_decode_auto_splits(B, Hkv, L_cap, kv_dtype)
+
+
+def attn_decode_workspace_size(B, Hq, d, num_splits):
+    return load_library().attn_decode_workspace_size(B, Hq, d, num_splits)
+
+
+def attn_decode_plan(L_cap, num_splits):
+    """(S, chunk): splits used and keys per split for a requested split count."""
+    chunk = ctypes.c_int(0)
+    S = load_library().attn_decode_plan(L_cap, num_splits, ctypes.byref(chunk))
+    return S, chunk.value
+
+
+def attn_decode(q, k, v, k_scale=None, v_scale=None, kv_lens=None, softmax_scale=0.0, causal=False, num_splits=0,
+                out=None, lse=None, workspace=None, stream=None):
+    """Single-query decode. q [B,Hq,1,d]; k, v [B,Hkv,L_cap,d]. Returns (out, lse)."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    Hkv, L_cap = k.shape[1], k.shape[2]
+    if Lq != 1:
+        raise ValueError("attn_decode takes one query per sequence (q.shape[2] == 1)")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    S = num_splits if num_splits > 0 else lib.attn_decode_auto_splits(B, Hkv, L_cap, _dtype_code(k))
+    if S <= 0:
+        raise AttnError(4, "could not plan splits")
+    need = lib.attn_decode_workspace_size(B, Hq, d, S)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    st = lib.attn_decode(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), _ptr(k_scale), _ptr(v_scale),
+                         _ptr(kv_lens), B, Hq, Hkv, d, L_cap, float(softmax_scale), int(bool(causal)), int(S),
+                         ctypes.byref(ot), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                         _stream(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_partials(q, k, v, k_scale=None, v_scale=None, kv_lens=None, softmax_scale=0.0, causal=False,
+                         num_splits=0, o_part=None, m_part=None, l_part=None, stream=None):
+    """First level of the decode: returns (o_part [B*Hq,S,d], m_part [B*Hq,S], l_part [B*Hq,S])."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    Hkv, L_cap = k.shape[1], k.shape[2]
+    if Lq != 1:
+        raise ValueError("attn_decode_partials takes one query per sequence (q.shape[2] == 1)")
+    req = num_splits if num_splits > 0 else lib.attn_decode_auto_splits(B, Hkv, L_cap, _dtype_code(k))
+    S, _ = attn_decode_plan(L_cap, req)
+    if S <= 0:
+        raise AttnError(4, "could not plan splits")
+    dev = q.device
+    o_part = torch.empty((B * Hq, S, d), dtype=torch.float32, device=dev) if o_part is None else o_part
+    m_part = torch.empty((B * Hq, S), dtype=torch.float32, device=dev) if m_part is None else m_part
+    l_part = torch.empty((B * Hq, S), dtype=torch.float32, device=dev) if l_part is None else l_part
+    for t, shape in ((o_part, (B * Hq, S, d)), (m_part, (B * Hq, S)), (l_part, (B * Hq, S))):
+        if tuple(t.shape) != shape or t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("partials must be contiguous fp32 of shape %s" % (shape,))
+    used = ctypes.c_int(0)
+    qt, kt, vt = _tensor(q), _tensor(k), _tensor(v)
+    st = lib.attn_decode_partials(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), _ptr(k_scale),
+                                  _ptr(v_scale), _ptr(kv_lens), B, Hq, Hkv, d, L_cap, float(softmax_scale),
+                                  int(bool(causal)), int(req), _ptr(o_part), _ptr(m_part), _ptr(l_part),
+                                  ctypes.byref(used), _stream(stream, dev))
+    _check(st)
+    return o_part, m_part, l_part
+
+
+def attn_prefill(q, k, v, softmax_scale=0.0, causal=True, out=None, lse=None, stream=None):
+    """Prefill attention. q [B,Hq,Lq,d]; k, v [B,Hkv,Lkv,d] (bf16). Returns (out, lse [B,Hq,Lq])."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    st = lib.attn_prefill(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), B, Hq, Hkv, d, Lq, Lkv,
+                          float(softmax_scale), int(bool(causal)), ctypes.byref(ot), _ptr(lse),
+                          _stream(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_combine_partials(o_part, m_part, l_part, out=None, lse=None, out_dtype=torch.float32, stream=None):
+    """Merge partials o [R,S,d], m [R,S], l [R,S] (fp32) into (out [R,d], lse [R])."""
+    lib = load_library()
+    R, S, d = o_part.shape
+    for t in (o_part, m_part, l_part):
+        if t.dtype != torch.float32 or not t.is_contiguous():
+            raise ValueError("partials must be contiguous fp32")
+    if out is None:
+        out = torch.empty((R, d), dtype=out_dtype, device=o_part.device)
+    if lse is None:
+        lse = torch.empty((R,), dtype=torch.float32, device=o_part.device)
+    if out.stride(1) != 1:
+        raise ValueError("out rows must be contiguous")
+    ot = attn_tensor(out.data_ptr(), _dtype_code(out), 0, 0, out.stride(0))
+    st = lib.attn_combine_partials(_ptr(o_part), _ptr(m_part), _ptr(l_part), R, S, d, ctypes.byref(ot), _ptr(lse),
+                                   _stream(stream, o_part.device))
+    _check(st)
+    return out, lse

@@ -1,0 +1,346 @@
+// C-ABI front end of libattn.so: argument validation (host only, before any
+// HIP call), the split plan, workspace layout and kernel dispatch. The
+// operations and their sources are described in include/attn.h.
+#include "attn.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+attn_status fail(attn_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+constexpr int kChunkQuantum = 64;  // keys per workgroup step (4 waves x 16 keys)
+constexpr float kLog2e = 1.44269504088896340736f;
+
+int elem_size(int dt) {
+    switch (dt) {
+    case ATTN_F32: return 4;
+    case ATTN_BF16: return 2;
+    case ATTN_FP8_E4M3: return 1;
+    default: return 0;
+    }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks a [*, *, *, d] operand: data present, known dtype, 16-byte aligned
+// base and 16-byte multiples for the strides the kernels step with.
+attn_status check_tensor(const attn_tensor* t, const char* name, bool need_row_alignment) {
+    if (!t) return fail(ATTN_ERR_INVALID_ARG, "%s: null tensor", name);
+    if (!t->data) return fail(ATTN_ERR_INVALID_ARG, "%s: null data pointer", name);
+    const int es = elem_size(t->dtype);
+    if (!es) return fail(ATTN_ERR_INVALID_ARG, "%s: unknown dtype %d", name, t->dtype);
+    if (t->stride_b < 0 || t->stride_h < 0 || t->stride_s < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: negative stride", name);
+    if (need_row_alignment) {
+        if (!aligned16(t->data)) return fail(ATTN_ERR_INVALID_ARG, "%s: data must be 16-byte aligned", name);
+        if ((t->stride_b * es) % 16 || (t->stride_h * es) % 16 || (t->stride_s * es) % 16)
+            return fail(ATTN_ERR_INVALID_ARG, "%s: strides must be multiples of 16 bytes", name);
+    }
+    return ATTN_OK;
+}
+
+int device_cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Split plan shared by attn_decode and its size queries.
+struct Plan {
+    int chunk;  // keys per split, a multiple of kChunkQuantum
+    int S;      // splits actually launched
+};
+
+Plan plan_splits(int L_cap, int requested) {
+    Plan pl;
+    pl.chunk = (int)(ceil_div(ceil_div(L_cap, requested), kChunkQuantum) * kChunkQuantum);
+    pl.S = (int)ceil_div(L_cap, pl.chunk);
+    return pl;
+}
+
+size_t partial_bytes(int64_t rows, int64_t S, int64_t d) { return (size_t)(rows * S * (d + 2) * 4); }
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(attn_status status) {
+    switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "ATTN_UNKNOWN_STATUS";
+    }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype) {
+    if (B <= 0 || Hkv <= 0 || L_cap <= 0 || !elem_size(kv_dtype)) return 0;
+    const int cus = device_cu_count();
+    if (cus <= 0) return 0;
+    // About four resident workgroups per compute unit in total, but no split
+    // shorter than 256 keys.
+    const int64_t target_wgs = 4LL * cus;
+    int64_t S = ceil_div(target_wgs, (int64_t)B * Hkv);
+    const int64_t max_s = ceil_div(L_cap, 256);
+    if (S > max_s) S = max_s;
+    if (S < 1) S = 1;
+    return (int)S;
+}
+
+size_t attn_decode_workspace_size(int B, int Hq, int d, int num_splits) {
+    if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 0) return 0;
+    return partial_bytes((int64_t)B * Hq, num_splits, d);
+}
+
+int attn_decode_plan(int L_cap, int num_splits, int* chunk) {
+    if (L_cap <= 0 || num_splits <= 0) return 0;
+    const Plan pl = plan_splits(L_cap, num_splits);
+    if (chunk) *chunk = pl.chunk;
+    return pl.S;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation and the first level (partials) shared by attn_decode and
+// attn_decode_partials. On success *pl holds the split plan used.
+attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const float* k_scale,
+                          const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int d, int L_cap,
+                          float softmax_scale, int num_splits, const attn_tensor* out, float* o_part,
+                          float* m_part, float* l_part, size_t part_bytes, Plan* pl, hipStream_t stream) {
+    attn_status st;
+    if ((st = check_tensor(q, "q", true)) || (st = check_tensor(k, "k", true)) || (st = check_tensor(v, "v", true)))
+        return st;
+    if (out && (st = check_tensor(out, "out", false))) return st;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || L_cap <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d d=%d L_cap=%d)", B, Hq, Hkv, d,
+                    L_cap);
+    if (B > 65535 || Hkv > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and Hkv must be <= 65535");
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    const int G = Hq / Hkv;
+    if (num_splits < 0) return fail(ATTN_ERR_INVALID_ARG, "num_splits must be >= 0");
+    if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (k->dtype != v->dtype) return fail(ATTN_ERR_INVALID_ARG, "k and v dtypes differ");
+    if (out && out->dtype != q->dtype) return fail(ATTN_ERR_INVALID_ARG, "out dtype must equal q dtype");
+    const bool fp8 = k->dtype == ATTN_FP8_E4M3;
+    if (q->dtype == ATTN_F32 && k->dtype != ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "fp32 q needs fp32 k/v");
+    if (q->dtype == ATTN_BF16 && k->dtype == ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "bf16 q with fp32 k/v");
+    if (q->dtype == ATTN_FP8_E4M3) return fail(ATTN_ERR_UNSUPPORTED, "q must be fp32 or bf16");
+    if (fp8 && (!k_scale || !v_scale)) return fail(ATTN_ERR_INVALID_ARG, "fp8 k/v need k_scale and v_scale");
+    if (!fp8 && (k_scale || v_scale)) return fail(ATTN_ERR_INVALID_ARG, "scales are only for fp8 k/v");
+    if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);
+    if (G != 1 && G != 2 && G != 4 && G != 8)
+        return fail(ATTN_ERR_UNSUPPORTED, "Hq/Hkv = %d (supported: 1, 2, 4, 8)", G);
+
+    int requested = num_splits;
+    if (requested == 0) {
+        requested = attn_decode_auto_splits(B, Hkv, L_cap, k->dtype);
+        if (requested <= 0) return fail(ATTN_ERR_HIP, "could not query the device for the split plan");
+    }
+    *pl = plan_splits(L_cap, requested);
+    const int64_t rows = (int64_t)B * Hq;
+    if (!o_part || !m_part || !l_part) return fail(ATTN_ERR_WORKSPACE, "workspace (partials) is null");
+    if (!aligned16(o_part)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (part_bytes != (size_t)-1 && part_bytes < partial_bytes(rows, pl->S, d))
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need %zu for %d splits", part_bytes,
+                    partial_bytes(rows, pl->S, d), pl->S);
+
+    const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+    attn::DecodeParams p;
+    p.q = q->data;
+    p.q_sb = q->stride_b;
+    p.q_sh = q->stride_h;
+    p.k = k->data;
+    p.k_sb = k->stride_b;
+    p.k_sh = k->stride_h;
+    p.k_ss = k->stride_s;
+    p.v = v->data;
+    p.v_sb = v->stride_b;
+    p.v_sh = v->stride_h;
+    p.v_ss = v->stride_s;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.kv_lens = kv_lens;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.L_cap = L_cap;
+    p.chunk = pl->chunk;
+    p.S = pl->S;
+    p.scale_log2 = sc * kLog2e;
+    p.o_part = o_part;
+    p.m_part = m_part;
+    p.l_part = l_part;
+
+    hipError_t e;
+    const bool mfma = q->dtype == ATTN_BF16 && G == 4 && d == 128;
+    if (mfma) e = attn::launch_decode_mfma(p, fp8 ? attn::DT_FP8 : attn::DT_BF16, stream);
+    else e = attn::launch_decode_valu(p, q->dtype, k->dtype, G, stream);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const float* k_scale,
+                        const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int d, int L_cap,
+                        float softmax_scale, int causal, int num_splits, attn_tensor* out, float* lse,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    (void)causal;  // one query aligned bottom-right sees every valid key
+    g_last_error[0] = 0;
+    if (!out) return fail(ATTN_ERR_INVALID_ARG, "out: null tensor");
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
+    // Partials layout inside the workspace depends on the plan; compute it first.
+    Plan pl{0, 0};
+    int requested = num_splits;
+    if (requested == 0 && B > 0 && Hkv > 0 && L_cap > 0 && k) requested = attn_decode_auto_splits(B, Hkv, L_cap, k->dtype);
+    const int64_t rows = (int64_t)(B > 0 ? B : 0) * (Hq > 0 ? Hq : 0);
+    int S_guess = (requested > 0 && L_cap > 0) ? plan_splits(L_cap, requested).S : 1;
+    float* o_part = static_cast<float*>(workspace);
+    float* m_part = o_part + rows * S_guess * (d > 0 ? d : 0);
+    float* l_part = m_part + rows * S_guess;
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    attn_status st = decode_level1(q, k, v, k_scale, v_scale, kv_lens, B, Hq, Hkv, d, L_cap, softmax_scale,
+                                   num_splits, out, o_part, m_part, l_part, workspace_bytes, &pl, hs);
+    if (st != ATTN_OK) return st;
+
+    attn::CombineParams cp;
+    cp.o_part = o_part;
+    cp.m_part = m_part;
+    cp.l_part = l_part;
+    cp.R = (int)rows;
+    cp.S = pl.S;
+    cp.d = d;
+    cp.Hq = Hq;
+    cp.kv_lens = kv_lens;
+    cp.chunk = pl.chunk;
+    cp.L_cap = L_cap;
+    cp.out = out->data;
+    cp.out_dtype = out->dtype;
+    cp.out_sb = out->stride_b;
+    cp.out_sh = out->stride_h;
+    cp.lse = lse;
+    hipError_t e = attn::launch_combine(cp, hs);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+attn_status attn_decode_partials(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                 const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B, int Hq,
+                                 int Hkv, int d, int L_cap, float softmax_scale, int causal, int num_splits,
+                                 float* o_part, float* m_part, float* l_part, int* splits_used, void* stream) {
+    (void)causal;
+    g_last_error[0] = 0;
+    Plan pl{0, 0};
+    attn_status st = decode_level1(q, k, v, k_scale, v_scale, kv_lens, B, Hq, Hkv, d, L_cap, softmax_scale,
+                                   num_splits, nullptr, o_part, m_part, l_part, (size_t)-1, &pl,
+                                   static_cast<hipStream_t>(stream));
+    if (st == ATTN_OK && splits_used) *splits_used = pl.S;
+    return st;
+}
+
+attn_status attn_combine_partials(const float* o_part, const float* m_part, const float* l_part, int R, int S,
+                                  int d, attn_tensor* out, float* lse, void* stream) {
+    g_last_error[0] = 0;
+    if (!o_part || !m_part || !l_part) return fail(ATTN_ERR_INVALID_ARG, "null partial pointer");
+    attn_status st;
+    if ((st = check_tensor(out, "out", false))) return st;
+    if (R <= 0 || S <= 0 || d <= 0) return fail(ATTN_ERR_INVALID_ARG, "R, S and d must be positive");
+    if (out->dtype != ATTN_F32 && out->dtype != ATTN_BF16)
+        return fail(ATTN_ERR_UNSUPPORTED, "out must be fp32 or bf16");
+    attn::CombineParams cp;
+    cp.o_part = o_part;
+    cp.m_part = m_part;
+    cp.l_part = l_part;
+    cp.R = R;
+    cp.S = S;
+    cp.d = d;
+    cp.Hq = 1;
+    cp.kv_lens = nullptr;
+    cp.chunk = 1;
+    cp.L_cap = 0;
+    cp.out = out->data;
+    cp.out_dtype = out->dtype;
+    cp.out_sb = out->stride_s;  // row r = "batch" r with Hq = 1
+    cp.out_sh = 0;
+    cp.lse = lse;
+    hipError_t e = attn::launch_combine(cp, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B, int Hq, int Hkv,
+                         int d, int Lq, int Lkv, float softmax_scale, int causal, attn_tensor* out, float* lse,
+                         void* stream) {
+    g_last_error[0] = 0;
+    attn_status st;
+    if ((st = check_tensor(q, "q", true)) || (st = check_tensor(k, "k", true)) || (st = check_tensor(v, "v", true)) ||
+        (st = check_tensor(out, "out", true)))
+        return st;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Lq <= 0 || Lkv <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive");
+    if (B > 65535 || Hq > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and Hq must be <= 65535");
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (causal && Lq > Lkv) return fail(ATTN_ERR_INVALID_ARG, "causal with Lq (%d) > Lkv (%d)", Lq, Lkv);
+    if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (q->dtype != ATTN_BF16 || k->dtype != ATTN_BF16 || v->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
+        return fail(ATTN_ERR_UNSUPPORTED, "prefill supports bf16 q/k/v/out");
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "prefill head dim %d (supported: 128)", d);
+    const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+    attn::PrefillParams p;
+    p.q = q->data;
+    p.q_sb = q->stride_b;
+    p.q_sh = q->stride_h;
+    p.q_ss = q->stride_s;
+    p.k = k->data;
+    p.k_sb = k->stride_b;
+    p.k_sh = k->stride_h;
+    p.k_ss = k->stride_s;
+    p.v = v->data;
+    p.v_sb = v->stride_b;
+    p.v_sh = v->stride_h;
+    p.v_ss = v->stride_s;
+    p.out = out->data;
+    p.o_sb = out->stride_b;
+    p.o_sh = out->stride_h;
+    p.o_ss = out->stride_s;
+    p.lse = lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.Lq = Lq;
+    p.Lkv = Lkv;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = sc * kLog2e;
+    hipError_t e = attn::launch_prefill(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// Level-2 merge of split-KV partials: the global step of the two-level
+// log-sum-exp tree (the reduction along the sequence axis of the explainer of
+// "Tree Attention: Topology-aware Decoding for Long-Context Attention on GPU
+// Clusters", section 3; "exact, not approximate", its section 2).
+//
+// For a row with partials (o_s, m_s, l_s), s < n:
+//   m = max_s m_s,  w_s = exp(m_s - m),
+//   O = sum_s w_s o_s / sum_s w_s l_s,  lse = m + ln sum_s w_s l_s.
+// Workgroup (r, 32-dim block): 8 lane groups of 32 threads each take every 8th
+// partial in order; the 8 group sums are then added as a fixed balanced tree,
+// so the result is deterministic for a given n.
+#include "internal.h"
+
+namespace attn {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__global__ __launch_bounds__(256) void combine_partials_kernel(CombineParams p) {
+    const int r = blockIdx.x;
+    const int c0 = blockIdx.y * 32;
+    const int tid = threadIdx.x;
+    const int b = r / p.Hq, h = r % p.Hq;
+    int n = p.S;
+    if (p.kv_lens) {
+        const int len = min(max(p.kv_lens[b], 0), p.L_cap);
+        n = min((len + p.chunk - 1) / p.chunk, p.S);
+    }
+    const float* m_row = p.m_part + (int64_t)r * p.S;
+    const float* l_row = p.l_part + (int64_t)r * p.S;
+
+    __shared__ float red[256];
+    float mx = kNegInf;
+    for (int s = tid; s < n; s += 256) mx = fmaxf(mx, m_row[s]);
+    red[tid] = mx;
+    __syncthreads();
+    for (int off = 128; off > 0; off >>= 1) {
+        if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+        __syncthreads();
+    }
+    mx = red[0];
+    __syncthreads();
+
+    const int grp = tid >> 5, c = c0 + (tid & 31);
+    float ao = 0.f, al = 0.f;
+    if (mx != kNegInf) {
+        for (int s = grp; s < n; s += 8) {
+            const float ms = m_row[s];
+            const float wgt = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ms - mx) * kLog2e);
+            al = fmaf(wgt, l_row[s], al);
+            if (c < p.d) ao = fmaf(wgt, p.o_part[((int64_t)r * p.S + s) * p.d + c], ao);
+        }
+    }
+    __shared__ float red_o[8][32];
+    __shared__ float red_l[8];
+    red_o[grp][tid & 31] = ao;
+    if ((tid & 31) == 0) red_l[grp] = al;
+    __syncthreads();
+    if (grp == 0 && c < p.d) {
+        const int j = tid & 31;
+        const float so = ((red_o[0][j] + red_o[1][j]) + (red_o[2][j] + red_o[3][j])) +
+                         ((red_o[4][j] + red_o[5][j]) + (red_o[6][j] + red_o[7][j]));
+        const float sl = ((red_l[0] + red_l[1]) + (red_l[2] + red_l[3])) + ((red_l[4] + red_l[5]) + (red_l[6] + red_l[7]));
+        const bool empty = (mx == kNegInf) || !(sl > 0.f);
+        const float val = empty ? 0.f : so / sl;
+        const int64_t off = b * p.out_sb + h * p.out_sh + c;
+        if (p.out_dtype == DT_BF16) static_cast<uint16_t*>(p.out)[off] = f32_to_bf16_rne(val);
+        else static_cast<float*>(p.out)[off] = val;
+        if (p.lse && blockIdx.y == 0 && j == 0) p.lse[r] = empty ? kNegInf : mx + logf(sl);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
+    dim3 grid(p.R, (p.d + 31) / 32);
+    hipLaunchKernelGGL(combine_partials_kernel, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -1,0 +1,318 @@
+// Split-KV grouped-query decode for gfx950: one query token, four query heads
+// per KV head, head dim 128, KV cache in bf16 or OCP fp8-e4m3.
+//
+// Work split (the single-GPU form of the sequence-axis tree reduction in the
+// explainer of "Tree Attention: Topology-aware Decoding for Long-Context
+// Attention on GPU Clusters", section 3): workgroup (s, g, b) owns one chunk of
+// keys of KV head g of sequence b and emits one partial (o, m, l) per query
+// head. The four waves of the workgroup interleave 16-key tiles of the chunk;
+// inside a wave, each group of 16 lanes keeps its own running partial, so the
+// hot loop needs no cross-lane reduction at all. The partials are merged in
+// registers (lane groups), then in LDS (waves) -- the level-1 tree -- and the
+// level-2 tree across workgroups runs in combine.hip.
+//
+// Per 16-key tile and wave:
+//  * scores: S^T = K Q^T on one v_mfma_f32_16x16x32_bf16 chain (4 steps over
+//    d=128). A = 16 key rows, B = Q^T with the four query heads repeated in the
+//    16 columns, so lane l receives the scores of head (l & 3) for keys
+//    4*(l>>4) .. 4*(l>>4)+3 of the tile. MFMA is used only because this product
+//    is a dense contraction; 75% of its columns are repeats, which costs
+//    nothing that matters at 4 flop/byte.
+//  * softmax: scores stay in base-2 units (scale folded with log2 e). The
+//    running maximum moves only when a score exceeds it by 8 (2^8 headroom
+//    in fp32), so rescaling the accumulators is rare; the result is the same
+//    exact quantity, normalised with the same maximum in o and l. The
+//    stability step is the max subtraction the Grayskull explainer names in
+//    section 3.
+//  * P.V on the vector ALUs: lane l holds V for the same four keys at dims
+//    8*(l&15) .. +7, fetches the four heads' weights of each key from its quad
+//    with DPP broadcasts, and accumulates 4 heads x 8 dims in fp32.
+// K is read 16 rows x 64 bytes per load (the MFMA operand layout), V four full
+// 256-byte rows per load; every valid key is read from HBM exactly once, and
+// the next tile's loads are issued before the current tile is computed.
+#include "internal.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 4;
+constexpr int kTile = 16;          // keys per wave per step
+constexpr float kHeadroom = 8.0f;  // base-2 units a score may exceed the running max by
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Value of lane (l & ~3) + H, for every lane l (DPP quad_perm broadcast).
+template <int H>
+__device__ __forceinline__ float quad_bcast(float x) {
+    constexpr int ctrl = H | (H << 2) | (H << 4) | (H << 6);
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <bool FP8>
+struct Tile;
+template <>
+struct Tile<false> {
+    u32x4 k[4];  // MFMA step i: 8 bf16 at dims 32i + 8*(lane>>4) of key row (lane & 15)
+    u32x4 v[4];  // key 4*(lane>>4) + u: 8 bf16 at dims 8*(lane & 15)
+};
+template <>
+struct Tile<true> {
+    u32x4 k[2];  // half h: 16 fp8 at dims 64h + 16*(lane>>4) of key row (lane & 15)
+    u32x2 v[4];  // key 4*(lane>>4) + u: 8 fp8 at dims 8*(lane & 15)
+};
+
+// Loads one 16-key tile; key indices past `tlast` are clamped to it, so every
+// address stays inside the cache and the clamped keys are masked later.
+template <bool FP8>
+__device__ __forceinline__ void load_tile(Tile<FP8>& t, const char* kbase, const char* vbase, int64_t kss,
+                                          int64_t vss, int tok0, int tlast, int lane) {
+    const int rk = min(tok0 + (lane & 15), tlast);
+    const char* krow = kbase + (int64_t)rk * kss;
+    if constexpr (!FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            t.k[i] = *reinterpret_cast<const u32x4*>(krow + 2 * (32 * i + 8 * (lane >> 4)));
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) t.k[h] = *reinterpret_cast<const u32x4*>(krow + 64 * h + 16 * (lane >> 4));
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
+        const char* vrow = vbase + (int64_t)rv * vss;
+        if constexpr (!FP8) t.v[u] = *reinterpret_cast<const u32x4*>(vrow + 2 * 8 * (lane & 15));
+        else t.v[u] = *reinterpret_cast<const u32x2*>(vrow + 8 * (lane & 15));
+    }
+}
+
+// Four OCP e4m3 codes of a dword pair -> eight bf16 (exact widening).
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+    bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <bool FP8>
+__device__ __forceinline__ void v_to_f32(const Tile<FP8>& t, int u, float (&vf)[8]) {
+    if constexpr (!FP8) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vf[2 * e] = bf16_lo(t.v[u][e]);
+            vf[2 * e + 1] = bf16_hi(t.v[u][e]);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(t.v[u][e], false);
+            f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(t.v[u][e], true);
+            vf[4 * e + 0] = a[0];
+            vf[4 * e + 1] = a[1];
+            vf[4 * e + 2] = b[0];
+            vf[4 * e + 3] = b[1];
+        }
+    }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void compute_tile(const Tile<FP8>& t, const bf16x8 (&qop)[4], float scale2, int tok0,
+                                             int tend, int lane, float& m_run, float& l_run, float (&o)[4][8]) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (!FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[i]), qop[i], acc, 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(t.k[h][0], t.k[h][1]), qop[2 * h], acc, 0,
+                                                          0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(t.k[h][2], t.k[h][3]), qop[2 * h + 1], acc,
+                                                          0, 0, 0);
+        }
+    }
+    const int kb = tok0 + 4 * (lane >> 4);
+    float s[4];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        s[r] = (kb + r < tend) ? acc[r] * scale2 : kNegInf;
+        tmax = fmaxf(tmax, s[r]);
+    }
+    const bool need = tmax > m_run + kHeadroom;
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+        const float a[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] *= a[h];
+    }
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = (s[r] == kNegInf) ? 0.f : fast_exp2(s[r] - m_run);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const float pb[4] = {quad_bcast<0>(p[u]), quad_bcast<1>(p[u]), quad_bcast<2>(p[u]), quad_bcast<3>(p[u])};
+        float vf[8];
+        v_to_f32<FP8>(t, u, vf);
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pb[h], vf[e], o[h][e]);
+    }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
+    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    int L_b = p.L_cap;
+    if (p.kv_lens) L_b = min(max(p.kv_lens[b], 0), p.L_cap);
+    const int t_begin = s * p.chunk;
+    const int t_end = min(t_begin + p.chunk, L_b);
+    if (t_begin >= t_end) {
+        // A split past the end of a shorter sequence: the identity partial.
+        for (int i = tid; i < 4 * 128; i += 256) {
+            const int64_t row = (int64_t)b * p.Hq + g * 4 + i / 128;
+            p.o_part[(row * p.S + s) * 128 + i % 128] = 0.f;
+            if (i % 128 == 0) {
+                p.m_part[row * p.S + s] = kNegInf;
+                p.l_part[row * p.S + s] = 0.f;
+            }
+        }
+        return;
+    }
+    const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
+
+    constexpr int esz = FP8 ? 1 : 2;
+    const char* kbase = static_cast<const char*>(p.k) + (b * p.k_sb + g * p.k_sh) * esz;
+    const char* vbase = static_cast<const char*>(p.v) + (b * p.v_sb + g * p.v_sh) * esz;
+    const int64_t kss = p.k_ss * esz, vss = p.v_ss * esz;
+
+    // Q^T operand: column (lane & 15) is query head 4g + (lane & 3); its k-slots
+    // follow the same dim order as the K operand.
+    const __bf16* qrow = static_cast<const __bf16*>(p.q) + b * p.q_sb + (int64_t)(g * 4 + (lane & 3)) * p.q_sh;
+    bf16x8 qop[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int dim = FP8 ? 64 * (i >> 1) + 16 * (lane >> 4) + 8 * (i & 1) : 32 * i + 8 * (lane >> 4);
+        qop[i] = *reinterpret_cast<const bf16x8*>(qrow + dim);
+    }
+    float scale2 = p.scale_log2;
+    float vsc = 1.0f;
+    if constexpr (FP8) {
+        scale2 *= p.k_scale[b * p.Hkv + g];
+        vsc = p.v_scale[b * p.Hkv + g];
+    }
+
+    float m_run = kNegInf, l_run = 0.f;
+    float o[4][8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+
+    int k = w;
+    if (k < ntiles) {
+        Tile<FP8> cur;
+        load_tile<FP8>(cur, kbase, vbase, kss, vss, t_begin + kTile * k, t_end - 1, lane);
+        for (; k < ntiles; k += kWaves) {
+            Tile<FP8> nxt;
+            const bool more = k + kWaves < ntiles;
+            if (more) load_tile<FP8>(nxt, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+            compute_tile<FP8>(cur, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+            if (more) cur = nxt;
+        }
+    }
+
+    // Level 1a: merge the four lane groups (keys 4*(lane>>4)..) of this wave.
+    float M = fmaxf(m_run, __shfl_xor(m_run, 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float f = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - M);
+    float lw = l_run * f;
+    lw += __shfl_xor(lw, 16);
+    lw += __shfl_xor(lw, 32);
+    {
+        const float fh[4] = {quad_bcast<0>(f), quad_bcast<1>(f), quad_bcast<2>(f), quad_bcast<3>(f)};
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float x = o[h][e] * fh[h];
+                x += __shfl_xor(x, 16);
+                x += __shfl_xor(x, 32);
+                o[h][e] = x;
+            }
+    }
+
+    // Level 1b: merge the four waves in LDS.
+    __shared__ float lds_o[kWaves][4][128];
+    __shared__ float lds_m[kWaves][4];
+    __shared__ float lds_l[kWaves][4];
+    if (lane < 16) {
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lds_o[w][h][8 * lane + e] = o[h][e];
+    }
+    if (lane < 4) {
+        lds_m[w][lane] = M;
+        lds_l[w][lane] = lw;
+    }
+    __syncthreads();
+
+    const int h = tid >> 6;
+    const int c = (tid & 63) * 2;
+    float mw[kWaves], fw[kWaves];
+    float Mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        mw[i] = lds_m[i][h];
+        Mx = fmaxf(Mx, mw[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) fw[i] = (mw[i] == kNegInf) ? 0.f : fast_exp2(mw[i] - Mx);
+    const float L = (fw[0] * lds_l[0][h] + fw[1] * lds_l[1][h]) + (fw[2] * lds_l[2][h] + fw[3] * lds_l[3][h]);
+    f32x2 out;
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+        const float v = (fw[0] * lds_o[0][h][c + cc] + fw[1] * lds_o[1][h][c + cc]) +
+                        (fw[2] * lds_o[2][h][c + cc] + fw[3] * lds_o[3][h][c + cc]);
+        out[cc] = v * vsc;
+    }
+    const int64_t row = (int64_t)b * p.Hq + g * 4 + h;
+    *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s) * 128 + c) = out;
+    if ((tid & 63) == 0) {
+        p.m_part[row * p.S + s] = Mx * kLn2;
+        p.l_part[row * p.S + s] = L;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
+    dim3 grid(p.S, p.Hkv, p.B);
+    if (kv_dtype == DT_FP8) hipLaunchKernelGGL(decode_gqa4_d128<true>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(decode_gqa4_d128<false>, grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace attn

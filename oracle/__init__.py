@@ -60,7 +60,7 @@ def _load():
 
 
 def _threads():
-    return max(1, min(os.cpu_count() or 1, 64))
+    return max(1, min(os.cpu_count() or 1, 16))
 
 
 def _p(a):

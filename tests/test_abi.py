@@ -1,0 +1,134 @@
+"""The C ABI on the CPU: libattn.so loads, exports every function that
+include/attn.h declares, and rejects bad arguments with the documented status
+codes before touching the GPU (so these run without one)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import long_context_decode_kv_amd as lib
+from long_context_decode_kv_amd import attn_tensor
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+F32, BF16, FP8 = 0, 1, 2
+
+
+@pytest.fixture(scope="module")
+def so():
+    if not os.path.exists(lib.library_path):
+        from long_context_decode_kv_amd import build
+        build.build()
+    return lib.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "attn.h")).read()
+    return re.findall(r"ATTN_API\s+[\w\s\*]+?\b(attn_\w+)\s*\(", text)
+
+
+def test_every_declared_symbol_is_exported(so):
+    names = declared_functions()
+    assert set(names) == {"attn_status_string", "attn_last_error", "attn_decode_auto_splits",
+                          "attn_decode_workspace_size", "attn_decode_plan", "attn_decode", "attn_decode_partials",
+                          "attn_prefill", "attn_combine_partials"}
+    nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
+    for n in names:
+        assert n in exported, n
+        assert getattr(so, n) is not None
+    # nothing else named attn_* leaks out
+    assert {e for e in exported if e.startswith("attn_")} == set(names)
+
+
+def test_status_strings(so):
+    assert [lib.attn_status_string(s) for s in range(5)] == [
+        "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP"]
+
+
+def test_split_plan(so):
+    # chunk = roundup(ceil(L/S), 64); S_used = ceil(L/chunk)
+    assert lib.attn_decode_plan(131072, 256) == (256, 512)
+    assert lib.attn_decode_plan(131072, 100) == (98, 1344)
+    assert lib.attn_decode_plan(1024, 4) == (4, 256)
+    assert lib.attn_decode_plan(1000, 7) == (6, 192)
+    assert lib.attn_decode_plan(100, 64) == (2, 64)
+    assert lib.attn_decode_plan(0, 4)[0] == 0 and lib.attn_decode_plan(10, 0)[0] == 0
+    for L in (1, 63, 64, 65, 1000, 65536, 1 << 20):
+        for S in (1, 2, 3, 7, 64, 1000):
+            used, chunk = lib.attn_decode_plan(L, S)
+            assert chunk % 64 == 0 and used <= S and (used - 1) * chunk < L <= used * chunk
+
+
+def test_workspace_size(so):
+    assert lib.attn_decode_workspace_size(1, 32, 128, 256) == 32 * 256 * 130 * 4
+    assert lib.attn_decode_workspace_size(16, 32, 128, 0) == 0
+    assert lib.attn_decode_workspace_size(0, 32, 128, 4) == 0
+
+
+FAKE = 0x100000  # never dereferenced: validation fails first
+
+
+def T(dtype, sb, sh, ss, data=FAKE):
+    return attn_tensor(data, dtype, sb, sh, ss)
+
+
+def decode(so, q=None, k=None, v=None, ks=None, vs=None, B=1, Hq=8, Hkv=2, d=128, L=1024, S=4, out=None,
+           ws=FAKE, ws_bytes=1 << 30, scale=0.0):
+    q = q or T(BF16, Hq * d, d, d)
+    k = k or T(BF16, Hkv * L * d, L * d, d)
+    v = v or T(BF16, Hkv * L * d, L * d, d)
+    out = out or T(BF16, Hq * d, d, d)
+    return so.attn_decode(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ks, vs, None, B, Hq, Hkv, d, L,
+                          scale, 0, S, ctypes.byref(out), None, ws, ws_bytes, None)
+
+
+def test_decode_argument_errors(so):
+    assert decode(so, q=T(BF16, 1024, 128, 128, data=0)) == INVALID
+    assert decode(so, Hq=6, Hkv=4) == INVALID
+    assert decode(so, B=0) == INVALID
+    assert decode(so, S=-1) == INVALID
+    assert decode(so, scale=float("nan")) == INVALID
+    assert decode(so, d=96) == UNSUPPORTED
+    assert decode(so, Hq=6, Hkv=2) == UNSUPPORTED  # 3 query heads per KV head
+    assert decode(so, k=T(FP8, 2 * 1024 * 128, 1024 * 128, 128), v=T(FP8, 2 * 1024 * 128, 1024 * 128, 128)) == INVALID
+    assert decode(so, ks=FAKE, vs=FAKE) == INVALID  # scales with bf16 k/v
+    assert decode(so, k=T(F32, 2 * 1024 * 128, 1024 * 128, 128)) == INVALID  # k and v dtypes differ
+    assert decode(so, q=T(BF16, 1024, 128, 128, data=FAKE + 2)) == INVALID  # misaligned
+    assert decode(so, k=T(BF16, 2 * 1024 * 129, 1024 * 129, 129)) == INVALID
+    assert decode(so, ws=None) == WORKSPACE
+    assert decode(so, ws_bytes=100) == WORKSPACE
+    assert decode(so, ws=FAKE + 4) == WORKSPACE
+    assert decode(so, out=T(F32, 1024, 128, 128)) == INVALID  # out dtype must equal q dtype
+
+
+def test_error_message_names_the_problem(so):
+    assert decode(so, ws_bytes=100) == WORKSPACE
+    msg = lib.load_library().attn_last_error().decode()
+    assert "workspace" in msg and "need" in msg
+
+
+def prefill(so, dtype=BF16, d=128, Lq=256, Lkv=256, causal=1, Hq=8, Hkv=2):
+    q = T(dtype, Hq * Lq * d, Lq * d, d)
+    k = T(dtype, Hkv * Lkv * d, Lkv * d, d)
+    o = T(dtype, Hq * Lq * d, Lq * d, d)
+    return so.attn_prefill(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 1, Hq, Hkv, d, Lq, Lkv, 0.0, causal,
+                           ctypes.byref(o), None, None)
+
+
+def test_prefill_argument_errors(so):
+    assert prefill(so, Lq=300, Lkv=200, causal=1) == INVALID
+    assert prefill(so, dtype=F32) == UNSUPPORTED
+    assert prefill(so, d=64) == UNSUPPORTED
+    assert prefill(so, Hq=6, Hkv=4) == INVALID
+    assert prefill(so, Lq=0) == INVALID
+
+
+def test_combine_argument_errors(so):
+    out = T(BF16, 0, 0, 128)
+    assert so.attn_combine_partials(None, FAKE, FAKE, 4, 2, 128, ctypes.byref(out), None, None) == INVALID
+    assert so.attn_combine_partials(FAKE, FAKE, FAKE, 0, 2, 128, ctypes.byref(out), None, None) == INVALID
+    bad = T(FP8, 0, 0, 128)
+    assert so.attn_combine_partials(FAKE, FAKE, FAKE, 4, 2, 128, ctypes.byref(bad), None, None) == UNSUPPORTED

@@ -1,0 +1,202 @@
+"""GPU parity of attn_decode (split-KV decode + level-2 combine) against the
+double-precision oracle, element by element, on seeded inputs: the five
+workloads' decode shapes at full size, small shapes spanning several tiles with
+ragged tails, edge lengths, every fp8 code, strided views, all split counts of a
+sweep, and bit-identical repeats for a fixed split plan."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+from _gpu import (assert_close, assert_lse_close, decode_on_gpu, errors, from_dev, needs_gpu, oracle_decode,
+                  to_dev)
+from datagen.workloads import make_inputs
+
+pytestmark = [pytest.mark.gpu, needs_gpu]
+
+
+def _check(inp, S, kind, causal=False, lse_tol=None, scale=None, what=""):
+    out, lse = decode_on_gpu(inp, num_splits=S, causal=causal, softmax_scale=scale or 0.0)
+    ref, ref_lse = oracle_decode(inp, causal=causal, scale=scale)
+    got = from_dev(out)[:, :, 0, :]
+    res = assert_close(got, ref, kind, what="%s S=%s" % (what, S))
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, lse_tol or (1e-5 if kind == "f32" else 2e-3))
+    print("%s S=%s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (what, S, *res), flush=True)
+    return out, lse
+
+
+# ------------------------------------------------------------ workload 1 (fp32)
+
+def test_workload1_single_head_fp32_four_splits():
+    _check(make_inputs(1), 4, "f32", what="wl1")
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5, 8, 16])
+def test_fp32_split_count_sweep(S):
+    _check(make_inputs(1), S, "f32", what="wl1-sweep")
+
+
+# ------------------------------------------------------------ MFMA path, small shapes
+
+@pytest.mark.parametrize("L,S", [(1000, 1), (1000, 3), (1000, 7), (77, 2), (17, 1), (5, 1), (4096, 16), (4096, 64)])
+def test_gqa_bf16_small(L, S):
+    inp = make_inputs(2, B=2, Hq=8, Hkv=2, L=L, seed=20 + L)
+    _check(inp, S, "bf16", what="gqa-bf16 L=%d" % L)
+
+
+def test_gqa_bf16_peaked_queries():
+    # Q scaled x8: a much sharper softmax, running max moves often
+    inp = make_inputs(2, B=1, Hq=8, Hkv=2, L=3000, q_mul=4.0, seed=31)
+    _check(inp, 5, "bf16", what="gqa-bf16 q*8")
+
+
+def test_gqa_bf16_needles():
+    # Keys planted along head 0's query make single keys dominate (needle case)
+    inp = make_inputs(2, B=1, Hq=8, Hkv=2, L=5000, seed=32)
+    q = datagen_bf16_to_f32(inp["q"])
+    k = inp["k"].copy()
+    rng = np.random.default_rng(5)
+    for g in range(2):
+        qd = q[0, 4 * g, 0]
+        needle = (6.0 * qd / np.linalg.norm(qd) * np.sqrt(128)).astype(np.float32)
+        for pos in rng.choice(5000, size=3, replace=False):
+            k[0, g, pos] = datagen.f32_to_bf16_bits(needle)
+    inp["k"] = k
+    ref, _ = oracle_decode(inp)
+    assert np.abs(ref).max() > 0.3  # the needles really dominate
+    _check(inp, 7, "bf16", what="gqa-bf16 needles")
+
+
+def datagen_bf16_to_f32(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_softmax_scale_override():
+    inp = make_inputs(2, B=1, Hq=4, Hkv=1, L=700, seed=33)
+    _check(inp, 3, "bf16", scale=0.02, what="scale=0.02")
+
+
+# ------------------------------------------------------------ ragged batches
+
+def test_ragged_edge_lengths():
+    lens = np.array([0, 1, 15, 16, 17, 63, 64, 65, 300, 129], np.int32)
+    inp = make_inputs(3, B=10, Hq=8, Hkv=2, L=300, seed=34)
+    inp["kv_lens"] = lens
+    out, lse = _check(inp, 5, "bf16", causal=True, what="ragged edges")
+    got = from_dev(out)
+    assert np.all(got[0] == 0.0) and np.all(np.isneginf(lse.cpu().numpy()[0]))
+
+
+def test_ragged_lengths_beyond_capacity_are_clamped():
+    inp = make_inputs(3, B=3, Hq=4, Hkv=1, L=256, seed=35)
+    inp["kv_lens"] = np.array([-5, 1000, 100], np.int32)
+    ref_inp = dict(inp, kv_lens=np.array([0, 256, 100], np.int32))
+    out, lse = decode_on_gpu(inp, num_splits=2, causal=True)
+    ref, ref_lse = oracle_decode(ref_inp, causal=True)
+    assert_close(from_dev(out)[:, :, 0], ref, "bf16")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, 2e-3)
+
+
+def test_workload3_ragged_batch_full_size():
+    inp = make_inputs(3)
+    print("lengths", inp["kv_lens"].tolist(), flush=True)
+    _check(inp, 0, "bf16", causal=True, what="wl3")
+
+
+# ------------------------------------------------------------ workload 2, full size
+
+@pytest.mark.parametrize("S", [64, 128, 256])
+def test_workload2_full_size(S):
+    _check(make_inputs(2), S, "bf16", what="wl2")
+
+
+def test_workload2_auto_splits_and_determinism():
+    inp = make_inputs(2)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    outs = [decode_on_gpu(inp, num_splits=128, dev=dev) for _ in range(3)]
+    b0 = outs[0][0].view(torch.int16).cpu().numpy()
+    l0 = outs[0][1].cpu().numpy()
+    for o, l in outs[1:]:
+        assert np.array_equal(o.view(torch.int16).cpu().numpy(), b0)
+        assert np.array_equal(l.cpu().numpy().view(np.uint32), l0.view(np.uint32))
+    out, _ = decode_on_gpu(inp, num_splits=0, dev=dev)
+    ref, _ = oracle_decode(inp)
+    assert_close(from_dev(out)[:, :, 0], ref, "bf16", what="wl2 auto")
+
+
+# ------------------------------------------------------------ fp8 KV
+
+@pytest.mark.parametrize("S", [1, 3, 16])
+def test_fp8_small(S):
+    inp = make_inputs(5, B=2, Hq=8, Hkv=2, L=2000, seed=40)
+    _check(inp, S, "e4m3", what="fp8")
+
+
+def test_fp8_every_code():
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    B, Hkv, L, d = 1, 2, 256, 128
+    idx = np.arange(B * Hkv * L * d).reshape(B, Hkv, L, d)
+    inp = make_inputs(5, B=B, Hq=8, Hkv=Hkv, L=L, seed=41)
+    inp["k"] = finite[idx % finite.size]
+    inp["v"] = finite[(idx * 7 + 3) % finite.size]
+    inp["k_scale"] = np.array([0.003, 0.0011], np.float32)
+    inp["v_scale"] = np.array([0.7, 1.9], np.float32)
+    _check(inp, 2, "e4m3", lse_tol=5e-3, what="fp8 all codes")
+
+
+def test_workload5_fp8_1m_full_size():
+    inp = make_inputs(5)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    out1, lse1 = decode_on_gpu(inp, num_splits=1024, dev=dev)
+    out2, lse2 = decode_on_gpu(inp, num_splits=1024, dev=dev)
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse1.view(torch.int32), lse2.view(torch.int32))
+    ref, ref_lse = oracle_decode(inp)
+    res = assert_close(from_dev(out1)[:, :, 0], ref, "e4m3", what="wl5")
+    assert_lse_close(lse1.cpu().numpy().astype(np.float64), ref_lse, 2e-3)
+    print("wl5 max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % res, flush=True)
+    del dev
+
+
+# ------------------------------------------------------------ vector-ALU path
+
+@pytest.mark.parametrize("G,d,fmt", [(1, 64, "bf16"), (2, 128, "bf16"), (8, 128, "bf16"), (4, 64, "bf16"),
+                                     (1, 128, "f32"), (8, 64, "f32"), (2, 128, "e4m3"), (4, 64, "e4m3")])
+def test_valu_paths(G, d, fmt):
+    wl = {"bf16": 2, "f32": 1, "e4m3": 5}[fmt]
+    inp = make_inputs(wl, B=2, Hq=2 * G, Hkv=2, d=d, L=1111, seed=50 + G + d)
+    kind = "f32" if fmt == "f32" else "bf16"
+    _check(inp, 4, kind, what="valu G=%d d=%d %s" % (G, d, fmt))
+
+
+# ------------------------------------------------------------ strided views
+
+def test_strided_bshd_cache_and_padded_q():
+    B, Hq, Hkv, L, d = 2, 8, 2, 900, 128
+    inp = make_inputs(2, B=B, Hq=Hq, Hkv=Hkv, L=L, seed=60)
+    # K/V stored as [B, L, Hkv, d] (sequence-major) and viewed as [B, Hkv, L, d]
+    k_bshd = to_dev(np.ascontiguousarray(inp["k"].transpose(0, 2, 1, 3)))
+    v_bshd = to_dev(np.ascontiguousarray(inp["v"].transpose(0, 2, 1, 3)))
+    # Q inside a larger buffer: [B, Hq, 1, 2d], first half used
+    qbig = np.zeros((B, Hq, 1, 2 * d), np.uint16)
+    qbig[..., :d] = inp["q"]
+    qdev = to_dev(qbig)[..., :d]
+    dev = dict(q=qdev, k=k_bshd.permute(0, 2, 1, 3), v=v_bshd.permute(0, 2, 1, 3))
+    out, lse = decode_on_gpu(inp, num_splits=3, dev=dev)
+    ref, ref_lse = oracle_decode(inp)
+    assert_close(from_dev(out)[:, :, 0], ref, "bf16", what="strided")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, 2e-3)
+
+
+# ------------------------------------------------------------ split sweep agreement
+
+def test_split_counts_agree_with_each_other():
+    inp = make_inputs(2, B=1, Hq=8, Hkv=2, L=8192, seed=70)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    ref, _ = oracle_decode(inp)
+    worst = 0.0
+    for S in (1, 2, 3, 4, 7, 16, 33, 64, 128):
+        out, _ = decode_on_gpu(inp, num_splits=S, dev=dev)
+        mx, _, _ = assert_close(from_dev(out)[:, :, 0], ref, "bf16", what="S=%d" % S)
+        worst = max(worst, mx)
+    print("worst max_abs over splits %.3g" % worst, flush=True)
