@@ -92,17 +92,27 @@ ATTN_API const char* attn_last_error(void);
 
 /*
  * Split count that attn_decode uses when num_splits == 0: a pure function of
- * the shapes, the KV storage type and the compute-unit count of the current
- * device. Returns >= 1, or 0 on a bad argument or when the device cannot be
- * queried.
+ * the shapes, the KV storage type, whether per-sequence lengths are given
+ * (ragged != 0) and the compute-unit count of the current device. Returns
+ * >= 1, or 0 on a bad argument or when the device cannot be queried.
  */
-ATTN_API int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype);
+ATTN_API int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype, int ragged);
 
 /*
  * Bytes of device workspace attn_decode needs for `num_splits` splits (>= 1):
- * fp32 partials o [B*Hq, S, d], m [B*Hq, S], l [B*Hq, S]. 0 on a bad argument.
+ * a fixed 4 MiB block of merge counters followed by the fp32 partials
+ * o [B*Hq, S, d], m [B*Hq, S], l [B*Hq, S]. 0 on a bad argument.
  */
 ATTN_API size_t attn_decode_workspace_size(int B, int Hq, int d, int num_splits);
+
+/*
+ * Prepares a decode workspace for its first use: zeroes its counter block
+ * (asynchronously on `stream`). A workspace must be prepared once, after it
+ * is allocated; every attn_decode call leaves the counters zero again, so
+ * calls may reuse it with any shapes. Calls that share one workspace must be
+ * ordered (the same stream, or synchronised): overlapping calls race.
+ */
+ATTN_API attn_status attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Split plan of attn_decode / attn_decode_partials for a capacity of L_cap keys
@@ -125,13 +135,17 @@ ATTN_API int attn_decode_plan(int L_cap, int num_splits, int* chunk);
  * softmax_scale  <= 0 selects 1/sqrt(d)
  * causal   accepted for either value; with one query aligned bottom-right the
  *          query sees every valid key, so it does not change the result
- * num_splits  0 = attn_decode_auto_splits(); otherwise >= 1. The sequence is
+ * num_splits  0 = attn_decode_auto_splits(..., kv_lens != NULL); otherwise
+ *          >= 1. The sequence is
  *          cut into chunks of roundup(ceil(L_cap/num_splits), 64) keys; a
  *          sequence of L_b keys uses ceil(L_b/chunk) of them.
  * out      [B, Hq, 1, d] same dtype as q (bf16 output is rounded to nearest even)
  * lse      device float [B*Hq] or NULL
  * workspace  device memory of at least attn_decode_workspace_size(B, Hq, d, S)
- *          bytes for the split count S in use, 16-byte aligned
+ *          bytes for the split count S in use, 16-byte aligned, prepared once
+ *          by attn_decode_workspace_init. On the MFMA path the last workgroup
+ *          of each (sequence, KV head) merges the partials (one kernel); the
+ *          vector-ALU path runs the merge as a second kernel.
  *
  * q, k and v need 16-byte aligned data and strides that are multiples of 16
  * bytes. Supported: d in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
@@ -151,7 +165,8 @@ ATTN_API attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, con
  * 1 and 3). Arguments as for attn_decode, except the outputs:
  *   o_part [B*Hq, S, d], m_part [B*Hq, S], l_part [B*Hq, S]: contiguous device
  *   fp32, row r = b*Hq + h, S = attn_decode_plan(L_cap, num_splits, NULL)
- *   (num_splits = 0 selects attn_decode_auto_splits()). Splits past the end of
+ *   (num_splits = 0 selects attn_decode_auto_splits()). No workspace and no
+ *   counters are involved. Splits past the end of
  *   a shorter sequence hold the identity (0, -inf, 0). *splits_used (host
  *   pointer, may be NULL) receives S.
  * attn_combine_partials(o_part, m_part, l_part, B*Hq, S, d, ...) on the result

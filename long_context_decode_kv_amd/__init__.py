@@ -14,8 +14,9 @@ import torch
 
 __all__ = [
     "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_FP8_E4M3", "library_path", "load_library",
-    "attn_status_string", "attn_decode_auto_splits", "attn_decode_workspace_size", "attn_decode_plan",
-    "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials",
+    "attn_status_string", "attn_decode_auto_splits", "attn_decode_workspace_size", "attn_decode_workspace_init",
+    "attn_decode_plan",
+    "attn_decode", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
 ]
 
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
@@ -52,10 +53,12 @@ def load_library():
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_last_error.argtypes = []
     lib.attn_last_error.restype = ctypes.c_char_p
-    lib.attn_decode_auto_splits.argtypes = [i32, i32, i32, i32]
+    lib.attn_decode_auto_splits.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_decode_auto_splits.restype = i32
     lib.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.attn_decode_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
+    lib.attn_decode_workspace_init.restype = i32
     lib.attn_decode.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, tp, vp, vp,
                                 ctypes.c_size_t, vp]
     lib.attn_decode.restype = i32
@@ -111,12 +114,26 @@ def attn_status_string(status):
     return load_library().attn_status_string(int(status)).decode()
 
 
-def attn_decode_auto_splits(B, Hkv, L_cap, kv_dtype=ATTN_BF16):
-    return load_library().attn_decode_auto_splits(B, Hkv, L_cap, kv_dtype)
+def attn_decode_auto_splits(B, Hkv, L_cap, kv_dtype=ATTN_BF16, ragged=False):
+    return load_library().attn_decode_auto_splits(B, Hkv, L_cap, kv_dtype, int(bool(ragged)))
 
 
 def attn_decode_workspace_size(B, Hq, d, num_splits):
     return load_library().attn_decode_workspace_size(B, Hq, d, num_splits)
+
+
+def attn_decode_workspace_init(workspace, stream=None):
+    """Zero the merge counters of a freshly allocated decode workspace."""
+    st = load_library().attn_decode_workspace_init(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                                   _stream(stream, workspace.device))
+    _check(st)
+    return workspace
+
+
+def attn_decode_workspace(B, Hq, d, num_splits, device="cuda"):
+    """Allocate and prepare a decode workspace for up to `num_splits` splits."""
+    need = load_library().attn_decode_workspace_size(B, Hq, d, num_splits)
+    return torch.zeros(need, dtype=torch.uint8, device=device)
 
 
 def attn_decode_plan(L_cap, num_splits):
@@ -138,12 +155,12 @@ def attn_decode(q, k, v, k_scale=None, v_scale=None, kv_lens=None, softmax_scale
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    S = num_splits if num_splits > 0 else lib.attn_decode_auto_splits(B, Hkv, L_cap, _dtype_code(k))
+    S = num_splits if num_splits > 0 else lib.attn_decode_auto_splits(B, Hkv, L_cap, _dtype_code(k),
+                                                                      int(kv_lens is not None))
     if S <= 0:
         raise AttnError(4, "could not plan splits")
-    need = lib.attn_decode_workspace_size(B, Hq, d, S)
     if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+        workspace = attn_decode_workspace(B, Hq, d, S, device=q.device)
     qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     st = lib.attn_decode(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), _ptr(k_scale), _ptr(v_scale),
                          _ptr(kv_lens), B, Hq, Hkv, d, L_cap, float(softmax_scale), int(bool(causal)), int(S),
@@ -161,7 +178,8 @@ def attn_decode_partials(q, k, v, k_scale=None, v_scale=None, kv_lens=None, soft
     Hkv, L_cap = k.shape[1], k.shape[2]
     if Lq != 1:
         raise ValueError("attn_decode_partials takes one query per sequence (q.shape[2] == 1)")
-    req = num_splits if num_splits > 0 else lib.attn_decode_auto_splits(B, Hkv, L_cap, _dtype_code(k))
+    req = num_splits if num_splits > 0 else lib.attn_decode_auto_splits(B, Hkv, L_cap, _dtype_code(k),
+                                                                        int(kv_lens is not None))
     S, _ = attn_decode_plan(L_cap, req)
     if S <= 0:
         raise AttnError(4, "could not plan splits")

@@ -94,15 +94,25 @@ const char* attn_status_string(attn_status status) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
-int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype) {
+int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype, int ragged) {
     if (B <= 0 || Hkv <= 0 || L_cap <= 0 || !elem_size(kv_dtype)) return 0;
     const int cus = device_cu_count();
     if (cus <= 0) return 0;
-    // About four resident workgroups per compute unit in total, but no split
-    // shorter than 256 keys.
-    const int64_t target_wgs = 4LL * cus;
-    int64_t S = ceil_div(target_wgs, (int64_t)B * Hkv);
-    const int64_t max_s = ceil_div(L_cap, 256);
+    int64_t S;
+    if (ragged) {
+        // Lengths are only known on the device: cut every sequence into chunks
+        // of about 1024 keys (2048 for fp8, the same bytes) so that short and
+        // long sequences balance across many workgroups.
+        const int64_t chunk = kv_dtype == ATTN_FP8_E4M3 ? 2048 : 1024;
+        S = ceil_div(L_cap, chunk);
+    } else {
+        // Equal chunks, all workgroups resident at once and the same number
+        // on every compute unit: 1 per CU for 16-bit caches, 4 for fp8 (a
+        // quarter of the bytes per load, more waves to keep the bytes in flight).
+        const int64_t per_cu = kv_dtype == ATTN_FP8_E4M3 ? 4 : 1;
+        S = (per_cu * cus) / ((int64_t)B * Hkv);
+    }
+    const int64_t max_s = ceil_div(L_cap, 256);  // no split shorter than 256 keys
     if (S > max_s) S = max_s;
     if (S < 1) S = 1;
     return (int)S;
@@ -110,7 +120,18 @@ int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype) {
 
 size_t attn_decode_workspace_size(int B, int Hq, int d, int num_splits) {
     if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 0) return 0;
-    return partial_bytes((int64_t)B * Hq, num_splits, d);
+    return attn::kCounterBytes + partial_bytes((int64_t)B * Hq, num_splits, d) +
+           partial_bytes((int64_t)B * Hq, attn::kMaxTicketBlocks, d);
+}
+
+attn_status attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = 0;
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
+    if (workspace_bytes < attn::kCounterBytes)
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need at least %zu", workspace_bytes, attn::kCounterBytes);
+    hipError_t e = hipMemsetAsync(workspace, 0, attn::kCounterBytes, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "workspace init: %s", hipGetErrorString(e));
+    return ATTN_OK;
 }
 
 int attn_decode_plan(int L_cap, int num_splits, int* chunk) {
@@ -126,10 +147,27 @@ namespace {
 
 // Validation and the first level (partials) shared by attn_decode and
 // attn_decode_partials. On success *pl holds the split plan used.
+struct FusedOut {
+    uint32_t* counters;
+    const attn_tensor* out;
+    float* lse;
+    float* blk_o;
+    float* blk_m;
+    float* blk_l;
+};
+
+int requested_splits(int B, int Hkv, int L_cap, const attn_tensor* k, const int32_t* kv_lens, int num_splits) {
+    if (num_splits > 0) return num_splits;
+    if (B <= 0 || Hkv <= 0 || L_cap <= 0 || !k) return 0;
+    return attn_decode_auto_splits(B, Hkv, L_cap, k->dtype, kv_lens != nullptr);
+}
+
 attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const float* k_scale,
                           const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int d, int L_cap,
                           float softmax_scale, int num_splits, const attn_tensor* out, float* o_part,
-                          float* m_part, float* l_part, size_t part_bytes, Plan* pl, hipStream_t stream) {
+                          float* m_part, float* l_part, size_t part_bytes, Plan* pl, hipStream_t stream,
+                          const FusedOut* fused, bool* used_fused) {
+    *used_fused = false;
     attn_status st;
     if ((st = check_tensor(q, "q", true)) || (st = check_tensor(k, "k", true)) || (st = check_tensor(v, "v", true)))
         return st;
@@ -154,11 +192,8 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     if (G != 1 && G != 2 && G != 4 && G != 8)
         return fail(ATTN_ERR_UNSUPPORTED, "Hq/Hkv = %d (supported: 1, 2, 4, 8)", G);
 
-    int requested = num_splits;
-    if (requested == 0) {
-        requested = attn_decode_auto_splits(B, Hkv, L_cap, k->dtype);
-        if (requested <= 0) return fail(ATTN_ERR_HIP, "could not query the device for the split plan");
-    }
+    const int requested = requested_splits(B, Hkv, L_cap, k, kv_lens, num_splits);
+    if (requested <= 0) return fail(ATTN_ERR_HIP, "could not query the device for the split plan");
     *pl = plan_splits(L_cap, requested);
     const int64_t rows = (int64_t)B * Hq;
     if (!o_part || !m_part || !l_part) return fail(ATTN_ERR_WORKSPACE, "workspace (partials) is null");
@@ -194,9 +229,40 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     p.o_part = o_part;
     p.m_part = m_part;
     p.l_part = l_part;
+    p.counters = nullptr;
+    p.ticket_block = 1;
+    p.blk_o = p.blk_m = p.blk_l = nullptr;
+    p.out = nullptr;
+    p.out_sb = p.out_sh = 0;
+    p.lse = nullptr;
 
     hipError_t e;
     const bool mfma = q->dtype == ATTN_BF16 && G == 4 && d == 128;
+    // Fuse the merge into the decode kernel when every workgroup is resident at
+    // once (at most two per compute unit): each workgroup's publish-and-ticket
+    // tail is then paid once instead of once per round of workgroups.
+    const int cus = device_cu_count();
+    const int64_t wgs = (int64_t)B * Hkv * pl->S;
+    if (mfma && fused && (int64_t)B * Hkv <= attn::kMaxCounterGroups && pl->S <= attn::kMaxFusedSplits &&
+        cus > 0 && wgs <= 2LL * cus) {
+        p.counters = fused->counters;
+        // one level up to 32 splits, else blocks of about sqrt(S) splits
+        int tb = pl->S;
+        if (tb > 32) {
+            tb = 1;
+            while (tb * tb < pl->S) ++tb;
+            while ((pl->S + tb - 1) / tb > attn::kMaxTicketBlocks) ++tb;
+        }
+        p.ticket_block = tb;
+        p.blk_o = fused->blk_o;
+        p.blk_m = fused->blk_m;
+        p.blk_l = fused->blk_l;
+        p.out = fused->out->data;
+        p.out_sb = fused->out->stride_b;
+        p.out_sh = fused->out->stride_h;
+        p.lse = fused->lse;
+        *used_fused = true;
+    }
     if (mfma) e = attn::launch_decode_mfma(p, fp8 ? attn::DT_FP8 : attn::DT_BF16, stream);
     else e = attn::launch_decode_valu(p, q->dtype, k->dtype, G, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
@@ -215,19 +281,33 @@ attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_t
     g_last_error[0] = 0;
     if (!out) return fail(ATTN_ERR_INVALID_ARG, "out: null tensor");
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
-    // Partials layout inside the workspace depends on the plan; compute it first.
-    Plan pl{0, 0};
-    int requested = num_splits;
-    if (requested == 0 && B > 0 && Hkv > 0 && L_cap > 0 && k) requested = attn_decode_auto_splits(B, Hkv, L_cap, k->dtype);
+    if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < attn::kCounterBytes)
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need more than %zu", workspace_bytes,
+                    attn::kCounterBytes);
+    // Layout: [merge counters | o_part | m_part | l_part]; the partial arrays
+    // depend on the split plan, which is a pure function of the arguments.
+    const int requested = requested_splits(B, Hkv, L_cap, k, kv_lens, num_splits);
+    const int S_layout = (requested > 0 && L_cap > 0) ? plan_splits(L_cap, requested).S : 1;
     const int64_t rows = (int64_t)(B > 0 ? B : 0) * (Hq > 0 ? Hq : 0);
-    int S_guess = (requested > 0 && L_cap > 0) ? plan_splits(L_cap, requested).S : 1;
-    float* o_part = static_cast<float*>(workspace);
-    float* m_part = o_part + rows * S_guess * (d > 0 ? d : 0);
-    float* l_part = m_part + rows * S_guess;
+    uint32_t* counters = static_cast<uint32_t*>(workspace);
+    float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn::kCounterBytes);
+    float* m_part = o_part + rows * S_layout * (d > 0 ? d : 0);
+    float* l_part = m_part + rows * S_layout;
+    float* blk_o = l_part + rows * S_layout;
+    float* blk_m = blk_o + rows * attn::kMaxTicketBlocks * (d > 0 ? d : 0);
+    float* blk_l = blk_m + rows * attn::kMaxTicketBlocks;
     hipStream_t hs = static_cast<hipStream_t>(stream);
+    Plan pl{0, 0};
+    const FusedOut fo{counters, out, lse, blk_o, blk_m, blk_l};
+    bool fused = false;
+    const size_t fixed = attn::kCounterBytes + partial_bytes(rows, attn::kMaxTicketBlocks, d > 0 ? d : 0);
+    if (workspace_bytes < fixed)
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need more than %zu", workspace_bytes, fixed);
     attn_status st = decode_level1(q, k, v, k_scale, v_scale, kv_lens, B, Hq, Hkv, d, L_cap, softmax_scale,
-                                   num_splits, out, o_part, m_part, l_part, workspace_bytes, &pl, hs);
-    if (st != ATTN_OK) return st;
+                                   num_splits, out, o_part, m_part, l_part, workspace_bytes - fixed, &pl, hs, &fo,
+                                   &fused);
+    if (st != ATTN_OK || fused) return st;
 
     attn::CombineParams cp;
     cp.o_part = o_part;
@@ -257,9 +337,10 @@ attn_status attn_decode_partials(const attn_tensor* q, const attn_tensor* k, con
     (void)causal;
     g_last_error[0] = 0;
     Plan pl{0, 0};
+    bool fused = false;
     attn_status st = decode_level1(q, k, v, k_scale, v_scale, kv_lens, B, Hq, Hkv, d, L_cap, softmax_scale,
                                    num_splits, nullptr, o_part, m_part, l_part, (size_t)-1, &pl,
-                                   static_cast<hipStream_t>(stream));
+                                   static_cast<hipStream_t>(stream), nullptr, &fused);
     if (st == ATTN_OK && splits_used) *splits_used = pl.S;
     return st;
 }

@@ -27,9 +27,10 @@
 //  * P.V on the vector ALUs: lane l holds V for the same four keys at dims
 //    8*(l&15) .. +7, fetches the four heads' weights of each key from its quad
 //    with DPP broadcasts, and accumulates 4 heads x 8 dims in fp32.
-// K is read 16 rows x 64 bytes per load (the MFMA operand layout), V four full
-// 256-byte rows per load; every valid key is read from HBM exactly once, and
-// the next tile's loads are issued before the current tile is computed.
+// K and V are both read as whole rows per load instruction with non-temporal
+// loads (K then goes through a small wave-private LDS stage into the MFMA
+// operand layout); every valid key is read from HBM exactly once, and the next
+// tile's loads are issued before the current tile is computed.
 #include "internal.h"
 
 namespace attn {
@@ -46,6 +47,7 @@ constexpr int kWaves = 4;
 constexpr int kTile = 16;          // keys per wave per step
 constexpr float kHeadroom = 8.0f;  // base-2 units a score may exceed the running max by
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 // Value of lane (l & ~3) + H, for every lane l (DPP quad_perm broadcast).
@@ -64,36 +66,67 @@ template <bool FP8>
 struct Tile;
 template <>
 struct Tile<false> {
-    u32x4 k[4];  // MFMA step i: 8 bf16 at dims 32i + 8*(lane>>4) of key row (lane & 15)
+    u32x4 k[4];  // key row 4i + (lane>>4), bytes 16*(lane & 15) .. +15 (coalesced rows)
     u32x4 v[4];  // key 4*(lane>>4) + u: 8 bf16 at dims 8*(lane & 15)
 };
 template <>
 struct Tile<true> {
-    u32x4 k[2];  // half h: 16 fp8 at dims 64h + 16*(lane>>4) of key row (lane & 15)
+    u32x4 k[2];  // key row 8i + (lane>>3), bytes 16*(lane & 7) .. +15 (coalesced rows)
     u32x2 v[4];  // key 4*(lane>>4) + u: 8 fp8 at dims 8*(lane & 15)
 };
+
+// Streaming loads: every byte of the cache is read once, so they are marked
+// non-temporal; each load instruction of a wave covers whole 128/256-byte rows.
+template <typename T>
+__device__ __forceinline__ T ld_stream(const char* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
+}
 
 // Loads one 16-key tile; key indices past `tlast` are clamped to it, so every
 // address stays inside the cache and the clamped keys are masked later.
 template <bool FP8>
 __device__ __forceinline__ void load_tile(Tile<FP8>& t, const char* kbase, const char* vbase, int64_t kss,
                                           int64_t vss, int tok0, int tlast, int lane) {
-    const int rk = min(tok0 + (lane & 15), tlast);
-    const char* krow = kbase + (int64_t)rk * kss;
     if constexpr (!FP8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            t.k[i] = *reinterpret_cast<const u32x4*>(krow + 2 * (32 * i + 8 * (lane >> 4)));
+        for (int i = 0; i < 4; ++i) {
+            const int rk = min(tok0 + 4 * i + (lane >> 4), tlast);
+            t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 15));
+        }
     } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) t.k[h] = *reinterpret_cast<const u32x4*>(krow + 64 * h + 16 * (lane >> 4));
+        for (int i = 0; i < 2; ++i) {
+            const int rk = min(tok0 + 8 * i + (lane >> 3), tlast);
+            t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 7));
+        }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
         const char* vrow = vbase + (int64_t)rv * vss;
-        if constexpr (!FP8) t.v[u] = *reinterpret_cast<const u32x4*>(vrow + 2 * 8 * (lane & 15));
-        else t.v[u] = *reinterpret_cast<const u32x2*>(vrow + 8 * (lane & 15));
+        if constexpr (!FP8) t.v[u] = ld_stream<u32x4>(vrow + 2 * 8 * (lane & 15));
+        else t.v[u] = ld_stream<u32x2>(vrow + 8 * (lane & 15));
+    }
+}
+
+// The K tile passes through a wave-private LDS stage to change from row-major
+// lanes to the MFMA operand layout (lane = key row, 16 bytes of dims). 16-byte
+// chunks are XOR-swizzled by row so both the row writes and the column reads
+// touch every bank once per 16 lanes.
+template <bool FP8>
+__device__ __forceinline__ int kstage_index(int row, int chunk) {
+    if constexpr (!FP8) return row * 16 + (chunk ^ (row & 15));
+    else return row * 8 + (chunk ^ ((row >> 1) & 7));
+}
+
+template <bool FP8>
+__device__ __forceinline__ void stage_k(const Tile<FP8>& t, u32x4* ks, int lane) {
+    if constexpr (!FP8) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ks[kstage_index<false>(4 * i + (lane >> 4), lane & 15)] = t.k[i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ks[kstage_index<true>(8 * i + (lane >> 3), lane & 7)] = t.k[i];
     }
 }
 
@@ -128,20 +161,25 @@ __device__ __forceinline__ void v_to_f32(const Tile<FP8>& t, int u, float (&vf)[
 }
 
 template <bool FP8>
-__device__ __forceinline__ void compute_tile(const Tile<FP8>& t, const bf16x8 (&qop)[4], float scale2, int tok0,
-                                             int tend, int lane, float& m_run, float& l_run, float (&o)[4][8]) {
+__device__ __forceinline__ void compute_tile(const Tile<FP8>& t, u32x4* ks, const bf16x8 (&qop)[4], float scale2,
+                                             int tok0, int tend, int lane, float& m_run, float& l_run,
+                                             float (&o)[4][8]) {
+    stage_k<FP8>(t, ks, lane);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const int row = lane & 15;
     if constexpr (!FP8) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t.k[i]), qop[i], acc, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 a = ks[kstage_index<false>(row, 4 * i + (lane >> 4))];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qop[i], acc, 0, 0, 0);
+        }
     } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(t.k[h][0], t.k[h][1]), qop[2 * h], acc, 0,
-                                                          0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(t.k[h][2], t.k[h][3]), qop[2 * h + 1], acc,
-                                                          0, 0, 0);
+            const u32x4 a = ks[kstage_index<true>(row, 4 * h + (lane >> 4))];
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[0], a[1]), qop[2 * h], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[2], a[3]), qop[2 * h + 1], acc, 0, 0,
+                                                          0);
         }
     }
     const int kb = tok0 + 4 * (lane >> 4);
@@ -180,7 +218,160 @@ __device__ __forceinline__ void compute_tile(const Tile<FP8>& t, const bf16x8 (&
     }
 }
 
-template <bool FP8>
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return 0x7fc0;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Agent-scope relaxed atomics: on this GPU they are performed at the
+// device-wide coherence point (past the per-XCD L2), so values written by a
+// workgroup on one XCD are read back fresh by a workgroup on another.
+__device__ __forceinline__ void st_agent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent2(float* p, f32x2 v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_agent(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 ld_agent2(const float* p) {
+    return __builtin_bit_cast(
+        f32x2, __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT));
+}
+
+// Merge n <= kMergeMax partials of the four heads of one KV group, in
+// the fixed order j = 0, 1, ...: partial j of head h has o at
+// o + (h*rs + j)*128, m at m[h*rs + j], l at l[h*rs + j] (natural-log units).
+// Leaves the unnormalised sums in part[h][c] and (max, sum) in red[h].
+constexpr int kMergeMax = 32;  // partials one merge4 call takes (two load batches)
+struct MergeLds {
+    float w[4][kMergeMax];
+    float l[4][kMergeMax];
+    float red[4][2];
+    float part[2][4][128];
+};
+
+__device__ __forceinline__ void merge4(const float* o, const float* m, const float* l, int64_t rs, int n, int tid,
+                                       MergeLds& sm) {
+    const int lane = tid & 63, h = tid >> 6;
+    if (lane < n) {
+        sm.w[h][lane] = ld_agent(m + h * rs + lane);
+        sm.l[h][lane] = ld_agent(l + h * rs + lane);
+    }  // n <= kMergeMax < 64
+    __syncthreads();
+    if (lane == 0) {
+        float M = kNegInf;
+        for (int j = 0; j < n; ++j) M = fmaxf(M, sm.w[h][j]);
+        float L = 0.f;
+        for (int j = 0; j < n; ++j) {
+            const float mj = sm.w[h][j];
+            const float wgt = (mj == kNegInf) ? 0.f : fast_exp2((mj - M) * kLog2e);
+            sm.w[h][j] = wgt;
+            L = fmaf(wgt, sm.l[h][j], L);
+        }
+        sm.red[h][0] = M;
+        sm.red[h][1] = L;
+    }
+    __syncthreads();
+    // thread = (half, head, 4 columns); half k takes j = k, k+2, ...; 16 loads in
+    // flight per batch of 16 partials
+    const int half = tid >> 7, idx = tid & 127, hh = idx >> 5, c4 = (idx & 31) * 4;
+    const float* ob = o + hh * rs * 128 + c4;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < n; j0 += 16) {
+        f32x2 v[8][2];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = min(j0 + half + 2 * u, n - 1);
+            v[u][0] = ld_agent2(ob + (int64_t)j * 128);
+            v[u][1] = ld_agent2(ob + (int64_t)j * 128 + 2);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + half + 2 * u;
+            const float wv = (j < n) ? sm.w[hh][j] : 0.f;
+            acc[0] = fmaf(wv, v[u][0][0], acc[0]);
+            acc[1] = fmaf(wv, v[u][0][1], acc[1]);
+            acc[2] = fmaf(wv, v[u][1][0], acc[2]);
+            acc[3] = fmaf(wv, v[u][1][1], acc[3]);
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.part[half][hh][c4 + e] = acc[e];
+    __syncthreads();
+}
+
+// Level 2, fused: a tree over the splits of each (b, g) group. Every
+// workgroup publishes its partial (agent-scope stores, waited for), then takes
+// a ticket in its block of `ticket_block` splits; the last of a block merges
+// the block into a block partial and, if there are several blocks, takes a
+// ticket on the group; the last block merges the block partials into O and
+// lse. Counters are reset by their last user. The tree shape is a function of
+// n and the plan only, so results are deterministic.
+__device__ __forceinline__ void merge_group_if_last(const DecodeParams& p, int b, int g, int L_b, int tid) {
+    __shared__ int role;  // 0: done, 1: merged its block, not last; 2: final merger
+    __shared__ MergeLds sm;
+    const int n = (L_b + p.chunk - 1) / p.chunk;  // splits this sequence uses
+    const int s = blockIdx.x, k = p.ticket_block;
+    const int nb = (n + k - 1) / k, bi = s / k;
+    const int in_block = min(k, n - bi * k);
+    uint32_t* line = p.counters + (int64_t)(b * p.Hkv + g) * (1 + kMaxTicketBlocks) * kCounterStride;
+    const int64_t row0 = (int64_t)b * p.Hq + g * 4;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t* blk = line + (1 + bi) * kCounterStride;
+        const uint32_t o1 = __hip_atomic_fetch_add(blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        role = (o1 == (uint32_t)(in_block - 1)) ? 1 : 0;
+        if (role) __hip_atomic_store(blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!role) return;
+    const int lane = tid & 63, h = tid >> 6;
+    // level 2a: this block's splits
+    merge4(p.o_part + (row0 * p.S + bi * k) * 128, p.m_part + row0 * p.S + bi * k, p.l_part + row0 * p.S + bi * k,
+           p.S, in_block, tid, sm);
+    if (nb > 1) {
+        // publish the block partial, then take a ticket on the group
+        float* bo = p.blk_o + (row0 * kMaxTicketBlocks + bi) * 128;
+        const int c = lane * 2;
+        f32x2 v;
+        v[0] = sm.part[0][h][c] + sm.part[1][h][c];
+        v[1] = sm.part[0][h][c + 1] + sm.part[1][h][c + 1];
+        st_agent2(bo + (int64_t)h * kMaxTicketBlocks * 128 + c, v);
+        if (lane == 0) {
+            st_agent(p.blk_m + (row0 + h) * kMaxTicketBlocks + bi, sm.red[h][0]);
+            st_agent(p.blk_l + (row0 + h) * kMaxTicketBlocks + bi, sm.red[h][1]);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t o2 = __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            role = (o2 == (uint32_t)(nb - 1)) ? 2 : 0;
+            if (role) __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!role) return;
+        // level 2b: the block partials
+        merge4(p.blk_o + row0 * kMaxTicketBlocks * 128, p.blk_m + row0 * kMaxTicketBlocks,
+               p.blk_l + row0 * kMaxTicketBlocks, kMaxTicketBlocks, nb, tid, sm);
+    }
+    const int c = lane * 2;
+    const float Mh = sm.red[h][0], Lh = sm.red[h][1];
+    const bool empty = !(Lh > 0.f);
+    const float inv = empty ? 0.f : 1.0f / Lh;
+    uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)(g * 4 + h) * p.out_sh;
+    orow[c] = f32_to_bf16_rne((sm.part[0][h][c] + sm.part[1][h][c]) * inv);
+    orow[c + 1] = f32_to_bf16_rne((sm.part[0][h][c + 1] + sm.part[1][h][c + 1]) * inv);
+    if (p.lse && lane == 0) p.lse[row0 + h] = empty ? kNegInf : Mh + logf(Lh);
+}
+
+template <bool FP8, bool FUSED>
 __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
     const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
@@ -196,6 +387,14 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
             if (i % 128 == 0) {
                 p.m_part[row * p.S + s] = kNegInf;
                 p.l_part[row * p.S + s] = 0.f;
+            }
+        }
+        if (FUSED && L_b == 0 && s == 0) {
+            // an empty sequence: O = 0, lse = -inf (no workgroup of it merges)
+            for (int i = tid; i < 4 * 128; i += 256) {
+                uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)(g * 4 + i / 128) * p.out_sh;
+                orow[i % 128] = 0;
+                if (p.lse && i % 128 == 0) p.lse[(int64_t)b * p.Hq + g * 4 + i / 128] = kNegInf;
             }
         }
         return;
@@ -230,16 +429,25 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
 
+    // Two tile buffers used in turn: the next tile is in flight while the
+    // current one is computed.
+    __shared__ u32x4 kstage[kWaves][256];
+    u32x4* ks = kstage[w];
     int k = w;
     if (k < ntiles) {
-        Tile<FP8> cur;
-        load_tile<FP8>(cur, kbase, vbase, kss, vss, t_begin + kTile * k, t_end - 1, lane);
-        for (; k < ntiles; k += kWaves) {
-            Tile<FP8> nxt;
-            const bool more = k + kWaves < ntiles;
-            if (more) load_tile<FP8>(nxt, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-            compute_tile<FP8>(cur, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
-            if (more) cur = nxt;
+        Tile<FP8> ta, tb;
+        load_tile<FP8>(ta, kbase, vbase, kss, vss, t_begin + kTile * k, t_end - 1, lane);
+        while (true) {
+            const bool more_b = k + kWaves < ntiles;
+            if (more_b) load_tile<FP8>(tb, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+            compute_tile<FP8>(ta, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+            if (!more_b) break;
+            k += kWaves;
+            const bool more_a = k + kWaves < ntiles;
+            if (more_a) load_tile<FP8>(ta, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+            compute_tile<FP8>(tb, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+            if (!more_a) break;
+            k += kWaves;
         }
     }
 
@@ -299,10 +507,19 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
         out[cc] = v * vsc;
     }
     const int64_t row = (int64_t)b * p.Hq + g * 4 + h;
-    *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s) * 128 + c) = out;
-    if ((tid & 63) == 0) {
-        p.m_part[row * p.S + s] = Mx * kLn2;
-        p.l_part[row * p.S + s] = L;
+    if constexpr (FUSED) {
+        st_agent2(p.o_part + (row * p.S + s) * 128 + c, out);
+        if ((tid & 63) == 0) {
+            st_agent(p.m_part + row * p.S + s, Mx * kLn2);
+            st_agent(p.l_part + row * p.S + s, L);
+        }
+        merge_group_if_last(p, b, g, L_b, tid);
+    } else {
+        *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s) * 128 + c) = out;
+        if ((tid & 63) == 0) {
+            p.m_part[row * p.S + s] = Mx * kLn2;
+            p.l_part[row * p.S + s] = L;
+        }
     }
 }
 
@@ -310,8 +527,14 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
     dim3 grid(p.S, p.Hkv, p.B);
-    if (kv_dtype == DT_FP8) hipLaunchKernelGGL(decode_gqa4_d128<true>, grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL(decode_gqa4_d128<false>, grid, dim3(256), 0, stream, p);
+    const bool fused = p.counters != nullptr;
+    if (kv_dtype == DT_FP8) {
+        if (fused) hipLaunchKernelGGL((decode_gqa4_d128<true, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_gqa4_d128<true, false>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (fused) hipLaunchKernelGGL((decode_gqa4_d128<false, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_gqa4_d128<false, false>), grid, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -29,7 +29,30 @@ struct DecodeParams {
     float* o_part;     // [B*Hq, S, d]
     float* m_part;     // [B*Hq, S], natural-log units
     float* l_part;     // [B*Hq, S]
+    // Fused level 2 (decode_mfma only): when `counters` is set, the last
+    // workgroup of each (b, g) to finish merges that group's partials and
+    // writes the normalised output itself.
+    uint32_t* counters;  // ticket lines (see kCounterBytes), zero on entry, left zero on exit
+    int ticket_block;    // splits per first-level ticket block
+    float* blk_o;        // block partials [B*Hq, kMaxTicketBlocks, d]
+    float* blk_m;        // [B*Hq, kMaxTicketBlocks]
+    float* blk_l;        // [B*Hq, kMaxTicketBlocks]
+    void* out;           // [B, Hq, 1, d] bf16
+    int64_t out_sb, out_sh;
+    float* lse;          // [B*Hq] or nullptr
 };
+
+// Bytes at the start of a decode workspace reserved for the fused-merge
+// tickets. Each (batch, KV head) group owns 1 + kMaxTicketBlocks counters:
+// one per block of splits and one for the group; each counter sits alone in a
+// 256-byte line (tickets on one address are served one after another, so the
+// two levels keep that queue short).
+constexpr size_t kCounterBytes = 4 << 20;
+constexpr int kCounterStride = 64;  // uint32 per counter line
+constexpr int kMaxTicketBlocks = 16;
+constexpr int kMaxCounterGroups = (int)(kCounterBytes / (4 * kCounterStride * (1 + kMaxTicketBlocks)));
+// Largest split count whose merge is fused into the decode kernel.
+constexpr int kMaxFusedSplits = 256;
 
 // Level-2 merge: one output row per (b, h) from its partials.
 struct CombineParams {

@@ -32,8 +32,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
     assert set(names) == {"attn_status_string", "attn_last_error", "attn_decode_auto_splits",
-                          "attn_decode_workspace_size", "attn_decode_plan", "attn_decode", "attn_decode_partials",
-                          "attn_prefill", "attn_combine_partials"}
+                          "attn_decode_workspace_size", "attn_decode_workspace_init", "attn_decode_plan",
+                          "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials"}
     nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
     for n in names:
@@ -63,7 +63,8 @@ def test_split_plan(so):
 
 
 def test_workspace_size(so):
-    assert lib.attn_decode_workspace_size(1, 32, 128, 256) == 32 * 256 * 130 * 4
+    # a fixed 64 KiB block of merge counters, then the fp32 partials
+    assert lib.attn_decode_workspace_size(1, 32, 128, 256) == (4 << 20) + 32 * 256 * 130 * 4 + 32 * 16 * 130 * 4
     assert lib.attn_decode_workspace_size(16, 32, 128, 0) == 0
     assert lib.attn_decode_workspace_size(0, 32, 128, 4) == 0
 
@@ -100,12 +101,18 @@ def test_decode_argument_errors(so):
     assert decode(so, k=T(BF16, 2 * 1024 * 129, 1024 * 129, 129)) == INVALID
     assert decode(so, ws=None) == WORKSPACE
     assert decode(so, ws_bytes=100) == WORKSPACE
+    assert decode(so, ws_bytes=(4 << 20) + 8 * 16 * 130 * 4 + 100) == WORKSPACE
     assert decode(so, ws=FAKE + 4) == WORKSPACE
     assert decode(so, out=T(F32, 1024, 128, 128)) == INVALID  # out dtype must equal q dtype
 
 
+def test_workspace_init_errors(so):
+    assert so.attn_decode_workspace_init(None, 1 << 20, None) == WORKSPACE
+    assert so.attn_decode_workspace_init(FAKE, 1000, None) == WORKSPACE
+
+
 def test_error_message_names_the_problem(so):
-    assert decode(so, ws_bytes=100) == WORKSPACE
+    assert decode(so, ws_bytes=(4 << 20) + 8 * 16 * 130 * 4 + 100) == WORKSPACE
     msg = lib.load_library().attn_last_error().decode()
     assert "workspace" in msg and "need" in msg
 
