@@ -186,7 +186,8 @@ ATTN_API attn_status attn_decode_partials(const attn_tensor* q, const attn_tenso
  * 16-byte aligned data and strides.
  * lse: device float [B, Hq, Lq] (contiguous) or NULL.
  * causal with Lq > Lkv is rejected (queries with no visible key).
- * Supported: d == 128, Hq % Hkv == 0.
+ * Supported: d == 128, Hq % Hkv == 0, k and v row strides (stride_s) below
+ * 2^24 elements (32 MiB per key row); larger ones give ATTN_ERR_UNSUPPORTED.
  */
 ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B,
                                   int Hq, int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal,

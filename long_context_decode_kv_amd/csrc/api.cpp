@@ -392,6 +392,9 @@ attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_
     if (q->dtype != ATTN_BF16 || k->dtype != ATTN_BF16 || v->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
         return fail(ATTN_ERR_UNSUPPORTED, "prefill supports bf16 q/k/v/out");
     if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "prefill head dim %d (supported: 128)", d);
+    // K/V tiles are read through 32-bit buffer offsets covering 64 key rows
+    if (k->stride_s >= (1 << 24) || v->stride_s >= (1 << 24))
+        return fail(ATTN_ERR_UNSUPPORTED, "prefill k/v row stride must be below 2^24 elements");
     const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
     attn::PrefillParams p;
     p.q = q->data;

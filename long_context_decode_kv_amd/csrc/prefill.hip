@@ -10,9 +10,16 @@
 // one KV head (up to 4 of them) times consecutive 32-position blocks, so every
 // K/V tile staged in LDS serves all eight waves (and each KV byte is read from
 // L2 once per 256 query rows). Each wave keeps, per query row, a running max m
-// and sum l and an fp32 output accumulator, and walks 64-key tiles (double
-// buffered in LDS, loads two tiles ahead, one barrier per tile). Waves 0-3
-// stage V, waves 4-7 stage K.
+// and sum l and an fp32 output accumulator, and walks 64-key tiles.
+//
+// The eight waves form two groups (waves 0-3 and 4-7, one of each on every
+// SIMD) that run the same per-tile sequence -- scores (MFMA), softmax (vector
+// ALU, mostly exponentials), P.V (MFMA) -- half a tile apart, separated by
+// workgroup barriers, so that one wave of each SIMD feeds the matrix core
+// while the other computes exponentials (details at the loop). K and V tiles
+// pass through registers into a three-tile LDS ring: group 0 stages V^T,
+// group 1 stages K, each through buffer loads whose out-of-range rows read as
+// zero.
 //
 // Both products are computed transposed so that one query row lives in one
 // lane and the softmax needs no cross-lane reduction except one lane-pair exchange:
@@ -24,7 +31,7 @@
 // which makes P^T usable directly as the B operand of the second product and
 // lets V^T be read from LDS with one 16-byte load per operand.
 //
-// LDS layout: K tile [64 keys][128 dims] with rows padded to 272 bytes and
+// LDS layout (per slot): K tile [64 keys][128 dims] with rows padded to 272 bytes and
 // each key stored at the permuted row position it is read from, and V^T tile
 // [128 dims][64 keys] with rows padded to 144 bytes. Every MFMA-operand read is
 // then a per-lane base plus a constant offset, and every 8 lanes of a 16-byte
@@ -35,6 +42,8 @@
 // applied only on tiles that cross the diagonal; tiles past it are skipped.
 // Workgroups are issued heaviest (latest) query block first.
 #include "internal.h"
+
+#include <type_traits>
 
 namespace attn {
 namespace {
@@ -77,61 +86,37 @@ __device__ __forceinline__ int perm_row(int r) { return (r & ~12) | ((r & 4) << 
 // half hb, given the permuted row order.
 __device__ __forceinline__ int key_of(int j, int hb) { return j < 8 ? 8 * hb + j : 16 + 8 * hb + (j - 8); }
 
-// Per-thread share of one tile (512 threads): threads 0-255 load 4 keys x 8
-// dims of V (16 consecutive lanes read 16 different keys, so the transposed
-// 8-byte writes below hit 16 different bank pairs); threads 256-511 load four
-// 16-byte pieces of K (16 lanes per 256-byte row).
-struct Staged {
-    u32x4 x[4];
-};
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle): loads at
+// or past the resource's byte size return zero.
+constexpr int kRsrcWord3 = 0x00020000;
 
-__device__ __forceinline__ void load_tile(Staged& st, const char* kbase, const char* vbase, int64_t kss, int64_t vss,
-                                          int key0, int klast, int tid) {
-    if (tid < 256) {
-        const int u = tid & 15, c = tid >> 4;  // keys 4u.., dims 8c..
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = min(key0 + 4 * u + i, klast);
-            st.x[i] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)key * vss + 16 * c);
-        }
-    } else {
-        const int t = tid - 256;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = min(key0 + 16 * i + (t >> 4), klast);
-            st.x[i] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)key * kss + 16 * (t & 15));
-        }
-    }
+// Buffer resource over `rows` rows of `row_bytes` bytes starting at `base`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, int rows, int row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, rows * row_bytes, kRsrcWord3);
 }
 
-__device__ __forceinline__ void store_tile(const Staged& st, uint16_t* kl, uint16_t* vl, int tid) {
-    if (tid < 256) {
-        const int u = tid & 15, c = tid >> 4;
-        // 4x8 transpose: dims 8c+e of keys 4u..4u+3 -> V^T row 8c+e, columns 4u..4u+3
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            u32x2 o;
-            o[0] = __builtin_amdgcn_perm(st.x[1][e >> 1], st.x[0][e >> 1], sel);
-            o[1] = __builtin_amdgcn_perm(st.x[3][e >> 1], st.x[2][e >> 1], sel);
-            *reinterpret_cast<u32x2*>(vl + (8 * c + e) * kVStride + 4 * u) = o;
-        }
-    } else {
-        const int t = tid - 256;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int key = 16 * i + (t >> 4);  // stored at its permuted row position
-            const int pos = (key & ~31) | perm_row(key & 31);
-            *reinterpret_cast<u32x4*>(kl + pos * kKStride + 8 * (t & 15)) = st.x[i];
-        }
-    }
+__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-__global__ __launch_bounds__(512, 2) void prefill_fwd_d128(PrefillParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds_k[2][kKElems];
-    __shared__ __attribute__((aligned(16))) uint16_t lds_v[2][kVElems];
+// LDS: three K tiles, then three V^T tiles (byte offsets).
+constexpr int kKBytes = kKElems * 2;
+constexpr int kVBytes = kVElems * 2;
+constexpr int kVBase = 3 * kKBytes;
+constexpr int kLdsBytes = 3 * (kKBytes + kVBytes);
 
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+// Moves a byte offset into a ring of three slots of `size` bytes from the
+// slot `slot` (0..2) to the next one.
+__device__ __forceinline__ uint32_t next_slot(uint32_t off, int slot, int size) {
+    return off + (slot == 2 ? -2 * size : size);
+}
+
+__global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
+    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = w >> 2;  // wave group: 0 = waves 0-3, 1 = waves 4-7 (one of each per SIMD)
     const int hb = lane >> 5, row = lane & 31;
     const int G = p.Hq / p.Hkv;
     const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);  // query heads per workgroup
@@ -159,7 +144,7 @@ __global__ __launch_bounds__(512, 2) void prefill_fwd_d128(PrefillParams p) {
 
     const char* kbase = static_cast<const char*>(p.k) + (b * p.k_sb + g * p.k_sh) * 2;
     const char* vbase = static_cast<const char*>(p.v) + (b * p.v_sb + g * p.v_sh) * 2;
-    const int64_t kss = p.k_ss * 2, vss = p.v_ss * 2;
+    const int kss = (int)(p.k_ss * 2), vss = (int)(p.v_ss * 2);  // row strides in bytes
 
     // Q^T operand: column `row` is query q0 + row; k-slots are dims 16ks + 8hb + e.
     bf16x8 qop[8];
@@ -179,125 +164,231 @@ __global__ __launch_bounds__(512, 2) void prefill_fwd_d128(PrefillParams p) {
         for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    // Tiles are staged through two register sets: tile t+2 is requested while
-    // tile t is computed and tile t+1 (requested one iteration earlier) is
-    // written to LDS.
-    Staged st0, st1;
-    load_tile(st0, kbase, vbase, kss, vss, 0, p.Lkv - 1, tid);
-    if (ntiles > 1) load_tile(st1, kbase, vbase, kss, vss, kN, p.Lkv - 1, tid);
-    store_tile(st0, lds_k[0], lds_v[0], tid);
-    __syncthreads();
-
-    // One tile: `ld` receives tile t+2 from global memory, `nx` (tile t+1,
-    // requested an iteration earlier) is written to LDS.
-    auto tile_step = [&](int t, Staged& ld, const Staged& nx) {
-            const uint16_t* kl = lds_k[t & 1] + row * kKStride + 8 * hb;   // + 32kb*kKStride + 16ks
-            const uint16_t* vl = lds_v[t & 1] + row * kVStride + 8 * hb;   // + 32dblk*kVStride + 32kb + 16half
-            const bool more = t + 1 < ntiles;
-            if (t + 2 < ntiles) load_tile(ld, kbase, vbase, kss, vss, (t + 2) * kN, p.Lkv - 1, tid);
-
-            const int key0 = t * kN;
-            if (key0 <= wave_last_key) {
-                // All 16 K operands of the tile are read before the first MFMA, so
-                // LDS latency is paid once per tile, not once per MFMA.
-                bf16x8 ka[2][8];
-    #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-    #pragma unroll
-                    for (int ks = 0; ks < 8; ++ks)
-                        ka[kb][ks] = *reinterpret_cast<const bf16x8*>(kl + 32 * kb * kKStride + 16 * ks);
-                __builtin_amdgcn_sched_barrier(0);
-                f32x16 sacc[2];
-    #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-    #pragma unroll
-                    for (int j = 0; j < 16; ++j) sacc[kb][j] = 0.f;
-    #pragma unroll
-                    for (int ks = 0; ks < 8; ++ks)
-                        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], qop[ks], sacc[kb], 0, 0, 0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                // V operands of key block 0, in flight during the softmax
-                bf16x8 va[8];
-    #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    va[i] = *reinterpret_cast<const bf16x8*>(vl + 32 * (i >> 1) * kVStride + 16 * (i & 1));
-                __builtin_amdgcn_sched_barrier(0);
-                // mask keys past the diagonal or past the end
-                const bool edge = (key0 + kN > p.Lkv) || (p.causal && key0 + kN - 1 > q0 + off);
-                if (edge) {
-                    const int lim = p.causal ? min(qabs, p.Lkv - 1) : p.Lkv - 1;
-    #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
-    #pragma unroll
-                        for (int j = 0; j < 16; ++j)
-                            if (key0 + 32 * kb + key_of(j, hb) > lim) sacc[kb][j] = kNegInf;
-                }
-                // Lazy running max: the exponentials use m_run as long as no score
-                // of the lane exceeds it by the headroom; only then (wave vote) the
-                // row max over the lane pair is taken and the accumulators rescaled.
-                float lm = kNegInf;
-    #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-    #pragma unroll
-                    for (int j = 0; j < 16; j += 2) lm = fmaxf(lm, fmaxf(sacc[kb][j], sacc[kb][j + 1]));
-                if (__builtin_amdgcn_ballot_w64(lm * c2 > m_run + kHeadroom) != 0) {
-                    const float m_new = fmaxf(m_run, pair_max(lm) * c2);
-                    const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
-                    m_run = m_new;
-                    l_run *= alpha;
-    #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-    #pragma unroll
-                        for (int j = 0; j < 16; ++j) oacc[i][j] *= alpha;
-                }
-                const float nm = -m_run;
-                // key block 0: exponentials, bf16 weights
-                u32x4 pk[2][2];
-                float lsum = 0.f;
-    #pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    float pr[8];
-    #pragma unroll
-                    for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sacc[0][8 * half + e], c2, nm));
-                    lsum += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
-    #pragma unroll
-                    for (int e = 0; e < 4; ++e) pk[0][half][e] = pack_bf16(pr[2 * e], pr[2 * e + 1]);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                // P.V of key block 0 (8 MFMAs); between them, the V operands of key
-                // block 1 are requested and its exponentials computed (two scores
-                // per MFMA), so the matrix core and the vector ALU overlap
-                bf16x8 vb[8];
-                float ls1 = 0.f;
-    #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int dblk = i >> 1, half = i & 1;
-                    oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], __builtin_bit_cast(bf16x8, pk[0][half]),
-                                                                         oacc[dblk], 0, 0, 0);
-                    vb[i] = *reinterpret_cast<const bf16x8*>(vl + 32 * dblk * kVStride + 32 + 16 * half);
-                    const float p0 = fast_exp2(fmaf(sacc[1][2 * i], c2, nm));
-                    const float p1 = fast_exp2(fmaf(sacc[1][2 * i + 1], c2, nm));
-                    ls1 += p0 + p1;
-                    pk[1][i >> 2][i & 3] = pack_bf16(p0, p1);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-                l_run += lsum + ls1;
-                // P.V of key block 1
-    #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int dblk = i >> 1, half = i & 1;
-                    oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[i], __builtin_bit_cast(bf16x8, pk[1][half]),
-                                                                         oacc[dblk], 0, 0, 0);
-                }
-            }
-            if (more) store_tile(nx, lds_k[(t + 1) & 1], lds_v[(t + 1) & 1], tid);
-            __syncthreads();
+    // ---- staging. Group 0 stages V^T, group 1 stages K; each of the 256
+    // threads of a group moves four 16-byte pieces per tile through registers.
+    // Group 0 thread (u, c): keys 4u..4u+3, dims 8c..8c+7 (16 consecutive lanes
+    // read 16 different keys, so the transposed 8-byte LDS writes hit 16
+    // different bank pairs). Group 1 thread (u, c): bytes 16u.. of key rows
+    // c + 16i, written at their permuted row positions 16i + perm_row(c).
+    // Rows past the end of the sequence load as zeros.
+    const int gt = tid & 255;
+    const int su = gt & 15, sc = gt >> 4;
+    int soff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) soff[i] = grp ? (16 * i + sc) * kss + 16 * su : (4 * su + i) * vss + 16 * sc;
+    const int wr_size = grp ? kKBytes : kVBytes;
+    const uint32_t wr_lane = grp ? (kKStride * perm_row(sc) + 8 * su) * 2 : (kVStride * 8 * sc + 4 * su) * 2;
+    const uint32_t wr0 = (grp ? 0 : kVBase) + wr_lane;  // slot 0
+    u32x4 st[4];
+    // The group is a compile-time tag (G = 0 or 1) in everything the loops
+    // call, so that no branch on it remains inside them.
+    auto stage_load = [&](int t, auto gtag) __attribute__((always_inline)) {
+        constexpr int G = decltype(gtag)::value;
+        const int key0 = t * kN;
+        const int rows = min(kN, p.Lkv - key0);
+        const __amdgpu_buffer_rsrc_t r =
+            G ? rows_rsrc(kbase + (int64_t)key0 * kss, rows, kss) : rows_rsrc(vbase + (int64_t)key0 * vss, rows, vss);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st[i] = load16(r, soff[i]);
     };
-    for (int t = 0; t < ntiles; t += 2) {
-        tile_step(t, st0, st1);
-        if (t + 1 < ntiles) tile_step(t + 1, st1, st0);
-    }
+    auto stage_store = [&](uint32_t wr, auto gtag) __attribute__((always_inline)) {
+        constexpr int G = decltype(gtag)::value;
+        if constexpr (G == 0) {
+            // 4x8 transpose: dims 8c+e of keys 4u..4u+3 -> V^T row 8c+e, columns 4u..4u+3
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+                u32x2 o;
+                o[0] = __builtin_amdgcn_perm(st[1][e >> 1], st[0][e >> 1], sel);
+                o[1] = __builtin_amdgcn_perm(st[3][e >> 1], st[2][e >> 1], sel);
+                *reinterpret_cast<u32x2*>(lds + wr + e * kVStride * 2) = o;
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(lds + wr + 16 * i * kKStride * 2) = st[i];
+        }
+    };
+
+    f32x16 sacc[2];  // scores of the tile whose softmax is next
+    u32x4 pk[2][2];  // bf16 weights of the tile whose P.V is next
+
+    // ---- M phase: P.V of tile j, then the scores of tile j+1. Each product is
+    // 16 MFMAs whose operands are read from LDS six ahead. `vrd` and `krd` are
+    // this lane's read offsets in the slots of V^T tile j and K tile j+1.
+    constexpr int kAhead = 6;
+    auto pv_block = [&](uint32_t vrd) __attribute__((always_inline)) {
+        // operand i: key block i >> 3, dim block (i >> 1) & 3, half i & 1
+        auto addr = [&](int i) __attribute__((always_inline)) {
+            return reinterpret_cast<const bf16x8*>(lds + vrd +
+                                                   2 * (32 * ((i >> 1) & 3) * kVStride + 32 * (i >> 3) + 16 * (i & 1)));
+        };
+        bf16x8 opnd[kAhead];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) opnd[i] = *addr(i);
+        // the scheduling fences keep the reads six MFMAs ahead
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bf16x8 a = opnd[i % kAhead];
+            if (i + kAhead < 16) opnd[i % kAhead] = *addr(i + kAhead);
+            const int kb = i >> 3, dblk = (i >> 1) & 3, half = i & 1;
+            oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pk[kb][half]),
+                                                                 oacc[dblk], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto qk_block = [&](uint32_t krd) __attribute__((always_inline)) {
+        // operand i: key block i >> 3, d-step i & 7
+        auto addr = [&](int i) __attribute__((always_inline)) {
+            return reinterpret_cast<const bf16x8*>(lds + krd + 2 * (32 * (i >> 3) * kKStride + 16 * (i & 7)));
+        };
+        bf16x8 opnd[kAhead];
+#pragma unroll
+        for (int i = 0; i < kAhead; ++i) opnd[i] = *addr(i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bf16x8 a = opnd[i % kAhead];
+            if (i + kAhead < 16) opnd[i % kAhead] = *addr(i + kAhead);
+            const int kb = i >> 3, ks = i & 7;
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], ks ? sacc[kb] : (f32x16){}, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+
+    // ---- V phase: mask, running max, exponentials and bf16 weights of tile j.
+    auto vphase = [&](int j) __attribute__((always_inline)) {
+        const int key0 = j * kN;
+        // mask keys past the diagonal or past the end
+        const bool edge = (key0 + kN > p.Lkv) || (p.causal && key0 + kN - 1 > q0 + off);
+        if (edge) {
+            // largest visible key offset within the tile, relative to this
+            // lane's first key (8hb), so each test is against a constant
+            const int lim = (p.causal ? min(qabs, p.Lkv - 1) : p.Lkv - 1) - key0 - 8 * hb;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) {
+                    const float x = sacc[kb][jj];
+                    sacc[kb][jj] = (32 * kb + key_of(jj, 0) > lim) ? kNegInf : x;
+                }
+        }
+        // Lazy running max: the exponentials use m_run as long as no score of
+        // the lane exceeds it by the headroom; only then (wave vote) the row max
+        // over the lane pair is taken and the accumulators rescaled.
+        float lm = kNegInf;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int jj = 0; jj < 16; jj += 2) lm = fmaxf(lm, fmaxf(sacc[kb][jj], sacc[kb][jj + 1]));
+        if (__builtin_amdgcn_ballot_w64(lm * c2 > m_run + kHeadroom) != 0) {
+            const float m_new = fmaxf(m_run, pair_max(lm) * c2);
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
+            m_run = m_new;
+            l_run *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int jj = 0; jj < 16; ++jj) oacc[i][jj] *= alpha;
+        }
+        const float nm = -m_run;
+        float ls = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                float pr[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sacc[kb][8 * half + e], c2, nm));
+                ls += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pk[kb][half][e] = pack_bf16(pr[2 * e], pr[2 * e + 1]);
+            }
+        l_run += ls;
+    };
+
+    // Writes piece `t` of this group (V^T for group 0, K for group 1) at `wr`
+    // and requests piece t+1.
+    auto stage = [&](int t, uint32_t wr, auto gtag) __attribute__((always_inline)) {
+        if (t < ntiles) {
+            // the piece was requested two segments ago
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+            stage_store(wr, gtag);
+            if (t + 1 < ntiles) stage_load(t + 1, gtag);
+        }
+    };
+    // M phase of tile j (P.V of j, scores of j+1) for this wave, if any, after
+    // the group's staging step.
+    auto mstep = [&](int j, int t, uint32_t wr, uint32_t vrd, uint32_t krd, auto gtag) __attribute__((always_inline)) {
+        const bool pv = j >= 0 && j * kN <= wave_last_key;
+        const bool qk = j + 1 < ntiles && (j + 1) * kN <= wave_last_key;
+        __builtin_amdgcn_s_setprio(1);
+        stage(t, wr, gtag);
+        if (pv) pv_block(vrd);
+        if (qk) qk_block(krd);
+        __builtin_amdgcn_s_setprio(0);
+    };
+    auto vstep = [&](int j) __attribute__((always_inline)) {
+        if (j >= 0 && j < ntiles && j * kN <= wave_last_key) vphase(j);
+    };
+
+    // ---- Schedule. Per wave, tile j goes through M(j-1) (its scores, with the
+    // P.V of tile j-1), V(j) (softmax) and M(j) (its P.V, with the scores of
+    // tile j+1). The two wave groups run this sequence one segment apart, with
+    // a workgroup barrier between segments, so that on every SIMD one wave
+    // issues MFMAs while the other one computes exponentials:
+    //   segment 2k:   group 0 M(k-1)   group 1 V(k-1)
+    //   segment 2k+1: group 0 V(k)     group 1 M(k-1)
+    // The V phase is the softmax alone; LDS staging rides in the M phase, whose
+    // vector ALU is otherwise idle. LDS holds three tiles (slot = tile % 3):
+    // group 0 writes V^T of tile k in segment 2k (read from segment 2k+2 on),
+    // group 1 writes K of tile k+1 in segment 2k+1 (read from segment 2k+2
+    // on); a slot is rewritten only after both groups have passed the M phase
+    // that read its previous tile. Each group requests its next piece from
+    // global memory two segments before writing it. Both groups pass the same
+    // 2(ntiles + 1) barriers.
+    // In iteration k the read offsets point at slots (k+2)%3 (V^T of tile
+    // k-1) and k%3 (K of tile k); the write offset at k%3 (group 0) or
+    // (k+1)%3 (group 1). All move one slot per iteration.
+    auto run = [&](auto gtag) __attribute__((always_inline)) {
+        constexpr int G = decltype(gtag)::value;
+        uint32_t vrd = kVBase + 2 * kVBytes + (row * kVStride + 8 * hb) * 2;
+        uint32_t krd = (row * kKStride + 8 * hb) * 2;
+        uint32_t wr = G ? wr0 + wr_size : wr0;
+        stage_load(0, gtag);
+        if constexpr (G == 1) {
+            stage_store(wr0, gtag);
+            if (ntiles > 1) stage_load(1, gtag);
+        }
+        __syncthreads();
+        for (int k = 0; k <= ntiles; ++k) {
+            const int s0 = k % 3;
+            if constexpr (G == 0) {
+                mstep(k - 1, k, wr, vrd, krd, gtag);
+                __syncthreads();
+                vstep(k);
+                __syncthreads();
+            } else {
+                vstep(k - 1);
+                __syncthreads();
+                mstep(k - 1, k + 1, wr, vrd, krd, gtag);
+                __syncthreads();
+            }
+            vrd = next_slot(vrd, (s0 + 2) % 3, kVBytes);
+            krd = next_slot(krd, s0, kKBytes);
+            wr = next_slot(wr, G ? (s0 + 1) % 3 : s0, wr_size);
+        }
+    };
+    if (grp == 0)
+        run(std::integral_constant<int, 0>{});
+    else
+        run(std::integral_constant<int, 1>{});
+
+    // Keep the staging registers live to here, so that both loops (and the
+    // prologue) stage through the same registers and no other loop-carried
+    // value is given a register that a load of the other group's loop writes
+    // (the compiler would then wait for those loads before using it).
+    asm volatile("" ::"v"(st[0]), "v"(st[1]), "v"(st[2]), "v"(st[3]));
 
     // epilogue: O = acc / l, lse = m ln2 + ln l
     const float l_tot = pair_sum(l_run);

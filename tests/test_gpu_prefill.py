@@ -76,3 +76,19 @@ def test_workload4_causal_16k_sampled_rows():
     vmax = np.abs((inp["v"].astype(np.uint32) << 16).view(np.float32)).max()
     assert np.isfinite(o).all() and np.abs(o).max() <= vmax * (1 + 1e-2)
     print("wl4 sampled rows=%d max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (rows.size, *res), flush=True)
+
+
+def test_prefill_strided_bshd_kv_and_q():
+    # K/V stored [B, L, Hkv, d] (the cache layout of a running model) and Q
+    # [B, Lq, Hq, d], passed as strided views; results must not depend on layout.
+    B, Hq, Hkv, L = 2, 8, 2, 333
+    inp = make_inputs(4, B=B, Hq=Hq, Hkv=Hkv, L=L, seed=97)
+    dev = {}
+    for name in ("q", "k", "v"):
+        t = to_dev(inp[name])
+        dev[name] = t.transpose(1, 2).contiguous().transpose(1, 2)
+        assert not dev[name].is_contiguous()
+    out, lse = prefill_on_gpu(inp, True, dev=dev)
+    ref, ref_lse = oracle_rows(inp, True)
+    assert_close(from_dev(out).reshape(-1, 128), ref, "bf16", what="strided prefill")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 2e-3)
