@@ -100,14 +100,17 @@ ATTN_API int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype, in
 
 /*
  * Bytes of device workspace attn_decode needs for `num_splits` splits (>= 1):
- * a fixed 4 MiB block of merge counters followed by the fp32 partials
- * o [B*Hq, S, d], m [B*Hq, S], l [B*Hq, S]. 0 on a bad argument.
+ * a fixed 4 MiB block of merge counters, the fp32 partials o [B*Hq, S, d],
+ * m [B*Hq, S], l [B*Hq, S], and the same three arrays for 16 merge blocks
+ * (the first level of the fused merge). 0 on a bad argument.
  */
 ATTN_API size_t attn_decode_workspace_size(int B, int Hq, int d, int num_splits);
 
 /*
  * Prepares a decode workspace for its first use: zeroes its counter block
- * (asynchronously on `stream`). A workspace must be prepared once, after it
+ * with a small kernel on `stream` (asynchronous; no memset, so the call may be
+ * captured in a graph). The workspace must be 16-byte aligned. A workspace
+ * must be prepared once, after it
  * is allocated; every attn_decode call leaves the counters zero again, so
  * calls may reuse it with any shapes. Calls that share one workspace must be
  * ordered (the same stream, or synchronised): overlapping calls race.

@@ -133,7 +133,7 @@ def attn_decode_workspace_init(workspace, stream=None):
 def attn_decode_workspace(B, Hq, d, num_splits, device="cuda"):
     """Allocate and prepare a decode workspace for up to `num_splits` splits."""
     need = load_library().attn_decode_workspace_size(B, Hq, d, num_splits)
-    return torch.zeros(need, dtype=torch.uint8, device=device)
+    return attn_decode_workspace_init(torch.empty(need, dtype=torch.uint8, device=device))
 
 
 def attn_decode_plan(L_cap, num_splits):

@@ -129,7 +129,8 @@ attn_status attn_decode_workspace_init(void* workspace, size_t workspace_bytes, 
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
     if (workspace_bytes < attn::kCounterBytes)
         return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need at least %zu", workspace_bytes, attn::kCounterBytes);
-    hipError_t e = hipMemsetAsync(workspace, 0, attn::kCounterBytes, static_cast<hipStream_t>(stream));
+    if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    hipError_t e = attn::launch_zero(workspace, attn::kCounterBytes, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "workspace init: %s", hipGetErrorString(e));
     return ATTN_OK;
 }

@@ -80,6 +80,21 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(CombineParams p) 
 
 }  // namespace
 
+// Zero-fill of `n16` 16-byte words (a kernel rather than a memset, so that
+// the clear is an ordinary kernel node when a caller captures the stream).
+__global__ __launch_bounds__(256) void zero16_kernel(uint4* p, size_t n16) {
+    for (size_t i = blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256) p[i] = make_uint4(0, 0, 0, 0);
+}
+
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
+    if (bytes % 16 || reinterpret_cast<uintptr_t>(p) % 16) return hipErrorInvalidValue;
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    const size_t blocks = (n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024;
+    hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, static_cast<uint4*>(p), n16);
+    return hipGetLastError();
+}
+
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
     dim3 grid(p.R, (p.d + 31) / 32);
     hipLaunchKernelGGL(combine_partials_kernel, grid, dim3(256), 0, stream, p);

@@ -89,6 +89,8 @@ struct PrefillParams {
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int q_dtype, int kv_dtype, int G, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+// Zeroes `bytes` (a multiple of 16) at 16-byte aligned device address `p`.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
 }  // namespace attn

@@ -227,6 +227,24 @@ def test_workspace_reused_across_shapes_and_split_counts():
         assert int(ws[:4 << 20].view(torch.int32).abs().sum()) == 0
 
 
+def test_workspace_init_clears_a_dirty_workspace():
+    # attn_decode_workspace_init must zero the counter block whatever it held
+    import long_context_decode_kv_amd as lib
+    inp = make_inputs(2, B=1, Hq=32, Hkv=8, L=8192, seed=105)
+    S = 32
+    ws = torch.full((lib.attn_decode_workspace_size(1, 32, 128, S),), 0x5A, dtype=torch.uint8, device="cuda")
+    lib.attn_decode_workspace_init(ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4 << 20].view(torch.int32).abs().sum()) == 0
+    assert int(ws[4 << 20].item()) == 0x5A  # only the counter block is touched
+    d = {k: to_dev(v) for k, v in inp.items()}
+    out, lse = lib.attn_decode(d["q"], d["k"], d["v"], num_splits=S, workspace=ws)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle_decode(inp)
+    assert_close(from_dev(out)[:, :, 0], ref, "bf16", what="after init")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, 2e-3)
+
+
 @pytest.mark.parametrize("wl,S", [(2, 64), (5, 128), (3, 0)])
 def test_two_level_api_matches_fused_decode(wl, S):
     import long_context_decode_kv_amd as lib
