@@ -50,14 +50,31 @@ __global__ __launch_bounds__(256) void combine_partials_kernel(CombineParams p) 
     __syncthreads();
 
     const int grp = tid >> 5, c = c0 + (tid & 31);
+    const int cc = min(c, p.d - 1);  // lanes past d read a valid column and discard it
+    const float* o_col = p.o_part + (int64_t)r * p.S * p.d + cc;
     float ao = 0.f, al = 0.f;
+    auto step = [&](float ms, float ls, float os) {
+        const float wgt = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ms - mx) * kLog2e);
+        al = fmaf(wgt, ls, al);
+        ao = fmaf(wgt, os, ao);
+    };
     if (mx != kNegInf) {
-        for (int s = grp; s < n; s += 8) {
-            const float ms = m_row[s];
-            const float wgt = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ms - mx) * kLog2e);
-            al = fmaf(wgt, l_row[s], al);
-            if (c < p.d) ao = fmaf(wgt, p.o_part[((int64_t)r * p.S + s) * p.d + c], ao);
+        // the group's partials s = grp, grp + 8, ... in order; loads for eight
+        // of them are issued before their terms are added (the adds keep the
+        // same order, so the result does not depend on the unrolling)
+        int s = grp;
+        for (; s + 56 < n; s += 64) {
+            float ms[8], ls[8], os[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                ms[i] = m_row[s + 8 * i];
+                ls[i] = l_row[s + 8 * i];
+                os[i] = o_col[(int64_t)(s + 8 * i) * p.d];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) step(ms[i], ls[i], os[i]);
         }
+        for (; s < n; s += 8) step(m_row[s], l_row[s], o_col[(int64_t)s * p.d]);
     }
     __shared__ float red_o[8][32];
     __shared__ float red_l[8];

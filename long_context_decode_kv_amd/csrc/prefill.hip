@@ -17,9 +17,9 @@
 // ALU, mostly exponentials), P.V (MFMA) -- half a tile apart, separated by
 // workgroup barriers, so that one wave of each SIMD feeds the matrix core
 // while the other computes exponentials (details at the loop). K and V tiles
-// pass through registers into a three-tile LDS ring: group 0 stages V^T,
-// group 1 stages K, each through buffer loads whose out-of-range rows read as
-// zero.
+// go from global memory straight into a four-tile LDS ring (buffer loads with
+// an LDS destination, no registers; out-of-range rows arrive as zeros): group
+// 0 moves V, group 1 moves K.
 //
 // Both products are computed transposed so that one query row lives in one
 // lane and the softmax needs no cross-lane reduction except one lane-pair exchange:
@@ -28,15 +28,15 @@
 // Lane l holds query row (l & 31) and 16 of the 32 keys of each key block; the
 // K rows are fed to the MFMA in a permuted order (bits 2 and 3 of the row
 // index swapped) so that those 16 keys come as two runs of 8 consecutive keys,
-// which makes P^T usable directly as the B operand of the second product and
-// lets V^T be read from LDS with one 16-byte load per operand.
+// which makes P^T usable directly as the B operand of the second product.
+// V stays row-major in LDS; its V^T operands come from the transposed LDS
+// read (ds_read_b64_tr_b16: 16 lanes read a 4-key x 16-dim block and each
+// lane receives the 4 keys of its own dim), two per operand.
 //
-// LDS layout (per slot): K tile [64 keys][128 dims] with rows padded to 272 bytes and
-// each key stored at the permuted row position it is read from, and V^T tile
-// [128 dims][64 keys] with rows padded to 144 bytes. Every MFMA-operand read is
-// then a per-lane base plus a constant offset, and every 8 lanes of a 16-byte
-// read or write touch 8 distinct 16-byte bank groups (no bank conflicts). V is
-// transposed 8x8 in registers before it is written.
+// LDS layout (per slot): K and V tiles of 64 rows x 256 bytes, unpadded, with
+// the 16-byte chunks of K rows and the 64-byte segments of V rows rotated by
+// row so that every operand read is free of bank conflicts (details at the
+// staging code).
 //
 // Causal masking (bottom-right aligned: query i sees keys <= Lkv - Lq + i) is
 // applied only on tiles that cross the diagonal; tiles past it are skipped.
@@ -59,10 +59,11 @@ constexpr int kRows = 32;        // query rows per wave
 constexpr int kWaves = 8;        // waves per workgroup
 constexpr int kN = 64;           // keys per tile
 constexpr int kD = 128;          // head dim
-constexpr int kKStride = 136;    // bf16 per K row in LDS (272 bytes)
-constexpr int kVStride = 72;     // bf16 per V^T row in LDS (144 bytes)
-constexpr int kKElems = kN * kKStride;
-constexpr int kVElems = kD * kVStride;
+constexpr int kRowBytes = kD * 2;            // one K or V row (256 bytes)
+constexpr int kTileBytes = kN * kRowBytes;    // one K or V tile in LDS (16 KB)
+constexpr int kSlots = 4;                     // LDS ring of tiles
+constexpr int kSlotBytes = 2 * kTileBytes;    // K tile, then V tile
+constexpr int kLdsBytes = kSlots * kSlotBytes;
 constexpr float kHeadroom = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
@@ -87,7 +88,7 @@ __device__ __forceinline__ int perm_row(int r) { return (r & ~12) | ((r & 4) << 
 __device__ __forceinline__ int key_of(int j, int hb) { return j < 8 ? 8 * hb + j : 16 + 8 * hb + (j - 8); }
 
 // Word 3 of a raw buffer resource (32-bit data format, no swizzle): loads at
-// or past the resource's byte size return zero.
+// or past the resource's byte size return zero (also into LDS).
 constexpr int kRsrcWord3 = 0x00020000;
 
 // Buffer resource over `rows` rows of `row_bytes` bytes starting at `base`.
@@ -95,28 +96,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const char* base, in
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, rows * row_bytes, kRsrcWord3);
 }
 
-__device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, int off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
+typedef __attribute__((address_space(3))) char lds_char;
 
-// LDS: three K tiles, then three V^T tiles (byte offsets).
-constexpr int kKBytes = kKElems * 2;
-constexpr int kVBytes = kVElems * 2;
-constexpr int kVBase = 3 * kKBytes;
-constexpr int kLdsBytes = 3 * (kKBytes + kVBytes);
-
-// Moves a byte offset into a ring of three slots of `size` bytes from the
-// slot `slot` (0..2) to the next one.
-__device__ __forceinline__ uint32_t next_slot(uint32_t off, int slot, int size) {
-    return off + (slot == 2 ? -2 * size : size);
+// Workgroup barrier for the main loop. Unlike __syncthreads it does not wait
+// for outstanding loads into LDS (the compiler's release fence would): those
+// are completed explicitly, one M phase after they are issued, so they stay
+// in flight across the barriers in between. It waits for this wave's own LDS
+// reads (lgkmcnt(0)), so no slot is overwritten while a read of it is in
+// flight, and the empty asm statements keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void loop_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
-    __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = w >> 2;  // wave group: 0 = waves 0-3, 1 = waves 4-7 (one of each per SIMD)
+    const int wv = w & 3;    // wave within its group
     const int hb = lane >> 5, row = lane & 31;
     const int G = p.Hq / p.Hkv;
     const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);  // query heads per workgroup
@@ -164,92 +167,103 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
 
-    // ---- staging. Group 0 stages V^T, group 1 stages K; each of the 256
-    // threads of a group moves four 16-byte pieces per tile through registers.
-    // Group 0 thread (u, c): keys 4u..4u+3, dims 8c..8c+7 (16 consecutive lanes
-    // read 16 different keys, so the transposed 8-byte LDS writes hit 16
-    // different bank pairs). Group 1 thread (u, c): bytes 16u.. of key rows
-    // c + 16i, written at their permuted row positions 16i + perm_row(c).
-    // Rows past the end of the sequence load as zeros.
-    const int gt = tid & 255;
-    const int su = gt & 15, sc = gt >> 4;
+    // ---- LDS tiles. Slot s holds K of one tile at s * kSlotBytes and V of the
+    // same tile right after it, both as 64 rows of 256 bytes, no padding:
+    //  * K row r holds the key whose row in the MFMA order is r (rows are fed
+    //    with bits 2 and 3 of the index swapped), and its 16-byte chunk c sits
+    //    at position c ^ (r & 15), so the 16 rows one operand read touches per
+    //    16 lanes hit 16 different bank groups;
+    //  * V row r holds key r, and its 64-byte segment d (dims 32d..32d+31)
+    //    sits at position (d + r) & 3, so the four rows one transposed read
+    //    touches per 32 lanes cover all 64 banks once.
+    // Tiles go from global memory straight into LDS (buffer loads with an LDS
+    // destination, no registers): each wave moves 4 KB per tile with four
+    // 1 KB instructions, lane i writing bytes 16i..16i+15 of each; the global
+    // address each lane asks for makes the layout above. Group 0 moves V,
+    // group 1 moves K. Rows past the end of the sequence arrive as zeros.
     int soff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) soff[i] = grp ? (16 * i + sc) * kss + 16 * su : (4 * su + i) * vss + 16 * sc;
-    const int wr_size = grp ? kKBytes : kVBytes;
-    const uint32_t wr_lane = grp ? (kKStride * perm_row(sc) + 8 * su) * 2 : (kVStride * 8 * sc + 4 * su) * 2;
-    const uint32_t wr0 = (grp ? 0 : kVBase) + wr_lane;  // slot 0
-    u32x4 st[4];
-    // The group is a compile-time tag (G = 0 or 1) in everything the loops
-    // call, so that no branch on it remains inside them.
-    auto stage_load = [&](int t, auto gtag) __attribute__((always_inline)) {
-        constexpr int G = decltype(gtag)::value;
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * wv + 4 * i + (lane >> 4), q = lane & 15;  // LDS row and 16-byte chunk written
+        if (grp) {
+            const int key = (r & ~31) | perm_row(r & 31);
+            soff[i] = key * kss + 16 * (q ^ (r & 15));
+        } else {
+            soff[i] = r * vss + 64 * (((q >> 2) - r) & 3) + 16 * (q & 3);
+        }
+    }
+    // Requests this group's piece of tile t into LDS slot t % kSlots.
+    auto dma = [&](int t, auto gtag) __attribute__((always_inline)) {
+        constexpr int GG = decltype(gtag)::value;
         const int key0 = t * kN;
         const int rows = min(kN, p.Lkv - key0);
-        const __amdgpu_buffer_rsrc_t r =
-            G ? rows_rsrc(kbase + (int64_t)key0 * kss, rows, kss) : rows_rsrc(vbase + (int64_t)key0 * vss, rows, vss);
+        const __amdgpu_buffer_rsrc_t r = GG ? rows_rsrc(kbase + (int64_t)key0 * kss, rows, kss)
+                                            : rows_rsrc(vbase + (int64_t)key0 * vss, rows, vss);
+        lds_char* dst = (lds_char*)lds + (t % kSlots) * kSlotBytes + (GG ? 0 : kTileBytes) + wv * 4096;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) st[i] = load16(r, soff[i]);
+        for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * i, 16, soff[i], 0, 0, 0);
     };
-    auto stage_store = [&](uint32_t wr, auto gtag) __attribute__((always_inline)) {
-        constexpr int G = decltype(gtag)::value;
-        if constexpr (G == 0) {
-            // 4x8 transpose: dims 8c+e of keys 4u..4u+3 -> V^T row 8c+e, columns 4u..4u+3
+
+    // Per-lane read offsets within a slot. K operand (key block kb, d-step
+    // ks): row 32kb + row, chunk (2ks + hb) ^ (row & 15). V^T operand (dim
+    // block dblk, keys kk..kk+3 for the transposed read): this lane supplies
+    // the address of keys kk + (i16 >> 2), dims 32dblk + 16g + 4(i16 & 3).
+    uint32_t kofs[8], vofs[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-                u32x2 o;
-                o[0] = __builtin_amdgcn_perm(st[1][e >> 1], st[0][e >> 1], sel);
-                o[1] = __builtin_amdgcn_perm(st[3][e >> 1], st[2][e >> 1], sel);
-                *reinterpret_cast<u32x2*>(lds + wr + e * kVStride * 2) = o;
-            }
-        } else {
+    for (int ks = 0; ks < 8; ++ks) kofs[ks] = row * kRowBytes + 16 * ((2 * ks + hb) ^ (row & 15));
+    {
+        const int i16 = lane & 15, ga = i16 >> 2, gb = i16 & 3, gg = (lane >> 4) & 1;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(lds + wr + 16 * i * kKStride * 2) = st[i];
-        }
-    };
+        for (int dblk = 0; dblk < 4; ++dblk)
+            vofs[dblk] = kTileBytes + (8 * hb + ga) * kRowBytes + 64 * ((dblk + ga) & 3) + 32 * gg + 8 * gb;
+    }
 
     f32x16 sacc[2];  // scores of the tile whose softmax is next
     u32x4 pk[2][2];  // bf16 weights of the tile whose P.V is next
 
     // ---- M phase: P.V of tile j, then the scores of tile j+1. Each product is
-    // 16 MFMAs whose operands are read from LDS six ahead. `vrd` and `krd` are
-    // this lane's read offsets in the slots of V^T tile j and K tile j+1.
+    // 16 MFMAs whose operands are read from LDS four (V^T: transposed reads,
+    // two per operand) or six (K) MFMAs ahead.
     constexpr int kAhead = 6;
-    auto pv_block = [&](uint32_t vrd) __attribute__((always_inline)) {
-        // operand i: key block i >> 3, dim block (i >> 1) & 3, half i & 1
-        auto addr = [&](int i) __attribute__((always_inline)) {
-            return reinterpret_cast<const bf16x8*>(lds + vrd +
-                                                   2 * (32 * ((i >> 1) & 3) * kVStride + 32 * (i >> 3) + 16 * (i & 1)));
+    auto pv_block = [&](uint32_t slot) __attribute__((always_inline)) {
+        // operand i: key block kb = i >> 3, dim block (i >> 1) & 3, half i & 1:
+        // keys 32kb + 16half + 8hb + (0..7), dim 32dblk + (lane & 31)
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            const int kb = i >> 3, dblk = (i >> 1) & 3, half = i & 1;
+            const uint32_t a0 = slot + vofs[dblk] + (32 * kb + 16 * half) * kRowBytes;
+            const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)((lds_char*)lds + a0));
+            const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) v4i16*)((lds_char*)lds + a0 + 4 * kRowBytes));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        bf16x8 opnd[kAhead];
+        constexpr int kA = 4;
+        bf16x8 opnd[kA];
 #pragma unroll
-        for (int i = 0; i < kAhead; ++i) opnd[i] = *addr(i);
-        // the scheduling fences keep the reads six MFMAs ahead
+        for (int i = 0; i < kA; ++i) opnd[i] = rd(i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const bf16x8 a = opnd[i % kAhead];
-            if (i + kAhead < 16) opnd[i % kAhead] = *addr(i + kAhead);
+            const bf16x8 a = opnd[i % kA];
+            if (i + kA < 16) opnd[i % kA] = rd(i + kA);
             const int kb = i >> 3, dblk = (i >> 1) & 3, half = i & 1;
             oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pk[kb][half]),
                                                                  oacc[dblk], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
-    auto qk_block = [&](uint32_t krd) __attribute__((always_inline)) {
+    auto qk_block = [&](uint32_t slot) __attribute__((always_inline)) {
         // operand i: key block i >> 3, d-step i & 7
-        auto addr = [&](int i) __attribute__((always_inline)) {
-            return reinterpret_cast<const bf16x8*>(lds + krd + 2 * (32 * (i >> 3) * kKStride + 16 * (i & 7)));
+        auto rd = [&](int i) __attribute__((always_inline)) {
+            return *reinterpret_cast<const bf16x8*>(lds + slot + kofs[i & 7] + 32 * (i >> 3) * kRowBytes);
         };
         bf16x8 opnd[kAhead];
 #pragma unroll
-        for (int i = 0; i < kAhead; ++i) opnd[i] = *addr(i);
+        for (int i = 0; i < kAhead; ++i) opnd[i] = rd(i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const bf16x8 a = opnd[i % kAhead];
-            if (i + kAhead < 16) opnd[i % kAhead] = *addr(i + kAhead);
+            if (i + kAhead < 16) opnd[i % kAhead] = rd(i + kAhead);
             const int kb = i >> 3, ks = i & 7;
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], ks ? sacc[kb] : (f32x16){}, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -307,26 +321,25 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         l_run += ls;
     };
 
-    // Writes piece `t` of this group (V^T for group 0, K for group 1) at `wr`
-    // and requests piece t+1.
-    auto stage = [&](int t, uint32_t wr, auto gtag) __attribute__((always_inline)) {
-        if (t < ntiles) {
-            // the piece was requested two segments ago
-            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
-            stage_store(wr, gtag);
-            if (t + 1 < ntiles) stage_load(t + 1, gtag);
-        }
-    };
     // M phase of tile j (P.V of j, scores of j+1) for this wave, if any, after
-    // the group's staging step.
-    auto mstep = [&](int j, int t, uint32_t wr, uint32_t vrd, uint32_t krd, auto gtag) __attribute__((always_inline)) {
+    // requesting the group's piece of tile j+3. The wait at the end (vmcnt)
+    // completes the previous request, tile j+2's piece, before the barrier
+    // that precedes its first reader.
+    auto mstep = [&](int j, auto gtag) __attribute__((always_inline)) {
         const bool pv = j >= 0 && j * kN <= wave_last_key;
         const bool qk = j + 1 < ntiles && (j + 1) * kN <= wave_last_key;
         __builtin_amdgcn_s_setprio(1);
-        stage(t, wr, gtag);
-        if (pv) pv_block(vrd);
-        if (qk) qk_block(krd);
+        const bool more = j + 3 < ntiles;
+        // the request goes after the transposed V reads: the compiler makes
+        // those wait for every outstanding LDS load
+        if (pv) pv_block((uint32_t)((j % kSlots) * kSlotBytes));
+        if (more) dma(j + 3, gtag);
+        if (qk) qk_block((uint32_t)(((j + 1) % kSlots) * kSlotBytes));
         __builtin_amdgcn_s_setprio(0);
+        if (more)
+            __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4): all but the four just issued
+        else
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     };
     auto vstep = [&](int j) __attribute__((always_inline)) {
         if (j >= 0 && j < ntiles && j * kN <= wave_last_key) vphase(j);
@@ -339,56 +352,38 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // issues MFMAs while the other one computes exponentials:
     //   segment 2k:   group 0 M(k-1)   group 1 V(k-1)
     //   segment 2k+1: group 0 V(k)     group 1 M(k-1)
-    // The V phase is the softmax alone; LDS staging rides in the M phase, whose
-    // vector ALU is otherwise idle. LDS holds three tiles (slot = tile % 3):
-    // group 0 writes V^T of tile k in segment 2k (read from segment 2k+2 on),
-    // group 1 writes K of tile k+1 in segment 2k+1 (read from segment 2k+2
-    // on); a slot is rewritten only after both groups have passed the M phase
-    // that read its previous tile. Each group requests its next piece from
-    // global memory two segments before writing it. Both groups pass the same
-    // 2(ntiles + 1) barriers.
-    // In iteration k the read offsets point at slots (k+2)%3 (V^T of tile
-    // k-1) and k%3 (K of tile k); the write offset at k%3 (group 0) or
-    // (k+1)%3 (group 1). All move one slot per iteration.
+    // Tile t lives in LDS slot t % 4. In M(j) (segment 2j+2+g for group g)
+    // each group requests its piece of tile j+3, after its P.V reads: the
+    // slot's previous tile, j-1, was last read as K in M(j-2) and as V in
+    // M(j-1), both in earlier segments. The request is complete at the end of
+    // the group's next M phase, M(j+1), before the barrier that precedes the
+    // first reader of tile j+3, M(j+2) of group 0. Tiles 0 and 1 are
+    // requested before the loop. Both groups pass the same 2(ntiles + 1)
+    // barriers.
     auto run = [&](auto gtag) __attribute__((always_inline)) {
-        constexpr int G = decltype(gtag)::value;
-        uint32_t vrd = kVBase + 2 * kVBytes + (row * kVStride + 8 * hb) * 2;
-        uint32_t krd = (row * kKStride + 8 * hb) * 2;
-        uint32_t wr = G ? wr0 + wr_size : wr0;
-        stage_load(0, gtag);
-        if constexpr (G == 1) {
-            stage_store(wr0, gtag);
-            if (ntiles > 1) stage_load(1, gtag);
-        }
+        constexpr int GG = decltype(gtag)::value;
+        dma(0, gtag);
+        if (ntiles > 1) dma(1, gtag);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tiles 0-1 and the Q loads
         __syncthreads();
         for (int k = 0; k <= ntiles; ++k) {
-            const int s0 = k % 3;
-            if constexpr (G == 0) {
-                mstep(k - 1, k, wr, vrd, krd, gtag);
-                __syncthreads();
+            if constexpr (GG == 0) {
+                mstep(k - 1, gtag);
+                loop_barrier();
                 vstep(k);
-                __syncthreads();
+                loop_barrier();
             } else {
                 vstep(k - 1);
-                __syncthreads();
-                mstep(k - 1, k + 1, wr, vrd, krd, gtag);
-                __syncthreads();
+                loop_barrier();
+                mstep(k - 1, gtag);
+                loop_barrier();
             }
-            vrd = next_slot(vrd, (s0 + 2) % 3, kVBytes);
-            krd = next_slot(krd, s0, kKBytes);
-            wr = next_slot(wr, G ? (s0 + 1) % 3 : s0, wr_size);
         }
     };
     if (grp == 0)
         run(std::integral_constant<int, 0>{});
     else
         run(std::integral_constant<int, 1>{});
-
-    // Keep the staging registers live to here, so that both loops (and the
-    // prologue) stage through the same registers and no other loop-carried
-    // value is given a register that a load of the other group's loop writes
-    // (the compiler would then wait for those loads before using it).
-    asm volatile("" ::"v"(st[0]), "v"(st[1]), "v"(st[2]), "v"(st[3]));
 
     // epilogue: O = acc / l, lse = m ln2 + ln l
     const float l_tot = pair_sum(l_run);

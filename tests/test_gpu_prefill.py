@@ -92,3 +92,20 @@ def test_prefill_strided_bshd_kv_and_q():
     ref, ref_lse = oracle_rows(inp, True)
     assert_close(from_dev(out).reshape(-1, 128), ref, "bf16", what="strided prefill")
     assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 2e-3)
+
+
+def test_prefill_repeats_are_bit_identical():
+    # The K/V ring in LDS is filled asynchronously; a missing wait would show
+    # up as results that change from run to run. Ten runs must agree bit for bit
+    # and match the oracle on sampled rows.
+    inp = make_inputs(4, B=1, Hq=32, Hkv=8, L=4096, seed=98)
+    dev = {k: to_dev(inp[k]) for k in ("q", "k", "v")}
+    first, first_lse = prefill_on_gpu(inp, True, dev=dev)
+    for _ in range(9):
+        o, l = prefill_on_gpu(inp, True, dev=dev)
+        assert torch.equal(o.view(torch.int16), first.view(torch.int16)) and torch.equal(l, first_lse)
+    rows, _ = _sample_rows(32, 4096)
+    ref, ref_lse = oracle_rows(inp, True, rows=rows)
+    got = from_dev(first).reshape(-1, 128)[rows]
+    assert_close(got, ref, "bf16", what="repeats")
+    assert_lse_close(first_lse.cpu().numpy().astype(np.float64).ravel()[rows], ref_lse, 2e-3)
