@@ -288,3 +288,38 @@ def test_combine_partials_api_against_oracle():
             assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
         assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, 1e-5)
         assert np.all(got[1] == 0) and np.isneginf(lse.cpu().numpy()[1])
+
+
+def test_decode_captured_in_a_graph_matches_eager_on_every_replay():
+    # A decode step replayed from a HIP graph (as a serving loop would run it):
+    # no memset is recorded (the merge counters are left zero by each call),
+    # and every replay, with eager work in between, must equal the eager call.
+    import long_context_decode_kv_amd as lib
+    inp = make_inputs(2, B=1, Hq=32, Hkv=8, L=20000, seed=106)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    S = 32
+    ws = lib.attn_decode_workspace(1, 32, 128, S)
+    out = torch.empty_like(d["q"])
+    lse = torch.empty((1, 32), dtype=torch.float32, device="cuda")
+    ref_out, ref_lse = lib.attn_decode(d["q"], d["k"], d["v"], num_splits=S, workspace=ws)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        lib.attn_decode(d["q"], d["k"], d["v"], num_splits=S, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        lib.attn_decode(d["q"], d["k"], d["v"], num_splits=S, out=out, lse=lse, workspace=ws)
+    for i in range(5):
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), "replay %d" % i
+        assert torch.equal(lse, ref_lse), "replay %d" % i
+        # eager work between replays, on the same workspace
+        o2, _ = lib.attn_decode(d["q"], d["k"], d["v"], num_splits=S, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int16), ref_out.view(torch.int16))
+    assert int(ws[:4 << 20].view(torch.int32).abs().sum()) == 0
