@@ -8,8 +8,10 @@
 // head. The four waves of the workgroup interleave 16-key tiles of the chunk;
 // inside a wave, each group of 16 lanes keeps its own running partial, so the
 // hot loop needs no cross-lane reduction at all. The partials are merged in
-// registers (lane groups), then in LDS (waves) -- the level-1 tree -- and the
-// level-2 tree across workgroups runs in combine.hip.
+// registers (lane groups), then in LDS (waves) -- the level-1 tree. The
+// level-2 tree across workgroups runs either here (the last workgroup of each
+// (sequence, KV head) to finish merges its group's partials, see FUSED) or in
+// combine.hip.
 //
 // Per 16-key tile and wave:
 //  * scores: S^T = K Q^T on one v_mfma_f32_16x16x32_bf16 chain (4 steps over
