@@ -4,7 +4,8 @@ Holds no attention arithmetic: it only draws numbers (counter-based SplitMix64
 stream + Box-Muller, see ``datagen.c``) and encodes them into the storage
 formats the library reads. Random numbers never come from the GPU path.
 
-Tensor ids used by the workloads: Q=0, K=1, V=2, per-sequence lengths=3.
+Tensor ids used by the workloads: Q=0, K=1, V=2, per-sequence lengths=3; the
+fp8 span of a two-precision cache: K=4, V=5, its lengths=6.
 """
 import ctypes
 import os
@@ -17,6 +18,7 @@ _LIB_PATH = os.path.join(_HERE, "libdatagen.so")
 _lib = None
 
 TID_Q, TID_K, TID_V, TID_LENS = 0, 1, 2, 3
+TID_K_LO, TID_V_LO, TID_LENS_LO = 4, 5, 6
 
 
 def build():

@@ -10,7 +10,8 @@ per (batch, KV head).
 """
 import numpy as np
 
-from . import TID_K, TID_LENS, TID_Q, TID_V, normal_bf16_bits, normal_e4m3, normal_f32, uniform_int
+from . import (TID_K, TID_K_LO, TID_LENS, TID_LENS_LO, TID_Q, TID_V, TID_V_LO, normal_bf16_bits, normal_e4m3,
+               normal_f32, uniform_int)
 
 WORKLOADS = {
     1: dict(name="single-head decode, fp32, L=1024, d=64, 4 splits", kind="decode", B=1, Hq=1, Hkv=1, d=64,
@@ -23,6 +24,8 @@ WORKLOADS = {
             L=16384, q="bf16", kv="bf16", mul=1.0, causal=True),
     5: dict(name="fp8-e4m3 KV decode, L=1048576, 32q/8kv, d=128", kind="decode", B=1, Hq=32, Hkv=8, d=128,
             L=1048576, q="bf16", kv="e4m3", mul=1.0, causal=False, splits=1024),
+    6: dict(name="two-precision KV decode, L=131072: first and last 10% bf16, the rest fp8-e4m3, 32q/8kv, d=128",
+            kind="mixed", B=1, Hq=32, Hkv=8, d=128, L=131072, hi_frac=0.1, q="bf16", mul=0.5, causal=False),
 }
 
 
@@ -61,3 +64,41 @@ def make_inputs(wl, seed=None, B=None, Hq=None, Hkv=None, d=None, L=None, Lq=Non
         kv_lens = uniform_int(seed, TID_LENS, B, int(rng[0]), int(min(rng[1], L)))
     return dict(q=q, k=k, v=v, k_scale=None if ks is None else ks.ravel(),
                 v_scale=None if vs is None else vs.ravel(), kv_lens=kv_lens)
+
+
+def make_mixed_inputs(wl=6, seed=None, B=None, Hq=None, Hkv=None, d=None, L=None, hi_frac=None, L_hi=None,
+                      L_lo=None, lens=None):
+    """Host inputs of a two-precision cache: the first and the last hi_frac of
+    the L tokens (2 * round(hi_frac * L) keys) in bf16, the others in fp8-e4m3.
+
+    Key order does not change single-query attention, so the bf16 keys are
+    stored as one span k_hi/v_hi [B,Hkv,L_hi,d] and the fp8 keys as another,
+    k_lo/v_lo [B,Hkv,L_lo,d] with one amax/448 scale per (batch, KV head).
+    `lens` = (lo, hi) draws a valid length per (batch, KV head) for each span
+    uniformly from [lo*cap, hi*cap] (ragged per head); None = full spans.
+    Returns dict(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens, lo_lens)."""
+    cfg = WORKLOADS[wl]
+    seed = wl if seed is None else seed
+    B = B or cfg["B"]
+    Hq = Hq or cfg["Hq"]
+    Hkv = Hkv or cfg["Hkv"]
+    d = d or cfg["d"]
+    L = L or cfg["L"]
+    frac = cfg["hi_frac"] if hi_frac is None else hi_frac
+    if L_hi is None:
+        L_hi = 2 * int(round(frac * L))
+    if L_lo is None:
+        L_lo = L - L_hi
+    mul = cfg["mul"]
+    q = normal_bf16_bits(seed, TID_Q, (B, Hq, 1, d), mul)
+    k_hi = normal_bf16_bits(seed, TID_K, (B, Hkv, L_hi, d), mul) if L_hi else None
+    v_hi = normal_bf16_bits(seed, TID_V, (B, Hkv, L_hi, d), mul) if L_hi else None
+    k_lo, ks = normal_e4m3(seed, TID_K_LO, (B, Hkv, L_lo, d), mul) if L_lo else (None, None)
+    v_lo, vs = normal_e4m3(seed, TID_V_LO, (B, Hkv, L_lo, d), mul) if L_lo else (None, None)
+    hi_lens = lo_lens = None
+    if lens is not None:
+        lo_f, hi_f = lens
+        hi_lens = uniform_int(seed, TID_LENS, B * Hkv, int(lo_f * L_hi), int(hi_f * L_hi))
+        lo_lens = uniform_int(seed, TID_LENS_LO, B * Hkv, int(lo_f * L_lo), int(hi_f * L_lo))
+    return dict(q=q, k_hi=k_hi, v_hi=v_hi, k_lo=k_lo, v_lo=v_lo, k_scale=None if ks is None else ks.ravel(),
+                v_scale=None if vs is None else vs.ravel(), hi_lens=hi_lens, lo_lens=lo_lens)

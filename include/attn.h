@@ -182,6 +182,59 @@ ATTN_API attn_status attn_decode_partials(const attn_tensor* q, const attn_tenso
                                           float* l_part, int* splits_used, void* stream);
 
 /*
+ * Selective mixed-precision decode: one decode over a KV cache kept in two
+ * precisions, bf16 for the keys that are sensitive to quantisation and fp8
+ * for the rest (the ThriftAttention page: its introduction assigns each head
+ * or token a precision by its sensitivity and keeps the first and last tokens
+ * of the sequence in high precision; the COMPUTE and ORCHESTRATE layers of its
+ * Physical AI Stack section switch precisions inside one kernel and name the
+ * first and last 10 % of the tokens). The softmax over all keys is a sum over
+ * keys, so the order in which keys are stored does not change O: the cache of
+ * each (sequence, KV head) is two key sets, and the result is exact attention
+ * over their union, with the fp8 keys and values taken at code * scale. The
+ * split partials of both spans go through one log-sum-exp merge (Tree
+ * Attention explainer, section 3).
+ *
+ * q        [B, Hq, 1, d] bf16, d = 128, Hq = 4 * Hkv
+ * k_hi, v_hi  [B, Hkv, L_hi_cap, d] bf16: the high-precision span (may be NULL
+ *          when L_hi_cap = 0)
+ * hi_lens  device int32 [B, Hkv] (index b*Hkv + g): valid keys of the bf16 span
+ *          per (sequence, KV head), clamped to [0, L_hi_cap]; NULL = L_hi_cap
+ * k_lo, v_lo  [B, Hkv, L_lo_cap, d] ATTN_FP8_E4M3: the low-precision span (may
+ *          be NULL when L_lo_cap = 0)
+ * k_scale, v_scale  device float [B*Hkv]: the fp8 span's scales
+ * lo_lens  device int32 [B, Hkv]: valid keys of the fp8 span, as hi_lens
+ * L_hi_cap, L_lo_cap  >= 0, not both 0
+ * num_splits_hi, num_splits_lo  requested splits of each span (planned as by
+ *          attn_decode_plan); 0 takes that span's value from
+ *          attn_decode_mixed_splits(). S = S_hi + S_lo splits in all.
+ * out      [B, Hq, 1, d] bf16; lse device float [B*Hq] or NULL
+ * workspace  attn_decode_workspace_size(B, Hq, d, S) bytes, 16-byte aligned,
+ *          prepared by attn_decode_workspace_init (shared with attn_decode).
+ *
+ * A (sequence, KV head) with no valid key in either span gets O = 0 and lse =
+ * -inf. Errors as for attn_decode; a dtype or shape outside the above returns
+ * ATTN_ERR_UNSUPPORTED.
+ */
+ATTN_API attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
+                                       const int32_t* hi_lens, int L_hi_cap, const attn_tensor* k_lo,
+                                       const attn_tensor* v_lo, const float* k_scale, const float* v_scale,
+                                       const int32_t* lo_lens, int L_lo_cap, int B, int Hq, int Hkv, int d,
+                                       float softmax_scale, int num_splits_hi, int num_splits_lo,
+                                       attn_tensor* out, float* lse, void* workspace, size_t workspace_bytes,
+                                       void* stream);
+
+/*
+ * Automatic split plan of attn_decode_mixed: about two workgroups per compute
+ * unit of the current device in all, shared between the spans in proportion
+ * to their bytes, no split shorter than 256 keys. Stores the splits each span
+ * will use (after planning) in *splits_hi and *splits_lo (host pointers, may
+ * be NULL) and returns their sum; 0 on a bad argument or a failed device
+ * query.
+ */
+ATTN_API int attn_decode_mixed_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi, int* splits_lo);
+
+/*
  * Prefill: attention of Lq queries over Lkv keys (causal or not), fused so the
  * Lq x Lkv score matrix never reaches memory.
  *

@@ -17,6 +17,7 @@ __all__ = [
     "attn_status_string", "attn_decode_auto_splits", "attn_decode_workspace_size", "attn_decode_workspace_init",
     "attn_decode_plan",
     "attn_decode", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
+    "attn_decode_mixed", "attn_decode_mixed_splits",
 ]
 
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
@@ -71,6 +72,12 @@ def load_library():
     lib.attn_prefill.restype = i32
     lib.attn_combine_partials.argtypes = [vp, vp, vp, i32, i32, i32, tp, vp, vp]
     lib.attn_combine_partials.restype = i32
+    lib.attn_decode_mixed.argtypes = [tp, tp, tp, vp, i32, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32,
+                                      tp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_decode_mixed.restype = i32
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.attn_decode_mixed_splits.argtypes = [i32, i32, i32, i32, ip, ip]
+    lib.attn_decode_mixed_splits.restype = i32
     _lib = lib
     return lib
 
@@ -233,5 +240,54 @@ def attn_combine_partials(o_part, m_part, l_part, out=None, lse=None, out_dtype=
     ot = attn_tensor(out.data_ptr(), _dtype_code(out), 0, 0, out.stride(0))
     st = lib.attn_combine_partials(_ptr(o_part), _ptr(m_part), _ptr(l_part), R, S, d, ctypes.byref(ot), _ptr(lse),
                                    _stream(stream, o_part.device))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_mixed_splits(B, Hkv, L_hi_cap, L_lo_cap):
+    """(S_hi, S_lo): the automatic split plan of attn_decode_mixed."""
+    hi, lo = ctypes.c_int(0), ctypes.c_int(0)
+    total = load_library().attn_decode_mixed_splits(B, Hkv, L_hi_cap, L_lo_cap, ctypes.byref(hi), ctypes.byref(lo))
+    if total <= 0:
+        raise AttnError(4, "could not plan splits")
+    return hi.value, lo.value
+
+
+def attn_decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale=None, v_scale=None, hi_lens=None, lo_lens=None,
+                      softmax_scale=0.0, num_splits_hi=0, num_splits_lo=0, out=None, lse=None, workspace=None,
+                      stream=None):
+    """Decode over a two-precision KV cache: a bf16 span (k_hi, v_hi [B,Hkv,L_hi,d]) and an fp8 span (k_lo,
+    v_lo [B,Hkv,L_lo,d] with k_scale, v_scale [B*Hkv]); hi_lens / lo_lens are int32 [B,Hkv] or None. Either
+    span may be None (no keys). Returns (out [B,Hq,1,d] bf16, lse [B,Hq])."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    if Lq != 1:
+        raise ValueError("attn_decode_mixed takes one query per sequence (q.shape[2] == 1)")
+    L_hi = 0 if k_hi is None else k_hi.shape[2]
+    L_lo = 0 if k_lo is None else k_lo.shape[2]
+    Hkv = (k_hi if k_hi is not None else k_lo).shape[1]
+    for lens in (hi_lens, lo_lens):
+        if lens is not None and (lens.dtype != torch.int32 or lens.numel() != B * Hkv or not lens.is_contiguous()):
+            raise ValueError("span lengths must be contiguous int32 with B*Hkv entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    auto_hi, auto_lo = (0, 0)
+    if (num_splits_hi <= 0 and L_hi) or (num_splits_lo <= 0 and L_lo):
+        auto_hi, auto_lo = attn_decode_mixed_splits(B, Hkv, L_hi, L_lo)
+    S_hi = attn_decode_plan(L_hi, num_splits_hi if num_splits_hi > 0 else auto_hi)[0] if L_hi else 0
+    S_lo = attn_decode_plan(L_lo, num_splits_lo if num_splits_lo > 0 else auto_lo)[0] if L_lo else 0
+    if workspace is None:
+        workspace = attn_decode_workspace(B, Hq, d, S_hi + S_lo, device=q.device)
+
+    def view(t):
+        return None if t is None else ctypes.byref(_tensor(t))
+
+    qt, ot = _tensor(q), _tensor(out)
+    st = lib.attn_decode_mixed(ctypes.byref(qt), view(k_hi), view(v_hi), _ptr(hi_lens), L_hi, view(k_lo), view(v_lo),
+                               _ptr(k_scale), _ptr(v_scale), _ptr(lo_lens), L_lo, B, Hq, Hkv, d,
+                               float(softmax_scale), int(S_hi), int(S_lo), ctypes.byref(ot), _ptr(lse), _ptr(workspace),
+                               workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     _check(st)
     return out, lse

@@ -157,6 +157,18 @@ struct FusedOut {
     float* blk_l;
 };
 
+// Splits per first-level ticket block of the fused merge: one level up to 32
+// splits, else blocks of about sqrt(S) splits (at most kMaxTicketBlocks).
+int ticket_block_for(int S) {
+    int tb = S;
+    if (tb > 32) {
+        tb = 1;
+        while (tb * tb < S) ++tb;
+        while ((S + tb - 1) / tb > attn::kMaxTicketBlocks) ++tb;
+    }
+    return tb;
+}
+
 int requested_splits(int B, int Hkv, int L_cap, const attn_tensor* k, const int32_t* kv_lens, int num_splits) {
     if (num_splits > 0) return num_splits;
     if (B <= 0 || Hkv <= 0 || L_cap <= 0 || !k) return 0;
@@ -233,6 +245,8 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     p.counters = nullptr;
     p.ticket_block = 1;
     p.blk_o = p.blk_m = p.blk_l = nullptr;
+    p.S_hi = 0;
+    p.hi = p.lo = attn::KvSpan{};
     p.out = nullptr;
     p.out_sb = p.out_sh = 0;
     p.lse = nullptr;
@@ -247,14 +261,7 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     if (mfma && fused && (int64_t)B * Hkv <= attn::kMaxCounterGroups && pl->S <= attn::kMaxFusedSplits &&
         cus > 0 && wgs <= 2LL * cus) {
         p.counters = fused->counters;
-        // one level up to 32 splits, else blocks of about sqrt(S) splits
-        int tb = pl->S;
-        if (tb > 32) {
-            tb = 1;
-            while (tb * tb < pl->S) ++tb;
-            while ((pl->S + tb - 1) / tb > attn::kMaxTicketBlocks) ++tb;
-        }
-        p.ticket_block = tb;
+        p.ticket_block = ticket_block_for(pl->S);
         p.blk_o = fused->blk_o;
         p.blk_m = fused->blk_m;
         p.blk_l = fused->blk_l;
@@ -372,6 +379,173 @@ attn_status attn_combine_partials(const float* o_part, const float* m_part, cons
     cp.out_sh = 0;
     cp.lse = lse;
     hipError_t e = attn::launch_combine(cp, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+int attn_decode_mixed_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi, int* splits_lo) {
+    if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0) return 0;
+    const int cus = device_cu_count();
+    if (cus <= 0) return 0;
+    // Two resident workgroups per compute unit in all, shared between the spans
+    // in proportion to their bytes (2 per bf16 key and value element, 1 per
+    // fp8 one), every split at least 256 keys long.
+    int64_t T = (2LL * cus) / ((int64_t)B * Hkv);
+    if (T < 2) T = 2;
+    const double w_hi = 2.0 * L_hi_cap, w_lo = 1.0 * L_lo_cap;
+    int64_t r_hi = L_hi_cap ? (int64_t)llround((double)T * w_hi / (w_hi + w_lo)) : 0;
+    int64_t r_lo = L_lo_cap ? T - r_hi : 0;
+    auto clamp = [](int64_t r, int L) -> int64_t {
+        if (!L) return 0;
+        const int64_t max_s = ceil_div(L, 256);
+        return r < 1 ? 1 : (r > max_s ? max_s : r);
+    };
+    r_hi = clamp(r_hi, L_hi_cap);
+    r_lo = clamp(r_lo, L_lo_cap);
+    const int S_hi = L_hi_cap ? plan_splits(L_hi_cap, (int)r_hi).S : 0;
+    const int S_lo = L_lo_cap ? plan_splits(L_lo_cap, (int)r_lo).S : 0;
+    if (splits_hi) *splits_hi = S_hi;
+    if (splits_lo) *splits_lo = S_lo;
+    return S_hi + S_lo;
+}
+
+attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
+                              const int32_t* hi_lens, int L_hi_cap, const attn_tensor* k_lo,
+                              const attn_tensor* v_lo, const float* k_scale, const float* v_scale,
+                              const int32_t* lo_lens, int L_lo_cap, int B, int Hq, int Hkv, int d,
+                              float softmax_scale, int num_splits_hi, int num_splits_lo, attn_tensor* out,
+                              float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = 0;
+    attn_status st;
+    if ((st = check_tensor(q, "q", true)) || (st = check_tensor(out, "out", false))) return st;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d d=%d)", B, Hq, Hkv, d);
+    if (L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "span capacities must be >= 0 and not both 0 (%d, %d)", L_hi_cap,
+                    L_lo_cap);
+    if (B > 65535 || Hkv > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and Hkv must be <= 65535");
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (num_splits_hi < 0 || num_splits_lo < 0) return fail(ATTN_ERR_INVALID_ARG, "split counts must be >= 0");
+    if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (L_hi_cap) {
+        if ((st = check_tensor(k_hi, "k_hi", true)) || (st = check_tensor(v_hi, "v_hi", true))) return st;
+        if (k_hi->dtype != ATTN_BF16 || v_hi->dtype != ATTN_BF16)
+            return fail(ATTN_ERR_UNSUPPORTED, "the high-precision span must be bf16");
+    }
+    if (L_lo_cap) {
+        if ((st = check_tensor(k_lo, "k_lo", true)) || (st = check_tensor(v_lo, "v_lo", true))) return st;
+        if (k_lo->dtype != ATTN_FP8_E4M3 || v_lo->dtype != ATTN_FP8_E4M3)
+            return fail(ATTN_ERR_UNSUPPORTED, "the low-precision span must be fp8 e4m3");
+        if (!k_scale || !v_scale) return fail(ATTN_ERR_INVALID_ARG, "the fp8 span needs k_scale and v_scale");
+    }
+    if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode takes bf16 q and out");
+    if (d != 128 || Hq != 4 * Hkv)
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+
+    int auto_hi = 0, auto_lo = 0;
+    if ((!num_splits_hi && L_hi_cap) || (!num_splits_lo && L_lo_cap)) {
+        if (attn_decode_mixed_splits(B, Hkv, L_hi_cap, L_lo_cap, &auto_hi, &auto_lo) <= 0)
+            return fail(ATTN_ERR_HIP, "could not query the device for the split plan");
+    }
+    const Plan ph = L_hi_cap ? plan_splits(L_hi_cap, num_splits_hi ? num_splits_hi : auto_hi) : Plan{kChunkQuantum, 0};
+    const Plan plo = L_lo_cap ? plan_splits(L_lo_cap, num_splits_lo ? num_splits_lo : auto_lo) : Plan{kChunkQuantum, 0};
+    const int S = ph.S + plo.S;
+
+    // Workspace: [merge counters | o_part | m_part | l_part | block partials],
+    // the layout of attn_decode with S = S_hi + S_lo splits.
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
+    if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    const int64_t rows = (int64_t)B * Hq;
+    const size_t need = attn_decode_workspace_size(B, Hq, d, S);
+    if (workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need %zu for %d splits", workspace_bytes, need, S);
+    uint32_t* counters = static_cast<uint32_t*>(workspace);
+    float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn::kCounterBytes);
+    float* m_part = o_part + rows * S * d;
+    float* l_part = m_part + rows * S;
+    float* blk_o = l_part + rows * S;
+    float* blk_m = blk_o + rows * attn::kMaxTicketBlocks * d;
+    float* blk_l = blk_m + rows * attn::kMaxTicketBlocks;
+
+    const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+    attn::DecodeParams p{};
+    p.q = q->data;
+    p.q_sb = q->stride_b;
+    p.q_sh = q->stride_h;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.S = S;
+    p.S_hi = ph.S;
+    p.scale_log2 = sc * kLog2e;
+    p.o_part = o_part;
+    p.m_part = m_part;
+    p.l_part = l_part;
+    p.ticket_block = 1;
+    auto span = [&](const attn_tensor* k, const attn_tensor* v, const int32_t* lens, int L_cap, int chunk) {
+        attn::KvSpan sp{};
+        if (L_cap) {
+            sp.k = k->data;
+            sp.k_sb = k->stride_b;
+            sp.k_sh = k->stride_h;
+            sp.k_ss = k->stride_s;
+            sp.v = v->data;
+            sp.v_sb = v->stride_b;
+            sp.v_sh = v->stride_h;
+            sp.v_ss = v->stride_s;
+        }
+        sp.kv_lens = lens;  // [B, Hkv]: one length per (sequence, KV head)
+        sp.lens_sb = Hkv;
+        sp.lens_sh = 1;
+        sp.L_cap = L_cap;
+        sp.chunk = chunk;
+        return sp;
+    };
+    p.hi = span(k_hi, v_hi, hi_lens, L_hi_cap, ph.chunk);
+    p.lo = span(k_lo, v_lo, lo_lens, L_lo_cap, plo.chunk);
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const int cus = device_cu_count();
+    const int64_t wgs = (int64_t)B * Hkv * S;
+    const bool fused = (int64_t)B * Hkv <= attn::kMaxCounterGroups && S <= attn::kMaxFusedSplits && cus > 0 &&
+                       wgs <= 2LL * cus;
+    if (fused) {
+        p.counters = counters;
+        p.ticket_block = ticket_block_for(S);
+        p.blk_o = blk_o;
+        p.blk_m = blk_m;
+        p.blk_l = blk_l;
+        p.out = out->data;
+        p.out_sb = out->stride_b;
+        p.out_sh = out->stride_h;
+        p.lse = lse;
+    }
+    hipError_t e = attn::launch_decode_mfma_mixed(p, hs);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    if (fused) return ATTN_OK;
+
+    // every split publishes a partial (the identity when empty): merge all S
+    attn::CombineParams cp;
+    cp.o_part = o_part;
+    cp.m_part = m_part;
+    cp.l_part = l_part;
+    cp.R = (int)rows;
+    cp.S = S;
+    cp.d = d;
+    cp.Hq = Hq;
+    cp.kv_lens = nullptr;
+    cp.chunk = 1;
+    cp.L_cap = 0;
+    cp.out = out->data;
+    cp.out_dtype = out->dtype;
+    cp.out_sb = out->stride_b;
+    cp.out_sh = out->stride_h;
+    cp.lse = lse;
+    e = attn::launch_combine(cp, hs);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
     return ATTN_OK;
 }

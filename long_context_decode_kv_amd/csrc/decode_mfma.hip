@@ -315,10 +315,10 @@ __device__ __forceinline__ void merge4(const float* o, const float* m, const flo
 // ticket on the group; the last block merges the block partials into O and
 // lse. Counters are reset by their last user. The tree shape is a function of
 // n and the plan only, so results are deterministic.
-__device__ __forceinline__ void merge_group_if_last(const DecodeParams& p, int b, int g, int L_b, int tid) {
+__device__ __forceinline__ void merge_group_if_last(const DecodeParams& p, int b, int g, int n, int tid) {
     __shared__ int role;  // 0: done, 1: merged its block, not last; 2: final merger
     __shared__ MergeLds sm;
-    const int n = (L_b + p.chunk - 1) / p.chunk;  // splits this sequence uses
+    // n: the splits of this sequence that publish a partial
     const int s = blockIdx.x, k = p.ticket_block;
     const int nb = (n + k - 1) / k, bi = s / k;
     const int in_block = min(k, n - bi * k);
@@ -373,25 +373,48 @@ __device__ __forceinline__ void merge_group_if_last(const DecodeParams& p, int b
     if (p.lse && lane == 0) p.lse[row0 + h] = empty ? kNegInf : Mh + logf(Lh);
 }
 
-template <bool FP8, bool FUSED>
-__global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
-    const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+// LDS of one decode workgroup: the per-wave K staging buffers and the
+// cross-wave merge (level 1b).
+struct DecodeLds {
+    u32x4 kstage[kWaves][256];
+    float o[kWaves][4][128];
+    float m[kWaves][4];
+    float l[kWaves][4];
+};
+
+// One workgroup: split s of span `sp`, publishing partial s_out of its rows.
+// MIXED: every split of the launch publishes a partial (an empty one the
+// identity) and takes part in the fused merge, which covers all p.S of them.
+template <bool FP8, bool FUSED, bool MIXED>
+__device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& sp, int s, int s_out,
+                                          DecodeLds& lds) {
+    const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    int L_b = p.L_cap;
-    if (p.kv_lens) L_b = min(max(p.kv_lens[b], 0), p.L_cap);
-    const int t_begin = s * p.chunk;
-    const int t_end = min(t_begin + p.chunk, L_b);
+    int L_b = sp.L_cap;
+    if (sp.kv_lens) L_b = min(max(sp.kv_lens[b * sp.lens_sb + g * sp.lens_sh], 0), sp.L_cap);
+    const int t_begin = s * sp.chunk;
+    const int t_end = min(t_begin + sp.chunk, L_b);
+    const int n_merge = MIXED ? p.S : (L_b + sp.chunk - 1) / sp.chunk;
     if (t_begin >= t_end) {
         // A split past the end of a shorter sequence: the identity partial.
         for (int i = tid; i < 4 * 128; i += 256) {
             const int64_t row = (int64_t)b * p.Hq + g * 4 + i / 128;
-            p.o_part[(row * p.S + s) * 128 + i % 128] = 0.f;
-            if (i % 128 == 0) {
-                p.m_part[row * p.S + s] = kNegInf;
-                p.l_part[row * p.S + s] = 0.f;
+            if constexpr (FUSED && MIXED) {
+                st_agent(p.o_part + (row * p.S + s_out) * 128 + i % 128, 0.f);
+                if (i % 128 == 0) {
+                    st_agent(p.m_part + row * p.S + s_out, kNegInf);
+                    st_agent(p.l_part + row * p.S + s_out, 0.f);
+                }
+            } else {
+                p.o_part[(row * p.S + s_out) * 128 + i % 128] = 0.f;
+                if (i % 128 == 0) {
+                    p.m_part[row * p.S + s_out] = kNegInf;
+                    p.l_part[row * p.S + s_out] = 0.f;
+                }
             }
         }
-        if (FUSED && L_b == 0 && s == 0) {
+        if constexpr (FUSED && MIXED) merge_group_if_last(p, b, g, n_merge, tid);
+        if (FUSED && !MIXED && L_b == 0 && s == 0) {
             // an empty sequence: O = 0, lse = -inf (no workgroup of it merges)
             for (int i = tid; i < 4 * 128; i += 256) {
                 uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)(g * 4 + i / 128) * p.out_sh;
@@ -404,9 +427,9 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
     const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
 
     constexpr int esz = FP8 ? 1 : 2;
-    const char* kbase = static_cast<const char*>(p.k) + (b * p.k_sb + g * p.k_sh) * esz;
-    const char* vbase = static_cast<const char*>(p.v) + (b * p.v_sb + g * p.v_sh) * esz;
-    const int64_t kss = p.k_ss * esz, vss = p.v_ss * esz;
+    const char* kbase = static_cast<const char*>(sp.k) + (b * sp.k_sb + g * sp.k_sh) * esz;
+    const char* vbase = static_cast<const char*>(sp.v) + (b * sp.v_sb + g * sp.v_sh) * esz;
+    const int64_t kss = sp.k_ss * esz, vss = sp.v_ss * esz;
 
     // Q^T operand: column (lane & 15) is query head 4g + (lane & 3); its k-slots
     // follow the same dim order as the K operand.
@@ -433,8 +456,7 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
 
     // Two tile buffers used in turn: the next tile is in flight while the
     // current one is computed.
-    __shared__ u32x4 kstage[kWaves][256];
-    u32x4* ks = kstage[w];
+    u32x4* ks = lds.kstage[w];
     int k = w;
     if (k < ntiles) {
         Tile<FP8> ta, tb;
@@ -474,18 +496,15 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
     }
 
     // Level 1b: merge the four waves in LDS.
-    __shared__ float lds_o[kWaves][4][128];
-    __shared__ float lds_m[kWaves][4];
-    __shared__ float lds_l[kWaves][4];
     if (lane < 16) {
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lds_o[w][h][8 * lane + e] = o[h][e];
+            for (int e = 0; e < 8; ++e) lds.o[w][h][8 * lane + e] = o[h][e];
     }
     if (lane < 4) {
-        lds_m[w][lane] = M;
-        lds_l[w][lane] = lw;
+        lds.m[w][lane] = M;
+        lds.l[w][lane] = lw;
     }
     __syncthreads();
 
@@ -495,34 +514,54 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
     float Mx = kNegInf;
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) {
-        mw[i] = lds_m[i][h];
+        mw[i] = lds.m[i][h];
         Mx = fmaxf(Mx, mw[i]);
     }
 #pragma unroll
     for (int i = 0; i < kWaves; ++i) fw[i] = (mw[i] == kNegInf) ? 0.f : fast_exp2(mw[i] - Mx);
-    const float L = (fw[0] * lds_l[0][h] + fw[1] * lds_l[1][h]) + (fw[2] * lds_l[2][h] + fw[3] * lds_l[3][h]);
+    const float L = (fw[0] * lds.l[0][h] + fw[1] * lds.l[1][h]) + (fw[2] * lds.l[2][h] + fw[3] * lds.l[3][h]);
     f32x2 out;
 #pragma unroll
     for (int cc = 0; cc < 2; ++cc) {
-        const float v = (fw[0] * lds_o[0][h][c + cc] + fw[1] * lds_o[1][h][c + cc]) +
-                        (fw[2] * lds_o[2][h][c + cc] + fw[3] * lds_o[3][h][c + cc]);
+        const float v = (fw[0] * lds.o[0][h][c + cc] + fw[1] * lds.o[1][h][c + cc]) +
+                        (fw[2] * lds.o[2][h][c + cc] + fw[3] * lds.o[3][h][c + cc]);
         out[cc] = v * vsc;
     }
     const int64_t row = (int64_t)b * p.Hq + g * 4 + h;
     if constexpr (FUSED) {
-        st_agent2(p.o_part + (row * p.S + s) * 128 + c, out);
+        st_agent2(p.o_part + (row * p.S + s_out) * 128 + c, out);
         if ((tid & 63) == 0) {
-            st_agent(p.m_part + row * p.S + s, Mx * kLn2);
-            st_agent(p.l_part + row * p.S + s, L);
+            st_agent(p.m_part + row * p.S + s_out, Mx * kLn2);
+            st_agent(p.l_part + row * p.S + s_out, L);
         }
-        merge_group_if_last(p, b, g, L_b, tid);
+        merge_group_if_last(p, b, g, n_merge, tid);
     } else {
-        *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s) * 128 + c) = out;
+        *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s_out) * 128 + c) = out;
         if ((tid & 63) == 0) {
-            p.m_part[row * p.S + s] = Mx * kLn2;
-            p.l_part[row * p.S + s] = L;
+            p.m_part[row * p.S + s_out] = Mx * kLn2;
+            p.l_part[row * p.S + s_out] = L;
         }
     }
+}
+
+__device__ __forceinline__ KvSpan main_span(const DecodeParams& p) {
+    return KvSpan{p.k, p.k_sb, p.k_sh, p.k_ss, p.v, p.v_sb, p.v_sh, p.v_ss, p.kv_lens, 1, 0, p.L_cap, p.chunk};
+}
+
+template <bool FP8, bool FUSED>
+__global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
+    __shared__ DecodeLds lds;
+    decode_wg<FP8, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
+}
+
+// Mixed-precision cache: splits [0, S_hi) stream the bf16 span, the others the
+// fp8 span; one merge over all splits.
+template <bool FUSED>
+__global__ __launch_bounds__(256) void decode_gqa4_d128_mixed(DecodeParams p) {
+    __shared__ DecodeLds lds;  // one copy for both branches
+    const int s = blockIdx.x;
+    if (s < p.S_hi) decode_wg<false, FUSED, true>(p, p.hi, s, s, lds);
+    else decode_wg<true, FUSED, true>(p, p.lo, s - p.S_hi, s, lds);
 }
 
 }  // namespace
@@ -537,6 +576,13 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t s
         if (fused) hipLaunchKernelGGL((decode_gqa4_d128<false, true>), grid, dim3(256), 0, stream, p);
         else hipLaunchKernelGGL((decode_gqa4_d128<false, false>), grid, dim3(256), 0, stream, p);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma_mixed(const DecodeParams& p, hipStream_t stream) {
+    dim3 grid(p.S, p.Hkv, p.B);
+    if (p.counters) hipLaunchKernelGGL((decode_gqa4_d128_mixed<true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_gqa4_d128_mixed<false>), grid, dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

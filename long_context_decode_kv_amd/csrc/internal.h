@@ -9,6 +9,20 @@ namespace attn {
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
+// One span of a KV cache: [B, Hkv, L_cap, d] K and V with element strides,
+// valid lengths kv_lens[b*lens_sb + g*lens_sh] (or nullptr: all L_cap), cut
+// into splits of `chunk` keys.
+struct KvSpan {
+    const void* k;
+    int64_t k_sb, k_sh, k_ss;
+    const void* v;
+    int64_t v_sb, v_sh, v_ss;
+    const int32_t* kv_lens;
+    int lens_sb, lens_sh;
+    int L_cap;
+    int chunk;
+};
+
 // One split-KV decode launch: grid (S, Hkv, B); workgroup (s, g, b) owns keys
 // [s*chunk, min((s+1)*chunk, L_b)) of KV head g of sequence b and writes one
 // partial (o, m, l) for each of the G query heads of that group.
@@ -40,6 +54,12 @@ struct DecodeParams {
     void* out;           // [B, Hq, 1, d] bf16
     int64_t out_sb, out_sh;
     float* lse;          // [B*Hq] or nullptr
+    // Mixed precision (decode_mfma_mixed only; k, v, kv_lens, L_cap and chunk
+    // above are then unused): splits [0, S_hi) read the bf16 span `hi`, splits
+    // [S_hi, S) the fp8 span `lo` (with k_scale and v_scale); all S partials of
+    // a row are merged.
+    int S_hi;
+    KvSpan hi, lo;
 };
 
 // Bytes at the start of a decode workspace reserved for the fused-merge
@@ -87,6 +107,7 @@ struct PrefillParams {
 };
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream);
+hipError_t launch_decode_mfma_mixed(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int q_dtype, int kv_dtype, int G, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // Zeroes `bytes` (a multiple of 16) at 16-byte aligned device address `p`.

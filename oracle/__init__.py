@@ -19,8 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-F32, BF16, E4M3 = 0, 1, 2
-_DTYPE_OF_NUMPY = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): E4M3}
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
+_DTYPE_OF_NUMPY = {np.dtype(np.float32): F32, np.dtype(np.uint16): BF16, np.dtype(np.uint8): E4M3,
+                   np.dtype(np.float64): F64}
 
 
 def build():
@@ -55,6 +56,8 @@ def _load():
     lib.oracle_bf16_to_f64.restype = dbl
     lib.oracle_e4m3_to_f64.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_to_f64.restype = dbl
+    lib.oracle_decode_elems.argtypes = [vp, i32, i64, vp]
+    lib.oracle_decode_elems.restype = None
     _lib = lib
     return lib
 
@@ -71,8 +74,8 @@ class Problem:
     """Inputs of one attention call, exactly as stored for the GPU.
 
     q: [B,Hq,Lq,d] float32 / uint16 (bf16 bits); k, v: [B,Hkv,Lcap,d] float32 /
-    uint16 (bf16) / uint8 (e4m3 codes); k_scale, v_scale: float32 [B*Hkv] for
-    e4m3; kv_lens: int32 [B] or None.
+    uint16 (bf16) / uint8 (e4m3 codes) / float64 (values already decoded);
+    k_scale, v_scale: float32 [B*Hkv] for e4m3; kv_lens: int32 [B] or None.
     """
 
     def __init__(self, q, k, v, k_scale=None, v_scale=None, kv_lens=None, scale=None, causal=False):
@@ -181,3 +184,65 @@ def e4m3_to_f64(codes):
     lib = _load()
     codes = np.asarray(codes, dtype=np.uint8)
     return np.array([lib.oracle_e4m3_to_f64(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def decode_elems(a):
+    """Real values (float64) of stored elements: float32, bf16 bits (uint16),
+    e4m3 codes (uint8) or float64, with no scale applied."""
+    lib = _load()
+    a = np.ascontiguousarray(a)
+    out = np.empty(a.shape, dtype=np.float64)
+    if a.size:
+        lib.oracle_decode_elems(_p(a), _DTYPE_OF_NUMPY[a.dtype], a.size, _p(out))
+    return out
+
+
+def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_lens=None, scale=None,
+                 heads=None):
+    """Single-query decode over a cache kept in two precisions.
+
+    q [B,Hq,1,d] (bf16 bits or float32); k_hi, v_hi [B,Hkv,L_hi,d] bf16 bits
+    (or None: no such keys); k_lo, v_lo [B,Hkv,L_lo,d] e4m3 codes (or None)
+    with k_scale, v_scale float32 [B*Hkv]; hi_lens, lo_lens int32 [B*Hkv]
+    (valid keys per (sequence, KV head), clamped to the capacity) or None =
+    the capacity. Each query head sees the union of its group's valid bf16
+    keys and valid fp8 keys (the latter at code * scale): the union is built in
+    float64 and handed to the plain attention above. `heads` lists flat query
+    heads b*Hq + h (all when None). Returns (out [n,d], lse [n]) in float64.
+    """
+    q = np.ascontiguousarray(q)
+    B, Hq, Lq, d = q.shape
+    assert Lq == 1
+    Hkv = (k_hi if k_hi is not None else k_lo).shape[1]
+    G = Hq // Hkv
+    L_hi = 0 if k_hi is None else k_hi.shape[2]
+    L_lo = 0 if k_lo is None else k_lo.shape[2]
+    hl = np.full(B * Hkv, L_hi, np.int64) if hi_lens is None else np.clip(np.asarray(hi_lens).ravel(), 0, L_hi)
+    ll = np.full(B * Hkv, L_lo, np.int64) if lo_lens is None else np.clip(np.asarray(lo_lens).ravel(), 0, L_lo)
+    ks = None if k_scale is None else np.asarray(k_scale, np.float32).ravel()
+    vs = None if v_scale is None else np.asarray(v_scale, np.float32).ravel()
+    heads = np.arange(B * Hq) if heads is None else np.asarray(heads).ravel()
+    out = np.zeros((heads.size, d), np.float64)
+    lse = np.zeros(heads.size, np.float64)
+    by_group = {}
+    for i, r in enumerate(heads):
+        by_group.setdefault((int(r) // Hq, (int(r) % Hq) // G), []).append((i, int(r) % Hq))
+    for (b, g), items in by_group.items():
+        bg = b * Hkv + g
+        kparts, vparts = [], []
+        if hl[bg]:
+            kparts.append(decode_elems(k_hi[b, g, :hl[bg]]))
+            vparts.append(decode_elems(v_hi[b, g, :hl[bg]]))
+        if ll[bg]:
+            kparts.append(decode_elems(k_lo[b, g, :ll[bg]]) * np.float64(ks[bg]))
+            vparts.append(decode_elems(v_lo[b, g, :ll[bg]]) * np.float64(vs[bg]))
+        n = int(hl[bg] + ll[bg])
+        kk = np.concatenate(kparts) if n else np.zeros((1, d))
+        vv = np.concatenate(vparts) if n else np.zeros((1, d))
+        prob = Problem(q[b:b + 1, g * G:(g + 1) * G], kk[None, None], vv[None, None],
+                       kv_lens=np.array([n], np.int32), scale=scale)
+        o, l_ = attention(prob, rows=[h - g * G for _, h in items])
+        for j, (i, _) in enumerate(items):
+            out[i] = o[j]
+            lse[i] = l_[j]
+    return out, lse

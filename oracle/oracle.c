@@ -32,6 +32,14 @@
  *  finalise: O = o / l, lse = m + ln l;
  *  energy F(zeta) = ln sum_J exp(s_j + zeta . v_j), so F(0) = lse and the
  *  gradient of F at 0 is O.
+ *
+ * A cache kept in two precisions (the ThriftAttention page: its introduction
+ * gives each token or head a precision, its Physical AI Stack section keeps
+ * the first and last tenth of the tokens in bf16) is, for one query, plain
+ * attention over the union of the two key sets at their real values: the
+ * Python side decodes both spans with oracle_decode_elems, multiplies the fp8
+ * span by its scale in double, concatenates them, and calls oracle_attention
+ * with OR_F64 keys and values.
  */
 #include <math.h>
 #include <pthread.h>
@@ -42,6 +50,7 @@
 #define OR_F32 0
 #define OR_BF16 1
 #define OR_E4M3 2
+#define OR_F64 3 /* already-decoded values, e.g. the union of two cache spans */
 
 /* bf16: the upper 16 bits of an IEEE-754 binary32. */
 double oracle_bf16_to_f64(uint16_t bits) {
@@ -84,8 +93,14 @@ static double elem(const void* base, int dtype, int64_t idx) {
     case OR_F32: return (double)((const float*)base)[idx];
     case OR_BF16: return oracle_bf16_to_f64(((const uint16_t*)base)[idx]);
     case OR_E4M3: return oracle_e4m3_to_f64(((const uint8_t*)base)[idx]);
+    case OR_F64: return ((const double*)base)[idx];
     default: return NAN;
     }
+}
+
+/* The real values of n stored elements (no scale applied). */
+void oracle_decode_elems(const void* src, int dtype, int64_t n, double* dst) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = elem(src, dtype, i);
 }
 
 /* Decoded key or value row j of (b, g), multiplied by its fp8 scale if any. */

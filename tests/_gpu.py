@@ -69,3 +69,23 @@ def assert_lse_close(got, ref, tol):
     assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "-inf lse differs"
     if fin.any():
         assert np.abs(got[fin] - ref[fin]).max() <= tol, np.abs(got[fin] - ref[fin]).max()
+
+
+def mixed_on_gpu(inp, num_splits_hi=0, num_splits_lo=0, dev=None, softmax_scale=0.0):
+    import long_context_decode_kv_amd as lib
+    dev = dev or {k: to_dev(v) for k, v in inp.items()}
+    out, lse = lib.attn_decode_mixed(dev["q"], dev["k_hi"], dev["v_hi"], dev["k_lo"], dev["v_lo"],
+                                     k_scale=dev["k_scale"], v_scale=dev["v_scale"], hi_lens=dev["hi_lens"],
+                                     lo_lens=dev["lo_lens"], softmax_scale=softmax_scale,
+                                     num_splits_hi=num_splits_hi, num_splits_lo=num_splits_lo)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_mixed(inp, heads=None, scale=None):
+    out, lse = oracle.decode_mixed(inp["q"], inp["k_hi"], inp["v_hi"], inp["k_lo"], inp["v_lo"], inp["k_scale"],
+                                   inp["v_scale"], inp["hi_lens"], inp["lo_lens"], scale=scale, heads=heads)
+    if heads is not None:
+        return out, lse
+    B, Hq = inp["q"].shape[:2]
+    return out.reshape(B, Hq, -1), lse.reshape(B, Hq)

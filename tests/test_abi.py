@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(so):
     names = declared_functions()
     assert set(names) == {"attn_status_string", "attn_last_error", "attn_decode_auto_splits",
                           "attn_decode_workspace_size", "attn_decode_workspace_init", "attn_decode_plan",
-                          "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials"}
+                          "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials",
+                          "attn_decode_mixed", "attn_decode_mixed_splits"}
     nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
     for n in names:
@@ -139,3 +140,36 @@ def test_combine_argument_errors(so):
     assert so.attn_combine_partials(FAKE, FAKE, FAKE, 0, 2, 128, ctypes.byref(out), None, None) == INVALID
     bad = T(FP8, 0, 0, 128)
     assert so.attn_combine_partials(FAKE, FAKE, FAKE, 4, 2, 128, ctypes.byref(bad), None, None) == UNSUPPORTED
+
+
+def mixed(so, q=None, khi=None, klo=None, ks=FAKE, vs=FAKE, B=1, Hq=8, Hkv=2, d=128, L_hi=256, L_lo=1024, S_hi=2,
+          S_lo=4, out=None, ws=FAKE, ws_bytes=1 << 30, no_hi=False):
+    q = q or T(BF16, Hq * d, d, d)
+    khi = None if no_hi else (khi or T(BF16, Hkv * L_hi * d, L_hi * d, d))
+    klo = klo or T(FP8, Hkv * L_lo * d, L_lo * d, d)
+    out = out or T(BF16, Hq * d, d, d)
+    ref = lambda t: None if t is None else ctypes.byref(t)
+    return so.attn_decode_mixed(ctypes.byref(q), ref(khi), ref(khi), None, L_hi, ref(klo), ref(klo), ks, vs, None,
+                                L_lo, B, Hq, Hkv, d, 0.0, S_hi, S_lo, ctypes.byref(out), None, ws, ws_bytes, None)
+
+
+def test_mixed_decode_argument_errors(so):
+    assert mixed(so, L_hi=0, L_lo=0) == INVALID
+    assert mixed(so, L_hi=-1) == INVALID
+    assert mixed(so, S_hi=-1) == INVALID
+    assert mixed(so, ks=None) == INVALID  # the fp8 span needs its scales
+    assert mixed(so, khi=T(FP8, 2 * 256 * 128, 256 * 128, 128)) == UNSUPPORTED  # bf16 span holds fp8
+    assert mixed(so, klo=T(BF16, 2 * 1024 * 128, 1024 * 128, 128)) == UNSUPPORTED  # fp8 span holds bf16
+    assert mixed(so, Hq=16, Hkv=2) == UNSUPPORTED  # 8 query heads per KV head
+    assert mixed(so, d=64) == UNSUPPORTED
+    assert mixed(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
+    assert mixed(so, Hq=6, Hkv=4) == INVALID
+    assert mixed(so, ws=None) == WORKSPACE
+    # 2 + 4 splits: counters, then (d + 2) floats per split and per block partial
+    need = (4 << 20) + 8 * 6 * 130 * 4 + 8 * 16 * 130 * 4
+    assert lib.attn_decode_workspace_size(1, 8, 128, 6) == need
+    assert mixed(so, ws_bytes=need - 1) == WORKSPACE
+    assert "6 splits" in lib.load_library().attn_last_error().decode()
+    # an empty span may come without tensors
+    assert mixed(so, L_hi=0, S_hi=0, no_hi=True, ws=None) == WORKSPACE  # validation reaches the workspace check
+    assert mixed(so, L_hi=16, no_hi=True) == INVALID

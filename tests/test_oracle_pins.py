@@ -360,3 +360,106 @@ def test_e4m3_inputs_apply_their_scale():
         o_ref, l_ref = brute_row(q[0, h, 0], kd[0, 0], vd[0, 0], 1 / math.sqrt(d))
         np.testing.assert_allclose(out[0, h, 0], o_ref, rtol=1e-12, atol=1e-14)
         assert abs(lse[0, h, 0] - l_ref) < 1e-12
+
+
+# ------------------------------------------------ two-precision cache (union)
+# A cache that keeps some keys in bf16 and the rest in fp8 (the ThriftAttention
+# page, introduction and Physical AI Stack section) is, for one query, exact
+# attention over the union of both key sets at their real values.
+
+def _bits(t):
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def _mixed_case(B, Hq, Hkv, L_hi, L_lo, d, seed):
+    g = torch.Generator().manual_seed(seed)
+    tq = torch.randn(B, Hq, 1, d, generator=g).to(torch.bfloat16)
+    khi = torch.randn(B, Hkv, L_hi, d, generator=g).to(torch.bfloat16)
+    vhi = torch.randn(B, Hkv, L_hi, d, generator=g).to(torch.bfloat16)
+    klo = (torch.randn(B, Hkv, L_lo, d, generator=g) * 40).to(torch.float8_e4m3fn)
+    vlo = (torch.randn(B, Hkv, L_lo, d, generator=g) * 40).to(torch.float8_e4m3fn)
+    ks = (torch.rand(B * Hkv, generator=g) * 0.05 + 0.01).numpy().astype(np.float32)
+    vs = (torch.rand(B * Hkv, generator=g) * 0.05 + 0.01).numpy().astype(np.float32)
+    return tq, khi, vhi, klo, vlo, ks, vs
+
+
+def test_mixed_matches_bruteforce_over_the_union():
+    B, Hq, Hkv, L_hi, L_lo, d = 2, 4, 2, 6, 9, 8
+    tq, khi, vhi, klo, vlo, ks, vs = _mixed_case(B, Hq, Hkv, L_hi, L_lo, d, 7)
+    hl = np.array([6, 0, 3, 5], np.int32)  # per (sequence, KV head); one head has no bf16 key
+    ll = np.array([9, 4, 0, 2], np.int32)  # and one no fp8 key
+    out, lse = oracle.decode_mixed(_bits(tq), _bits(khi), _bits(vhi), klo.view(torch.uint8).numpy(),
+                                   vlo.view(torch.uint8).numpy(), ks, vs, hl, ll)
+    qd = tq.to(torch.float64).numpy()
+    khd, vhd = khi.to(torch.float64).numpy(), vhi.to(torch.float64).numpy()
+    kld, vld = klo.to(torch.float64).numpy(), vlo.to(torch.float64).numpy()
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            bg = b * Hkv + h // G
+            krows = list(khd[b, h // G, :hl[bg]]) + list(kld[b, h // G, :ll[bg]] * float(ks[bg]))
+            vrows = list(vhd[b, h // G, :hl[bg]]) + list(vld[b, h // G, :ll[bg]] * float(vs[bg]))
+            o_ref, l_ref = brute_row(qd[b, h, 0], krows, vrows, 1 / math.sqrt(d))
+            np.testing.assert_allclose(out[b * Hq + h], o_ref, rtol=1e-12, atol=1e-14)
+            assert abs(lse[b * Hq + h] - l_ref) < 1e-12
+
+
+def test_mixed_with_no_fp8_keys_is_the_bf16_decode():
+    B, Hq, Hkv, L_hi, L_lo, d = 3, 8, 2, 40, 16, 16
+    tq, khi, vhi, klo, vlo, ks, vs = _mixed_case(B, Hq, Hkv, L_hi, L_lo, d, 8)
+    lens = np.array([40, 17, 1], np.int32)
+    out, lse = oracle.decode_mixed(_bits(tq), _bits(khi), _bits(vhi), klo.view(torch.uint8).numpy(),
+                                   vlo.view(torch.uint8).numpy(), ks, vs, np.repeat(lens, Hkv),
+                                   np.zeros(B * Hkv, np.int32))
+    ref, ref_lse = oracle.attention(oracle.Problem(_bits(tq), _bits(khi), _bits(vhi), kv_lens=lens))
+    np.testing.assert_array_equal(out, ref)
+    np.testing.assert_array_equal(lse, ref_lse)
+
+
+def test_mixed_with_no_bf16_keys_is_the_fp8_decode():
+    B, Hq, Hkv, L_hi, L_lo, d = 2, 8, 2, 8, 50, 16
+    tq, khi, vhi, klo, vlo, ks, vs = _mixed_case(B, Hq, Hkv, L_hi, L_lo, d, 9)
+    kc, vc = klo.view(torch.uint8).numpy(), vlo.view(torch.uint8).numpy()
+    out, lse = oracle.decode_mixed(_bits(tq), None, None, kc, vc, ks, vs, None, None)
+    ref, ref_lse = oracle.attention(oracle.Problem(_bits(tq), kc, vc, k_scale=ks, v_scale=vs))
+    np.testing.assert_array_equal(out, ref)
+    np.testing.assert_array_equal(lse, ref_lse)
+
+
+def test_mixed_does_not_depend_on_which_span_holds_a_key():
+    # fp8 values times a power-of-two scale are exact bf16 values, so any key can
+    # move between the spans without changing its real value; the result may
+    # only move by rounding.
+    B, Hq, Hkv, L, d = 1, 4, 1, 24, 8
+    g = torch.Generator().manual_seed(10)
+    tq = torch.randn(B, Hq, 1, d, generator=g).to(torch.bfloat16)
+    kf = (torch.randn(B, Hkv, L, d, generator=g) * 30).to(torch.float8_e4m3fn)
+    vf = (torch.randn(B, Hkv, L, d, generator=g) * 30).to(torch.float8_e4m3fn)
+    ks, vs = np.array([2.0 ** -4], np.float32), np.array([2.0 ** -3], np.float32)
+    kb = (kf.to(torch.float32) * float(ks[0])).to(torch.bfloat16)
+    vb = (vf.to(torch.float32) * float(vs[0])).to(torch.bfloat16)
+    kc, vc = kf.view(torch.uint8).numpy(), vf.view(torch.uint8).numpy()
+    ref, ref_lse = oracle.decode_mixed(_bits(tq), _bits(kb), _bits(vb), None, None, None, None)
+    for cut in (0, 5, 13, 24):
+        # keys [cut, L) stored in bf16 first, keys [0, cut) in fp8
+        out, lse = oracle.decode_mixed(_bits(tq), _bits(kb[:, :, cut:]), _bits(vb[:, :, cut:]), kc[:, :, :cut],
+                                       vc[:, :, :cut], ks, vs)
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
+
+
+def test_mixed_with_no_key_at_all_is_empty():
+    tq, khi, vhi, klo, vlo, ks, vs = _mixed_case(1, 4, 1, 4, 4, 8, 11)
+    out, lse = oracle.decode_mixed(_bits(tq), _bits(khi), _bits(vhi), klo.view(torch.uint8).numpy(),
+                                   vlo.view(torch.uint8).numpy(), ks, vs, np.zeros(1, np.int32),
+                                   np.zeros(1, np.int32))
+    assert np.all(out == 0) and np.all(np.isneginf(lse))
+
+
+def test_f64_inputs_are_taken_as_given():
+    B, Hq, Hkv, L, d = 1, 2, 1, 7, 8
+    q, k, v = rand_f32(B, Hq, 1, d), rand_f32(B, Hkv, L, d), rand_f32(B, Hkv, L, d)
+    out32, lse32 = oracle.attention(oracle.Problem(q, k, v))
+    out64, lse64 = oracle.attention(oracle.Problem(q, k.astype(np.float64), v.astype(np.float64)))
+    np.testing.assert_array_equal(out32, out64)
+    np.testing.assert_array_equal(lse32, lse64)
