@@ -387,12 +387,15 @@ int attn_decode_mixed_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* sp
     if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0) return 0;
     const int cus = device_cu_count();
     if (cus <= 0) return 0;
-    // Two resident workgroups per compute unit in all, shared between the spans
-    // in proportion to their bytes (2 per bf16 key and value element, 1 per
-    // fp8 one), every split at least 256 keys long.
+    // Two resident workgroups per compute unit in all (so the merge is fused),
+    // shared between the spans in proportion to their cost per key: 2 for bf16
+    // (bytes per element) and 1.3 for fp8, whose workgroups convert and
+    // multiply twice the keys per byte and stream about 1.3x slower per byte.
+    // (128K keys, 20% bf16, 8 KV heads: 18 + 46 splits take 60.8 us, the
+    // bytes-proportional 21 + 43 take 63.7 us.) No split shorter than 256 keys.
     int64_t T = (2LL * cus) / ((int64_t)B * Hkv);
     if (T < 2) T = 2;
-    const double w_hi = 2.0 * L_hi_cap, w_lo = 1.0 * L_lo_cap;
+    const double w_hi = 2.0 * L_hi_cap, w_lo = 1.3 * L_lo_cap;
     int64_t r_hi = L_hi_cap ? (int64_t)llround((double)T * w_hi / (w_hi + w_lo)) : 0;
     int64_t r_lo = L_lo_cap ? T - r_hi : 0;
     auto clamp = [](int64_t r, int L) -> int64_t {
