@@ -44,6 +44,8 @@ def _load():
     common = [vp, i32, vp, vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, i32, dbl, i32]
     lib.oracle_attention.argtypes = common + [vp, i64, vp, vp, i32]
     lib.oracle_attention.restype = i32
+    lib.oracle_pi_attention.argtypes = common + [i32, i32, vp, vp, i64, vp, vp, i32]
+    lib.oracle_pi_attention.restype = i32
     lib.oracle_partial.argtypes = common + [i32, i32, i32, i64, i64, vp, vp, vp]
     lib.oracle_partial.restype = i32
     lib.oracle_energy.argtypes = common + [i32, i32, i32, vp]
@@ -114,6 +116,29 @@ def attention(prob, rows=None, nthreads=None):
     rc = lib.oracle_attention(*prob._common(), _p(rows_arr), n, _p(out), _p(lse), nthreads or _threads())
     if rc != 0:
         raise ValueError("oracle_attention: bad arguments")
+    return out, lse
+
+
+def pi_attention(prob, window, period, alpha=None, rows=None, nthreads=None):
+    """pi-Attention: the ring-local window, the period-pi skip keys and the
+    log-prior alpha (float32 [B, Hq, Lq] or None), as defined in oracle.c.
+    Returns (out [nrows, d], lse [nrows]) like attention()."""
+    lib = _load()
+    if rows is None:
+        n = prob.B * prob.Hq * prob.Lq
+        rows_arr = None
+    else:
+        rows_arr = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows_arr.size
+    a = None if alpha is None else np.ascontiguousarray(alpha, dtype=np.float32).ravel()
+    if a is not None and a.size != prob.B * prob.Hq * prob.Lq:
+        raise ValueError("alpha needs one value per (batch, query head, query)")
+    out = np.zeros((n, prob.d), dtype=np.float64)
+    lse = np.zeros(n, dtype=np.float64)
+    rc = lib.oracle_pi_attention(*prob._common(), int(window), int(period), _p(a), _p(rows_arr), n, _p(out),
+                                 _p(lse), nthreads or _threads())
+    if rc != 0:
+        raise ValueError("oracle_pi_attention: bad arguments")
     return out, lse
 
 

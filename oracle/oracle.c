@@ -86,6 +86,10 @@ typedef struct {
     int B, Hq, Hkv, Lq, Lcap, d;
     double scale;
     int causal;
+    /* pi-Attention mask (pi_mask != 0): window, period, prior (see below) */
+    int pi_mask;
+    int window, period;
+    const float* alpha;
 } problem;
 
 static double elem(const void* base, int dtype, int64_t idx) {
@@ -167,6 +171,69 @@ static void attend_row(const problem* p, int b, int h, int i, double* s, double*
     *lse = mx + log(z);
 }
 
+/*
+ * pi-Attention's key set and log-prior for row (b, h, i) (the pi-Attention
+ * explainer, method section A: a ring-local neighbourhood of k tokens on either
+ * side, skip links to tokens a whole number of periods pi away -- past only
+ * when causal -- and an adaptive gate alpha that enters the one softmax as a
+ * log-prior). The query sits at pos = n - Lq + i. Key j is
+ *   local  if |pos - j| <= window (and j <= pos when causal),
+ *   skip   if not local, period > 0, (pos - j) is a multiple of period
+ *          (and j < pos when causal),
+ *   absent otherwise.
+ * With alpha (clamped to [0, 1], one per row [B, Hq, Lq]) the logits of local
+ * keys get + ln(alpha) and those of skip keys + ln(1 - alpha); without it no
+ * prior is added. Returns 0 (absent), 1 (local) or 2 (skip).
+ */
+static int pi_class(const problem* p, int64_t pos, int64_t j) {
+    int64_t dist = pos - j;
+    if (p->causal && dist < 0) return 0;
+    if ((dist < 0 ? -dist : dist) <= p->window) return 1;
+    if (p->period > 0 && dist % p->period == 0) return 2;
+    return 0;
+}
+
+static void attend_row_pi(const problem* p, int b, int h, int i, double* s, double* tmp, double* qd, double* out,
+                          double* lse) {
+    int g = h / (p->Hq / p->Hkv);
+    int64_t n = seq_len(p, b), pos = n - p->Lq + i;
+    double bias_local = 0.0, bias_skip = 0.0;
+    if (p->alpha) {
+        double a = (double)p->alpha[((int64_t)b * p->Hq + h) * p->Lq + i];
+        if (!(a >= 0.0)) a = 0.0; /* NaN or negative */
+        if (a > 1.0) a = 1.0;
+        bias_local = log(a);
+        bias_skip = log(1.0 - a);
+    }
+    for (int c = 0; c < p->d; ++c) out[c] = 0.0;
+    load_q_row(p, b, h, i, qd);
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+        int cls = pi_class(p, pos, j);
+        if (!cls) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        load_kv_row(p, p->k, p->k_scale, b, g, j, tmp);
+        s[j] = score(p, qd, tmp) + (cls == 1 ? bias_local : bias_skip);
+        if (s[j] > mx) mx = s[j];
+    }
+    if (mx == -INFINITY) { /* no key, or every key weighted zero by the prior */
+        *lse = -INFINITY;
+        return;
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+        if (s[j] == -INFINITY) continue;
+        double w = exp(s[j] - mx);
+        z += w;
+        load_kv_row(p, p->v, p->v_scale, b, g, j, tmp);
+        for (int c = 0; c < p->d; ++c) out[c] += w * tmp[c];
+    }
+    for (int c = 0; c < p->d; ++c) out[c] /= z;
+    *lse = mx + log(z);
+}
+
 typedef struct {
     const problem* p;
     const int64_t* rows;
@@ -187,7 +254,8 @@ static void* row_worker(void* arg) {
         int i = (int)(flat % p->Lq);
         int h = (int)((flat / p->Lq) % p->Hq);
         int b = (int)(flat / ((int64_t)p->Lq * p->Hq));
-        attend_row(p, b, h, i, s, tmp, qd, j->out + r * p->d, j->lse + r);
+        if (p->pi_mask) attend_row_pi(p, b, h, i, s, tmp, qd, j->out + r * p->d, j->lse + r);
+        else attend_row(p, b, h, i, s, tmp, qd, j->out + r * p->d, j->lse + r);
     }
     free(s);
     free(tmp);
@@ -202,6 +270,8 @@ static int check_problem(const problem* p) {
     return 0;
 }
 
+static int run_rows(const problem* pp, const int64_t* rows, int64_t nrows, double* out, double* lse, int nthreads);
+
 /*
  * Exact attention for the listed rows (flat row id r = (b*Hq + h)*Lq + i), or for
  * every row when rows == NULL. Layouts are contiguous: q [B,Hq,Lq,d],
@@ -213,8 +283,29 @@ int oracle_attention(const void* q, int q_dtype, const void* k, const void* v, i
                      int Lq, int Lcap, int d, double scale, int causal, const int64_t* rows, int64_t nrows,
                      double* out, double* lse, int nthreads) {
     problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, kv_lens, B, Hq, Hkv, Lq, Lcap, d, scale, causal};
+    return run_rows(&p, rows, nrows, out, lse, nthreads);
+}
+
+/*
+ * pi-Attention (see pi_class above) for the listed rows, or every row when
+ * rows == NULL; arguments as oracle_attention plus window >= 0, period >= 0
+ * (0: no skip links) and alpha (float [B, Hq, Lq] or NULL).
+ */
+int oracle_pi_attention(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                        const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv,
+                        int Lq, int Lcap, int d, double scale, int causal, int window, int period,
+                        const float* alpha, const int64_t* rows, int64_t nrows, double* out, double* lse,
+                        int nthreads) {
+    problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, kv_lens, B, Hq, Hkv, Lq, Lcap, d, scale, causal,
+                 1, window, period, alpha};
+    if (window < 0 || period < 0) return 1;
+    return run_rows(&p, rows, nrows, out, lse, nthreads);
+}
+
+static int run_rows(const problem* pp, const int64_t* rows, int64_t nrows, double* out, double* lse, int nthreads) {
+    problem p = *pp;
     if (check_problem(&p)) return 1;
-    if (!rows) nrows = (int64_t)B * Hq * Lq;
+    if (!rows) nrows = (int64_t)p.B * p.Hq * p.Lq;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
     if (nthreads > nrows) nthreads = (int)(nrows > 0 ? nrows : 1);

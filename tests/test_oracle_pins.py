@@ -463,3 +463,132 @@ def test_f64_inputs_are_taken_as_given():
     out64, lse64 = oracle.attention(oracle.Problem(q, k.astype(np.float64), v.astype(np.float64)))
     np.testing.assert_array_equal(out32, out64)
     np.testing.assert_array_equal(lse32, lse64)
+
+
+# ------------------------------------------------------------- pi-Attention
+# The pi-Attention explainer (method section A): a ring-local window of k
+# tokens on either side, skip keys a whole number of periods pi away (past
+# only when causal), and a gate alpha used as a log-prior in the one softmax.
+
+def _pi_keys(pos, n, window, period, causal):
+    """Local and skip key lists written out with ranges (not the oracle's
+    modular test)."""
+    hi_local = pos if causal else min(n - 1, pos + window)
+    local = list(range(max(0, pos - window), hi_local + 1)) if pos >= 0 else []
+    skip = []
+    if period > 0:
+        skip = [j for j in range(pos - period, -1, -period) if j < pos - window]
+        if not causal:
+            skip += [j for j in range(pos + period, n, period) if j > pos + window]
+    return [j for j in local if 0 <= j < n], skip
+
+
+def _brute_biased(qrow, keys, vals, biases, scale):
+    s = [scale * math.fsum(float(a) * float(b) for a, b in zip(qrow, k)) + bb for k, bb in zip(keys, biases)]
+    fin = [x for x in s if x != -math.inf]
+    if not fin:
+        return np.zeros(len(qrow)), -math.inf
+    e = [math.exp(x) if x != -math.inf else 0.0 for x in s]
+    z = math.fsum(e)
+    out = [math.fsum(e[j] * float(vals[j][c]) for j in range(len(keys))) / z for c in range(len(qrow))]
+    return np.array(out), math.log(z)
+
+
+@pytest.mark.parametrize("window,period,causal,Lq", [(2, 3, True, 1), (0, 4, True, 1), (3, 2, True, 9),
+                                                     (1, 5, False, 9), (4, 1, True, 6), (2, 0, True, 9),
+                                                     (30, 3, True, 9)])
+def test_pi_matches_bruteforce_on_explicit_key_lists(window, period, causal, Lq):
+    B, Hq, Hkv, L, d = 2, 4, 2, 23, 6
+    q, k, v = rand_f32(B, Hq, Lq, d), rand_f32(B, Hkv, L, d), rand_f32(B, Hkv, L, d)
+    lens = np.array([23, 14], np.int32)
+    alpha = RNG.uniform(0.05, 0.95, size=(B, Hq, Lq)).astype(np.float32)
+    alpha[0, 0, 0] = 1.0  # skip keys switched off
+    alpha[1, 1, -1] = 0.0  # local keys switched off
+    prob = oracle.Problem(q, k, v, kv_lens=lens, scale=0.41, causal=causal)
+    out, lse = oracle.pi_attention(prob, window, period, alpha)
+    out = out.reshape(B, Hq, Lq, d)
+    lse = lse.reshape(B, Hq, Lq)
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            for i in range(Lq):
+                pos = n - Lq + i
+                local, skip = _pi_keys(pos, n, window, period, causal)
+                a = float(alpha[b, h, i])
+                bl = math.log(a) if a > 0 else -math.inf
+                bs = math.log(1 - a) if a < 1 else -math.inf
+                keys = [k[b, g, j] for j in local + skip]
+                vals = [v[b, g, j] for j in local + skip]
+                o_ref, l_ref = _brute_biased(q[b, h, i], keys, vals, [bl] * len(local) + [bs] * len(skip), 0.41)
+                np.testing.assert_allclose(out[b, h, i], o_ref, rtol=1e-12, atol=1e-14)
+                if l_ref == -math.inf:
+                    assert lse[b, h, i] == -math.inf
+                else:
+                    assert abs(lse[b, h, i] - l_ref) < 1e-12
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_pi_with_period_one_is_full_attention(causal):
+    # every key is a whole number of periods away: the union is every key
+    B, Hq, Hkv, L, d = 1, 4, 2, 40, 8
+    q, k, v = rand_f32(B, Hq, 12, d), rand_f32(B, Hkv, L, d), rand_f32(B, Hkv, L, d)
+    prob = oracle.Problem(q, k, v, causal=causal)
+    ref, ref_lse = oracle.attention(prob)
+    for window in (0, 5, 100):
+        out, lse = oracle.pi_attention(prob, window, 1)
+        np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
+
+
+def test_pi_alpha_one_is_the_window_and_alpha_zero_the_strided_slice():
+    B, Hq, Hkv, L, d = 1, 4, 1, 50, 8
+    q, k, v = rand_f32(B, Hq, 1, d), rand_f32(B, Hkv, L, d), rand_f32(B, Hkv, L, d)
+    window, period = 6, 7
+    prob = oracle.Problem(q, k, v, causal=True)
+    pos = L - 1
+    ones = np.ones((B, Hq, 1), np.float32)
+    out, lse = oracle.pi_attention(prob, window, period, ones)
+    win = oracle.Problem(q, k[:, :, pos - window:], v[:, :, pos - window:])
+    ref, ref_lse = oracle.attention(win)
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
+    out, lse = oracle.pi_attention(prob, window, period, np.zeros_like(ones))
+    r = pos % period
+    last = pos - window - 1
+    sl = slice(r, last + 1, period)
+    ref, ref_lse = oracle.attention(oracle.Problem(q, np.ascontiguousarray(k[:, :, sl]),
+                                                   np.ascontiguousarray(v[:, :, sl])))
+    np.testing.assert_allclose(out, ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
+
+
+def test_pi_half_alpha_changes_only_lse():
+    B, Hq, Hkv, L, d = 1, 2, 1, 30, 8
+    q, k, v = rand_f32(B, Hq, 5, d), rand_f32(B, Hkv, L, d), rand_f32(B, Hkv, L, d)
+    prob = oracle.Problem(q, k, v, causal=True)
+    out0, lse0 = oracle.pi_attention(prob, 3, 4)
+    out1, lse1 = oracle.pi_attention(prob, 3, 4, np.full((B, Hq, 5), 0.5, np.float32))
+    np.testing.assert_allclose(out1, out0, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(lse1, lse0 + math.log(0.5), rtol=1e-13)
+
+
+def test_pi_is_the_merge_of_its_window_and_its_skip_keys():
+    # the prior shifts each part's log-sum-exp; the tree merge of the two
+    # shifted parts is the whole (the Tree Attention explainer, section 3)
+    B, Hq, Hkv, L, d = 1, 4, 1, 64, 8
+    q, k, v = rand_f32(B, Hq, 1, d), rand_f32(B, Hkv, L, d), rand_f32(B, Hkv, L, d)
+    alpha = np.array([0.2, 0.5, 0.7, 0.9], np.float32).reshape(B, Hq, 1)
+    window, period = 9, 5
+    prob = oracle.Problem(q, k, v, causal=True)
+    out, lse = oracle.pi_attention(prob, window, period, alpha)
+    pos = L - 1
+    for h in range(Hq):
+        a = float(alpha[0, h, 0])
+        o_l, m_l, l_l = oracle.partial(prob, 0, h, 0, pos - window, pos + 1)
+        sk = oracle.Problem(q, np.ascontiguousarray(k[:, :, pos % period:pos - window:period]),
+                            np.ascontiguousarray(v[:, :, pos % period:pos - window:period]))
+        o_s, m_s, l_s = oracle.partial(sk, 0, h, 0, 0, L)
+        merged = oracle.finalize(oracle.merge((o_l, m_l + math.log(a), l_l), (o_s, m_s + math.log(1 - a), l_s)))
+        np.testing.assert_allclose(out[h], merged[0], rtol=1e-12, atol=1e-14)
+        assert abs(lse[h] - merged[1]) < 1e-12
