@@ -237,6 +237,51 @@ ATTN_API attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* 
 ATTN_API int attn_decode_mixed_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi, int* splits_lo);
 
 /*
+ * pi-Attention decode: the query of each sequence (at position i = L_b - 1)
+ * attends to a structured subset of its keys inside one softmax (the
+ * pi-Attention explainer, method section A):
+ *  - the ring-local window: keys j with i - window <= j <= i;
+ *  - the periodic skip keys: keys below the window that lie a whole number of
+ *    periods from i, j = i - m * period (m >= 1), read as a strided gather;
+ *  - the adaptive fusion gate as a log-prior: with alpha (clamped to [0, 1])
+ *    the window's logits get + ln(alpha) and the skip keys' + ln(1 - alpha).
+ * The window and the skip keys are the two spans of one launch; their split
+ * partials carry the prior in their max and go through one log-sum-exp merge
+ * (Tree Attention explainer, section 3), so the result is exact attention over
+ * the union with those priors.
+ *
+ * q, k, v, k_scale, v_scale, kv_lens ([B] per sequence), softmax_scale, out,
+ * lse, workspace: as attn_decode, with bf16 q/out, bf16 or fp8 k/v, d = 128
+ * and Hq = 4 * Hkv.
+ * window   >= 0 keys before the query (the query's own key is always local)
+ * period   >= 1, or 0 for no skip keys
+ * alpha    device float [B*Hq] (row b*Hq + h) or NULL (no prior: plain
+ *          attention over the union)
+ * num_splits_window, num_splits_skip  requested splits per span; 0 takes the
+ *          value of attn_decode_pi_splits(). S = S_window + S_skip splits, and
+ *          the workspace is attn_decode_workspace_size(B, Hq, d, S) bytes.
+ * A row whose keys all carry weight zero (alpha = 0 with no skip key) gets O =
+ * 0 and lse = -inf.
+ */
+ATTN_API attn_status attn_decode_pi(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                    const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B,
+                                    int Hq, int Hkv, int d, int L_cap, float softmax_scale, int window, int period,
+                                    const float* alpha, int num_splits_window, int num_splits_skip,
+                                    attn_tensor* out, float* lse, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/*
+ * Automatic split plan of attn_decode_pi for a cache of capacity L_cap: the
+ * window holds at most min(window + 1, L_cap) keys and the skip keys at most
+ * floor((L_cap - 2 - window) / period) + 1; about two workgroups per compute
+ * unit in all, shared in proportion to those counts, no split shorter than 256
+ * keys. Stores each span's splits (host pointers, may be NULL) and returns
+ * their sum; 0 on a bad argument or a failed device query.
+ */
+ATTN_API int attn_decode_pi_splits(int B, int Hkv, int L_cap, int window, int period, int kv_dtype,
+                                   int* splits_window, int* splits_skip);
+
+/*
  * Prefill: attention of Lq queries over Lkv keys (causal or not), fused so the
  * Lq x Lkv score matrix never reaches memory.
  *

@@ -17,7 +17,7 @@ __all__ = [
     "attn_status_string", "attn_decode_auto_splits", "attn_decode_workspace_size", "attn_decode_workspace_init",
     "attn_decode_plan",
     "attn_decode", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
-    "attn_decode_mixed", "attn_decode_mixed_splits",
+    "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi", "attn_decode_pi_splits",
 ]
 
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
@@ -78,6 +78,11 @@ def load_library():
     ip = ctypes.POINTER(ctypes.c_int)
     lib.attn_decode_mixed_splits.argtypes = [i32, i32, i32, i32, ip, ip]
     lib.attn_decode_mixed_splits.restype = i32
+    lib.attn_decode_pi.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, i32, i32, tp, vp,
+                                   vp, ctypes.c_size_t, vp]
+    lib.attn_decode_pi.restype = i32
+    lib.attn_decode_pi_splits.argtypes = [i32, i32, i32, i32, i32, i32, ip, ip]
+    lib.attn_decode_pi_splits.restype = i32
     _lib = lib
     return lib
 
@@ -289,5 +294,52 @@ def attn_decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale=None, v_scale=None, hi_
                                _ptr(k_scale), _ptr(v_scale), _ptr(lo_lens), L_lo, B, Hq, Hkv, d,
                                float(softmax_scale), int(S_hi), int(S_lo), ctypes.byref(ot), _ptr(lse), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_pi_splits(B, Hkv, L_cap, window, period, kv_dtype=ATTN_BF16):
+    """(S_window, S_skip): the automatic split plan of attn_decode_pi."""
+    sw, ss = ctypes.c_int(0), ctypes.c_int(0)
+    total = load_library().attn_decode_pi_splits(B, Hkv, L_cap, window, period, kv_dtype, ctypes.byref(sw),
+                                                 ctypes.byref(ss))
+    if total <= 0:
+        raise AttnError(4, "could not plan splits")
+    return sw.value, ss.value
+
+
+def attn_decode_pi(q, k, v, window, period, alpha=None, k_scale=None, v_scale=None, kv_lens=None,
+                   softmax_scale=0.0, num_splits_window=0, num_splits_skip=0, out=None, lse=None, workspace=None,
+                   stream=None):
+    """pi-Attention decode: the window of `window` keys before each sequence's query, the keys a whole number of
+    `period`s further back, and the gate alpha (float [B*Hq] or None) as a log-prior. q [B,Hq,1,d]; k, v
+    [B,Hkv,L_cap,d]. Returns (out, lse)."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    Hkv, L_cap = k.shape[1], k.shape[2]
+    if Lq != 1:
+        raise ValueError("attn_decode_pi takes one query per sequence (q.shape[2] == 1)")
+    if alpha is not None and (alpha.dtype != torch.float32 or alpha.numel() != B * Hq or not alpha.is_contiguous()):
+        raise ValueError("alpha must be contiguous float32 with B*Hq entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    sw, ss = num_splits_window, num_splits_skip
+    if sw <= 0 or ss <= 0:
+        aw, as_ = attn_decode_pi_splits(B, Hkv, L_cap, window, period, _dtype_code(k))
+        sw = sw if sw > 0 else aw
+        ss = ss if ss > 0 else as_
+    cap_w = min(window + 1, L_cap)
+    last = L_cap - 2 - window
+    cap_s = last // period + 1 if period > 0 and last >= 0 else 0
+    S = attn_decode_plan(cap_w, sw)[0] + (attn_decode_plan(cap_s, ss)[0] if cap_s else 0)
+    if workspace is None:
+        workspace = attn_decode_workspace(B, Hq, d, S, device=q.device)
+    qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    st = lib.attn_decode_pi(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), _ptr(k_scale), _ptr(v_scale),
+                            _ptr(kv_lens), B, Hq, Hkv, d, L_cap, float(softmax_scale), int(window), int(period),
+                            _ptr(alpha), int(sw), int(ss), ctypes.byref(ot), _ptr(lse), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     _check(st)
     return out, lse

@@ -245,8 +245,9 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     p.counters = nullptr;
     p.ticket_block = 1;
     p.blk_o = p.blk_m = p.blk_l = nullptr;
-    p.S_hi = 0;
-    p.hi = p.lo = attn::KvSpan{};
+    p.S0 = 0;
+    p.sp0 = p.sp1 = attn::KvSpan{};
+    p.alpha = nullptr;
     p.out = nullptr;
     p.out_sb = p.out_sh = 0;
     p.lse = nullptr;
@@ -274,6 +275,152 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     if (mfma) e = attn::launch_decode_mfma(p, fp8 ? attn::DT_FP8 : attn::DT_BF16, stream);
     else e = attn::launch_decode_valu(p, q->dtype, k->dtype, G, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+
+// Automatic split plan of a two-span launch: two resident workgroups per
+// compute unit in all, shared in proportion to keys * cost, every split at
+// least 256 keys long. Returns S0 + S1 (after planning), 0 on failure.
+int two_span_splits(int B, int Hkv, int L0, double cost0, int L1, double cost1, int* s0, int* s1) {
+    const int cus = device_cu_count();
+    if (cus <= 0 || L0 + L1 <= 0) return 0;
+    int64_t T = (2LL * cus) / ((int64_t)B * Hkv);
+    if (T < 2) T = 2;
+    const double w0 = cost0 * L0, w1 = cost1 * L1;
+    int64_t r0 = L0 ? (int64_t)llround((double)T * w0 / (w0 + w1)) : 0;
+    int64_t r1 = L1 ? T - r0 : 0;
+    auto clamp = [](int64_t r, int L) -> int64_t {
+        if (!L) return 0;
+        const int64_t max_s = ceil_div(L, 256);
+        return r < 1 ? 1 : (r > max_s ? max_s : r);
+    };
+    r0 = clamp(r0, L0);
+    r1 = clamp(r1, L1);
+    const int S0 = L0 ? plan_splits(L0, (int)r0).S : 0;
+    const int S1 = L1 ? plan_splits(L1, (int)r1).S : 0;
+    if (s0) *s0 = S0;
+    if (s1) *s1 = S1;
+    return S0 + S1;
+}
+
+// Most keys each pi-Attention span can hold for a decode query at position
+// L_cap - 1: the window's window + 1 keys, and the skip keys below the window.
+struct PiCaps {
+    int window, skip;
+};
+PiCaps pi_caps(int L_cap, int window, int period) {
+    PiCaps c;
+    c.window = (int)(window + 1 < (int64_t)L_cap ? window + 1 : L_cap);
+    const int64_t last = (int64_t)L_cap - 2 - window;  // highest row a skip key can take
+    c.skip = (period > 0 && last >= 0) ? (int)(last / period + 1) : 0;
+    return c;
+}
+
+// A span over a [B, Hkv, L_cap, d] cache; lens_per_head: lens is [B, Hkv]
+// rather than [B].
+attn::KvSpan span_of(const attn_tensor* k, const attn_tensor* v, const int32_t* lens, int lens_per_head_hkv,
+                     int L_cap, int chunk) {
+    attn::KvSpan sp{};
+    if (L_cap && k && v) {
+        sp.k = k->data;
+        sp.k_sb = k->stride_b;
+        sp.k_sh = k->stride_h;
+        sp.k_ss = k->stride_s;
+        sp.v = v->data;
+        sp.v_sb = v->stride_b;
+        sp.v_sh = v->stride_h;
+        sp.v_ss = v->stride_s;
+    }
+    sp.kv_lens = lens;
+    sp.lens_sb = lens_per_head_hkv ? lens_per_head_hkv : 1;
+    sp.lens_sh = lens_per_head_hkv ? 1 : 0;
+    sp.L_cap = L_cap;
+    sp.chunk = chunk;
+    sp.geom = attn::kGeomAll;
+    sp.period = 1;
+    return sp;
+}
+
+attn::DecodeParams two_span_params(const attn_tensor* q, int B, int Hq, int Hkv, int d, float softmax_scale,
+                                   const float* k_scale, const float* v_scale) {
+    const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+    attn::DecodeParams p{};
+    p.q = q->data;
+    p.q_sb = q->stride_b;
+    p.q_sh = q->stride_h;
+    p.k_scale = k_scale;
+    p.v_scale = v_scale;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.scale_log2 = sc * kLog2e;
+    p.ticket_block = 1;
+    return p;
+}
+
+// Workspace layout (that of attn_decode with S splits), the fused-merge
+// decision, the launch, and the separate merge when not fused.
+attn_status two_span_launch(attn::DecodeParams& p, int S, bool fp8_0, bool fp8_1, attn_tensor* out, float* lse,
+                            void* workspace, size_t workspace_bytes, hipStream_t hs) {
+    const int B = p.B, Hq = p.Hq, Hkv = p.Hkv, d = p.d;
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
+    if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    const int64_t rows = (int64_t)B * Hq;
+    const size_t need = attn_decode_workspace_size(B, Hq, d, S);
+    if (workspace_bytes < need)
+        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need %zu for %d splits", workspace_bytes, need, S);
+    uint32_t* counters = static_cast<uint32_t*>(workspace);
+    float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn::kCounterBytes);
+    float* m_part = o_part + rows * S * d;
+    float* l_part = m_part + rows * S;
+    float* blk_o = l_part + rows * S;
+    float* blk_m = blk_o + rows * attn::kMaxTicketBlocks * d;
+    float* blk_l = blk_m + rows * attn::kMaxTicketBlocks;
+    p.S = S;
+    p.o_part = o_part;
+    p.m_part = m_part;
+    p.l_part = l_part;
+
+    const int cus = device_cu_count();
+    const int64_t wgs = (int64_t)B * Hkv * S;
+    const bool fused = (int64_t)B * Hkv <= attn::kMaxCounterGroups && S <= attn::kMaxFusedSplits && cus > 0 &&
+                       wgs <= 2LL * cus;
+    if (fused) {
+        p.counters = counters;
+        p.ticket_block = ticket_block_for(S);
+        p.blk_o = blk_o;
+        p.blk_m = blk_m;
+        p.blk_l = blk_l;
+        p.out = out->data;
+        p.out_sb = out->stride_b;
+        p.out_sh = out->stride_h;
+        p.lse = lse;
+    }
+    hipError_t e = attn::launch_decode_mfma_two(p, fp8_0, fp8_1, hs);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+    if (fused) return ATTN_OK;
+
+    // every split publishes a partial (the identity when empty): merge all S
+    attn::CombineParams cp;
+    cp.o_part = o_part;
+    cp.m_part = m_part;
+    cp.l_part = l_part;
+    cp.R = (int)rows;
+    cp.S = S;
+    cp.d = d;
+    cp.Hq = Hq;
+    cp.kv_lens = nullptr;
+    cp.chunk = 1;
+    cp.L_cap = 0;
+    cp.out = out->data;
+    cp.out_dtype = out->dtype;
+    cp.out_sb = out->stride_b;
+    cp.out_sh = out->stride_h;
+    cp.lse = lse;
+    e = attn::launch_combine(cp, hs);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
     return ATTN_OK;
 }
 
@@ -385,31 +532,11 @@ attn_status attn_combine_partials(const float* o_part, const float* m_part, cons
 
 int attn_decode_mixed_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi, int* splits_lo) {
     if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0) return 0;
-    const int cus = device_cu_count();
-    if (cus <= 0) return 0;
-    // Two resident workgroups per compute unit in all (so the merge is fused),
-    // shared between the spans in proportion to their cost per key: 2 for bf16
-    // (bytes per element) and 1.3 for fp8, whose workgroups convert and
-    // multiply twice the keys per byte and stream about 1.3x slower per byte.
-    // (128K keys, 20% bf16, 8 KV heads: 18 + 46 splits take 60.8 us, the
-    // bytes-proportional 21 + 43 take 63.7 us.) No split shorter than 256 keys.
-    int64_t T = (2LL * cus) / ((int64_t)B * Hkv);
-    if (T < 2) T = 2;
-    const double w_hi = 2.0 * L_hi_cap, w_lo = 1.3 * L_lo_cap;
-    int64_t r_hi = L_hi_cap ? (int64_t)llround((double)T * w_hi / (w_hi + w_lo)) : 0;
-    int64_t r_lo = L_lo_cap ? T - r_hi : 0;
-    auto clamp = [](int64_t r, int L) -> int64_t {
-        if (!L) return 0;
-        const int64_t max_s = ceil_div(L, 256);
-        return r < 1 ? 1 : (r > max_s ? max_s : r);
-    };
-    r_hi = clamp(r_hi, L_hi_cap);
-    r_lo = clamp(r_lo, L_lo_cap);
-    const int S_hi = L_hi_cap ? plan_splits(L_hi_cap, (int)r_hi).S : 0;
-    const int S_lo = L_lo_cap ? plan_splits(L_lo_cap, (int)r_lo).S : 0;
-    if (splits_hi) *splits_hi = S_hi;
-    if (splits_lo) *splits_lo = S_lo;
-    return S_hi + S_lo;
+    // Cost per key: 2 for bf16 (bytes per element) and 1.3 for fp8, whose
+    // workgroups convert and multiply twice the keys per byte and stream about
+    // 1.3x slower per byte. (128K keys, 20% bf16, 8 KV heads: 18 + 46 splits
+    // take 60.8 us, the bytes-proportional 21 + 43 take 63.7 us.)
+    return two_span_splits(B, Hkv, L_hi_cap, 2.0, L_lo_cap, 1.3, splits_hi, splits_lo);
 }
 
 attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
@@ -453,104 +580,75 @@ attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, con
     }
     const Plan ph = L_hi_cap ? plan_splits(L_hi_cap, num_splits_hi ? num_splits_hi : auto_hi) : Plan{kChunkQuantum, 0};
     const Plan plo = L_lo_cap ? plan_splits(L_lo_cap, num_splits_lo ? num_splits_lo : auto_lo) : Plan{kChunkQuantum, 0};
-    const int S = ph.S + plo.S;
 
-    // Workspace: [merge counters | o_part | m_part | l_part | block partials],
-    // the layout of attn_decode with S = S_hi + S_lo splits.
-    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
-    if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-    const int64_t rows = (int64_t)B * Hq;
-    const size_t need = attn_decode_workspace_size(B, Hq, d, S);
-    if (workspace_bytes < need)
-        return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need %zu for %d splits", workspace_bytes, need, S);
-    uint32_t* counters = static_cast<uint32_t*>(workspace);
-    float* o_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + attn::kCounterBytes);
-    float* m_part = o_part + rows * S * d;
-    float* l_part = m_part + rows * S;
-    float* blk_o = l_part + rows * S;
-    float* blk_m = blk_o + rows * attn::kMaxTicketBlocks * d;
-    float* blk_l = blk_m + rows * attn::kMaxTicketBlocks;
+    attn::DecodeParams p = two_span_params(q, B, Hq, Hkv, d, softmax_scale, k_scale, v_scale);
+    p.S0 = ph.S;
+    p.sp0 = span_of(k_hi, v_hi, hi_lens, Hkv, L_hi_cap, ph.chunk);
+    p.sp1 = span_of(k_lo, v_lo, lo_lens, Hkv, L_lo_cap, plo.chunk);
+    return two_span_launch(p, ph.S + plo.S, false, true, out, lse, workspace, workspace_bytes,
+                           static_cast<hipStream_t>(stream));
+}
 
-    const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
-    attn::DecodeParams p{};
-    p.q = q->data;
-    p.q_sb = q->stride_b;
-    p.q_sh = q->stride_h;
-    p.k_scale = k_scale;
-    p.v_scale = v_scale;
-    p.B = B;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.d = d;
-    p.S = S;
-    p.S_hi = ph.S;
-    p.scale_log2 = sc * kLog2e;
-    p.o_part = o_part;
-    p.m_part = m_part;
-    p.l_part = l_part;
-    p.ticket_block = 1;
-    auto span = [&](const attn_tensor* k, const attn_tensor* v, const int32_t* lens, int L_cap, int chunk) {
-        attn::KvSpan sp{};
-        if (L_cap) {
-            sp.k = k->data;
-            sp.k_sb = k->stride_b;
-            sp.k_sh = k->stride_h;
-            sp.k_ss = k->stride_s;
-            sp.v = v->data;
-            sp.v_sb = v->stride_b;
-            sp.v_sh = v->stride_h;
-            sp.v_ss = v->stride_s;
-        }
-        sp.kv_lens = lens;  // [B, Hkv]: one length per (sequence, KV head)
-        sp.lens_sb = Hkv;
-        sp.lens_sh = 1;
-        sp.L_cap = L_cap;
-        sp.chunk = chunk;
-        return sp;
-    };
-    p.hi = span(k_hi, v_hi, hi_lens, L_hi_cap, ph.chunk);
-    p.lo = span(k_lo, v_lo, lo_lens, L_lo_cap, plo.chunk);
+int attn_decode_pi_splits(int B, int Hkv, int L_cap, int window, int period, int kv_dtype, int* splits_window,
+                          int* splits_skip) {
+    if (B <= 0 || Hkv <= 0 || L_cap <= 0 || window < 0 || period < 0 || !elem_size(kv_dtype)) return 0;
+    const PiCaps c = pi_caps(L_cap, window, period);
+    // both spans hold the same dtype: split in proportion to their keys
+    return two_span_splits(B, Hkv, c.window, 1.0, c.skip, 1.0, splits_window, splits_skip);
+}
 
-    hipStream_t hs = static_cast<hipStream_t>(stream);
-    const int cus = device_cu_count();
-    const int64_t wgs = (int64_t)B * Hkv * S;
-    const bool fused = (int64_t)B * Hkv <= attn::kMaxCounterGroups && S <= attn::kMaxFusedSplits && cus > 0 &&
-                       wgs <= 2LL * cus;
-    if (fused) {
-        p.counters = counters;
-        p.ticket_block = ticket_block_for(S);
-        p.blk_o = blk_o;
-        p.blk_m = blk_m;
-        p.blk_l = blk_l;
-        p.out = out->data;
-        p.out_sb = out->stride_b;
-        p.out_sh = out->stride_h;
-        p.lse = lse;
+attn_status attn_decode_pi(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const float* k_scale,
+                           const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int d, int L_cap,
+                           float softmax_scale, int window, int period, const float* alpha,
+                           int num_splits_window, int num_splits_skip, attn_tensor* out, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = 0;
+    attn_status st;
+    if ((st = check_tensor(q, "q", true)) || (st = check_tensor(k, "k", true)) || (st = check_tensor(v, "v", true)) ||
+        (st = check_tensor(out, "out", false)))
+        return st;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || L_cap <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d d=%d L_cap=%d)", B, Hq, Hkv, d,
+                    L_cap);
+    if (B > 65535 || Hkv > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and Hkv must be <= 65535");
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (window < 0 || period < 0) return fail(ATTN_ERR_INVALID_ARG, "window and period must be >= 0");
+    if (num_splits_window < 0 || num_splits_skip < 0) return fail(ATTN_ERR_INVALID_ARG, "split counts must be >= 0");
+    if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (k->dtype != v->dtype) return fail(ATTN_ERR_INVALID_ARG, "k and v dtypes differ");
+    const bool fp8 = k->dtype == ATTN_FP8_E4M3;
+    if (fp8 && (!k_scale || !v_scale)) return fail(ATTN_ERR_INVALID_ARG, "fp8 k/v need k_scale and v_scale");
+    if (!fp8 && (k_scale || v_scale)) return fail(ATTN_ERR_INVALID_ARG, "scales are only for fp8 k/v");
+    if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16 || (k->dtype != ATTN_BF16 && !fp8))
+        return fail(ATTN_ERR_UNSUPPORTED, "pi decode takes bf16 q and out, bf16 or fp8 k/v");
+    if (d != 128 || Hq != 4 * Hkv)
+        return fail(ATTN_ERR_UNSUPPORTED, "pi decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+
+    const PiCaps c = pi_caps(L_cap, window, period);
+    int auto_w = 0, auto_s = 0;
+    if (!num_splits_window || (!num_splits_skip && c.skip)) {
+        if (attn_decode_pi_splits(B, Hkv, L_cap, window, period, k->dtype, &auto_w, &auto_s) <= 0)
+            return fail(ATTN_ERR_HIP, "could not query the device for the split plan");
     }
-    hipError_t e = attn::launch_decode_mfma_mixed(p, hs);
-    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
-    if (fused) return ATTN_OK;
+    const Plan pw = plan_splits(c.window, num_splits_window ? num_splits_window : auto_w);
+    const Plan ps = c.skip ? plan_splits(c.skip, num_splits_skip ? num_splits_skip : auto_s) : Plan{kChunkQuantum, 0};
 
-    // every split publishes a partial (the identity when empty): merge all S
-    attn::CombineParams cp;
-    cp.o_part = o_part;
-    cp.m_part = m_part;
-    cp.l_part = l_part;
-    cp.R = (int)rows;
-    cp.S = S;
-    cp.d = d;
-    cp.Hq = Hq;
-    cp.kv_lens = nullptr;
-    cp.chunk = 1;
-    cp.L_cap = 0;
-    cp.out = out->data;
-    cp.out_dtype = out->dtype;
-    cp.out_sb = out->stride_b;
-    cp.out_sh = out->stride_h;
-    cp.lse = lse;
-    e = attn::launch_combine(cp, hs);
-    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
-    return ATTN_OK;
+    attn::DecodeParams p = two_span_params(q, B, Hq, Hkv, d, softmax_scale, k_scale, v_scale);
+    p.S0 = pw.S;
+    p.sp0 = span_of(k, v, kv_lens, 0, L_cap, pw.chunk);
+    p.sp0.geom = attn::kGeomWindow;
+    p.sp0.window = window;
+    p.sp1 = span_of(k, v, kv_lens, 0, L_cap, ps.chunk);
+    p.sp1.geom = attn::kGeomSkip;
+    p.sp1.window = window;
+    p.sp1.period = period > 0 ? period : 1;
+    p.alpha = alpha;
+    if (alpha) {
+        p.sp0.prior = 1;  // ln(alpha) on the window's logits
+        p.sp1.prior = 2;  // ln(1 - alpha) on the skip keys' logits
+    }
+    return two_span_launch(p, pw.S + ps.S, fp8, fp8, out, lse, workspace, workspace_bytes,
+                           static_cast<hipStream_t>(stream));
 }
 
 attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B, int Hq, int Hkv,

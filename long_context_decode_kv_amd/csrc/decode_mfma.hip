@@ -383,23 +383,39 @@ struct DecodeLds {
 };
 
 // One workgroup: split s of span `sp`, publishing partial s_out of its rows.
-// MIXED: every split of the launch publishes a partial (an empty one the
-// identity) and takes part in the fused merge, which covers all p.S of them.
-template <bool FP8, bool FUSED, bool MIXED>
+// TWO (two-span launches): the span's key geometry and log-prior apply; every
+// split of the launch publishes a partial (an empty one the identity) and
+// takes part in the fused merge, which covers all p.S of them.
+template <bool FP8, bool FUSED, bool TWO>
 __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& sp, int s, int s_out,
                                           DecodeLds& lds) {
     const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     int L_b = sp.L_cap;
     if (sp.kv_lens) L_b = min(max(sp.kv_lens[b * sp.lens_sb + g * sp.lens_sh], 0), sp.L_cap);
+    // keys visited: rows row0 + t * rmul for t in [0, n_keys)
+    int n_keys = L_b, row0 = 0, rmul = 1;
+    if constexpr (TWO) {
+        const int i = L_b - 1;  // the query's position
+        if (sp.geom == kGeomWindow) {
+            row0 = max(0, i - sp.window);
+            n_keys = L_b - row0;
+        } else if (sp.geom == kGeomSkip) {
+            const int last = i - sp.window - 1;  // the highest row a skip key may take
+            const int r = i >= 0 ? i % sp.period : 0;
+            n_keys = last >= r ? (last - r) / sp.period + 1 : 0;
+            row0 = r;
+            rmul = sp.period;
+        }
+    }
     const int t_begin = s * sp.chunk;
-    const int t_end = min(t_begin + sp.chunk, L_b);
-    const int n_merge = MIXED ? p.S : (L_b + sp.chunk - 1) / sp.chunk;
+    const int t_end = min(t_begin + sp.chunk, n_keys);
+    const int n_merge = TWO ? p.S : (L_b + sp.chunk - 1) / sp.chunk;
     if (t_begin >= t_end) {
         // A split past the end of a shorter sequence: the identity partial.
         for (int i = tid; i < 4 * 128; i += 256) {
             const int64_t row = (int64_t)b * p.Hq + g * 4 + i / 128;
-            if constexpr (FUSED && MIXED) {
+            if constexpr (FUSED && TWO) {
                 st_agent(p.o_part + (row * p.S + s_out) * 128 + i % 128, 0.f);
                 if (i % 128 == 0) {
                     st_agent(p.m_part + row * p.S + s_out, kNegInf);
@@ -413,8 +429,8 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
                 }
             }
         }
-        if constexpr (FUSED && MIXED) merge_group_if_last(p, b, g, n_merge, tid);
-        if (FUSED && !MIXED && L_b == 0 && s == 0) {
+        if constexpr (FUSED && TWO) merge_group_if_last(p, b, g, n_merge, tid);
+        if (FUSED && !TWO && L_b == 0 && s == 0) {
             // an empty sequence: O = 0, lse = -inf (no workgroup of it merges)
             for (int i = tid; i < 4 * 128; i += 256) {
                 uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)(g * 4 + i / 128) * p.out_sh;
@@ -427,9 +443,9 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
     const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
 
     constexpr int esz = FP8 ? 1 : 2;
-    const char* kbase = static_cast<const char*>(sp.k) + (b * sp.k_sb + g * sp.k_sh) * esz;
-    const char* vbase = static_cast<const char*>(sp.v) + (b * sp.v_sb + g * sp.v_sh) * esz;
-    const int64_t kss = sp.k_ss * esz, vss = sp.v_ss * esz;
+    const char* kbase = static_cast<const char*>(sp.k) + (b * sp.k_sb + g * sp.k_sh + row0 * sp.k_ss) * esz;
+    const char* vbase = static_cast<const char*>(sp.v) + (b * sp.v_sb + g * sp.v_sh + row0 * sp.v_ss) * esz;
+    const int64_t kss = sp.k_ss * esz * rmul, vss = sp.v_ss * esz * rmul;
 
     // Q^T operand: column (lane & 15) is query head 4g + (lane & 3); its k-slots
     // follow the same dim order as the K operand.
@@ -528,24 +544,33 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         out[cc] = v * vsc;
     }
     const int64_t row = (int64_t)b * p.Hq + g * 4 + h;
+    float m_out = Mx * kLn2;
+    if constexpr (TWO) {
+        // the span's log-prior shifts its partial's max (natural-log units)
+        if (sp.prior && p.alpha) {
+            const float a = fminf(fmaxf(p.alpha[row], 0.f), 1.f);
+            m_out += logf(sp.prior == 1 ? a : 1.f - a);
+        }
+    }
     if constexpr (FUSED) {
         st_agent2(p.o_part + (row * p.S + s_out) * 128 + c, out);
         if ((tid & 63) == 0) {
-            st_agent(p.m_part + row * p.S + s_out, Mx * kLn2);
+            st_agent(p.m_part + row * p.S + s_out, m_out);
             st_agent(p.l_part + row * p.S + s_out, L);
         }
         merge_group_if_last(p, b, g, n_merge, tid);
     } else {
         *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s_out) * 128 + c) = out;
         if ((tid & 63) == 0) {
-            p.m_part[row * p.S + s_out] = Mx * kLn2;
+            p.m_part[row * p.S + s_out] = m_out;
             p.l_part[row * p.S + s_out] = L;
         }
     }
 }
 
 __device__ __forceinline__ KvSpan main_span(const DecodeParams& p) {
-    return KvSpan{p.k, p.k_sb, p.k_sh, p.k_ss, p.v, p.v_sb, p.v_sh, p.v_ss, p.kv_lens, 1, 0, p.L_cap, p.chunk};
+    return KvSpan{p.k,       p.k_sb, p.k_sh,  p.k_ss,    p.v, p.v_sb, p.v_sh, p.v_ss, p.kv_lens,
+                  1,         0,      p.L_cap, p.chunk,   kGeomAll, 0, 1, 0};
 }
 
 template <bool FP8, bool FUSED>
@@ -554,14 +579,15 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
     decode_wg<FP8, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
 }
 
-// Mixed-precision cache: splits [0, S_hi) stream the bf16 span, the others the
-// fp8 span; one merge over all splits.
-template <bool FUSED>
-__global__ __launch_bounds__(256) void decode_gqa4_d128_mixed(DecodeParams p) {
+// Two spans in one launch (a two-precision cache, or pi-Attention's window
+// and skip keys): splits [0, S0) stream span sp0, the others span sp1; one
+// merge over all splits.
+template <bool FP8_0, bool FP8_1, bool FUSED>
+__global__ __launch_bounds__(256) void decode_gqa4_d128_two(DecodeParams p) {
     __shared__ DecodeLds lds;  // one copy for both branches
     const int s = blockIdx.x;
-    if (s < p.S_hi) decode_wg<false, FUSED, true>(p, p.hi, s, s, lds);
-    else decode_wg<true, FUSED, true>(p, p.lo, s - p.S_hi, s, lds);
+    if (s < p.S0) decode_wg<FP8_0, FUSED, true>(p, p.sp0, s, s, lds);
+    else decode_wg<FP8_1, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
 }
 
 }  // namespace
@@ -579,10 +605,21 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma_mixed(const DecodeParams& p, hipStream_t stream) {
+hipError_t launch_decode_mfma_two(const DecodeParams& p, bool fp8_0, bool fp8_1, hipStream_t stream) {
     dim3 grid(p.S, p.Hkv, p.B);
-    if (p.counters) hipLaunchKernelGGL((decode_gqa4_d128_mixed<true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_gqa4_d128_mixed<false>), grid, dim3(256), 0, stream, p);
+    const bool f = p.counters != nullptr;
+    if (!fp8_0 && fp8_1) {
+        if (f) hipLaunchKernelGGL((decode_gqa4_d128_two<false, true, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_gqa4_d128_two<false, true, false>), grid, dim3(256), 0, stream, p);
+    } else if (!fp8_0 && !fp8_1) {
+        if (f) hipLaunchKernelGGL((decode_gqa4_d128_two<false, false, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_gqa4_d128_two<false, false, false>), grid, dim3(256), 0, stream, p);
+    } else if (fp8_0 && fp8_1) {
+        if (f) hipLaunchKernelGGL((decode_gqa4_d128_two<true, true, true>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((decode_gqa4_d128_two<true, true, false>), grid, dim3(256), 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;  // no fp8-then-bf16 variant
+    }
     return hipGetLastError();
 }
 

@@ -10,8 +10,16 @@ namespace attn {
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 
 // One span of a KV cache: [B, Hkv, L_cap, d] K and V with element strides,
-// valid lengths kv_lens[b*lens_sb + g*lens_sh] (or nullptr: all L_cap), cut
-// into splits of `chunk` keys.
+// valid lengths L_b = kv_lens[b*lens_sb + g*lens_sh] (or nullptr: all L_cap).
+// The keys a span visits follow from L_b and `geom`, and are cut into splits
+// of `chunk` keys:
+//   kGeomAll:    rows [0, L_b);
+//   kGeomWindow: for a query at position i = L_b - 1, rows [max(0, i - window), i];
+//   kGeomSkip:   rows below i - window that are a whole number of periods from
+//                i, in increasing order r, r + period, ... (r = i mod period).
+// `prior` selects the log-prior added to the span's logits per query head:
+// 0 none, 1 ln(alpha), 2 ln(1 - alpha), alpha from DecodeParams::alpha.
+enum { kGeomAll = 0, kGeomWindow = 1, kGeomSkip = 2 };
 struct KvSpan {
     const void* k;
     int64_t k_sb, k_sh, k_ss;
@@ -21,6 +29,8 @@ struct KvSpan {
     int lens_sb, lens_sh;
     int L_cap;
     int chunk;
+    int geom, window, period;
+    int prior;
 };
 
 // One split-KV decode launch: grid (S, Hkv, B); workgroup (s, g, b) owns keys
@@ -54,12 +64,13 @@ struct DecodeParams {
     void* out;           // [B, Hq, 1, d] bf16
     int64_t out_sb, out_sh;
     float* lse;          // [B*Hq] or nullptr
-    // Mixed precision (decode_mfma_mixed only; k, v, kv_lens, L_cap and chunk
-    // above are then unused): splits [0, S_hi) read the bf16 span `hi`, splits
-    // [S_hi, S) the fp8 span `lo` (with k_scale and v_scale); all S partials of
+    // Two-span launches (launch_decode_mfma_two; k, v, kv_lens, L_cap and
+    // chunk above are then unused): splits [0, S0) read span sp0, splits
+    // [S0, S) span sp1; every split publishes a partial and all S partials of
     // a row are merged.
-    int S_hi;
-    KvSpan hi, lo;
+    int S0;
+    KvSpan sp0, sp1;
+    const float* alpha;  // [B*Hq] gate of the spans' log-priors, or nullptr
 };
 
 // Bytes at the start of a decode workspace reserved for the fused-merge
@@ -107,7 +118,8 @@ struct PrefillParams {
 };
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream);
-hipError_t launch_decode_mfma_mixed(const DecodeParams& p, hipStream_t stream);
+// Two-span decode: fp8_0 / fp8_1 give the KV dtype of sp0 / sp1 (bf16 or fp8).
+hipError_t launch_decode_mfma_two(const DecodeParams& p, bool fp8_0, bool fp8_1, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int q_dtype, int kv_dtype, int G, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // Zeroes `bytes` (a multiple of 16) at 16-byte aligned device address `p`.

@@ -89,3 +89,22 @@ def oracle_mixed(inp, heads=None, scale=None):
         return out, lse
     B, Hq = inp["q"].shape[:2]
     return out.reshape(B, Hq, -1), lse.reshape(B, Hq)
+
+
+def pi_on_gpu(inp, window, period, alpha=None, num_splits_window=0, num_splits_skip=0, dev=None):
+    import long_context_decode_kv_amd as lib
+    dev = dev or {k: to_dev(v) for k, v in inp.items()}
+    a = None if alpha is None else torch.from_numpy(np.ascontiguousarray(alpha, np.float32).ravel()).cuda()
+    out, lse = lib.attn_decode_pi(dev["q"], dev["k"], dev["v"], window, period, alpha=a, k_scale=dev.get("k_scale"),
+                                  v_scale=dev.get("v_scale"), kv_lens=dev.get("kv_lens"),
+                                  num_splits_window=num_splits_window, num_splits_skip=num_splits_skip)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def oracle_pi(inp, window, period, alpha=None):
+    prob = oracle.Problem(inp["q"], inp["k"], inp["v"], k_scale=inp.get("k_scale"), v_scale=inp.get("v_scale"),
+                          kv_lens=inp.get("kv_lens"), causal=True)
+    out, lse = oracle.pi_attention(prob, window, period, alpha)
+    B, Hq = inp["q"].shape[:2]
+    return out.reshape(B, Hq, -1), lse.reshape(B, Hq)

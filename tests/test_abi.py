@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(so):
     assert set(names) == {"attn_status_string", "attn_last_error", "attn_decode_auto_splits",
                           "attn_decode_workspace_size", "attn_decode_workspace_init", "attn_decode_plan",
                           "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials",
-                          "attn_decode_mixed", "attn_decode_mixed_splits"}
+                          "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi",
+                          "attn_decode_pi_splits"}
     nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
     for n in names:
@@ -173,3 +174,34 @@ def test_mixed_decode_argument_errors(so):
     # an empty span may come without tensors
     assert mixed(so, L_hi=0, S_hi=0, no_hi=True, ws=None) == WORKSPACE  # validation reaches the workspace check
     assert mixed(so, L_hi=16, no_hi=True) == INVALID
+
+
+def pi(so, kv=BF16, ks=None, vs=None, B=1, Hq=8, Hkv=2, d=128, L=4096, window=512, period=16, Sw=2, Ss=2, out=None,
+       ws=FAKE, ws_bytes=1 << 30):
+    q = T(BF16, Hq * d, d, d)
+    k = T(kv, Hkv * L * d, L * d, d)
+    out = out or T(BF16, Hq * d, d, d)
+    return so.attn_decode_pi(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ks, vs, None, B, Hq, Hkv, d, L, 0.0,
+                             window, period, None, Sw, Ss, ctypes.byref(out), None, ws, ws_bytes, None)
+
+
+def test_pi_decode_argument_errors(so):
+    assert pi(so, window=-1) == INVALID
+    assert pi(so, period=-2) == INVALID
+    assert pi(so, Sw=-1) == INVALID
+    assert pi(so, L=0) == INVALID
+    assert pi(so, kv=FP8) == INVALID  # fp8 without scales
+    assert pi(so, ks=FAKE, vs=FAKE) == INVALID  # scales with bf16
+    assert pi(so, kv=F32) == UNSUPPORTED
+    assert pi(so, d=64) == UNSUPPORTED
+    assert pi(so, Hq=16) == UNSUPPORTED
+    assert pi(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
+    assert pi(so, ws=None) == WORKSPACE
+    # window 513 keys in 2 splits, (4096 - 2 - 512) // 16 + 1 = 224 skip keys in 2 splits
+    need = lib.attn_decode_workspace_size(1, 8, 128, 4)
+    assert pi(so, ws_bytes=need - 1) == WORKSPACE
+    assert "4 splits" in lib.load_library().attn_last_error().decode()
+    # no skip keys at all (period 0, or a window covering the cache): one span
+    assert pi(so, period=0, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 2) - 1) == WORKSPACE
+    assert "2 splits" in lib.load_library().attn_last_error().decode()
+    assert pi(so, window=5000, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 2) - 1) == WORKSPACE
