@@ -297,6 +297,38 @@ ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, co
                                   attn_tensor* out, float* lse, void* stream);
 
 /*
+ * pi-Attention prefill (causal, Lq = Lkv = L): query i attends to its ring-local
+ * window, keys i - window .. i, and to its periodic skip keys, i - m * period
+ * below the window (m >= 1), in one softmax, with the gate alpha as a
+ * log-prior: + ln(alpha) on the window's logits, + ln(1 - alpha) on the skip
+ * keys' (the pi-Attention explainer, method section A; the oracle's masked
+ * definition). Computed as two banded prefills -- the window, then, for each
+ * residue class of the positions modulo `period`, the class's queries
+ * against the class's keys as strided views (the strided gather the page
+ * names) -- and a per-row log-sum-exp merge of the two parts (Tree Attention
+ * explainer, section 3).
+ *
+ * q, k, v, out, lse, softmax_scale: as attn_prefill (bf16, d = 128), with
+ * Lq = Lkv = L.
+ * window   >= 0; period >= 1, or 0 for no skip keys. period * k/v row stride
+ *          must be below 2^24 elements.
+ * alpha    device float [B, Hq, L] contiguous (clamped to [0, 1]) or NULL (no
+ *          prior).
+ * workspace  attn_prefill_pi_workspace_size(B, Hq, L, d) bytes of device
+ *          memory, 16-byte aligned, no preparation needed (the skip part's
+ *          outputs and both parts' lse).
+ * The two parts are rounded to bf16 before the merge. A row whose keys all
+ * carry weight zero (alpha = 0 with no skip key) gets O = 0 and lse = -inf.
+ */
+ATTN_API attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B,
+                                     int Hq, int Hkv, int d, int L, float softmax_scale, int window, int period,
+                                     const float* alpha, attn_tensor* out, float* lse, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of attn_prefill_pi (0 on a bad argument). */
+ATTN_API size_t attn_prefill_pi_workspace_size(int B, int Hq, int L, int d);
+
+/*
  * Merge S partials per row into the exact normalised result (the reduction
  * step of the Tree Attention explainer, section 3, on one device): with
  * m = max_s m_s and w_s = exp(m_s - m), O = sum_s w_s o_s / sum_s w_s l_s and

@@ -17,7 +17,8 @@ __all__ = [
     "attn_status_string", "attn_decode_auto_splits", "attn_decode_workspace_size", "attn_decode_workspace_init",
     "attn_decode_plan",
     "attn_decode", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
-    "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi", "attn_decode_pi_splits",
+    "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi", "attn_decode_pi_splits", "attn_prefill_pi",
+    "attn_prefill_pi_workspace_size",
 ]
 
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
@@ -83,6 +84,11 @@ def load_library():
     lib.attn_decode_pi.restype = i32
     lib.attn_decode_pi_splits.argtypes = [i32, i32, i32, i32, i32, i32, ip, ip]
     lib.attn_decode_pi_splits.restype = i32
+    lib.attn_prefill_pi.argtypes = [tp, tp, tp, i32, i32, i32, i32, i32, f32, i32, i32, vp, tp, vp, vp,
+                                    ctypes.c_size_t, vp]
+    lib.attn_prefill_pi.restype = i32
+    lib.attn_prefill_pi_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.attn_prefill_pi_workspace_size.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -341,5 +347,34 @@ def attn_decode_pi(q, k, v, window, period, alpha=None, k_scale=None, v_scale=No
                             _ptr(kv_lens), B, Hq, Hkv, d, L_cap, float(softmax_scale), int(window), int(period),
                             _ptr(alpha), int(sw), int(ss), ctypes.byref(ot), _ptr(lse), _ptr(workspace),
                             workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_prefill_pi_workspace_size(B, Hq, L, d):
+    return load_library().attn_prefill_pi_workspace_size(B, Hq, L, d)
+
+
+def attn_prefill_pi(q, k, v, window, period, alpha=None, softmax_scale=0.0, out=None, lse=None, workspace=None,
+                    stream=None):
+    """pi-Attention causal prefill: window keys i-window..i, skip keys a whole number of `period`s below the window,
+    alpha (float [B,Hq,L] or None) as a log-prior. q [B,Hq,L,d]; k, v [B,Hkv,L,d] bf16. Returns (out, lse)."""
+    lib = load_library()
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[2] != L:
+        raise ValueError("attn_prefill_pi takes as many keys as queries")
+    if alpha is not None and (alpha.dtype != torch.float32 or alpha.numel() != B * Hq * L or not alpha.is_contiguous()):
+        raise ValueError("alpha must be contiguous float32 with B*Hq*L entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(lib.attn_prefill_pi_workspace_size(B, Hq, L, d), dtype=torch.uint8, device=q.device)
+    qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    st = lib.attn_prefill_pi(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), B, Hq, Hkv, d, L,
+                             float(softmax_scale), int(window), int(period), _ptr(alpha), ctypes.byref(ot), _ptr(lse),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     _check(st)
     return out, lse

@@ -424,6 +424,68 @@ attn_status two_span_launch(attn::DecodeParams& p, int S, bool fp8_0, bool fp8_1
     return ATTN_OK;
 }
 
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+attn_status check_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const attn_tensor* out,
+                          int B, int Hq, int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal) {
+    attn_status st;
+    if ((st = check_tensor(q, "q", true)) || (st = check_tensor(k, "k", true)) || (st = check_tensor(v, "v", true)) ||
+        (st = check_tensor(out, "out", true)))
+        return st;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Lq <= 0 || Lkv <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive");
+    if (B > 65535 || Hq > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and Hq must be <= 65535");
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (causal && Lq > Lkv) return fail(ATTN_ERR_INVALID_ARG, "causal with Lq (%d) > Lkv (%d)", Lq, Lkv);
+    if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (q->dtype != ATTN_BF16 || k->dtype != ATTN_BF16 || v->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
+        return fail(ATTN_ERR_UNSUPPORTED, "prefill supports bf16 q/k/v/out");
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "prefill head dim %d (supported: 128)", d);
+    // K/V tiles are read through 32-bit buffer offsets covering 64 key rows
+    if (k->stride_s >= (1 << 24) || v->stride_s >= (1 << 24))
+        return fail(ATTN_ERR_UNSUPPORTED, "prefill k/v row stride must be below 2^24 elements");
+    return ATTN_OK;
+}
+
+attn::PrefillParams prefill_params(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                   const attn_tensor* out, float* lse, int B, int Hq, int Hkv, int d, int Lq, int Lkv,
+                                   float softmax_scale, int causal) {
+    const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+    attn::PrefillParams p;
+    p.q = q->data;
+    p.q_sb = q->stride_b;
+    p.q_sh = q->stride_h;
+    p.q_ss = q->stride_s;
+    p.k = k->data;
+    p.k_sb = k->stride_b;
+    p.k_sh = k->stride_h;
+    p.k_ss = k->stride_s;
+    p.v = v->data;
+    p.v_sb = v->stride_b;
+    p.v_sh = v->stride_h;
+    p.v_ss = v->stride_s;
+    p.out = out->data;
+    p.o_sb = out->stride_b;
+    p.o_sh = out->stride_h;
+    p.o_ss = out->stride_s;
+    p.lse = lse;
+    p.lse_sb = (int64_t)Hq * Lq;
+    p.lse_sh = Lq;
+    p.lse_ss = 1;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.Lq = Lq;
+    p.Lkv = Lkv;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = sc * kLog2e;
+    p.band = 0;
+    p.diag = Lkv - Lq;
+    p.window = -1;
+    return p;
+}
+
 }  // namespace
 
 extern "C" {
@@ -655,51 +717,111 @@ attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_
                          int d, int Lq, int Lkv, float softmax_scale, int causal, attn_tensor* out, float* lse,
                          void* stream) {
     g_last_error[0] = 0;
-    attn_status st;
-    if ((st = check_tensor(q, "q", true)) || (st = check_tensor(k, "k", true)) || (st = check_tensor(v, "v", true)) ||
-        (st = check_tensor(out, "out", true)))
-        return st;
-    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0 || Lq <= 0 || Lkv <= 0)
-        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive");
-    if (B > 65535 || Hq > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and Hq must be <= 65535");
-    if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
-    if (causal && Lq > Lkv) return fail(ATTN_ERR_INVALID_ARG, "causal with Lq (%d) > Lkv (%d)", Lq, Lkv);
-    if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
-    if (q->dtype != ATTN_BF16 || k->dtype != ATTN_BF16 || v->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
-        return fail(ATTN_ERR_UNSUPPORTED, "prefill supports bf16 q/k/v/out");
-    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "prefill head dim %d (supported: 128)", d);
-    // K/V tiles are read through 32-bit buffer offsets covering 64 key rows
-    if (k->stride_s >= (1 << 24) || v->stride_s >= (1 << 24))
-        return fail(ATTN_ERR_UNSUPPORTED, "prefill k/v row stride must be below 2^24 elements");
-    const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
-    attn::PrefillParams p;
-    p.q = q->data;
-    p.q_sb = q->stride_b;
-    p.q_sh = q->stride_h;
-    p.q_ss = q->stride_s;
-    p.k = k->data;
-    p.k_sb = k->stride_b;
-    p.k_sh = k->stride_h;
-    p.k_ss = k->stride_s;
-    p.v = v->data;
-    p.v_sb = v->stride_b;
-    p.v_sh = v->stride_h;
-    p.v_ss = v->stride_s;
-    p.out = out->data;
-    p.o_sb = out->stride_b;
-    p.o_sh = out->stride_h;
-    p.o_ss = out->stride_s;
-    p.lse = lse;
-    p.B = B;
-    p.Hq = Hq;
-    p.Hkv = Hkv;
-    p.d = d;
-    p.Lq = Lq;
-    p.Lkv = Lkv;
-    p.causal = causal ? 1 : 0;
-    p.scale_log2 = sc * kLog2e;
+    attn_status st = check_prefill(q, k, v, out, B, Hq, Hkv, d, Lq, Lkv, softmax_scale, causal);
+    if (st != ATTN_OK) return st;
+    attn::PrefillParams p = prefill_params(q, k, v, out, lse, B, Hq, Hkv, d, Lq, Lkv, softmax_scale, causal);
     hipError_t e = attn::launch_prefill(p, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
+size_t attn_prefill_pi_workspace_size(int B, int Hq, int L, int d) {
+    if (B <= 0 || Hq <= 0 || L <= 0 || d <= 0) return 0;
+    const size_t rows = (size_t)B * Hq * L;
+    return round_up(rows * d * 2, 256) + 2 * round_up(rows * 4, 256);
+}
+
+attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B, int Hq, int Hkv,
+                            int d, int L, float softmax_scale, int window, int period, const float* alpha,
+                            attn_tensor* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = 0;
+    attn_status st = check_prefill(q, k, v, out, B, Hq, Hkv, d, L, L, softmax_scale, 1);
+    if (st != ATTN_OK) return st;
+    if (window < 0 || period < 0) return fail(ATTN_ERR_INVALID_ARG, "window and period must be >= 0");
+    if (period > 0 && ((int64_t)period * k->stride_s >= (1 << 24) || (int64_t)period * v->stride_s >= (1 << 24)))
+        return fail(ATTN_ERR_UNSUPPORTED, "period * k/v row stride must be below 2^24 elements");
+    const size_t need = attn_prefill_pi_workspace_size(B, Hq, L, d);
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
+    if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+    const size_t rows = (size_t)B * Hq * L;
+    uint16_t* o_skip = static_cast<uint16_t*>(workspace);
+    float* lse_w = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * d * 2, 256));
+    float* lse_s = reinterpret_cast<float*>(reinterpret_cast<char*>(lse_w) + round_up(rows * 4, 256));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const bool has_skip = period > 0 && L > window + 1;  // some query has a key below its window
+    const bool merge = has_skip || alpha != nullptr;
+
+    // 1. the window: keys [i - window, i] of query i
+    attn::PrefillParams pw = prefill_params(q, k, v, out, merge ? lse_w : lse, B, Hq, Hkv, d, L, L, softmax_scale, 1);
+    pw.band = 1;
+    pw.diag = 0;
+    pw.window = window;
+    hipError_t e = attn::launch_prefill(pw, hs);
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+
+    // 2. the skip keys: for each residue class r of the positions mod period,
+    // queries r, r + period, ... against keys r, r + period, ...; query m of
+    // the class sees keys m' <= m - delta (positions at least window + 1
+    // below). Classes are the batch of a banded launch over strided views;
+    // the first L % period classes have one row more than the others.
+    if (has_skip) {
+        const int delta = window / period + 1;
+        const int n = L / period, rem = L % period;
+        const int64_t d64 = d;
+        for (int b = 0; b < B; ++b) {
+            for (int part = 0; part < 2; ++part) {
+                const int r0 = part ? rem : 0;
+                const int ncls = part ? period - rem : rem;
+                const int nrows = part ? n : n + 1;
+                if (ncls <= 0 || nrows <= 0) continue;
+                attn::PrefillParams ps = pw;
+                ps.q = static_cast<const uint16_t*>(q->data) + b * q->stride_b + r0 * q->stride_s;
+                ps.q_sb = q->stride_s;
+                ps.q_ss = (int64_t)period * q->stride_s;
+                ps.k = static_cast<const uint16_t*>(k->data) + b * k->stride_b + r0 * k->stride_s;
+                ps.k_sb = k->stride_s;
+                ps.k_ss = (int64_t)period * k->stride_s;
+                ps.v = static_cast<const uint16_t*>(v->data) + b * v->stride_b + r0 * v->stride_s;
+                ps.v_sb = v->stride_s;
+                ps.v_ss = (int64_t)period * v->stride_s;
+                ps.out = o_skip + ((int64_t)b * Hq * L + r0) * d64;
+                ps.o_sb = d64;
+                ps.o_sh = (int64_t)L * d64;
+                ps.o_ss = (int64_t)period * d64;
+                ps.lse = lse_s + (int64_t)b * Hq * L + r0;
+                ps.lse_sb = 1;
+                ps.lse_sh = L;
+                ps.lse_ss = period;
+                ps.B = ncls;
+                ps.Lq = ps.Lkv = nrows;
+                ps.diag = -delta;
+                ps.window = -1;
+                e = attn::launch_prefill(ps, hs);
+                if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+            }
+        }
+    }
+
+    // 3. one softmax over both parts, with the priors
+    if (merge) {
+        attn::PiMergeParams pm;
+        pm.out = out->data;
+        pm.o_sb = out->stride_b;
+        pm.o_sh = out->stride_h;
+        pm.o_ss = out->stride_s;
+        pm.o_skip = has_skip ? o_skip : nullptr;
+        pm.lse_w = lse_w;
+        pm.lse_s = has_skip ? lse_s : nullptr;
+        pm.alpha = alpha;
+        pm.lse = lse;
+        pm.B = B;
+        pm.Hq = Hq;
+        pm.L = L;
+        pm.d = d;
+        e = attn::launch_pi_merge(pm, hs);
+        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
+    }
     return ATTN_OK;
 }
 

@@ -111,10 +111,14 @@ struct PrefillParams {
     int64_t v_sb, v_sh, v_ss;
     void* out;
     int64_t o_sb, o_sh, o_ss;
-    float* lse;  // [B, Hq, Lq] or nullptr
+    float* lse;  // element (b, h, i) at b*lse_sb + h*lse_sh + i*lse_ss, or nullptr
+    int64_t lse_sb, lse_sh, lse_ss;
     int B, Hq, Hkv, d, Lq, Lkv;
     int causal;
     float scale_log2;
+    // Banded variant (band != 0): query i sits at position i + diag and sees
+    // keys [position - window, position] (window < 0: no lower bound).
+    int band, diag, window;
 };
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream);
@@ -125,5 +129,20 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // Zeroes `bytes` (a multiple of 16) at 16-byte aligned device address `p`.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+
+// pi-Attention prefill, last step: per row, merge the window part (read from
+// and written back to `out`) with the skip part, each shifted by its
+// log-prior.
+struct PiMergeParams {
+    void* out;  // bf16 [B, Hq, L, d] view: the window part in, the result out
+    int64_t o_sb, o_sh, o_ss;
+    const uint16_t* o_skip;  // bf16 [B, Hq, L, d] contiguous, or nullptr (no skip part)
+    const float* lse_w;      // [B*Hq*L]
+    const float* lse_s;      // [B*Hq*L], or nullptr with o_skip
+    const float* alpha;      // [B*Hq*L] or nullptr (no prior)
+    float* lse;              // [B, Hq, L] contiguous, or nullptr
+    int B, Hq, L, d;
+};
+hipError_t launch_pi_merge(const PiMergeParams& p, hipStream_t stream);
 
 }  // namespace attn

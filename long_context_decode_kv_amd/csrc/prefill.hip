@@ -113,6 +113,13 @@ __device__ __forceinline__ void loop_barrier() {
 }
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
+// BAND: the key set of a query at position qpos = i + p.diag is bounded on
+// both sides, keys j with qpos - p.window <= j <= qpos (no lower bound when
+// p.window < 0; p.diag may be negative, so a row can see no key at all: it
+// gets O = 0 and lse = -inf). Used for pi-Attention's window and its strided
+// skip classes; without BAND the kernel is plain causal (diag = Lkv - Lq) or
+// full attention.
+template <bool BAND>
 __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
 
@@ -138,12 +145,19 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     const int b = bg / p.Hkv, g = bg % p.Hkv;
     const int h = g * G + hgi * HW + (w % HW);
 
-    const int off = p.Lkv - p.Lq;  // bottom-right alignment
+    const int off = BAND ? p.diag : p.Lkv - p.Lq;  // bottom-right alignment unless banded
     const int p0 = qb * span;
     const int q0 = p0 + kRows * (w / HW);  // first query row of this wave
     const int kv_limit = p.causal ? min(p.Lkv, p0 + span + off) : p.Lkv;
-    const int ntiles = (kv_limit + kN - 1) / kN;
+    // tiles t0 .. t0 + ntiles - 1 hold this workgroup's keys
+    const bool lower = BAND && p.window >= 0;
+    const int t0 = lower ? max(0, p0 + off - p.window) / kN : 0;
+    const int ntiles = max(0, (kv_limit + kN - 1) / kN - t0);
     const int wave_last_key = p.causal ? min(p.Lkv - 1, q0 + kRows - 1 + off) : p.Lkv - 1;
+    // local tiles [jw_lo, jw_hi] hold keys some row of this wave sees
+    // (wave_last_key may be negative when banded; floor division)
+    const int jw_hi = (wave_last_key >= 0 ? wave_last_key / kN : -1) - t0;
+    const int jw_lo = lower ? max(0, max(0, q0 + off - p.window) / kN - t0) : 0;
 
     const char* kbase = static_cast<const char*>(p.k) + (b * p.k_sb + g * p.k_sh) * 2;
     const char* vbase = static_cast<const char*>(p.v) + (b * p.v_sb + g * p.v_sh) * 2;
@@ -195,7 +209,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // Requests this group's piece of tile t into LDS slot t % kSlots.
     auto dma = [&](int t, auto gtag) __attribute__((always_inline)) {
         constexpr int GG = decltype(gtag)::value;
-        const int key0 = t * kN;
+        const int key0 = (t0 + t) * kN;
         const int rows = min(kN, p.Lkv - key0);
         const __amdgpu_buffer_rsrc_t r = GG ? rows_rsrc(kbase + (int64_t)key0 * kss, rows, kss)
                                             : rows_rsrc(vbase + (int64_t)key0 * vss, rows, vss);
@@ -272,20 +286,39 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
 
     // ---- V phase: mask, running max, exponentials and bf16 weights of tile j.
     auto vphase = [&](int j) __attribute__((always_inline)) {
-        const int key0 = j * kN;
-        // mask keys past the diagonal or past the end
-        const bool edge = (key0 + kN > p.Lkv) || (p.causal && key0 + kN - 1 > q0 + off);
+        const int key0 = (t0 + j) * kN;
+        // mask keys past the diagonal or past the end (and, banded, below the window)
+        const bool edge = (key0 + kN > p.Lkv) || (p.causal && key0 + kN - 1 > q0 + off) ||
+                          (lower && key0 < q0 + kRows - 1 + off - p.window);
         if (edge) {
             // largest visible key offset within the tile, relative to this
             // lane's first key (8hb), so each test is against a constant
             const int lim = (p.causal ? min(qabs, p.Lkv - 1) : p.Lkv - 1) - key0 - 8 * hb;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int jj = 0; jj < 16; ++jj) {
-                    const float x = sacc[kb][jj];
-                    sacc[kb][jj] = (32 * kb + key_of(jj, 0) > lim) ? kNegInf : x;
+            if constexpr (BAND) {
+                // visible offsets [lo, lim] as one unsigned range test
+                int lo = lower ? qabs - p.window - key0 - 8 * hb : -kN;
+                int wd = lim - lo;
+                if (wd < 0) {  // nothing visible: a range no offset falls in
+                    lo = 1 << 20;
+                    wd = 0;
                 }
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) {
+                        const float x = sacc[kb][jj];
+                        const int ko = 32 * kb + key_of(jj, 0);
+                        sacc[kb][jj] = ((uint32_t)(ko - lo) > (uint32_t)wd) ? kNegInf : x;
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int jj = 0; jj < 16; ++jj) {
+                        const float x = sacc[kb][jj];
+                        sacc[kb][jj] = (32 * kb + key_of(jj, 0) > lim) ? kNegInf : x;
+                    }
+            }
         }
         // Lazy running max: the exponentials use m_run as long as no score of
         // the lane exceeds it by the headroom; only then (wave vote) the row max
@@ -305,7 +338,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) oacc[i][jj] *= alpha;
         }
-        const float nm = -m_run;
+        // banded rows may have seen no key yet (m_run = -inf): their masked
+        // scores must give weight 0, not exp2(-inf + inf)
+        const float nm = (BAND && m_run == kNegInf) ? 0.f : -m_run;
         float ls = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -326,8 +361,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // completes the previous request, tile j+2's piece, before the barrier
     // that precedes its first reader.
     auto mstep = [&](int j, auto gtag) __attribute__((always_inline)) {
-        const bool pv = j >= 0 && j * kN <= wave_last_key;
-        const bool qk = j + 1 < ntiles && (j + 1) * kN <= wave_last_key;
+        const bool pv = j >= jw_lo && j <= jw_hi;
+        const bool qk = j + 1 < ntiles && j + 1 >= jw_lo && j + 1 <= jw_hi;
         __builtin_amdgcn_s_setprio(1);
         const bool more = j + 3 < ntiles;
         // the request goes after the transposed V reads: the compiler makes
@@ -342,7 +377,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
             __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     };
     auto vstep = [&](int j) __attribute__((always_inline)) {
-        if (j >= 0 && j < ntiles && j * kN <= wave_last_key) vphase(j);
+        if (j >= jw_lo && j < ntiles && j <= jw_hi) vphase(j);
     };
 
     // ---- Schedule. Per wave, tile j goes through M(j-1) (its scores, with the
@@ -362,7 +397,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // barriers.
     auto run = [&](auto gtag) __attribute__((always_inline)) {
         constexpr int GG = decltype(gtag)::value;
-        dma(0, gtag);
+        if (ntiles > 0) dma(0, gtag);
         if (ntiles > 1) dma(1, gtag);
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tiles 0-1 and the Q loads
         __syncthreads();
@@ -389,7 +424,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     const float l_tot = pair_sum(l_run);
     const int qr = q0 + row;
     if (qr < p.Lq) {
-        const float inv = 1.0f / l_tot;
+        const bool empty = BAND && !(l_tot > 0.f);  // a banded row that saw no key
+        const float inv = empty ? 0.f : 1.0f / l_tot;
         uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_ss;
 #pragma unroll
         for (int dblk = 0; dblk < 4; ++dblk)
@@ -401,7 +437,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
                 pk[1] = pack_bf16(oacc[dblk][4 * jj + 2] * inv, oacc[dblk][4 * jj + 3] * inv);
                 *reinterpret_cast<u32x2*>(orow + d0) = pk;
             }
-        if (p.lse && hb == 0) p.lse[((int64_t)b * p.Hq + h) * p.Lq + qr] = m_run * kLn2 + logf(l_tot);
+        if (p.lse && hb == 0)
+            p.lse[b * p.lse_sb + h * p.lse_sh + (int64_t)qr * p.lse_ss] = empty ? kNegInf : m_run * kLn2 + logf(l_tot);
     }
 }
 
@@ -415,7 +452,11 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     const int64_t nqb = (p.Lq + span - 1) / span;
     const int64_t wgs = nqb * p.B * p.Hkv * (G / HW);
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(prefill_fwd_d128, dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, p);
+    if (wgs == 0) return hipSuccess;
+    if (p.band)
+        hipLaunchKernelGGL(prefill_fwd_d128<true>, dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, p);
+    else
+        hipLaunchKernelGGL(prefill_fwd_d128<false>, dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported(so):
                           "attn_decode_workspace_size", "attn_decode_workspace_init", "attn_decode_plan",
                           "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials",
                           "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi",
-                          "attn_decode_pi_splits"}
+                          "attn_decode_pi_splits", "attn_prefill_pi", "attn_prefill_pi_workspace_size"}
     nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
     for n in names:
@@ -205,3 +205,26 @@ def test_pi_decode_argument_errors(so):
     assert pi(so, period=0, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 2) - 1) == WORKSPACE
     assert "2 splits" in lib.load_library().attn_last_error().decode()
     assert pi(so, window=5000, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 2) - 1) == WORKSPACE
+
+
+def pi_prefill(so, dtype=BF16, d=128, L=256, Hq=8, Hkv=2, window=16, period=4, ws=FAKE, ws_bytes=1 << 30):
+    q = T(dtype, Hq * L * d, L * d, d)
+    k = T(dtype, Hkv * L * d, L * d, d)
+    o = T(dtype, Hq * L * d, L * d, d)
+    return so.attn_prefill_pi(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 1, Hq, Hkv, d, L, 0.0, window,
+                              period, None, ctypes.byref(o), None, ws, ws_bytes, None)
+
+
+def test_pi_prefill_argument_errors(so):
+    assert pi_prefill(so, window=-1) == INVALID
+    assert pi_prefill(so, period=-1) == INVALID
+    assert pi_prefill(so, L=0) == INVALID
+    assert pi_prefill(so, dtype=F32) == UNSUPPORTED
+    assert pi_prefill(so, d=64) == UNSUPPORTED
+    assert pi_prefill(so, period=1 << 17) == UNSUPPORTED  # strided rows past the 32-bit buffer offsets
+    assert pi_prefill(so, ws=None) == WORKSPACE
+    # skip outputs (bf16) and two lse arrays, each rounded up to 256 bytes
+    need = lib.attn_prefill_pi_workspace_size(1, 8, 256, 128)
+    assert need == 8 * 256 * 128 * 2 + 2 * 8 * 256 * 4
+    assert pi_prefill(so, ws_bytes=need - 1) == WORKSPACE
+    assert lib.attn_prefill_pi_workspace_size(0, 8, 256, 128) == 0
