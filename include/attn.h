@@ -302,11 +302,11 @@ ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, co
  * below the window (m >= 1), in one softmax, with the gate alpha as a
  * log-prior: + ln(alpha) on the window's logits, + ln(1 - alpha) on the skip
  * keys' (the pi-Attention explainer, method section A; the oracle's masked
- * definition). Computed as two banded prefills -- the window, then, for each
+ * definition). Computed as two banded prefills: the window, then, for each
  * residue class of the positions modulo `period`, the class's queries
  * against the class's keys as strided views (the strided gather the page
- * names) -- and a per-row log-sum-exp merge of the two parts (Tree Attention
- * explainer, section 3).
+ * names), whose epilogue merges each row's two parts by log-sum-exp (Tree
+ * Attention explainer, section 3).
  *
  * q, k, v, out, lse, softmax_scale: as attn_prefill (bf16, d = 128), with
  * Lq = Lkv = L.
@@ -315,9 +315,9 @@ ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, co
  * alpha    device float [B, Hq, L] contiguous (clamped to [0, 1]) or NULL (no
  *          prior).
  * workspace  attn_prefill_pi_workspace_size(B, Hq, L, d) bytes of device
- *          memory, 16-byte aligned, no preparation needed (the skip part's
- *          outputs and both parts' lse).
- * The two parts are rounded to bf16 before the merge. A row whose keys all
+ *          memory, 16-byte aligned, no preparation needed (the window part's
+ *          lse).
+ * The window part passes through `out` in bf16 before the merge. A row whose keys all
  * carry weight zero (alpha = 0 with no skip key) gets O = 0 and lse = -inf.
  */
 ATTN_API attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B,

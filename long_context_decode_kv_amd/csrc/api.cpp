@@ -483,6 +483,9 @@ attn::PrefillParams prefill_params(const attn_tensor* q, const attn_tensor* k, c
     p.band = 0;
     p.diag = Lkv - Lq;
     p.window = -1;
+    p.merge = 0;
+    p.lse_w = nullptr;
+    p.alpha = nullptr;
     return p;
 }
 
@@ -727,8 +730,7 @@ attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_
 
 size_t attn_prefill_pi_workspace_size(int B, int Hq, int L, int d) {
     if (B <= 0 || Hq <= 0 || L <= 0 || d <= 0) return 0;
-    const size_t rows = (size_t)B * Hq * L;
-    return round_up(rows * d * 2, 256) + 2 * round_up(rows * 4, 256);
+    return round_up((size_t)B * Hq * L * 4, 256);  // the window part's lse
 }
 
 attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B, int Hq, int Hkv,
@@ -744,83 +746,66 @@ attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const at
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
     if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
-    const size_t rows = (size_t)B * Hq * L;
-    uint16_t* o_skip = static_cast<uint16_t*>(workspace);
-    float* lse_w = reinterpret_cast<float*>(static_cast<char*>(workspace) + round_up(rows * d * 2, 256));
-    float* lse_s = reinterpret_cast<float*>(reinterpret_cast<char*>(lse_w) + round_up(rows * 4, 256));
+    float* lse_w = static_cast<float*>(workspace);
     hipStream_t hs = static_cast<hipStream_t>(stream);
     const bool has_skip = period > 0 && L > window + 1;  // some query has a key below its window
-    const bool merge = has_skip || alpha != nullptr;
 
-    // 1. the window: keys [i - window, i] of query i
-    attn::PrefillParams pw = prefill_params(q, k, v, out, merge ? lse_w : lse, B, Hq, Hkv, d, L, L, softmax_scale, 1);
+    // 1. the window: keys [i - window, i] of query i. With skip keys to come,
+    // its lse goes to the workspace and the skip launches merge; without, it
+    // applies the prior itself.
+    attn::PrefillParams pw = prefill_params(q, k, v, out, has_skip ? lse_w : lse, B, Hq, Hkv, d, L, L, softmax_scale, 1);
     pw.band = 1;
     pw.diag = 0;
     pw.window = window;
+    pw.merge = (!has_skip && alpha) ? 2 : 0;
+    pw.alpha = alpha;
     hipError_t e = attn::launch_prefill(pw, hs);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+    if (!has_skip) return ATTN_OK;
 
     // 2. the skip keys: for each residue class r of the positions mod period,
     // queries r, r + period, ... against keys r, r + period, ...; query m of
-    // the class sees keys m' <= m - delta (positions at least window + 1
-    // below). Classes are the batch of a banded launch over strided views;
-    // the first L % period classes have one row more than the others.
-    if (has_skip) {
-        const int delta = window / period + 1;
-        const int n = L / period, rem = L % period;
-        const int64_t d64 = d;
-        for (int b = 0; b < B; ++b) {
-            for (int part = 0; part < 2; ++part) {
-                const int r0 = part ? rem : 0;
-                const int ncls = part ? period - rem : rem;
-                const int nrows = part ? n : n + 1;
-                if (ncls <= 0 || nrows <= 0) continue;
-                attn::PrefillParams ps = pw;
-                ps.q = static_cast<const uint16_t*>(q->data) + b * q->stride_b + r0 * q->stride_s;
-                ps.q_sb = q->stride_s;
-                ps.q_ss = (int64_t)period * q->stride_s;
-                ps.k = static_cast<const uint16_t*>(k->data) + b * k->stride_b + r0 * k->stride_s;
-                ps.k_sb = k->stride_s;
-                ps.k_ss = (int64_t)period * k->stride_s;
-                ps.v = static_cast<const uint16_t*>(v->data) + b * v->stride_b + r0 * v->stride_s;
-                ps.v_sb = v->stride_s;
-                ps.v_ss = (int64_t)period * v->stride_s;
-                ps.out = o_skip + ((int64_t)b * Hq * L + r0) * d64;
-                ps.o_sb = d64;
-                ps.o_sh = (int64_t)L * d64;
-                ps.o_ss = (int64_t)period * d64;
-                ps.lse = lse_s + (int64_t)b * Hq * L + r0;
-                ps.lse_sb = 1;
-                ps.lse_sh = L;
-                ps.lse_ss = period;
-                ps.B = ncls;
-                ps.Lq = ps.Lkv = nrows;
-                ps.diag = -delta;
-                ps.window = -1;
-                e = attn::launch_prefill(ps, hs);
-                if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
-            }
+    // the class sees keys m' <= m - delta (positions more than window below).
+    // Classes are the batch of a banded launch over strided views; the first
+    // L % period classes have one row more than the others. Each row's
+    // epilogue merges its skip part with its window part, already in `out`.
+    const int delta = window / period + 1;
+    const int n = L / period, rem = L % period;
+    for (int b = 0; b < B; ++b) {
+        for (int part = 0; part < 2; ++part) {
+            const int r0 = part ? rem : 0;
+            const int ncls = part ? period - rem : rem;
+            const int nrows = part ? n : n + 1;
+            if (ncls <= 0 || nrows <= 0) continue;
+            attn::PrefillParams ps = pw;
+            ps.q = static_cast<const uint16_t*>(q->data) + b * q->stride_b + r0 * q->stride_s;
+            ps.q_sb = q->stride_s;
+            ps.q_ss = (int64_t)period * q->stride_s;
+            ps.k = static_cast<const uint16_t*>(k->data) + b * k->stride_b + r0 * k->stride_s;
+            ps.k_sb = k->stride_s;
+            ps.k_ss = (int64_t)period * k->stride_s;
+            ps.v = static_cast<const uint16_t*>(v->data) + b * v->stride_b + r0 * v->stride_s;
+            ps.v_sb = v->stride_s;
+            ps.v_ss = (int64_t)period * v->stride_s;
+            ps.out = static_cast<uint16_t*>(out->data) + b * out->stride_b + r0 * out->stride_s;
+            ps.o_sb = out->stride_s;
+            ps.o_ss = (int64_t)period * out->stride_s;
+            // lse, lse_w and alpha are [B, Hq, L] contiguous: the same class view
+            const int64_t base = (int64_t)b * Hq * L + r0;
+            ps.lse = lse ? lse + base : nullptr;
+            ps.lse_w = lse_w + base;
+            ps.alpha = alpha ? alpha + base : nullptr;
+            ps.lse_sb = 1;
+            ps.lse_sh = L;
+            ps.lse_ss = period;
+            ps.B = ncls;
+            ps.Lq = ps.Lkv = nrows;
+            ps.diag = -delta;
+            ps.window = -1;
+            ps.merge = 1;
+            e = attn::launch_prefill(ps, hs);
+            if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
         }
-    }
-
-    // 3. one softmax over both parts, with the priors
-    if (merge) {
-        attn::PiMergeParams pm;
-        pm.out = out->data;
-        pm.o_sb = out->stride_b;
-        pm.o_sh = out->stride_h;
-        pm.o_ss = out->stride_s;
-        pm.o_skip = has_skip ? o_skip : nullptr;
-        pm.lse_w = lse_w;
-        pm.lse_s = has_skip ? lse_s : nullptr;
-        pm.alpha = alpha;
-        pm.lse = lse;
-        pm.B = B;
-        pm.Hq = Hq;
-        pm.L = L;
-        pm.d = d;
-        e = attn::launch_pi_merge(pm, hs);
-        if (e != hipSuccess) return fail(ATTN_ERR_HIP, "merge launch: %s", hipGetErrorString(e));
     }
     return ATTN_OK;
 }

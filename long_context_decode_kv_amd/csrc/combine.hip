@@ -112,61 +112,6 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
     return hipGetLastError();
 }
 
-// pi-Attention prefill: the window part (O_w, lse_w) and the skip part
-// (O_s, lse_s) of one row are two partials of one softmax; with the gate
-// alpha their maxima move by ln(alpha) and ln(1 - alpha) (the log-prior of
-// the pi-Attention explainer's adaptive fusion, method section A), then
-//   M = max(m_w, m_s), w_x = exp(m_x - M), O = (w_w O_w + w_s O_s) / (w_w + w_s),
-//   lse = M + ln(w_w + w_s).
-// One wave per row, two dims per lane (d = 128).
-__global__ __launch_bounds__(256) void pi_merge_kernel(PiMergeParams p) {
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int64_t R = (int64_t)p.B * p.Hq * p.L;
-    if (r >= R) return;
-    const int i = (int)(r % p.L);
-    const int64_t bh = r / p.L;
-    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
-    float bw = 0.f, bs = 0.f;
-    if (p.alpha) {
-        const float a = fminf(fmaxf(p.alpha[r], 0.f), 1.f);
-        bw = logf(a);
-        bs = logf(1.f - a);
-    }
-    const float mw = p.lse_w[r] + bw;
-    const float ms = p.o_skip ? p.lse_s[r] + bs : kNegInf;
-    const float M = fmaxf(mw, ms);
-    uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)i * p.o_ss;
-    const uint32_t ow = reinterpret_cast<const uint32_t*>(orow)[lane];
-    float o0 = 0.f, o1 = 0.f, lse = kNegInf;
-    if (M != kNegInf) {
-        const float ww = (mw == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((mw - M) * kLog2e);
-        const float ws = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ms - M) * kLog2e);
-        const float z = ww + ws;
-        const float inv = 1.f / z;
-        o0 = ww * __builtin_bit_cast(float, ow << 16);
-        o1 = ww * __builtin_bit_cast(float, ow & 0xffff0000u);
-        if (ws > 0.f) {
-            const uint32_t os = reinterpret_cast<const uint32_t*>(p.o_skip + r * p.d)[lane];
-            o0 = fmaf(ws, __builtin_bit_cast(float, os << 16), o0);
-            o1 = fmaf(ws, __builtin_bit_cast(float, os & 0xffff0000u), o1);
-        }
-        o0 *= inv;
-        o1 *= inv;
-        lse = M + logf(z);
-    }
-    reinterpret_cast<uint32_t*>(orow)[lane] = (uint32_t)f32_to_bf16_rne(o0) | ((uint32_t)f32_to_bf16_rne(o1) << 16);
-    if (p.lse && lane == 0) p.lse[r] = lse;
-}
-
-hipError_t launch_pi_merge(const PiMergeParams& p, hipStream_t stream) {
-    if (p.d != 128) return hipErrorInvalidValue;
-    const int64_t R = (int64_t)p.B * p.Hq * p.L;
-    if (R == 0) return hipSuccess;
-    hipLaunchKernelGGL(pi_merge_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
-
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
     dim3 grid(p.R, (p.d + 31) / 32);
     hipLaunchKernelGGL(combine_partials_kernel, grid, dim3(256), 0, stream, p);

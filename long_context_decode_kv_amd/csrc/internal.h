@@ -119,6 +119,14 @@ struct PrefillParams {
     // Banded variant (band != 0): query i sits at position i + diag and sees
     // keys [position - window, position] (window < 0: no lower bound).
     int band, diag, window;
+    // Banded epilogue for pi-Attention (lse_w and alpha use the lse strides):
+    // merge 0: plain; 1: this launch computes the skip part of its rows and
+    // merges it with the window part already in `out` (its lse in lse_w),
+    // the parts weighted by the priors ln(alpha) and ln(1 - alpha);
+    // 2: the window part alone, shifted by ln(alpha).
+    int merge;
+    const float* lse_w;
+    const float* alpha;  // or nullptr: no prior
 };
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream);
@@ -130,19 +138,5 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
-// pi-Attention prefill, last step: per row, merge the window part (read from
-// and written back to `out`) with the skip part, each shifted by its
-// log-prior.
-struct PiMergeParams {
-    void* out;  // bf16 [B, Hq, L, d] view: the window part in, the result out
-    int64_t o_sb, o_sh, o_ss;
-    const uint16_t* o_skip;  // bf16 [B, Hq, L, d] contiguous, or nullptr (no skip part)
-    const float* lse_w;      // [B*Hq*L]
-    const float* lse_s;      // [B*Hq*L], or nullptr with o_skip
-    const float* alpha;      // [B*Hq*L] or nullptr (no prior)
-    float* lse;              // [B, Hq, L] contiguous, or nullptr
-    int B, Hq, L, d;
-};
-hipError_t launch_pi_merge(const PiMergeParams& p, hipStream_t stream);
 
 }  // namespace attn

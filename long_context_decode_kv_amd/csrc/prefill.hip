@@ -66,6 +66,7 @@ constexpr int kSlotBytes = 2 * kTileBytes;    // K tile, then V tile
 constexpr int kLdsBytes = kSlots * kSlotBytes;
 constexpr float kHeadroom = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -425,20 +426,60 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     const int qr = q0 + row;
     if (qr < p.Lq) {
         const bool empty = BAND && !(l_tot > 0.f);  // a banded row that saw no key
-        const float inv = empty ? 0.f : 1.0f / l_tot;
+        float inv = empty ? 0.f : 1.0f / l_tot;
+        float lse = empty ? kNegInf : m_run * kLn2 + logf(l_tot);
+        const int64_t li = b * p.lse_sb + h * p.lse_sh + (int64_t)qr * p.lse_ss;
         uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_ss;
+        float wprev = 0.f;  // weight of the part already in `out` (merge == 1)
+        if constexpr (BAND) {
+            if (p.merge) {
+                // pi-Attention's log-priors: + ln(alpha) on the window part,
+                // + ln(1 - alpha) on the skip part
+                float bw = 0.f, bs = 0.f;
+                if (p.alpha) {
+                    const float a = fminf(fmaxf(p.alpha[li], 0.f), 1.f);
+                    bw = logf(a);
+                    bs = logf(1.f - a);
+                }
+                if (p.merge == 2) {  // the window alone
+                    lse += bw;
+                    if (lse == kNegInf) inv = 0.f;
+                } else {  // this launch's part is the skip part; the window part is in out / lse_w
+                    const float mw = p.lse_w[li] + bw, ms = lse + bs;
+                    const float M = fmaxf(mw, ms);
+                    const float ww = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * kLog2e);
+                    const float ws = (ms == kNegInf) ? 0.f : fast_exp2((ms - M) * kLog2e);
+                    const float z = ww + ws;
+                    const float iz = (M == kNegInf) ? 0.f : 1.f / z;
+                    wprev = ww * iz;
+                    inv *= ws * iz;
+                    lse = (M == kNegInf) ? kNegInf : M + logf(z);
+                }
+            }
+        }
 #pragma unroll
         for (int dblk = 0; dblk < 4; ++dblk)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int d0 = 32 * dblk + 8 * jj + 4 * hb;
+                float o[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o[e] = oacc[dblk][4 * jj + e] * inv;
+                if (BAND && p.merge == 1) {
+                    const u32x2 prev = *reinterpret_cast<const u32x2*>(orow + d0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t w2 = prev[e >> 1];
+                        const float x = __builtin_bit_cast(float, (e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+                        o[e] = fmaf(wprev, x, o[e]);
+                    }
+                }
                 u32x2 pk;
-                pk[0] = pack_bf16(oacc[dblk][4 * jj] * inv, oacc[dblk][4 * jj + 1] * inv);
-                pk[1] = pack_bf16(oacc[dblk][4 * jj + 2] * inv, oacc[dblk][4 * jj + 3] * inv);
+                pk[0] = pack_bf16(o[0], o[1]);
+                pk[1] = pack_bf16(o[2], o[3]);
                 *reinterpret_cast<u32x2*>(orow + d0) = pk;
             }
-        if (p.lse && hb == 0)
-            p.lse[b * p.lse_sb + h * p.lse_sh + (int64_t)qr * p.lse_ss] = empty ? kNegInf : m_run * kLn2 + logf(l_tot);
+        if (p.lse && hb == 0) p.lse[li] = lse;
     }
 }
 

@@ -223,8 +223,8 @@ def test_pi_prefill_argument_errors(so):
     assert pi_prefill(so, d=64) == UNSUPPORTED
     assert pi_prefill(so, period=1 << 17) == UNSUPPORTED  # strided rows past the 32-bit buffer offsets
     assert pi_prefill(so, ws=None) == WORKSPACE
-    # skip outputs (bf16) and two lse arrays, each rounded up to 256 bytes
+    # the window part's lse, rounded up to 256 bytes
     need = lib.attn_prefill_pi_workspace_size(1, 8, 256, 128)
-    assert need == 8 * 256 * 128 * 2 + 2 * 8 * 256 * 4
+    assert need == 8 * 256 * 4
     assert pi_prefill(so, ws_bytes=need - 1) == WORKSPACE
     assert lib.attn_prefill_pi_workspace_size(0, 8, 256, 128) == 0
