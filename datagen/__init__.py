@@ -5,7 +5,8 @@ stream + Box-Muller, see ``datagen.c``) and encodes them into the storage
 formats the library reads. Random numbers never come from the GPU path.
 
 Tensor ids used by the workloads: Q=0, K=1, V=2, per-sequence lengths=3; the
-fp8 span of a two-precision cache: K=4, V=5, its lengths=6.
+fp8 span of a two-precision cache: K=4, V=5, its lengths=6; the pi-Attention
+gate alpha=7.
 """
 import ctypes
 import os
@@ -96,6 +97,14 @@ def uniform_int(seed, tensor_id, n, lo, hi):
     out = np.empty(n, dtype=np.int32)
     _load().dg_uniform_int(seed, tensor_id, n, lo, hi, _ptr(out))
     return out
+
+
+def uniform_f32(seed, tensor_id, shape, lo, hi):
+    """float32 uniform in [lo, hi): the top 53 bits of each stream word as a
+    fraction in [0, 1)."""
+    n = int(np.prod(shape))
+    u = (words(seed, tensor_id, n) >> np.uint64(11)).astype(np.float64) * (2.0 ** -53)
+    return (lo + (hi - lo) * u).astype(np.float32).reshape(shape)
 
 
 def words(seed, tensor_id, n):

@@ -26,7 +26,15 @@ WORKLOADS = {
             L=1048576, q="bf16", kv="e4m3", mul=1.0, causal=False, splits=1024),
     6: dict(name="two-precision KV decode, L=131072: first and last 10% bf16, the rest fp8-e4m3, 32q/8kv, d=128",
             kind="mixed", B=1, Hq=32, Hkv=8, d=128, L=131072, hi_frac=0.1, q="bf16", mul=0.5, causal=False),
+    7: dict(name="pi-Attention decode, bf16, L=131072, window 4096, period 64, 32q/8kv, d=128", kind="decode", B=1,
+            Hq=32, Hkv=8, d=128, L=131072, q="bf16", kv="bf16", mul=0.5, causal=True, window=4096, period=64),
+    8: dict(name="pi-Attention causal prefill, bf16, L=16384, window 512, period 64, 32q/8kv, d=128", kind="prefill",
+            B=1, Hq=32, Hkv=8, d=128, L=16384, q="bf16", kv="bf16", mul=1.0, causal=True, window=512, period=64),
 }
+
+# Tensor id of the pi-Attention gate alpha (one value per query row, uniform in
+# [0.05, 0.95]; a trained gate is not available, so any value in (0, 1) serves).
+TID_ALPHA = 7
 
 
 def _draw(fmt, seed, tid, shape, mul):
@@ -102,3 +110,10 @@ def make_mixed_inputs(wl=6, seed=None, B=None, Hq=None, Hkv=None, d=None, L=None
         lo_lens = uniform_int(seed, TID_LENS_LO, B * Hkv, int(lo_f * L_lo), int(hi_f * L_lo))
     return dict(q=q, k_hi=k_hi, v_hi=v_hi, k_lo=k_lo, v_lo=v_lo, k_scale=None if ks is None else ks.ravel(),
                 v_scale=None if vs is None else vs.ravel(), hi_lens=hi_lens, lo_lens=lo_lens)
+
+
+def make_alpha(wl, shape, seed=None):
+    """The gate alpha of a pi-Attention workload: uniform in [0.05, 0.95]."""
+    from . import uniform_f32
+    seed = wl if seed is None else seed
+    return uniform_f32(seed, TID_ALPHA, shape, 0.05, 0.95)
