@@ -46,6 +46,8 @@ def _load():
     lib.oracle_attention.restype = i32
     lib.oracle_pi_attention.argtypes = common + [i32, i32, vp, vp, i64, vp, vp, i32]
     lib.oracle_pi_attention.restype = i32
+    lib.oracle_backward.argtypes = common + [vp, vp, vp, vp, i32]
+    lib.oracle_backward.restype = i32
     lib.oracle_partial.argtypes = common + [i32, i32, i32, i64, i64, vp, vp, vp]
     lib.oracle_partial.restype = i32
     lib.oracle_energy.argtypes = common + [i32, i32, i32, vp]
@@ -140,6 +142,22 @@ def pi_attention(prob, window, period, alpha=None, rows=None, nthreads=None):
     if rc != 0:
         raise ValueError("oracle_pi_attention: bad arguments")
     return out, lse
+
+
+def backward(prob, dout, nthreads=None):
+    """Gradients of exact attention for output gradient dout (same layout and
+    dtype as q): returns (dq [B,Hq,Lq,d], dk [B,Hkv,Lcap,d], dv) in float64."""
+    lib = _load()
+    dout = np.ascontiguousarray(dout)
+    if dout.dtype != prob.q.dtype or dout.shape != prob.q.shape:
+        raise ValueError("dout must match q in shape and dtype")
+    dq = np.zeros(prob.q.shape, dtype=np.float64)
+    dk = np.zeros(prob.k.shape, dtype=np.float64)
+    dv = np.zeros(prob.k.shape, dtype=np.float64)
+    rc = lib.oracle_backward(*prob._common(), _p(dout), _p(dq), _p(dk), _p(dv), nthreads or _threads())
+    if rc != 0:
+        raise ValueError("oracle_backward: bad arguments")
+    return dq, dk, dv
 
 
 def partial(prob, b, h, i, j0, j1):

@@ -33,6 +33,14 @@
  *  energy F(zeta) = ln sum_J exp(s_j + zeta . v_j), so F(0) = lse and the
  *  gradient of F at 0 is O.
  *
+ * The backward pass (oracle_backward) differentiates the same definition: for
+ * a loss with gradient dO on the outputs, with z_ij = sigma q_i . k_j and P the
+ * softmax of each row over its visible keys,
+ *  dV_j = sum_i P_ij dO_i,   dP_ij = dO_i . v_j,   D_i = sum_j P_ij dP_ij,
+ *  dz_ij = P_ij (dP_ij - D_i),   dQ_i = sigma sum_j dz_ij k_j,
+ *  dK_j = sigma sum_i dz_ij q_i   (sums over every query head sharing the KV
+ *  head). It is pinned against finite differences of the forward.
+ *
  * A cache kept in two precisions (the ThriftAttention page: its introduction
  * gives each token or head a precision, its Physical AI Stack section keeps
  * the first and last tenth of the tokens in bf16) is, for one query, plain
@@ -314,6 +322,103 @@ static int run_rows(const problem* pp, const int64_t* rows, int64_t nrows, doubl
     for (int t = 0; t < nthreads; ++t) {
         jobs[t] = (row_job){&p, rows, nrows, t, nthreads, out, lse};
         pthread_create(&th[t], NULL, row_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+    return 0;
+}
+
+typedef struct {
+    const problem* p;
+    const void* dout;
+    int g0, ng; /* the (b, g) groups this thread owns: flat ids g0, g0 + ng, ... */
+    double *dq, *dk, *dv;
+} bwd_job;
+
+static void* bwd_worker(void* arg) {
+    bwd_job* j = (bwd_job*)arg;
+    const problem* p = j->p;
+    const int G = p->Hq / p->Hkv, d = p->d;
+    double* qd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dod = (double*)malloc(sizeof(double) * (size_t)d);
+    double* tmp = (double*)malloc(sizeof(double) * (size_t)d);
+    double* P = (double*)malloc(sizeof(double) * (size_t)(p->Lcap > 0 ? p->Lcap : 1));
+    double* dP = (double*)malloc(sizeof(double) * (size_t)(p->Lcap > 0 ? p->Lcap : 1));
+    for (int flat = j->g0; flat < p->B * p->Hkv; flat += j->ng) {
+        const int b = flat / p->Hkv, g = flat % p->Hkv;
+        for (int h = g * G; h < (g + 1) * G; ++h) {
+            for (int i = 0; i < p->Lq; ++i) {
+                const int64_t hi = visible_end(p, b, i);
+                double* dqi = j->dq + (((int64_t)b * p->Hq + h) * p->Lq + i) * d;
+                for (int c = 0; c < d; ++c) dqi[c] = 0.0;
+                if (hi <= 0) continue;
+                load_q_row(p, b, h, i, qd);
+                const int64_t off = (((int64_t)b * p->Hq + h) * p->Lq + i) * d;
+                for (int c = 0; c < d; ++c) dod[c] = elem(j->dout, p->q_dtype, off + c);
+                /* P: the softmax of the row, by the definition */
+                double mx = -INFINITY;
+                for (int64_t jj = 0; jj < hi; ++jj) {
+                    load_kv_row(p, p->k, p->k_scale, b, g, jj, tmp);
+                    P[jj] = score(p, qd, tmp);
+                    if (P[jj] > mx) mx = P[jj];
+                }
+                double z = 0.0;
+                for (int64_t jj = 0; jj < hi; ++jj) {
+                    P[jj] = exp(P[jj] - mx);
+                    z += P[jj];
+                }
+                double D = 0.0;
+                for (int64_t jj = 0; jj < hi; ++jj) {
+                    P[jj] /= z;
+                    load_kv_row(p, p->v, p->v_scale, b, g, jj, tmp);
+                    double acc = 0.0;
+                    for (int c = 0; c < d; ++c) acc += dod[c] * tmp[c];
+                    dP[jj] = acc;
+                    D += P[jj] * acc;
+                }
+                for (int64_t jj = 0; jj < hi; ++jj) {
+                    const double dz = P[jj] * (dP[jj] - D);
+                    double* dkj = j->dk + (((int64_t)b * p->Hkv + g) * p->Lcap + jj) * d;
+                    double* dvj = j->dv + (((int64_t)b * p->Hkv + g) * p->Lcap + jj) * d;
+                    load_kv_row(p, p->k, p->k_scale, b, g, jj, tmp);
+                    for (int c = 0; c < d; ++c) {
+                        dqi[c] += p->scale * dz * tmp[c];
+                        dkj[c] += p->scale * dz * qd[c];
+                        dvj[c] += P[jj] * dod[c];
+                    }
+                }
+            }
+        }
+    }
+    free(qd);
+    free(dod);
+    free(tmp);
+    free(P);
+    free(dP);
+    return NULL;
+}
+
+/*
+ * Gradients of exact attention: given dout [B,Hq,Lq,d] (the q dtype), writes
+ * dq [B,Hq,Lq,d], dk and dv [B,Hkv,Lcap,d] (double, zero for keys no query
+ * sees). Arguments otherwise as oracle_attention. Returns 0, or 1 on a bad
+ * argument.
+ */
+int oracle_backward(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype, const float* k_scale,
+                    const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int Lq, int Lcap, int d,
+                    double scale, int causal, const void* dout, double* dq, double* dk, double* dv, int nthreads) {
+    problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, kv_lens, B, Hq, Hkv, Lq, Lcap, d, scale, causal};
+    if (check_problem(&p) || !dout) return 1;
+    const int64_t nkv = (int64_t)B * Hkv * Lcap * d;
+    for (int64_t x = 0; x < nkv; ++x) dk[x] = dv[x] = 0.0;
+    const int groups = B * Hkv;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > groups) nthreads = groups;
+    pthread_t th[256];
+    bwd_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (bwd_job){&p, dout, t, nthreads, dq, dk, dv};
+        pthread_create(&th[t], NULL, bwd_worker, &jobs[t]);
     }
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
     return 0;

@@ -592,3 +592,50 @@ def test_pi_is_the_merge_of_its_window_and_its_skip_keys():
         merged = oracle.finalize(oracle.merge((o_l, m_l + math.log(a), l_l), (o_s, m_s + math.log(1 - a), l_s)))
         np.testing.assert_allclose(out[h], merged[0], rtol=1e-12, atol=1e-14)
         assert abs(lse[h] - merged[1]) < 1e-12
+
+
+# ------------------------------------------------------------- backward
+# Gradients of a loss L = sum(dO * O) with respect to q, k and v.
+
+def _loss(q, k, v, dout, **kw):
+    out, _ = oracle.attention(oracle.Problem(q, k, v, **kw))
+    return float((out.reshape(dout.shape) * dout).sum())
+
+
+@pytest.mark.parametrize("causal,Lq,lens", [(True, 6, None), (False, 6, None), (True, 3, None), (True, 6, [4])])
+def test_backward_matches_central_differences(causal, Lq, lens):
+    B, Hq, Hkv, L, d = 1, 4, 2, 6, 5
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((B, Hq, Lq, d))
+    k = rng.standard_normal((B, Hkv, L, d))
+    v = rng.standard_normal((B, Hkv, L, d))
+    dout = rng.standard_normal((B, Hq, Lq, d))
+    kw = dict(causal=causal, scale=0.6, kv_lens=None if lens is None else np.array(lens, np.int32))
+    dq, dk, dv = oracle.backward(oracle.Problem(q, k, v, **kw), dout)
+    h = 1e-5
+    for name, x, g in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"q": q, "k": k, "v": v}
+            args[name] = xp
+            lp = _loss(args["q"], args["k"], args["v"], dout, **kw)
+            args[name] = xm
+            lm = _loss(args["q"], args["k"], args["v"], dout, **kw)
+            num[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+def test_backward_key_gradients_sum_to_zero():
+    # adding a constant to every logit of a row changes nothing, so the logit
+    # gradients of a row sum to zero, and so do the key gradients of a head
+    B, Hq, Hkv, L, d = 2, 8, 2, 40, 16
+    q, k, v = rand_f32(B, Hq, 40, d), rand_f32(B, Hkv, L, d), rand_f32(B, Hkv, L, d)
+    dout = rand_f32(B, Hq, 40, d)
+    dq, dk, dv = oracle.backward(oracle.Problem(q, k, v, causal=True), dout)
+    assert np.abs(dk.sum(axis=2)).max() < 1e-10
+    # and the value gradients of a head add up to the sum of its rows' dO
+    np.testing.assert_allclose(dv.sum(axis=2), dout.astype(np.float64).reshape(B, Hkv, -1, d).sum(axis=2),
+                               rtol=1e-12, atol=1e-10)
