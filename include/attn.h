@@ -329,6 +329,35 @@ ATTN_API attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k,
 ATTN_API size_t attn_prefill_pi_workspace_size(int B, int Hq, int L, int d);
 
 /*
+ * Backward pass of attn_prefill: the gradients of a loss with respect to q, k
+ * and v, given its gradient dout with respect to the output. Attention is the
+ * gradient of a scalar energy function (Tree Attention explainer, section 3);
+ * this differentiates the same definition once more. With logits z = sigma q.k,
+ * P the softmax of each row over its visible keys and D_i = dout_i . out_i:
+ *   dv_j = sum_i P_ij dout_i,   dz_ij = P_ij (dout_i . v_j - D_i),
+ *   dq_i = sigma sum_j dz_ij k_j,   dk_j = sigma sum_i dz_ij q_i,
+ * dk and dv summing over the query heads that share a KV head. P is
+ * recomputed from `lse`; no L x L matrix is stored.
+ *
+ * q, k, v, softmax_scale, causal, B, Hq, Hkv, d, Lq, Lkv: as passed to
+ * attn_prefill (bf16, d = 128). out and lse: what attn_prefill returned for
+ * them (lse [B, Hq, Lq] contiguous, required). dout: bf16 like out.
+ * dq [B, Hq, Lq, d], dk and dv [B, Hkv, Lkv, d]: all bf16 or all fp32,
+ * written entirely (zero for keys no query sees); strided views allowed.
+ * workspace: attn_prefill_backward_workspace_size(B, Hq, Lq) bytes of device
+ * memory, 16-byte aligned, no preparation needed.
+ * Deterministic: no atomics. P and dz enter the products as bf16.
+ */
+ATTN_API attn_status attn_prefill_backward(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                           const attn_tensor* out, const float* lse, const attn_tensor* dout, int B,
+                                           int Hq, int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal,
+                                           attn_tensor* dq, attn_tensor* dk, attn_tensor* dv, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of attn_prefill_backward (0 on a bad argument). */
+ATTN_API size_t attn_prefill_backward_workspace_size(int B, int Hq, int Lq);
+
+/*
  * Merge S partials per row into the exact normalised result (the reduction
  * step of the Tree Attention explainer, section 3, on one device): with
  * m = max_s m_s and w_s = exp(m_s - m), O = sum_s w_s o_s / sum_s w_s l_s and

@@ -18,7 +18,7 @@ __all__ = [
     "attn_decode_plan",
     "attn_decode", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
     "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi", "attn_decode_pi_splits", "attn_prefill_pi",
-    "attn_prefill_pi_workspace_size",
+    "attn_prefill_pi_workspace_size", "attn_prefill_backward", "attn_prefill_backward_workspace_size",
 ]
 
 ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
@@ -89,6 +89,11 @@ def load_library():
     lib.attn_prefill_pi.restype = i32
     lib.attn_prefill_pi_workspace_size.argtypes = [i32, i32, i32, i32]
     lib.attn_prefill_pi_workspace_size.restype = ctypes.c_size_t
+    lib.attn_prefill_backward.argtypes = [tp, tp, tp, tp, vp, tp, i32, i32, i32, i32, i32, i32, f32, i32, tp, tp, tp, vp,
+                                          ctypes.c_size_t, vp]
+    lib.attn_prefill_backward.restype = i32
+    lib.attn_prefill_backward_workspace_size.argtypes = [i32, i32, i32]
+    lib.attn_prefill_backward_workspace_size.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -378,3 +383,34 @@ def attn_prefill_pi(q, k, v, window, period, alpha=None, softmax_scale=0.0, out=
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     _check(st)
     return out, lse
+
+
+def attn_prefill_backward_workspace_size(B, Hq, Lq):
+    return load_library().attn_prefill_backward_workspace_size(B, Hq, Lq)
+
+
+def attn_prefill_backward(q, k, v, out, lse, dout, causal=True, softmax_scale=0.0, dq=None, dk=None, dv=None,
+                          grad_dtype=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of attn_prefill for output gradient dout; out and lse are the forward's results."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    Hkv, Lkv = k.shape[1], k.shape[2]
+    gd = grad_dtype or q.dtype
+    if dq is None:
+        dq = torch.empty(q.shape, dtype=gd, device=q.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=gd, device=q.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=gd, device=q.device)
+    if not lse.is_contiguous() or lse.dtype != torch.float32 or lse.numel() != B * Hq * Lq:
+        raise ValueError("lse must be the forward's contiguous float32 [B, Hq, Lq]")
+    if workspace is None:
+        workspace = torch.empty(lib.attn_prefill_backward_workspace_size(B, Hq, Lq), dtype=torch.uint8, device=q.device)
+    ts = [_tensor(t) for t in (q, k, v, out, dout, dq, dk, dv)]
+    st = lib.attn_prefill_backward(ctypes.byref(ts[0]), ctypes.byref(ts[1]), ctypes.byref(ts[2]), ctypes.byref(ts[3]),
+                                   _ptr(lse), ctypes.byref(ts[4]), B, Hq, Hkv, d, Lq, Lkv, float(softmax_scale),
+                                   int(bool(causal)), ctypes.byref(ts[5]), ctypes.byref(ts[6]), ctypes.byref(ts[7]),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream, q.device))
+    _check(st)
+    return dq, dk, dv

@@ -810,4 +810,78 @@ attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const at
     return ATTN_OK;
 }
 
+size_t attn_prefill_backward_workspace_size(int B, int Hq, int Lq) {
+    if (B <= 0 || Hq <= 0 || Lq <= 0) return 0;
+    return round_up((size_t)B * Hq * Lq * 4, 256);
+}
+
+attn_status attn_prefill_backward(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                  const attn_tensor* out, const float* lse, const attn_tensor* dout, int B, int Hq,
+                                  int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal, attn_tensor* dq,
+                                  attn_tensor* dk, attn_tensor* dv, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    g_last_error[0] = 0;
+    attn_status st;
+    if ((st = check_prefill(q, k, v, out, B, Hq, Hkv, d, Lq, Lkv, softmax_scale, causal))) return st;
+    if ((st = check_tensor(dout, "dout", true)) || (st = check_tensor(dq, "dq", false)) ||
+        (st = check_tensor(dk, "dk", false)) || (st = check_tensor(dv, "dv", false)))
+        return st;
+    if (!lse) return fail(ATTN_ERR_INVALID_ARG, "lse (from the forward pass) is required");
+    if (dout->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dout must be bf16");
+    if (dq->dtype != dk->dtype || dq->dtype != dv->dtype || (dq->dtype != ATTN_BF16 && dq->dtype != ATTN_F32))
+        return fail(ATTN_ERR_UNSUPPORTED, "dq, dk and dv must all be bf16 or all fp32");
+    if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
+    if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+    const size_t need = attn_prefill_backward_workspace_size(B, Hq, Lq);
+    if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
+    const float sc = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf((float)d);
+    attn::BackwardParams p;
+    p.q = q->data;
+    p.q_sb = q->stride_b;
+    p.q_sh = q->stride_h;
+    p.q_ss = q->stride_s;
+    p.k = k->data;
+    p.k_sb = k->stride_b;
+    p.k_sh = k->stride_h;
+    p.k_ss = k->stride_s;
+    p.v = v->data;
+    p.v_sb = v->stride_b;
+    p.v_sh = v->stride_h;
+    p.v_ss = v->stride_s;
+    p.o = out->data;
+    p.o_sb = out->stride_b;
+    p.o_sh = out->stride_h;
+    p.o_ss = out->stride_s;
+    p.dout = dout->data;
+    p.do_sb = dout->stride_b;
+    p.do_sh = dout->stride_h;
+    p.do_ss = dout->stride_s;
+    p.lse = lse;
+    p.delta = static_cast<float*>(workspace);
+    p.dq = dq->data;
+    p.dq_sb = dq->stride_b;
+    p.dq_sh = dq->stride_h;
+    p.dq_ss = dq->stride_s;
+    p.dk = dk->data;
+    p.dk_sb = dk->stride_b;
+    p.dk_sh = dk->stride_h;
+    p.dk_ss = dk->stride_s;
+    p.dv = dv->data;
+    p.dv_sb = dv->stride_b;
+    p.dv_sh = dv->stride_h;
+    p.dv_ss = dv->stride_s;
+    p.grad_dtype = dq->dtype == ATTN_BF16 ? attn::DT_BF16 : attn::DT_F32;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.d = d;
+    p.Lq = Lq;
+    p.Lkv = Lkv;
+    p.causal = causal ? 1 : 0;
+    p.scale_log2 = sc * kLog2e;
+    hipError_t e = attn::launch_backward(p, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(ATTN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+    return ATTN_OK;
+}
+
 }  // extern "C"

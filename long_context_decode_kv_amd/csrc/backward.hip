@@ -1,0 +1,351 @@
+// Backward pass of exact attention for gfx950 (bf16 inputs, head dim 128).
+//
+// The gradient of the attention output with respect to its inputs (attention
+// as the gradient of a scalar energy function is the starting point of the
+// Tree Attention explainer, section 3; the backward pass differentiates that
+// forward once more). With logits z = sigma q.k, P the row softmax over the
+// visible keys, O = P V and the incoming gradient dO:
+//   D_i = dO_i . O_i,  dP_ij = dO_i . v_j,  dz_ij = P_ij (dP_ij - D_i),
+//   dV_j = sum_i P_ij dO_i,  dK_j = sigma sum_i dz_ij q_i,  dQ_i = sigma sum_j dz_ij k_j.
+// P is recomputed from the forward's lse (P_ij = exp(z_ij - lse_i)), so
+// nothing of size L x L is stored.
+//
+// Three kernels, no atomics (results are deterministic):
+//  * bwd_prep:  D per row (one wave per row).
+//  * bwd_dkdv:  one workgroup per 64-key block of one KV head; it walks the
+//    64-row query blocks of every query head of the group that see the block,
+//    recomputes P and dz for the 64 x 64 tile, and accumulates dV = P^T dO and
+//    dK = dz^T Q in registers.
+//  * bwd_dq:    one workgroup per 64-row query block of one query head; it
+//    walks the key blocks the rows see and accumulates dQ = dz K.
+// Every product runs on v_mfma_f32_32x32x16_bf16 with 32 x 32 tiles, one or
+// two per wave (4 waves per workgroup). Operands come from LDS tiles padded
+// to 16 bytes past every row, so the 16-byte fragment reads of 16 lanes hit
+// distinct banks; the products that contract over the sequence read
+// transposed copies of Q, dO and K written while staging. P and dz are
+// rounded to bf16 as MFMA operands, like P in the forward pass.
+#include "internal.h"
+
+namespace attn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBlk = 64;                 // rows or keys per block
+constexpr int kD = 128;                  // head dim
+constexpr int kPitch = kD * 2 + 16;      // bytes per padded [.][128] bf16 row
+constexpr int kTPitch = kBlk * 2 + 16;   // bytes per padded [.][64] bf16 row
+constexpr float kLog2e = 1.44269504088896340736f;
+constexpr float kInf = __builtin_huge_valf();
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row (M index) of accumulator register j of a lane in half hb of a 32 x 32
+// MFMA tile; the lane's column (N index) is lane & 31.
+__device__ __forceinline__ int acc_row(int j, int hb) { return 8 * (j >> 2) + 4 * hb + (j & 3); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const char* lds, int byte_off) {
+    return *reinterpret_cast<const bf16x8*>(lds + byte_off);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Stages a 64 x 128 bf16 block (rows row0 .. row0 + 63 of a [rows][128] view
+// with element row stride `ss`; rows past `nrows` repeat the last row) into
+// `dst` (row-major, kPitch) and, if `dstT` is set, its transpose into `dstT`
+// ([128][64], kTPitch). 256 threads; lane r of a wave takes row r.
+__device__ __forceinline__ void stage_block(const uint16_t* base, int64_t ss, int row0, int nrows, char* dst,
+                                            char* dstT, int tid) {
+    const int r = tid & 63;
+    const int row = min(row0 + r, nrows - 1);
+    const uint16_t* src = base + (int64_t)row * ss;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int c = (tid >> 6) + 4 * i;  // 16-byte chunk: dims 8c .. 8c + 7
+        const u32x4 x = *reinterpret_cast<const u32x4*>(src + 8 * c);
+        *reinterpret_cast<u32x4*>(dst + r * kPitch + 16 * c) = x;
+        if (dstT) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                *reinterpret_cast<uint16_t*>(dstT + (8 * c + 2 * e) * kTPitch + 2 * r) = (uint16_t)(x[e] & 0xffff);
+                *reinterpret_cast<uint16_t*>(dstT + (8 * c + 2 * e + 1) * kTPitch + 2 * r) = (uint16_t)(x[e] >> 16);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- D = rowsum(dO * O)
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BackwardParams p) {
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int64_t R = (int64_t)p.B * p.Hq * p.Lq;
+    if (r >= R) return;
+    const int i = (int)(r % p.Lq);
+    const int64_t bh = r / p.Lq;
+    const int h = (int)(bh % p.Hq), b = (int)(bh / p.Hq);
+    const uint32_t o = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.o) + b * p.o_sb + h * p.o_sh +
+                                                         (int64_t)i * p.o_ss)[lane];
+    const uint32_t g = reinterpret_cast<const uint32_t*>(static_cast<const uint16_t*>(p.dout) + b * p.do_sb +
+                                                         h * p.do_sh + (int64_t)i * p.do_ss)[lane];
+    float acc = fmaf(bf16_lo(o), bf16_lo(g), bf16_hi(o) * bf16_hi(g));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) p.delta[r] = acc;
+}
+
+// Stores one 32 x 32 fp32 accumulator tile whose rows are sequence positions
+// (row0 + acc_row) and columns dims (col0 + lane & 31), as bf16 or fp32.
+__device__ __forceinline__ void store_tile(void* base, int dtype, int64_t ss, int row0, int nrows, int col0,
+                                           const f32x16& acc, float mul, int lane) {
+    const int hb = lane >> 5, col = col0 + (lane & 31);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int row = row0 + acc_row(j, hb);
+        if (row < nrows) {
+            const float v = acc[j] * mul;
+            if (dtype == DT_BF16) {
+                static_cast<__bf16*>(base)[(int64_t)row * ss + col] = (__bf16)v;
+            } else {
+                static_cast<float*>(base)[(int64_t)row * ss + col] = v;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- dK, dV
+struct DkdvLds {
+    char q[kBlk * kPitch];
+    char dout[kBlk * kPitch];
+    char qT[kD * kTPitch];
+    char doutT[kD * kTPitch];
+    char pT[kBlk * kTPitch];   // P^T  [key][row] bf16
+    char dsT[kBlk * kTPitch];  // dz^T [key][row] bf16
+    float lse2[kBlk];          // lse * log2(e), +inf for rows without weights
+    float delta[kBlk];
+};
+
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BackwardParams p) {
+    __shared__ __attribute__((aligned(16))) DkdvLds s;
+    const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5, w = tid >> 6;
+    const int kt = w >> 1;  // this wave's 32-key half of the block
+    const int rt = w & 1;   // its 32-row half for S and dP; its 64-dim half for dK and dV
+    const int G = p.Hq / p.Hkv;
+    const int off = p.Lkv - p.Lq;  // query i sits at position i + off
+    const int key0 = kb * kBlk;
+    const float c2 = p.scale_log2;
+
+    // K and V of the wave's 32 keys as B operands (column = key, k = dims)
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + b * p.k_sb + g * p.k_sh;
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + b * p.v_sb + g * p.v_sh;
+    const int mykey = min(key0 + 32 * kt + (lane & 31), p.Lkv - 1);
+    bf16x8 kf[8], vf[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        kf[ks] = *reinterpret_cast<const bf16x8*>(kbase + (int64_t)mykey * p.k_ss + 16 * ks + 8 * hb);
+        vf[ks] = *reinterpret_cast<const bf16x8*>(vbase + (int64_t)mykey * p.v_ss + 16 * ks + 8 * hb);
+    }
+    f32x16 dk[2], dv[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dk[u][j] = dv[u][j] = 0.f;
+
+    // query blocks whose rows see some key of this block
+    const int nqb = (p.Lq + kBlk - 1) / kBlk;
+    const int qb0 = p.causal ? max(0, (key0 - off) / kBlk) : 0;
+    for (int h = g * G; h < (g + 1) * G; ++h) {
+        const uint16_t* qbase = static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
+        const uint16_t* dobase = static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh;
+        const float* lse = p.lse + ((int64_t)b * p.Hq + h) * p.Lq;
+        const float* delta = p.delta + ((int64_t)b * p.Hq + h) * p.Lq;
+        for (int qb = qb0; qb < nqb; ++qb) {
+            const int row0 = qb * kBlk;
+            __syncthreads();  // the previous tile's readers are done
+            stage_block(qbase, p.q_ss, row0, p.Lq, s.q, s.qT, tid);
+            stage_block(dobase, p.do_ss, row0, p.Lq, s.dout, s.doutT, tid);
+            if (tid < kBlk) {
+                const int i = row0 + tid;
+                const float l = i < p.Lq ? lse[i] : -kInf;
+                s.lse2[tid] = (l == -kInf) ? kInf : l * kLog2e;
+                s.delta[tid] = i < p.Lq ? delta[i] : 0.f;
+            }
+            __syncthreads();
+
+            // S and dP for rows 32rt.., keys 32kt.. (row = M, key = N)
+            f32x16 sa = {}, dpa = {};
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int ao = (32 * rt + (lane & 31)) * kPitch + 32 * ks + 16 * hb;
+                sa = mfma(lds_frag(s.q, ao), kf[ks], sa);
+                dpa = mfma(lds_frag(s.dout, ao), vf[ks], dpa);
+            }
+            // P and dz; stored transposed ([key][row]) as bf16, four rows per write
+            const int key = key0 + 32 * kt + (lane & 31);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                float pv[4], dz[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * t + e;
+                    const int r = 32 * rt + acc_row(j, hb);
+                    const int i = row0 + r;
+                    const bool vis = key < p.Lkv && i < p.Lq && (!p.causal || key <= i + off);
+                    pv[e] = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -s.lse2[r])) : 0.f;
+                    dz[e] = pv[e] * (dpa[j] - s.delta[r]);
+                }
+                const int rbyte = 2 * (32 * rt + 8 * t + 4 * hb);
+                const int kr = 32 * kt + (lane & 31);
+                *reinterpret_cast<u32x2*>(s.pT + kr * kTPitch + rbyte) = (u32x2){pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
+                *reinterpret_cast<u32x2*>(s.dsT + kr * kTPitch + rbyte) = (u32x2){pack_bf16(dz[0], dz[1]), pack_bf16(dz[2], dz[3])};
+            }
+            __syncthreads();
+
+            // dV += P^T dO and dK += dz^T Q for keys 32kt.., dims 64rt + 32u..
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ao = (32 * kt + (lane & 31)) * kTPitch + 32 * ks + 16 * hb;
+                const bf16x8 pa = lds_frag(s.pT, ao), da = lds_frag(s.dsT, ao);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int bo = (64 * rt + 32 * u + (lane & 31)) * kTPitch + 32 * ks + 16 * hb;
+                    dv[u] = mfma(pa, lds_frag(s.doutT, bo), dv[u]);
+                    dk[u] = mfma(da, lds_frag(s.qT, bo), dk[u]);
+                }
+            }
+        }
+    }
+    const float sigma = p.scale_log2 / kLog2e;
+    void* dkb = static_cast<char*>(p.dk) + (b * p.dk_sb + g * p.dk_sh) * (p.grad_dtype == DT_BF16 ? 2 : 4);
+    void* dvb = static_cast<char*>(p.dv) + (b * p.dv_sb + g * p.dv_sh) * (p.grad_dtype == DT_BF16 ? 2 : 4);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        store_tile(dkb, p.grad_dtype, p.dk_ss, key0 + 32 * kt, p.Lkv, 64 * rt + 32 * u, dk[u], sigma, lane);
+        store_tile(dvb, p.grad_dtype, p.dv_ss, key0 + 32 * kt, p.Lkv, 64 * rt + 32 * u, dv[u], 1.f, lane);
+    }
+}
+
+// ---------------------------------------------------------------- dQ
+struct DqLds {
+    char k[kBlk * kPitch];
+    char v[kBlk * kPitch];
+    char kT[kD * kTPitch];
+    char ds[kBlk * kTPitch];  // dz [row][key] bf16
+};
+
+__global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
+    __shared__ __attribute__((aligned(16))) DqLds s;
+    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5, w = tid >> 6;
+    const int rt = w & 1;   // this wave's 32-row half
+    const int kt = w >> 1;  // its 32-key half for S and dP; its 64-dim half for dQ
+    const int G = p.Hq / p.Hkv, g = h / G;
+    const int off = p.Lkv - p.Lq;
+    const int row0 = qb * kBlk;
+    const float c2 = p.scale_log2;
+
+    // Q and dO of the wave's 32 rows as B operands (column = row, k = dims)
+    const int myrow = row0 + 32 * rt + (lane & 31);
+    const int qr = min(myrow, p.Lq - 1);
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)qr * p.q_ss;
+    const uint16_t* dorow = static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)qr * p.do_ss;
+    bf16x8 qf[8], df[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hb);
+        df[ks] = *reinterpret_cast<const bf16x8*>(dorow + 16 * ks + 8 * hb);
+    }
+    float lse2 = kInf, dlt = 0.f;
+    if (myrow < p.Lq) {
+        const float l = p.lse[((int64_t)b * p.Hq + h) * p.Lq + myrow];
+        lse2 = (l == -kInf) ? kInf : l * kLog2e;
+        dlt = p.delta[((int64_t)b * p.Hq + h) * p.Lq + myrow];
+    }
+    f32x16 dq[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dq[u][j] = 0.f;
+
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + b * p.k_sb + g * p.k_sh;
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + b * p.v_sb + g * p.v_sh;
+    const int nkb_all = (p.Lkv + kBlk - 1) / kBlk;
+    const int last_key = min(p.Lkv - 1, row0 + kBlk - 1 + off);
+    const int nkb = p.causal ? (last_key >= 0 ? last_key / kBlk + 1 : 0) : nkb_all;
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int key0 = kb * kBlk;
+        __syncthreads();
+        stage_block(kbase, p.k_ss, key0, p.Lkv, s.k, s.kT, tid);
+        stage_block(vbase, p.v_ss, key0, p.Lkv, s.v, nullptr, tid);
+        __syncthreads();
+
+        // S^T and dP^T for keys 32kt.. (M) and rows 32rt.. (N)
+        f32x16 sa = {}, dpa = {};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const int ao = (32 * kt + (lane & 31)) * kPitch + 32 * ks + 16 * hb;
+            sa = mfma(lds_frag(s.k, ao), qf[ks], sa);
+            dpa = mfma(lds_frag(s.v, ao), df[ks], dpa);
+        }
+        // dz for this lane's row, stored as [row][key] bf16, four keys per write
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float dz[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * t + e;
+                const int key = key0 + 32 * kt + acc_row(j, hb);
+                const bool vis = key < p.Lkv && myrow < p.Lq && (!p.causal || key <= myrow + off);
+                const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -lse2)) : 0.f;
+                dz[e] = pv * (dpa[j] - dlt);
+            }
+            const int kbyte = 2 * (32 * kt + 8 * t + 4 * hb);
+            *reinterpret_cast<u32x2*>(s.ds + (32 * rt + (lane & 31)) * kTPitch + kbyte) =
+                (u32x2){pack_bf16(dz[0], dz[1]), pack_bf16(dz[2], dz[3])};
+        }
+        __syncthreads();
+
+        // dQ += dz K for rows 32rt.., dims 64kt + 32u..
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 a = lds_frag(s.ds, (32 * rt + (lane & 31)) * kTPitch + 32 * ks + 16 * hb);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                dq[u] = mfma(a, lds_frag(s.kT, (64 * kt + 32 * u + (lane & 31)) * kTPitch + 32 * ks + 16 * hb), dq[u]);
+        }
+    }
+    const float sigma = p.scale_log2 / kLog2e;
+    void* dqb = static_cast<char*>(p.dq) + (b * p.dq_sb + h * p.dq_sh) * (p.grad_dtype == DT_BF16 ? 2 : 4);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) store_tile(dqb, p.grad_dtype, p.dq_ss, row0 + 32 * rt, p.Lq, 64 * kt + 32 * u, dq[u], sigma, lane);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
+    if (p.d != kD) return hipErrorInvalidValue;
+    const int64_t R = (int64_t)p.B * p.Hq * p.Lq;
+    if (R == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((p.Lkv + kBlk - 1) / kBlk, p.Hkv, p.B), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3((p.Lq + kBlk - 1) / kBlk, p.Hq, p.B), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace attn

@@ -138,5 +138,32 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 
+// Backward pass of (causal or full) attention, bf16 inputs, d = 128.
+struct BackwardParams {
+    const void* q;
+    int64_t q_sb, q_sh, q_ss;
+    const void* k;
+    int64_t k_sb, k_sh, k_ss;
+    const void* v;
+    int64_t v_sb, v_sh, v_ss;
+    const void* o;  // the forward output
+    int64_t o_sb, o_sh, o_ss;
+    const void* dout;
+    int64_t do_sb, do_sh, do_ss;
+    const float* lse;  // [B, Hq, Lq] contiguous, from the forward
+    float* delta;      // [B, Hq, Lq] workspace: rowsum(dO * O)
+    void* dq;
+    int64_t dq_sb, dq_sh, dq_ss;
+    void* dk;
+    int64_t dk_sb, dk_sh, dk_ss;
+    void* dv;
+    int64_t dv_sb, dv_sh, dv_ss;
+    int grad_dtype;  // DT_BF16 or DT_F32 for dq, dk, dv
+    int B, Hq, Hkv, d, Lq, Lkv;
+    int causal;
+    float scale_log2;
+};
+hipError_t launch_backward(const BackwardParams& p, hipStream_t stream);
+
 
 }  // namespace attn

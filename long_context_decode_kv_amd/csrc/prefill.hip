@@ -324,11 +324,12 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         // Lazy running max: the exponentials use m_run as long as no score of
         // the lane exceeds it by the headroom; only then (wave vote) the row max
         // over the lane pair is taken and the accumulators rescaled.
-        float lm = kNegInf;
+        // one chain of three-input maxima (two new scores per step)
+        float lm = fmaxf(sacc[0][0], sacc[0][1]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int jj = 0; jj < 16; jj += 2) lm = fmaxf(lm, fmaxf(sacc[kb][jj], sacc[kb][jj + 1]));
+            for (int jj = kb ? 0 : 2; jj < 16; jj += 2) lm = fmaxf(fmaxf(lm, sacc[kb][jj]), sacc[kb][jj + 1]);
         if (__builtin_amdgcn_ballot_w64(lm * c2 > m_run + kHeadroom) != 0) {
             const float m_new = fmaxf(m_run, pair_max(lm) * c2);
             const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);

@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported(so):
                           "attn_decode_workspace_size", "attn_decode_workspace_init", "attn_decode_plan",
                           "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials",
                           "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi",
-                          "attn_decode_pi_splits", "attn_prefill_pi", "attn_prefill_pi_workspace_size"}
+                          "attn_decode_pi_splits", "attn_prefill_pi", "attn_prefill_pi_workspace_size",
+                          "attn_prefill_backward", "attn_prefill_backward_workspace_size"}
     nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
     for n in names:
@@ -228,3 +229,26 @@ def test_pi_prefill_argument_errors(so):
     assert need == 8 * 256 * 4
     assert pi_prefill(so, ws_bytes=need - 1) == WORKSPACE
     assert lib.attn_prefill_pi_workspace_size(0, 8, 256, 128) == 0
+
+
+def backward(so, dtype=BF16, gdt=F32, d=128, Lq=256, Lkv=256, causal=1, Hq=8, Hkv=2, lse=FAKE, ws=FAKE,
+             ws_bytes=1 << 30):
+    q = T(dtype, Hq * Lq * d, Lq * d, d)
+    k = T(dtype, Hkv * Lkv * d, Lkv * d, d)
+    g = T(gdt, Hq * Lq * d, Lq * d, d)
+    gk = T(gdt, Hkv * Lkv * d, Lkv * d, d)
+    return so.attn_prefill_backward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), ctypes.byref(q), lse,
+                                    ctypes.byref(q), 1, Hq, Hkv, d, Lq, Lkv, 0.0, causal, ctypes.byref(g),
+                                    ctypes.byref(gk), ctypes.byref(gk), ws, ws_bytes, None)
+
+
+def test_backward_argument_errors(so):
+    assert backward(so, lse=None) == INVALID
+    assert backward(so, Lq=300, Lkv=200) == INVALID
+    assert backward(so, dtype=F32) == UNSUPPORTED
+    assert backward(so, d=64) == UNSUPPORTED
+    assert backward(so, gdt=FP8) == UNSUPPORTED
+    assert backward(so, ws=None) == WORKSPACE
+    need = lib.attn_prefill_backward_workspace_size(1, 8, 256)
+    assert need == 8 * 256 * 4
+    assert backward(so, ws_bytes=need - 1) == WORKSPACE
