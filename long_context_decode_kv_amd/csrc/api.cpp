@@ -827,6 +827,8 @@ attn_status attn_prefill_backward(const attn_tensor* q, const attn_tensor* k, co
         (st = check_tensor(dk, "dk", false)) || (st = check_tensor(dv, "dv", false)))
         return st;
     if (!lse) return fail(ATTN_ERR_INVALID_ARG, "lse (from the forward pass) is required");
+    if ((Lq + 63) / 64 > 65535 || (Lkv + 63) / 64 > 65535)
+        return fail(ATTN_ERR_UNSUPPORTED, "backward supports up to 65535 blocks of 64 positions");
     if (dout->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "dout must be bf16");
     if (dq->dtype != dk->dtype || dq->dtype != dv->dtype || (dq->dtype != ATTN_BF16 && dq->dtype != ATTN_F32))
         return fail(ATTN_ERR_UNSUPPORTED, "dq, dk and dv must all be bf16 or all fp32");

@@ -21,9 +21,10 @@
 // Every product runs on v_mfma_f32_32x32x16_bf16 with 32 x 32 tiles, one or
 // two per wave (4 waves per workgroup). Operands come from LDS tiles padded
 // to 16 bytes past every row, so the 16-byte fragment reads of 16 lanes hit
-// distinct banks; the products that contract over the sequence read
-// transposed copies of Q, dO and K written while staging. P and dz are
-// rounded to bf16 as MFMA operands, like P in the forward pass.
+// distinct banks; the products that contract over the sequence take Q, dO
+// and K through transposed LDS reads of the same row-major tiles. The next
+// block's global loads are issued before the current block is computed. P
+// and dz are rounded to bf16 as MFMA operands, like P in the forward pass.
 #include "internal.h"
 
 namespace attn {
@@ -62,28 +63,42 @@ __device__ __forceinline__ bf16x8 lds_frag(const char* lds, int byte_off) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-// Stages a 64 x 128 bf16 block (rows row0 .. row0 + 63 of a [rows][128] view
-// with element row stride `ss`; rows past `nrows` repeat the last row) into
-// `dst` (row-major, kPitch) and, if `dstT` is set, its transpose into `dstT`
-// ([128][64], kTPitch). 256 threads; lane r of a wave takes row r.
-__device__ __forceinline__ void stage_block(const uint16_t* base, int64_t ss, int row0, int nrows, char* dst,
-                                            char* dstT, int tid) {
-    const int r = tid & 63;
-    const int row = min(row0 + r, nrows - 1);
+// One thread's share of a 64 x 128 bf16 block: lane r of a wave takes row
+// r, chunks (tid >> 6) + 4i (16 bytes each, dims 8c .. 8c + 7). Rows past
+// `nrows` repeat the last row (their results are masked).
+struct BlockRegs {
+    u32x4 x[4];
+};
+
+__device__ __forceinline__ void load_block(BlockRegs& br, const uint16_t* base, int64_t ss, int row0, int nrows,
+                                           int tid) {
+    const int row = min(row0 + (tid & 63), nrows - 1);
     const uint16_t* src = base + (int64_t)row * ss;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = (tid >> 6) + 4 * i;  // 16-byte chunk: dims 8c .. 8c + 7
-        const u32x4 x = *reinterpret_cast<const u32x4*>(src + 8 * c);
-        *reinterpret_cast<u32x4*>(dst + r * kPitch + 16 * c) = x;
-        if (dstT) {
+    for (int i = 0; i < 4; ++i) br.x[i] = *reinterpret_cast<const u32x4*>(src + 8 * ((tid >> 6) + 4 * i));
+}
+
+__device__ __forceinline__ void store_block(const BlockRegs& br, char* dst, int tid) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                *reinterpret_cast<uint16_t*>(dstT + (8 * c + 2 * e) * kTPitch + 2 * r) = (uint16_t)(x[e] & 0xffff);
-                *reinterpret_cast<uint16_t*>(dstT + (8 * c + 2 * e + 1) * kTPitch + 2 * r) = (uint16_t)(x[e] >> 16);
-            }
-        }
-    }
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + (tid & 63) * kPitch + 16 * ((tid >> 6) + 4 * i)) = br.x[i];
+}
+
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// B operand of a product over the sequence from a row-major [seq][128] LDS
+// tile: k = rows 16ks + 8hb + (0..7), n = dim 32dblk + (lane & 31), built from
+// two transposed reads (ds_read_b64_tr_b16: in each group of 16 lanes, lane
+// 4a + b names row a and dims 4b .. 4b + 3 of a 4 x 16 block, and lane i
+// receives the four rows of dim i).
+__device__ __forceinline__ bf16x8 tr_frag(const char* tile, int ks, int dblk, int lane) {
+    const int i16 = lane & 15, ga = i16 >> 2, gb = i16 & 3, gg = (lane >> 4) & 1, hb = lane >> 5;
+    const int off = (16 * ks + 8 * hb + ga) * kPitch + 2 * (32 * dblk + 16 * gg + 4 * gb);
+    lds_char* t = (lds_char*)tile;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(t + off));
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(t + off + 4 * kPitch));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // ---------------------------------------------------------------- D = rowsum(dO * O)
@@ -128,17 +143,17 @@ __device__ __forceinline__ void store_tile(void* base, int dtype, int64_t ss, in
 struct DkdvLds {
     char q[kBlk * kPitch];
     char dout[kBlk * kPitch];
-    char qT[kD * kTPitch];
-    char doutT[kD * kTPitch];
     char pT[kBlk * kTPitch];   // P^T  [key][row] bf16
     char dsT[kBlk * kTPitch];  // dz^T [key][row] bf16
     float lse2[kBlk];          // lse * log2(e), +inf for rows without weights
     float delta[kBlk];
 };
 
-__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BackwardParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BackwardParams p) {
     __shared__ __attribute__((aligned(16))) DkdvLds s;
-    const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // grid (Hkv, key blocks, B): the heads of one key block are issued
+    // together, the blocks most queries see (the first, when causal) first
+    const int g = blockIdx.x, kb = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5, w = tid >> 6;
     const int kt = w >> 1;  // this wave's 32-key half of the block
     const int rt = w & 1;   // its 32-row half for S and dP; its 64-dim half for dK and dV
@@ -163,67 +178,75 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BackwardParams p) {
 #pragma unroll
         for (int j = 0; j < 16; ++j) dk[u][j] = dv[u][j] = 0.f;
 
-    // query blocks whose rows see some key of this block
+    // (head, query block) pairs whose rows see some key of this block, in
+    // order; the next pair's Q and dO are loaded while this one is computed
     const int nqb = (p.Lq + kBlk - 1) / kBlk;
     const int qb0 = p.causal ? max(0, (key0 - off) / kBlk) : 0;
-    for (int h = g * G; h < (g + 1) * G; ++h) {
-        const uint16_t* qbase = static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh;
-        const uint16_t* dobase = static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh;
-        const float* lse = p.lse + ((int64_t)b * p.Hq + h) * p.Lq;
-        const float* delta = p.delta + ((int64_t)b * p.Hq + h) * p.Lq;
-        for (int qb = qb0; qb < nqb; ++qb) {
-            const int row0 = qb * kBlk;
-            __syncthreads();  // the previous tile's readers are done
-            stage_block(qbase, p.q_ss, row0, p.Lq, s.q, s.qT, tid);
-            stage_block(dobase, p.do_ss, row0, p.Lq, s.dout, s.doutT, tid);
-            if (tid < kBlk) {
-                const int i = row0 + tid;
-                const float l = i < p.Lq ? lse[i] : -kInf;
-                s.lse2[tid] = (l == -kInf) ? kInf : l * kLog2e;
-                s.delta[tid] = i < p.Lq ? delta[i] : 0.f;
-            }
-            __syncthreads();
+    const int nq = max(0, nqb - qb0), nit = G * nq;
+    BlockRegs qr, dr;
+    float lse_n = 0.f, dl_n = 0.f;
+    auto fetch = [&](int it) __attribute__((always_inline)) {
+        const int h = g * G + it / nq, row0 = (qb0 + it % nq) * kBlk;
+        load_block(qr, static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh, p.q_ss, row0, p.Lq, tid);
+        load_block(dr, static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh, p.do_ss, row0, p.Lq, tid);
+        if (tid < kBlk) {
+            const int i = row0 + tid;
+            const int64_t ri = ((int64_t)b * p.Hq + h) * p.Lq + i;
+            lse_n = i < p.Lq ? p.lse[ri] : -kInf;
+            dl_n = i < p.Lq ? p.delta[ri] : 0.f;
+        }
+    };
+    if (nit > 0) fetch(0);
+    for (int it = 0; it < nit; ++it) {
+        const int row0 = (qb0 + it % nq) * kBlk;
+        __syncthreads();  // the previous pair's readers are done
+        store_block(qr, s.q, tid);
+        store_block(dr, s.dout, tid);
+        if (tid < kBlk) {
+            s.lse2[tid] = (lse_n == -kInf) ? kInf : lse_n * kLog2e;
+            s.delta[tid] = dl_n;
+        }
+        __syncthreads();
+        if (it + 1 < nit) fetch(it + 1);
 
-            // S and dP for rows 32rt.., keys 32kt.. (row = M, key = N)
-            f32x16 sa = {}, dpa = {};
+        // S and dP for rows 32rt.., keys 32kt.. (row = M, key = N)
+        f32x16 sa = {}, dpa = {};
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int ao = (32 * rt + (lane & 31)) * kPitch + 32 * ks + 16 * hb;
-                sa = mfma(lds_frag(s.q, ao), kf[ks], sa);
-                dpa = mfma(lds_frag(s.dout, ao), vf[ks], dpa);
+        for (int ks = 0; ks < 8; ++ks) {
+            const int ao = (32 * rt + (lane & 31)) * kPitch + 32 * ks + 16 * hb;
+            sa = mfma(lds_frag(s.q, ao), kf[ks], sa);
+            dpa = mfma(lds_frag(s.dout, ao), vf[ks], dpa);
+        }
+        // P and dz; stored transposed ([key][row]) as bf16, four rows per write
+        const int key = key0 + 32 * kt + (lane & 31);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            float pv[4], dz[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * t + e;
+                const int r = 32 * rt + acc_row(j, hb);
+                const int i = row0 + r;
+                const bool vis = key < p.Lkv && i < p.Lq && (!p.causal || key <= i + off);
+                pv[e] = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -s.lse2[r])) : 0.f;
+                dz[e] = pv[e] * (dpa[j] - s.delta[r]);
             }
-            // P and dz; stored transposed ([key][row]) as bf16, four rows per write
-            const int key = key0 + 32 * kt + (lane & 31);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                float pv[4], dz[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * t + e;
-                    const int r = 32 * rt + acc_row(j, hb);
-                    const int i = row0 + r;
-                    const bool vis = key < p.Lkv && i < p.Lq && (!p.causal || key <= i + off);
-                    pv[e] = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -s.lse2[r])) : 0.f;
-                    dz[e] = pv[e] * (dpa[j] - s.delta[r]);
-                }
-                const int rbyte = 2 * (32 * rt + 8 * t + 4 * hb);
-                const int kr = 32 * kt + (lane & 31);
-                *reinterpret_cast<u32x2*>(s.pT + kr * kTPitch + rbyte) = (u32x2){pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
-                *reinterpret_cast<u32x2*>(s.dsT + kr * kTPitch + rbyte) = (u32x2){pack_bf16(dz[0], dz[1]), pack_bf16(dz[2], dz[3])};
-            }
-            __syncthreads();
+            const int rbyte = 2 * (32 * rt + 8 * t + 4 * hb);
+            const int kr = 32 * kt + (lane & 31);
+            *reinterpret_cast<u32x2*>(s.pT + kr * kTPitch + rbyte) = (u32x2){pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3])};
+            *reinterpret_cast<u32x2*>(s.dsT + kr * kTPitch + rbyte) = (u32x2){pack_bf16(dz[0], dz[1]), pack_bf16(dz[2], dz[3])};
+        }
+        __syncthreads();
 
-            // dV += P^T dO and dK += dz^T Q for keys 32kt.., dims 64rt + 32u..
+        // dV += P^T dO and dK += dz^T Q for keys 32kt.., dims 64rt + 32u..
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int ao = (32 * kt + (lane & 31)) * kTPitch + 32 * ks + 16 * hb;
-                const bf16x8 pa = lds_frag(s.pT, ao), da = lds_frag(s.dsT, ao);
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ao = (32 * kt + (lane & 31)) * kTPitch + 32 * ks + 16 * hb;
+            const bf16x8 pa = lds_frag(s.pT, ao), da = lds_frag(s.dsT, ao);
 #pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int bo = (64 * rt + 32 * u + (lane & 31)) * kTPitch + 32 * ks + 16 * hb;
-                    dv[u] = mfma(pa, lds_frag(s.doutT, bo), dv[u]);
-                    dk[u] = mfma(da, lds_frag(s.qT, bo), dk[u]);
-                }
+            for (int u = 0; u < 2; ++u) {
+                dv[u] = mfma(pa, tr_frag(s.dout, ks, 2 * rt + u, lane), dv[u]);
+                dk[u] = mfma(da, tr_frag(s.q, ks, 2 * rt + u, lane), dk[u]);
             }
         }
     }
@@ -241,13 +264,14 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BackwardParams p) {
 struct DqLds {
     char k[kBlk * kPitch];
     char v[kBlk * kPitch];
-    char kT[kD * kTPitch];
     char ds[kBlk * kTPitch];  // dz [row][key] bf16
 };
 
-__global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
     __shared__ __attribute__((aligned(16))) DqLds s;
-    const int qb = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // grid (Hq, query blocks, B): the heads of one query block are issued
+    // together, the blocks that see the most keys (the last, when causal) first
+    const int h = blockIdx.x, qb = gridDim.y - 1 - blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5, w = tid >> 6;
     const int rt = w & 1;   // this wave's 32-row half
     const int kt = w >> 1;  // its 32-key half for S and dP; its 64-dim half for dQ
@@ -258,9 +282,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
 
     // Q and dO of the wave's 32 rows as B operands (column = row, k = dims)
     const int myrow = row0 + 32 * rt + (lane & 31);
-    const int qr = min(myrow, p.Lq - 1);
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)qr * p.q_ss;
-    const uint16_t* dorow = static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)qr * p.do_ss;
+    const int qrw = min(myrow, p.Lq - 1);
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)qrw * p.q_ss;
+    const uint16_t* dorow = static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)qrw * p.do_ss;
     bf16x8 qf[8], df[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
@@ -284,12 +308,21 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
     const int nkb_all = (p.Lkv + kBlk - 1) / kBlk;
     const int last_key = min(p.Lkv - 1, row0 + kBlk - 1 + off);
     const int nkb = p.causal ? (last_key >= 0 ? last_key / kBlk + 1 : 0) : nkb_all;
+    BlockRegs kr, vr;  // the next key block, loaded while this one is computed
+    if (nkb > 0) {
+        load_block(kr, kbase, p.k_ss, 0, p.Lkv, tid);
+        load_block(vr, vbase, p.v_ss, 0, p.Lkv, tid);
+    }
     for (int kb = 0; kb < nkb; ++kb) {
         const int key0 = kb * kBlk;
         __syncthreads();
-        stage_block(kbase, p.k_ss, key0, p.Lkv, s.k, s.kT, tid);
-        stage_block(vbase, p.v_ss, key0, p.Lkv, s.v, nullptr, tid);
+        store_block(kr, s.k, tid);
+        store_block(vr, s.v, tid);
         __syncthreads();
+        if (kb + 1 < nkb) {
+            load_block(kr, kbase, p.k_ss, key0 + kBlk, p.Lkv, tid);
+            load_block(vr, vbase, p.v_ss, key0 + kBlk, p.Lkv, tid);
+        }
 
         // S^T and dP^T for keys 32kt.. (M) and rows 32rt.. (N)
         f32x16 sa = {}, dpa = {};
@@ -322,8 +355,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BackwardParams p) {
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 a = lds_frag(s.ds, (32 * rt + (lane & 31)) * kTPitch + 32 * ks + 16 * hb);
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                dq[u] = mfma(a, lds_frag(s.kT, (64 * kt + 32 * u + (lane & 31)) * kTPitch + 32 * ks + 16 * hb), dq[u]);
+            for (int u = 0; u < 2; ++u) dq[u] = mfma(a, tr_frag(s.k, ks, 2 * kt + u, lane), dq[u]);
         }
     }
     const float sigma = p.scale_log2 / kLog2e;
@@ -341,10 +373,10 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((R + 3) / 4)), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((p.Lkv + kBlk - 1) / kBlk, p.Hkv, p.B), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.Hkv, (p.Lkv + kBlk - 1) / kBlk, p.B), dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3((p.Lq + kBlk - 1) / kBlk, p.Hq, p.B), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.Hq, (p.Lq + kBlk - 1) / kBlk, p.B), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
