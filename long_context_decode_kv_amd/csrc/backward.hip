@@ -217,19 +217,24 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BackwardParams p) {
             sa = mfma(lds_frag(s.q, ao), kf[ks], sa);
             dpa = mfma(lds_frag(s.dout, ao), vf[ks], dpa);
         }
-        // P and dz; stored transposed ([key][row]) as bf16, four rows per write
+        // P and dz; stored transposed ([key][row]) as bf16, four rows per write.
+        // A tile with every key visible to every row needs no mask.
         const int key = key0 + 32 * kt + (lane & 31);
+        const bool full = key0 + kBlk <= p.Lkv && row0 + kBlk <= p.Lq && (!p.causal || key0 + kBlk - 1 <= row0 + off);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
+            const int r0 = 32 * rt + 8 * t + 4 * hb;  // rows r0 .. r0 + 3
+            const float4 l4 = *reinterpret_cast<const float4*>(&s.lse2[r0]);
+            const float4 d4 = *reinterpret_cast<const float4*>(&s.delta[r0]);
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dlv[4] = {d4.x, d4.y, d4.z, d4.w};
             float pv[4], dz[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 4 * t + e;
-                const int r = 32 * rt + acc_row(j, hb);
-                const int i = row0 + r;
-                const bool vis = key < p.Lkv && i < p.Lq && (!p.causal || key <= i + off);
-                pv[e] = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -s.lse2[r])) : 0.f;
-                dz[e] = pv[e] * (dpa[j] - s.delta[r]);
+                const int i = row0 + r0 + e;
+                const bool vis = full || (key < p.Lkv && i < p.Lq && (!p.causal || key <= i + off));
+                pv[e] = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -lv[e])) : 0.f;
+                dz[e] = pv[e] * (dpa[j] - dlv[e]);
             }
             const int rbyte = 2 * (32 * rt + 8 * t + 4 * hb);
             const int kr = 32 * kt + (lane & 31);
@@ -332,7 +337,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
             sa = mfma(lds_frag(s.k, ao), qf[ks], sa);
             dpa = mfma(lds_frag(s.v, ao), df[ks], dpa);
         }
-        // dz for this lane's row, stored as [row][key] bf16, four keys per write
+        // dz for this lane's row, stored as [row][key] bf16, four keys per write.
+        // A tile with every key visible to every row needs no mask.
+        const bool full = key0 + kBlk <= p.Lkv && row0 + kBlk <= p.Lq && (!p.causal || key0 + kBlk - 1 <= row0 + off);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             float dz[4];
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
             for (int e = 0; e < 4; ++e) {
                 const int j = 4 * t + e;
                 const int key = key0 + 32 * kt + acc_row(j, hb);
-                const bool vis = key < p.Lkv && myrow < p.Lq && (!p.causal || key <= myrow + off);
+                const bool vis = full || (key < p.Lkv && myrow < p.Lq && (!p.causal || key <= myrow + off));
                 const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -lse2)) : 0.f;
                 dz[e] = pv * (dpa[j] - dlt);
             }
