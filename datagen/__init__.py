@@ -6,7 +6,7 @@ formats the library reads. Random numbers never come from the GPU path.
 
 Tensor ids used by the workloads: Q=0, K=1, V=2, per-sequence lengths=3; the
 fp8 span of a two-precision cache: K=4, V=5, its lengths=6; the pi-Attention
-gate alpha=7.
+gate alpha=7; the output gradient of the backward pass=9.
 """
 import ctypes
 import os
@@ -20,6 +20,7 @@ _lib = None
 
 TID_Q, TID_K, TID_V, TID_LENS = 0, 1, 2, 3
 TID_K_LO, TID_V_LO, TID_LENS_LO = 4, 5, 6
+TID_DOUT = 9
 
 
 def build():

@@ -19,10 +19,11 @@
 //  * bwd_dq:    one workgroup per 64-row query block of one query head; it
 //    walks the key blocks the rows see and accumulates dQ = dz K.
 // Every product runs on v_mfma_f32_32x32x16_bf16 with 32 x 32 tiles, one or
-// two per wave (4 waves per workgroup). Operands come from LDS tiles padded
-// to 16 bytes past every row, so the 16-byte fragment reads of 16 lanes hit
-// distinct banks; the products that contract over the sequence take Q, dO
-// and K through transposed LDS reads of the same row-major tiles. The next
+// two per wave (4 waves per workgroup). Operands come from LDS tiles laid
+// out so that fragment reads hit distinct banks (16-byte chunks swizzled by
+// row in the 128-wide tiles, 16 bytes of padding per row in the 64-wide
+// ones); the products that contract over the sequence take Q, dO and K
+// through transposed LDS reads of the same row-major tiles. The next
 // block's global loads are issued before the current block is computed. P
 // and dz are rounded to bf16 as MFMA operands, like P in the forward pass.
 #include "internal.h"
@@ -39,7 +40,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBlk = 64;                 // rows or keys per block
 constexpr int kD = 128;                  // head dim
-constexpr int kPitch = kD * 2 + 16;      // bytes per padded [.][128] bf16 row
+constexpr int kPitch = kD * 2;           // bytes per [.][128] bf16 row (16-byte chunks swizzled, below)
 constexpr int kTPitch = kBlk * 2 + 16;   // bytes per padded [.][64] bf16 row
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kInf = __builtin_huge_valf();
@@ -59,6 +60,14 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 __device__ __forceinline__ bf16x8 lds_frag(const char* lds, int byte_off) {
     return *reinterpret_cast<const bf16x8*>(lds + byte_off);
 }
+
+// [.][128] tiles keep 16-byte chunk c of row r at chunk position c ^ swz(r),
+// swz swapping the two low 2-bit fields of r. Sixteen consecutive rows then
+// cover all 16 positions (row-wise 16-byte reads and writes of 16 lanes hit
+// distinct banks), and the four rows of a transposed read fall on four
+// different chunk pairs (its 8-byte pieces hit distinct banks too).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int chunk_at(int r, int c) { return r * kPitch + 16 * (c ^ swz(r)); }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
@@ -80,7 +89,7 @@ __device__ __forceinline__ void load_block(BlockRegs& br, const uint16_t* base, 
 
 __device__ __forceinline__ void store_block(const BlockRegs& br, char* dst, int tid) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + (tid & 63) * kPitch + 16 * ((tid >> 6) + 4 * i)) = br.x[i];
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(dst + chunk_at(tid & 63, (tid >> 6) + 4 * i)) = br.x[i];
 }
 
 typedef __attribute__((address_space(3))) char lds_char;
@@ -93,11 +102,12 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // receives the four rows of dim i).
 __device__ __forceinline__ bf16x8 tr_frag(const char* tile, int ks, int dblk, int lane) {
     const int i16 = lane & 15, ga = i16 >> 2, gb = i16 & 3, gg = (lane >> 4) & 1, hb = lane >> 5;
-    const int off = (16 * ks + 8 * hb + ga) * kPitch + 2 * (32 * dblk + 16 * gg + 4 * gb);
+    const int r = 16 * ks + 8 * hb + ga, c = 4 * dblk + 2 * gg + (gb >> 1), half = 8 * (gb & 1);
     lds_char* t = (lds_char*)tile;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(t + off));
-    const v4i16 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(t + off + 4 * kPitch));
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(t + chunk_at(r, c) + half));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(t + chunk_at(r + 4, c) + half));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
@@ -213,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BackwardParams p) {
         f32x16 sa = {}, dpa = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const int ao = (32 * rt + (lane & 31)) * kPitch + 32 * ks + 16 * hb;
+            const int ao = chunk_at(32 * rt + (lane & 31), 2 * ks + hb);
             sa = mfma(lds_frag(s.q, ao), kf[ks], sa);
             dpa = mfma(lds_frag(s.dout, ao), vf[ks], dpa);
         }
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
         f32x16 sa = {}, dpa = {};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            const int ao = (32 * kt + (lane & 31)) * kPitch + 32 * ks + 16 * hb;
+            const int ao = chunk_at(32 * kt + (lane & 31), 2 * ks + hb);
             sa = mfma(lds_frag(s.k, ao), qf[ks], sa);
             dpa = mfma(lds_frag(s.v, ao), df[ks], dpa);
         }

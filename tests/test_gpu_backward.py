@@ -15,11 +15,10 @@ import torch
 
 import oracle
 from _gpu import from_dev, needs_gpu, to_dev
-from datagen import normal_bf16_bits
+from datagen import TID_DOUT, normal_bf16_bits
 from datagen.workloads import make_inputs
 
 pytestmark = [pytest.mark.gpu, needs_gpu]
-TID_DOUT = 9  # tensor id of the seeded output gradient
 
 
 def _run(inp, causal, grad_dtype=torch.float32, scale=0.0, seed=0):
