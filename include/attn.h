@@ -285,12 +285,14 @@ ATTN_API int attn_decode_pi_splits(int B, int Hkv, int L_cap, int window, int pe
  * Prefill: attention of Lq queries over Lkv keys (causal or not), fused so the
  * Lq x Lkv score matrix never reaches memory.
  *
- * q [B, Hq, Lq, d], k and v [B, Hkv, Lkv, d], out [B, Hq, Lq, d]: ATTN_BF16,
+ * q [B, Hq, Lq, d], k and v [B, Hkv, Lkv, d], out [B, Hq, Lq, d]: one dtype,
  * 16-byte aligned data and strides.
  * lse: device float [B, Hq, Lq] (contiguous) or NULL.
  * causal with Lq > Lkv is rejected (queries with no visible key).
- * Supported: d == 128, Hq % Hkv == 0, k and v row strides (stride_s) below
- * 2^24 elements (32 MiB per key row); larger ones give ATTN_ERR_UNSUPPORTED.
+ * bf16 with d == 128 runs on MFMA; fp32 with d == 64 or 128 and bf16 with
+ * d == 64 run on a slower vector-ALU kernel (one wave per query row). Other
+ * combinations give ATTN_ERR_UNSUPPORTED, as do k and v row strides
+ * (stride_s) of 2^24 elements or more. Hq % Hkv == 0.
  */
 ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B,
                                   int Hq, int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal,

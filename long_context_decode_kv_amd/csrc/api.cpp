@@ -426,8 +426,11 @@ attn_status two_span_launch(attn::DecodeParams& p, int S, bool fp8_0, bool fp8_1
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// general: also accept what the vector-ALU prefill takes (fp32 with d = 64 or
+// 128, bf16 with d = 64); otherwise only the MFMA kernel's bf16, d = 128.
 attn_status check_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const attn_tensor* out,
-                          int B, int Hq, int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal) {
+                          int B, int Hq, int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal,
+                          bool general = false) {
     attn_status st;
     if ((st = check_tensor(q, "q", true)) || (st = check_tensor(k, "k", true)) || (st = check_tensor(v, "v", true)) ||
         (st = check_tensor(out, "out", true)))
@@ -438,9 +441,14 @@ attn_status check_prefill(const attn_tensor* q, const attn_tensor* k, const attn
     if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
     if (causal && Lq > Lkv) return fail(ATTN_ERR_INVALID_ARG, "causal with Lq (%d) > Lkv (%d)", Lq, Lkv);
     if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
-    if (q->dtype != ATTN_BF16 || k->dtype != ATTN_BF16 || v->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
-        return fail(ATTN_ERR_UNSUPPORTED, "prefill supports bf16 q/k/v/out");
-    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "prefill head dim %d (supported: 128)", d);
+    const bool same = q->dtype == k->dtype && q->dtype == v->dtype && q->dtype == out->dtype;
+    const bool mfma = same && q->dtype == ATTN_BF16 && d == 128;
+    const bool valu = same && ((q->dtype == ATTN_F32 && (d == 64 || d == 128)) || (q->dtype == ATTN_BF16 && d == 64));
+    if (!mfma && !(general && valu)) {
+        if (general) return fail(ATTN_ERR_UNSUPPORTED, "prefill takes bf16 with d = 64 or 128, or fp32 with d = 64 or 128 "
+                                                       "(q, k, v and out of one dtype; got d = %d)", d);
+        return fail(ATTN_ERR_UNSUPPORTED, "this entry point takes bf16 q/k/v/out with d = 128 (got d = %d)", d);
+    }
     // K/V tiles are read through 32-bit buffer offsets covering 64 key rows
     if (k->stride_s >= (1 << 24) || v->stride_s >= (1 << 24))
         return fail(ATTN_ERR_UNSUPPORTED, "prefill k/v row stride must be below 2^24 elements");
@@ -720,10 +728,13 @@ attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_
                          int d, int Lq, int Lkv, float softmax_scale, int causal, attn_tensor* out, float* lse,
                          void* stream) {
     g_last_error[0] = 0;
-    attn_status st = check_prefill(q, k, v, out, B, Hq, Hkv, d, Lq, Lkv, softmax_scale, causal);
+    attn_status st = check_prefill(q, k, v, out, B, Hq, Hkv, d, Lq, Lkv, softmax_scale, causal, true);
     if (st != ATTN_OK) return st;
     attn::PrefillParams p = prefill_params(q, k, v, out, lse, B, Hq, Hkv, d, Lq, Lkv, softmax_scale, causal);
-    hipError_t e = attn::launch_prefill(p, static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (q->dtype == ATTN_BF16 && d == 128) e = attn::launch_prefill(p, static_cast<hipStream_t>(stream));
+    else e = attn::launch_prefill_valu(p, q->dtype == ATTN_F32 ? attn::DT_F32 : attn::DT_BF16,
+                                       static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ATTN_OK;
 }

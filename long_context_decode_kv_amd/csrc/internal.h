@@ -137,6 +137,8 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // Zeroes `bytes` (a multiple of 16) at 16-byte aligned device address `p`.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+// Vector-ALU prefill: fp32 with d = 64 or 128, bf16 with d = 64 (dtype DT_F32 or DT_BF16).
+hipError_t launch_prefill_valu(const PrefillParams& p, int dtype, hipStream_t stream);
 
 // Backward pass of (causal or full) attention, bf16 inputs, d = 128.
 struct BackwardParams {

@@ -130,8 +130,8 @@ def prefill(so, dtype=BF16, d=128, Lq=256, Lkv=256, causal=1, Hq=8, Hkv=2):
 
 def test_prefill_argument_errors(so):
     assert prefill(so, Lq=300, Lkv=200, causal=1) == INVALID
-    assert prefill(so, dtype=F32) == UNSUPPORTED
-    assert prefill(so, d=64) == UNSUPPORTED
+    assert prefill(so, dtype=FP8) == UNSUPPORTED
+    assert prefill(so, d=96) == UNSUPPORTED
     assert prefill(so, Hq=6, Hkv=4) == INVALID
     assert prefill(so, Lq=0) == INVALID
 

@@ -109,3 +109,23 @@ def test_prefill_repeats_are_bit_identical():
     got = from_dev(first).reshape(-1, 128)[rows]
     assert_close(got, ref, "bf16", what="repeats")
     assert_lse_close(first_lse.cpu().numpy().astype(np.float64).ravel()[rows], ref_lse, 2e-3)
+
+
+# ------------------------------------------------------------ vector-ALU prefill (fp32, head dim 64)
+
+@pytest.mark.parametrize("wl,B,Hq,Hkv,d,Lq,Lkv,causal,kind", [
+    (1, 1, 4, 2, 128, 150, 150, True, "f32"),
+    (1, 2, 2, 2, 64, 100, 230, True, "f32"),
+    (1, 1, 8, 1, 64, 77, 77, False, "f32"),
+    (4, 1, 8, 2, 64, 300, 300, True, "bf16"),
+    (4, 1, 4, 4, 64, 1, 90, True, "bf16"),
+])
+def test_prefill_valu_path(wl, B, Hq, Hkv, d, Lq, Lkv, causal, kind):
+    inp = make_inputs(wl, B=B, Hq=Hq, Hkv=Hkv, d=d, L=Lkv, Lq=Lq, seed=140 + Lq + d)
+    out, lse = prefill_on_gpu(inp, causal)
+    ref, ref_lse = oracle_rows(inp, causal)
+    got = from_dev(out).reshape(-1, d)
+    res = assert_close(got, ref, kind, what="prefill valu")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 1e-5 if kind == "f32" else 2e-3)
+    print("prefill valu %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % ((wl, B, Hq, Hkv, d, Lq, Lkv, causal), *res),
+          flush=True)
