@@ -57,7 +57,8 @@ def test_prefill_scale_override_and_determinism():
 
 
 def _sample_rows(Hq, L):
-    per_head = np.unique(np.concatenate([np.arange(128), np.arange(L - 128, L), np.linspace(0, L - 1, 128).astype(int)]))
+    # every head: the first 256 rows, the last 256 and 512 spread over the sequence
+    per_head = np.unique(np.concatenate([np.arange(256), np.arange(L - 256, L), np.linspace(0, L - 1, 512).astype(int)]))
     return np.concatenate([h * L + per_head for h in range(Hq)]), per_head
 
 
