@@ -1,0 +1,42 @@
+"""The byte and flop models bench.py divides by, checked against counts made
+another way (the per-head KV size the ThriftAttention page prints for a
+128K-token FP16 cache, brute-force enumeration of pi-Attention's visible
+pairs)."""
+import os
+import sys
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+
+import bench  # noqa: E402
+
+
+def test_kv_bytes_per_head_at_128k():
+    # 131072 keys x 128 dims x 2 (K and V) x 2 bytes = 67,108,864 bytes (about 67 MB per head)
+    assert bench.kv_bytes(131072, 1, 128, 2) == 67108864
+    assert bench.decode_algorithmic_bytes(1, 32, 8, 128, 131072) == 8 * 67108864 + 2 * 32 * 128 * 2
+
+
+def test_prefill_flops_count_the_causal_pairs():
+    L = 37
+    pairs = sum(i + 1 for i in range(L))
+    assert bench.prefill_flops(3, 16, L) == 4 * 3 * 16 * pairs
+    assert bench.prefill_flops(32, 128, 16384) == 2199157473280
+
+
+def test_mixed_bytes():
+    assert bench.mixed_algorithmic_bytes(1, 32, 8, 128, 26214, 104858) == \
+        2 * 8 * 26214 * 128 * 2 + 2 * 8 * 104858 * 128 + 2 * 4 * 8 + 2 * 32 * 128 * 2
+
+
+def test_pi_counts_by_enumeration():
+    for L, w, per in ((300, 37, 11), (129, 0, 1), (200, 250, 7), (64, 5, 0), (1000, 64, 64)):
+        pairs = 0
+        for i in range(L):
+            for j in range(i + 1):
+                d = i - j
+                if d <= w or (per > 0 and d % per == 0):
+                    pairs += 1
+        assert bench.pi_prefill_pairs(L, w, per) == pairs
+        i = L - 1
+        keys = sum(1 for j in range(L) if (i - j) <= w or (per > 0 and (i - j) % per == 0))
+        assert bench.pi_decode_keys(L, w, per) == keys

@@ -92,3 +92,17 @@ def test_uniform_int_range():
     x = datagen.uniform_int(3, 3, 10000, 4096, 65536)
     assert x.min() >= 4096 and x.max() <= 65536
     assert abs(x.mean() - (4096 + 65536) / 2) < 1500
+
+
+def test_bf16_encoder_rounds_midpoints_to_even():
+    # every midpoint between adjacent bf16 values of one binade per exponent
+    # (mantissas 0..126 and their successors) is a tie: the even neighbour wins
+    lo = np.arange(0x0080, 0x7F00, 1, dtype=np.uint32)  # positive normal bf16 patterns below the top binade
+    lo = lo[(lo & 0x7F) != 0x7F]
+    mid = ((lo << 16) | 0x8000).view(np.float32)        # exactly halfway to the next pattern
+    enc = datagen.f32_to_bf16_bits(mid).astype(np.uint32)
+    want = np.where(lo & 1, lo + 1, lo)
+    assert np.array_equal(enc, want)
+    # just above and just below a midpoint go to the nearer neighbour
+    assert np.array_equal(datagen.f32_to_bf16_bits(((lo << 16) | 0x8001).view(np.float32)).astype(np.uint32), lo + 1)
+    assert np.array_equal(datagen.f32_to_bf16_bits(((lo << 16) | 0x7FFF).view(np.float32)).astype(np.uint32), lo)
