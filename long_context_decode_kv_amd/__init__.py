@@ -289,13 +289,14 @@ def attn_decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale=None, v_scale=None, hi_
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    auto_hi, auto_lo = (0, 0)
-    if (num_splits_hi <= 0 and L_hi) or (num_splits_lo <= 0 and L_lo):
+    S_hi, S_lo = num_splits_hi, num_splits_lo
+    if (S_hi <= 0 and L_hi) or (S_lo <= 0 and L_lo):
         auto_hi, auto_lo = attn_decode_mixed_splits(B, Hkv, L_hi, L_lo)
-    S_hi = attn_decode_plan(L_hi, num_splits_hi if num_splits_hi > 0 else auto_hi)[0] if L_hi else 0
-    S_lo = attn_decode_plan(L_lo, num_splits_lo if num_splits_lo > 0 else auto_lo)[0] if L_lo else 0
+        S_hi = S_hi if S_hi > 0 else auto_hi
+        S_lo = S_lo if S_lo > 0 else auto_lo
     if workspace is None:
-        workspace = attn_decode_workspace(B, Hq, d, S_hi + S_lo, device=q.device)
+        used = (attn_decode_plan(L_hi, S_hi)[0] if L_hi else 0) + (attn_decode_plan(L_lo, S_lo)[0] if L_lo else 0)
+        workspace = attn_decode_workspace(B, Hq, d, used, device=q.device)
 
     def view(t):
         return None if t is None else ctypes.byref(_tensor(t))
@@ -341,11 +342,11 @@ def attn_decode_pi(q, k, v, window, period, alpha=None, k_scale=None, v_scale=No
         aw, as_ = attn_decode_pi_splits(B, Hkv, L_cap, window, period, _dtype_code(k))
         sw = sw if sw > 0 else aw
         ss = ss if ss > 0 else as_
-    cap_w = min(window + 1, L_cap)
-    last = L_cap - 2 - window
-    cap_s = last // period + 1 if period > 0 and last >= 0 else 0
-    S = attn_decode_plan(cap_w, sw)[0] + (attn_decode_plan(cap_s, ss)[0] if cap_s else 0)
     if workspace is None:
+        cap_w = min(window + 1, L_cap)
+        last = L_cap - 2 - window
+        cap_s = last // period + 1 if period > 0 and last >= 0 else 0
+        S = attn_decode_plan(cap_w, sw)[0] + (attn_decode_plan(cap_s, ss)[0] if cap_s else 0)
         workspace = attn_decode_workspace(B, Hq, d, S, device=q.device)
     qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     st = lib.attn_decode_pi(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), _ptr(k_scale), _ptr(v_scale),
