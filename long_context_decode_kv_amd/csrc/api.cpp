@@ -101,9 +101,12 @@ int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype, int ragged)
     int64_t S;
     if (ragged) {
         // Lengths are only known on the device: cut every sequence into chunks
-        // of about 1024 keys (2048 for fp8, the same bytes) so that short and
-        // long sequences balance across many workgroups.
-        const int64_t chunk = kv_dtype == ATTN_FP8_E4M3 ? 2048 : 1024;
+        // of 1216 keys (twice that for fp8, the same bytes) so that short and
+        // long sequences balance across many workgroups. Not a power of two:
+        // with 1024-key chunks every split starts on a 256 KiB boundary and a
+        // batch of 16 x 8 heads of 4K-64K keys ran 6 % slower (330 us against
+        // 309 us).
+        const int64_t chunk = kv_dtype == ATTN_FP8_E4M3 ? 2432 : 1216;
         S = ceil_div(L_cap, chunk);
     } else {
         // Equal chunks, all workgroups resident at once and the same number
