@@ -314,7 +314,7 @@ struct PiCaps {
 };
 PiCaps pi_caps(int L_cap, int window, int period) {
     PiCaps c;
-    c.window = (int)(window + 1 < (int64_t)L_cap ? window + 1 : L_cap);
+    c.window = (int)((int64_t)window + 1 < (int64_t)L_cap ? window + 1 : L_cap);
     const int64_t last = (int64_t)L_cap - 2 - window;  // highest row a skip key can take
     c.skip = (period > 0 && last >= 0) ? (int)(last / period + 1) : 0;
     return c;
@@ -668,6 +668,7 @@ attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, con
 int attn_decode_pi_splits(int B, int Hkv, int L_cap, int window, int period, int kv_dtype, int* splits_window,
                           int* splits_skip) {
     if (B <= 0 || Hkv <= 0 || L_cap <= 0 || window < 0 || period < 0 || !elem_size(kv_dtype)) return 0;
+    if (window > L_cap) window = L_cap;  // a window past the cache is the whole cache
     const PiCaps c = pi_caps(L_cap, window, period);
     // both spans hold the same dtype: split in proportion to their keys
     return two_span_splits(B, Hkv, c.window, 1.0, c.skip, 1.0, splits_window, splits_skip);
@@ -699,6 +700,7 @@ attn_status attn_decode_pi(const attn_tensor* q, const attn_tensor* k, const att
         return fail(ATTN_ERR_UNSUPPORTED, "pi decode takes bf16 q and out, bf16 or fp8 k/v");
     if (d != 128 || Hq != 4 * Hkv)
         return fail(ATTN_ERR_UNSUPPORTED, "pi decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+    if (window > L_cap) window = L_cap;  // same keys; keeps window arithmetic in range
 
     const PiCaps c = pi_caps(L_cap, window, period);
     int auto_w = 0, auto_s = 0;
@@ -754,6 +756,7 @@ attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const at
     attn_status st = check_prefill(q, k, v, out, B, Hq, Hkv, d, L, L, softmax_scale, 1);
     if (st != ATTN_OK) return st;
     if (window < 0 || period < 0) return fail(ATTN_ERR_INVALID_ARG, "window and period must be >= 0");
+    if (window > L) window = L;  // same keys; keeps window arithmetic in range
     if (period > 0 && ((int64_t)period * k->stride_s >= (1 << 24) || (int64_t)period * v->stride_s >= (1 << 24)))
         return fail(ATTN_ERR_UNSUPPORTED, "period * k/v row stride must be below 2^24 elements");
     const size_t need = attn_prefill_pi_workspace_size(B, Hq, L, d);

@@ -206,6 +206,8 @@ def test_pi_decode_argument_errors(so):
     assert pi(so, period=0, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 2) - 1) == WORKSPACE
     assert "2 splits" in lib.load_library().attn_last_error().decode()
     assert pi(so, window=5000, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 2) - 1) == WORKSPACE
+    # a window far past the cache is the whole cache (no overflow in the plan)
+    assert pi(so, window=2 ** 31 - 1, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 2) - 1) == WORKSPACE
 
 
 def pi_prefill(so, dtype=BF16, d=128, L=256, Hq=8, Hkv=2, window=16, period=4, ws=FAKE, ws_bytes=1 << 30):
