@@ -261,9 +261,10 @@ def test_two_level_api_matches_fused_decode(wl, S):
     B, Hq = inp["q"].shape[:2]
     assert_close(from_dev(o2).reshape(B, Hq, -1), ref, "bf16", what="two-level")
     assert_lse_close(lse2.cpu().numpy().astype(np.float64).reshape(B, Hq), ref_lse, 2e-3)
-    # both paths agree to within one bf16 rounding of the output
+    # both paths agree to within one bf16 rounding of the output: bf16 keeps 8
+    # significant bits, so one unit in the last place at x is at most 2^-7 |x|
     a, b = from_dev(out).reshape(B * Hq, -1), from_dev(o2)
-    assert np.all(np.abs(a - b) <= 2.0 ** -8 * np.maximum(np.abs(a), np.abs(b)) + 1e-6)
+    assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-6)
 
 
 def test_combine_partials_api_against_oracle():
