@@ -1,14 +1,18 @@
 // Level-2 merge of split-KV partials: the global step of the two-level
 // log-sum-exp tree (the reduction along the sequence axis of the explainer of
 // "Tree Attention: Topology-aware Decoding for Long-Context Attention on GPU
-// Clusters", section 3; "exact, not approximate", its section 2).
+// Clusters", section 3; the merge is exact, as its section 2 stresses).
 //
 // For a row with partials (o_s, m_s, l_s), s < n:
 //   m = max_s m_s,  w_s = exp(m_s - m),
 //   O = sum_s w_s o_s / sum_s w_s l_s,  lse = m + ln sum_s w_s l_s.
-// Workgroup (r, 32-dim block): 8 lane groups of 32 threads each take every 8th
-// partial in order; the 8 group sums are then added as a fixed balanced tree,
-// so the result is deterministic for a given n.
+// Workgroup (r, 128-dim block) with W = 4..16 waves: wave w takes the
+// partials s = w, w + W, ... in order, eight at a time, and keeps its own
+// running (max, sum, accumulator) so that all loads of a batch -- and those of
+// the next batch, issued before the current one is added -- are in flight at
+// once: merging a row of up to 128 partials costs one memory round trip. The W
+// wave results are then merged in a fixed order, so the result is
+// deterministic for a given n and S.
 #include "internal.h"
 
 namespace attn {
@@ -16,6 +20,8 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kBatch = 8;      // partials per wave per batch
+constexpr int kMaxWaves = 16;  // waves per workgroup
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -24,74 +30,110 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     return (uint16_t)(u >> 16);
 }
 
-__global__ __launch_bounds__(256) void combine_partials_kernel(CombineParams p) {
+// One batch of a wave's partials: s = s0 + W*i, i < kBatch (clamped to n - 1;
+// the clamped copies are not added).
+struct Batch {
+    float m[kBatch], l[kBatch], o0[kBatch], o1[kBatch];
+};
+
+__global__ __launch_bounds__(64 * kMaxWaves) void combine_partials_kernel(CombineParams p) {
     const int r = blockIdx.x;
-    const int c0 = blockIdx.y * 32;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int W = blockDim.x >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int b = r / p.Hq, h = r % p.Hq;
     int n = p.S;
     if (p.kv_lens) {
         const int len = min(max(p.kv_lens[b], 0), p.L_cap);
         n = min((len + p.chunk - 1) / p.chunk, p.S);
     }
+    // this lane's two columns (lanes past d read a valid column and discard it)
+    const int c0 = blockIdx.y * 128 + 2 * lane, c1 = c0 + 1;
+    const int64_t cc0 = min(c0, p.d - 1), cc1 = min(c1, p.d - 1);
     const float* m_row = p.m_part + (int64_t)r * p.S;
     const float* l_row = p.l_part + (int64_t)r * p.S;
+    const float* o_row = p.o_part + (int64_t)r * p.S * p.d;
 
-    __shared__ float red[256];
-    float mx = kNegInf;
-    for (int s = tid; s < n; s += 256) mx = fmaxf(mx, m_row[s]);
-    red[tid] = mx;
-    __syncthreads();
-    for (int off = 128; off > 0; off >>= 1) {
-        if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
-        __syncthreads();
-    }
-    mx = red[0];
-    __syncthreads();
-
-    const int grp = tid >> 5, c = c0 + (tid & 31);
-    const int cc = min(c, p.d - 1);  // lanes past d read a valid column and discard it
-    const float* o_col = p.o_part + (int64_t)r * p.S * p.d + cc;
-    float ao = 0.f, al = 0.f;
-    auto step = [&](float ms, float ls, float os) {
-        const float wgt = (ms == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((ms - mx) * kLog2e);
-        al = fmaf(wgt, ls, al);
-        ao = fmaf(wgt, os, ao);
-    };
-    if (mx != kNegInf) {
-        // the group's partials s = grp, grp + 8, ... in order; loads for eight
-        // of them are issued before their terms are added (the adds keep the
-        // same order, so the result does not depend on the unrolling)
-        int s = grp;
-        for (; s + 56 < n; s += 64) {
-            float ms[8], ls[8], os[8];
+    auto load = [&](Batch& t, int s0) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                ms[i] = m_row[s + 8 * i];
-                ls[i] = l_row[s + 8 * i];
-                os[i] = o_col[(int64_t)(s + 8 * i) * p.d];
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) step(ms[i], ls[i], os[i]);
+        for (int i = 0; i < kBatch; ++i) {
+            const int64_t s = min(s0 + W * i, n - 1);
+            t.m[i] = m_row[s];
+            t.l[i] = l_row[s];
+            t.o0[i] = o_row[s * p.d + cc0];
+            t.o1[i] = o_row[s * p.d + cc1];
         }
-        for (; s < n; s += 8) step(m_row[s], l_row[s], o_col[(int64_t)s * p.d]);
+    };
+    float M = kNegInf, L = 0.f, a0 = 0.f, a1 = 0.f;
+    auto add = [&](const Batch& t, int s0) __attribute__((always_inline)) {
+        float bm = M;
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i)
+            if (s0 + W * i < n) bm = fmaxf(bm, t.m[i]);
+        if (bm > M) {  // the running max moves: rescale what is summed so far
+            const float f = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((M - bm) * kLog2e);
+            L *= f;
+            a0 *= f;
+            a1 *= f;
+            M = bm;
+        }
+#pragma unroll
+        for (int i = 0; i < kBatch; ++i) {
+            const bool use = s0 + W * i < n && t.m[i] != kNegInf;
+            const float wgt = use ? __builtin_amdgcn_exp2f((t.m[i] - M) * kLog2e) : 0.f;
+            L = fmaf(wgt, t.l[i], L);
+            a0 = fmaf(wgt, t.o0[i], a0);
+            a1 = fmaf(wgt, t.o1[i], a1);
+        }
+    };
+    if (w < n) {
+        Batch cur, nxt;
+        int s0 = w;
+        load(cur, s0);
+        while (true) {
+            const int s1 = s0 + W * kBatch;
+            const bool more = s1 < n;
+            if (more) load(nxt, s1);
+            add(cur, s0);
+            if (!more) break;
+            cur = nxt;
+            s0 = s1;
+        }
     }
-    __shared__ float red_o[8][32];
-    __shared__ float red_l[8];
-    red_o[grp][tid & 31] = ao;
-    if ((tid & 31) == 0) red_l[grp] = al;
+    __shared__ float sm_m[kMaxWaves], sm_l[kMaxWaves];
+    __shared__ float sm_o[kMaxWaves][128];
+    sm_o[w][2 * lane] = a0;
+    sm_o[w][2 * lane + 1] = a1;
+    if (lane == 0) {
+        sm_m[w] = M;
+        sm_l[w] = L;
+    }
     __syncthreads();
-    if (grp == 0 && c < p.d) {
-        const int j = tid & 31;
-        const float so = ((red_o[0][j] + red_o[1][j]) + (red_o[2][j] + red_o[3][j])) +
-                         ((red_o[4][j] + red_o[5][j]) + (red_o[6][j] + red_o[7][j]));
-        const float sl = ((red_l[0] + red_l[1]) + (red_l[2] + red_l[3])) + ((red_l[4] + red_l[5]) + (red_l[6] + red_l[7]));
+    if (w == 0) {
+        float mx = kNegInf;
+        for (int i = 0; i < W; ++i) mx = fmaxf(mx, sm_m[i]);
+        float so0 = 0.f, so1 = 0.f, sl = 0.f;
+        if (mx != kNegInf)
+            for (int i = 0; i < W; ++i) {
+                const float mi = sm_m[i];
+                const float f = (mi == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((mi - mx) * kLog2e);
+                sl = fmaf(f, sm_l[i], sl);
+                so0 = fmaf(f, sm_o[i][2 * lane], so0);
+                so1 = fmaf(f, sm_o[i][2 * lane + 1], so1);
+            }
         const bool empty = (mx == kNegInf) || !(sl > 0.f);
-        const float val = empty ? 0.f : so / sl;
-        const int64_t off = b * p.out_sb + h * p.out_sh + c;
-        if (p.out_dtype == DT_BF16) static_cast<uint16_t*>(p.out)[off] = f32_to_bf16_rne(val);
-        else static_cast<float*>(p.out)[off] = val;
-        if (p.lse && blockIdx.y == 0 && j == 0) p.lse[r] = empty ? kNegInf : mx + logf(sl);
+        const float inv = empty ? 0.f : 1.f / sl;
+        const int64_t off = b * p.out_sb + h * p.out_sh;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            const int c = e ? c1 : c0;
+            if (c < p.d) {
+                const float val = (e ? so1 : so0) * inv;
+                if (p.out_dtype == DT_BF16) static_cast<uint16_t*>(p.out)[off + c] = f32_to_bf16_rne(val);
+                else static_cast<float*>(p.out)[off + c] = val;
+            }
+        }
+        if (p.lse && blockIdx.y == 0 && lane == 0) p.lse[r] = empty ? kNegInf : mx + logf(sl);
     }
 }
 
@@ -113,8 +155,12 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-    dim3 grid(p.R, (p.d + 31) / 32);
-    hipLaunchKernelGGL(combine_partials_kernel, grid, dim3(256), 0, stream, p);
+    // enough waves that each takes at most one batch up to n = 128, more
+    // batches per wave beyond
+    const int need = (p.S + kBatch - 1) / kBatch;
+    const int waves = need < 4 ? 4 : (need > kMaxWaves ? kMaxWaves : need);
+    dim3 grid(p.R, (p.d + 127) / 128);
+    hipLaunchKernelGGL(combine_partials_kernel, grid, dim3(64 * waves), 0, stream, p);
     return hipGetLastError();
 }
 

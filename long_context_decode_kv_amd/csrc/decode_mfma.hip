@@ -250,53 +250,56 @@ __device__ __forceinline__ f32x2 ld_agent2(const float* p) {
 // the fixed order j = 0, 1, ...: partial j of head h has o at
 // o + (h*rs + j)*128, m at m[h*rs + j], l at l[h*rs + j] (natural-log units).
 // Leaves the unnormalised sums in part[h][c] and (max, sum) in red[h].
-constexpr int kMergeMax = 32;  // partials one merge4 call takes (two load batches)
+constexpr int kMergeMax = 32;  // partials one merge4 call takes
 struct MergeLds {
     float w[4][kMergeMax];
-    float l[4][kMergeMax];
     float red[4][2];
     float part[2][4][128];
 };
 
+// Every load is issued before any is used (the o values do not depend on the
+// weights), so the merge waits for one round trip to the other workgroups'
+// writes; the weights of head h are computed by wave h, one partial per lane.
 __device__ __forceinline__ void merge4(const float* o, const float* m, const float* l, int64_t rs, int n, int tid,
                                        MergeLds& sm) {
     const int lane = tid & 63, h = tid >> 6;
-    if (lane < n) {
-        sm.w[h][lane] = ld_agent(m + h * rs + lane);
-        sm.l[h][lane] = ld_agent(l + h * rs + lane);
-    }  // n <= kMergeMax < 64
-    __syncthreads();
-    if (lane == 0) {
-        float M = kNegInf;
-        for (int j = 0; j < n; ++j) M = fmaxf(M, sm.w[h][j]);
-        float L = 0.f;
-        for (int j = 0; j < n; ++j) {
-            const float mj = sm.w[h][j];
-            const float wgt = (mj == kNegInf) ? 0.f : fast_exp2((mj - M) * kLog2e);
-            sm.w[h][j] = wgt;
-            L = fmaf(wgt, sm.l[h][j], L);
+    // thread = (half, head, 4 columns); half k takes j = k, k+2, ... (wave-uniform)
+    const int half = tid >> 7, idx = tid & 127, hh = idx >> 5, c4 = (idx & 31) * 4;
+    const float* ob = o + hh * rs * 128 + c4;
+    f32x2 v[kMergeMax / 2][2];
+#pragma unroll
+    for (int u = 0; u < kMergeMax / 2; ++u) {
+        const int j = half + 2 * u;
+        if (j < n) {
+            v[u][0] = ld_agent2(ob + (int64_t)j * 128);
+            v[u][1] = ld_agent2(ob + (int64_t)j * 128 + 2);
         }
+    }
+    float mj = kNegInf, lj = 0.f;
+    if (lane < n) {  // n <= kMergeMax < 64
+        mj = ld_agent(m + h * rs + lane);
+        lj = ld_agent(l + h * rs + lane);
+    }
+    // butterflies: every lane ends with the same, order-fixed result
+    float M = mj;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float wgt = (mj == kNegInf) ? 0.f : fast_exp2((mj - M) * kLog2e);
+    float L = wgt * lj;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) L += __shfl_xor(L, off);
+    if (lane < kMergeMax) sm.w[h][lane] = wgt;
+    if (lane == 0) {
         sm.red[h][0] = M;
         sm.red[h][1] = L;
     }
     __syncthreads();
-    // thread = (half, head, 4 columns); half k takes j = k, k+2, ...; 16 loads in
-    // flight per batch of 16 partials
-    const int half = tid >> 7, idx = tid & 127, hh = idx >> 5, c4 = (idx & 31) * 4;
-    const float* ob = o + hh * rs * 128 + c4;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int j0 = 0; j0 < n; j0 += 16) {
-        f32x2 v[8][2];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = min(j0 + half + 2 * u, n - 1);
-            v[u][0] = ld_agent2(ob + (int64_t)j * 128);
-            v[u][1] = ld_agent2(ob + (int64_t)j * 128 + 2);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = j0 + half + 2 * u;
-            const float wv = (j < n) ? sm.w[hh][j] : 0.f;
+    for (int u = 0; u < kMergeMax / 2; ++u) {
+        const int j = half + 2 * u;
+        if (j < n) {
+            const float wv = sm.w[hh][j];
             acc[0] = fmaf(wv, v[u][0][0], acc[0]);
             acc[1] = fmaf(wv, v[u][0][1], acc[1]);
             acc[2] = fmaf(wv, v[u][1][0], acc[2]);
