@@ -257,13 +257,15 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
 
     hipError_t e;
     const bool mfma = q->dtype == ATTN_BF16 && G == 4 && d == 128;
-    // Fuse the merge into the decode kernel when every workgroup is resident at
-    // once (at most two per compute unit): each workgroup's publish-and-ticket
-    // tail is then paid once instead of once per round of workgroups.
+    // Fuse the merge into the decode kernel when the launch has at most one
+    // workgroup per compute unit. Timed back to back, the fused tail (publish,
+    // ticket, merge by the last workgroup) costs about what a second kernel
+    // does; with one workgroup per CU the two were even at 128K keys, with two
+    // the second kernel won (64 splits: 88.5 against 86.8 us).
     const int cus = device_cu_count();
     const int64_t wgs = (int64_t)B * Hkv * pl->S;
     if (mfma && fused && (int64_t)B * Hkv <= attn::kMaxCounterGroups && pl->S <= attn::kMaxFusedSplits &&
-        cus > 0 && wgs <= 2LL * cus) {
+        cus > 0 && wgs <= cus) {
         p.counters = fused->counters;
         p.ticket_block = ticket_block_for(pl->S);
         p.blk_o = fused->blk_o;
@@ -388,8 +390,11 @@ attn_status two_span_launch(attn::DecodeParams& p, int S, bool fp8_0, bool fp8_1
 
     const int cus = device_cu_count();
     const int64_t wgs = (int64_t)B * Hkv * S;
+    // the same rule as the one-span decode (pi decode, 200 workgroups: fused
+    // 12.8 us, two kernels 13.5 us; two-precision, 512: fused 65 us, two
+    // kernels 64 us)
     const bool fused = (int64_t)B * Hkv <= attn::kMaxCounterGroups && S <= attn::kMaxFusedSplits && cus > 0 &&
-                       wgs <= 2LL * cus;
+                       wgs <= cus;
     if (fused) {
         p.counters = counters;
         p.ticket_block = ticket_block_for(S);

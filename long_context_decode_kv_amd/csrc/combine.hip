@@ -6,13 +6,16 @@
 // For a row with partials (o_s, m_s, l_s), s < n:
 //   m = max_s m_s,  w_s = exp(m_s - m),
 //   O = sum_s w_s o_s / sum_s w_s l_s,  lse = m + ln sum_s w_s l_s.
-// Workgroup (r, 128-dim block) with W = 4..16 waves: wave w takes the
-// partials s = w, w + W, ... in order, eight at a time, and keeps its own
-// running (max, sum, accumulator) so that all loads of a batch -- and those of
-// the next batch, issued before the current one is added -- are in flight at
-// once: merging a row of up to 128 partials costs one memory round trip. The W
-// wave results are then merged in a fixed order, so the result is
-// deterministic for a given n and S.
+// Workgroup (r, column block) with W = 4..16 waves. Each wave is cut into
+// 64/LP lane groups of LP lanes, and each lane group -- a "slot" -- takes
+// every (number of slots)-th partial in order, eight at a time, over 2*LP
+// columns (two per lane), keeping its own running (max, sum, accumulator), so
+// that all loads of a batch -- and those of the next batch, issued before the
+// current one is added -- are in flight at once: a row of up to 128 partials
+// costs one memory round trip. LP = 64 normally; launches with few rows and
+// many partials use LP = 32 or 16, i.e. narrower column blocks and more
+// workgroups. The slot results are merged in a fixed order, so the result is
+// deterministic for a given n and launch shape (which depends on R, S, d).
 #include "internal.h"
 
 namespace attn {
@@ -20,8 +23,10 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kBatch = 8;      // partials per wave per batch
+constexpr int kBatch = 8;      // partials per slot per batch
 constexpr int kMaxWaves = 16;  // waves per workgroup
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     uint32_t u = __builtin_bit_cast(uint32_t, x);
@@ -30,26 +35,33 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
     return (uint16_t)(u >> 16);
 }
 
-// One batch of a wave's partials: s = s0 + W*i, i < kBatch (clamped to n - 1;
-// the clamped copies are not added).
+// One batch of a slot's partials: s = s0 + NS*i, i < kBatch (clamped to
+// n - 1; the clamped copies are not added).
 struct Batch {
-    float m[kBatch], l[kBatch], o0[kBatch], o1[kBatch];
+    float m[kBatch], l[kBatch];
+    f32x2 o[kBatch];
 };
 
+template <int LP>
 __global__ __launch_bounds__(64 * kMaxWaves) void combine_partials_kernel(CombineParams p) {
+    constexpr int G = 64 / LP;  // slots per wave
     const int r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int W = blockDim.x >> 6;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int li = lane % LP;
+    const int slot = w * G + lane / LP, NS = W * G;
     const int b = r / p.Hq, h = r % p.Hq;
     int n = p.S;
     if (p.kv_lens) {
         const int len = min(max(p.kv_lens[b], 0), p.L_cap);
         n = min((len + p.chunk - 1) / p.chunk, p.S);
     }
-    // this lane's two columns (lanes past d read a valid column and discard it)
-    const int c0 = blockIdx.y * 128 + 2 * lane, c1 = c0 + 1;
-    const int64_t cc0 = min(c0, p.d - 1), cc1 = min(c1, p.d - 1);
+    // this lane's two columns; lanes past d read valid columns and discard them
+    const int c0 = blockIdx.y * 2 * LP + 2 * li;
+    const bool even = (p.d & 1) == 0;  // then (row * S + s) * d + c0 is even: 8-byte loads
+    const int64_t cv = min(c0, p.d - 2);
+    const int64_t cc0 = min(c0, p.d - 1), cc1 = min(c0 + 1, p.d - 1);
     const float* m_row = p.m_part + (int64_t)r * p.S;
     const float* l_row = p.l_part + (int64_t)r * p.S;
     const float* o_row = p.o_part + (int64_t)r * p.S * p.d;
@@ -57,11 +69,15 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_partials_kernel(Combin
     auto load = [&](Batch& t, int s0) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
-            const int64_t s = min(s0 + W * i, n - 1);
+            const int64_t s = min(s0 + NS * i, n - 1);
             t.m[i] = m_row[s];
             t.l[i] = l_row[s];
-            t.o0[i] = o_row[s * p.d + cc0];
-            t.o1[i] = o_row[s * p.d + cc1];
+            if (even) {
+                t.o[i] = *reinterpret_cast<const f32x2*>(o_row + s * p.d + cv);
+            } else {
+                t.o[i][0] = o_row[s * p.d + cc0];
+                t.o[i][1] = o_row[s * p.d + cc1];
+            }
         }
     };
     float M = kNegInf, L = 0.f, a0 = 0.f, a1 = 0.f;
@@ -69,7 +85,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_partials_kernel(Combin
         float bm = M;
 #pragma unroll
         for (int i = 0; i < kBatch; ++i)
-            if (s0 + W * i < n) bm = fmaxf(bm, t.m[i]);
+            if (s0 + NS * i < n) bm = fmaxf(bm, t.m[i]);
         if (bm > M) {  // the running max moves: rescale what is summed so far
             const float f = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((M - bm) * kLog2e);
             L *= f;
@@ -79,19 +95,19 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_partials_kernel(Combin
         }
 #pragma unroll
         for (int i = 0; i < kBatch; ++i) {
-            const bool use = s0 + W * i < n && t.m[i] != kNegInf;
+            const bool use = s0 + NS * i < n && t.m[i] != kNegInf;
             const float wgt = use ? __builtin_amdgcn_exp2f((t.m[i] - M) * kLog2e) : 0.f;
             L = fmaf(wgt, t.l[i], L);
-            a0 = fmaf(wgt, t.o0[i], a0);
-            a1 = fmaf(wgt, t.o1[i], a1);
+            a0 = fmaf(wgt, t.o[i][0], a0);
+            a1 = fmaf(wgt, t.o[i][1], a1);
         }
     };
-    if (w < n) {
+    if (slot < n) {
         Batch cur, nxt;
-        int s0 = w;
+        int s0 = slot;
         load(cur, s0);
         while (true) {
-            const int s1 = s0 + W * kBatch;
+            const int s1 = s0 + NS * kBatch;
             const bool more = s1 < n;
             if (more) load(nxt, s1);
             add(cur, s0);
@@ -100,40 +116,41 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_partials_kernel(Combin
             s0 = s1;
         }
     }
-    __shared__ float sm_m[kMaxWaves], sm_l[kMaxWaves];
-    __shared__ float sm_o[kMaxWaves][128];
-    sm_o[w][2 * lane] = a0;
-    sm_o[w][2 * lane + 1] = a1;
-    if (lane == 0) {
-        sm_m[w] = M;
-        sm_l[w] = L;
+    // slot-major: slot k's columns at [k * 2LP, (k + 1) * 2LP)
+    __shared__ float sm_m[kMaxWaves * G], sm_l[kMaxWaves * G];
+    __shared__ float sm_o[kMaxWaves * 128];
+    sm_o[slot * 2 * LP + 2 * li] = a0;
+    sm_o[slot * 2 * LP + 2 * li + 1] = a1;
+    if (li == 0) {
+        sm_m[slot] = M;
+        sm_l[slot] = L;
     }
     __syncthreads();
-    if (w == 0) {
+    if (tid < LP) {  // wave 0, lane group 0: the row's 2*LP columns
         float mx = kNegInf;
-        for (int i = 0; i < W; ++i) mx = fmaxf(mx, sm_m[i]);
+        for (int k = 0; k < NS; ++k) mx = fmaxf(mx, sm_m[k]);
         float so0 = 0.f, so1 = 0.f, sl = 0.f;
         if (mx != kNegInf)
-            for (int i = 0; i < W; ++i) {
-                const float mi = sm_m[i];
-                const float f = (mi == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((mi - mx) * kLog2e);
-                sl = fmaf(f, sm_l[i], sl);
-                so0 = fmaf(f, sm_o[i][2 * lane], so0);
-                so1 = fmaf(f, sm_o[i][2 * lane + 1], so1);
+            for (int k = 0; k < NS; ++k) {
+                const float mk = sm_m[k];
+                const float f = (mk == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((mk - mx) * kLog2e);
+                sl = fmaf(f, sm_l[k], sl);
+                so0 = fmaf(f, sm_o[k * 2 * LP + 2 * li], so0);
+                so1 = fmaf(f, sm_o[k * 2 * LP + 2 * li + 1], so1);
             }
         const bool empty = (mx == kNegInf) || !(sl > 0.f);
         const float inv = empty ? 0.f : 1.f / sl;
         const int64_t off = b * p.out_sb + h * p.out_sh;
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
-            const int c = e ? c1 : c0;
+            const int c = c0 + e;
             if (c < p.d) {
                 const float val = (e ? so1 : so0) * inv;
                 if (p.out_dtype == DT_BF16) static_cast<uint16_t*>(p.out)[off + c] = f32_to_bf16_rne(val);
                 else static_cast<float*>(p.out)[off + c] = val;
             }
         }
-        if (p.lse && blockIdx.y == 0 && lane == 0) p.lse[r] = empty ? kNegInf : mx + logf(sl);
+        if (p.lse && blockIdx.y == 0 && tid == 0) p.lse[r] = empty ? kNegInf : mx + logf(sl);
     }
 }
 
@@ -155,12 +172,17 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t stream) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
-    // enough waves that each takes at most one batch up to n = 128, more
-    // batches per wave beyond
-    const int need = (p.S + kBatch - 1) / kBatch;
+    // Lanes per partial: 64 unless that leaves fewer than 256 workgroups for a
+    // deep merge (more than 64 partials per row); then narrower column blocks.
+    int lp = 64;
+    while (lp > 16 && p.S > 64 && (int64_t)p.R * ((p.d + 2 * lp - 1) / (2 * lp)) < 256) lp >>= 1;
+    // enough waves (4 to 16) that each slot takes one batch where it can
+    const int need = (p.S + kBatch * (64 / lp) - 1) / (kBatch * (64 / lp));
     const int waves = need < 4 ? 4 : (need > kMaxWaves ? kMaxWaves : need);
-    dim3 grid(p.R, (p.d + 127) / 128);
-    hipLaunchKernelGGL(combine_partials_kernel, grid, dim3(64 * waves), 0, stream, p);
+    const dim3 grid(p.R, (p.d + 2 * lp - 1) / (2 * lp)), block(64 * waves);
+    if (lp == 64) hipLaunchKernelGGL(combine_partials_kernel<64>, grid, block, 0, stream, p);
+    else if (lp == 32) hipLaunchKernelGGL(combine_partials_kernel<32>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(combine_partials_kernel<16>, grid, block, 0, stream, p);
     return hipGetLastError();
 }
 

@@ -267,17 +267,22 @@ def test_two_level_api_matches_fused_decode(wl, S):
     assert np.all(np.abs(a - b) <= 2.0 ** -7 * np.maximum(np.abs(a), np.abs(b)) + 1e-6)
 
 
-def test_combine_partials_api_against_oracle():
+# (R, S, d): one column block of 64 lanes; a deep merge over few rows (32- and
+# 16-lane slots, three column blocks); odd d (4-byte loads); one partial
+@pytest.mark.parametrize("R,S,d", [(5, 37, 96), (4, 300, 96), (3, 200, 7), (4, 1, 128)])
+def test_combine_partials_api_against_oracle(R, S, d):
     import long_context_decode_kv_amd as lib
-    rng = np.random.default_rng(9)
-    R, S, d = 5, 37, 96
+    rng = np.random.default_rng(9 + S)
     o = rng.standard_normal((R, S, d)).astype(np.float32)
     m = (rng.standard_normal((R, S)) * 3).astype(np.float32)
     l = rng.uniform(0.5, 20, (R, S)).astype(np.float32)
     m[1, :] = -np.inf
     l[1, :] = 0.0
-    m[2, 5:] = -np.inf
-    l[2, 5:] = 0.0
+    if S > 5:
+        m[2, 5:] = -np.inf
+        l[2, 5:] = 0.0
+    if R > 3:
+        m[3] = np.arange(S, dtype=np.float32) * 0.25  # the max moves with every batch
     for dt, kind in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
         out, lse = lib.attn_combine_partials(to_dev(o), to_dev(m), to_dev(l), out_dtype=dt)
         torch.cuda.synchronize()
