@@ -125,6 +125,24 @@ def test_workload2_auto_splits_and_determinism():
     assert_close(from_dev(out)[:, :, 0], ref, "bf16", what="wl2 auto")
 
 
+# ------------------------------------------------------------ many splits
+
+@pytest.mark.parametrize("wl,B,L,S", [(2, 2, 65436, 256), (2, 1, 100000, 521), (5, 1, 100000, 521)])
+def test_many_splits_several_rounds_of_workgroups(wl, B, L, S):
+    # Several rounds of workgroups, merged by the second kernel. Covers a short
+    # last split ending mid-tile, an odd split count and 192-key chunks.
+    inp = make_inputs(wl, B=B, Hq=32, Hkv=8, L=L, seed=60 + S)
+    dev = {k: to_dev(v) for k, v in inp.items()}
+    out, lse = decode_on_gpu(inp, num_splits=S, dev=dev)
+    ref, ref_lse = oracle_decode(inp)
+    res = assert_close(from_dev(out)[:, :, 0, :], ref, "bf16" if wl == 2 else "e4m3", what="multi L=%d S=%d" % (L, S))
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, 2e-3)
+    print("multi wl%d L=%d S=%d max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (wl, L, S, *res), flush=True)
+    out2, lse2 = decode_on_gpu(inp, num_splits=S, dev=dev)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+
+
 # ------------------------------------------------------------ fp8 KV
 
 @pytest.mark.parametrize("S", [1, 3, 16])
