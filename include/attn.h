@@ -146,9 +146,10 @@ ATTN_API int attn_decode_plan(int L_cap, int num_splits, int* chunk);
  * lse      device float [B*Hq] or NULL
  * workspace  device memory of at least attn_decode_workspace_size(B, Hq, d, S)
  *          bytes for the split count S in use, 16-byte aligned, prepared once
- *          by attn_decode_workspace_init. On the MFMA path the last workgroup
- *          of each (sequence, KV head) merges the partials (one kernel); the
- *          vector-ALU path runs the merge as a second kernel.
+ *          by attn_decode_workspace_init. The partials are merged by a second
+ *          kernel, except on the MFMA path when the launch has at most one
+ *          workgroup per compute unit (B * Hkv * S <= CUs): then the last
+ *          workgroup of each (sequence, KV head) merges them in the same kernel.
  *
  * q, k and v need 16-byte aligned data and strides that are multiples of 16
  * bytes. Supported: d in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.

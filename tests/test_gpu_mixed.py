@@ -48,7 +48,7 @@ def test_mixed_per_head_ragged_lengths_and_empty_spans():
 def test_mixed_fused_and_separate_merge_agree_with_the_oracle():
     # 4 (sequence, KV head) groups: 2 + 5 splits keep every workgroup resident
     # (merge fused into the decode kernel); 100 + 100 splits do not (separate
-    # combine kernel); 300 + 300 exceed the fused merge's split limit.
+    # combine kernel); 200 + 300 exceed the fused merge's split limit.
     inp = make_mixed_inputs(B=2, Hq=8, Hkv=2, L_hi=12800, L_lo=38400, lens=(0.3, 1.0), seed=62)
     dev = {k: to_dev(v) for k, v in inp.items()}
     for S_hi, S_lo in ((2, 5), (100, 100), (200, 300)):
