@@ -49,6 +49,9 @@ def _load():
     lib.dg_f32_to_bf16.restype = ctypes.c_uint16
     lib.dg_f32_to_e4m3.argtypes = [ctypes.c_float]
     lib.dg_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.dg_f32_to_e2m1.argtypes = [ctypes.c_float]
+    lib.dg_f32_to_e2m1.restype = ctypes.c_uint8
+    lib.dg_fill_mxfp4.argtypes = [u64, u64, u64, u64, dbl, vp, vp, i32]
     _lib = lib
     return lib
 
@@ -94,6 +97,25 @@ def normal_e4m3(seed, tensor_id, shape, mul=1.0):
     return out, scales
 
 
+def normal_mxfp4(seed, tensor_id, shape, mul=1.0):
+    """OCP MX fp4 of N(0,1)*mul (the values normal_f32 draws for ``shape``):
+    ``shape`` is (..., d) with d a multiple of 32; every 32 consecutive values
+    of the last dimension share a power-of-two scale 2^X, X = floor(log2 amax)
+    - 2, stored as the E8M0 byte X + 127, and each value is the E2M1 code of
+    x / 2^X (nearest, ties to even, saturating to 6), two codes per byte with
+    element 2i in the low nibble of byte i. Returns (codes (..., d/2) uint8,
+    scales (..., d/32) uint8)."""
+    d = int(shape[-1])
+    if d % 32:
+        raise ValueError("d must be a multiple of 32")
+    rows = int(np.prod(shape[:-1])) if len(shape) > 1 else 1
+    codes = np.empty(tuple(shape[:-1]) + (d // 2,), dtype=np.uint8)
+    scales = np.empty(tuple(shape[:-1]) + (d // 32,), dtype=np.uint8)
+    if rows:
+        _load().dg_fill_mxfp4(seed, tensor_id, rows, d, mul, _ptr(codes), _ptr(scales), _threads())
+    return codes, scales
+
+
 def uniform_int(seed, tensor_id, n, lo, hi):
     out = np.empty(n, dtype=np.int32)
     _load().dg_uniform_int(seed, tensor_id, n, lo, hi, _ptr(out))
@@ -119,6 +141,14 @@ def f32_to_bf16_bits(x):
     lib = _load()
     x = np.asarray(x, dtype=np.float32)
     return np.array([lib.dg_f32_to_bf16(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def f32_to_e2m1(x):
+    """Encode an fp32 array into E2M1 codes (0..15; nearest, ties to even,
+    saturating to +-6)."""
+    lib = _load()
+    x = np.asarray(x, dtype=np.float32)
+    return np.array([lib.dg_f32_to_e2m1(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
 
 
 def f32_to_e4m3(x):

@@ -3,7 +3,8 @@
  *
  * This module holds NONE of the attention arithmetic. It only draws numbers
  * and stores them in the storage formats the library reads (fp32, bf16 bit
- * patterns, OCP fp8-e4m3 codes with a per-head fp32 scale). Both the HIP path
+ * patterns, OCP fp8-e4m3 codes with a per-head fp32 scale, OCP MX fp4 codes
+ * with one power-of-two scale per 32 elements). Both the HIP path
  * and the double-precision oracle consume its output; neither shares any other
  * code with the other.
  *
@@ -182,6 +183,89 @@ void dg_fill_e4m3(uint64_t seed, uint64_t tensor_id, uint64_t groups, uint64_t p
         jobs[t].out = out;
         jobs[t].scales = scales;
         pthread_create(&th[t], NULL, e4m3_worker, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/* OCP MX FP4 element (E2M1): sign bit, 2-bit exponent (bias 1), 1-bit
+ * mantissa; code c = eem holds the magnitude 0, 0.5, 1, 1.5, 2, 3, 4, 6 for
+ * c = 0 .. 7. Round to nearest, ties to the even code (mantissa bit 0),
+ * saturating to +-6. */
+uint8_t dg_f32_to_e2m1(float xf) {
+    static const double grid[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+    double x = (double)xf;
+    uint8_t sign = 0;
+    if (x != x) return 0;
+    if (x < 0 || (x == 0 && signbit(x))) { sign = 0x8; x = -x; }
+    if (x >= 6.0) return sign | 7;
+    int c = 0;
+    while (grid[c + 1] <= x) ++c; /* grid[c] <= x < grid[c + 1], c < 7 */
+    const double mid = 0.5 * (grid[c] + grid[c + 1]);
+    if (x > mid || (x == mid && (c & 1))) ++c;
+    return sign | (uint8_t)c;
+}
+
+/* OCP MX FP4 with block size 32 along the last dimension: per block of 32
+ * consecutive values, the shared scale is 2^X with X = floor(log2(amax)) - 2
+ * (2 = the largest E2M1 exponent), stored as the E8M0 byte X + 127 (X held
+ * in [-127, 127]; an all-zero block stores 127), and each element is
+ * e2m1(x / 2^X). Codes pack two per byte, element 2i in the low nibble of
+ * byte i of its row. `d` must be a multiple of 32. */
+typedef struct {
+    uint64_t key, d, r0, r1;
+    double mul;
+    uint8_t* codes;
+    uint8_t* scales;
+} mx_job;
+
+static void* mx_worker(void* arg) {
+    mx_job* j = (mx_job*)arg;
+    for (uint64_t r = j->r0; r < j->r1; ++r) {
+        for (uint64_t b0 = 0; b0 < j->d; b0 += 32) {
+            float v[32];
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                v[i] = (float)(normal_at(j->key, r * j->d + b0 + i) * j->mul);
+                if (fabsf(v[i]) > amax) amax = fabsf(v[i]);
+            }
+            int X = 0;
+            if (amax > 0.0f) {
+                int e;
+                frexp((double)amax, &e); /* amax = f * 2^e, f in [0.5, 1): floor(log2 amax) = e - 1 */
+                X = (e - 1) - 2;
+                if (X < -127) X = -127;
+                if (X > 127) X = 127;
+            }
+            j->scales[r * (j->d / 32) + b0 / 32] = (uint8_t)(X + 127);
+            uint8_t* o = j->codes + r * (j->d / 2) + b0 / 2;
+            for (int i = 0; i < 32; i += 2) {
+                const uint8_t lo = dg_f32_to_e2m1((float)ldexp((double)v[i], -X));
+                const uint8_t hi = dg_f32_to_e2m1((float)ldexp((double)v[i + 1], -X));
+                o[i / 2] = (uint8_t)(lo | (hi << 4));
+            }
+        }
+    }
+    return NULL;
+}
+
+void dg_fill_mxfp4(uint64_t seed, uint64_t tensor_id, uint64_t rows, uint64_t d, double mul, uint8_t* codes,
+                   uint8_t* scales, int nthreads) {
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if ((uint64_t)nthreads > rows) nthreads = (int)rows;
+    if (nthreads < 1) return;
+    pthread_t th[256];
+    mx_job jobs[256];
+    uint64_t key = stream_key(seed, tensor_id);
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t].key = key;
+        jobs[t].d = d;
+        jobs[t].r0 = rows * (uint64_t)t / (uint64_t)nthreads;
+        jobs[t].r1 = rows * (uint64_t)(t + 1) / (uint64_t)nthreads;
+        jobs[t].mul = mul;
+        jobs[t].codes = codes;
+        jobs[t].scales = scales;
+        pthread_create(&th[t], NULL, mx_worker, &jobs[t]);
     }
     for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
 }

@@ -11,7 +11,7 @@ per (batch, KV head).
 import numpy as np
 
 from . import (TID_K, TID_K_LO, TID_LENS, TID_LENS_LO, TID_Q, TID_V, TID_V_LO, normal_bf16_bits, normal_e4m3,
-               normal_f32, uniform_int)
+               normal_f32, normal_mxfp4, uniform_int)
 
 WORKLOADS = {
     1: dict(name="single-head decode, fp32, L=1024, d=64, 4 splits", kind="decode", B=1, Hq=1, Hkv=1, d=64,
@@ -30,6 +30,10 @@ WORKLOADS = {
             Hq=32, Hkv=8, d=128, L=131072, q="bf16", kv="bf16", mul=0.5, causal=True, window=4096, period=64),
     8: dict(name="pi-Attention causal prefill, bf16, L=16384, window 512, period 64, 32q/8kv, d=128", kind="prefill",
             B=1, Hq=32, Hkv=8, d=128, L=16384, q="bf16", kv="bf16", mul=1.0, causal=True, window=512, period=64),
+    9: dict(name="two-precision KV decode, L=131072: first and last 10% bf16, the rest MX fp4 (e2m1, one e8m0 scale "
+                 "per 32), 32q/8kv, d=128",
+            kind="mixed", B=1, Hq=32, Hkv=8, d=128, L=131072, hi_frac=0.1, q="bf16", mul=0.5, causal=False,
+            lo="mxfp4"),
 }
 
 # Tensor id of the pi-Attention gate alpha (one value per query row, uniform in
@@ -82,6 +86,9 @@ def make_mixed_inputs(wl=6, seed=None, B=None, Hq=None, Hkv=None, d=None, L=None
     Key order does not change single-query attention, so the bf16 keys are
     stored as one span k_hi/v_hi [B,Hkv,L_hi,d] and the fp8 keys as another,
     k_lo/v_lo [B,Hkv,L_lo,d] with one amax/448 scale per (batch, KV head).
+    A workload with lo="mxfp4" keeps the low span as MX fp4 instead: k_lo/v_lo
+    are codes [B,Hkv,L_lo,d/2] and k_scale/v_scale their E8M0 block scales
+    [B,Hkv,L_lo,d/32].
     `lens` = (lo, hi) draws a valid length per (batch, KV head) for each span
     uniformly from [lo*cap, hi*cap] (ragged per head); None = full spans.
     Returns dict(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens, lo_lens)."""
@@ -101,13 +108,18 @@ def make_mixed_inputs(wl=6, seed=None, B=None, Hq=None, Hkv=None, d=None, L=None
     q = normal_bf16_bits(seed, TID_Q, (B, Hq, 1, d), mul)
     k_hi = normal_bf16_bits(seed, TID_K, (B, Hkv, L_hi, d), mul) if L_hi else None
     v_hi = normal_bf16_bits(seed, TID_V, (B, Hkv, L_hi, d), mul) if L_hi else None
-    k_lo, ks = normal_e4m3(seed, TID_K_LO, (B, Hkv, L_lo, d), mul) if L_lo else (None, None)
-    v_lo, vs = normal_e4m3(seed, TID_V_LO, (B, Hkv, L_lo, d), mul) if L_lo else (None, None)
+    mx = cfg.get("lo") == "mxfp4"
+    lo_fill = normal_mxfp4 if mx else normal_e4m3
+    k_lo, ks = lo_fill(seed, TID_K_LO, (B, Hkv, L_lo, d), mul) if L_lo else (None, None)
+    v_lo, vs = lo_fill(seed, TID_V_LO, (B, Hkv, L_lo, d), mul) if L_lo else (None, None)
     hi_lens = lo_lens = None
     if lens is not None:
         lo_f, hi_f = lens
         hi_lens = uniform_int(seed, TID_LENS, B * Hkv, int(lo_f * L_hi), int(hi_f * L_hi))
         lo_lens = uniform_int(seed, TID_LENS_LO, B * Hkv, int(lo_f * L_lo), int(hi_f * L_lo))
+    if mx:
+        return dict(q=q, k_hi=k_hi, v_hi=v_hi, k_lo=k_lo, v_lo=v_lo, k_scale=ks, v_scale=vs, hi_lens=hi_lens,
+                    lo_lens=lo_lens, lo_format="mxfp4")
     return dict(q=q, k_hi=k_hi, v_hi=v_hi, k_lo=k_lo, v_lo=v_lo, k_scale=None if ks is None else ks.ravel(),
                 v_scale=None if vs is None else vs.ravel(), hi_lens=hi_lens, lo_lens=lo_lens)
 

@@ -62,6 +62,12 @@ def _load():
     lib.oracle_e4m3_to_f64.restype = dbl
     lib.oracle_decode_elems.argtypes = [vp, i32, i64, vp]
     lib.oracle_decode_elems.restype = None
+    lib.oracle_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_to_f64.restype = dbl
+    lib.oracle_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+    lib.oracle_e8m0_to_f64.restype = dbl
+    lib.oracle_mxfp4_decode.argtypes = [vp, vp, i64, i32, vp]
+    lib.oracle_mxfp4_decode.restype = None
     _lib = lib
     return lib
 
@@ -229,6 +235,33 @@ def e4m3_to_f64(codes):
     return np.array([lib.oracle_e4m3_to_f64(int(c)) for c in codes.ravel()]).reshape(codes.shape)
 
 
+def e2m1_to_f64(codes):
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e2m1_to_f64(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def e8m0_to_f64(codes):
+    lib = _load()
+    codes = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.oracle_e8m0_to_f64(int(c)) for c in codes.ravel()]).reshape(codes.shape)
+
+
+def mxfp4_to_f64(codes, scales):
+    """Real values (float64) of MX FP4 rows: codes (..., d/2) uint8 (element 2i
+    in the low nibble of byte i), scales (..., d/32) uint8 E8M0."""
+    lib = _load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    d = codes.shape[-1] * 2
+    assert scales.shape[-1] * 32 == d and codes.shape[:-1] == scales.shape[:-1]
+    rows = int(np.prod(codes.shape[:-1])) if codes.ndim > 1 else 1
+    out = np.empty(codes.shape[:-1] + (d,), dtype=np.float64)
+    if out.size:
+        lib.oracle_mxfp4_decode(_p(codes), _p(scales), rows, d, _p(out))
+    return out
+
+
 def decode_elems(a):
     """Real values (float64) of stored elements: float32, bf16 bits (uint16),
     e4m3 codes (uint8) or float64, with no scale applied."""
@@ -241,7 +274,7 @@ def decode_elems(a):
 
 
 def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_lens=None, scale=None,
-                 heads=None):
+                 heads=None, lo_format="e4m3"):
     """Single-query decode over a cache kept in two precisions.
 
     q [B,Hq,1,d] (bf16 bits or float32); k_hi, v_hi [B,Hkv,L_hi,d] bf16 bits
@@ -252,6 +285,8 @@ def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_l
     keys and valid fp8 keys (the latter at code * scale): the union is built in
     float64 and handed to the plain attention above. `heads` lists flat query
     heads b*Hq + h (all when None). Returns (out [n,d], lse [n]) in float64.
+    With lo_format="mxfp4" the low span is MX FP4: k_lo, v_lo are codes
+    [B,Hkv,L_lo,d/2] and k_scale, v_scale their E8M0 scales [B,Hkv,L_lo,d/32].
     """
     q = np.ascontiguousarray(q)
     B, Hq, Lq, d = q.shape
@@ -262,8 +297,12 @@ def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_l
     L_lo = 0 if k_lo is None else k_lo.shape[2]
     hl = np.full(B * Hkv, L_hi, np.int64) if hi_lens is None else np.clip(np.asarray(hi_lens).ravel(), 0, L_hi)
     ll = np.full(B * Hkv, L_lo, np.int64) if lo_lens is None else np.clip(np.asarray(lo_lens).ravel(), 0, L_lo)
-    ks = None if k_scale is None else np.asarray(k_scale, np.float32).ravel()
-    vs = None if v_scale is None else np.asarray(v_scale, np.float32).ravel()
+    mx = lo_format == "mxfp4"
+    if mx:
+        ks, vs = k_scale, v_scale
+    else:
+        ks = None if k_scale is None else np.asarray(k_scale, np.float32).ravel()
+        vs = None if v_scale is None else np.asarray(v_scale, np.float32).ravel()
     heads = np.arange(B * Hq) if heads is None else np.asarray(heads).ravel()
     out = np.zeros((heads.size, d), np.float64)
     lse = np.zeros(heads.size, np.float64)
@@ -276,7 +315,10 @@ def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_l
         if hl[bg]:
             kparts.append(decode_elems(k_hi[b, g, :hl[bg]]))
             vparts.append(decode_elems(v_hi[b, g, :hl[bg]]))
-        if ll[bg]:
+        if ll[bg] and mx:
+            kparts.append(mxfp4_to_f64(k_lo[b, g, :ll[bg]], ks[b, g, :ll[bg]]))
+            vparts.append(mxfp4_to_f64(v_lo[b, g, :ll[bg]], vs[b, g, :ll[bg]]))
+        elif ll[bg]:
             kparts.append(decode_elems(k_lo[b, g, :ll[bg]]) * np.float64(ks[bg]))
             vparts.append(decode_elems(v_lo[b, g, :ll[bg]]) * np.float64(vs[bg]))
         n = int(hl[bg] + ll[bg])

@@ -47,7 +47,11 @@
  * attention over the union of the two key sets at their real values: the
  * Python side decodes both spans with oracle_decode_elems, multiplies the fp8
  * span by its scale in double, concatenates them, and calls oracle_attention
- * with OR_F64 keys and values.
+ * with OR_F64 keys and values. The low-precision span may also be FP4 (the
+ * page names a 4-bit float with a 2-bit exponent): stored as OCP MX FP4, whose
+ * elements are E2M1 codes and whose every 32 consecutive elements of a row
+ * share a power-of-two E8M0 scale (OCP Microscaling Formats (MX) v1.0); it is
+ * decoded exactly by oracle_mxfp4_decode.
  */
 #include <math.h>
 #include <pthread.h>
@@ -80,6 +84,35 @@ double oracle_e4m3_to_f64(uint8_t code) {
     if (e == 0) v = ldexp((double)m / 8.0, 1 - 7);
     else v = ldexp(1.0 + (double)m / 8.0, e - 7);
     return s ? -v : v;
+}
+
+/* E2M1 (the MX FP4 element): 1 sign, 2 exponent (bias 1), 1 mantissa bit.
+ * Exponent field 0: subnormal, value m * 2^-1; otherwise (1 + m/2) * 2^(e-1).
+ * No infinities or NaN. */
+double oracle_e2m1_to_f64(uint8_t code) {
+    int s = (code >> 3) & 1;
+    int e = (code >> 1) & 3;
+    int m = code & 1;
+    double v = e ? ldexp(1.0 + (double)m / 2.0, e - 1) : ldexp((double)m, -1);
+    return s ? -v : v;
+}
+
+/* E8M0 (the MX shared scale): 2^(E - 127); E = 255 is NaN. */
+double oracle_e8m0_to_f64(uint8_t e) {
+    if (e == 255) return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* Real values of `rows` rows of d MX FP4 elements: codes [rows][d/2] (element
+ * 2i in the low nibble of byte i, element 2i + 1 in the high nibble), scales
+ * [rows][d/32] (one per 32 consecutive elements); dst [rows][d]. */
+void oracle_mxfp4_decode(const uint8_t* codes, const uint8_t* scales, int64_t rows, int d, double* dst) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int c = 0; c < d; ++c) {
+            const uint8_t byte = codes[r * (d / 2) + c / 2];
+            const uint8_t code = (c & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+            dst[r * d + c] = oracle_e2m1_to_f64(code) * oracle_e8m0_to_f64(scales[r * (d / 32) + c / 32]);
+        }
 }
 
 typedef struct {

@@ -106,3 +106,27 @@ def test_bf16_encoder_rounds_midpoints_to_even():
     # just above and just below a midpoint go to the nearer neighbour
     assert np.array_equal(datagen.f32_to_bf16_bits(((lo << 16) | 0x8001).view(np.float32)).astype(np.uint32), lo + 1)
     assert np.array_equal(datagen.f32_to_bf16_bits(((lo << 16) | 0x7FFF).view(np.float32)).astype(np.uint32), lo)
+
+
+def test_e2m1_encoder_rounds_ties_to_even_and_saturates():
+    # midpoints between neighbouring E2M1 magnitudes go to the code whose
+    # mantissa bit is 0; magnitudes past 6 saturate; the sign is bit 3
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    assert datagen.f32_to_e2m1(mids).tolist() == [0, 2, 2, 4, 4, 6, 6]
+    assert datagen.f32_to_e2m1(-mids).tolist() == [8, 10, 10, 12, 12, 14, 14]
+    assert datagen.f32_to_e2m1(np.array([6.0, 6.5, 1e30, -7.0], np.float32)).tolist() == [7, 7, 7, 15]
+    # just off a midpoint goes to the nearer neighbour
+    assert datagen.f32_to_e2m1(np.array([0.2501, 0.7499, 4.99, 5.01], np.float32)).tolist() == [1, 1, 6, 7]
+
+
+def test_mxfp4_fill_is_reproducible_and_thread_independent():
+    a = datagen.normal_mxfp4(5, 4, (7, 3, 128), 0.5)
+    b = datagen.normal_mxfp4(5, 4, (7, 3, 128), 0.5)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+    lib = datagen._load()
+    c1 = np.empty((21, 64), np.uint8); s1 = np.empty((21, 4), np.uint8)
+    c7 = np.empty((21, 64), np.uint8); s7 = np.empty((21, 4), np.uint8)
+    lib.dg_fill_mxfp4(5, 4, 21, 128, 0.5, datagen._ptr(c1), datagen._ptr(s1), 1)
+    lib.dg_fill_mxfp4(5, 4, 21, 128, 0.5, datagen._ptr(c7), datagen._ptr(s7), 7)
+    assert np.array_equal(c1, c7) and np.array_equal(s1, s7)
+    assert np.array_equal(c1.reshape(a[0].shape), a[0]) and np.array_equal(s1.reshape(a[1].shape), a[1])

@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 import torch
 
+import datagen
 import oracle
 
 RNG = np.random.default_rng(12345)
@@ -639,3 +640,94 @@ def test_backward_key_gradients_sum_to_zero():
     # and the value gradients of a head add up to the sum of its rows' dO
     np.testing.assert_allclose(dv.sum(axis=2), dout.astype(np.float64).reshape(B, Hkv, -1, d).sum(axis=2),
                                rtol=1e-12, atol=1e-10)
+
+
+# ------------------------------------------------ MX FP4 low-precision span
+# The page's FP4 (a 4-bit float with a 2-bit exponent) held as OCP MX FP4:
+# E2M1 elements, one E8M0 power-of-two scale per 32 consecutive elements of a
+# row, two elements per byte with the first in the low nibble.
+
+def _e2m1_table(code):
+    # the magnitudes OCP MX v1.0 lists for E2M1 codes 0..7; bit 3 is the sign
+    mag = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0][code & 7]
+    return -mag if code & 8 else mag
+
+
+def test_e2m1_decoder_is_the_ocp_table():
+    got = oracle.e2m1_to_f64(np.arange(16, dtype=np.uint8))
+    assert [float(x) for x in got] == [_e2m1_table(c) for c in range(16)]
+    assert math.copysign(1.0, float(got[8])) == -1.0  # code 8 is negative zero
+
+
+def test_e8m0_decoder_is_a_power_of_two():
+    got = oracle.e8m0_to_f64(np.arange(256, dtype=np.uint8))
+    assert all(float(got[e]) == math.ldexp(1.0, e - 127) for e in range(255))
+    assert math.isnan(float(got[255]))
+
+
+def test_mxfp4_rows_low_nibble_first_one_scale_per_32():
+    codes = np.zeros((2, 32), np.uint8)
+    scales = np.array([[127, 130], [120, 127]], np.uint8)
+    codes[0, 0] = 0x71   # element 0: code 1 (0.5); element 1: code 7 (6)
+    codes[0, 16] = 0x0A  # element 32: code 10 (-1), in the second block (scale 2^3)
+    codes[1, 31] = 0xF0  # element 62: 0; element 63: code 15 (-6)
+    out = oracle.mxfp4_to_f64(codes, scales)
+    assert out[0, 0] == 0.5 and out[0, 1] == 6.0 and out[0, 32] == -8.0 and out[1, 63] == -6.0
+    assert np.count_nonzero(out) == 4
+
+
+def test_mxfp4_codes_of_the_input_generator_decode_to_their_values():
+    # the generator's encoder (OCP MX conversion) and the oracle's decoder are
+    # separate code: decoded values are the drawn values to within half a grid
+    # step of the block, or the block's +-6 * scale where the value saturates
+    shape = (3, 5, 128)
+    f = datagen.normal_f32(7, 4, shape, 0.5).astype(np.float64)
+    codes, sc = datagen.normal_mxfp4(7, 4, shape, 0.5)
+    got = oracle.mxfp4_to_f64(codes, sc)
+    s = np.repeat(np.ldexp(1.0, sc.astype(np.int64) - 127), 32, axis=-1)
+    y = f / s
+    blk = np.abs(y).reshape(-1, 32).max(axis=1)
+    assert np.all((blk >= 4) & (blk < 8))  # the shared exponent is floor(log2 amax) - 2
+    sat = np.abs(y) > 6
+    assert np.all(got[sat] == np.sign(f[sat]) * 6 * s[sat])
+    step = np.where(np.abs(y) < 2, 0.5, np.where(np.abs(y) < 4, 1.0, 2.0))
+    assert np.all(np.abs(got - f)[~sat] <= 0.5 * step[~sat] * s[~sat])
+
+
+def test_mixed_fp4_span_is_attention_over_the_decoded_union():
+    B, Hq, Hkv, L_hi, L_lo, d = 2, 4, 2, 5, 9, 64
+    rng = np.random.default_rng(11)
+    tq = torch.from_numpy(rng.standard_normal((B, Hq, 1, d)).astype(np.float32)).to(torch.bfloat16)
+    khi = torch.from_numpy(rng.standard_normal((B, Hkv, L_hi, d)).astype(np.float32)).to(torch.bfloat16)
+    vhi = torch.from_numpy(rng.standard_normal((B, Hkv, L_hi, d)).astype(np.float32)).to(torch.bfloat16)
+    klo = rng.integers(0, 256, (B, Hkv, L_lo, d // 2), dtype=np.uint8)
+    vlo = rng.integers(0, 256, (B, Hkv, L_lo, d // 2), dtype=np.uint8)
+    ksc = rng.integers(121, 129, (B, Hkv, L_lo, d // 32), dtype=np.uint8)
+    vsc = rng.integers(121, 129, (B, Hkv, L_lo, d // 32), dtype=np.uint8)
+    hl = np.array([5, 0, 2, 4], np.int32)  # per (sequence, KV head); one head has no bf16 key
+    ll = np.array([9, 3, 0, 1], np.int32)  # and one no fp4 key
+    out, lse = oracle.decode_mixed(_bits(tq), _bits(khi), _bits(vhi), klo, vlo, ksc, vsc, hl, ll,
+                                   lo_format="mxfp4")
+
+    def dec(codes, scales):  # test-side decode: the table above, ldexp for the scale
+        vals = np.empty(codes.shape[:-1] + (d,))
+        for idx in np.ndindex(*codes.shape[:-1]):
+            for c in range(d):
+                byte = int(codes[idx + (c // 2,)])
+                code = byte >> 4 if c & 1 else byte & 15
+                vals[idx + (c,)] = math.ldexp(_e2m1_table(code), int(scales[idx + (c // 32,)]) - 127)
+        return vals
+
+    kld, vld = dec(klo, ksc), dec(vlo, vsc)
+    qd = tq.to(torch.float64).numpy()
+    khd, vhd = khi.to(torch.float64).numpy(), vhi.to(torch.float64).numpy()
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            bg = b * Hkv + g
+            krows = list(khd[b, g, :hl[bg]]) + list(kld[b, g, :ll[bg]])
+            vrows = list(vhd[b, g, :hl[bg]]) + list(vld[b, g, :ll[bg]])
+            o_ref, l_ref = brute_row(qd[b, h, 0], krows, vrows, 1 / math.sqrt(d))
+            np.testing.assert_allclose(out[b * Hq + h], o_ref, rtol=1e-12, atol=1e-14)
+            assert abs(lse[b * Hq + h] - l_ref) < 1e-12
