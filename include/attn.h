@@ -74,7 +74,16 @@ typedef enum attn_status {
 typedef enum attn_dtype {
     ATTN_F32 = 0,
     ATTN_BF16 = 1,
-    ATTN_FP8_E4M3 = 2
+    ATTN_FP8_E4M3 = 2,
+    /* OCP MX fp4 elements (E2M1: sign, 2-bit exponent with bias 1, 1-bit
+     * mantissa; magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte, the
+     * first of a pair in the low nibble. A tensor of this dtype is a tensor of
+     * those bytes: [batch, heads, seq, d/2], strides in bytes. */
+    ATTN_MXFP4 = 3,
+    /* OCP MX E8M0 shared scales, one byte per 32 consecutive elements of a
+     * row: the byte e stands for 2^(e - 127) (255: NaN). [batch, heads, seq,
+     * d/32], strides in bytes. */
+    ATTN_E8M0 = 4
 } attn_dtype;
 
 /* A strided 4-D view [batch, heads, sequence, d]; strides in elements. */
@@ -224,6 +233,38 @@ ATTN_API attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* 
                                        float softmax_scale, int num_splits_hi, int num_splits_lo,
                                        attn_tensor* out, float* lse, void* workspace, size_t workspace_bytes,
                                        void* stream);
+
+/*
+ * The same decode with the low-precision span held in OCP MX fp4, the page's
+ * FP4 on this hardware (the ThriftAttention page keeps most tokens in FP4 and
+ * the first and last tenth in high precision): a key or value row of d = 128
+ * elements is 64 bytes of E2M1 codes plus 4 E8M0 scale bytes, one per 32
+ * elements (OCP Microscaling Formats (MX) v1.0). The result is exact attention
+ * over the union of the bf16 keys and the fp4 keys at code * 2^(scale - 127).
+ *
+ * k_lo, v_lo  [B, Hkv, L_lo_cap, d/2] ATTN_MXFP4 (16-byte aligned data and
+ *          strides)
+ * k_lo_scale, v_lo_scale  [B, Hkv, L_lo_cap, d/32] ATTN_E8M0, the scales of
+ *          k_lo and v_lo (4-byte aligned data, strides multiples of 4 bytes)
+ * Everything else as attn_decode_mixed; the split plan is that of
+ * attn_decode_mixed_fp4_splits(). An fp4 span with 0 keys (L_lo_cap = 0)
+ * makes this the bf16 decode.
+ */
+ATTN_API attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
+                                           const int32_t* hi_lens, int L_hi_cap, const attn_tensor* k_lo,
+                                           const attn_tensor* v_lo, const attn_tensor* k_lo_scale,
+                                           const attn_tensor* v_lo_scale, const int32_t* lo_lens, int L_lo_cap,
+                                           int B, int Hq, int Hkv, int d, float softmax_scale, int num_splits_hi,
+                                           int num_splits_lo, attn_tensor* out, float* lse, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+/*
+ * Automatic split plan of attn_decode_mixed_fp4: as attn_decode_mixed_splits,
+ * with a cost per key of 2 for bf16 and 1 for fp4. Returns S_hi + S_lo, 0 on a
+ * bad argument or a failed device query.
+ */
+ATTN_API int attn_decode_mixed_fp4_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi,
+                                          int* splits_lo);
 
 /*
  * Automatic split plan of attn_decode_mixed: about two workgroups per compute

@@ -13,15 +13,16 @@ import os
 import torch
 
 __all__ = [
-    "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_FP8_E4M3", "library_path", "load_library",
+    "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_MXFP4", "ATTN_E8M0", "library_path", "load_library",
     "attn_status_string", "attn_decode_auto_splits", "attn_decode_workspace_size", "attn_decode_workspace_init",
     "attn_decode_plan",
     "attn_decode", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
-    "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi", "attn_decode_pi_splits", "attn_prefill_pi",
+    "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_mixed_fp4", "attn_decode_mixed_fp4_splits",
+    "attn_decode_pi", "attn_decode_pi_splits", "attn_prefill_pi",
     "attn_prefill_pi_workspace_size", "attn_prefill_backward", "attn_prefill_backward_workspace_size",
 ]
 
-ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3 = 0, 1, 2
+ATTN_F32, ATTN_BF16, ATTN_FP8_E4M3, ATTN_MXFP4, ATTN_E8M0 = 0, 1, 2, 3, 4
 _STATUS = {0: "ATTN_OK", 1: "ATTN_ERR_INVALID_ARG", 2: "ATTN_ERR_UNSUPPORTED", 3: "ATTN_ERR_WORKSPACE",
            4: "ATTN_ERR_HIP"}
 
@@ -79,6 +80,11 @@ def load_library():
     ip = ctypes.POINTER(ctypes.c_int)
     lib.attn_decode_mixed_splits.argtypes = [i32, i32, i32, i32, ip, ip]
     lib.attn_decode_mixed_splits.restype = i32
+    lib.attn_decode_mixed_fp4.argtypes = [tp, tp, tp, vp, i32, tp, tp, tp, tp, vp, i32, i32, i32, i32, i32, f32, i32,
+                                          i32, tp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_decode_mixed_fp4.restype = i32
+    lib.attn_decode_mixed_fp4_splits.argtypes = [i32, i32, i32, i32, ip, ip]
+    lib.attn_decode_mixed_fp4_splits.restype = i32
     lib.attn_decode_pi.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, i32, i32, tp, vp,
                                    vp, ctypes.c_size_t, vp]
     lib.attn_decode_pi.restype = i32
@@ -108,12 +114,17 @@ def _dtype_code(t):
     raise TypeError("unsupported dtype %s" % t.dtype)
 
 
-def _tensor(t):
+def _tensor(t, dtype=None):
+    """attn_tensor view of a 4-D tensor; `dtype` overrides the code taken from
+    t.dtype (uint8 tensors holding MX fp4 codes or E8M0 scales)."""
     if t.dim() != 4:
         raise ValueError("expected a 4-D [batch, heads, seq, d] tensor, got shape %s" % (tuple(t.shape),))
     if t.stride(3) != 1:
         raise ValueError("the last dimension must be contiguous")
-    return attn_tensor(t.data_ptr(), _dtype_code(t), t.stride(0), t.stride(1), t.stride(2))
+    if dtype is not None and t.dtype != torch.uint8:
+        raise TypeError("MX fp4 codes and E8M0 scales are uint8 tensors")
+    code = _dtype_code(t) if dtype is None else dtype
+    return attn_tensor(t.data_ptr(), code, t.stride(0), t.stride(1), t.stride(2))
 
 
 def _ptr(t):
@@ -306,6 +317,60 @@ def attn_decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale=None, v_scale=None, hi_
                                _ptr(k_scale), _ptr(v_scale), _ptr(lo_lens), L_lo, B, Hq, Hkv, d,
                                float(softmax_scale), int(S_hi), int(S_lo), ctypes.byref(ot), _ptr(lse), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_mixed_fp4_splits(B, Hkv, L_hi_cap, L_lo_cap):
+    """(S_hi, S_lo): the automatic split plan of attn_decode_mixed_fp4."""
+    hi, lo = ctypes.c_int(0), ctypes.c_int(0)
+    total = load_library().attn_decode_mixed_fp4_splits(B, Hkv, L_hi_cap, L_lo_cap, ctypes.byref(hi),
+                                                        ctypes.byref(lo))
+    if total <= 0:
+        raise AttnError(4, "could not plan splits")
+    return hi.value, lo.value
+
+
+def attn_decode_mixed_fp4(q, k_hi, v_hi, k_lo, v_lo, k_lo_scale=None, v_lo_scale=None, hi_lens=None, lo_lens=None,
+                          softmax_scale=0.0, num_splits_hi=0, num_splits_lo=0, out=None, lse=None, workspace=None,
+                          stream=None):
+    """Decode over a cache with a bf16 span (k_hi, v_hi [B,Hkv,L_hi,d]) and an MX fp4 span: k_lo, v_lo uint8
+    [B,Hkv,L_lo,d/2] (E2M1 codes, first of a pair in the low nibble) with k_lo_scale, v_lo_scale uint8
+    [B,Hkv,L_lo,d/32] (E8M0). hi_lens / lo_lens are int32 [B,Hkv] or None; either span may be None. Returns
+    (out [B,Hq,1,d] bf16, lse [B,Hq])."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    if Lq != 1:
+        raise ValueError("attn_decode_mixed_fp4 takes one query per sequence (q.shape[2] == 1)")
+    L_hi = 0 if k_hi is None else k_hi.shape[2]
+    L_lo = 0 if k_lo is None else k_lo.shape[2]
+    Hkv = (k_hi if k_hi is not None else k_lo).shape[1]
+    for lens in (hi_lens, lo_lens):
+        if lens is not None and (lens.dtype != torch.int32 or lens.numel() != B * Hkv or not lens.is_contiguous()):
+            raise ValueError("span lengths must be contiguous int32 with B*Hkv entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    S_hi, S_lo = num_splits_hi, num_splits_lo
+    if workspace is None:
+        if (S_hi <= 0 and L_hi) or (S_lo <= 0 and L_lo):
+            auto_hi, auto_lo = attn_decode_mixed_fp4_splits(B, Hkv, L_hi, L_lo)
+            S_hi = S_hi if S_hi > 0 else auto_hi
+            S_lo = S_lo if S_lo > 0 else auto_lo
+        used = (attn_decode_plan(L_hi, S_hi)[0] if L_hi else 0) + (attn_decode_plan(L_lo, S_lo)[0] if L_lo else 0)
+        workspace = attn_decode_workspace(B, Hq, d, used, device=q.device)
+
+    def view(t, dtype=None):
+        return None if t is None else ctypes.byref(_tensor(t, dtype))
+
+    qt, ot = _tensor(q), _tensor(out)
+    st = lib.attn_decode_mixed_fp4(ctypes.byref(qt), view(k_hi), view(v_hi), _ptr(hi_lens), L_hi,
+                                   view(k_lo, ATTN_MXFP4), view(v_lo, ATTN_MXFP4), view(k_lo_scale, ATTN_E8M0),
+                                   view(v_lo_scale, ATTN_E8M0), _ptr(lo_lens), L_lo, B, Hq, Hkv, d,
+                                   float(softmax_scale), int(max(S_hi, 0)), int(max(S_lo, 0)), ctypes.byref(ot),
+                                   _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream, q.device))
     _check(st)
     return out, lse
 

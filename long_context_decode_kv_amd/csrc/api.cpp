@@ -23,6 +23,7 @@ attn_status fail(attn_status st, const char* fmt, ...) {
 }
 
 constexpr int kChunkQuantum = 64;  // keys per workgroup step (4 waves x 16 keys)
+constexpr int kPrecBf16 = 0, kPrecFp8 = 1, kPrecFp4 = 2;  // span precisions of launch_decode_mfma_two
 constexpr float kLog2e = 1.44269504088896340736f;
 
 int elem_size(int dt) {
@@ -30,6 +31,8 @@ int elem_size(int dt) {
     case ATTN_F32: return 4;
     case ATTN_BF16: return 2;
     case ATTN_FP8_E4M3: return 1;
+    case ATTN_MXFP4: return 1;  // a byte of two codes
+    case ATTN_E8M0: return 1;
     default: return 0;
     }
 }
@@ -367,7 +370,7 @@ attn::DecodeParams two_span_params(const attn_tensor* q, int B, int Hq, int Hkv,
 
 // Workspace layout (that of attn_decode with S splits), the fused-merge
 // decision, the launch, and the separate merge when not fused.
-attn_status two_span_launch(attn::DecodeParams& p, int S, bool fp8_0, bool fp8_1, attn_tensor* out, float* lse,
+attn_status two_span_launch(attn::DecodeParams& p, int S, int prec0, int prec1, attn_tensor* out, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t hs) {
     const int B = p.B, Hq = p.Hq, Hkv = p.Hkv, d = p.d;
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
@@ -406,7 +409,7 @@ attn_status two_span_launch(attn::DecodeParams& p, int S, bool fp8_0, bool fp8_1
         p.out_sh = out->stride_h;
         p.lse = lse;
     }
-    hipError_t e = attn::launch_decode_mfma_two(p, fp8_0, fp8_1, hs);
+    hipError_t e = attn::launch_decode_mfma_two(p, prec0, prec1, hs);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     if (fused) return ATTN_OK;
 
@@ -666,7 +669,86 @@ attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, con
     p.S0 = ph.S;
     p.sp0 = span_of(k_hi, v_hi, hi_lens, Hkv, L_hi_cap, ph.chunk);
     p.sp1 = span_of(k_lo, v_lo, lo_lens, Hkv, L_lo_cap, plo.chunk);
-    return two_span_launch(p, ph.S + plo.S, false, true, out, lse, workspace, workspace_bytes,
+    return two_span_launch(p, ph.S + plo.S, kPrecBf16, kPrecFp8, out, lse, workspace, workspace_bytes,
+                           static_cast<hipStream_t>(stream));
+}
+
+int attn_decode_mixed_fp4_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi, int* splits_lo) {
+    if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0) return 0;
+    return two_span_splits(B, Hkv, L_hi_cap, 2.0, L_lo_cap, 1.0, splits_hi, splits_lo);
+}
+
+// An E8M0 scale array [B, Hkv, L, d/32] read as one 4-byte word per row.
+attn_status check_scales(const attn_tensor* t, const char* name) {
+    if (!t) return fail(ATTN_ERR_INVALID_ARG, "%s: null tensor", name);
+    if (!t->data) return fail(ATTN_ERR_INVALID_ARG, "%s: null data pointer", name);
+    if (t->dtype != ATTN_E8M0) return fail(ATTN_ERR_INVALID_ARG, "%s: dtype must be ATTN_E8M0", name);
+    if (t->stride_b < 0 || t->stride_h < 0 || t->stride_s < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: negative stride", name);
+    if ((reinterpret_cast<uintptr_t>(t->data) & 3u) || t->stride_b % 4 || t->stride_h % 4 || t->stride_s % 4)
+        return fail(ATTN_ERR_INVALID_ARG, "%s: data and strides must be multiples of 4 bytes", name);
+    return ATTN_OK;
+}
+
+attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
+                                  const int32_t* hi_lens, int L_hi_cap, const attn_tensor* k_lo,
+                                  const attn_tensor* v_lo, const attn_tensor* k_lo_scale,
+                                  const attn_tensor* v_lo_scale, const int32_t* lo_lens, int L_lo_cap, int B, int Hq,
+                                  int Hkv, int d, float softmax_scale, int num_splits_hi, int num_splits_lo,
+                                  attn_tensor* out, float* lse, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+    g_last_error[0] = 0;
+    attn_status st;
+    if ((st = check_tensor(q, "q", true)) || (st = check_tensor(out, "out", false))) return st;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d d=%d)", B, Hq, Hkv, d);
+    if (L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "span capacities must be >= 0 and not both 0 (%d, %d)", L_hi_cap,
+                    L_lo_cap);
+    if (B > 65535 || Hkv > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and Hkv must be <= 65535");
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (num_splits_hi < 0 || num_splits_lo < 0) return fail(ATTN_ERR_INVALID_ARG, "split counts must be >= 0");
+    if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (L_hi_cap) {
+        if ((st = check_tensor(k_hi, "k_hi", true)) || (st = check_tensor(v_hi, "v_hi", true))) return st;
+        if (k_hi->dtype != ATTN_BF16 || v_hi->dtype != ATTN_BF16)
+            return fail(ATTN_ERR_UNSUPPORTED, "the high-precision span must be bf16");
+    }
+    if (L_lo_cap) {
+        if ((st = check_tensor(k_lo, "k_lo", true)) || (st = check_tensor(v_lo, "v_lo", true))) return st;
+        if (k_lo->dtype != ATTN_MXFP4 || v_lo->dtype != ATTN_MXFP4)
+            return fail(ATTN_ERR_UNSUPPORTED, "the low-precision span must be ATTN_MXFP4");
+        if ((st = check_scales(k_lo_scale, "k_lo_scale")) || (st = check_scales(v_lo_scale, "v_lo_scale")))
+            return st;
+    }
+    if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode takes bf16 q and out");
+    if (d != 128 || Hq != 4 * Hkv)
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+
+    int auto_hi = 0, auto_lo = 0;
+    if ((!num_splits_hi && L_hi_cap) || (!num_splits_lo && L_lo_cap)) {
+        if (attn_decode_mixed_fp4_splits(B, Hkv, L_hi_cap, L_lo_cap, &auto_hi, &auto_lo) <= 0)
+            return fail(ATTN_ERR_HIP, "could not query the device for the split plan");
+    }
+    const Plan ph = L_hi_cap ? plan_splits(L_hi_cap, num_splits_hi ? num_splits_hi : auto_hi) : Plan{kChunkQuantum, 0};
+    const Plan plo = L_lo_cap ? plan_splits(L_lo_cap, num_splits_lo ? num_splits_lo : auto_lo) : Plan{kChunkQuantum, 0};
+
+    attn::DecodeParams p = two_span_params(q, B, Hq, Hkv, d, softmax_scale, nullptr, nullptr);
+    p.S0 = ph.S;
+    p.sp0 = span_of(k_hi, v_hi, hi_lens, Hkv, L_hi_cap, ph.chunk);
+    p.sp1 = span_of(k_lo, v_lo, lo_lens, Hkv, L_lo_cap, plo.chunk);  // strides of byte tensors: bytes
+    if (L_lo_cap) {
+        p.sp1.k_sc = k_lo_scale->data;
+        p.sp1.ksc_sb = k_lo_scale->stride_b;
+        p.sp1.ksc_sh = k_lo_scale->stride_h;
+        p.sp1.ksc_ss = k_lo_scale->stride_s;
+        p.sp1.v_sc = v_lo_scale->data;
+        p.sp1.vsc_sb = v_lo_scale->stride_b;
+        p.sp1.vsc_sh = v_lo_scale->stride_h;
+        p.sp1.vsc_ss = v_lo_scale->stride_s;
+    }
+    return two_span_launch(p, ph.S + plo.S, kPrecBf16, kPrecFp4, out, lse, workspace, workspace_bytes,
                            static_cast<hipStream_t>(stream));
 }
 
@@ -730,7 +812,8 @@ attn_status attn_decode_pi(const attn_tensor* q, const attn_tensor* k, const att
         p.sp0.prior = 1;  // ln(alpha) on the window's logits
         p.sp1.prior = 2;  // ln(1 - alpha) on the skip keys' logits
     }
-    return two_span_launch(p, pw.S + ps.S, fp8, fp8, out, lse, workspace, workspace_bytes,
+    return two_span_launch(p, pw.S + ps.S, fp8 ? kPrecFp8 : kPrecBf16, fp8 ? kPrecFp8 : kPrecBf16, out, lse,
+                           workspace, workspace_bytes,
                            static_cast<hipStream_t>(stream));
 }
 

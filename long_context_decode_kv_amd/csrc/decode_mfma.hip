@@ -64,18 +64,45 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-template <bool FP8>
+// Storage precision of a span of the cache: bf16; OCP fp8-e4m3 with one fp32
+// scale per (sequence, KV head); OCP MX fp4 (E2M1 codes, two per byte with
+// the first in the low nibble, and one E8M0 power-of-two scale per 32
+// consecutive elements of a row, in a separate array of 4 bytes per row).
+constexpr int kBf16 = 0, kFp8 = 1, kFp4 = 2;
+
+template <int P>
 struct Tile;
 template <>
-struct Tile<false> {
+struct Tile<kBf16> {
     u32x4 k[4];  // key row 4i + (lane>>4), bytes 16*(lane & 15) .. +15 (coalesced rows)
     u32x4 v[4];  // key 4*(lane>>4) + u: 8 bf16 at dims 8*(lane & 15)
 };
 template <>
-struct Tile<true> {
+struct Tile<kFp8> {
     u32x4 k[2];  // key row 8i + (lane>>3), bytes 16*(lane & 7) .. +15 (coalesced rows)
     u32x2 v[4];  // key 4*(lane>>4) + u: 8 fp8 at dims 8*(lane & 15)
 };
+template <>
+struct Tile<kFp4> {
+    u32x4 k;         // key row lane>>2, bytes 16*(lane & 3) .. +15: the 32 codes of block lane & 3
+    uint32_t ks;     // the four block scales of key row lane & 15 (byte i: block i)
+    uint32_t v[4];   // key 4*(lane>>4) + u: 8 codes at dims 8*(lane & 15)
+    uint32_t vs[4];  // the four block scales of that key
+};
+
+// Rows of an MX fp4 span's scale arrays (unused for the other precisions).
+struct ScaleRows {
+    const char* k;
+    const char* v;
+    int64_t kss, vss;  // bytes between rows
+};
+
+// E8M0 byte (low 8 bits of e) -> 2^(e - 127) as a float (255: NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    e &= 255u;
+    const uint32_t bits = e == 0u ? 0x00400000u : (e == 255u ? 0x7fc00000u : e << 23);
+    return __builtin_bit_cast(float, bits);
+}
 
 // Streaming loads: every byte of the cache is read once, so they are marked
 // non-temporal; each load instruction of a wave covers whole 128/256-byte rows.
@@ -86,50 +113,77 @@ __device__ __forceinline__ T ld_stream(const char* p) {
 
 // Loads one 16-key tile; key indices past `tlast` are clamped to it, so every
 // address stays inside the cache and the clamped keys are masked later.
-template <bool FP8>
-__device__ __forceinline__ void load_tile(Tile<FP8>& t, const char* kbase, const char* vbase, int64_t kss,
-                                          int64_t vss, int tok0, int tlast, int lane) {
-    if constexpr (!FP8) {
+template <int P>
+__device__ __forceinline__ void load_tile(Tile<P>& t, const char* kbase, const char* vbase, int64_t kss,
+                                          int64_t vss, const ScaleRows& sc, int tok0, int tlast, int lane) {
+    if constexpr (P == kFp4) {
+        t.k = ld_stream<u32x4>(kbase + (int64_t)min(tok0 + (lane >> 2), tlast) * kss + 16 * (lane & 3));
+        t.ks = ld_stream<uint32_t>(sc.k + (int64_t)min(tok0 + (lane & 15), tlast) * sc.kss);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rk = min(tok0 + 4 * i + (lane >> 4), tlast);
-            t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 15));
+        for (int u = 0; u < 4; ++u) {
+            const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
+            t.v[u] = ld_stream<uint32_t>(vbase + (int64_t)rv * vss + 4 * (lane & 15));
+            t.vs[u] = ld_stream<uint32_t>(sc.v + (int64_t)rv * sc.vss);
         }
     } else {
+        if constexpr (P == kBf16) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int rk = min(tok0 + 8 * i + (lane >> 3), tlast);
-            t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 7));
+            for (int i = 0; i < 4; ++i) {
+                const int rk = min(tok0 + 4 * i + (lane >> 4), tlast);
+                t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 15));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int rk = min(tok0 + 8 * i + (lane >> 3), tlast);
+                t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 7));
+            }
         }
-    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
-        const char* vrow = vbase + (int64_t)rv * vss;
-        if constexpr (!FP8) t.v[u] = ld_stream<u32x4>(vrow + 2 * 8 * (lane & 15));
-        else t.v[u] = ld_stream<u32x2>(vrow + 8 * (lane & 15));
+        for (int u = 0; u < 4; ++u) {
+            const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
+            const char* vrow = vbase + (int64_t)rv * vss;
+            if constexpr (P == kBf16) t.v[u] = ld_stream<u32x4>(vrow + 2 * 8 * (lane & 15));
+            else t.v[u] = ld_stream<u32x2>(vrow + 8 * (lane & 15));
+        }
     }
 }
 
 // The K tile passes through a wave-private LDS stage to change from row-major
 // lanes to the MFMA operand layout (lane = key row, 16 bytes of dims). 16-byte
 // chunks are XOR-swizzled by row so both the row writes and the column reads
-// touch every bank once per 16 lanes.
-template <bool FP8>
+// touch every bank once per 16 lanes. (fp4: four 16-byte chunks per row, chunk
+// c of row r at c ^ (r >> 2); the operand reads are 4-byte words, word g of
+// chunk i for row r, which then cover all 64 banks.)
+template <int P>
 __device__ __forceinline__ int kstage_index(int row, int chunk) {
-    if constexpr (!FP8) return row * 16 + (chunk ^ (row & 15));
-    else return row * 8 + (chunk ^ ((row >> 1) & 7));
+    if constexpr (P == kBf16) return row * 16 + (chunk ^ (row & 15));
+    else if constexpr (P == kFp8) return row * 8 + (chunk ^ ((row >> 1) & 7));
+    else return row * 4 + (chunk ^ (row >> 2));
 }
 
-template <bool FP8>
-__device__ __forceinline__ void stage_k(const Tile<FP8>& t, u32x4* ks, int lane) {
-    if constexpr (!FP8) {
+template <int P>
+__device__ __forceinline__ void stage_k(const Tile<P>& t, u32x4* ks, int lane) {
+    if constexpr (P == kBf16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ks[kstage_index<false>(4 * i + (lane >> 4), lane & 15)] = t.k[i];
+        for (int i = 0; i < 4; ++i) ks[kstage_index<kBf16>(4 * i + (lane >> 4), lane & 15)] = t.k[i];
+    } else if constexpr (P == kFp8) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ks[kstage_index<kFp8>(8 * i + (lane >> 3), lane & 7)] = t.k[i];
     } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) ks[kstage_index<true>(8 * i + (lane >> 3), lane & 7)] = t.k[i];
+        ks[kstage_index<kFp4>(lane >> 2, lane & 3)] = t.k;
     }
+}
+
+// Eight MX fp4 codes (a dword, first code in the low nibble) times 2^scale ->
+// eight floats (exact).
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t w, float sc, float (&f)[8]) {
+    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+    const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
+    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
 }
 
 // Four OCP e4m3 codes of a dword pair -> eight bf16 (exact widening).
@@ -141,9 +195,12 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <bool FP8>
-__device__ __forceinline__ void v_to_f32(const Tile<FP8>& t, int u, float (&vf)[8]) {
-    if constexpr (!FP8) {
+template <int P>
+__device__ __forceinline__ void v_to_f32(const Tile<P>& t, int u, int lane, float (&vf)[8]) {
+    if constexpr (P == kFp4) {
+        // dims 8*(lane & 15) .. +7 lie in block (lane & 15) >> 2
+        fp4x8_to_f32(t.v[u], e8m0_to_f32(t.vs[u] >> (8 * ((lane & 15) >> 2))), vf);
+    } else if constexpr (P == kBf16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             vf[2 * e] = bf16_lo(t.v[u][e]);
@@ -162,14 +219,27 @@ __device__ __forceinline__ void v_to_f32(const Tile<FP8>& t, int u, float (&vf)[
     }
 }
 
-template <bool FP8>
-__device__ __forceinline__ void compute_tile(const Tile<FP8>& t, u32x4* ks, const bf16x8 (&qop)[4], float scale2,
+template <int P>
+__device__ __forceinline__ void compute_tile(const Tile<P>& t, u32x4* ks, const bf16x8 (&qop)[4], float scale2,
                                              int tok0, int tend, int lane, float& m_run, float& l_run,
                                              float (&o)[4][8]) {
-    stage_k<FP8>(t, ks, lane);
+    stage_k<P>(t, ks, lane);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int row = lane & 15;
-    if constexpr (!FP8) {
+    if constexpr (P == kFp4) {
+        // MFMA step i is block i (dims 32i .. 32i + 31): this lane's eight
+        // codes, dims 32i + 8*(lane >> 4) .., widened with the block's scale
+        const uint32_t* ks32 = reinterpret_cast<const uint32_t*>(ks);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float f[8];
+            fp4x8_to_f32(ks32[4 * kstage_index<kFp4>(row, i) + (lane >> 4)], e8m0_to_f32(t.ks >> (8 * i)), f);
+            bf16x8 a;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[e] = (__bf16)f[e];  // exact: two significant bits
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], acc, 0, 0, 0);
+        }
+    } else if constexpr (P == kBf16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const u32x4 a = ks[kstage_index<false>(row, 4 * i + (lane >> 4))];
@@ -212,7 +282,7 @@ __device__ __forceinline__ void compute_tile(const Tile<FP8>& t, u32x4* ks, cons
     for (int u = 0; u < 4; ++u) {
         const float pb[4] = {quad_bcast<0>(p[u]), quad_bcast<1>(p[u]), quad_bcast<2>(p[u]), quad_bcast<3>(p[u])};
         float vf[8];
-        v_to_f32<FP8>(t, u, vf);
+        v_to_f32<P>(t, u, lane, vf);
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
@@ -389,9 +459,10 @@ struct DecodeLds {
 // TWO (two-span launches): the span's key geometry and log-prior apply; every
 // split of the launch publishes a partial (an empty one the identity) and
 // takes part in the fused merge, which covers all p.S of them.
-template <bool FP8, bool FUSED, bool TWO>
+template <int P, bool FUSED, bool TWO>
 __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& sp, int s, int s_out,
                                           DecodeLds& lds) {
+    constexpr bool FP8 = P == kFp8;
     const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     int L_b = sp.L_cap;
@@ -445,10 +516,17 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
     }
     const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
 
-    constexpr int esz = FP8 ? 1 : 2;
+    constexpr int esz = P == kBf16 ? 2 : 1;  // bytes per stride unit (fp4 spans carry byte strides)
     const char* kbase = static_cast<const char*>(sp.k) + (b * sp.k_sb + g * sp.k_sh + row0 * sp.k_ss) * esz;
     const char* vbase = static_cast<const char*>(sp.v) + (b * sp.v_sb + g * sp.v_sh + row0 * sp.v_ss) * esz;
     const int64_t kss = sp.k_ss * esz * rmul, vss = sp.v_ss * esz * rmul;
+    ScaleRows sc{nullptr, nullptr, 0, 0};
+    if constexpr (P == kFp4) {
+        sc.k = static_cast<const char*>(sp.k_sc) + b * sp.ksc_sb + g * sp.ksc_sh + row0 * sp.ksc_ss;
+        sc.v = static_cast<const char*>(sp.v_sc) + b * sp.vsc_sb + g * sp.vsc_sh + row0 * sp.vsc_ss;
+        sc.kss = sp.ksc_ss * rmul;
+        sc.vss = sp.vsc_ss * rmul;
+    }
 
     // Q^T operand: column (lane & 15) is query head 4g + (lane & 3); its k-slots
     // follow the same dim order as the K operand.
@@ -478,17 +556,17 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
     u32x4* ks = lds.kstage[w];
     int k = w;
     if (k < ntiles) {
-        Tile<FP8> ta, tb;
-        load_tile<FP8>(ta, kbase, vbase, kss, vss, t_begin + kTile * k, t_end - 1, lane);
+        Tile<P> ta, tb;
+        load_tile<P>(ta, kbase, vbase, kss, vss, sc, t_begin + kTile * k, t_end - 1, lane);
         while (true) {
             const bool more_b = k + kWaves < ntiles;
-            if (more_b) load_tile<FP8>(tb, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-            compute_tile<FP8>(ta, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+            if (more_b) load_tile<P>(tb, kbase, vbase, kss, vss, sc, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+            compute_tile<P>(ta, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
             if (!more_b) break;
             k += kWaves;
             const bool more_a = k + kWaves < ntiles;
-            if (more_a) load_tile<FP8>(ta, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-            compute_tile<FP8>(tb, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+            if (more_a) load_tile<P>(ta, kbase, vbase, kss, vss, sc, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+            compute_tile<P>(tb, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
             if (!more_a) break;
             k += kWaves;
         }
@@ -579,18 +657,18 @@ __device__ __forceinline__ KvSpan main_span(const DecodeParams& p) {
 template <bool FP8, bool FUSED>
 __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
     __shared__ DecodeLds lds;
-    decode_wg<FP8, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
+    decode_wg<FP8 ? kFp8 : kBf16, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
 }
 
 // Two spans in one launch (a two-precision cache, or pi-Attention's window
 // and skip keys): splits [0, S0) stream span sp0, the others span sp1; one
 // merge over all splits.
-template <bool FP8_0, bool FP8_1, bool FUSED>
+template <int P0, int P1, bool FUSED>
 __global__ __launch_bounds__(256) void decode_gqa4_d128_two(DecodeParams p) {
     __shared__ DecodeLds lds;  // one copy for both branches
     const int s = blockIdx.x;
-    if (s < p.S0) decode_wg<FP8_0, FUSED, true>(p, p.sp0, s, s, lds);
-    else decode_wg<FP8_1, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
+    if (s < p.S0) decode_wg<P0, FUSED, true>(p, p.sp0, s, s, lds);
+    else decode_wg<P1, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
 }
 
 }  // namespace
@@ -608,22 +686,21 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma_two(const DecodeParams& p, bool fp8_0, bool fp8_1, hipStream_t stream) {
+hipError_t launch_decode_mfma_two(const DecodeParams& p, int prec0, int prec1, hipStream_t stream) {
     dim3 grid(p.S, p.Hkv, p.B);
     const bool f = p.counters != nullptr;
-    if (!fp8_0 && fp8_1) {
-        if (f) hipLaunchKernelGGL((decode_gqa4_d128_two<false, true, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((decode_gqa4_d128_two<false, true, false>), grid, dim3(256), 0, stream, p);
-    } else if (!fp8_0 && !fp8_1) {
-        if (f) hipLaunchKernelGGL((decode_gqa4_d128_two<false, false, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((decode_gqa4_d128_two<false, false, false>), grid, dim3(256), 0, stream, p);
-    } else if (fp8_0 && fp8_1) {
-        if (f) hipLaunchKernelGGL((decode_gqa4_d128_two<true, true, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((decode_gqa4_d128_two<true, true, false>), grid, dim3(256), 0, stream, p);
-    } else {
-        return hipErrorInvalidValue;  // no fp8-then-bf16 variant
+#define ATTN_TWO(P0, P1)                                                                                  \
+    if (prec0 == P0 && prec1 == P1) {                                                                     \
+        if (f) hipLaunchKernelGGL((decode_gqa4_d128_two<P0, P1, true>), grid, dim3(256), 0, stream, p);  \
+        else hipLaunchKernelGGL((decode_gqa4_d128_two<P0, P1, false>), grid, dim3(256), 0, stream, p);   \
+        return hipGetLastError();                                                                         \
     }
-    return hipGetLastError();
+    ATTN_TWO(kBf16, kFp8)
+    ATTN_TWO(kBf16, kBf16)
+    ATTN_TWO(kFp8, kFp8)
+    ATTN_TWO(kBf16, kFp4)
+#undef ATTN_TWO
+    return hipErrorInvalidValue;  // no kernel for this pair of precisions
 }
 
 }  // namespace attn

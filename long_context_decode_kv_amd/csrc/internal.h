@@ -31,6 +31,12 @@ struct KvSpan {
     int chunk;
     int geom, window, period;
     int prior;
+    // MX fp4 spans only (k and its strides above are then in bytes): the E8M0
+    // block scales, 4 bytes per row (d = 128), strides in bytes
+    const void* k_sc;
+    int64_t ksc_sb, ksc_sh, ksc_ss;
+    const void* v_sc;
+    int64_t vsc_sb, vsc_sh, vsc_ss;
 };
 
 // One split-KV decode launch: grid (S, Hkv, B); workgroup (s, g, b) owns keys
@@ -131,7 +137,8 @@ struct PrefillParams {
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream);
 // Two-span decode: fp8_0 / fp8_1 give the KV dtype of sp0 / sp1 (bf16 or fp8).
-hipError_t launch_decode_mfma_two(const DecodeParams& p, bool fp8_0, bool fp8_1, hipStream_t stream);
+// Span precisions: 0 bf16, 1 fp8-e4m3, 2 MX fp4.
+hipError_t launch_decode_mfma_two(const DecodeParams& p, int prec0, int prec1, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int q_dtype, int kv_dtype, int G, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // Zeroes `bytes` (a multiple of 16) at 16-byte aligned device address `p`.

@@ -82,9 +82,21 @@ def mixed_on_gpu(inp, num_splits_hi=0, num_splits_lo=0, dev=None, softmax_scale=
     return out, lse
 
 
+def mixed_fp4_on_gpu(inp, num_splits_hi=0, num_splits_lo=0, dev=None):
+    import long_context_decode_kv_amd as lib
+    dev = dev or {k: to_dev(v) for k, v in inp.items() if k != "lo_format"}
+    out, lse = lib.attn_decode_mixed_fp4(dev["q"], dev["k_hi"], dev["v_hi"], dev["k_lo"], dev["v_lo"],
+                                         k_lo_scale=dev["k_scale"], v_lo_scale=dev["v_scale"], hi_lens=dev["hi_lens"],
+                                         lo_lens=dev["lo_lens"], num_splits_hi=num_splits_hi,
+                                         num_splits_lo=num_splits_lo)
+    torch.cuda.synchronize()
+    return out, lse
+
+
 def oracle_mixed(inp, heads=None, scale=None):
     out, lse = oracle.decode_mixed(inp["q"], inp["k_hi"], inp["v_hi"], inp["k_lo"], inp["v_lo"], inp["k_scale"],
-                                   inp["v_scale"], inp["hi_lens"], inp["lo_lens"], scale=scale, heads=heads)
+                                   inp["v_scale"], inp["hi_lens"], inp["lo_lens"], scale=scale, heads=heads,
+                                   lo_format=inp.get("lo_format", "e4m3"))
     if heads is not None:
         return out, lse
     B, Hq = inp["q"].shape[:2]

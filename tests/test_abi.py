@@ -34,7 +34,8 @@ def test_every_declared_symbol_is_exported(so):
     assert set(names) == {"attn_status_string", "attn_last_error", "attn_decode_auto_splits",
                           "attn_decode_workspace_size", "attn_decode_workspace_init", "attn_decode_plan",
                           "attn_decode", "attn_decode_partials", "attn_prefill", "attn_combine_partials",
-                          "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_pi",
+                          "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_mixed_fp4",
+                          "attn_decode_mixed_fp4_splits", "attn_decode_pi",
                           "attn_decode_pi_splits", "attn_prefill_pi", "attn_prefill_pi_workspace_size",
                           "attn_prefill_backward", "attn_prefill_backward_workspace_size"}
     nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
@@ -175,6 +176,45 @@ def test_mixed_decode_argument_errors(so):
     # an empty span may come without tensors
     assert mixed(so, L_hi=0, S_hi=0, no_hi=True, ws=None) == WORKSPACE  # validation reaches the workspace check
     assert mixed(so, L_hi=16, no_hi=True) == INVALID
+
+
+MXFP4, E8M0 = 3, 4
+
+
+_DEFAULT = object()
+
+
+def mixed_fp4(so, klo=_DEFAULT, ksc=_DEFAULT, vsc=_DEFAULT, B=1, Hq=8, Hkv=2, d=128, L_hi=256, L_lo=1024, S_hi=2,
+              S_lo=4, out=None, ws=FAKE, ws_bytes=1 << 30, no_lo=False):
+    q = T(BF16, Hq * d, d, d)
+    khi = T(BF16, Hkv * L_hi * d, L_hi * d, d)
+    pick = lambda x, dflt: None if no_lo else (dflt if x is _DEFAULT else x)
+    klo = pick(klo, T(MXFP4, Hkv * L_lo * d // 2, L_lo * d // 2, d // 2))
+    ksc = pick(ksc, T(E8M0, Hkv * L_lo * 4, L_lo * 4, 4))
+    vsc = pick(vsc, T(E8M0, Hkv * L_lo * 4, L_lo * 4, 4))
+    out = out or T(BF16, Hq * d, d, d)
+    ref = lambda t: None if t is None else ctypes.byref(t)
+    return so.attn_decode_mixed_fp4(ctypes.byref(q), ref(khi), ref(khi), None, L_hi, ref(klo), ref(klo), ref(ksc),
+                                    ref(vsc), None, L_lo, B, Hq, Hkv, d, 0.0, S_hi, S_lo, ctypes.byref(out), None, ws,
+                                    ws_bytes, None)
+
+
+def test_mixed_fp4_decode_argument_errors(so):
+    assert mixed_fp4(so, L_hi=0, L_lo=0) == INVALID
+    assert mixed_fp4(so, S_lo=-1) == INVALID
+    assert mixed_fp4(so, ksc=None) == INVALID  # the fp4 span needs its scales
+    assert mixed_fp4(so, ksc=T(FP8, 2 * 1024 * 4, 1024 * 4, 4)) == INVALID  # scales of the wrong dtype
+    assert mixed_fp4(so, vsc=T(E8M0, 2 * 1024 * 4, 1024 * 4, 6)) == INVALID  # row stride not a multiple of 4
+    assert mixed_fp4(so, ksc=T(E8M0, 0, 0, 4, data=FAKE + 2)) == INVALID  # misaligned scales
+    assert mixed_fp4(so, klo=T(FP8, 2 * 1024 * 128, 1024 * 128, 128)) == UNSUPPORTED  # fp4 span holds fp8
+    assert mixed_fp4(so, klo=T(MXFP4, 0, 0, 72)) == INVALID  # code rows must be 16-byte multiples
+    assert mixed_fp4(so, d=64) == UNSUPPORTED
+    assert mixed_fp4(so, Hq=16, Hkv=2) == UNSUPPORTED
+    assert mixed_fp4(so, ws=None) == WORKSPACE
+    assert mixed_fp4(so, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 6) - 1) == WORKSPACE
+    assert "6 splits" in lib.load_library().attn_last_error().decode()
+    assert mixed_fp4(so, L_lo=0, S_lo=0, no_lo=True, ws=None) == WORKSPACE  # no fp4 span: bf16 only
+    assert mixed_fp4(so, L_lo=16, no_lo=True) == INVALID
 
 
 def pi(so, kv=BF16, ks=None, vs=None, B=1, Hq=8, Hkv=2, d=128, L=4096, window=512, period=16, Sw=2, Ss=2, out=None,
