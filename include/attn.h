@@ -260,8 +260,9 @@ ATTN_API attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tens
 
 /*
  * Automatic split plan of attn_decode_mixed_fp4: as attn_decode_mixed_splits,
- * with a cost per key of 2 for bf16 and 1 for fp4. Returns S_hi + S_lo, 0 on a
- * bad argument or a failed device query.
+ * with a cost per key of 2 for bf16 and 1.8 for fp4 (the fp4 span is bound by
+ * widening and P.V work, not by its bytes). Returns S_hi + S_lo, 0 on a bad
+ * argument or a failed device query.
  */
 ATTN_API int attn_decode_mixed_fp4_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi,
                                           int* splits_lo);

@@ -675,7 +675,10 @@ attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, con
 
 int attn_decode_mixed_fp4_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi, int* splits_lo) {
     if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0) return 0;
-    return two_span_splits(B, Hkv, L_hi_cap, 2.0, L_lo_cap, 1.0, splits_hi, splits_lo);
+    // cost per key: the fp4 span is bound by its vector work (widening and
+    // P.V per key), not by its bytes, so a key costs nearly what a bf16 key
+    // does (128K-key sweep: 12-16 + 48-52 splits fastest)
+    return two_span_splits(B, Hkv, L_hi_cap, 2.0, L_lo_cap, 1.8, splits_hi, splits_lo);
 }
 
 // An E8M0 scale array [B, Hkv, L, d/32] read as one 4-byte word per row.
@@ -720,6 +723,11 @@ attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tensor* k_hi,
             return fail(ATTN_ERR_UNSUPPORTED, "the low-precision span must be ATTN_MXFP4");
         if ((st = check_scales(k_lo_scale, "k_lo_scale")) || (st = check_scales(v_lo_scale, "v_lo_scale")))
             return st;
+        // the kernel steps through a 16-row tile with 32-bit offsets
+        const int64_t lim = int64_t(1) << 26;
+        if (k_lo->stride_s >= lim || v_lo->stride_s >= lim || k_lo_scale->stride_s >= lim ||
+            v_lo_scale->stride_s >= lim)
+            return fail(ATTN_ERR_INVALID_ARG, "fp4 span row strides must be below 64 MiB");
     }
     if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
         return fail(ATTN_ERR_UNSUPPORTED, "mixed decode takes bf16 q and out");

@@ -117,13 +117,21 @@ template <int P>
 __device__ __forceinline__ void load_tile(Tile<P>& t, const char* kbase, const char* vbase, int64_t kss,
                                           int64_t vss, const ScaleRows& sc, int tok0, int tlast, int lane) {
     if constexpr (P == kFp4) {
-        t.k = ld_stream<u32x4>(kbase + (int64_t)min(tok0 + (lane >> 2), tlast) * kss + 16 * (lane & 3));
-        t.ks = ld_stream<uint32_t>(sc.k + (int64_t)min(tok0 + (lane & 15), tlast) * sc.kss);
+        // the tile's first row in wide arithmetic (uniform), the lanes' rows
+        // as 32-bit offsets from it (a span's row strides are far below 2^27)
+        const int last = tlast - tok0;
+        const char* kt = kbase + (int64_t)tok0 * kss;
+        const char* vt = vbase + (int64_t)tok0 * vss;
+        const char* kst = sc.k + (int64_t)tok0 * sc.kss;
+        const char* vst = sc.v + (int64_t)tok0 * sc.vss;
+        const int ik = (int)kss, iv = (int)vss, iks = (int)sc.kss, ivs = (int)sc.vss;
+        t.k = ld_stream<u32x4>(kt + min(lane >> 2, last) * ik + 16 * (lane & 3));
+        t.ks = ld_stream<uint32_t>(kst + min(lane & 15, last) * iks);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
-            t.v[u] = ld_stream<uint32_t>(vbase + (int64_t)rv * vss + 4 * (lane & 15));
-            t.vs[u] = ld_stream<uint32_t>(sc.v + (int64_t)rv * sc.vss);
+            const int rv = min(4 * (lane >> 4) + u, last);
+            t.v[u] = ld_stream<uint32_t>(vt + rv * iv + 4 * (lane & 15));
+            t.vs[u] = ld_stream<uint32_t>(vst + rv * ivs);
         }
     } else {
         if constexpr (P == kBf16) {
@@ -464,7 +472,8 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
                                           DecodeLds& lds) {
     constexpr bool FP8 = P == kFp8;
     const int g = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile rows and bases in scalar registers
     int L_b = sp.L_cap;
     if (sp.kv_lens) L_b = min(max(sp.kv_lens[b * sp.lens_sb + g * sp.lens_sh], 0), sp.L_cap);
     // keys visited: rows row0 + t * rmul for t in [0, n_keys)
@@ -551,11 +560,27 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
 
-    // Two tile buffers used in turn: the next tile is in flight while the
-    // current one is computed.
+    // Tile buffers used in turn: the next tile is in flight while the current
+    // one is computed -- the next two for MX fp4, whose 16-key tiles hold a
+    // quarter of a bf16 tile's bytes.
     u32x4* ks = lds.kstage[w];
     int k = w;
-    if (k < ntiles) {
+    if (P == kFp4 && k < ntiles) {
+        Tile<P> ta, tb, tc;
+        load_tile<P>(ta, kbase, vbase, kss, vss, sc, t_begin + kTile * k, t_end - 1, lane);
+        if (k + kWaves < ntiles)
+            load_tile<P>(tb, kbase, vbase, kss, vss, sc, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+        // ahead <- tile k + 2 kWaves; compute cur (tile k); false when done
+        auto step = [&](Tile<P>& cur, Tile<P>& ahead) __attribute__((always_inline)) {
+            if (k + 2 * kWaves < ntiles)
+                load_tile<P>(ahead, kbase, vbase, kss, vss, sc, t_begin + kTile * (k + 2 * kWaves), t_end - 1, lane);
+            compute_tile<P>(cur, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+            k += kWaves;
+            return k < ntiles;
+        };
+        while (step(ta, tc) && step(tb, ta) && step(tc, tb)) {
+        }
+    } else if (k < ntiles) {
         Tile<P> ta, tb;
         load_tile<P>(ta, kbase, vbase, kss, vss, sc, t_begin + kTile * k, t_end - 1, lane);
         while (true) {

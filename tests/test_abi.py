@@ -208,6 +208,7 @@ def test_mixed_fp4_decode_argument_errors(so):
     assert mixed_fp4(so, ksc=T(E8M0, 0, 0, 4, data=FAKE + 2)) == INVALID  # misaligned scales
     assert mixed_fp4(so, klo=T(FP8, 2 * 1024 * 128, 1024 * 128, 128)) == UNSUPPORTED  # fp4 span holds fp8
     assert mixed_fp4(so, klo=T(MXFP4, 0, 0, 72)) == INVALID  # code rows must be 16-byte multiples
+    assert mixed_fp4(so, klo=T(MXFP4, 0, 0, 1 << 26)) == INVALID  # row stride too large for the tile offsets
     assert mixed_fp4(so, d=64) == UNSUPPORTED
     assert mixed_fp4(so, Hq=16, Hkv=2) == UNSUPPORTED
     assert mixed_fp4(so, ws=None) == WORKSPACE
