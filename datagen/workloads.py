@@ -1,4 +1,4 @@
-"""The five synthetic workloads: shapes and input recipes (no arithmetic of the
+"""The nine synthetic workloads: shapes and input recipes (no arithmetic of the
 method). Shapes follow Llama-3.1-8B's attention (32 query heads, 8 KV heads,
 head dim 128), the model the Tree Attention explainer evaluates on (section 4);
 no weights, prompts or datasets are involved -- every tensor is drawn from the
@@ -6,7 +6,8 @@ seeded generator.
 
 Recipe: seed = workload number; tensor ids Q=0, K=1, V=2, lengths=3. Values are
 N(0,1) * mul rounded to the storage format; fp8 tensors get one amax/448 scale
-per (batch, KV head).
+per (batch, KV head); MX fp4 tensors get one power-of-two (e8m0) scale per 32
+consecutive elements of a row, chosen from the block's largest magnitude.
 """
 import numpy as np
 

@@ -66,7 +66,7 @@ extern "C" {
 typedef enum attn_status {
     ATTN_OK = 0,
     ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, inconsistent shapes */
-    ATTN_ERR_UNSUPPORTED = 2, /* valid request this build has no kernel for */
+    ATTN_ERR_UNSUPPORTED = 2, /* valid request the library has no kernel for */
     ATTN_ERR_WORKSPACE = 3,   /* workspace missing or too small */
     ATTN_ERR_HIP = 4          /* the HIP runtime reported an error */
 } attn_status;
