@@ -238,13 +238,15 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
 
     // ---- M phase: P.V of tile j, then the scores of tile j+1. Each product is
     // 16 MFMAs whose operands are read from LDS four (V^T: transposed reads,
-    // two per operand) or six (K) MFMAs ahead.
+    // two per operand) or six (K) MFMAs ahead. Consecutive MFMAs accumulate
+    // into different tiles (the four dim blocks of O, the two key blocks of
+    // S); each tile still sums its steps in the same order.
     constexpr int kAhead = 6;
     auto pv_block = [&](uint32_t slot) __attribute__((always_inline)) {
-        // operand i: key block kb = i >> 3, dim block (i >> 1) & 3, half i & 1:
+        // operand i: key block kb = i >> 3, dim block i & 3, half (i >> 2) & 1:
         // keys 32kb + 16half + 8hb + (0..7), dim 32dblk + (lane & 31)
         auto rd = [&](int i) __attribute__((always_inline)) {
-            const int kb = i >> 3, dblk = (i >> 1) & 3, half = i & 1;
+            const int kb = i >> 3, dblk = i & 3, half = (i >> 2) & 1;
             const uint32_t a0 = slot + vofs[dblk] + (32 * kb + 16 * half) * kRowBytes;
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)((lds_char*)lds + a0));
             const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -260,16 +262,16 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         for (int i = 0; i < 16; ++i) {
             const bf16x8 a = opnd[i % kA];
             if (i + kA < 16) opnd[i % kA] = rd(i + kA);
-            const int kb = i >> 3, dblk = (i >> 1) & 3, half = i & 1;
+            const int kb = i >> 3, dblk = i & 3, half = (i >> 2) & 1;
             oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pk[kb][half]),
                                                                  oacc[dblk], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
     auto qk_block = [&](uint32_t slot) __attribute__((always_inline)) {
-        // operand i: key block i >> 3, d-step i & 7
+        // operand i: key block i & 1, d-step i >> 1
         auto rd = [&](int i) __attribute__((always_inline)) {
-            return *reinterpret_cast<const bf16x8*>(lds + slot + kofs[i & 7] + 32 * (i >> 3) * kRowBytes);
+            return *reinterpret_cast<const bf16x8*>(lds + slot + kofs[i >> 1] + 32 * (i & 1) * kRowBytes);
         };
         bf16x8 opnd[kAhead];
 #pragma unroll
@@ -279,7 +281,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         for (int i = 0; i < 16; ++i) {
             const bf16x8 a = opnd[i % kAhead];
             if (i + kAhead < 16) opnd[i % kAhead] = rd(i + kAhead);
-            const int kb = i >> 3, ks = i & 7;
+            const int kb = i & 1, ks = i >> 1;
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], ks ? sacc[kb] : (f32x16){}, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         }
