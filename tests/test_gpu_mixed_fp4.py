@@ -4,7 +4,8 @@ FP4 on this hardware) against the oracle's attention over the union of both
 spans at their decoded values: small shapes with several tiles and ragged
 tails, per-head ragged lengths with empty spans, both merge paths, every E2M1
 code and a wide range of E8M0 scales, either span absent, strided views, the
-full 128K-token workload, and bit-identical repeats."""
+full 128K-token workload (also with per-head ragged lengths), and
+bit-identical repeats."""
 import numpy as np
 import pytest
 import torch
@@ -121,3 +122,10 @@ def test_workload9_full_size_auto_plan_and_repeats():
     print("wl9 auto %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (lib.attn_decode_mixed_fp4_splits(1, 8, 26214 * 1, 104858), *res), flush=True)
     out2, _ = mixed_fp4_on_gpu(inp, 64, 128, dev=dev)
     assert_close(from_dev(out2).reshape(B * Hq, -1), ref, "bf16", what="wl9 64+128")
+
+
+def test_workload9_full_size_ragged_heads():
+    # each (sequence, KV head) keeps between half and all of each span's capacity
+    inp = make_mixed_inputs(9, lens=(0.5, 1.0))
+    assert inp["hi_lens"].min() < inp["hi_lens"].max() and inp["lo_lens"].min() < inp["lo_lens"].max()
+    _check(inp, 0, 0, what="wl9 ragged")
