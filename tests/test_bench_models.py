@@ -28,6 +28,13 @@ def test_mixed_bytes():
         2 * 8 * 26214 * 128 * 2 + 2 * 8 * 104858 * 128 + 2 * 4 * 8 + 2 * 32 * 128 * 2
 
 
+def test_mixed_fp4_bytes():
+    # per key and KV head: bf16 K + V rows (2 x 256 B); fp4 K + V codes (2 x 64 B) and e8m0 scales (2 x 4 B)
+    per_bf16, per_fp4 = 2 * 128 * 2, 2 * (128 // 2 + 128 // 32)
+    assert bench.mixed_fp4_algorithmic_bytes(1, 32, 8, 128, 26214, 104858) == \
+        8 * (26214 * per_bf16 + 104858 * per_fp4) + 2 * 32 * 128 * 2 == 221474432
+
+
 def test_pi_counts_by_enumeration():
     for L, w, per in ((300, 37, 11), (129, 0, 1), (200, 250, 7), (64, 5, 0), (1000, 64, 64)):
         pairs = 0
