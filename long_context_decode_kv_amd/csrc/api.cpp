@@ -204,7 +204,10 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     const bool fp8 = k->dtype == ATTN_FP8_E4M3;
     if (q->dtype == ATTN_F32 && k->dtype != ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "fp32 q needs fp32 k/v");
     if (q->dtype == ATTN_BF16 && k->dtype == ATTN_F32) return fail(ATTN_ERR_UNSUPPORTED, "bf16 q with fp32 k/v");
-    if (q->dtype == ATTN_FP8_E4M3) return fail(ATTN_ERR_UNSUPPORTED, "q must be fp32 or bf16");
+    if (q->dtype != ATTN_F32 && q->dtype != ATTN_BF16) return fail(ATTN_ERR_UNSUPPORTED, "q must be fp32 or bf16");
+    // MX fp4 codes and E8M0 scales have their own entry point (attn_decode_mixed_fp4)
+    if (k->dtype != ATTN_F32 && k->dtype != ATTN_BF16 && !fp8)
+        return fail(ATTN_ERR_UNSUPPORTED, "k/v must be fp32, bf16 or fp8 e4m3 (dtype %d)", k->dtype);
     if (fp8 && (!k_scale || !v_scale)) return fail(ATTN_ERR_INVALID_ARG, "fp8 k/v need k_scale and v_scale");
     if (!fp8 && (k_scale || v_scale)) return fail(ATTN_ERR_INVALID_ARG, "scales are only for fp8 k/v");
     if (d != 64 && d != 128) return fail(ATTN_ERR_UNSUPPORTED, "head dim %d (supported: 64, 128)", d);

@@ -13,7 +13,7 @@ from long_context_decode_kv_amd import attn_tensor
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, MXFP4, E8M0 = 0, 1, 2, 3, 4
 
 
 @pytest.fixture(scope="module")
@@ -67,7 +67,7 @@ def test_split_plan(so):
 
 
 def test_workspace_size(so):
-    # a fixed 64 KiB block of merge counters, then the fp32 partials
+    # a fixed 4 MiB block of merge counters, then the fp32 partials
     assert lib.attn_decode_workspace_size(1, 32, 128, 256) == (4 << 20) + 32 * 256 * 130 * 4 + 32 * 16 * 130 * 4
     assert lib.attn_decode_workspace_size(16, 32, 128, 0) == 0
     assert lib.attn_decode_workspace_size(0, 32, 128, 4) == 0
@@ -108,6 +108,30 @@ def test_decode_argument_errors(so):
     assert decode(so, ws_bytes=(4 << 20) + 8 * 16 * 130 * 4 + 100) == WORKSPACE
     assert decode(so, ws=FAKE + 4) == WORKSPACE
     assert decode(so, out=T(F32, 1024, 128, 128)) == INVALID  # out dtype must equal q dtype
+    # MX fp4 codes and E8M0 scales are not decode inputs: rejected before any launch
+    fp4 = T(MXFP4, 2 * 1024 * 64, 1024 * 64, 64)
+    assert decode(so, k=fp4, v=fp4) == UNSUPPORTED
+    e8 = T(E8M0, 2 * 1024 * 16, 1024 * 16, 16)
+    assert decode(so, k=e8, v=e8) == UNSUPPORTED
+    assert decode(so, q=T(MXFP4, 1024, 128, 128), out=T(MXFP4, 1024, 128, 128)) == UNSUPPORTED
+    assert decode(so, q=T(E8M0, 1024, 128, 128), out=T(E8M0, 1024, 128, 128)) == UNSUPPORTED
+
+
+def partials(so, q=None, k=None, B=1, Hq=8, Hkv=2, d=128, L=1024, S=4):
+    q = q or T(BF16, Hq * d, d, d)
+    k = k or T(BF16, Hkv * L * d, L * d, d)
+    used = ctypes.c_int(0)
+    return so.attn_decode_partials(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), None, None, None, B, Hq, Hkv,
+                                   d, L, 0.0, 0, S, FAKE, FAKE, FAKE, ctypes.byref(used), None)
+
+
+def test_decode_partials_argument_errors(so):
+    assert partials(so, B=0) == INVALID
+    assert partials(so, d=96) == UNSUPPORTED
+    assert partials(so, k=T(MXFP4, 2 * 1024 * 64, 1024 * 64, 64)) == UNSUPPORTED
+    assert partials(so, k=T(E8M0, 2 * 1024 * 16, 1024 * 16, 16)) == UNSUPPORTED
+    assert partials(so, q=T(MXFP4, 1024, 128, 128)) == UNSUPPORTED
+    assert partials(so, q=T(E8M0, 1024, 128, 128)) == UNSUPPORTED
 
 
 def test_workspace_init_errors(so):
@@ -176,9 +200,6 @@ def test_mixed_decode_argument_errors(so):
     # an empty span may come without tensors
     assert mixed(so, L_hi=0, S_hi=0, no_hi=True, ws=None) == WORKSPACE  # validation reaches the workspace check
     assert mixed(so, L_hi=16, no_hi=True) == INVALID
-
-
-MXFP4, E8M0 = 3, 4
 
 
 _DEFAULT = object()
