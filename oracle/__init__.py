@@ -48,6 +48,8 @@ def _load():
     lib.oracle_pi_attention.restype = i32
     lib.oracle_backward.argtypes = common + [vp, vp, vp, vp, i32]
     lib.oracle_backward.restype = i32
+    lib.oracle_backward_subset.argtypes = common + [vp, vp, i64, vp, i64, vp, vp, vp, i32]
+    lib.oracle_backward_subset.restype = i32
     lib.oracle_partial.argtypes = common + [i32, i32, i32, i64, i64, vp, vp, vp]
     lib.oracle_partial.restype = i32
     lib.oracle_energy.argtypes = common + [i32, i32, i32, vp]
@@ -163,6 +165,27 @@ def backward(prob, dout, nthreads=None):
     rc = lib.oracle_backward(*prob._common(), _p(dout), _p(dq), _p(dk), _p(dv), nthreads or _threads())
     if rc != 0:
         raise ValueError("oracle_backward: bad arguments")
+    return dq, dk, dv
+
+
+def backward_subset(prob, dout, q_rows=(), keys=(), nthreads=None):
+    """The gradients of backward() at chosen places only: dq of the query rows
+    q_rows (flat ids (b*Hq + h)*Lq + i) and dk, dv of the keys `keys` (flat
+    ids (b*Hkv + g)*Lcap + j). Returns (dq [len(q_rows), d], dk [len(keys), d],
+    dv [len(keys), d]) in float64."""
+    lib = _load()
+    dout = np.ascontiguousarray(dout)
+    if dout.dtype != prob.q.dtype or dout.shape != prob.q.shape:
+        raise ValueError("dout must match q in shape and dtype")
+    qr = np.ascontiguousarray(q_rows, dtype=np.int64).ravel()
+    ky = np.ascontiguousarray(keys, dtype=np.int64).ravel()
+    dq = np.zeros((qr.size, prob.d), dtype=np.float64)
+    dk = np.zeros((ky.size, prob.d), dtype=np.float64)
+    dv = np.zeros((ky.size, prob.d), dtype=np.float64)
+    rc = lib.oracle_backward_subset(*prob._common(), _p(dout), _p(qr), qr.size, _p(ky), ky.size, _p(dq), _p(dk),
+                                    _p(dv), nthreads or _threads())
+    if rc != 0:
+        raise ValueError("oracle_backward_subset: bad arguments")
     return dq, dk, dv
 
 

@@ -457,6 +457,247 @@ int oracle_backward(const void* q, int q_dtype, const void* k, const void* v, in
     return 0;
 }
 
+/*
+ * The same gradients for chosen rows and keys only, for problems too large for
+ * oracle_backward: dq of the listed query rows and dk, dv of the listed keys,
+ * each by the formulas above. A key's gradients sum over every query row of
+ * its KV head's query heads that sees it, so for each (b, g) that owns a
+ * listed key the softmax statistics of all those rows come first: the row
+ * maximum M_i, Z_i = sum_j exp(s_ij - M_i) and D_i = sum_j P_ij dP_ij over
+ * the row's visible keys. Then P_ij = exp(s_ij - M_i) / Z_i and
+ * dz_ij = P_ij (dP_ij - D_i) as before.
+ */
+typedef struct {
+    const problem* p;
+    const void* dout;
+    const int64_t* items; /* query rows or keys, flat ids */
+    int64_t n;
+    int tid, nthreads;
+    /* key mode: the (b, g) being processed and its decoded operands */
+    int b, g;
+    const double *kd, *vd, *qg, *dog, *M, *Z, *D;
+    double *out0, *out1;
+} sub_job;
+
+static double dot(const double* a, const double* b, int d) {
+    double acc = 0.0;
+    for (int c = 0; c < d; ++c) acc += a[c] * b[c];
+    return acc;
+}
+
+/* dq of listed rows (b*Hq + h)*Lq + i: one row at a time, by the definition. */
+static void* sub_dq_worker(void* arg) {
+    sub_job* j = (sub_job*)arg;
+    const problem* p = j->p;
+    const int d = p->d;
+    double* qd = (double*)malloc(sizeof(double) * (size_t)d);
+    double* dod = (double*)malloc(sizeof(double) * (size_t)d);
+    double* kr = (double*)malloc(sizeof(double) * (size_t)d);
+    double* vr = (double*)malloc(sizeof(double) * (size_t)d);
+    double* P = (double*)malloc(sizeof(double) * (size_t)(p->Lcap > 0 ? p->Lcap : 1));
+    double* dP = (double*)malloc(sizeof(double) * (size_t)(p->Lcap > 0 ? p->Lcap : 1));
+    for (int64_t r = j->tid; r < j->n; r += j->nthreads) {
+        const int64_t flat = j->items[r];
+        const int i = (int)(flat % p->Lq), h = (int)((flat / p->Lq) % p->Hq);
+        const int b = (int)(flat / ((int64_t)p->Lq * p->Hq)), g = h / (p->Hq / p->Hkv);
+        double* dqi = j->out0 + r * d;
+        for (int c = 0; c < d; ++c) dqi[c] = 0.0;
+        const int64_t hi = visible_end(p, b, i);
+        if (hi <= 0) continue;
+        load_q_row(p, b, h, i, qd);
+        for (int c = 0; c < d; ++c) dod[c] = elem(j->dout, p->q_dtype, flat * d + c);
+        double mx = -INFINITY;
+        for (int64_t jj = 0; jj < hi; ++jj) {
+            load_kv_row(p, p->k, p->k_scale, b, g, jj, kr);
+            P[jj] = score(p, qd, kr);
+            if (P[jj] > mx) mx = P[jj];
+        }
+        double z = 0.0;
+        for (int64_t jj = 0; jj < hi; ++jj) {
+            P[jj] = exp(P[jj] - mx);
+            z += P[jj];
+        }
+        double D = 0.0;
+        for (int64_t jj = 0; jj < hi; ++jj) {
+            P[jj] /= z;
+            load_kv_row(p, p->v, p->v_scale, b, g, jj, vr);
+            dP[jj] = dot(dod, vr, d);
+            D += P[jj] * dP[jj];
+        }
+        for (int64_t jj = 0; jj < hi; ++jj) {
+            const double dz = P[jj] * (dP[jj] - D);
+            load_kv_row(p, p->k, p->k_scale, b, g, jj, kr);
+            for (int c = 0; c < d; ++c) dqi[c] += p->scale * dz * kr[c];
+        }
+    }
+    free(qd);
+    free(dod);
+    free(kr);
+    free(vr);
+    free(P);
+    free(dP);
+    return NULL;
+}
+
+/* Statistics M, Z, D of the rows of (b, g): row index hl*Lq + i for the
+ * group's local query head hl. */
+static void* sub_stats_worker(void* arg) {
+    sub_job* j = (sub_job*)arg;
+    const problem* p = j->p;
+    const int d = p->d, G = p->Hq / p->Hkv;
+    double* s = (double*)malloc(sizeof(double) * (size_t)(p->Lcap > 0 ? p->Lcap : 1));
+    double* M = (double*)j->M;
+    double* Z = (double*)j->Z;
+    double* D = (double*)j->D;
+    for (int64_t r = j->tid; r < (int64_t)G * p->Lq; r += j->nthreads) {
+        const int i = (int)(r % p->Lq);
+        const double* qd = j->qg + r * d;
+        const double* dod = j->dog + r * d;
+        const int64_t hi = visible_end(p, j->b, i);
+        double mx = -INFINITY;
+        for (int64_t jj = 0; jj < hi; ++jj) {
+            s[jj] = p->scale * dot(qd, j->kd + jj * d, d);
+            if (s[jj] > mx) mx = s[jj];
+        }
+        double z = 0.0;
+        for (int64_t jj = 0; jj < hi; ++jj) z += exp(s[jj] - mx);
+        double dd = 0.0;
+        for (int64_t jj = 0; jj < hi; ++jj) dd += exp(s[jj] - mx) / z * dot(dod, j->vd + jj * d, d);
+        M[r] = mx;
+        Z[r] = z;
+        D[r] = dd;
+    }
+    free(s);
+    return NULL;
+}
+
+/* dk, dv of the listed keys that belong to (b, g). */
+static void* sub_key_worker(void* arg) {
+    sub_job* j = (sub_job*)arg;
+    const problem* p = j->p;
+    const int d = p->d, G = p->Hq / p->Hkv;
+    int64_t mine = 0;
+    for (int64_t r = 0; r < j->n; ++r) {
+        const int64_t flat = j->items[r];
+        const int64_t jj = flat % p->Lcap;
+        if (flat / p->Lcap != (int64_t)j->b * p->Hkv + j->g) continue;
+        if (mine++ % j->nthreads != j->tid) continue;
+        double* dkj = j->out0 + r * d;
+        double* dvj = j->out1 + r * d;
+        for (int c = 0; c < d; ++c) dkj[c] = dvj[c] = 0.0;
+        const double* kr = j->kd + jj * d;
+        const double* vr = j->vd + jj * d;
+        for (int hl = 0; hl < G; ++hl) {
+            for (int i = 0; i < p->Lq; ++i) {
+                if (jj >= visible_end(p, j->b, i)) continue;
+                const int64_t row = (int64_t)hl * p->Lq + i;
+                const double* qd = j->qg + row * d;
+                const double* dod = j->dog + row * d;
+                const double P = exp(p->scale * dot(qd, kr, d) - j->M[row]) / j->Z[row];
+                const double dz = P * (dot(dod, vr, d) - j->D[row]);
+                for (int c = 0; c < d; ++c) {
+                    dkj[c] += p->scale * dz * qd[c];
+                    dvj[c] += P * dod[c];
+                }
+            }
+        }
+    }
+    return NULL;
+}
+
+static void run_sub(void* (*fn)(void*), sub_job* proto, int nthreads) {
+    pthread_t th[256];
+    sub_job jobs[256];
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = *proto;
+        jobs[t].tid = t;
+        jobs[t].nthreads = nthreads;
+        pthread_create(&th[t], NULL, fn, &jobs[t]);
+    }
+    for (int t = 0; t < nthreads; ++t) pthread_join(th[t], NULL);
+}
+
+/*
+ * Arguments as oracle_backward, plus: q_rows [nq] flat query rows
+ * (b*Hq + h)*Lq + i with dq [nq, d]; keys [nk] flat keys (b*Hkv + g)*Lcap + j
+ * with dk, dv [nk, d] (zero for a key no query sees). Returns 0, or 1 on a
+ * bad argument (including an id out of range).
+ */
+int oracle_backward_subset(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype,
+                           const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B, int Hq,
+                           int Hkv, int Lq, int Lcap, int d, double scale, int causal, const void* dout,
+                           const int64_t* q_rows, int64_t nq, const int64_t* keys, int64_t nk, double* dq,
+                           double* dk, double* dv, int nthreads) {
+    problem p = {q, q_dtype, k, v, kv_dtype, k_scale, v_scale, kv_lens, B, Hq, Hkv, Lq, Lcap, d, scale, causal};
+    if (check_problem(&p) || !dout || nq < 0 || nk < 0) return 1;
+    for (int64_t r = 0; r < nq; ++r)
+        if (q_rows[r] < 0 || q_rows[r] >= (int64_t)B * Hq * Lq) return 1;
+    for (int64_t r = 0; r < nk; ++r)
+        if (keys[r] < 0 || keys[r] >= (int64_t)B * Hkv * Lcap) return 1;
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    sub_job job;
+    memset(&job, 0, sizeof(job));
+    job.p = &p;
+    job.dout = dout;
+    if (nq > 0) {
+        job.items = q_rows;
+        job.n = nq;
+        job.out0 = dq;
+        run_sub(sub_dq_worker, &job, nthreads);
+    }
+    if (nk == 0) return 0;
+    const int G = Hq / Hkv;
+    double* kd = (double*)malloc(sizeof(double) * (size_t)Lcap * d + 8);
+    double* vd = (double*)malloc(sizeof(double) * (size_t)Lcap * d + 8);
+    double* qg = (double*)malloc(sizeof(double) * (size_t)G * Lq * d);
+    double* dog = (double*)malloc(sizeof(double) * (size_t)G * Lq * d);
+    double* M = (double*)malloc(sizeof(double) * (size_t)G * Lq);
+    double* Z = (double*)malloc(sizeof(double) * (size_t)G * Lq);
+    double* D = (double*)malloc(sizeof(double) * (size_t)G * Lq);
+    for (int b = 0; b < B; ++b) {
+        for (int g = 0; g < Hkv; ++g) {
+            int used = 0;
+            for (int64_t r = 0; r < nk && !used; ++r) used = keys[r] / Lcap == (int64_t)b * Hkv + g;
+            if (!used) continue;
+            for (int64_t jj = 0; jj < Lcap; ++jj) {
+                load_kv_row(&p, k, k_scale, b, g, jj, kd + jj * d);
+                load_kv_row(&p, v, v_scale, b, g, jj, vd + jj * d);
+            }
+            for (int hl = 0; hl < G; ++hl)
+                for (int i = 0; i < Lq; ++i) {
+                    const int64_t row = (int64_t)hl * Lq + i;
+                    const int64_t off = (((int64_t)b * Hq + g * G + hl) * Lq + i) * d;
+                    load_q_row(&p, b, g * G + hl, i, qg + row * d);
+                    for (int c = 0; c < d; ++c) dog[row * d + c] = elem(dout, q_dtype, off + c);
+                }
+            job.b = b;
+            job.g = g;
+            job.kd = kd;
+            job.vd = vd;
+            job.qg = qg;
+            job.dog = dog;
+            job.M = M;
+            job.Z = Z;
+            job.D = D;
+            run_sub(sub_stats_worker, &job, nthreads);
+            job.items = keys;
+            job.n = nk;
+            job.out0 = dk;
+            job.out1 = dv;
+            run_sub(sub_key_worker, &job, nthreads);
+        }
+    }
+    free(kd);
+    free(vd);
+    free(qg);
+    free(dog);
+    free(M);
+    free(Z);
+    free(D);
+    return 0;
+}
+
 /* Partial (o, m, l) of row (b, h, i) over keys [j0, j1) intersected with the
  * keys the row may see. An empty set gives the identity (0, -inf, 0). */
 int oracle_partial(const void* q, int q_dtype, const void* k, const void* v, int kv_dtype, const float* k_scale,

@@ -1,8 +1,8 @@
 """GPU parity of attn_prefill_backward (dq, dk, dv of causal or full attention)
 against the oracle's backward: causal and full, Lq < Lkv alignment, grouped
 heads (G = 1, 4, 8), lengths that are not multiples of the 64-row blocks, one
-query row, bf16 and fp32 gradient outputs, determinism, and invariants at the
-16K-token size.
+query row, bf16 and fp32 gradient outputs, determinism, and at the 16K-token
+size element-wise parity on sampled rows and keys plus two sum invariants.
 
 Tolerance. P and dz enter the MFMAs rounded to bf16 (relative error 2^-9 each)
 and D = dO . O uses the forward's bf16 output, so each gradient element carries
@@ -87,16 +87,38 @@ def test_backward_1024_tokens_all_heads_and_determinism():
         assert torch.equal(a.view(torch.int32), b_.view(torch.int32))
 
 
-def test_backward_16k_invariants():
-    # at full size: each KV head's key gradients sum to zero (a row's logit
-    # gradients do), and its value gradients sum to the dO of its query rows
+def _row_sample(L):
+    """The prefill's row sample: the first and last 256 rows and 512 rows spread between them."""
+    return np.unique(np.concatenate([np.arange(256), np.arange(L - 256, L),
+                                     np.linspace(256, L - 257, 512).astype(np.int64)]))
+
+
+def test_backward_16k_sampled_rows_and_keys():
+    # the timed size (16K causal, 32q/8kv): dq element by element on the row
+    # sample of every query head, dk and dv on 512 keys of each of two KV heads
+    # (the first and last 64 keys and 384 spread between), against the oracle
+    # computed at those places only; then the two sum invariants over all keys
     inp = make_inputs(4)
     (dq, dk, dv), dout_bits, _, _ = _run(inp, True, seed=134)
+    B, Hq, L, d = inp["q"].shape
+    Hkv = inp["k"].shape[1]
+    rows_i = _row_sample(L)
+    q_rows = (np.arange(Hq)[:, None] * L + rows_i[None, :]).ravel()
+    keys_j = np.unique(np.concatenate([np.arange(64), np.arange(L - 64, L),
+                                       np.linspace(64, L - 65, 384).astype(np.int64)]))
+    keys = np.concatenate([g * L + keys_j for g in (0, 5)])
+    prob = oracle.Problem(inp["q"], inp["k"], inp["v"], causal=True)
+    rq, rk, rv = oracle.backward_subset(prob, dout_bits, q_rows=q_rows, keys=keys)
+    _check(dq.reshape(-1, d)[torch.from_numpy(q_rows).cuda()], rq, "bwd 16k dq (%d rows)" % q_rows.size)
+    kidx = torch.from_numpy(keys).cuda()
+    _check(dk.reshape(-1, d)[kidx], rk, "bwd 16k dk (%d keys)" % keys.size)
+    _check(dv.reshape(-1, d)[kidx], rv, "bwd 16k dv (%d keys)" % keys.size)
+    # each KV head's key gradients sum to zero (a row's logit gradients do),
+    # and its value gradients sum to the dO of its query rows
     dk64 = dk.double().sum(dim=2)
     assert dk64.abs().max().item() <= 1e-3 * dk.double().abs().sum(dim=2).max().item()
     do = torch.from_numpy(dout_bits.view(np.int16)).view(torch.bfloat16).double()
-    B, Hq, L, d = do.shape
-    ref_sum = do.reshape(B, 8, Hq // 8 * L, d).sum(dim=2)
+    ref_sum = do.reshape(B, Hkv, Hq // Hkv * L, d).sum(dim=2)
     got_sum = dv.double().sum(dim=2).cpu()
     rel = (got_sum - ref_sum).norm() / ref_sum.norm()
     print("16k: dk column sums max %.3g, dv sums rel %.3g" % (dk64.abs().max().item(), rel.item()), flush=True)

@@ -642,6 +642,60 @@ def test_backward_key_gradients_sum_to_zero():
                                rtol=1e-12, atol=1e-10)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,L,causal,lens", [
+    (1, 4, 2, 6, 6, True, None), (2, 8, 2, 37, 50, True, [50, 23]), (1, 4, 1, 20, 33, False, None),
+    (1, 8, 2, 1, 40, True, None), (2, 4, 4, 30, 30, True, [0, 30])])
+def test_backward_subset_equals_the_full_backward(B, Hq, Hkv, Lq, L, causal, lens):
+    # the full backward is pinned by central differences above; the subset
+    # must give the same rows and keys, in any order and with repeats
+    rng = np.random.default_rng(B * 100 + Lq)
+    q, k, v = rand_f32(B, Hq, Lq, 16), rand_f32(B, Hkv, L, 16), rand_f32(B, Hkv, L, 16)
+    dout = rand_f32(B, Hq, Lq, 16)
+    prob = oracle.Problem(q, k, v, causal=causal, kv_lens=None if lens is None else np.array(lens, np.int32))
+    dq, dk, dv = oracle.backward(prob, dout)
+    rows = rng.permutation(B * Hq * Lq)[:max(1, B * Hq * Lq // 2)]
+    rows = np.concatenate([rows, rows[:2]])
+    keys = rng.permutation(B * Hkv * L)[:max(1, B * Hkv * L // 3)]
+    keys = np.concatenate([keys, keys[:1]])
+    sq, sk, sv = oracle.backward_subset(prob, dout, q_rows=rows, keys=keys)
+    np.testing.assert_allclose(sq, dq.reshape(-1, 16)[rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(sk, dk.reshape(-1, 16)[keys], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(sv, dv.reshape(-1, 16)[keys], rtol=1e-12, atol=1e-13)
+
+
+def test_backward_subset_matches_central_differences_directly():
+    B, Hq, Hkv, L, d = 1, 4, 2, 7, 4
+    rng = np.random.default_rng(11)
+    q, k, v = rng.standard_normal((B, Hq, L, d)), rng.standard_normal((B, Hkv, L, d)), rng.standard_normal((B, Hkv, L, d))
+    dout = rng.standard_normal((B, Hq, L, d))
+    kw = dict(causal=True, scale=0.7)
+    rows, keys = [3, 9, 27], [0, 5, 13]
+    sq, sk, sv = oracle.backward_subset(oracle.Problem(q, k, v, **kw), dout, q_rows=rows, keys=keys)
+    h = 1e-5
+    for name, x, got, ids in (("q", q, sq, rows), ("k", k, sk, keys), ("v", v, sv, keys)):
+        for n, flat in enumerate(ids):
+            for c in range(d):
+                idx = np.unravel_index(flat, x.shape[:3]) + (c,)
+                args = {"q": q, "k": k, "v": v}
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args[name] = xp
+                lp = _loss(args["q"], args["k"], args["v"], dout, **kw)
+                args[name] = xm
+                lm = _loss(args["q"], args["k"], args["v"], dout, **kw)
+                assert abs(got[n, c] - (lp - lm) / (2 * h)) <= 1e-6 * max(1.0, abs(got[n, c])), (name, flat, c)
+
+
+def test_backward_subset_rejects_ids_out_of_range():
+    q, k, v = rand_f32(1, 2, 4, 8), rand_f32(1, 1, 4, 8), rand_f32(1, 1, 4, 8)
+    prob = oracle.Problem(q, k, v, causal=True)
+    with pytest.raises(ValueError):
+        oracle.backward_subset(prob, q, q_rows=[8])
+    with pytest.raises(ValueError):
+        oracle.backward_subset(prob, q, keys=[-1])
+
+
 # ------------------------------------------------ MX FP4 low-precision span
 # The page's FP4 (a 4-bit float with a 2-bit exponent) held as OCP MX FP4:
 # E2M1 elements, one E8M0 power-of-two scale per 32 consecutive elements of a
