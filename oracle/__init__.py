@@ -296,36 +296,32 @@ def decode_elems(a):
     return out
 
 
-def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_lens=None, scale=None,
-                 heads=None, lo_format="e4m3"):
-    """Single-query decode over a cache kept in two precisions.
+def decode_spans(q, spans, scale=None, heads=None):
+    """Single-query decode over a cache kept as several key spans, each in its
+    own storage format (a cache kept in several precisions).
 
-    q [B,Hq,1,d] (bf16 bits or float32); k_hi, v_hi [B,Hkv,L_hi,d] bf16 bits
-    (or None: no such keys); k_lo, v_lo [B,Hkv,L_lo,d] e4m3 codes (or None)
-    with k_scale, v_scale float32 [B*Hkv]; hi_lens, lo_lens int32 [B*Hkv]
-    (valid keys per (sequence, KV head), clamped to the capacity) or None =
-    the capacity. Each query head sees the union of its group's valid bf16
-    keys and valid fp8 keys (the latter at code * scale): the union is built in
-    float64 and handed to the plain attention above. `heads` lists flat query
-    heads b*Hq + h (all when None). Returns (out [n,d], lse [n]) in float64.
-    With lo_format="mxfp4" the low span is MX FP4: k_lo, v_lo are codes
-    [B,Hkv,L_lo,d/2] and k_scale, v_scale their E8M0 scales [B,Hkv,L_lo,d/32].
-    """
+    q [B,Hq,1,d] (bf16 bits or float32). Each span is a dict with k, v and
+    "format": "bf16" (k, v [B,Hkv,L,d] bf16 bits), "e4m3" (codes
+    [B,Hkv,L,d] with "k_scale", "v_scale" float32 [B*Hkv]) or "mxfp4" (codes
+    [B,Hkv,L,d/2] with E8M0 "k_scale", "v_scale" [B,Hkv,L,d/32]); "lens" int32
+    [B*Hkv] (valid keys per (sequence, KV head), clamped to the capacity) or
+    None = the capacity. A span with k None has no keys. Each query head sees
+    the union of its group's valid keys of every span at their real values,
+    built in float64 (spans in the order given) and handed to the plain
+    attention above. `heads` lists flat query heads b*Hq + h (all when None).
+    Returns (out [n,d], lse [n]) in float64."""
     q = np.ascontiguousarray(q)
     B, Hq, Lq, d = q.shape
     assert Lq == 1
-    Hkv = (k_hi if k_hi is not None else k_lo).shape[1]
+    present = [sp for sp in spans if sp.get("k") is not None]
+    Hkv = present[0]["k"].shape[1] if present else Hq
     G = Hq // Hkv
-    L_hi = 0 if k_hi is None else k_hi.shape[2]
-    L_lo = 0 if k_lo is None else k_lo.shape[2]
-    hl = np.full(B * Hkv, L_hi, np.int64) if hi_lens is None else np.clip(np.asarray(hi_lens).ravel(), 0, L_hi)
-    ll = np.full(B * Hkv, L_lo, np.int64) if lo_lens is None else np.clip(np.asarray(lo_lens).ravel(), 0, L_lo)
-    mx = lo_format == "mxfp4"
-    if mx:
-        ks, vs = k_scale, v_scale
-    else:
-        ks = None if k_scale is None else np.asarray(k_scale, np.float32).ravel()
-        vs = None if v_scale is None else np.asarray(v_scale, np.float32).ravel()
+    caps, lens = [], []
+    for sp in spans:
+        cap = 0 if sp.get("k") is None else sp["k"].shape[2]
+        caps.append(cap)
+        ln = sp.get("lens")
+        lens.append(np.full(B * Hkv, cap, np.int64) if ln is None else np.clip(np.asarray(ln).ravel(), 0, cap))
     heads = np.arange(B * Hq) if heads is None else np.asarray(heads).ravel()
     out = np.zeros((heads.size, d), np.float64)
     lse = np.zeros(heads.size, np.float64)
@@ -335,16 +331,25 @@ def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_l
     for (b, g), items in by_group.items():
         bg = b * Hkv + g
         kparts, vparts = [], []
-        if hl[bg]:
-            kparts.append(decode_elems(k_hi[b, g, :hl[bg]]))
-            vparts.append(decode_elems(v_hi[b, g, :hl[bg]]))
-        if ll[bg] and mx:
-            kparts.append(mxfp4_to_f64(k_lo[b, g, :ll[bg]], ks[b, g, :ll[bg]]))
-            vparts.append(mxfp4_to_f64(v_lo[b, g, :ll[bg]], vs[b, g, :ll[bg]]))
-        elif ll[bg]:
-            kparts.append(decode_elems(k_lo[b, g, :ll[bg]]) * np.float64(ks[bg]))
-            vparts.append(decode_elems(v_lo[b, g, :ll[bg]]) * np.float64(vs[bg]))
-        n = int(hl[bg] + ll[bg])
+        for sp, ln in zip(spans, lens):
+            n_s = int(ln[bg]) if sp.get("k") is not None else 0
+            if not n_s:
+                continue
+            fmt = sp["format"]
+            if fmt == "mxfp4":
+                kparts.append(mxfp4_to_f64(sp["k"][b, g, :n_s], sp["k_scale"][b, g, :n_s]))
+                vparts.append(mxfp4_to_f64(sp["v"][b, g, :n_s], sp["v_scale"][b, g, :n_s]))
+            elif fmt == "e4m3":
+                ks = np.asarray(sp["k_scale"], np.float32).ravel()
+                vs = np.asarray(sp["v_scale"], np.float32).ravel()
+                kparts.append(decode_elems(sp["k"][b, g, :n_s]) * np.float64(ks[bg]))
+                vparts.append(decode_elems(sp["v"][b, g, :n_s]) * np.float64(vs[bg]))
+            elif fmt == "bf16":
+                kparts.append(decode_elems(sp["k"][b, g, :n_s]))
+                vparts.append(decode_elems(sp["v"][b, g, :n_s]))
+            else:
+                raise ValueError("unknown span format %r" % (fmt,))
+        n = sum(x.shape[0] for x in kparts)
         kk = np.concatenate(kparts) if n else np.zeros((1, d))
         vv = np.concatenate(vparts) if n else np.zeros((1, d))
         prob = Problem(q[b:b + 1, g * G:(g + 1) * G], kk[None, None], vv[None, None],
@@ -354,3 +359,22 @@ def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_l
             out[i] = o[j]
             lse[i] = l_[j]
     return out, lse
+
+
+def decode_mixed(q, k_hi, v_hi, k_lo, v_lo, k_scale, v_scale, hi_lens=None, lo_lens=None, scale=None,
+                 heads=None, lo_format="e4m3"):
+    """Single-query decode over a cache kept in two precisions: decode_spans
+    with a bf16 span and a low-precision span.
+
+    q [B,Hq,1,d] (bf16 bits or float32); k_hi, v_hi [B,Hkv,L_hi,d] bf16 bits
+    (or None: no such keys); k_lo, v_lo [B,Hkv,L_lo,d] e4m3 codes (or None)
+    with k_scale, v_scale float32 [B*Hkv]; hi_lens, lo_lens int32 [B*Hkv]
+    (valid keys per (sequence, KV head), clamped to the capacity) or None =
+    the capacity. With lo_format="mxfp4" the low span is MX FP4: k_lo, v_lo
+    are codes [B,Hkv,L_lo,d/2] and k_scale, v_scale their E8M0 scales
+    [B,Hkv,L_lo,d/32]. Returns (out [n,d], lse [n]) in float64.
+    """
+    spans = [dict(k=k_hi, v=v_hi, format="bf16", lens=hi_lens),
+             dict(k=k_lo, v=v_lo, format="mxfp4" if lo_format == "mxfp4" else "e4m3", k_scale=k_scale,
+                  v_scale=v_scale, lens=lo_lens)]
+    return decode_spans(q, spans, scale=scale, heads=heads)

@@ -785,3 +785,86 @@ def test_mixed_fp4_span_is_attention_over_the_decoded_union():
             o_ref, l_ref = brute_row(qd[b, h, 0], krows, vrows, 1 / math.sqrt(d))
             np.testing.assert_allclose(out[b * Hq + h], o_ref, rtol=1e-12, atol=1e-14)
             assert abs(lse[b * Hq + h] - l_ref) < 1e-12
+
+
+# ------------------------------------------- three precisions in one cache
+# The ThriftAttention page switches among FP4, FP8 and BF16 within one kernel
+# (COMPUTE layer of its Physical AI Stack section): one query's attention over
+# a cache whose keys are kept in all three formats is attention over the union.
+
+def _fp4_test_decode(codes, scales, d):
+    vals = np.empty(codes.shape[:-1] + (d,))
+    for idx in np.ndindex(*codes.shape[:-1]):
+        for c in range(d):
+            byte = int(codes[idx + (c // 2,)])
+            code = byte >> 4 if c & 1 else byte & 15
+            vals[idx + (c,)] = math.ldexp(_e2m1_table(code), int(scales[idx + (c // 32,)]) - 127)
+    return vals
+
+
+def _three_span_case(B, Hq, Hkv, L3, d, seed):
+    rng = np.random.default_rng(seed)
+    tq = torch.from_numpy(rng.standard_normal((B, Hq, 1, d)).astype(np.float32)).to(torch.bfloat16)
+    kb = torch.from_numpy(rng.standard_normal((B, Hkv, L3[0], d)).astype(np.float32)).to(torch.bfloat16)
+    vb = torch.from_numpy(rng.standard_normal((B, Hkv, L3[0], d)).astype(np.float32)).to(torch.bfloat16)
+    k8 = (torch.from_numpy(rng.standard_normal((B, Hkv, L3[1], d)).astype(np.float32)) * 40).to(torch.float8_e4m3fn)
+    v8 = (torch.from_numpy(rng.standard_normal((B, Hkv, L3[1], d)).astype(np.float32)) * 40).to(torch.float8_e4m3fn)
+    ks8 = rng.uniform(0.01, 0.06, B * Hkv).astype(np.float32)
+    vs8 = rng.uniform(0.01, 0.06, B * Hkv).astype(np.float32)
+    k4 = rng.integers(0, 256, (B, Hkv, L3[2], d // 2), dtype=np.uint8)
+    v4 = rng.integers(0, 256, (B, Hkv, L3[2], d // 2), dtype=np.uint8)
+    ks4 = rng.integers(121, 129, (B, Hkv, L3[2], d // 32), dtype=np.uint8)
+    vs4 = rng.integers(121, 129, (B, Hkv, L3[2], d // 32), dtype=np.uint8)
+    return tq, (kb, vb), (k8, v8, ks8, vs8), (k4, v4, ks4, vs4)
+
+
+def _spans(c, lens):
+    tq, (kb, vb), (k8, v8, ks8, vs8), (k4, v4, ks4, vs4) = c
+    return [dict(k=_bits(kb), v=_bits(vb), format="bf16", lens=lens[0]),
+            dict(k=k8.view(torch.uint8).numpy(), v=v8.view(torch.uint8).numpy(), format="e4m3", k_scale=ks8,
+                 v_scale=vs8, lens=lens[1]),
+            dict(k=k4, v=v4, format="mxfp4", k_scale=ks4, v_scale=vs4, lens=lens[2])]
+
+
+def test_three_span_cache_is_attention_over_the_decoded_union():
+    B, Hq, Hkv, d = 2, 4, 2, 64
+    c = _three_span_case(B, Hq, Hkv, (5, 7, 9), d, 21)
+    lens = (np.array([5, 0, 2, 3], np.int32), np.array([7, 4, 0, 1], np.int32), np.array([9, 3, 0, 0], np.int32))
+    out, lse = oracle.decode_spans(_bits(c[0]), _spans(c, lens))
+    tq, (kb, vb), (k8, v8, ks8, vs8), (k4, v4, ks4, vs4) = c
+    qd = tq.to(torch.float64).numpy()
+    kbd, vbd = kb.to(torch.float64).numpy(), vb.to(torch.float64).numpy()
+    k8d, v8d = k8.to(torch.float64).numpy(), v8.to(torch.float64).numpy()
+    k4d, v4d = _fp4_test_decode(k4, ks4, d), _fp4_test_decode(v4, vs4, d)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            bg = b * Hkv + g
+            krows = (list(kbd[b, g, :lens[0][bg]]) + list(k8d[b, g, :lens[1][bg]] * float(ks8[bg])) +
+                     list(k4d[b, g, :lens[2][bg]]))
+            vrows = (list(vbd[b, g, :lens[0][bg]]) + list(v8d[b, g, :lens[1][bg]] * float(vs8[bg])) +
+                     list(v4d[b, g, :lens[2][bg]]))
+            if not krows:  # (b=1, g=1) has no key in any span
+                assert np.all(out[b * Hq + h] == 0) and np.isneginf(lse[b * Hq + h])
+                continue
+            o_ref, l_ref = brute_row(qd[b, h, 0], krows, vrows, 1 / math.sqrt(d))
+            np.testing.assert_allclose(out[b * Hq + h], o_ref, rtol=1e-12, atol=1e-14)
+            assert abs(lse[b * Hq + h] - l_ref) < 1e-12
+
+
+def test_three_span_cache_does_not_depend_on_span_order():
+    c = _three_span_case(1, 8, 2, (30, 20, 40), 64, 22)
+    lens = (None, np.array([20, 11], np.int32), np.array([3, 40], np.int32))
+    sp = _spans(c, lens)
+    ref, ref_lse = oracle.decode_spans(_bits(c[0]), sp)
+    for order in ((2, 0, 1), (1, 2, 0), (2, 1, 0)):
+        out, lse = oracle.decode_spans(_bits(c[0]), [sp[i] for i in order])
+        np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(lse, ref_lse, rtol=1e-13)
+    # and two of the spans alone are the two-precision decode
+    two, two_lse = oracle.decode_mixed(_bits(c[0]), sp[0]["k"], sp[0]["v"], sp[2]["k"], sp[2]["v"], sp[2]["k_scale"],
+                                       sp[2]["v_scale"], None, lens[2], lo_format="mxfp4")
+    out, lse = oracle.decode_spans(_bits(c[0]), [sp[0], dict(sp[1], lens=np.zeros(2, np.int32)), sp[2]])
+    np.testing.assert_array_equal(out, two)
+    np.testing.assert_array_equal(lse, two_lse)
