@@ -5,8 +5,9 @@ stream + Box-Muller, see ``datagen.c``) and encodes them into the storage
 formats the library reads. Random numbers never come from the GPU path.
 
 Tensor ids used by the workloads: Q=0, K=1, V=2, per-sequence lengths=3; the
-fp8 span of a two-precision cache: K=4, V=5, its lengths=6; the pi-Attention
-gate alpha=7; the output gradient of the backward pass=9.
+low-precision span of a two-precision cache: K=4, V=5, its lengths=6; the
+pi-Attention gate alpha=7; the output gradient of the backward pass=9; the
+fp8 span of a three-precision cache: K=10, V=11, its lengths=12.
 """
 import ctypes
 import os
@@ -21,6 +22,7 @@ _lib = None
 TID_Q, TID_K, TID_V, TID_LENS = 0, 1, 2, 3
 TID_K_LO, TID_V_LO, TID_LENS_LO = 4, 5, 6
 TID_DOUT = 9
+TID_K_MID, TID_V_MID, TID_LENS_MID = 10, 11, 12
 
 
 def build():

@@ -11,8 +11,8 @@ consecutive elements of a row, chosen from the block's largest magnitude.
 """
 import numpy as np
 
-from . import (TID_K, TID_K_LO, TID_LENS, TID_LENS_LO, TID_Q, TID_V, TID_V_LO, normal_bf16_bits, normal_e4m3,
-               normal_f32, normal_mxfp4, uniform_int)
+from . import (TID_K, TID_K_LO, TID_K_MID, TID_LENS, TID_LENS_LO, TID_LENS_MID, TID_Q, TID_V, TID_V_LO,
+               TID_V_MID, normal_bf16_bits, normal_e4m3, normal_f32, normal_mxfp4, uniform_int)
 
 WORKLOADS = {
     1: dict(name="single-head decode, fp32, L=1024, d=64, 4 splits", kind="decode", B=1, Hq=1, Hkv=1, d=64,
@@ -35,6 +35,10 @@ WORKLOADS = {
                  "per 32), 32q/8kv, d=128",
             kind="mixed", B=1, Hq=32, Hkv=8, d=128, L=131072, hi_frac=0.1, q="bf16", mul=0.5, causal=False,
             lo="mxfp4"),
+    10: dict(name="three-precision KV decode, L=131072: first and last 10% bf16, 20% fp8-e4m3, 60% MX fp4, "
+                  "32q/8kv, d=128",
+             kind="mixed3", B=1, Hq=32, Hkv=8, d=128, L=131072, hi_frac=0.1, mid_frac=0.2, q="bf16", mul=0.5,
+             causal=False),
 }
 
 # Tensor id of the pi-Attention gate alpha (one value per query row, uniform in
@@ -130,3 +134,56 @@ def make_alpha(wl, shape, seed=None):
     from . import uniform_f32
     seed = wl if seed is None else seed
     return uniform_f32(seed, TID_ALPHA, shape, 0.05, 0.95)
+
+
+def make_mixed3_inputs(wl=10, seed=None, B=None, Hq=None, Hkv=None, d=None, L=None, L_hi=None, L_mid=None,
+                       L_lo=None, lens=None):
+    """Host inputs of a three-precision cache: the first and the last tenth of
+    the L tokens (2 * round(0.1 * L) keys) in bf16, 2 * round(0.1 * L) more in
+    fp8-e4m3 (one amax/448 scale per (batch, KV head)) and the rest in MX fp4
+    (one e8m0 scale per 32 elements of a row). Key order does not change
+    single-query attention, so each precision is one span. `lens` = (lo, hi)
+    draws a valid length per (batch, KV head) for each span uniformly from
+    [lo*cap, hi*cap]. Returns dict(q, k_hi, v_hi, k_mid, v_mid, k_mid_scale,
+    v_mid_scale, k_lo, v_lo, k_lo_scale, v_lo_scale, hi_lens, mid_lens,
+    lo_lens)."""
+    cfg = WORKLOADS[wl]
+    seed = wl if seed is None else seed
+    B = B or cfg["B"]
+    Hq = Hq or cfg["Hq"]
+    Hkv = Hkv or cfg["Hkv"]
+    d = d or cfg["d"]
+    L = L or cfg["L"]
+    if L_hi is None:
+        L_hi = 2 * int(round(cfg["hi_frac"] * L))
+    if L_mid is None:
+        L_mid = 2 * int(round((cfg["mid_frac"] / 2) * L))
+    if L_lo is None:
+        L_lo = L - L_hi - L_mid
+    mul = cfg["mul"]
+    out = dict(q=normal_bf16_bits(seed, TID_Q, (B, Hq, 1, d), mul))
+    out["k_hi"] = normal_bf16_bits(seed, TID_K, (B, Hkv, L_hi, d), mul) if L_hi else None
+    out["v_hi"] = normal_bf16_bits(seed, TID_V, (B, Hkv, L_hi, d), mul) if L_hi else None
+    k8, ks8 = normal_e4m3(seed, TID_K_MID, (B, Hkv, L_mid, d), mul) if L_mid else (None, None)
+    v8, vs8 = normal_e4m3(seed, TID_V_MID, (B, Hkv, L_mid, d), mul) if L_mid else (None, None)
+    out.update(k_mid=k8, v_mid=v8, k_mid_scale=None if ks8 is None else ks8.ravel(),
+               v_mid_scale=None if vs8 is None else vs8.ravel())
+    k4, ks4 = normal_mxfp4(seed, TID_K_LO, (B, Hkv, L_lo, d), mul) if L_lo else (None, None)
+    v4, vs4 = normal_mxfp4(seed, TID_V_LO, (B, Hkv, L_lo, d), mul) if L_lo else (None, None)
+    out.update(k_lo=k4, v_lo=v4, k_lo_scale=ks4, v_lo_scale=vs4)
+    out["hi_lens"] = out["mid_lens"] = out["lo_lens"] = None
+    if lens is not None:
+        lo_f, hi_f = lens
+        out["hi_lens"] = uniform_int(seed, TID_LENS, B * Hkv, int(lo_f * L_hi), int(hi_f * L_hi))
+        out["mid_lens"] = uniform_int(seed, TID_LENS_MID, B * Hkv, int(lo_f * L_mid), int(hi_f * L_mid))
+        out["lo_lens"] = uniform_int(seed, TID_LENS_LO, B * Hkv, int(lo_f * L_lo), int(hi_f * L_lo))
+    return out
+
+
+def mixed3_spans(inp):
+    """The three spans of make_mixed3_inputs() in the form oracle.decode_spans takes."""
+    return [dict(k=inp["k_hi"], v=inp["v_hi"], format="bf16", lens=inp["hi_lens"]),
+            dict(k=inp["k_mid"], v=inp["v_mid"], format="e4m3", k_scale=inp["k_mid_scale"],
+                 v_scale=inp["v_mid_scale"], lens=inp["mid_lens"]),
+            dict(k=inp["k_lo"], v=inp["v_lo"], format="mxfp4", k_scale=inp["k_lo_scale"],
+                 v_scale=inp["v_lo_scale"], lens=inp["lo_lens"])]

@@ -249,6 +249,13 @@ ATTN_API attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* 
  * Everything else as attn_decode_mixed; the split plan is that of
  * attn_decode_mixed_fp4_splits(). An fp4 span with 0 keys (L_lo_cap = 0)
  * makes this the bf16 decode.
+ *
+ * Range: codes are widened to fp32 with the block scale applied, then to bf16
+ * for the products. Scale bytes 1 .. 252 give exact values for every code; a
+ * value past the fp32 range (|code| * 2^(e - 127) >= 2^128: bytes 253 and 254
+ * with the larger codes) becomes +-inf, and byte 0 (2^-127) gives fp32
+ * subnormals, which the products may flush to zero. Byte 255 is NaN and makes
+ * the outputs it reaches NaN, as in the definition.
  */
 ATTN_API attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
                                            const int32_t* hi_lens, int L_hi_cap, const attn_tensor* k_lo,
@@ -260,12 +267,56 @@ ATTN_API attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tens
 
 /*
  * Automatic split plan of attn_decode_mixed_fp4: as attn_decode_mixed_splits,
- * with a cost per key of 2 for bf16 and 1.8 for fp4 (the fp4 span is bound by
- * widening and P.V work, not by its bytes). Returns S_hi + S_lo, 0 on a bad
- * argument or a failed device query.
+ * with a cost per key of 2 for bf16 and 1.3 for fp4 (measured: an fp4 key
+ * costs about what an fp8 key does, its widening making up for its fewer
+ * bytes). Returns S_hi + S_lo, 0 on a bad argument or a failed device query.
  */
 ATTN_API int attn_decode_mixed_fp4_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi,
                                           int* splits_lo);
+
+/*
+ * Selective mixed-precision decode over a cache kept in all three precisions
+ * the ThriftAttention page names (its Physical AI Stack section: BF16, FP8
+ * and FP4 switched inside one kernel; the COMPUTE layer): per (sequence, KV
+ * head) a bf16 span, an fp8-e4m3 span and an MX fp4 span, each with its own
+ * length, in one launch (each workgroup streams one span in one precision)
+ * and one log-sum-exp merge (Tree Attention explainer, section 3). The
+ * result is exact attention over the union of the three key sets at their
+ * real values (fp8 code * scale, fp4 code * 2^(scale - 127)).
+ *
+ * k_hi, v_hi, hi_lens, L_hi_cap: the bf16 span, as in attn_decode_mixed.
+ * k_mid, v_mid [B, Hkv, L_mid_cap, d] ATTN_FP8_E4M3 with k_mid_scale,
+ *          v_mid_scale device float [B*Hkv], mid_lens device int32 [B, Hkv]
+ *          (or NULL = L_mid_cap): the fp8 span.
+ * k_lo, v_lo, k_lo_scale, v_lo_scale, lo_lens, L_lo_cap: the MX fp4 span, as
+ *          in attn_decode_mixed_fp4.
+ * A span with capacity 0 may come without tensors; not all three may be 0.
+ * num_splits_*: requested splits per span, 0 = the value of
+ *          attn_decode_mixed3_splits(). S = S_hi + S_mid + S_lo splits, and
+ *          the workspace is attn_decode_workspace_size(B, Hq, d, S) bytes,
+ *          prepared by attn_decode_workspace_init.
+ * q, out, lse, softmax_scale, B, Hq, Hkv, d, stream and errors as
+ * attn_decode_mixed (bf16 q and out, d = 128, Hq = 4 * Hkv).
+ */
+ATTN_API attn_status attn_decode_mixed3(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
+                                        const int32_t* hi_lens, int L_hi_cap, const attn_tensor* k_mid,
+                                        const attn_tensor* v_mid, const float* k_mid_scale, const float* v_mid_scale,
+                                        const int32_t* mid_lens, int L_mid_cap, const attn_tensor* k_lo,
+                                        const attn_tensor* v_lo, const attn_tensor* k_lo_scale,
+                                        const attn_tensor* v_lo_scale, const int32_t* lo_lens, int L_lo_cap, int B,
+                                        int Hq, int Hkv, int d, float softmax_scale, int num_splits_hi,
+                                        int num_splits_mid, int num_splits_lo, attn_tensor* out, float* lse,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Automatic split plan of attn_decode_mixed3: about two workgroups per compute
+ * unit in all, shared among the three spans in proportion to keys times the
+ * cost per key of the two-precision plans (2 bf16, 1.3 fp8, 1.3 fp4), no
+ * split shorter than 256 keys. Stores each span's splits (host pointers, may
+ * be NULL) and returns their sum; 0 on a bad argument or a failed device query.
+ */
+ATTN_API int attn_decode_mixed3_splits(int B, int Hkv, int L_hi_cap, int L_mid_cap, int L_lo_cap, int* splits_hi,
+                                       int* splits_mid, int* splits_lo);
 
 /*
  * Automatic split plan of attn_decode_mixed: about two workgroups per compute

@@ -18,6 +18,7 @@ __all__ = [
     "attn_decode_plan",
     "attn_decode", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
     "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_mixed_fp4", "attn_decode_mixed_fp4_splits",
+    "attn_decode_mixed3", "attn_decode_mixed3_splits",
     "attn_decode_pi", "attn_decode_pi_splits", "attn_prefill_pi",
     "attn_prefill_pi_workspace_size", "attn_prefill_backward", "attn_prefill_backward_workspace_size",
 ]
@@ -85,6 +86,11 @@ def load_library():
     lib.attn_decode_mixed_fp4.restype = i32
     lib.attn_decode_mixed_fp4_splits.argtypes = [i32, i32, i32, i32, ip, ip]
     lib.attn_decode_mixed_fp4_splits.restype = i32
+    lib.attn_decode_mixed3.argtypes = [tp, tp, tp, vp, i32, tp, tp, vp, vp, vp, i32, tp, tp, tp, tp, vp, i32, i32, i32,
+                                       i32, i32, f32, i32, i32, i32, tp, vp, vp, ctypes.c_size_t, vp]
+    lib.attn_decode_mixed3.restype = i32
+    lib.attn_decode_mixed3_splits.argtypes = [i32, i32, i32, i32, i32, ip, ip, ip]
+    lib.attn_decode_mixed3_splits.restype = i32
     lib.attn_decode_pi.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, i32, i32, tp, vp,
                                    vp, ctypes.c_size_t, vp]
     lib.attn_decode_pi.restype = i32
@@ -337,7 +343,8 @@ def attn_decode_mixed_fp4(q, k_hi, v_hi, k_lo, v_lo, k_lo_scale=None, v_lo_scale
     """Decode over a cache with a bf16 span (k_hi, v_hi [B,Hkv,L_hi,d]) and an MX fp4 span: k_lo, v_lo uint8
     [B,Hkv,L_lo,d/2] (E2M1 codes, first of a pair in the low nibble) with k_lo_scale, v_lo_scale uint8
     [B,Hkv,L_lo,d/32] (E8M0). hi_lens / lo_lens are int32 [B,Hkv] or None; either span may be None. Returns
-    (out [B,Hq,1,d] bf16, lse [B,Hq])."""
+    (out [B,Hq,1,d] bf16, lse [B,Hq]). Scale bytes 1..252 are exact for every code; 253-254 can overflow to inf,
+    0 gives fp32 subnormals (may flush to zero), 255 is NaN."""
     lib = load_library()
     B, Hq, Lq, d = q.shape
     if Lq != 1:
@@ -371,6 +378,60 @@ def attn_decode_mixed_fp4(q, k_hi, v_hi, k_lo, v_lo, k_lo_scale=None, v_lo_scale
                                    float(softmax_scale), int(max(S_hi, 0)), int(max(S_lo, 0)), ctypes.byref(ot),
                                    _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_mixed3_splits(B, Hkv, L_hi_cap, L_mid_cap, L_lo_cap):
+    """(S_hi, S_mid, S_lo): the automatic split plan of attn_decode_mixed3."""
+    hi, mid, lo = ctypes.c_int(0), ctypes.c_int(0), ctypes.c_int(0)
+    total = load_library().attn_decode_mixed3_splits(B, Hkv, L_hi_cap, L_mid_cap, L_lo_cap, ctypes.byref(hi),
+                                                     ctypes.byref(mid), ctypes.byref(lo))
+    if total <= 0:
+        raise AttnError(4, "could not plan splits")
+    return hi.value, mid.value, lo.value
+
+
+def attn_decode_mixed3(q, k_hi, v_hi, k_mid, v_mid, k_lo, v_lo, k_mid_scale=None, v_mid_scale=None, k_lo_scale=None,
+                       v_lo_scale=None, hi_lens=None, mid_lens=None, lo_lens=None, softmax_scale=0.0,
+                       num_splits_hi=0, num_splits_mid=0, num_splits_lo=0, out=None, lse=None, workspace=None,
+                       stream=None):
+    """Decode over a cache with a bf16 span (k_hi, v_hi [B,Hkv,L_hi,d]), an fp8-e4m3 span (k_mid, v_mid uint8
+    [B,Hkv,L_mid,d] with k_mid_scale, v_mid_scale float32 [B*Hkv]) and an MX fp4 span (k_lo, v_lo uint8
+    [B,Hkv,L_lo,d/2] with E8M0 k_lo_scale, v_lo_scale uint8 [B,Hkv,L_lo,d/32]); *_lens int32 [B,Hkv] or None; any
+    span may be None. Returns (out [B,Hq,1,d] bf16, lse [B,Hq])."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    if Lq != 1:
+        raise ValueError("attn_decode_mixed3 takes one query per sequence (q.shape[2] == 1)")
+    caps = [0 if t is None else t.shape[2] for t in (k_hi, k_mid, k_lo)]
+    Hkv = next(t for t in (k_hi, k_mid, k_lo) if t is not None).shape[1]
+    for lens in (hi_lens, mid_lens, lo_lens):
+        if lens is not None and (lens.dtype != torch.int32 or lens.numel() != B * Hkv or not lens.is_contiguous()):
+            raise ValueError("span lengths must be contiguous int32 with B*Hkv entries")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    S = [num_splits_hi, num_splits_mid, num_splits_lo]
+    if workspace is None:
+        if any(s <= 0 and c for s, c in zip(S, caps)):
+            auto = attn_decode_mixed3_splits(B, Hkv, *caps)
+            S = [s if s > 0 else a for s, a in zip(S, auto)]
+        used = sum(attn_decode_plan(c, s)[0] for s, c in zip(S, caps) if c)
+        workspace = attn_decode_workspace(B, Hq, d, used, device=q.device)
+
+    def view(t, dtype=None):
+        return None if t is None else ctypes.byref(_tensor(t, dtype))
+
+    qt, ot = _tensor(q), _tensor(out)
+    st = lib.attn_decode_mixed3(ctypes.byref(qt), view(k_hi), view(v_hi), _ptr(hi_lens), caps[0],
+                                view(k_mid), view(v_mid), _ptr(k_mid_scale),
+                                _ptr(v_mid_scale), _ptr(mid_lens), caps[1], view(k_lo, ATTN_MXFP4),
+                                view(v_lo, ATTN_MXFP4), view(k_lo_scale, ATTN_E8M0), view(v_lo_scale, ATTN_E8M0),
+                                _ptr(lo_lens), caps[2], B, Hq, Hkv, d, float(softmax_scale), int(max(S[0], 0)),
+                                int(max(S[1], 0)), int(max(S[2], 0)), ctypes.byref(ot), _ptr(lse), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     _check(st)
     return out, lse
 

@@ -24,6 +24,11 @@ attn_status fail(attn_status st, const char* fmt, ...) {
 
 constexpr int kChunkQuantum = 64;  // keys per workgroup step (4 waves x 16 keys)
 constexpr int kPrecBf16 = 0, kPrecFp8 = 1, kPrecFp4 = 2;  // span precisions of launch_decode_mfma_two
+// Split-plan cost per key of an MX fp4 span, against 2 for bf16 and 1.3 for
+// fp8 (measured on the two-span decodes: with both products on the MFMA an
+// fp4 key costs about what an fp8 key does; 128K keys, 20 % bf16: 18 + 46
+// splits 49.3 us, 14 + 50 58.0 us, 22 + 42 51.6 us).
+constexpr double kFp4Cost = 1.3;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 int elem_size(int dt) {
@@ -113,9 +118,13 @@ int attn_decode_auto_splits(int B, int Hkv, int L_cap, int kv_dtype, int ragged)
         S = ceil_div(L_cap, chunk);
     } else {
         // Equal chunks, all workgroups resident at once and the same number
-        // on every compute unit: 1 per CU for 16-bit caches, 4 for fp8 (a
-        // quarter of the bytes per load, more waves to keep the bytes in flight).
-        const int64_t per_cu = kv_dtype == ATTN_FP8_E4M3 ? 4 : 1;
+        // on every compute unit: 2 per CU for 16-bit caches, 4 for fp8 (a
+        // quarter of the bytes per load, more waves to keep the bytes in
+        // flight). With one per CU the merge would be fused into the decode
+        // kernel, whose agent-scope release per workgroup costs more than the
+        // second kernel (128K keys: 32 splits fused 91.3 us, 64 splits and the
+        // merge kernel 86.3 us).
+        const int64_t per_cu = kv_dtype == ATTN_FP8_E4M3 ? 4 : 2;
         S = (per_cu * cus) / ((int64_t)B * Hkv);
     }
     const int64_t max_s = ceil_div(L_cap, 256);  // no split shorter than 256 keys
@@ -161,6 +170,7 @@ struct FusedOut {
     float* blk_o;
     float* blk_m;
     float* blk_l;
+    size_t clear_bytes;  // > 0: zero this many bytes of counters before a fused launch
 };
 
 // Splits per first-level ticket block of the fused merge: one level up to 32
@@ -282,6 +292,10 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
         p.out_sh = fused->out->stride_h;
         p.lse = fused->lse;
         *used_fused = true;
+        if (fused->clear_bytes) {
+            e = attn::launch_zero(fused->counters, fused->clear_bytes, stream);
+            if (e != hipSuccess) return fail(ATTN_ERR_HIP, "clearing the merge counters: %s", hipGetErrorString(e));
+        }
     }
     if (mfma) e = attn::launch_decode_mfma(p, fp8 ? attn::DT_FP8 : attn::DT_BF16, stream);
     else e = attn::launch_decode_valu(p, q->dtype, k->dtype, G, stream);
@@ -290,29 +304,51 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
 }
 
 
-// Automatic split plan of a two-span launch: two resident workgroups per
-// compute unit in all, shared in proportion to keys * cost, every split at
-// least 256 keys long. Returns S0 + S1 (after planning), 0 on failure.
-int two_span_splits(int B, int Hkv, int L0, double cost0, int L1, double cost1, int* s0, int* s1) {
+// Automatic split plan of a launch over n spans (n <= 3): two resident
+// workgroups per compute unit in all, shared in proportion to keys * cost,
+// every split at least 256 keys long. Stores each span's splits (after
+// planning) in S[i] and returns their sum, 0 on failure.
+int span_splits(int B, int Hkv, int n, const int* L, const double* cost, int* S) {
     const int cus = device_cu_count();
-    if (cus <= 0 || L0 + L1 <= 0) return 0;
+    int64_t keys = 0;
+    double W = 0.0;
+    int last = -1;  // the last span with keys takes what the others leave
+    for (int i = 0; i < n; ++i) {
+        keys += L[i];
+        W += cost[i] * L[i];
+        if (L[i]) last = i;
+    }
+    if (cus <= 0 || keys <= 0) return 0;
     int64_t T = (2LL * cus) / ((int64_t)B * Hkv);
-    if (T < 2) T = 2;
-    const double w0 = cost0 * L0, w1 = cost1 * L1;
-    int64_t r0 = L0 ? (int64_t)llround((double)T * w0 / (w0 + w1)) : 0;
-    int64_t r1 = L1 ? T - r0 : 0;
-    auto clamp = [](int64_t r, int L) -> int64_t {
-        if (!L) return 0;
-        const int64_t max_s = ceil_div(L, 256);
-        return r < 1 ? 1 : (r > max_s ? max_s : r);
-    };
-    r0 = clamp(r0, L0);
-    r1 = clamp(r1, L1);
-    const int S0 = L0 ? plan_splits(L0, (int)r0).S : 0;
-    const int S1 = L1 ? plan_splits(L1, (int)r1).S : 0;
-    if (s0) *s0 = S0;
-    if (s1) *s1 = S1;
-    return S0 + S1;
+    if (T < n) T = n;
+    int64_t r[3] = {0, 0, 0}, given = 0;
+    for (int i = 0; i < n; ++i) {
+        if (!L[i] || i == last) continue;
+        r[i] = (int64_t)llround((double)T * cost[i] * L[i] / W);
+        given += r[i];
+    }
+    r[last] = T - given;
+    int total = 0;
+    for (int i = 0; i < n; ++i) {
+        S[i] = 0;
+        if (!L[i]) continue;
+        const int64_t max_s = ceil_div(L[i], 256);
+        const int64_t ri = r[i] < 1 ? 1 : (r[i] > max_s ? max_s : r[i]);
+        S[i] = plan_splits(L[i], (int)ri).S;
+        total += S[i];
+    }
+    return total;
+}
+
+int two_span_splits(int B, int Hkv, int L0, double cost0, int L1, double cost1, int* s0, int* s1) {
+    const int L[2] = {L0, L1};
+    const double c[2] = {cost0, cost1};
+    int S[2];
+    const int total = span_splits(B, Hkv, 2, L, c, S);
+    if (total <= 0) return 0;
+    if (s0) *s0 = S[0];
+    if (s1) *s1 = S[1];
+    return total;
 }
 
 // Most keys each pi-Attention span can hold for a decode query at position
@@ -372,9 +408,10 @@ attn::DecodeParams two_span_params(const attn_tensor* q, int B, int Hq, int Hkv,
 }
 
 // Workspace layout (that of attn_decode with S splits), the fused-merge
-// decision, the launch, and the separate merge when not fused.
+// decision, the launch (two spans, or three when prec2 >= 0), and the
+// separate merge when not fused.
 attn_status two_span_launch(attn::DecodeParams& p, int S, int prec0, int prec1, attn_tensor* out, float* lse,
-                            void* workspace, size_t workspace_bytes, hipStream_t hs) {
+                            void* workspace, size_t workspace_bytes, hipStream_t hs, int prec2 = -1) {
     const int B = p.B, Hq = p.Hq, Hkv = p.Hkv, d = p.d;
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
     if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -412,7 +449,8 @@ attn_status two_span_launch(attn::DecodeParams& p, int S, int prec0, int prec1, 
         p.out_sh = out->stride_h;
         p.lse = lse;
     }
-    hipError_t e = attn::launch_decode_mfma_two(p, prec0, prec1, hs);
+    hipError_t e = prec2 < 0 ? attn::launch_decode_mfma_two(p, prec0, prec1, hs)
+                             : attn::launch_decode_mfma_three(p, prec0, prec1, prec2, hs);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     if (fused) return ATTN_OK;
 
@@ -519,8 +557,27 @@ attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_t
                         const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int d, int L_cap,
                         float softmax_scale, int causal, int num_splits, attn_tensor* out, float* lse,
                         void* workspace, size_t workspace_bytes, void* stream) {
-    (void)causal;  // one query aligned bottom-right sees every valid key
     g_last_error[0] = 0;
+    return attn::decode_impl(q, k, v, k_scale, v_scale, kv_lens, B, Hq, Hkv, d, L_cap, softmax_scale, causal,
+                             num_splits, out, lse, workspace, workspace_bytes, 0, stream);
+}
+
+}  // extern "C"
+
+namespace attn {
+
+void set_last_error(const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+}
+
+attn_status decode_impl(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const float* k_scale,
+                        const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int d, int L_cap,
+                        float softmax_scale, int causal, int num_splits, attn_tensor* out, float* lse,
+                        void* workspace, size_t workspace_bytes, size_t clear_counter_bytes, void* stream) {
+    (void)causal;  // one query aligned bottom-right sees every valid key
     if (!out) return fail(ATTN_ERR_INVALID_ARG, "out: null tensor");
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
     if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
@@ -541,7 +598,7 @@ attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_t
     float* blk_l = blk_m + rows * attn::kMaxTicketBlocks;
     hipStream_t hs = static_cast<hipStream_t>(stream);
     Plan pl{0, 0};
-    const FusedOut fo{counters, out, lse, blk_o, blk_m, blk_l};
+    const FusedOut fo{counters, out, lse, blk_o, blk_m, blk_l, clear_counter_bytes};
     bool fused = false;
     const size_t fixed = attn::kCounterBytes + partial_bytes(rows, attn::kMaxTicketBlocks, d > 0 ? d : 0);
     if (workspace_bytes < fixed)
@@ -571,6 +628,10 @@ attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_t
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "combine launch: %s", hipGetErrorString(e));
     return ATTN_OK;
 }
+
+}  // namespace attn
+
+extern "C" {
 
 attn_status attn_decode_partials(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                                  const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B, int Hq,
@@ -678,10 +739,7 @@ attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, con
 
 int attn_decode_mixed_fp4_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi, int* splits_lo) {
     if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0) return 0;
-    // cost per key: the fp4 span is bound by its vector work (widening and
-    // P.V per key), not by its bytes, so a key costs nearly what a bf16 key
-    // does (128K-key sweep: 12-16 + 48-52 splits fastest)
-    return two_span_splits(B, Hkv, L_hi_cap, 2.0, L_lo_cap, 1.8, splits_hi, splits_lo);
+    return two_span_splits(B, Hkv, L_hi_cap, 2.0, L_lo_cap, kFp4Cost, splits_hi, splits_lo);
 }
 
 // An E8M0 scale array [B, Hkv, L, d/32] read as one 4-byte word per row.
@@ -726,7 +784,7 @@ attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tensor* k_hi,
             return fail(ATTN_ERR_UNSUPPORTED, "the low-precision span must be ATTN_MXFP4");
         if ((st = check_scales(k_lo_scale, "k_lo_scale")) || (st = check_scales(v_lo_scale, "v_lo_scale")))
             return st;
-        // the kernel steps through a 16-row tile with 32-bit offsets
+        // the kernel steps through a 32-row tile with 32-bit offsets
         const int64_t lim = int64_t(1) << 26;
         if (k_lo->stride_s >= lim || v_lo->stride_s >= lim || k_lo_scale->stride_s >= lim ||
             v_lo_scale->stride_s >= lim)
@@ -761,6 +819,101 @@ attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tensor* k_hi,
     }
     return two_span_launch(p, ph.S + plo.S, kPrecBf16, kPrecFp4, out, lse, workspace, workspace_bytes,
                            static_cast<hipStream_t>(stream));
+}
+
+int attn_decode_mixed3_splits(int B, int Hkv, int L_hi_cap, int L_mid_cap, int L_lo_cap, int* splits_hi,
+                              int* splits_mid, int* splits_lo) {
+    if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_mid_cap < 0 || L_lo_cap < 0 ||
+        (int64_t)L_hi_cap + L_mid_cap + L_lo_cap <= 0)
+        return 0;
+    // the costs per key of the two-span plans: bf16 2, fp8 1.3, fp4 (see
+    // attn_decode_mixed_fp4_splits)
+    const int L[3] = {L_hi_cap, L_mid_cap, L_lo_cap};
+    const double c[3] = {2.0, 1.3, kFp4Cost};
+    int S[3];
+    const int total = span_splits(B, Hkv, 3, L, c, S);
+    if (total <= 0) return 0;
+    if (splits_hi) *splits_hi = S[0];
+    if (splits_mid) *splits_mid = S[1];
+    if (splits_lo) *splits_lo = S[2];
+    return total;
+}
+
+attn_status attn_decode_mixed3(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
+                               const int32_t* hi_lens, int L_hi_cap, const attn_tensor* k_mid,
+                               const attn_tensor* v_mid, const float* k_mid_scale, const float* v_mid_scale,
+                               const int32_t* mid_lens, int L_mid_cap, const attn_tensor* k_lo,
+                               const attn_tensor* v_lo, const attn_tensor* k_lo_scale, const attn_tensor* v_lo_scale,
+                               const int32_t* lo_lens, int L_lo_cap, int B, int Hq, int Hkv, int d,
+                               float softmax_scale, int num_splits_hi, int num_splits_mid, int num_splits_lo,
+                               attn_tensor* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+    g_last_error[0] = 0;
+    attn_status st;
+    if ((st = check_tensor(q, "q", true)) || (st = check_tensor(out, "out", false))) return st;
+    if (B <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "sizes must be positive (B=%d Hq=%d Hkv=%d d=%d)", B, Hq, Hkv, d);
+    if (L_hi_cap < 0 || L_mid_cap < 0 || L_lo_cap < 0 || (int64_t)L_hi_cap + L_mid_cap + L_lo_cap <= 0)
+        return fail(ATTN_ERR_INVALID_ARG, "span capacities must be >= 0 and not all 0 (%d, %d, %d)", L_hi_cap,
+                    L_mid_cap, L_lo_cap);
+    if (B > 65535 || Hkv > 65535) return fail(ATTN_ERR_INVALID_ARG, "B and Hkv must be <= 65535");
+    if (Hq % Hkv) return fail(ATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+    if (num_splits_hi < 0 || num_splits_mid < 0 || num_splits_lo < 0)
+        return fail(ATTN_ERR_INVALID_ARG, "split counts must be >= 0");
+    if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
+    if (L_hi_cap) {
+        if ((st = check_tensor(k_hi, "k_hi", true)) || (st = check_tensor(v_hi, "v_hi", true))) return st;
+        if (k_hi->dtype != ATTN_BF16 || v_hi->dtype != ATTN_BF16)
+            return fail(ATTN_ERR_UNSUPPORTED, "the high-precision span must be bf16");
+    }
+    if (L_mid_cap) {
+        if ((st = check_tensor(k_mid, "k_mid", true)) || (st = check_tensor(v_mid, "v_mid", true))) return st;
+        if (k_mid->dtype != ATTN_FP8_E4M3 || v_mid->dtype != ATTN_FP8_E4M3)
+            return fail(ATTN_ERR_UNSUPPORTED, "the middle span must be fp8 e4m3");
+        if (!k_mid_scale || !v_mid_scale) return fail(ATTN_ERR_INVALID_ARG, "the fp8 span needs its scales");
+    }
+    if (L_lo_cap) {
+        if ((st = check_tensor(k_lo, "k_lo", true)) || (st = check_tensor(v_lo, "v_lo", true))) return st;
+        if (k_lo->dtype != ATTN_MXFP4 || v_lo->dtype != ATTN_MXFP4)
+            return fail(ATTN_ERR_UNSUPPORTED, "the low-precision span must be ATTN_MXFP4");
+        if ((st = check_scales(k_lo_scale, "k_lo_scale")) || (st = check_scales(v_lo_scale, "v_lo_scale")))
+            return st;
+        const int64_t lim = int64_t(1) << 26;  // 32-row fp4 tiles with 32-bit offsets
+        if (k_lo->stride_s >= lim || v_lo->stride_s >= lim || k_lo_scale->stride_s >= lim ||
+            v_lo_scale->stride_s >= lim)
+            return fail(ATTN_ERR_INVALID_ARG, "fp4 span row strides must be below 64 MiB");
+    }
+    if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode takes bf16 q and out");
+    if (d != 128 || Hq != 4 * Hkv)
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+
+    int a[3] = {0, 0, 0};
+    if ((!num_splits_hi && L_hi_cap) || (!num_splits_mid && L_mid_cap) || (!num_splits_lo && L_lo_cap)) {
+        if (attn_decode_mixed3_splits(B, Hkv, L_hi_cap, L_mid_cap, L_lo_cap, &a[0], &a[1], &a[2]) <= 0)
+            return fail(ATTN_ERR_HIP, "could not query the device for the split plan");
+    }
+    const Plan ph = L_hi_cap ? plan_splits(L_hi_cap, num_splits_hi ? num_splits_hi : a[0]) : Plan{kChunkQuantum, 0};
+    const Plan pm = L_mid_cap ? plan_splits(L_mid_cap, num_splits_mid ? num_splits_mid : a[1]) : Plan{kChunkQuantum, 0};
+    const Plan pl = L_lo_cap ? plan_splits(L_lo_cap, num_splits_lo ? num_splits_lo : a[2]) : Plan{kChunkQuantum, 0};
+
+    attn::DecodeParams p = two_span_params(q, B, Hq, Hkv, d, softmax_scale, k_mid_scale, v_mid_scale);
+    p.S0 = ph.S;
+    p.S1 = ph.S + pm.S;
+    p.sp0 = span_of(k_hi, v_hi, hi_lens, Hkv, L_hi_cap, ph.chunk);
+    p.sp1 = span_of(k_mid, v_mid, mid_lens, Hkv, L_mid_cap, pm.chunk);
+    p.sp2 = span_of(k_lo, v_lo, lo_lens, Hkv, L_lo_cap, pl.chunk);  // strides of byte tensors: bytes
+    if (L_lo_cap) {
+        p.sp2.k_sc = k_lo_scale->data;
+        p.sp2.ksc_sb = k_lo_scale->stride_b;
+        p.sp2.ksc_sh = k_lo_scale->stride_h;
+        p.sp2.ksc_ss = k_lo_scale->stride_s;
+        p.sp2.v_sc = v_lo_scale->data;
+        p.sp2.vsc_sb = v_lo_scale->stride_b;
+        p.sp2.vsc_sh = v_lo_scale->stride_h;
+        p.sp2.vsc_ss = v_lo_scale->stride_s;
+    }
+    return two_span_launch(p, ph.S + pm.S + pl.S, kPrecBf16, kPrecFp8, out, lse, workspace, workspace_bytes,
+                           static_cast<hipStream_t>(stream), kPrecFp4);
 }
 
 int attn_decode_pi_splits(int B, int Hkv, int L_cap, int window, int period, int kv_dtype, int* splits_window,

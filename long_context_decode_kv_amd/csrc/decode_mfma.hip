@@ -82,13 +82,6 @@ struct Tile<kFp8> {
     u32x4 k[2];  // key row 8i + (lane>>3), bytes 16*(lane & 7) .. +15 (coalesced rows)
     u32x2 v[4];  // key 4*(lane>>4) + u: 8 fp8 at dims 8*(lane & 15)
 };
-template <>
-struct Tile<kFp4> {
-    u32x4 k;         // key row lane>>2, bytes 16*(lane & 3) .. +15: the 32 codes of block lane & 3
-    uint32_t ks;     // the four block scales of key row lane & 15 (byte i: block i)
-    uint32_t v[4];   // key 4*(lane>>4) + u: 8 codes at dims 8*(lane & 15)
-    uint32_t vs[4];  // the four block scales of that key
-};
 
 // Rows of an MX fp4 span's scale arrays (unused for the other precisions).
 struct ScaleRows {
@@ -111,63 +104,42 @@ __device__ __forceinline__ T ld_stream(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
-// Loads one 16-key tile; key indices past `tlast` are clamped to it, so every
-// address stays inside the cache and the clamped keys are masked later.
+// Loads one 16-key tile (bf16 or fp8); key indices past `tlast` are clamped to
+// it, so every address stays inside the cache and the clamped keys are masked
+// later.
 template <int P>
 __device__ __forceinline__ void load_tile(Tile<P>& t, const char* kbase, const char* vbase, int64_t kss,
-                                          int64_t vss, const ScaleRows& sc, int tok0, int tlast, int lane) {
-    if constexpr (P == kFp4) {
-        // the tile's first row in wide arithmetic (uniform), the lanes' rows
-        // as 32-bit offsets from it (a span's row strides are far below 2^27)
-        const int last = tlast - tok0;
-        const char* kt = kbase + (int64_t)tok0 * kss;
-        const char* vt = vbase + (int64_t)tok0 * vss;
-        const char* kst = sc.k + (int64_t)tok0 * sc.kss;
-        const char* vst = sc.v + (int64_t)tok0 * sc.vss;
-        const int ik = (int)kss, iv = (int)vss, iks = (int)sc.kss, ivs = (int)sc.vss;
-        t.k = ld_stream<u32x4>(kt + min(lane >> 2, last) * ik + 16 * (lane & 3));
-        t.ks = ld_stream<uint32_t>(kst + min(lane & 15, last) * iks);
+                                          int64_t vss, int tok0, int tlast, int lane) {
+    if constexpr (P == kBf16) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int rv = min(4 * (lane >> 4) + u, last);
-            t.v[u] = ld_stream<uint32_t>(vt + rv * iv + 4 * (lane & 15));
-            t.vs[u] = ld_stream<uint32_t>(vst + rv * ivs);
+        for (int i = 0; i < 4; ++i) {
+            const int rk = min(tok0 + 4 * i + (lane >> 4), tlast);
+            t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 15));
         }
     } else {
-        if constexpr (P == kBf16) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int rk = min(tok0 + 4 * i + (lane >> 4), tlast);
-                t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 15));
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int rk = min(tok0 + 8 * i + (lane >> 3), tlast);
-                t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 7));
-            }
+        for (int i = 0; i < 2; ++i) {
+            const int rk = min(tok0 + 8 * i + (lane >> 3), tlast);
+            t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 7));
         }
+    }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
-            const char* vrow = vbase + (int64_t)rv * vss;
-            if constexpr (P == kBf16) t.v[u] = ld_stream<u32x4>(vrow + 2 * 8 * (lane & 15));
-            else t.v[u] = ld_stream<u32x2>(vrow + 8 * (lane & 15));
-        }
+    for (int u = 0; u < 4; ++u) {
+        const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
+        const char* vrow = vbase + (int64_t)rv * vss;
+        if constexpr (P == kBf16) t.v[u] = ld_stream<u32x4>(vrow + 2 * 8 * (lane & 15));
+        else t.v[u] = ld_stream<u32x2>(vrow + 8 * (lane & 15));
     }
 }
 
 // The K tile passes through a wave-private LDS stage to change from row-major
 // lanes to the MFMA operand layout (lane = key row, 16 bytes of dims). 16-byte
 // chunks are XOR-swizzled by row so both the row writes and the column reads
-// touch every bank once per 16 lanes. (fp4: four 16-byte chunks per row, chunk
-// c of row r at c ^ (r >> 2); the operand reads are 4-byte words, word g of
-// chunk i for row r, which then cover all 64 banks.)
+// touch every bank once per 16 lanes.
 template <int P>
 __device__ __forceinline__ int kstage_index(int row, int chunk) {
     if constexpr (P == kBf16) return row * 16 + (chunk ^ (row & 15));
-    else if constexpr (P == kFp8) return row * 8 + (chunk ^ ((row >> 1) & 7));
-    else return row * 4 + (chunk ^ (row >> 2));
+    else return row * 8 + (chunk ^ ((row >> 1) & 7));
 }
 
 template <int P>
@@ -175,11 +147,9 @@ __device__ __forceinline__ void stage_k(const Tile<P>& t, u32x4* ks, int lane) {
     if constexpr (P == kBf16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) ks[kstage_index<kBf16>(4 * i + (lane >> 4), lane & 15)] = t.k[i];
-    } else if constexpr (P == kFp8) {
+    } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) ks[kstage_index<kFp8>(8 * i + (lane >> 3), lane & 7)] = t.k[i];
-    } else {
-        ks[kstage_index<kFp4>(lane >> 2, lane & 3)] = t.k;
     }
 }
 
@@ -205,10 +175,7 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 template <int P>
 __device__ __forceinline__ void v_to_f32(const Tile<P>& t, int u, int lane, float (&vf)[8]) {
-    if constexpr (P == kFp4) {
-        // dims 8*(lane & 15) .. +7 lie in block (lane & 15) >> 2
-        fp4x8_to_f32(t.v[u], e8m0_to_f32(t.vs[u] >> (8 * ((lane & 15) >> 2))), vf);
-    } else if constexpr (P == kBf16) {
+    if constexpr (P == kBf16) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             vf[2 * e] = bf16_lo(t.v[u][e]);
@@ -234,29 +201,16 @@ __device__ __forceinline__ void compute_tile(const Tile<P>& t, u32x4* ks, const 
     stage_k<P>(t, ks, lane);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int row = lane & 15;
-    if constexpr (P == kFp4) {
-        // MFMA step i is block i (dims 32i .. 32i + 31): this lane's eight
-        // codes, dims 32i + 8*(lane >> 4) .., widened with the block's scale
-        const uint32_t* ks32 = reinterpret_cast<const uint32_t*>(ks);
+    if constexpr (P == kBf16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float f[8];
-            fp4x8_to_f32(ks32[4 * kstage_index<kFp4>(row, i) + (lane >> 4)], e8m0_to_f32(t.ks >> (8 * i)), f);
-            bf16x8 a;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) a[e] = (__bf16)f[e];  // exact: two significant bits
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], acc, 0, 0, 0);
-        }
-    } else if constexpr (P == kBf16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 a = ks[kstage_index<false>(row, 4 * i + (lane >> 4))];
+            const u32x4 a = ks[kstage_index<kBf16>(row, 4 * i + (lane >> 4))];
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qop[i], acc, 0, 0, 0);
         }
     } else {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const u32x4 a = ks[kstage_index<true>(row, 4 * h + (lane >> 4))];
+            const u32x4 a = ks[kstage_index<kFp8>(row, 4 * h + (lane >> 4))];
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[0], a[1]), qop[2 * h], acc, 0, 0, 0);
             acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[2], a[3]), qop[2 * h + 1], acc, 0, 0,
                                                           0);
@@ -296,6 +250,143 @@ __device__ __forceinline__ void compute_tile(const Tile<P>& t, u32x4* ks, const 
 #pragma unroll
             for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pb[h], vf[e], o[h][e]);
     }
+}
+
+// ---- The MX fp4 span: 32-key tiles per wave, both products on the MFMA.
+//
+// Scores: S^T = K Q^T as two v_mfma_f32_16x16x32_bf16 chains over d (step i
+// is scale block i, dims 32i .. 32i + 31). Product a takes the tile's keys
+// 8(m >> 2) + (m & 3) as its A rows m, product b those keys + 4, so lane l
+// receives head l & 3 of keys 8(l >> 4) + r (from a) and 8(l >> 4) + 4 + r
+// (from b), r < 4: the eight keys 8(l >> 4) .. +7 that the same lane feeds to
+// the P.V product as its B operand. No lane exchange is needed between the two
+// products.
+// P.V: O^T = V^T P^T as eight products j = 0..7 over the 32 keys. Product j's
+// A row m is dim 8m + j (lane l holds those of the eight codes it loaded per
+// key, dims 8(l & 15) .. +7), its B column n is head n & 3 (the four heads
+// repeat across the 16 columns, as in the scores), so lane l ends with head
+// l & 3 at dims 32(l >> 4) + 8r + j in acc[j][r].
+// Codes widen exactly to fp32 with the block scale applied (gfx950's scaled
+// fp4 conversion; a one-bit mantissa times a power of two) and then exactly to
+// bf16; P is rounded to bf16 for the MFMA, the sum l takes the fp32 weights.
+// The running max is shared by the 16 lanes of a head, because every product
+// sums over all lanes' keys.
+constexpr int kTile4 = 32;
+struct Fp4Tile {
+    u32x4 k[2];      // key rows lane >> 2 and 16 + (lane >> 2): 16-byte chunk lane & 3 (32 codes, block lane & 3)
+    uint32_t ks[2];  // scale words of key rows fp4_row_a(lane & 15) and that + 4 (byte i: block i)
+    uint32_t v[8];   // key 8*(lane >> 4) + u: its 8 codes at dims 8*(lane & 15) .. +7
+    uint32_t vs[8];  // that key's scale word
+};
+
+// The tile row score product a takes as its A row m.
+__device__ __forceinline__ int fp4_row_a(int m) { return 8 * (m >> 2) + (m & 3); }
+
+// K stage of a 32-row tile (four 16-byte chunks a row, u32x4 units): chunk c
+// of row r at c ^ ((r >> 3) & 3). The operand reads (4-byte word g = lane >> 4
+// of chunk i of row fp4_row_a(lane & 15), or that + 4) then hit 64 distinct
+// banks.
+__device__ __forceinline__ int kidx4(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 3) & 3)); }
+
+__device__ __forceinline__ void load_fp4(Fp4Tile& t, const char* kbase, const char* vbase, int64_t kss, int64_t vss,
+                                         const ScaleRows& sc, int tok0, int tlast, int lane) {
+    // the tile's first row in wide arithmetic (uniform), the lanes' rows as
+    // 32-bit offsets from it (the host keeps a span's row strides below 2^26)
+    const int last = tlast - tok0;
+    const char* kt = kbase + (int64_t)tok0 * kss;
+    const char* vt = vbase + (int64_t)tok0 * vss;
+    const char* kst = sc.k + (int64_t)tok0 * sc.kss;
+    const char* vst = sc.v + (int64_t)tok0 * sc.vss;
+    const int ik = (int)kss, iv = (int)vss, iks = (int)sc.kss, ivs = (int)sc.vss;
+    t.k[0] = ld_stream<u32x4>(kt + min(lane >> 2, last) * ik + 16 * (lane & 3));
+    t.k[1] = ld_stream<u32x4>(kt + min(16 + (lane >> 2), last) * ik + 16 * (lane & 3));
+    const int ra = fp4_row_a(lane & 15);
+    t.ks[0] = ld_stream<uint32_t>(kst + min(ra, last) * iks);
+    t.ks[1] = ld_stream<uint32_t>(kst + min(ra + 4, last) * iks);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int rv = min(8 * (lane >> 4) + u, last);
+        t.v[u] = ld_stream<uint32_t>(vt + rv * iv + 4 * (lane & 15));
+        t.vs[u] = ld_stream<uint32_t>(vst + rv * ivs);
+    }
+}
+
+// P.V products 2 SEL and 2 SEL + 1: codes 2 SEL and 2 SEL + 1 of every key
+// (dims 8m + 2 SEL and 8m + 2 SEL + 1 of A row m).
+template <int SEL>
+__device__ __forceinline__ void fp4_pv_pair(const Fp4Tile& t, const float (&sc)[8], const bf16x8& pb, f32x4& acc0,
+                                            f32x4& acc1) {
+    bf16x8 a0, a1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const f32x2 x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.v[u], sc[u], SEL);
+        a0[u] = (__bf16)x[0];
+        a1[u] = (__bf16)x[1];
+    }
+    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, pb, acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, pb, acc1, 0, 0, 0);
+}
+
+__device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const bf16x8 (&qop)[4], float scale2, int tok0,
+                                         int tend, int lane, float& m_run, float& l_run, f32x4 (&acc)[8]) {
+    ks[kidx4(lane >> 2, lane & 3)] = t.k[0];
+    ks[kidx4(16 + (lane >> 2), lane & 3)] = t.k[1];
+    const uint32_t* ks32 = reinterpret_cast<const uint32_t*>(ks);
+    const int g = lane >> 4, ra = fp4_row_a(lane & 15);
+    f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        float f[8];
+        bf16x8 a;
+        fp4x8_to_f32(ks32[4 * kidx4(ra, i) + g], e8m0_to_f32(t.ks[0] >> (8 * i)), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)f[e];  // exact: two significant bits
+        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], sa, 0, 0, 0);
+        fp4x8_to_f32(ks32[4 * kidx4(ra + 4, i) + g], e8m0_to_f32(t.ks[1] >> (8 * i)), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = (__bf16)f[e];
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], sb, 0, 0, 0);
+    }
+    const int kb = tok0 + 8 * g;
+    float s[8];
+    float tmax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        s[r] = (kb + r < tend) ? sa[r] * scale2 : kNegInf;
+        s[4 + r] = (kb + 4 + r < tend) ? sb[r] * scale2 : kNegInf;
+        tmax = fmaxf(tmax, fmaxf(s[r], s[4 + r]));
+    }
+    if (__builtin_amdgcn_ballot_w64(tmax > m_run + kHeadroom) != 0) {
+        // the new running max of each head: over the 16 lanes with its lane & 3
+        float hm = fmaxf(tmax, __shfl_xor(tmax, 4));
+        hm = fmaxf(hm, __shfl_xor(hm, 8));
+        hm = fmaxf(hm, __shfl_xor(hm, 16));
+        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        const float m_new = fmaxf(m_run, hm);
+        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= alpha;
+    }
+    bf16x8 pb;
+    float lsum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const float pu = (s[u] == kNegInf) ? 0.f : fast_exp2(s[u] - m_run);
+        lsum += pu;
+        pb[u] = (__bf16)pu;
+    }
+    l_run += lsum;
+    // dims 8*(lane & 15) .. +7 lie in scale block (lane & 15) >> 2
+    const int sh = 8 * ((lane & 15) >> 2);
+    float sc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sc[u] = e8m0_to_f32(t.vs[u] >> sh);
+    fp4_pv_pair<0>(t, sc, pb, acc[0], acc[1]);
+    fp4_pv_pair<1>(t, sc, pb, acc[2], acc[3]);
+    fp4_pv_pair<2>(t, sc, pb, acc[4], acc[5]);
+    fp4_pv_pair<3>(t, sc, pb, acc[6], acc[7]);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -390,8 +481,8 @@ __device__ __forceinline__ void merge4(const float* o, const float* m, const flo
 }
 
 // Level 2, fused: a tree over the splits of each (b, g) group. Every
-// workgroup publishes its partial (agent-scope stores, waited for), then takes
-// a ticket in its block of `ticket_block` splits; the last of a block merges
+// workgroup publishes its partial (agent-scope stores, released at agent
+// scope), then takes a ticket in its block of `ticket_block` splits; the last of a block merges
 // the block into a block partial and, if there are several blocks, takes a
 // ticket on the group; the last block merges the block partials into O and
 // lse. Counters are reset by their last user. The tree shape is a function of
@@ -405,16 +496,21 @@ __device__ __forceinline__ void merge_group_if_last(const DecodeParams& p, int b
     const int in_block = min(k, n - bi * k);
     uint32_t* line = p.counters + (int64_t)(b * p.Hkv + g) * (1 + kMaxTicketBlocks) * kCounterStride;
     const int64_t row0 = (int64_t)b * p.Hq + g * 4;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's partial stores are complete
+    // The barrier orders every thread's partial stores before thread 0's
+    // ticket, which releases them at agent scope (happens-before is
+    // transitive across the two scopes); the threads of the workgroup that
+    // draws the last ticket acquire at agent scope before they read the other
+    // workgroups' partials.
     __syncthreads();
     if (tid == 0) {
         uint32_t* blk = line + (1 + bi) * kCounterStride;
-        const uint32_t o1 = __hip_atomic_fetch_add(blk, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t o1 = __hip_atomic_fetch_add(blk, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         role = (o1 == (uint32_t)(in_block - 1)) ? 1 : 0;
         if (role) __hip_atomic_store(blk, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!role) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int lane = tid & 63, h = tid >> 6;
     // level 2a: this block's splits
     merge4(p.o_part + (row0 * p.S + bi * k) * 128, p.m_part + row0 * p.S + bi * k, p.l_part + row0 * p.S + bi * k,
@@ -431,15 +527,15 @@ __device__ __forceinline__ void merge_group_if_last(const DecodeParams& p, int b
             st_agent(p.blk_m + (row0 + h) * kMaxTicketBlocks + bi, sm.red[h][0]);
             st_agent(p.blk_l + (row0 + h) * kMaxTicketBlocks + bi, sm.red[h][1]);
         }
-        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
-            const uint32_t o2 = __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t o2 = __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
             role = (o2 == (uint32_t)(nb - 1)) ? 2 : 0;
             if (role) __hip_atomic_store(line, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();
         if (!role) return;
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         // level 2b: the block partials
         merge4(p.blk_o + row0 * kMaxTicketBlocks * 128, p.blk_m + row0 * kMaxTicketBlocks,
                p.blk_l + row0 * kMaxTicketBlocks, kMaxTicketBlocks, nb, tid, sm);
@@ -554,80 +650,106 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
     }
 
     float m_run = kNegInf, l_run = 0.f;
-    float o[4][8];
-#pragma unroll
-    for (int h = 0; h < 4; ++h)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-
-    // Tile buffers used in turn: the next tile is in flight while the current
-    // one is computed -- the next two for MX fp4, whose 16-key tiles hold a
-    // quarter of a bf16 tile's bytes.
     u32x4* ks = lds.kstage[w];
     int k = w;
-    if (P == kFp4 && k < ntiles) {
-        Tile<P> ta, tb, tc;
-        load_tile<P>(ta, kbase, vbase, kss, vss, sc, t_begin + kTile * k, t_end - 1, lane);
-        if (k + kWaves < ntiles)
-            load_tile<P>(tb, kbase, vbase, kss, vss, sc, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-        // ahead <- tile k + 2 kWaves; compute cur (tile k); false when done
-        auto step = [&](Tile<P>& cur, Tile<P>& ahead) __attribute__((always_inline)) {
-            if (k + 2 * kWaves < ntiles)
-                load_tile<P>(ahead, kbase, vbase, kss, vss, sc, t_begin + kTile * (k + 2 * kWaves), t_end - 1, lane);
-            compute_tile<P>(cur, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
-            k += kWaves;
-            return k < ntiles;
-        };
-        while (step(ta, tc) && step(tb, ta) && step(tc, tb)) {
-        }
-    } else if (k < ntiles) {
-        Tile<P> ta, tb;
-        load_tile<P>(ta, kbase, vbase, kss, vss, sc, t_begin + kTile * k, t_end - 1, lane);
-        while (true) {
-            const bool more_b = k + kWaves < ntiles;
-            if (more_b) load_tile<P>(tb, kbase, vbase, kss, vss, sc, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-            compute_tile<P>(ta, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
-            if (!more_b) break;
-            k += kWaves;
-            const bool more_a = k + kWaves < ntiles;
-            if (more_a) load_tile<P>(ta, kbase, vbase, kss, vss, sc, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-            compute_tile<P>(tb, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
-            if (!more_a) break;
-            k += kWaves;
-        }
-    }
-
-    // Level 1a: merge the four lane groups (keys 4*(lane>>4)..) of this wave.
-    float M = fmaxf(m_run, __shfl_xor(m_run, 16));
-    M = fmaxf(M, __shfl_xor(M, 32));
-    const float f = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - M);
-    float lw = l_run * f;
-    lw += __shfl_xor(lw, 16);
-    lw += __shfl_xor(lw, 32);
-    {
-        const float fh[4] = {quad_bcast<0>(f), quad_bcast<1>(f), quad_bcast<2>(f), quad_bcast<3>(f)};
+    if constexpr (P == kFp4) {
+        // 32-key tiles, both products on the MFMA (fp4_tile); two tiles in flight
+        const int ntiles4 = (t_end - t_begin + kTile4 - 1) / kTile4;
+        f32x4 acc[8];
 #pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float x = o[h][e] * fh[h];
-                x += __shfl_xor(x, 16);
-                x += __shfl_xor(x, 32);
-                o[h][e] = x;
+        for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (k < ntiles4) {
+            Fp4Tile ta, tb;
+            load_fp4(ta, kbase, vbase, kss, vss, sc, t_begin + kTile4 * k, t_end - 1, lane);
+            while (true) {
+                const bool more_b = k + kWaves < ntiles4;
+                if (more_b) load_fp4(tb, kbase, vbase, kss, vss, sc, t_begin + kTile4 * (k + kWaves), t_end - 1, lane);
+                fp4_tile(ta, ks, qop, scale2, t_begin + kTile4 * k, t_end, lane, m_run, l_run, acc);
+                if (!more_b) break;
+                k += kWaves;
+                const bool more_a = k + kWaves < ntiles4;
+                if (more_a) load_fp4(ta, kbase, vbase, kss, vss, sc, t_begin + kTile4 * (k + kWaves), t_end - 1, lane);
+                fp4_tile(tb, ks, qop, scale2, t_begin + kTile4 * k, t_end, lane, m_run, l_run, acc);
+                if (!more_a) break;
+                k += kWaves;
             }
-    }
-
-    // Level 1b: merge the four waves in LDS.
-    if (lane < 16) {
+        }
+        // The MFMA summed over every key of the wave, so the wave's partial is
+        // complete: lane l holds head l & 3 at dims 32*(l>>4) + 8r + j (acc[j][r]),
+        // the same in the four lanes with equal l & 3 and l >> 4; l_run counts
+        // the keys of lane group l >> 4 once per lane of a head.
+        float lw = l_run + __shfl_xor(l_run, 16);
+        lw += __shfl_xor(lw, 32);
+        if ((lane & 12) == 0) {
+            float* orow = lds.o[w][lane & 3] + 32 * (lane >> 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) orow[8 * r + j] = acc[j][r];
+        }
+        if (lane < 4) {
+            lds.m[w][lane] = m_run;
+            lds.l[w][lane] = lw;
+        }
+    } else {
+        float o[4][8];
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) lds.o[w][h][8 * lane + e] = o[h][e];
+            for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
+
+        // Tile buffers used in turn: the next tile is in flight while the
+        // current one is computed.
+        if (k < ntiles) {
+            Tile<P> ta, tb;
+            load_tile<P>(ta, kbase, vbase, kss, vss, t_begin + kTile * k, t_end - 1, lane);
+            while (true) {
+                const bool more_b = k + kWaves < ntiles;
+                if (more_b) load_tile<P>(tb, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+                compute_tile<P>(ta, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+                if (!more_b) break;
+                k += kWaves;
+                const bool more_a = k + kWaves < ntiles;
+                if (more_a) load_tile<P>(ta, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+                compute_tile<P>(tb, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+                if (!more_a) break;
+                k += kWaves;
+            }
+        }
+
+        // Level 1a: merge the four lane groups (keys 4*(lane>>4)..) of this wave.
+        float M = fmaxf(m_run, __shfl_xor(m_run, 16));
+        M = fmaxf(M, __shfl_xor(M, 32));
+        const float f = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - M);
+        float lw = l_run * f;
+        lw += __shfl_xor(lw, 16);
+        lw += __shfl_xor(lw, 32);
+        {
+            const float fh[4] = {quad_bcast<0>(f), quad_bcast<1>(f), quad_bcast<2>(f), quad_bcast<3>(f)};
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float x = o[h][e] * fh[h];
+                    x += __shfl_xor(x, 16);
+                    x += __shfl_xor(x, 32);
+                    o[h][e] = x;
+                }
+        }
+
+        // Level 1b, first half: each wave's partial into LDS.
+        if (lane < 16) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) lds.o[w][h][8 * lane + e] = o[h][e];
+        }
+        if (lane < 4) {
+            lds.m[w][lane] = M;
+            lds.l[w][lane] = lw;
+        }
     }
-    if (lane < 4) {
-        lds.m[w][lane] = M;
-        lds.l[w][lane] = lw;
-    }
+    // Level 1b: merge the four waves in LDS.
     __syncthreads();
 
     const int h = tid >> 6;
@@ -696,6 +818,19 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128_two(DecodeParams p) {
     else decode_wg<P1, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
 }
 
+// Three spans in one launch (a cache kept in bf16, fp8 and MX fp4): splits
+// [0, S0) stream sp0, [S0, S1) sp1, the others sp2; one merge over all
+// splits. Each workgroup reads one precision, so no wave branches between
+// formats.
+template <int P0, int P1, int P2, bool FUSED>
+__global__ __launch_bounds__(256) void decode_gqa4_d128_three(DecodeParams p) {
+    __shared__ DecodeLds lds;
+    const int s = blockIdx.x;
+    if (s < p.S0) decode_wg<P0, FUSED, true>(p, p.sp0, s, s, lds);
+    else if (s < p.S1) decode_wg<P1, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
+    else decode_wg<P2, FUSED, true>(p, p.sp2, s - p.S1, s, lds);
+}
+
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
@@ -726,6 +861,14 @@ hipError_t launch_decode_mfma_two(const DecodeParams& p, int prec0, int prec1, h
     ATTN_TWO(kBf16, kFp4)
 #undef ATTN_TWO
     return hipErrorInvalidValue;  // no kernel for this pair of precisions
+}
+
+hipError_t launch_decode_mfma_three(const DecodeParams& p, int prec0, int prec1, int prec2, hipStream_t stream) {
+    if (prec0 != kBf16 || prec1 != kFp8 || prec2 != kFp4) return hipErrorInvalidValue;
+    dim3 grid(p.S, p.Hkv, p.B);
+    if (p.counters) hipLaunchKernelGGL((decode_gqa4_d128_three<kBf16, kFp8, kFp4, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((decode_gqa4_d128_three<kBf16, kFp8, kFp4, false>), grid, dim3(256), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace attn

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn.h"
+
 namespace attn {
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
@@ -77,6 +79,10 @@ struct DecodeParams {
     int S0;
     KvSpan sp0, sp1;
     const float* alpha;  // [B*Hq] gate of the spans' log-priors, or nullptr
+    // Three-span launches (launch_decode_mfma_three): splits [S0, S1) read
+    // sp1 and splits [S1, S) span sp2.
+    int S1;
+    KvSpan sp2;
 };
 
 // Bytes at the start of a decode workspace reserved for the fused-merge
@@ -90,6 +96,15 @@ constexpr int kMaxTicketBlocks = 16;
 constexpr int kMaxCounterGroups = (int)(kCounterBytes / (4 * kCounterStride * (1 + kMaxTicketBlocks)));
 // Largest split count whose merge is fused into the decode kernel.
 constexpr int kMaxFusedSplits = 256;
+
+// Sets the calling thread's attn_last_error() message.
+void set_last_error(const char* fmt, ...);
+// attn_decode on a given workspace; clear_counter_bytes > 0 zeroes that many
+// bytes of the counter block first when the launch takes the fused merge.
+attn_status decode_impl(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, const float* k_scale,
+                        const float* v_scale, const int32_t* kv_lens, int B, int Hq, int Hkv, int d, int L_cap,
+                        float softmax_scale, int causal, int num_splits, attn_tensor* out, float* lse,
+                        void* workspace, size_t workspace_bytes, size_t clear_counter_bytes, void* stream);
 
 // Level-2 merge: one output row per (b, h) from its partials.
 struct CombineParams {
@@ -139,6 +154,8 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t s
 // Two-span decode: fp8_0 / fp8_1 give the KV dtype of sp0 / sp1 (bf16 or fp8).
 // Span precisions: 0 bf16, 1 fp8-e4m3, 2 MX fp4.
 hipError_t launch_decode_mfma_two(const DecodeParams& p, int prec0, int prec1, hipStream_t stream);
+// Three spans in one launch: bf16, fp8-e4m3 and MX fp4 (precisions 0, 1, 2).
+hipError_t launch_decode_mfma_three(const DecodeParams& p, int prec0, int prec1, int prec2, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams& p, int q_dtype, int kv_dtype, int G, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 // Zeroes `bytes` (a multiple of 16) at 16-byte aligned device address `p`.

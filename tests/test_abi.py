@@ -37,7 +37,8 @@ def test_every_declared_symbol_is_exported(so):
                           "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_mixed_fp4",
                           "attn_decode_mixed_fp4_splits", "attn_decode_pi",
                           "attn_decode_pi_splits", "attn_prefill_pi", "attn_prefill_pi_workspace_size",
-                          "attn_prefill_backward", "attn_prefill_backward_workspace_size"}
+                          "attn_prefill_backward", "attn_prefill_backward_workspace_size",
+                          "attn_decode_mixed3", "attn_decode_mixed3_splits"}
     nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
     for n in names:
@@ -316,3 +317,37 @@ def test_backward_argument_errors(so):
     need = lib.attn_prefill_backward_workspace_size(1, 8, 256)
     assert need == 8 * 256 * 4
     assert backward(so, ws_bytes=need - 1) == WORKSPACE
+
+
+def mixed3(so, L_hi=256, L_mid=512, L_lo=1024, mid_dtype=FP8, lo_dtype=MXFP4, ks=FAKE, ksc=True, S=(2, 2, 4), B=1,
+           Hq=8, Hkv=2, d=128, out=None, ws=FAKE, ws_bytes=1 << 30):
+    q = T(BF16, Hq * d, d, d)
+    khi = T(BF16, Hkv * L_hi * d, L_hi * d, d)
+    kmid = T(mid_dtype, Hkv * L_mid * d, L_mid * d, d)
+    klo = T(lo_dtype, Hkv * L_lo * d // 2, L_lo * d // 2, d // 2)
+    sc = T(E8M0, Hkv * L_lo * 4, L_lo * 4, 4) if ksc else None
+    out = out or T(BF16, Hq * d, d, d)
+    ref = lambda t: None if t is None else ctypes.byref(t)
+    return so.attn_decode_mixed3(ctypes.byref(q), ref(khi), ref(khi), None, L_hi, ref(kmid), ref(kmid), ks, ks, None,
+                                 L_mid, ref(klo), ref(klo), ref(sc), ref(sc), None, L_lo, B, Hq, Hkv, d, 0.0, S[0], S[1],
+                                 S[2], ctypes.byref(out), None, ws, ws_bytes, None)
+
+
+def test_mixed3_decode_argument_errors(so):
+    assert mixed3(so, L_hi=0, L_mid=0, L_lo=0) == INVALID
+    assert mixed3(so, L_mid=-1) == INVALID
+    assert mixed3(so, S=(1, -1, 1)) == INVALID
+    assert mixed3(so, ks=None) == INVALID  # the fp8 span needs its scales
+    assert mixed3(so, ksc=False) == INVALID  # the fp4 span needs its scales
+    assert mixed3(so, mid_dtype=BF16) == UNSUPPORTED
+    assert mixed3(so, lo_dtype=FP8) == UNSUPPORTED
+    assert mixed3(so, Hq=16) == UNSUPPORTED
+    assert mixed3(so, d=64) == UNSUPPORTED
+    assert mixed3(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
+    assert mixed3(so, ws=None) == WORKSPACE
+    need = lib.attn_decode_workspace_size(1, 8, 128, 8)  # 2 + 2 + 4 splits
+    assert mixed3(so, ws_bytes=need - 1) == WORKSPACE
+    assert "8 splits" in lib.load_library().attn_last_error().decode()
+    # a span without keys takes no splits
+    assert mixed3(so, L_mid=0, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 6) - 1) == WORKSPACE
+    assert "6 splits" in lib.load_library().attn_last_error().decode()

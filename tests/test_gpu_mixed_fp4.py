@@ -129,3 +129,29 @@ def test_workload9_full_size_ragged_heads():
     inp = make_mixed_inputs(9, lens=(0.5, 1.0))
     assert inp["hi_lens"].min() < inp["hi_lens"].max() and inp["lo_lens"].min() < inp["lo_lens"].max()
     _check(inp, 0, 0, what="wl9 ragged")
+
+
+def test_mixed_fp4_scale_extremes_and_nan_scale():
+    # E8M0 bytes at the low end (1, 2: 2^-126, 2^-125) in K and V blocks, and
+    # 140 (2^13) in V blocks: all exact in fp32. Byte 255 is NaN: the V block
+    # that carries it makes its 32 output dims NaN for the heads of that KV
+    # group, in the kernel as in the definition, and leaves the rest finite.
+    inp = make_mixed_inputs(9, B=1, Hq=8, Hkv=2, L_hi=128, L_lo=1000, seed=97)
+    ks, vs = inp["k_scale"], inp["v_scale"]
+    ks[0, 0, 0:300:3, 1] = 1
+    ks[0, 1, 5:200:7, 2] = 2
+    vs[0, 0, 10:400:5, 0] = 1
+    vs[0, 1, 3:900:11, 3] = 140
+    vs[0, 1, 123, 2] = 255  # NaN scale: dims 64..95 of KV head 1
+    out, lse = mixed_fp4_on_gpu(inp, 2, 5)
+    ref, ref_lse = oracle_mixed(inp)
+    got = from_dev(out)[:, :, 0, :]
+    nan_ref = np.isnan(ref)
+    assert nan_ref[0, 4:8, 64:96].all() and nan_ref.sum() == 4 * 32
+    assert np.array_equal(np.isnan(got), nan_ref)
+    fin = ~nan_ref
+    err = np.abs(got[fin] - ref[fin])
+    rel = np.linalg.norm(got[fin] - ref[fin]) / np.linalg.norm(ref[fin])
+    print("fp4 scale extremes max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (err.max(), err.mean(), rel), flush=True)
+    assert err.max() <= 2e-2 * max(1.0, np.abs(ref[fin]).max()) and rel <= 1e-2
+    assert_lse_close(lse.cpu().numpy().astype(np.float64), ref_lse, 2e-3)
