@@ -43,6 +43,8 @@
  * Ownership and errors:
  *  - Every data pointer is device memory owned by the caller. The library
  *    allocates nothing and keeps no state between calls; it is thread-safe.
+ *    The one exception is attn_decode_noalloc, whose scratch is a fixed
+ *    array the library holds on each GPU (calls on one GPU share it).
  *  - Arguments are validated on the host before any launch; a bad argument
  *    returns an error code and launches nothing. Launches are asynchronous on
  *    `stream` (a hipStream_t; NULL = the null stream). A launch failure returns
@@ -170,6 +172,29 @@ ATTN_API attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, con
                                  int Hq, int Hkv, int d, int L_cap, float softmax_scale, int causal,
                                  int num_splits, attn_tensor* out, float* lse, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, serving loops and harnesses that forbid hipMalloc. Arguments,
+ * results, split plan and kernels are those of attn_decode, without the
+ * workspace: the merge counters and split partials live in a fixed array of
+ * 32 MiB (33,554,432 bytes) of device memory that the library holds on each
+ * GPU it runs on until the process ends. The call allocates nothing (no
+ * hipMalloc or allocating library routine).
+ *
+ * Limit: attn_decode_workspace_size(B, Hq, d, S) for the split count S in use
+ * must not exceed 32 MiB (e.g. 32 query rows with up to 1024 splits, or 512
+ * rows with 54); larger requests return ATTN_ERR_WORKSPACE before any launch.
+ * The array keeps the previous call's contents; a call that takes the fused
+ * merge first clears the counters it uses with a small kernel on `stream`.
+ * All calls on one GPU share the array: calls that overlap on one GPU (other
+ * streams, other threads, without ordering between them) race and give wrong
+ * results. Errors otherwise as attn_decode.
+ */
+ATTN_API attn_status attn_decode_noalloc(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                         const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B,
+                                         int Hq, int Hkv, int d, int L_cap, float softmax_scale, int causal,
+                                         int num_splits, attn_tensor* out, float* lse, void* stream);
 
 /*
  * The first level of attn_decode on its own: the per-chunk partials, merged

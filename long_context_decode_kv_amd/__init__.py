@@ -16,7 +16,7 @@ __all__ = [
     "AttnError", "ATTN_F32", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_MXFP4", "ATTN_E8M0", "library_path", "load_library",
     "attn_status_string", "attn_decode_auto_splits", "attn_decode_workspace_size", "attn_decode_workspace_init",
     "attn_decode_plan",
-    "attn_decode", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
+    "attn_decode", "attn_decode_noalloc", "attn_decode_partials", "attn_decode_workspace", "attn_prefill", "attn_combine_partials",
     "attn_decode_mixed", "attn_decode_mixed_splits", "attn_decode_mixed_fp4", "attn_decode_mixed_fp4_splits",
     "attn_decode_mixed3", "attn_decode_mixed3_splits",
     "attn_decode_pi", "attn_decode_pi_splits", "attn_prefill_pi",
@@ -66,6 +66,8 @@ def load_library():
     lib.attn_decode.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, tp, vp, vp,
                                 ctypes.c_size_t, vp]
     lib.attn_decode.restype = i32
+    lib.attn_decode_noalloc.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, tp, vp, vp]
+    lib.attn_decode_noalloc.restype = i32
     lib.attn_decode_plan.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_int)]
     lib.attn_decode_plan.restype = i32
     lib.attn_decode_partials.argtypes = [tp, tp, tp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, i32, vp, vp, vp,
@@ -206,6 +208,28 @@ def attn_decode(q, k, v, k_scale=None, v_scale=None, kv_lens=None, softmax_scale
                          _ptr(kv_lens), B, Hq, Hkv, d, L_cap, float(softmax_scale), int(bool(causal)), int(S),
                          ctypes.byref(ot), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
                          _stream(stream, q.device))
+    _check(st)
+    return out, lse
+
+
+def attn_decode_noalloc(q, k, v, k_scale=None, v_scale=None, kv_lens=None, softmax_scale=0.0, causal=False,
+                        num_splits=0, out=None, lse=None, stream=None):
+    """attn_decode without a workspace: the library's fixed per-GPU scratch
+    array holds the merge counters and partials (up to 32 MiB; larger requests
+    raise). Pass `out` and `lse` to make the call allocate nothing at all."""
+    lib = load_library()
+    B, Hq, Lq, d = q.shape
+    Hkv, L_cap = k.shape[1], k.shape[2]
+    if Lq != 1:
+        raise ValueError("attn_decode_noalloc takes one query per sequence (q.shape[2] == 1)")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
+    st = lib.attn_decode_noalloc(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), _ptr(k_scale), _ptr(v_scale),
+                                 _ptr(kv_lens), B, Hq, Hkv, d, L_cap, float(softmax_scale), int(bool(causal)),
+                                 int(num_splits), ctypes.byref(ot), _ptr(lse), _stream(stream, q.device))
     _check(st)
     return out, lse
 

@@ -38,7 +38,7 @@ def test_every_declared_symbol_is_exported(so):
                           "attn_decode_mixed_fp4_splits", "attn_decode_pi",
                           "attn_decode_pi_splits", "attn_prefill_pi", "attn_prefill_pi_workspace_size",
                           "attn_prefill_backward", "attn_prefill_backward_workspace_size",
-                          "attn_decode_mixed3", "attn_decode_mixed3_splits"}
+                          "attn_decode_noalloc", "attn_decode_mixed3", "attn_decode_mixed3_splits"}
     nm = subprocess.run(["nm", "-D", "--defined-only", lib.library_path], capture_output=True, text=True).stdout
     exported = {line.split()[-1] for line in nm.splitlines() if line.strip()}
     for n in names:
@@ -116,6 +116,27 @@ def test_decode_argument_errors(so):
     assert decode(so, k=e8, v=e8) == UNSUPPORTED
     assert decode(so, q=T(MXFP4, 1024, 128, 128), out=T(MXFP4, 1024, 128, 128)) == UNSUPPORTED
     assert decode(so, q=T(E8M0, 1024, 128, 128), out=T(E8M0, 1024, 128, 128)) == UNSUPPORTED
+
+
+def noalloc(so, B=1, Hq=8, Hkv=2, d=128, L=1024, S=4):
+    q = T(BF16, Hq * d, d, d)
+    k = T(BF16, Hkv * L * d, L * d, d)
+    out = T(BF16, Hq * d, d, d)
+    return so.attn_decode_noalloc(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), None, None, None, B, Hq, Hkv, d,
+                                  L, 0.0, 0, S, ctypes.byref(out), None, None)
+
+
+def test_decode_noalloc_argument_errors(so):
+    assert noalloc(so, B=0) == INVALID
+    assert noalloc(so, S=-1) == INVALID
+    # the fixed array holds 32 MiB: 4 MiB of counters, then (S + 16) partials of d + 2 floats per query row
+    limit = 32 << 20
+    assert lib.attn_decode_workspace_size(1, 32, 128, 1024) <= limit
+    assert lib.attn_decode_workspace_size(1, 32, 128, 2048) > limit
+    assert noalloc(so, Hq=32, Hkv=8, L=1 << 20, S=2048) == WORKSPACE  # before any device query or launch
+    msg = lib.load_library().attn_last_error().decode()
+    assert "2048 splits" in msg and "scratch" in msg
+    assert noalloc(so, B=16, Hq=32, Hkv=8, L=65536, S=128) == WORKSPACE
 
 
 def partials(so, q=None, k=None, B=1, Hq=8, Hkv=2, d=128, L=1024, S=4):
