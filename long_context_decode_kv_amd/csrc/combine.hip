@@ -13,8 +13,9 @@
 // that all loads of a batch -- and those of the next batch, issued before the
 // current one is added -- are in flight at once: a row of up to 128 partials
 // costs one memory round trip. LP = 64 normally; launches with few rows and
-// many partials use LP = 32 or 16, i.e. narrower column blocks and more
-// workgroups. The slot results are merged in a fixed order, so the result is
+// many partials use LP = 32, 16 or 8, i.e. narrower column blocks and more
+// workgroups. The slots of a wave are merged by a butterfly over its lane
+// groups, then the waves in LDS, each in a fixed order, so the result is
 // deterministic for a given n and launch shape (which depends on R, S, d).
 #include "internal.h"
 
@@ -116,22 +117,39 @@ __global__ __launch_bounds__(64 * kMaxWaves) void combine_partials_kernel(Combin
             s0 = s1;
         }
     }
-    // slot-major: slot k's columns at [k * 2LP, (k + 1) * 2LP)
-    __shared__ float sm_m[kMaxWaves * G], sm_l[kMaxWaves * G];
+    // The G slots of a wave hold the same columns: merge them in registers,
+    // a butterfly over the lane groups (both partners compute the same sum,
+    // so every lane ends with the wave's result, in a fixed order).
+#pragma unroll
+    for (int off = LP; off < 64; off <<= 1) {
+        const float Mo = __shfl_xor(M, off), Lo = __shfl_xor(L, off);
+        const float o0 = __shfl_xor(a0, off), o1 = __shfl_xor(a1, off);
+        const float Mn = fmaxf(M, Mo);
+        const float f = (M == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((M - Mn) * kLog2e);
+        const float fo = (Mo == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((Mo - Mn) * kLog2e);
+        L = f * L + fo * Lo;
+        a0 = f * a0 + fo * o0;
+        a1 = f * a1 + fo * o1;
+        M = Mn;
+    }
+    // wave-major: wave k's columns at [k * 2LP, (k + 1) * 2LP)
+    __shared__ float sm_m[kMaxWaves], sm_l[kMaxWaves];
     __shared__ float sm_o[kMaxWaves * 128];
-    sm_o[slot * 2 * LP + 2 * li] = a0;
-    sm_o[slot * 2 * LP + 2 * li + 1] = a1;
-    if (li == 0) {
-        sm_m[slot] = M;
-        sm_l[slot] = L;
+    if (lane < LP) {
+        sm_o[w * 2 * LP + 2 * li] = a0;
+        sm_o[w * 2 * LP + 2 * li + 1] = a1;
+        if (li == 0) {
+            sm_m[w] = M;
+            sm_l[w] = L;
+        }
     }
     __syncthreads();
     if (tid < LP) {  // wave 0, lane group 0: the row's 2*LP columns
         float mx = kNegInf;
-        for (int k = 0; k < NS; ++k) mx = fmaxf(mx, sm_m[k]);
+        for (int k = 0; k < W; ++k) mx = fmaxf(mx, sm_m[k]);
         float so0 = 0.f, so1 = 0.f, sl = 0.f;
         if (mx != kNegInf)
-            for (int k = 0; k < NS; ++k) {
+            for (int k = 0; k < W; ++k) {
                 const float mk = sm_m[k];
                 const float f = (mk == kNegInf) ? 0.f : __builtin_amdgcn_exp2f((mk - mx) * kLog2e);
                 sl = fmaf(f, sm_l[k], sl);
@@ -175,14 +193,15 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t stream) {
     // Lanes per partial: 64 unless that leaves fewer than 256 workgroups for a
     // deep merge (more than 64 partials per row); then narrower column blocks.
     int lp = 64;
-    while (lp > 16 && p.S > 64 && (int64_t)p.R * ((p.d + 2 * lp - 1) / (2 * lp)) < 256) lp >>= 1;
+    while (lp > 8 && p.S > 64 && (int64_t)p.R * ((p.d + 2 * lp - 1) / (2 * lp)) < 256) lp >>= 1;
     // enough waves (4 to 16) that each slot takes one batch where it can
     const int need = (p.S + kBatch * (64 / lp) - 1) / (kBatch * (64 / lp));
     const int waves = need < 4 ? 4 : (need > kMaxWaves ? kMaxWaves : need);
     const dim3 grid(p.R, (p.d + 2 * lp - 1) / (2 * lp)), block(64 * waves);
     if (lp == 64) hipLaunchKernelGGL(combine_partials_kernel<64>, grid, block, 0, stream, p);
     else if (lp == 32) hipLaunchKernelGGL(combine_partials_kernel<32>, grid, block, 0, stream, p);
-    else hipLaunchKernelGGL(combine_partials_kernel<16>, grid, block, 0, stream, p);
+    else if (lp == 16) hipLaunchKernelGGL(combine_partials_kernel<16>, grid, block, 0, stream, p);
+    else hipLaunchKernelGGL(combine_partials_kernel<8>, grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
