@@ -418,15 +418,21 @@ ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, co
                                   attn_tensor* out, float* lse, void* stream);
 
 /*
- * pi-Attention prefill (causal, Lq = Lkv = L): query i attends to its ring-local
- * window, keys i - window .. i, and to its periodic skip keys, i - m * period
- * below the window (m >= 1), in one softmax, with the gate alpha as a
- * log-prior: + ln(alpha) on the window's logits, + ln(1 - alpha) on the skip
- * keys' (the pi-Attention explainer, method section A; the oracle's masked
- * definition). Computed as two banded prefills: the window, then, for each
- * residue class of the positions modulo `period`, the class's queries
- * against the class's keys as strided views (the strided gather the page
- * names), whose epilogue merges each row's two parts by log-sum-exp (Tree
+ * pi-Attention prefill (Lq = Lkv = L): query i attends to its ring-local
+ * window and to its periodic skip keys in one softmax, with the gate alpha as
+ * a log-prior: + ln(alpha) on the window's logits, + ln(1 - alpha) on the
+ * skip keys' (the pi-Attention explainer, method section A; the oracle's
+ * masked definition).
+ *  causal != 0: the window is keys i - window .. i and the skip keys are
+ *          i - m * period below the window (m >= 1);
+ *  causal == 0 (two-sided, for tasks that also look ahead): the window is
+ *          keys i - window .. i + window and the skip keys are i +- m * period
+ *          outside it.
+ * Computed as banded prefills: the window (two-sided: a band of 2 window + 1
+ * keys), then, for each residue class of the positions modulo `period`, the
+ * class's queries against the class's keys as strided views (the strided
+ * gather the page names): the keys below, and two-sided also the keys above,
+ * each launch's epilogue merging its part into the row by log-sum-exp (Tree
  * Attention explainer, section 3).
  *
  * q, k, v, out, lse, softmax_scale: as attn_prefill (bf16, d = 128), with
@@ -436,14 +442,14 @@ ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, co
  * alpha    device float [B, Hq, L] contiguous (clamped to [0, 1]) or NULL (no
  *          prior).
  * workspace  attn_prefill_pi_workspace_size(B, Hq, L, d) bytes of device
- *          memory, 16-byte aligned, no preparation needed (the window part's
- *          lse).
- * The window part passes through `out` in bf16 before the merge. A row whose keys all
+ *          memory, 16-byte aligned, no preparation needed (the lse of the
+ *          parts merged so far).
+ * The parts pass through `out` in bf16 before the merge. A row whose keys all
  * carry weight zero (alpha = 0 with no skip key) gets O = 0 and lse = -inf.
  */
 ATTN_API attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B,
-                                     int Hq, int Hkv, int d, int L, float softmax_scale, int window, int period,
-                                     const float* alpha, attn_tensor* out, float* lse, void* workspace,
+                                     int Hq, int Hkv, int d, int L, float softmax_scale, int causal, int window,
+                                     int period, const float* alpha, attn_tensor* out, float* lse, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of attn_prefill_pi (0 on a bad argument). */

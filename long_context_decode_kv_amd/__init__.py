@@ -98,7 +98,7 @@ def load_library():
     lib.attn_decode_pi.restype = i32
     lib.attn_decode_pi_splits.argtypes = [i32, i32, i32, i32, i32, i32, ip, ip]
     lib.attn_decode_pi_splits.restype = i32
-    lib.attn_prefill_pi.argtypes = [tp, tp, tp, i32, i32, i32, i32, i32, f32, i32, i32, vp, tp, vp, vp,
+    lib.attn_prefill_pi.argtypes = [tp, tp, tp, i32, i32, i32, i32, i32, f32, i32, i32, i32, vp, tp, vp, vp,
                                     ctypes.c_size_t, vp]
     lib.attn_prefill_pi.restype = i32
     lib.attn_prefill_pi_workspace_size.argtypes = [i32, i32, i32, i32]
@@ -511,10 +511,11 @@ def attn_prefill_pi_workspace_size(B, Hq, L, d):
     return load_library().attn_prefill_pi_workspace_size(B, Hq, L, d)
 
 
-def attn_prefill_pi(q, k, v, window, period, alpha=None, softmax_scale=0.0, out=None, lse=None, workspace=None,
-                    stream=None):
-    """pi-Attention causal prefill: window keys i-window..i, skip keys a whole number of `period`s below the window,
-    alpha (float [B,Hq,L] or None) as a log-prior. q [B,Hq,L,d]; k, v [B,Hkv,L,d] bf16. Returns (out, lse)."""
+def attn_prefill_pi(q, k, v, window, period, alpha=None, softmax_scale=0.0, causal=True, out=None, lse=None,
+                    workspace=None, stream=None):
+    """pi-Attention prefill: window keys i-window..i, skip keys a whole number of `period`s below the window
+    (causal=False: window i-window..i+window, skip keys on both sides), alpha (float [B,Hq,L] or None) as a
+    log-prior. q [B,Hq,L,d]; k, v [B,Hkv,L,d] bf16. Returns (out, lse)."""
     lib = load_library()
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
@@ -530,7 +531,8 @@ def attn_prefill_pi(q, k, v, window, period, alpha=None, softmax_scale=0.0, out=
         workspace = torch.empty(lib.attn_prefill_pi_workspace_size(B, Hq, L, d), dtype=torch.uint8, device=q.device)
     qt, kt, vt, ot = _tensor(q), _tensor(k), _tensor(v), _tensor(out)
     st = lib.attn_prefill_pi(ctypes.byref(qt), ctypes.byref(kt), ctypes.byref(vt), B, Hq, Hkv, d, L,
-                             float(softmax_scale), int(window), int(period), _ptr(alpha), ctypes.byref(ot), _ptr(lse),
+                             float(softmax_scale), int(bool(causal)), int(window), int(period), _ptr(alpha),
+                             ctypes.byref(ot), _ptr(lse),
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream, q.device))
     _check(st)
     return out, lse

@@ -1002,13 +1002,14 @@ size_t attn_prefill_pi_workspace_size(int B, int Hq, int L, int d) {
 }
 
 attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B, int Hq, int Hkv,
-                            int d, int L, float softmax_scale, int window, int period, const float* alpha,
+                            int d, int L, float softmax_scale, int causal, int window, int period, const float* alpha,
                             attn_tensor* out, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
     g_last_error[0] = 0;
     attn_status st = check_prefill(q, k, v, out, B, Hq, Hkv, d, L, L, softmax_scale, 1);
     if (st != ATTN_OK) return st;
     if (window < 0 || period < 0) return fail(ATTN_ERR_INVALID_ARG, "window and period must be >= 0");
     if (window > L) window = L;  // same keys; keeps window arithmetic in range
+    if (!causal && 2LL * window > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "two-sided window too long");
     if (period > 0 && ((int64_t)period * k->stride_s >= (1 << 24) || (int64_t)period * v->stride_s >= (1 << 24)))
         return fail(ATTN_ERR_UNSUPPORTED, "period * k/v row stride must be below 2^24 elements");
     const size_t need = attn_prefill_pi_workspace_size(B, Hq, L, d);
@@ -1017,15 +1018,17 @@ attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const at
     if (workspace_bytes < need) return fail(ATTN_ERR_WORKSPACE, "workspace %zu bytes, need %zu", workspace_bytes, need);
     float* lse_w = static_cast<float*>(workspace);
     hipStream_t hs = static_cast<hipStream_t>(stream);
-    const bool has_skip = period > 0 && L > window + 1;  // some query has a key below its window
+    // some query has a key farther than the window (below it, or on either side)
+    const bool has_skip = period > 0 && L > window + 1;
 
-    // 1. the window: keys [i - window, i] of query i. With skip keys to come,
-    // its lse goes to the workspace and the skip launches merge; without, it
-    // applies the prior itself.
+    // 1. the window: keys [i - window, i] of query i (two-sided: [i - window,
+    // i + window], a band of 2 window + 1 keys ending at position i + window).
+    // With skip keys to come, its lse goes to the workspace and the skip
+    // launches merge; without, it applies the prior itself.
     attn::PrefillParams pw = prefill_params(q, k, v, out, has_skip ? lse_w : lse, B, Hq, Hkv, d, L, L, softmax_scale, 1);
     pw.band = 1;
-    pw.diag = 0;
-    pw.window = window;
+    pw.diag = causal ? 0 : window;
+    pw.window = causal ? window : 2 * window;
     pw.merge = (!has_skip && alpha) ? 2 : 0;
     pw.alpha = alpha;
     hipError_t e = attn::launch_prefill(pw, hs);
@@ -1034,10 +1037,13 @@ attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const at
 
     // 2. the skip keys: for each residue class r of the positions mod period,
     // queries r, r + period, ... against keys r, r + period, ...; query m of
-    // the class sees keys m' <= m - delta (positions more than window below).
-    // Classes are the batch of a banded launch over strided views; the first
-    // L % period classes have one row more than the others. Each row's
-    // epilogue merges its skip part with its window part, already in `out`.
+    // the class sees keys m' <= m - delta (positions more than window below)
+    // and, two-sided, keys m' >= m + delta (more than window above). Classes
+    // are the batch of banded launches over strided views; the first L %
+    // period classes have one row more than the others. Each row's epilogue
+    // merges its skip part with what `out` already holds: the window part
+    // (merge 1), or, for the keys above, the window and the keys below
+    // (merge 3; the keys below then leave their merged lse in the workspace).
     const int delta = window / period + 1;
     const int n = L / period, rem = L % period;
     for (int b = 0; b < B; ++b) {
@@ -1061,7 +1067,7 @@ attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const at
             ps.o_ss = (int64_t)period * out->stride_s;
             // lse, lse_w and alpha are [B, Hq, L] contiguous: the same class view
             const int64_t base = (int64_t)b * Hq * L + r0;
-            ps.lse = lse ? lse + base : nullptr;
+            float* lse_final = lse ? lse + base : nullptr;
             ps.lse_w = lse_w + base;
             ps.alpha = alpha ? alpha + base : nullptr;
             ps.lse_sb = 1;
@@ -1069,9 +1075,20 @@ attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const at
             ps.lse_ss = period;
             ps.B = ncls;
             ps.Lq = ps.Lkv = nrows;
+            // keys below: [0, m - delta]
+            const bool above = !causal && delta <= nrows - 1;  // some row has keys above
+            ps.lse = above ? lse_w + base : lse_final;
             ps.diag = -delta;
             ps.window = -1;
             ps.merge = 1;
+            e = attn::launch_prefill(ps, hs);
+            if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+            if (!above) continue;
+            // keys above: [m + delta, nrows - 1], a band ending at position m + nrows
+            ps.lse = lse_final;
+            ps.diag = nrows;
+            ps.window = nrows - delta;
+            ps.merge = 3;
             e = attn::launch_prefill(ps, hs);
             if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
         }

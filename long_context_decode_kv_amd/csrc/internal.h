@@ -144,7 +144,9 @@ struct PrefillParams {
     // merge 0: plain; 1: this launch computes the skip part of its rows and
     // merges it with the window part already in `out` (its lse in lse_w),
     // the parts weighted by the priors ln(alpha) and ln(1 - alpha);
-    // 2: the window part alone, shifted by ln(alpha).
+    // 2: the window part alone, shifted by ln(alpha); 3: as 1, but the part in
+    // `out` / lse_w already carries its priors (the window and the other
+    // skip keys of a two-sided row), so only ln(1 - alpha) is added here.
     int merge;
     const float* lse_w;
     const float* alpha;  // or nullptr: no prior

@@ -433,7 +433,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         float lse = empty ? kNegInf : m_run * kLn2 + logf(l_tot);
         const int64_t li = b * p.lse_sb + h * p.lse_sh + (int64_t)qr * p.lse_ss;
         uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_ss;
-        float wprev = 0.f;  // weight of the part already in `out` (merge == 1)
+        float wprev = 0.f;  // weight of the part already in `out` (merge 1 and 3)
         if constexpr (BAND) {
             if (p.merge) {
                 // pi-Attention's log-priors: + ln(alpha) on the window part,
@@ -447,7 +447,12 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
                 if (p.merge == 2) {  // the window alone
                     lse += bw;
                     if (lse == kNegInf) inv = 0.f;
-                } else {  // this launch's part is the skip part; the window part is in out / lse_w
+                } else {
+                    // this launch's part is skip keys; the part already in
+                    // out / lse_w is the window (merge 1: its prior still to
+                    // add) or the window and the other skip keys (merge 3:
+                    // priors included)
+                    if (p.merge == 3) bw = 0.f;
                     const float mw = p.lse_w[li] + bw, ms = lse + bs;
                     const float M = fmaxf(mw, ms);
                     const float ww = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * kLog2e);
@@ -468,7 +473,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
                 float o[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) o[e] = oacc[dblk][4 * jj + e] * inv;
-                if (BAND && p.merge == 1) {
+                if (BAND && (p.merge == 1 || p.merge == 3)) {
                     const u32x2 prev = *reinterpret_cast<const u32x2*>(orow + d0);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {

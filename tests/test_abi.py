@@ -294,12 +294,12 @@ def test_pi_decode_argument_errors(so):
     assert pi(so, window=2 ** 31 - 1, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 2) - 1) == WORKSPACE
 
 
-def pi_prefill(so, dtype=BF16, d=128, L=256, Hq=8, Hkv=2, window=16, period=4, ws=FAKE, ws_bytes=1 << 30):
+def pi_prefill(so, dtype=BF16, d=128, L=256, Hq=8, Hkv=2, window=16, period=4, ws=FAKE, ws_bytes=1 << 30, causal=1):
     q = T(dtype, Hq * L * d, L * d, d)
     k = T(dtype, Hkv * L * d, L * d, d)
     o = T(dtype, Hq * L * d, L * d, d)
-    return so.attn_prefill_pi(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 1, Hq, Hkv, d, L, 0.0, window,
-                              period, None, ctypes.byref(o), None, ws, ws_bytes, None)
+    return so.attn_prefill_pi(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 1, Hq, Hkv, d, L, 0.0, causal,
+                              window, period, None, ctypes.byref(o), None, ws, ws_bytes, None)
 
 
 def test_pi_prefill_argument_errors(so):
@@ -315,6 +315,9 @@ def test_pi_prefill_argument_errors(so):
     assert need == 8 * 256 * 4
     assert pi_prefill(so, ws_bytes=need - 1) == WORKSPACE
     assert lib.attn_prefill_pi_workspace_size(0, 8, 256, 128) == 0
+    assert pi_prefill(so, causal=0, window=-1) == INVALID
+    assert pi_prefill(so, causal=0, ws=None) == WORKSPACE
+    assert pi_prefill(so, causal=0, ws_bytes=need - 1) == WORKSPACE
 
 
 def backward(so, dtype=BF16, gdt=F32, d=128, Lq=256, Lkv=256, causal=1, Hq=8, Hkv=2, lse=FAKE, ws=FAKE,

@@ -47,3 +47,18 @@ def test_pi_counts_by_enumeration():
         i = L - 1
         keys = sum(1 for j in range(L) if (i - j) <= w or (per > 0 and (i - j) % per == 0))
         assert bench.pi_decode_keys(L, w, per) == keys
+
+
+def test_two_sided_pi_counts_by_enumeration():
+    for L, w, per in ((300, 37, 11), (129, 0, 1), (200, 250, 7), (64, 5, 0), (500, 64, 64)):
+        pairs = sum(1 for i in range(L) for j in range(L)
+                    if abs(i - j) <= w or (per > 0 and (i - j) % per == 0))
+        assert bench.pi_prefill_pairs(L, w, per, causal=False) == pairs
+
+
+def test_ragged_fp8_and_three_precision_bytes():
+    # per key and KV head: bf16 2 x 256 B, fp8 2 x 128 B, fp4 2 x (64 + 4) B
+    assert bench.ragged_bytes([4096, 100], 32, 8, 128) == 8 * 4196 * 512 + 2 * 2 * 32 * 128 * 2
+    assert bench.fp8_decode_bytes(1, 32, 8, 128, 1 << 20) == (1 << 31) + 64 + 2 * 32 * 128 * 2
+    assert bench.mixed3_algorithmic_bytes(1, 32, 8, 128, 26214, 26214, 78644) == \
+        8 * (26214 * 512 + 26214 * 256 + 78644 * 136) + 64 + 2 * 32 * 128 * 2

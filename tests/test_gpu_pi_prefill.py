@@ -1,9 +1,10 @@
-"""GPU parity of attn_prefill_pi (causal pi-Attention prefill: the ring-local
-window, the periodic skip keys of each residue class as strided views, and the
-alpha log-prior, merged per row) against the oracle's masked definition:
-window / period combinations on lengths that are multiples of neither the tile
-nor the period, alpha 0 and 1, skip sets that are empty for every row, period
-1 (every key), strided BSHD views, and the 16K-token cache on sampled rows."""
+"""GPU parity of attn_prefill_pi (pi-Attention prefill: the ring-local window,
+the periodic skip keys of each residue class as strided views, and the alpha
+log-prior, merged per row; causal, and two-sided with keys on both sides)
+against the oracle's masked definition: window / period combinations on
+lengths that are multiples of neither the tile nor the period, alpha 0 and 1,
+skip sets that are empty for every row, period 1 (every key), strided BSHD
+views, and the 16K-token cache on sampled rows."""
 import numpy as np
 import pytest
 import torch
@@ -15,23 +16,23 @@ from datagen.workloads import make_inputs
 pytestmark = [pytest.mark.gpu, needs_gpu]
 
 
-def pi_prefill_on_gpu(inp, window, period, alpha=None, dev=None):
+def pi_prefill_on_gpu(inp, window, period, alpha=None, dev=None, causal=True):
     import long_context_decode_kv_amd as lib
     dev = dev or {k: to_dev(inp[k]) for k in ("q", "k", "v")}
     a = None if alpha is None else torch.from_numpy(np.ascontiguousarray(alpha, np.float32)).cuda()
-    out, lse = lib.attn_prefill_pi(dev["q"], dev["k"], dev["v"], window, period, alpha=a)
+    out, lse = lib.attn_prefill_pi(dev["q"], dev["k"], dev["v"], window, period, alpha=a, causal=causal)
     torch.cuda.synchronize()
     return out, lse
 
 
-def oracle_pi_rows(inp, window, period, alpha=None, rows=None):
-    prob = oracle.Problem(inp["q"], inp["k"], inp["v"], causal=True)
+def oracle_pi_rows(inp, window, period, alpha=None, rows=None, causal=True):
+    prob = oracle.Problem(inp["q"], inp["k"], inp["v"], causal=causal)
     return oracle.pi_attention(prob, window, period, alpha, rows=rows)
 
 
-def _check(inp, window, period, alpha, what, dev=None, rows=None):
-    out, lse = pi_prefill_on_gpu(inp, window, period, alpha, dev=dev)
-    ref, ref_lse = oracle_pi_rows(inp, window, period, alpha, rows=rows)
+def _check(inp, window, period, alpha, what, dev=None, rows=None, causal=True):
+    out, lse = pi_prefill_on_gpu(inp, window, period, alpha, dev=dev, causal=causal)
+    ref, ref_lse = oracle_pi_rows(inp, window, period, alpha, rows=rows, causal=causal)
     got = from_dev(out).reshape(-1, 128)
     gl = lse.cpu().numpy().astype(np.float64).ravel()
     if rows is not None:
@@ -101,3 +102,47 @@ def test_pi_prefill_16k_sampled_rows():
     per_head = np.unique(np.concatenate([np.arange(64), np.arange(L - 64, L), np.linspace(0, L - 1, 64).astype(int)]))
     rows = np.concatenate([h * L + per_head for h in (0, 5, 17, 31)])
     _check(inp, 512, 64, alpha, "pi prefill 16K", rows=rows)
+
+
+# ---------------------------------------------------------------- two-sided
+# Keys on both sides of the query: the window i - w .. i + w, skip keys
+# i +- m * period outside it (the page's bidirectional case).
+
+@pytest.mark.parametrize("window,period", [(128, 16), (0, 3), (300, 1), (999, 5), (64, 0), (100, 7), (37, 200),
+                                           (450, 64)])
+@pytest.mark.parametrize("with_alpha", [False, True])
+def test_pi_prefill_two_sided_small(window, period, with_alpha):
+    B, Hq, Hkv, L = 2, 8, 2, 1000
+    inp = make_inputs(4, B=B, Hq=Hq, Hkv=Hkv, L=L, seed=200 + window + period)
+    alpha = np.random.default_rng(201).uniform(0.05, 0.95, size=(B, Hq, L)).astype(np.float32) if with_alpha else None
+    _check(inp, window, period, alpha, "pi prefill two-sided", causal=False)
+
+
+def test_pi_prefill_two_sided_alpha_extremes():
+    B, Hq, Hkv, L = 1, 4, 1, 700
+    inp = make_inputs(4, B=B, Hq=Hq, Hkv=Hkv, L=L, seed=202)
+    alpha = np.full((B, Hq, L), 0.5, np.float32)
+    alpha[0, 0] = 1.0  # head 0: the window only
+    alpha[0, 1] = 0.0  # head 1: the skip keys only, on both sides
+    out, lse = _check(inp, 50, 8, alpha, "pi prefill two-sided alpha 0/1", causal=False)
+    assert np.all(np.isfinite(lse.cpu().numpy()))
+
+
+def test_pi_prefill_two_sided_period_one_is_full_prefill():
+    import long_context_decode_kv_amd as lib
+    inp = make_inputs(4, B=1, Hq=8, Hkv=2, L=777, seed=203)
+    dev = {k: to_dev(inp[k]) for k in ("q", "k", "v")}
+    out, lse = pi_prefill_on_gpu(inp, 10, 1, dev=dev, causal=False)
+    ref_out, ref_lse = lib.attn_prefill(dev["q"], dev["k"], dev["v"], causal=False)
+    torch.cuda.synchronize()
+    assert (out.float() - ref_out.float()).abs().max().item() < 2e-2
+    assert (lse - ref_lse).abs().max().item() < 1e-3
+
+
+def test_pi_prefill_two_sided_16k_sampled_rows():
+    inp = make_inputs(4)
+    B, Hq, L = 1, 32, 16384
+    alpha = np.random.default_rng(204).uniform(0.05, 0.95, size=(B, Hq, L)).astype(np.float32)
+    per_head = np.unique(np.concatenate([np.arange(64), np.arange(L - 64, L), np.linspace(0, L - 1, 64).astype(int)]))
+    rows = np.concatenate([h * L + per_head for h in (0, 5, 17, 31)])
+    _check(inp, 512, 64, alpha, "pi prefill two-sided 16K", rows=rows, causal=False)
