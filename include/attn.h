@@ -138,7 +138,14 @@ ATTN_API attn_status attn_decode_workspace_init(void* workspace, size_t workspac
 ATTN_API int attn_decode_plan(int L_cap, int num_splits, int* chunk);
 
 /*
- * Single-query decode over a KV cache (one new token per sequence).
+ * Single-query decode over a KV cache (one new token per sequence): the
+ * memory-bound generation step the glossary page "Attention" describes in its
+ * sections on the KV cache and memory bandwidth, computed as the Tree
+ * Attention explainer's sequence-axis reduction (sections 1 and 3): the cache
+ * is cut into chunks (workgroups), each chunk's partial (o, m, l) is merged by
+ * log-sum-exp into the exact softmax result (section 2: exact, not an
+ * approximation), with the max subtracted before every exponential
+ * (Grayskull explainer, section 3).
  *
  * q        [B, Hq, 1, d]      ATTN_F32 or ATTN_BF16
  * k, v     [B, Hkv, L_cap, d] same dtype as q, or ATTN_FP8_E4M3 with bf16 q
@@ -401,7 +408,11 @@ ATTN_API int attn_decode_pi_splits(int B, int Hkv, int L_cap, int window, int pe
                                    int* splits_window, int* splits_skip);
 
 /*
- * Prefill: attention of Lq queries over Lkv keys (causal or not), fused so the
+ * Prefill: attention of Lq queries over Lkv keys (causal or not), the O(n^2)
+ * compute-bound case (glossary page "Attention", section on Self-Attention
+ * and Transformers; causal = past keys only, the pi-Attention explainer's
+ * method section), with matmul, scaling and softmax fused on chip as the
+ * Grayskull explainer's sections 1 and 3 describe, so the
  * Lq x Lkv score matrix never reaches memory.
  *
  * q [B, Hq, Lq, d], k and v [B, Hkv, Lkv, d], out [B, Hq, Lq, d]: one dtype,
@@ -488,7 +499,9 @@ ATTN_API size_t attn_prefill_backward_workspace_size(int B, int Hq, int Lq);
  * Merge S partials per row into the exact normalised result (the reduction
  * step of the Tree Attention explainer, section 3, on one device): with
  * m = max_s m_s and w_s = exp(m_s - m), O = sum_s w_s o_s / sum_s w_s l_s and
- * lse = m + ln sum_s w_s l_s, summed in a fixed balanced order.
+ * lse = m + ln sum_s w_s l_s, summed in an order fixed by R, S and d (each
+ * lane group a strided running merge, then the groups of a wave by a
+ * butterfly, then the waves in order).
  *
  * o_part [R, S, d], m_part [R, S], l_part [R, S]: contiguous device fp32.
  * out: row r of d elements at out->data + r * out->stride_s (F32 or BF16);
