@@ -25,10 +25,9 @@ attn_status fail(attn_status st, const char* fmt, ...) {
 constexpr int kChunkQuantum = 64;  // keys per workgroup step (4 waves x 16 keys)
 constexpr int kPrecBf16 = 0, kPrecFp8 = 1, kPrecFp4 = 2;  // span precisions of launch_decode_mfma_two
 // Split-plan cost per key of an MX fp4 span, against 2 for bf16 and 1.3 for
-// fp8 (measured on the two-span decodes: with both products on the MFMA an
-// fp4 key costs about what an fp8 key does; 128K keys, 20 % bf16: 18 + 46
-// splits 49.3 us, 14 + 50 58.0 us, 22 + 42 51.6 us).
-constexpr double kFp4Cost = 1.3;
+// fp8 (measured on the two-span decode, 128K keys, 20 % bf16: 22 + 42 splits
+// 44.7 us, 18 + 46 45.9 us, 26 + 38 47.4 us, 14 + 50 55.7 us).
+constexpr double kFp4Cost = 1.0;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 int elem_size(int dt) {

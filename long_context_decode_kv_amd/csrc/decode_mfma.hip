@@ -154,14 +154,14 @@ __device__ __forceinline__ void stage_k(const Tile<P>& t, u32x4* ks, int lane) {
 }
 
 // Eight MX fp4 codes (a dword, first code in the low nibble) times 2^scale ->
-// eight floats (exact).
-__device__ __forceinline__ void fp4x8_to_f32(uint32_t w, float sc, float (&f)[8]) {
-    const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
-    const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
-    const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
-    const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
-    f[0] = a[0]; f[1] = a[1]; f[2] = b[0]; f[3] = b[1];
-    f[4] = c[0]; f[5] = c[1]; f[6] = d[0]; f[7] = d[1];
+// eight bf16, in the code order (exact: a one-bit mantissa times a power of
+// two; a probe of every code at every scale byte matched the fp32 form).
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float sc) {
+    const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0);
+    const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1);
+    const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2);
+    const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3);
+    return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Four OCP e4m3 codes of a dword pair -> eight bf16 (exact widening).
@@ -288,26 +288,53 @@ __device__ __forceinline__ int fp4_row_a(int m) { return 8 * (m >> 2) + (m & 3);
 // banks.
 __device__ __forceinline__ int kidx4(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 3) & 3)); }
 
-__device__ __forceinline__ void load_fp4(Fp4Tile& t, const char* kbase, const char* vbase, int64_t kss, int64_t vss,
-                                         const ScaleRows& sc, int tok0, int tlast, int lane) {
-    // the tile's first row in wide arithmetic (uniform), the lanes' rows as
-    // 32-bit offsets from it (the host keeps a span's row strides below 2^26)
-    const int last = tlast - tok0;
-    const char* kt = kbase + (int64_t)tok0 * kss;
-    const char* vt = vbase + (int64_t)tok0 * vss;
-    const char* kst = sc.k + (int64_t)tok0 * sc.kss;
-    const char* vst = sc.v + (int64_t)tok0 * sc.vss;
-    const int ik = (int)kss, iv = (int)vss, iks = (int)sc.kss, ivs = (int)sc.vss;
-    t.k[0] = ld_stream<u32x4>(kt + min(lane >> 2, last) * ik + 16 * (lane & 3));
-    t.k[1] = ld_stream<u32x4>(kt + min(16 + (lane >> 2), last) * ik + 16 * (lane & 3));
-    const int ra = fp4_row_a(lane & 15);
-    t.ks[0] = ld_stream<uint32_t>(kst + min(ra, last) * iks);
-    t.ks[1] = ld_stream<uint32_t>(kst + min(ra + 4, last) * iks);
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle): loads at
+// or past the resource's byte size return zero.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;  // cache policy of the streaming buffer loads
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const char* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kRsrcWord3);
+}
+
+// This lane's byte offsets inside an fp4 tile, the same for every tile of a
+// split: K codes of row lane >> 2 (chunk lane & 3), K scales of row
+// fp4_row_a(lane & 15), V codes of row 8(lane >> 4) at dims 8(lane & 15),
+// V scales of row 8(lane >> 4). The other rows a lane reads are these plus a
+// multiple of the row stride, passed as the loads' scalar offset.
+struct Fp4Lanes {
+    uint32_t k, ks, v, vs;
+};
+__device__ __forceinline__ Fp4Lanes fp4_lanes(int ik, int iks, int iv, int ivs, int lane) {
+    Fp4Lanes o;
+    o.k = (lane >> 2) * ik + 16 * (lane & 3);
+    o.ks = fp4_row_a(lane & 15) * iks;
+    o.v = 8 * (lane >> 4) * iv + 4 * (lane & 15);
+    o.vs = 8 * (lane >> 4) * ivs;
+    return o;
+}
+
+// Loads the 32-key tile starting at key tok0. Buffer loads over the tile's
+// valid rows (up to key tlast): rows past it read as zero, so the tail needs
+// no clamping (a zero key scores 0 and is masked; a zero value adds nothing),
+// and the lanes' addresses are fixed offsets (the host keeps row strides below
+// 2^26 bytes, so 32 rows fit 32-bit offsets).
+__device__ __forceinline__ void load_fp4(Fp4Tile& t, const char* kbase, const char* vbase, int ik, int iv,
+                                         const ScaleRows& sc, int iks, int ivs, const Fp4Lanes& ln, int tok0,
+                                         int tlast) {
+    const int last = min(tlast - tok0, kTile4 - 1);
+    const __amdgpu_buffer_rsrc_t rk = bytes_rsrc(kbase + (int64_t)tok0 * ik, last * ik + 64);
+    const __amdgpu_buffer_rsrc_t rks = bytes_rsrc(sc.k + (int64_t)tok0 * iks, last * iks + 4);
+    const __amdgpu_buffer_rsrc_t rv = bytes_rsrc(vbase + (int64_t)tok0 * iv, last * iv + 64);
+    const __amdgpu_buffer_rsrc_t rvs = bytes_rsrc(sc.v + (int64_t)tok0 * ivs, last * ivs + 4);
+    t.k[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 0, kNonTemporal));
+    t.k[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 16 * ik, kNonTemporal));
+    t.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, ln.ks, 0, kNonTemporal);
+    t.ks[1] = __builtin_amdgcn_raw_buffer_load_b32(rks, ln.ks, 4 * iks, kNonTemporal);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        const int rv = min(8 * (lane >> 4) + u, last);
-        t.v[u] = ld_stream<uint32_t>(vt + rv * iv + 4 * (lane & 15));
-        t.vs[u] = ld_stream<uint32_t>(vst + rv * ivs);
+        t.v[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, ln.v, u * iv, kNonTemporal);
+        t.vs[u] = __builtin_amdgcn_raw_buffer_load_b32(rvs, ln.vs, u * ivs, kNonTemporal);
     }
 }
 
@@ -327,8 +354,9 @@ __device__ __forceinline__ void fp4_pv_pair(const Fp4Tile& t, const float (&sc)[
     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, pb, acc1, 0, 0, 0);
 }
 
-__device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const bf16x8 (&qop)[4], float scale2, int tok0,
-                                         int tend, int lane, float& m_run, float& l_run, f32x4 (&acc)[8]) {
+__device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const float* e8m0, const bf16x8 (&qop)[4],
+                                         float scale2, int tok0, int tend, int lane, float& m_run, float& l_run,
+                                         f32x4 (&acc)[8]) {
     ks[kidx4(lane >> 2, lane & 3)] = t.k[0];
     ks[kidx4(16 + (lane >> 2), lane & 3)] = t.k[1];
     const uint32_t* ks32 = reinterpret_cast<const uint32_t*>(ks);
@@ -336,26 +364,28 @@ __device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const bf16
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        float f[8];
-        bf16x8 a;
-        fp4x8_to_f32(ks32[4 * kidx4(ra, i) + g], e8m0_to_f32(t.ks[0] >> (8 * i)), f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = (__bf16)f[e];  // exact: two significant bits
+        const bf16x8 a = fp4x8_to_bf16(ks32[4 * kidx4(ra, i) + g], e8m0[(t.ks[0] >> (8 * i)) & 255u]);
         sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], sa, 0, 0, 0);
-        fp4x8_to_f32(ks32[4 * kidx4(ra + 4, i) + g], e8m0_to_f32(t.ks[1] >> (8 * i)), f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a[e] = (__bf16)f[e];
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], sb, 0, 0, 0);
+        const bf16x8 b = fp4x8_to_bf16(ks32[4 * kidx4(ra + 4, i) + g], e8m0[(t.ks[1] >> (8 * i)) & 255u]);
+        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, qop[i], sb, 0, 0, 0);
     }
     const int kb = tok0 + 8 * g;
     float s[8];
-    float tmax = kNegInf;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        s[r] = (kb + r < tend) ? sa[r] * scale2 : kNegInf;
-        s[4 + r] = (kb + 4 + r < tend) ? sb[r] * scale2 : kNegInf;
-        tmax = fmaxf(tmax, fmaxf(s[r], s[4 + r]));
+        s[r] = sa[r] * scale2;
+        s[4 + r] = sb[r] * scale2;
     }
+    if (tok0 + kTile4 > tend) {  // the split's last tile: mask the keys past its end
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            s[r] = (kb + r < tend) ? s[r] : kNegInf;
+            s[4 + r] = (kb + 4 + r < tend) ? s[4 + r] : kNegInf;
+        }
+    }
+    float tmax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, fmaxf(s[r], s[4 + r]));
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + kHeadroom) != 0) {
         // the new running max of each head: over the 16 lanes with its lane & 3
         float hm = fmaxf(tmax, __shfl_xor(tmax, 4));
@@ -369,11 +399,13 @@ __device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const bf16
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] *= alpha;
     }
+    // m_run is finite here: every tile has a valid key for every head (key
+    // tok0), so the first tile set it; masked scores give exp2(-inf) = 0
     bf16x8 pb;
     float lsum = 0.f;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        const float pu = (s[u] == kNegInf) ? 0.f : fast_exp2(s[u] - m_run);
+        const float pu = fast_exp2(s[u] - m_run);
         lsum += pu;
         pb[u] = (__bf16)pu;
     }
@@ -382,7 +414,7 @@ __device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const bf16
     const int sh = 8 * ((lane & 15) >> 2);
     float sc[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sc[u] = e8m0_to_f32(t.vs[u] >> sh);
+    for (int u = 0; u < 8; ++u) sc[u] = e8m0[(t.vs[u] >> sh) & 255u];
     fp4_pv_pair<0>(t, sc, pb, acc[0], acc[1]);
     fp4_pv_pair<1>(t, sc, pb, acc[2], acc[3]);
     fp4_pv_pair<2>(t, sc, pb, acc[4], acc[5]);
@@ -557,6 +589,7 @@ struct DecodeLds {
     float o[kWaves][4][128];
     float m[kWaves][4];
     float l[kWaves][4];
+    float e8m0[256];  // MX fp4 spans: the value of every E8M0 scale byte
 };
 
 // One workgroup: split s of span `sp`, publishing partial s_out of its rows.
@@ -658,18 +691,23 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         f32x4 acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // scale bytes are widened by a table lookup (exact, 2^-127 and NaN included)
+        lds.e8m0[tid] = e8m0_to_f32((uint32_t)tid);
+        __syncthreads();
         if (k < ntiles4) {
+            const int ik = (int)kss, iv = (int)vss, iks = (int)sc.kss, ivs = (int)sc.vss;
+            const Fp4Lanes ln = fp4_lanes(ik, iks, iv, ivs, lane);
             Fp4Tile ta, tb;
-            load_fp4(ta, kbase, vbase, kss, vss, sc, t_begin + kTile4 * k, t_end - 1, lane);
+            load_fp4(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile4 * k, t_end - 1);
             while (true) {
                 const bool more_b = k + kWaves < ntiles4;
-                if (more_b) load_fp4(tb, kbase, vbase, kss, vss, sc, t_begin + kTile4 * (k + kWaves), t_end - 1, lane);
-                fp4_tile(ta, ks, qop, scale2, t_begin + kTile4 * k, t_end, lane, m_run, l_run, acc);
+                if (more_b) load_fp4(tb, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile4 * (k + kWaves), t_end - 1);
+                fp4_tile(ta, ks, lds.e8m0, qop, scale2, t_begin + kTile4 * k, t_end, lane, m_run, l_run, acc);
                 if (!more_b) break;
                 k += kWaves;
                 const bool more_a = k + kWaves < ntiles4;
-                if (more_a) load_fp4(ta, kbase, vbase, kss, vss, sc, t_begin + kTile4 * (k + kWaves), t_end - 1, lane);
-                fp4_tile(tb, ks, qop, scale2, t_begin + kTile4 * k, t_end, lane, m_run, l_run, acc);
+                if (more_a) load_fp4(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile4 * (k + kWaves), t_end - 1);
+                fp4_tile(tb, ks, lds.e8m0, qop, scale2, t_begin + kTile4 * k, t_end, lane, m_run, l_run, acc);
                 if (!more_a) break;
                 k += kWaves;
             }
