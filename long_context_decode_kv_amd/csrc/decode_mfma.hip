@@ -70,17 +70,10 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // consecutive elements of a row, in a separate array of 4 bytes per row).
 constexpr int kBf16 = 0, kFp8 = 1, kFp4 = 2;
 
-template <int P>
-struct Tile;
-template <>
-struct Tile<kBf16> {
+// A bf16 span's 16-key tile, as one lane holds it.
+struct Tile {
     u32x4 k[4];  // key row 4i + (lane>>4), bytes 16*(lane & 15) .. +15 (coalesced rows)
     u32x4 v[4];  // key 4*(lane>>4) + u: 8 bf16 at dims 8*(lane & 15)
-};
-template <>
-struct Tile<kFp8> {
-    u32x4 k[2];  // key row 8i + (lane>>3), bytes 16*(lane & 7) .. +15 (coalesced rows)
-    u32x2 v[4];  // key 4*(lane>>4) + u: 8 fp8 at dims 8*(lane & 15)
 };
 
 // Rows of an MX fp4 span's scale arrays (unused for the other precisions).
@@ -104,31 +97,19 @@ __device__ __forceinline__ T ld_stream(const char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
 }
 
-// Loads one 16-key tile (bf16 or fp8); key indices past `tlast` are clamped to
-// it, so every address stays inside the cache and the clamped keys are masked
-// later.
-template <int P>
-__device__ __forceinline__ void load_tile(Tile<P>& t, const char* kbase, const char* vbase, int64_t kss,
-                                          int64_t vss, int tok0, int tlast, int lane) {
-    if constexpr (P == kBf16) {
+// Loads one 16-key bf16 tile; key indices past `tlast` are clamped to it, so
+// every address stays inside the cache and the clamped keys are masked later.
+__device__ __forceinline__ void load_tile(Tile& t, const char* kbase, const char* vbase, int64_t kss, int64_t vss,
+                                          int tok0, int tlast, int lane) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int rk = min(tok0 + 4 * i + (lane >> 4), tlast);
-            t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 15));
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int rk = min(tok0 + 8 * i + (lane >> 3), tlast);
-            t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 7));
-        }
+    for (int i = 0; i < 4; ++i) {
+        const int rk = min(tok0 + 4 * i + (lane >> 4), tlast);
+        t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 15));
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
-        const char* vrow = vbase + (int64_t)rv * vss;
-        if constexpr (P == kBf16) t.v[u] = ld_stream<u32x4>(vrow + 2 * 8 * (lane & 15));
-        else t.v[u] = ld_stream<u32x2>(vrow + 8 * (lane & 15));
+        t.v[u] = ld_stream<u32x4>(vbase + (int64_t)rv * vss + 2 * 8 * (lane & 15));
     }
 }
 
@@ -136,22 +117,7 @@ __device__ __forceinline__ void load_tile(Tile<P>& t, const char* kbase, const c
 // lanes to the MFMA operand layout (lane = key row, 16 bytes of dims). 16-byte
 // chunks are XOR-swizzled by row so both the row writes and the column reads
 // touch every bank once per 16 lanes.
-template <int P>
-__device__ __forceinline__ int kstage_index(int row, int chunk) {
-    if constexpr (P == kBf16) return row * 16 + (chunk ^ (row & 15));
-    else return row * 8 + (chunk ^ ((row >> 1) & 7));
-}
-
-template <int P>
-__device__ __forceinline__ void stage_k(const Tile<P>& t, u32x4* ks, int lane) {
-    if constexpr (P == kBf16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ks[kstage_index<kBf16>(4 * i + (lane >> 4), lane & 15)] = t.k[i];
-    } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) ks[kstage_index<kFp8>(8 * i + (lane >> 3), lane & 7)] = t.k[i];
-    }
-}
+__device__ __forceinline__ int kstage_index(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
 
 // Eight MX fp4 codes (a dword, first code in the low nibble) times 2^scale ->
 // eight bf16, in the code order (exact: a one-bit mantissa times a power of
@@ -173,48 +139,19 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-template <int P>
-__device__ __forceinline__ void v_to_f32(const Tile<P>& t, int u, int lane, float (&vf)[8]) {
-    if constexpr (P == kBf16) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vf[2 * e] = bf16_lo(t.v[u][e]);
-            vf[2 * e + 1] = bf16_hi(t.v[u][e]);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(t.v[u][e], false);
-            f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(t.v[u][e], true);
-            vf[4 * e + 0] = a[0];
-            vf[4 * e + 1] = a[1];
-            vf[4 * e + 2] = b[0];
-            vf[4 * e + 3] = b[1];
-        }
-    }
-}
-
-template <int P>
-__device__ __forceinline__ void compute_tile(const Tile<P>& t, u32x4* ks, const bf16x8 (&qop)[4], float scale2,
+// One 16-key bf16 tile of a wave: scores on the MFMA (lane l receives head
+// l & 3 of keys 4(l >> 4) + r), softmax update, P.V in fp32 on the VALU.
+__device__ __forceinline__ void compute_tile(const Tile& t, u32x4* ks, const bf16x8 (&qop)[4], float scale2,
                                              int tok0, int tend, int lane, float& m_run, float& l_run,
                                              float (&o)[4][8]) {
-    stage_k<P>(t, ks, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ks[kstage_index(4 * i + (lane >> 4), lane & 15)] = t.k[i];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const int row = lane & 15;
-    if constexpr (P == kBf16) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 a = ks[kstage_index<kBf16>(row, 4 * i + (lane >> 4))];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qop[i], acc, 0, 0, 0);
-        }
-    } else {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const u32x4 a = ks[kstage_index<kFp8>(row, 4 * h + (lane >> 4))];
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[0], a[1]), qop[2 * h], acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[2], a[3]), qop[2 * h + 1], acc, 0, 0,
-                                                          0);
-        }
+    for (int i = 0; i < 4; ++i) {
+        const u32x4 a = ks[kstage_index(row, 4 * i + (lane >> 4))];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qop[i], acc, 0, 0, 0);
     }
     const int kb = tok0 + 4 * (lane >> 4);
     float s[4];
@@ -244,7 +181,11 @@ __device__ __forceinline__ void compute_tile(const Tile<P>& t, u32x4* ks, const 
     for (int u = 0; u < 4; ++u) {
         const float pb[4] = {quad_bcast<0>(p[u]), quad_bcast<1>(p[u]), quad_bcast<2>(p[u]), quad_bcast<3>(p[u])};
         float vf[8];
-        v_to_f32<P>(t, u, lane, vf);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vf[2 * e] = bf16_lo(t.v[u][e]);
+            vf[2 * e + 1] = bf16_hi(t.v[u][e]);
+        }
 #pragma unroll
         for (int h = 0; h < 4; ++h)
 #pragma unroll
@@ -252,41 +193,56 @@ __device__ __forceinline__ void compute_tile(const Tile<P>& t, u32x4* ks, const 
     }
 }
 
-// ---- The MX fp4 span: 32-key tiles per wave, both products on the MFMA.
+// ---- fp8 and MX fp4 spans: 32-key tiles per wave, both products on the MFMA.
 //
-// Scores: S^T = K Q^T as two v_mfma_f32_16x16x32_bf16 chains over d (step i
-// is scale block i, dims 32i .. 32i + 31). Product a takes the tile's keys
-// 8(m >> 2) + (m & 3) as its A rows m, product b those keys + 4, so lane l
-// receives head l & 3 of keys 8(l >> 4) + r (from a) and 8(l >> 4) + 4 + r
-// (from b), r < 4: the eight keys 8(l >> 4) .. +7 that the same lane feeds to
-// the P.V product as its B operand. No lane exchange is needed between the two
-// products.
+// Scores: S^T = K Q^T as two v_mfma_f32_16x16x32_bf16 chains over d. Product
+// a takes the tile's keys 8(m >> 2) + (m & 3) as its A rows m, product b
+// those keys + 4, so lane l receives head l & 3 of keys 8(l >> 4) + r (from
+// a) and 8(l >> 4) + 4 + r (from b), r < 4: the eight keys 8(l >> 4) .. +7
+// that the same lane feeds to the P.V product as its B operand. No lane
+// exchange is needed between the two products.
 // P.V: O^T = V^T P^T as eight products j = 0..7 over the 32 keys. Product j's
-// A row m is dim 8m + j (lane l holds those of the eight codes it loaded per
+// A row m is dim 8m + j (lane l holds those of the eight values it loaded per
 // key, dims 8(l & 15) .. +7), its B column n is head n & 3 (the four heads
 // repeat across the 16 columns, as in the scores), so lane l ends with head
 // l & 3 at dims 32(l >> 4) + 8r + j in acc[j][r].
-// Codes widen exactly to fp32 with the block scale applied (gfx950's scaled
-// fp4 conversion; a one-bit mantissa times a power of two) and then exactly to
-// bf16; P is rounded to bf16 for the MFMA, the sum l takes the fp32 weights.
-// The running max is shared by the 16 lanes of a head, because every product
-// sums over all lanes' keys.
-constexpr int kTile4 = 32;
-struct Fp4Tile {
+// Codes widen exactly to bf16 (fp8-e4m3: three mantissa bits; MX fp4: one
+// mantissa bit times the block's power-of-two scale); P is rounded to bf16 for
+// the MFMA, the sum l takes the fp32 weights. The running max is shared by
+// the 16 lanes of a head, because every product sums over all lanes' keys.
+// fp8's per-head K scale is folded into the score scale and its V scale is
+// applied to the partial; fp4's block scales are applied in the conversion.
+constexpr int kTile32 = 32;
+template <int P>
+struct Tile32;
+template <>
+struct Tile32<kFp8> {
+    u32x4 k[4];  // key rows (lane >> 3) + 8i: 16-byte chunk lane & 7 (dims 16(lane & 7) ..)
+    u32x2 v[8];  // key 8*(lane >> 4) + u: its 8 codes at dims 8*(lane & 15) .. +7
+};
+template <>
+struct Tile32<kFp4> {
     u32x4 k[2];      // key rows lane >> 2 and 16 + (lane >> 2): 16-byte chunk lane & 3 (32 codes, block lane & 3)
-    uint32_t ks[2];  // scale words of key rows fp4_row_a(lane & 15) and that + 4 (byte i: block i)
+    uint32_t ks[2];  // scale words of key rows row_a(lane & 15) and that + 4 (byte i: block i)
     uint32_t v[8];   // key 8*(lane >> 4) + u: its 8 codes at dims 8*(lane & 15) .. +7
     uint32_t vs[8];  // that key's scale word
 };
 
 // The tile row score product a takes as its A row m.
-__device__ __forceinline__ int fp4_row_a(int m) { return 8 * (m >> 2) + (m & 3); }
+__device__ __forceinline__ int row_a(int m) { return 8 * (m >> 2) + (m & 3); }
 
-// K stage of a 32-row tile (four 16-byte chunks a row, u32x4 units): chunk c
-// of row r at c ^ ((r >> 3) & 3). The operand reads (4-byte word g = lane >> 4
-// of chunk i of row fp4_row_a(lane & 15), or that + 4) then hit 64 distinct
-// banks.
-__device__ __forceinline__ int kidx4(int row, int chunk) { return row * 4 + (chunk ^ ((row >> 3) & 3)); }
+// K stages of a 32-row tile (u32x4 units). fp4: four 16-byte chunks a row,
+// chunk c of row r at c ^ ((r >> 3) & 3); the operand reads (4-byte word
+// lane >> 4 of chunk i of row row_a(lane & 15), or that + 4) hit 64 distinct
+// banks. fp8: eight chunks a row, chunk c of row r at c ^ s(r) with s(r) =
+// 2((r >> 3) & 3) + ((r >> 1) & 1), distinct over the eight rows of each
+// parity that one read touches, so the 16-byte operand reads (chunk 4h +
+// (lane >> 4)) and the row writes both take the minimum of four passes.
+template <int P>
+__device__ __forceinline__ int kidx32(int row, int chunk) {
+    if constexpr (P == kFp4) return row * 4 + (chunk ^ ((row >> 3) & 3));
+    else return row * 8 + (chunk ^ ((((row >> 3) & 3) << 1) | ((row >> 1) & 1)));
+}
 
 // Word 3 of a raw buffer resource (32-bit data format, no swizzle): loads at
 // or past the resource's byte size return zero.
@@ -297,20 +253,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const char* base, i
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, bytes, kRsrcWord3);
 }
 
-// This lane's byte offsets inside an fp4 tile, the same for every tile of a
-// split: K codes of row lane >> 2 (chunk lane & 3), K scales of row
-// fp4_row_a(lane & 15), V codes of row 8(lane >> 4) at dims 8(lane & 15),
-// V scales of row 8(lane >> 4). The other rows a lane reads are these plus a
-// multiple of the row stride, passed as the loads' scalar offset.
-struct Fp4Lanes {
+// This lane's byte offsets inside a 32-key tile, the same for every tile of a
+// split: K codes (fp8: row lane >> 3, chunk lane & 7; fp4: row lane >> 2,
+// chunk lane & 3), K scales (fp4) of row row_a(lane & 15), V codes of row
+// 8(lane >> 4) at dims 8(lane & 15), V scales (fp4) of row 8(lane >> 4). The
+// other rows a lane reads are these plus a multiple of the row stride, passed
+// as the loads' scalar offset.
+struct Lanes32 {
     uint32_t k, ks, v, vs;
 };
-__device__ __forceinline__ Fp4Lanes fp4_lanes(int ik, int iks, int iv, int ivs, int lane) {
-    Fp4Lanes o;
-    o.k = (lane >> 2) * ik + 16 * (lane & 3);
-    o.ks = fp4_row_a(lane & 15) * iks;
-    o.v = 8 * (lane >> 4) * iv + 4 * (lane & 15);
-    o.vs = 8 * (lane >> 4) * ivs;
+template <int P>
+__device__ __forceinline__ Lanes32 lanes32(int ik, int iks, int iv, int ivs, int lane) {
+    Lanes32 o;
+    if constexpr (P == kFp4) {
+        o.k = (lane >> 2) * ik + 16 * (lane & 3);
+        o.ks = row_a(lane & 15) * iks;
+        o.v = 8 * (lane >> 4) * iv + 4 * (lane & 15);
+        o.vs = 8 * (lane >> 4) * ivs;
+    } else {
+        o.k = (lane >> 3) * ik + 16 * (lane & 7);
+        o.ks = 0;
+        o.v = 8 * (lane >> 4) * iv + 8 * (lane & 15);
+        o.vs = 0;
+    }
     return o;
 }
 
@@ -319,34 +284,47 @@ __device__ __forceinline__ Fp4Lanes fp4_lanes(int ik, int iks, int iv, int ivs, 
 // no clamping (a zero key scores 0 and is masked; a zero value adds nothing),
 // and the lanes' addresses are fixed offsets (the host keeps row strides below
 // 2^26 bytes, so 32 rows fit 32-bit offsets).
-__device__ __forceinline__ void load_fp4(Fp4Tile& t, const char* kbase, const char* vbase, int ik, int iv,
-                                         const ScaleRows& sc, int iks, int ivs, const Fp4Lanes& ln, int tok0,
-                                         int tlast) {
-    const int last = min(tlast - tok0, kTile4 - 1);
-    const __amdgpu_buffer_rsrc_t rk = bytes_rsrc(kbase + (int64_t)tok0 * ik, last * ik + 64);
-    const __amdgpu_buffer_rsrc_t rks = bytes_rsrc(sc.k + (int64_t)tok0 * iks, last * iks + 4);
-    const __amdgpu_buffer_rsrc_t rv = bytes_rsrc(vbase + (int64_t)tok0 * iv, last * iv + 64);
-    const __amdgpu_buffer_rsrc_t rvs = bytes_rsrc(sc.v + (int64_t)tok0 * ivs, last * ivs + 4);
-    t.k[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 0, kNonTemporal));
-    t.k[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 16 * ik, kNonTemporal));
-    t.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, ln.ks, 0, kNonTemporal);
-    t.ks[1] = __builtin_amdgcn_raw_buffer_load_b32(rks, ln.ks, 4 * iks, kNonTemporal);
+template <int P>
+__device__ __forceinline__ void load_tile32(Tile32<P>& t, const char* kbase, const char* vbase, int ik, int iv,
+                                            const ScaleRows& sc, int iks, int ivs, const Lanes32& ln, int tok0,
+                                            int tlast) {
+    const int last = min(tlast - tok0, kTile32 - 1);
+    constexpr int kRow = P == kFp4 ? 64 : 128;  // bytes of codes per row (d = 128)
+    const __amdgpu_buffer_rsrc_t rk = bytes_rsrc(kbase + (int64_t)tok0 * ik, last * ik + kRow);
+    const __amdgpu_buffer_rsrc_t rv = bytes_rsrc(vbase + (int64_t)tok0 * iv, last * iv + kRow);
+    if constexpr (P == kFp4) {
+        const __amdgpu_buffer_rsrc_t rks = bytes_rsrc(sc.k + (int64_t)tok0 * iks, last * iks + 4);
+        const __amdgpu_buffer_rsrc_t rvs = bytes_rsrc(sc.v + (int64_t)tok0 * ivs, last * ivs + 4);
+        t.k[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 0, kNonTemporal));
+        t.k[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 16 * ik, kNonTemporal));
+        t.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, ln.ks, 0, kNonTemporal);
+        t.ks[1] = __builtin_amdgcn_raw_buffer_load_b32(rks, ln.ks, 4 * iks, kNonTemporal);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        t.v[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, ln.v, u * iv, kNonTemporal);
-        t.vs[u] = __builtin_amdgcn_raw_buffer_load_b32(rvs, ln.vs, u * ivs, kNonTemporal);
+        for (int u = 0; u < 8; ++u) {
+            t.v[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, ln.v, u * iv, kNonTemporal);
+            t.vs[u] = __builtin_amdgcn_raw_buffer_load_b32(rvs, ln.vs, u * ivs, kNonTemporal);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            t.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 8 * i * ik, kNonTemporal));
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            t.v[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, ln.v, u * iv, kNonTemporal));
     }
 }
 
-// P.V products 2 SEL and 2 SEL + 1: codes 2 SEL and 2 SEL + 1 of every key
+// P.V products 2 SEL and 2 SEL + 1: values 2 SEL and 2 SEL + 1 of every key
 // (dims 8m + 2 SEL and 8m + 2 SEL + 1 of A row m).
-template <int SEL>
-__device__ __forceinline__ void fp4_pv_pair(const Fp4Tile& t, const float (&sc)[8], const bf16x8& pb, f32x4& acc0,
-                                            f32x4& acc1) {
+template <int P, int SEL>
+__device__ __forceinline__ void pv_pair(const Tile32<P>& t, const float (&sc)[8], const bf16x8& pb, f32x4& acc0,
+                                        f32x4& acc1) {
     bf16x8 a0, a1;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        const f32x2 x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.v[u], sc[u], SEL);
+        f32x2 x;
+        if constexpr (P == kFp4) x = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(t.v[u], sc[u], SEL);
+        else x = __builtin_amdgcn_cvt_pk_f32_fp8(t.v[u][SEL >> 1], (SEL & 1) != 0);
         a0[u] = (__bf16)x[0];
         a1[u] = (__bf16)x[1];
     }
@@ -354,20 +332,39 @@ __device__ __forceinline__ void fp4_pv_pair(const Fp4Tile& t, const float (&sc)[
     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, pb, acc1, 0, 0, 0);
 }
 
-__device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const float* e8m0, const bf16x8 (&qop)[4],
-                                         float scale2, int tok0, int tend, int lane, float& m_run, float& l_run,
-                                         f32x4 (&acc)[8]) {
-    ks[kidx4(lane >> 2, lane & 3)] = t.k[0];
-    ks[kidx4(16 + (lane >> 2), lane & 3)] = t.k[1];
-    const uint32_t* ks32 = reinterpret_cast<const uint32_t*>(ks);
-    const int g = lane >> 4, ra = fp4_row_a(lane & 15);
+// One 32-key tile of a wave: scores, softmax update, P.V (see above).
+template <int P>
+__device__ __forceinline__ void tile32(const Tile32<P>& t, u32x4* ks, const float* e8m0, const bf16x8 (&qop)[4],
+                                       float scale2, int tok0, int tend, int lane, float& m_run, float& l_run,
+                                       f32x4 (&acc)[8]) {
+    const int g = lane >> 4, ra = row_a(lane & 15);
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (P == kFp4) {
+        ks[kidx32<kFp4>(lane >> 2, lane & 3)] = t.k[0];
+        ks[kidx32<kFp4>(16 + (lane >> 2), lane & 3)] = t.k[1];
+        const uint32_t* ks32 = reinterpret_cast<const uint32_t*>(ks);
+        // step i is scale block i: dims 32i + 8g .. +7 of this lane's rows
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const bf16x8 a = fp4x8_to_bf16(ks32[4 * kidx4(ra, i) + g], e8m0[(t.ks[0] >> (8 * i)) & 255u]);
-        sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], sa, 0, 0, 0);
-        const bf16x8 b = fp4x8_to_bf16(ks32[4 * kidx4(ra + 4, i) + g], e8m0[(t.ks[1] >> (8 * i)) & 255u]);
-        sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, qop[i], sb, 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            const bf16x8 a = fp4x8_to_bf16(ks32[4 * kidx32<kFp4>(ra, i) + g], e8m0[(t.ks[0] >> (8 * i)) & 255u]);
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], sa, 0, 0, 0);
+            const bf16x8 b = fp4x8_to_bf16(ks32[4 * kidx32<kFp4>(ra + 4, i) + g], e8m0[(t.ks[1] >> (8 * i)) & 255u]);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, qop[i], sb, 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ks[kidx32<kFp8>((lane >> 3) + 8 * i, lane & 7)] = t.k[i];
+        // steps 2h and 2h + 1 take the two halves of chunk 4h + g: dims
+        // 64h + 16g .. +7 and +8 .. +15 (the Q operand's fp8 dim order)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4 a = ks[kidx32<kFp8>(ra, 4 * h + g)];
+            const u32x4 b = ks[kidx32<kFp8>(ra + 4, 4 * h + g)];
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[0], a[1]), qop[2 * h], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(b[0], b[1]), qop[2 * h], sb, 0, 0, 0);
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[2], a[3]), qop[2 * h + 1], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(b[2], b[3]), qop[2 * h + 1], sb, 0, 0, 0);
+        }
     }
     const int kb = tok0 + 8 * g;
     float s[8];
@@ -376,7 +373,7 @@ __device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const floa
         s[r] = sa[r] * scale2;
         s[4 + r] = sb[r] * scale2;
     }
-    if (tok0 + kTile4 > tend) {  // the split's last tile: mask the keys past its end
+    if (tok0 + kTile32 > tend) {  // the split's last tile: mask the keys past its end
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             s[r] = (kb + r < tend) ? s[r] : kNegInf;
@@ -410,15 +407,17 @@ __device__ __forceinline__ void fp4_tile(const Fp4Tile& t, u32x4* ks, const floa
         pb[u] = (__bf16)pu;
     }
     l_run += lsum;
-    // dims 8*(lane & 15) .. +7 lie in scale block (lane & 15) >> 2
-    const int sh = 8 * ((lane & 15) >> 2);
     float sc[8];
+    if constexpr (P == kFp4) {
+        // dims 8*(lane & 15) .. +7 lie in scale block (lane & 15) >> 2
+        const int sh = 8 * ((lane & 15) >> 2);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sc[u] = e8m0[(t.vs[u] >> sh) & 255u];
-    fp4_pv_pair<0>(t, sc, pb, acc[0], acc[1]);
-    fp4_pv_pair<1>(t, sc, pb, acc[2], acc[3]);
-    fp4_pv_pair<2>(t, sc, pb, acc[4], acc[5]);
-    fp4_pv_pair<3>(t, sc, pb, acc[6], acc[7]);
+        for (int u = 0; u < 8; ++u) sc[u] = e8m0[(t.vs[u] >> sh) & 255u];
+    }
+    pv_pair<P, 0>(t, sc, pb, acc[0], acc[1]);
+    pv_pair<P, 1>(t, sc, pb, acc[2], acc[3]);
+    pv_pair<P, 2>(t, sc, pb, acc[4], acc[5]);
+    pv_pair<P, 3>(t, sc, pb, acc[6], acc[7]);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -685,29 +684,33 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
     float m_run = kNegInf, l_run = 0.f;
     u32x4* ks = lds.kstage[w];
     int k = w;
-    if constexpr (P == kFp4) {
-        // 32-key tiles, both products on the MFMA (fp4_tile); two tiles in flight
-        const int ntiles4 = (t_end - t_begin + kTile4 - 1) / kTile4;
+    if constexpr (P == kFp4 || P == kFp8) {
+        // 32-key tiles, both products on the MFMA (tile32); two tiles in flight
+        const int ntiles32 = (t_end - t_begin + kTile32 - 1) / kTile32;
         f32x4 acc[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // scale bytes are widened by a table lookup (exact, 2^-127 and NaN included)
-        lds.e8m0[tid] = e8m0_to_f32((uint32_t)tid);
-        __syncthreads();
-        if (k < ntiles4) {
+        if constexpr (P == kFp4) {
+            // scale bytes are widened by a table lookup (exact, 2^-127 and NaN included)
+            lds.e8m0[tid] = e8m0_to_f32((uint32_t)tid);
+            __syncthreads();
+        }
+        if (k < ntiles32) {
             const int ik = (int)kss, iv = (int)vss, iks = (int)sc.kss, ivs = (int)sc.vss;
-            const Fp4Lanes ln = fp4_lanes(ik, iks, iv, ivs, lane);
-            Fp4Tile ta, tb;
-            load_fp4(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile4 * k, t_end - 1);
+            const Lanes32 ln = lanes32<P>(ik, iks, iv, ivs, lane);
+            Tile32<P> ta, tb;
+            load_tile32<P>(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * k, t_end - 1);
             while (true) {
-                const bool more_b = k + kWaves < ntiles4;
-                if (more_b) load_fp4(tb, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile4 * (k + kWaves), t_end - 1);
-                fp4_tile(ta, ks, lds.e8m0, qop, scale2, t_begin + kTile4 * k, t_end, lane, m_run, l_run, acc);
+                const bool more_b = k + kWaves < ntiles32;
+                if (more_b)
+                    load_tile32<P>(tb, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * (k + kWaves), t_end - 1);
+                tile32<P>(ta, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
                 if (!more_b) break;
                 k += kWaves;
-                const bool more_a = k + kWaves < ntiles4;
-                if (more_a) load_fp4(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile4 * (k + kWaves), t_end - 1);
-                fp4_tile(tb, ks, lds.e8m0, qop, scale2, t_begin + kTile4 * k, t_end, lane, m_run, l_run, acc);
+                const bool more_a = k + kWaves < ntiles32;
+                if (more_a)
+                    load_tile32<P>(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * (k + kWaves), t_end - 1);
+                tile32<P>(tb, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
                 if (!more_a) break;
                 k += kWaves;
             }
@@ -739,17 +742,17 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         // Tile buffers used in turn: the next tile is in flight while the
         // current one is computed.
         if (k < ntiles) {
-            Tile<P> ta, tb;
-            load_tile<P>(ta, kbase, vbase, kss, vss, t_begin + kTile * k, t_end - 1, lane);
+            Tile ta, tb;
+            load_tile(ta, kbase, vbase, kss, vss, t_begin + kTile * k, t_end - 1, lane);
             while (true) {
                 const bool more_b = k + kWaves < ntiles;
-                if (more_b) load_tile<P>(tb, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-                compute_tile<P>(ta, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+                if (more_b) load_tile(tb, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+                compute_tile(ta, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
                 if (!more_b) break;
                 k += kWaves;
                 const bool more_a = k + kWaves < ntiles;
-                if (more_a) load_tile<P>(ta, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-                compute_tile<P>(tb, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
+                if (more_a) load_tile(ta, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
+                compute_tile(tb, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
                 if (!more_a) break;
                 k += kWaves;
             }
