@@ -101,6 +101,10 @@ def test_decode_argument_errors(so):
     assert decode(so, Hq=6, Hkv=2) == UNSUPPORTED  # 3 query heads per KV head
     assert decode(so, k=T(FP8, 2 * 1024 * 128, 1024 * 128, 128), v=T(FP8, 2 * 1024 * 128, 1024 * 128, 128)) == INVALID
     assert decode(so, ks=FAKE, vs=FAKE) == INVALID  # scales with bf16 k/v
+    # fp8 rows are read in 32-row tiles with 32-bit byte offsets
+    big8 = T(FP8, 2 * 1024 * (1 << 26), 1024 * (1 << 26), 1 << 26)
+    assert decode(so, k=big8, v=big8, ks=FAKE, vs=FAKE) == INVALID
+    assert "2^26" in lib.load_library().attn_last_error().decode()
     assert decode(so, k=T(F32, 2 * 1024 * 128, 1024 * 128, 128)) == INVALID  # k and v dtypes differ
     assert decode(so, q=T(BF16, 1024, 128, 128, data=FAKE + 2)) == INVALID  # misaligned
     assert decode(so, k=T(BF16, 2 * 1024 * 129, 1024 * 129, 129)) == INVALID
@@ -213,6 +217,7 @@ def test_mixed_decode_argument_errors(so):
     assert mixed(so, d=64) == UNSUPPORTED
     assert mixed(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
     assert mixed(so, Hq=6, Hkv=4) == INVALID
+    assert mixed(so, klo=T(FP8, 2 * 1024 * (1 << 26), 1024 * (1 << 26), 1 << 26)) == INVALID  # 32-row tile offsets
     assert mixed(so, ws=None) == WORKSPACE
     # 2 + 4 splits: counters, then (d + 2) floats per split and per block partial
     need = (4 << 20) + 8 * 6 * 130 * 4 + 8 * 16 * 130 * 4
@@ -278,6 +283,10 @@ def test_pi_decode_argument_errors(so):
     assert pi(so, kv=FP8) == INVALID  # fp8 without scales
     assert pi(so, ks=FAKE, vs=FAKE) == INVALID  # scales with bf16
     assert pi(so, kv=F32) == UNSUPPORTED
+    # fp8 skip keys are read 32 at a time, period rows apart, with 32-bit byte offsets
+    assert pi(so, kv=FP8, ks=FAKE, vs=FAKE, period=1 << 19) == INVALID
+    assert "2^26" in lib.load_library().attn_last_error().decode()
+    assert pi(so, kv=FP8, ks=FAKE, vs=FAKE, period=(1 << 19) - 1, ws=None) == WORKSPACE  # within the limit
     assert pi(so, d=64) == UNSUPPORTED
     assert pi(so, Hq=16) == UNSUPPORTED
     assert pi(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
