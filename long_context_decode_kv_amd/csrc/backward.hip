@@ -16,8 +16,10 @@
 //    64-row query blocks of every query head of the group that see the block,
 //    recomputes P and dz for the 64 x 64 tile, and accumulates dV = P^T dO and
 //    dK = dz^T Q in registers.
-//  * bwd_dq:    one workgroup per 64-row query block of one query head; it
-//    walks the key blocks the rows see and accumulates dQ = dz K.
+//  * bwd_dq:    one workgroup per 128-row query block of one query head; it
+//    walks the key blocks the rows see and accumulates dQ = dz K, with dz
+//    fed from the accumulator registers (no LDS round trip) and the K/V
+//    blocks in two LDS buffers used in turn (one barrier per block).
 // Every product runs on v_mfma_f32_32x32x16_bf16 with 32 x 32 tiles, one or
 // two per wave (4 waves per workgroup). Operands come from LDS tiles laid
 // out so that fragment reads hit distinct banks (16-byte chunks swizzled by
@@ -276,27 +278,48 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_kernel(BackwardParams p) {
 }
 
 // ---------------------------------------------------------------- dQ
+// One workgroup per 128-row query block of one query head (a wave per 32
+// rows); K/V blocks of 64 keys pass through two LDS buffers used in turn.
+// Per block and 32-key half, a wave computes S^T and dP^T (keys x its rows)
+// and dz, and feeds dz straight from the accumulator registers to
+// dQ += dz K as the A operand: the C layout gives lane l its row l & 31 and,
+// for k-step t, the keys 16t + swap23(kappa) of its k-slots kappa = 8hb + e
+// (bits 2 and 3 swapped), so the K operand is read in that key order (two
+// transposed reads of rows 16t + 4hb .. +3 and 16t + 8 + 4hb .. +3).
 struct DqLds {
-    char k[kBlk * kPitch];
-    char v[kBlk * kPitch];
-    char ds[kBlk * kTPitch];  // dz [row][key] bf16
+    char k[2][kBlk * kPitch];
+    char v[2][kBlk * kPitch];
 };
+
+// B operand of dQ += dz K for k-step t of key half hk, dim block dblk: keys
+// 32hk + 16t + swap23(8hb + e), dim 32dblk + (lane & 31).
+__device__ __forceinline__ bf16x8 tr_frag_sw(const char* tile, int row0, int dblk, int lane) {
+    const int i16 = lane & 15, ga = i16 >> 2, gb = i16 & 3, gg = (lane >> 4) & 1, hb = lane >> 5;
+    const int r = row0 + 4 * hb + ga, c = 4 * dblk + 2 * gg + (gb >> 1), half = 8 * (gb & 1);
+    lds_char* t = (lds_char*)tile;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(t + chunk_at(r, c) + half));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) v4i16*)(t + chunk_at(r + 8, c) + half));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+constexpr int kDqRows = 128;  // query rows per dQ workgroup
 
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
     __shared__ __attribute__((aligned(16))) DqLds s;
     // grid (Hq, query blocks, B): the heads of one query block are issued
     // together, the blocks that see the most keys (the last, when causal) first
     const int h = blockIdx.x, qb = gridDim.y - 1 - blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5, w = tid >> 6;
-    const int rt = w & 1;   // this wave's 32-row half
-    const int kt = w >> 1;  // its 32-key half for S and dP; its 64-dim half for dQ
+    const int tid = threadIdx.x, lane = tid & 63, hb = lane >> 5;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // this wave's 32-row quarter
     const int G = p.Hq / p.Hkv, g = h / G;
     const int off = p.Lkv - p.Lq;
-    const int row0 = qb * kBlk;
+    const int row0 = qb * kDqRows, wrow0 = row0 + 32 * w;
     const float c2 = p.scale_log2;
 
     // Q and dO of the wave's 32 rows as B operands (column = row, k = dims)
-    const int myrow = row0 + 32 * rt + (lane & 31);
+    const int myrow = wrow0 + (lane & 31);
     const int qrw = min(myrow, p.Lq - 1);
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)qrw * p.q_ss;
     const uint16_t* dorow = static_cast<const uint16_t*>(p.dout) + b * p.do_sb + h * p.do_sh + (int64_t)qrw * p.do_ss;
@@ -312,73 +335,88 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BackwardParams p) {
         lse2 = (l == -kInf) ? kInf : l * kLog2e;
         dlt = p.delta[((int64_t)b * p.Hq + h) * p.Lq + myrow];
     }
-    f32x16 dq[2];
+    f32x16 dq[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int j = 0; j < 16; ++j) dq[u][j] = 0.f;
 
     const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + b * p.k_sb + g * p.k_sh;
     const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + b * p.v_sb + g * p.v_sh;
     const int nkb_all = (p.Lkv + kBlk - 1) / kBlk;
-    const int last_key = min(p.Lkv - 1, row0 + kBlk - 1 + off);
+    // key blocks some row of the workgroup sees, and those of this wave
+    const int last_key = min(p.Lkv - 1, row0 + kDqRows - 1 + off);
     const int nkb = p.causal ? (last_key >= 0 ? last_key / kBlk + 1 : 0) : nkb_all;
-    BlockRegs kr, vr;  // the next key block, loaded while this one is computed
+    const int wlast = min(p.Lkv - 1, wrow0 + 31 + off);
+    const int nkb_w = p.causal ? (wlast >= 0 ? wlast / kBlk + 1 : 0) : nkb_all;
+    BlockRegs kr, vr;  // the block after the one being stored, loaded while this one is computed
     if (nkb > 0) {
         load_block(kr, kbase, p.k_ss, 0, p.Lkv, tid);
         load_block(vr, vbase, p.v_ss, 0, p.Lkv, tid);
+        store_block(kr, s.k[0], tid);
+        store_block(vr, s.v[0], tid);
+    }
+    if (nkb > 1) {
+        load_block(kr, kbase, p.k_ss, kBlk, p.Lkv, tid);
+        load_block(vr, vbase, p.v_ss, kBlk, p.Lkv, tid);
     }
     for (int kb = 0; kb < nkb; ++kb) {
         const int key0 = kb * kBlk;
-        __syncthreads();
-        store_block(kr, s.k, tid);
-        store_block(vr, s.v, tid);
+        // block kb's buffer is complete; the other one was last read in
+        // iteration kb - 1, which every wave has finished
         __syncthreads();
         if (kb + 1 < nkb) {
-            load_block(kr, kbase, p.k_ss, key0 + kBlk, p.Lkv, tid);
-            load_block(vr, vbase, p.v_ss, key0 + kBlk, p.Lkv, tid);
-        }
-
-        // S^T and dP^T for keys 32kt.. (M) and rows 32rt.. (N)
-        f32x16 sa = {}, dpa = {};
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const int ao = chunk_at(32 * kt + (lane & 31), 2 * ks + hb);
-            sa = mfma(lds_frag(s.k, ao), qf[ks], sa);
-            dpa = mfma(lds_frag(s.v, ao), df[ks], dpa);
-        }
-        // dz for this lane's row, stored as [row][key] bf16, four keys per write.
-        // A tile with every key visible to every row needs no mask.
-        const bool full = key0 + kBlk <= p.Lkv && row0 + kBlk <= p.Lq && (!p.causal || key0 + kBlk - 1 <= row0 + off);
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            float dz[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 4 * t + e;
-                const int key = key0 + 32 * kt + acc_row(j, hb);
-                const bool vis = full || (key < p.Lkv && myrow < p.Lq && (!p.causal || key <= myrow + off));
-                const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -lse2)) : 0.f;
-                dz[e] = pv * (dpa[j] - dlt);
+            store_block(kr, s.k[(kb + 1) & 1], tid);
+            store_block(vr, s.v[(kb + 1) & 1], tid);
+            if (kb + 2 < nkb) {
+                load_block(kr, kbase, p.k_ss, key0 + 2 * kBlk, p.Lkv, tid);
+                load_block(vr, vbase, p.v_ss, key0 + 2 * kBlk, p.Lkv, tid);
             }
-            const int kbyte = 2 * (32 * kt + 8 * t + 4 * hb);
-            *reinterpret_cast<u32x2*>(s.ds + (32 * rt + (lane & 31)) * kTPitch + kbyte) =
-                (u32x2){pack_bf16(dz[0], dz[1]), pack_bf16(dz[2], dz[3])};
         }
-        __syncthreads();
-
-        // dQ += dz K for rows 32rt.., dims 64kt + 32u..
+        if (kb >= nkb_w) continue;  // past this wave's rows (causal): nothing to add
+        const char* sk = s.k[kb & 1];
+        const char* sv = s.v[kb & 1];
+        // a block every key of which every row of the wave sees needs no mask
+        const bool full = key0 + kBlk <= p.Lkv && wrow0 + 32 <= p.Lq && (!p.causal || key0 + kBlk - 1 <= wrow0 + off);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 a = lds_frag(s.ds, (32 * rt + (lane & 31)) * kTPitch + 32 * ks + 16 * hb);
+        for (int hk = 0; hk < 2; ++hk) {
+            // S^T and dP^T for keys 32hk.. (M) and the wave's rows (N)
+            f32x16 sa = {}, dpa = {};
 #pragma unroll
-            for (int u = 0; u < 2; ++u) dq[u] = mfma(a, tr_frag(s.k, ks, 2 * kt + u, lane), dq[u]);
+            for (int ks = 0; ks < 8; ++ks) {
+                const int ao = chunk_at(32 * hk + (lane & 31), 2 * ks + hb);
+                sa = mfma(lds_frag(sk, ao), qf[ks], sa);
+                dpa = mfma(lds_frag(sv, ao), df[ks], dpa);
+            }
+            // dz of this lane's row at keys 32hk + acc_row(j, hb), packed as bf16
+            u32x4 dz[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    float z[2];
+#pragma unroll
+                    for (int u = 0; u < 2; ++u) {
+                        const int j = 8 * t + 2 * e2 + u;
+                        const int key = key0 + 32 * hk + acc_row(j, hb);
+                        const bool vis = full || (key < p.Lkv && myrow < p.Lq && (!p.causal || key <= myrow + off));
+                        const float pv = vis ? __builtin_amdgcn_exp2f(fmaf(sa[j], c2, -lse2)) : 0.f;
+                        z[u] = pv * (dpa[j] - dlt);
+                    }
+                    dz[t][e2] = pack_bf16(z[0], z[1]);
+                }
+            // dQ += dz K over the half's 32 keys (two k-steps of 16)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    dq[u] = mfma(__builtin_bit_cast(bf16x8, dz[t]), tr_frag_sw(sk, 32 * hk + 16 * t, u, lane), dq[u]);
         }
     }
     const float sigma = p.scale_log2 / kLog2e;
     void* dqb = static_cast<char*>(p.dq) + (b * p.dq_sb + h * p.dq_sh) * (p.grad_dtype == DT_BF16 ? 2 : 4);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) store_tile(dqb, p.grad_dtype, p.dq_ss, row0 + 32 * rt, p.Lq, 64 * kt + 32 * u, dq[u], sigma, lane);
+    for (int u = 0; u < 4; ++u) store_tile(dqb, p.grad_dtype, p.dq_ss, wrow0, p.Lq, 32 * u, dq[u], sigma, lane);
 }
 
 }  // namespace
@@ -393,7 +431,7 @@ hipError_t launch_backward(const BackwardParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(p.Hkv, (p.Lkv + kBlk - 1) / kBlk, p.B), dim3(256), 0, stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.Hq, (p.Lq + kBlk - 1) / kBlk, p.B), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(bwd_dq_kernel, dim3(p.Hq, (p.Lq + kDqRows - 1) / kDqRows, p.B), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
