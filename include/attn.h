@@ -345,7 +345,7 @@ ATTN_API attn_status attn_decode_mixed3(const attn_tensor* q, const attn_tensor*
 /*
  * Automatic split plan of attn_decode_mixed3: about two workgroups per compute
  * unit in all, shared among the three spans in proportion to keys times the
- * cost per key of the two-precision plans (2 bf16, 1.3 fp8, 1.0 fp4), no
+ * cost per key of the two-precision plans (2 bf16, 0.95 fp8, 1.0 fp4), no
  * split shorter than 256 keys. Stores each span's splits (host pointers, may
  * be NULL) and returns their sum; 0 on a bad argument or a failed device query.
  */
@@ -355,7 +355,7 @@ ATTN_API int attn_decode_mixed3_splits(int B, int Hkv, int L_hi_cap, int L_mid_c
 /*
  * Automatic split plan of attn_decode_mixed: about two workgroups per compute
  * unit of the current device in all, shared between the spans in proportion
- * to 2 * L_hi_cap and 1.3 * L_lo_cap (a measured cost per key: an fp8
+ * to 2 * L_hi_cap and 0.95 * L_lo_cap (a measured cost per key: an fp8
  * workgroup streams its bytes more slowly than a bf16 one), no split shorter
  * than 256 keys. Stores the splits each span
  * will use (after planning) in *splits_hi and *splits_lo (host pointers, may

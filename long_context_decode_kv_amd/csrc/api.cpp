@@ -24,9 +24,14 @@ attn_status fail(attn_status st, const char* fmt, ...) {
 
 constexpr int kChunkQuantum = 64;  // keys per workgroup step (4 waves x 16 keys)
 constexpr int kPrecBf16 = 0, kPrecFp8 = 1, kPrecFp4 = 2;  // span precisions of launch_decode_mfma_two
-// Split-plan cost per key of an MX fp4 span, against 2 for bf16 and 1.3 for
-// fp8 (measured on the two-span decode, 128K keys, 20 % bf16: 22 + 42 splits
-// 44.7 us, 18 + 46 45.9 us, 26 + 38 47.4 us, 14 + 50 55.7 us).
+// Split-plan cost per key of an fp8 and of an MX fp4 span, against 2 for
+// bf16 (bytes per element), measured on the two-span decodes at 128K keys,
+// 20 % bf16, 8 KV heads. fp8: 22 + 42 splits 56.1-56.2 us, 20 + 44 56.5-56.8,
+// 18 + 46 58.6-58.7, 16 + 48 61.1-61.5. fp4: 20 + 44 43.5-44.1 us,
+// 21 + 43 44.3-44.6, 22 + 42 44.4-44.5, 24 + 40 45.4-45.5, 18 + 46 49.6-51.9.
+// Both bodies run scores and P.V on the MFMA; an fp8 key has twice the bytes
+// of an fp4 key, an fp4 key more conversion work per byte.
+constexpr double kFp8Cost = 0.95;
 constexpr double kFp4Cost = 1.0;
 constexpr float kLog2e = 1.44269504088896340736f;
 
@@ -705,11 +710,8 @@ attn_status attn_combine_partials(const float* o_part, const float* m_part, cons
 
 int attn_decode_mixed_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap, int* splits_hi, int* splits_lo) {
     if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_lo_cap < 0 || L_hi_cap + L_lo_cap <= 0) return 0;
-    // Cost per key: 2 for bf16 (bytes per element) and 1.3 for fp8, whose
-    // workgroups convert and multiply twice the keys per byte and stream about
-    // 1.3x slower per byte. (128K keys, 20% bf16, 8 KV heads: 18 + 46 splits
-    // take 60.8 us, the bytes-proportional 21 + 43 take 63.7 us.)
-    return two_span_splits(B, Hkv, L_hi_cap, 2.0, L_lo_cap, 1.3, splits_hi, splits_lo);
+    // cost per key: 2 for bf16, kFp8Cost for fp8
+    return two_span_splits(B, Hkv, L_hi_cap, 2.0, L_lo_cap, kFp8Cost, splits_hi, splits_lo);
 }
 
 attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
@@ -851,10 +853,10 @@ int attn_decode_mixed3_splits(int B, int Hkv, int L_hi_cap, int L_mid_cap, int L
     if (B <= 0 || Hkv <= 0 || L_hi_cap < 0 || L_mid_cap < 0 || L_lo_cap < 0 ||
         (int64_t)L_hi_cap + L_mid_cap + L_lo_cap <= 0)
         return 0;
-    // the costs per key of the two-span plans: bf16 2, fp8 1.3, fp4 (see
-    // attn_decode_mixed_fp4_splits)
+    // the costs per key of the two-span plans: bf16 2, fp8 and fp4 (see
+    // kFp8Cost and kFp4Cost)
     const int L[3] = {L_hi_cap, L_mid_cap, L_lo_cap};
-    const double c[3] = {2.0, 1.3, kFp4Cost};
+    const double c[3] = {2.0, kFp8Cost, kFp4Cost};
     int S[3];
     const int total = span_splits(B, Hkv, 3, L, c, S);
     if (total <= 0) return 0;

@@ -88,6 +88,18 @@ def test_ragged_edge_lengths():
     assert np.all(got[0] == 0.0) and np.all(np.isneginf(lse.cpu().numpy()[0]))
 
 
+@pytest.mark.parametrize("S", [1, 5])
+def test_fp8_ragged_edge_lengths(S):
+    # fp8 spans are read in 32-key tiles: lengths at and around the tile and
+    # the 64-key split quantum, a split holding a single key, an empty row
+    lens = np.array([0, 1, 31, 32, 33, 63, 64, 65, 96, 97, 300, 129], np.int32)
+    inp = make_inputs(5, B=12, Hq=8, Hkv=2, L=300, seed=36 + S)
+    inp["kv_lens"] = lens
+    out, lse = _check(inp, S, "e4m3", causal=True, what="fp8 ragged edges")
+    got = from_dev(out)
+    assert np.all(got[0] == 0.0) and np.all(np.isneginf(lse.cpu().numpy()[0]))
+
+
 def test_ragged_lengths_beyond_capacity_are_clamped():
     inp = make_inputs(3, B=3, Hq=4, Hkv=1, L=256, seed=35)
     inp["kv_lens"] = np.array([-5, 1000, 100], np.int32)
