@@ -173,8 +173,8 @@ ATTN_API int attn_decode_plan(int L_cap, int num_splits, int* chunk);
  * bytes. Supported: d in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
  * bf16 or fp8 KV with Hq/Hkv == 4 and d == 128 (grouped-query decode of
  * Llama-style models) runs on MFMA; everything else on the vector ALUs. On
- * that path fp8 rows are read 32 at a time with 32-bit byte offsets, so fp8
- * k/v row strides must be below 2^26 bytes (else ATTN_ERR_INVALID_ARG).
+ * that path rows are read 32 at a time with 32-bit byte offsets, so k/v row
+ * strides must be below 2^26 bytes (else ATTN_ERR_INVALID_ARG).
  */
 ATTN_API attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                                  const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B,
@@ -245,7 +245,9 @@ ATTN_API attn_status attn_decode_partials(const attn_tensor* q, const attn_tenso
  * hi_lens  device int32 [B, Hkv] (index b*Hkv + g): valid keys of the bf16 span
  *          per (sequence, KV head), clamped to [0, L_hi_cap]; NULL = L_hi_cap
  * k_lo, v_lo  [B, Hkv, L_lo_cap, d] ATTN_FP8_E4M3: the low-precision span (may
- *          be NULL when L_lo_cap = 0); row strides below 2^26 bytes
+ *          be NULL when L_lo_cap = 0)
+ * Every span's row strides must be below 2^26 bytes (rows are read 32 at a
+ * time with 32-bit byte offsets); else ATTN_ERR_INVALID_ARG.
  * k_scale, v_scale  device float [B*Hkv]: the fp8 span's scales
  * lo_lens  device int32 [B, Hkv]: valid keys of the fp8 span, as hi_lens
  * L_hi_cap, L_lo_cap  >= 0, not both 0
@@ -321,7 +323,8 @@ ATTN_API int attn_decode_mixed_fp4_splits(int B, int Hkv, int L_hi_cap, int L_lo
  * k_hi, v_hi, hi_lens, L_hi_cap: the bf16 span, as in attn_decode_mixed.
  * k_mid, v_mid [B, Hkv, L_mid_cap, d] ATTN_FP8_E4M3 with k_mid_scale,
  *          v_mid_scale device float [B*Hkv], mid_lens device int32 [B, Hkv]
- *          (or NULL = L_mid_cap): the fp8 span; row strides below 2^26 bytes.
+ *          (or NULL = L_mid_cap): the fp8 span. Every span's row strides
+ *          must be below 2^26 bytes.
  * k_lo, v_lo, k_lo_scale, v_lo_scale, lo_lens, L_lo_cap: the MX fp4 span, as
  *          in attn_decode_mixed_fp4.
  * A span with capacity 0 may come without tensors; not all three may be 0.
@@ -382,9 +385,9 @@ ATTN_API int attn_decode_mixed_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap
  * lse, workspace: as attn_decode, with bf16 q/out, bf16 or fp8 k/v, d = 128
  * and Hq = 4 * Hkv.
  * window   >= 0 keys before the query (the query's own key is always local)
- * period   >= 1, or 0 for no skip keys; with fp8 k/v, period times the row
- *          stride must be below 2^26 bytes (the skip keys are read 32 rows at
- *          a time with 32-bit byte offsets), else ATTN_ERR_INVALID_ARG
+ * period   >= 1, or 0 for no skip keys; period times the row stride in bytes
+ *          must be below 2^26 (the skip keys are read 32 rows at a time with
+ *          32-bit byte offsets), else ATTN_ERR_INVALID_ARG
  * alpha    device float [B*Hq] (row b*Hq + h) or NULL (no prior: plain
  *          attention over the union)
  * num_splits_window, num_splits_skip  requested splits per span; 0 takes the

@@ -277,9 +277,12 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
 
     hipError_t e;
     const bool mfma = q->dtype == ATTN_BF16 && G == 4 && d == 128;
-    // fp8 on the MFMA path: 32-key tiles addressed by 32-bit byte offsets
-    if (mfma && fp8 && (k->stride_s >= (int64_t(1) << 26) || v->stride_s >= (int64_t(1) << 26)))
-        return fail(ATTN_ERR_INVALID_ARG, "fp8 k/v row strides must be below 2^26 bytes");
+    // the MFMA path reads 32-key tiles addressed by 32-bit byte offsets
+    if (mfma) {
+        const int64_t esz = fp8 ? 1 : 2, lim = int64_t(1) << 26;
+        if (k->stride_s < 0 || v->stride_s < 0 || k->stride_s * esz >= lim || v->stride_s * esz >= lim)
+            return fail(ATTN_ERR_INVALID_ARG, "k/v row strides must be below 2^26 bytes on the grouped-query path");
+    }
     // Fuse the merge into the decode kernel when the launch has at most one
     // workgroup per compute unit. Timed back to back, the fused tail (publish,
     // ticket, merge by the last workgroup) costs about what a second kernel
@@ -396,14 +399,14 @@ attn::KvSpan span_of(const attn_tensor* k, const attn_tensor* v, const int32_t* 
     return sp;
 }
 
-// fp8 and MX fp4 spans are read in 32-key tiles addressed by 32-bit byte
-// offsets from the tile's first row: the distance between the rows a span
-// visits (the row stride, times the period of a skip span) must stay below
-// 2^26 bytes, so that 32 of them fit.
+// Spans are read in 32-key tiles addressed by 32-bit byte offsets from the
+// tile's first row: the distance between the rows a span visits (the row
+// stride in bytes, times the period of a skip span) must stay below 2^26
+// bytes, so that 32 of them fit.
 bool tile32_strides_ok(const attn::KvSpan& sp, int prec) {
-    if (prec == kPrecBf16 || sp.L_cap == 0) return true;
+    if (sp.L_cap == 0) return true;
     const int64_t lim = int64_t(1) << 26;
-    const int64_t mul = sp.geom == attn::kGeomSkip ? sp.period : 1;
+    const int64_t mul = (sp.geom == attn::kGeomSkip ? sp.period : 1) * (prec == kPrecBf16 ? 2 : 1);
     int64_t st[4] = {sp.k_ss, sp.v_ss, 0, 0};
     if (prec == kPrecFp4) {
         st[2] = sp.ksc_ss;
@@ -438,6 +441,10 @@ attn::DecodeParams two_span_params(const attn_tensor* q, int B, int Hq, int Hkv,
 attn_status two_span_launch(attn::DecodeParams& p, int S, int prec0, int prec1, attn_tensor* out, float* lse,
                             void* workspace, size_t workspace_bytes, hipStream_t hs, int prec2 = -1) {
     const int B = p.B, Hq = p.Hq, Hkv = p.Hkv, d = p.d;
+    if (!tile32_strides_ok(p.sp0, prec0) || !tile32_strides_ok(p.sp1, prec1) ||
+        (prec2 >= 0 && !tile32_strides_ok(p.sp2, prec2)))
+        return fail(ATTN_ERR_INVALID_ARG,
+                    "the bytes between the rows a span visits (row stride x skip period) must be below 2^26");
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
     if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");
     const int64_t rows = (int64_t)B * Hq;
@@ -451,11 +458,6 @@ attn_status two_span_launch(attn::DecodeParams& p, int S, int prec0, int prec1, 
     float* blk_o = l_part + rows * S;
     float* blk_m = blk_o + rows * attn::kMaxTicketBlocks * d;
     float* blk_l = blk_m + rows * attn::kMaxTicketBlocks;
-    if (!tile32_strides_ok(p.sp0, prec0) || !tile32_strides_ok(p.sp1, prec1) ||
-        (prec2 >= 0 && !tile32_strides_ok(p.sp2, prec2)))
-        return fail(ATTN_ERR_INVALID_ARG,
-                    "fp8 and fp4 spans: the bytes between visited rows (row stride x skip period) must be below "
-                    "2^26");
     p.S = S;
     p.o_part = o_part;
     p.m_part = m_part;

@@ -1,38 +1,31 @@
 // Split-KV grouped-query decode for gfx950: one query token, four query heads
-// per KV head, head dim 128, KV cache in bf16 or OCP fp8-e4m3.
+// per KV head, head dim 128, KV cache spans in bf16, OCP fp8-e4m3 or OCP MX
+// fp4.
 //
 // Work split (the single-GPU form of the sequence-axis tree reduction in the
 // explainer of "Tree Attention: Topology-aware Decoding for Long-Context
 // Attention on GPU Clusters", section 3): workgroup (s, g, b) owns one chunk of
 // keys of KV head g of sequence b and emits one partial (o, m, l) per query
-// head. The four waves of the workgroup interleave 16-key tiles of the chunk;
-// inside a wave, each group of 16 lanes keeps its own running partial, so the
-// hot loop needs no cross-lane reduction at all. The partials are merged in
-// registers (lane groups), then in LDS (waves) -- the level-1 tree. The
+// head. The four waves of the workgroup interleave 32-key tiles of the chunk;
+// each wave's products sum over all its keys, so its partial is complete in
+// registers. The waves' partials are merged in LDS -- the level-1 tree. The
 // level-2 tree across workgroups runs either here (the last workgroup of each
 // (sequence, KV head) to finish merges its group's partials, see FUSED) or in
 // combine.hip.
 //
-// Per 16-key tile and wave:
-//  * scores: S^T = K Q^T on one v_mfma_f32_16x16x32_bf16 chain (4 steps over
-//    d=128). A = 16 key rows, B = Q^T with the four query heads repeated in the
-//    16 columns, so lane l receives the scores of head (l & 3) for keys
-//    4*(l>>4) .. 4*(l>>4)+3 of the tile. MFMA is used only because this product
-//    is a dense contraction; 75% of its columns are repeats, which costs
-//    nothing that matters at 4 flop/byte.
-//  * softmax: scores stay in base-2 units (scale folded with log2 e). The
-//    running maximum moves only when a score exceeds it by 8 (2^8 headroom
-//    in fp32), so rescaling the accumulators is rare; the result is the same
-//    exact quantity, normalised with the same maximum in o and l. The
-//    stability step is the max subtraction the Grayskull explainer names in
-//    section 3.
-//  * P.V on the vector ALUs: lane l holds V for the same four keys at dims
-//    8*(l&15) .. +7, fetches the four heads' weights of each key from its quad
-//    with DPP broadcasts, and accumulates 4 heads x 8 dims in fp32.
-// K and V are both read as whole rows per load instruction with non-temporal
-// loads (K then goes through a small wave-private LDS stage into the MFMA
-// operand layout); every valid key is read from HBM exactly once, and the next
-// tile's loads are issued before the current tile is computed.
+// Per 32-key tile and wave (tile32 below): scores S^T = K Q^T and the product
+// O^T += V^T P^T both on v_mfma_f32_16x16x32_bf16, with the four query heads
+// repeated in the 16 columns (MFMA is used because both are dense
+// contractions; the repeated columns cost nothing that matters at a few
+// flop/byte). The softmax keeps scores in base-2 units (scale folded with
+// log2 e); the running maximum moves only when a score exceeds it by 8 (2^8
+// headroom in fp32), so rescaling the accumulators is rare, and the result is
+// the same exact quantity, normalised with the same maximum in o and l (the
+// max subtraction the Grayskull explainer names in section 3). K and V are
+// read as whole rows per load instruction with non-temporal buffer loads (K
+// then goes through a small wave-private LDS stage into the MFMA operand
+// layout); every valid key is read from HBM exactly once, and the next tile's
+// loads are issued before the current tile is computed.
 #include "internal.h"
 
 namespace attn {
@@ -46,21 +39,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
-constexpr int kTile = 16;          // keys per wave per step
 constexpr float kHeadroom = 8.0f;  // base-2 units a score may exceed the running max by
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kNegInf = -__builtin_huge_valf();
-
-// Value of lane (l & ~3) + H, for every lane l (DPP quad_perm broadcast).
-template <int H>
-__device__ __forceinline__ float quad_bcast(float x) {
-    constexpr int ctrl = H | (H << 2) | (H << 4) | (H << 6);
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xf, 0xf, false));
-}
-
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -69,12 +51,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // the first in the low nibble, and one E8M0 power-of-two scale per 32
 // consecutive elements of a row, in a separate array of 4 bytes per row).
 constexpr int kBf16 = 0, kFp8 = 1, kFp4 = 2;
-
-// A bf16 span's 16-key tile, as one lane holds it.
-struct Tile {
-    u32x4 k[4];  // key row 4i + (lane>>4), bytes 16*(lane & 15) .. +15 (coalesced rows)
-    u32x4 v[4];  // key 4*(lane>>4) + u: 8 bf16 at dims 8*(lane & 15)
-};
 
 // Rows of an MX fp4 span's scale arrays (unused for the other precisions).
 struct ScaleRows {
@@ -89,35 +65,6 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
     const uint32_t bits = e == 0u ? 0x00400000u : (e == 255u ? 0x7fc00000u : e << 23);
     return __builtin_bit_cast(float, bits);
 }
-
-// Streaming loads: every byte of the cache is read once, so they are marked
-// non-temporal; each load instruction of a wave covers whole 128/256-byte rows.
-template <typename T>
-__device__ __forceinline__ T ld_stream(const char* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const T*>(p));
-}
-
-// Loads one 16-key bf16 tile; key indices past `tlast` are clamped to it, so
-// every address stays inside the cache and the clamped keys are masked later.
-__device__ __forceinline__ void load_tile(Tile& t, const char* kbase, const char* vbase, int64_t kss, int64_t vss,
-                                          int tok0, int tlast, int lane) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rk = min(tok0 + 4 * i + (lane >> 4), tlast);
-        t.k[i] = ld_stream<u32x4>(kbase + (int64_t)rk * kss + 16 * (lane & 15));
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const int rv = min(tok0 + 4 * (lane >> 4) + u, tlast);
-        t.v[u] = ld_stream<u32x4>(vbase + (int64_t)rv * vss + 2 * 8 * (lane & 15));
-    }
-}
-
-// The K tile passes through a wave-private LDS stage to change from row-major
-// lanes to the MFMA operand layout (lane = key row, 16 bytes of dims). 16-byte
-// chunks are XOR-swizzled by row so both the row writes and the column reads
-// touch every bank once per 16 lanes.
-__device__ __forceinline__ int kstage_index(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
 
 // Eight MX fp4 codes (a dword, first code in the low nibble) times 2^scale ->
 // eight bf16, in the code order (exact: a one-bit mantissa times a power of
@@ -139,61 +86,7 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
     return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-// One 16-key bf16 tile of a wave: scores on the MFMA (lane l receives head
-// l & 3 of keys 4(l >> 4) + r), softmax update, P.V in fp32 on the VALU.
-__device__ __forceinline__ void compute_tile(const Tile& t, u32x4* ks, const bf16x8 (&qop)[4], float scale2,
-                                             int tok0, int tend, int lane, float& m_run, float& l_run,
-                                             float (&o)[4][8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ks[kstage_index(4 * i + (lane >> 4), lane & 15)] = t.k[i];
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    const int row = lane & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const u32x4 a = ks[kstage_index(row, 4 * i + (lane >> 4))];
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qop[i], acc, 0, 0, 0);
-    }
-    const int kb = tok0 + 4 * (lane >> 4);
-    float s[4];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        s[r] = (kb + r < tend) ? acc[r] * scale2 : kNegInf;
-        tmax = fmaxf(tmax, s[r]);
-    }
-    const bool need = tmax > m_run + kHeadroom;
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-        m_run = m_new;
-        const float a[4] = {quad_bcast<0>(alpha), quad_bcast<1>(alpha), quad_bcast<2>(alpha), quad_bcast<3>(alpha)};
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] *= a[h];
-    }
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = (s[r] == kNegInf) ? 0.f : fast_exp2(s[r] - m_run);
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        const float pb[4] = {quad_bcast<0>(p[u]), quad_bcast<1>(p[u]), quad_bcast<2>(p[u]), quad_bcast<3>(p[u])};
-        float vf[8];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            vf[2 * e] = bf16_lo(t.v[u][e]);
-            vf[2 * e + 1] = bf16_hi(t.v[u][e]);
-        }
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] = fmaf(pb[h], vf[e], o[h][e]);
-    }
-}
-
-// ---- fp8 and MX fp4 spans: 32-key tiles per wave, both products on the MFMA.
+// ---- 32-key tiles per wave, both products on the MFMA.
 //
 // Scores: S^T = K Q^T as two v_mfma_f32_16x16x32_bf16 chains over d. Product
 // a takes the tile's keys 8(m >> 2) + (m & 3) as its A rows m, product b
@@ -206,15 +99,21 @@ __device__ __forceinline__ void compute_tile(const Tile& t, u32x4* ks, const bf1
 // key, dims 8(l & 15) .. +7), its B column n is head n & 3 (the four heads
 // repeat across the 16 columns, as in the scores), so lane l ends with head
 // l & 3 at dims 32(l >> 4) + 8r + j in acc[j][r].
-// Codes widen exactly to bf16 (fp8-e4m3: three mantissa bits; MX fp4: one
-// mantissa bit times the block's power-of-two scale); P is rounded to bf16 for
-// the MFMA, the sum l takes the fp32 weights. The running max is shared by
+// bf16 values feed the MFMA as stored; fp8 and fp4 codes widen exactly to
+// bf16 (fp8-e4m3: three mantissa bits; MX fp4: one mantissa bit times the
+// block's power-of-two scale). P is rounded to bf16 for the MFMA, the sum l
+// takes the fp32 weights. The running max is shared by
 // the 16 lanes of a head, because every product sums over all lanes' keys.
 // fp8's per-head K scale is folded into the score scale and its V scale is
 // applied to the partial; fp4's block scales are applied in the conversion.
 constexpr int kTile32 = 32;
 template <int P>
 struct Tile32;
+template <>
+struct Tile32<kBf16> {
+    u32x4 k[8];  // key rows (lane >> 4) + 4i: 16-byte chunk lane & 15 (dims 8(lane & 15) ..)
+    u32x4 v[8];  // key 8*(lane >> 4) + u: its 8 values at dims 8*(lane & 15) .. +7
+};
 template <>
 struct Tile32<kFp8> {
     u32x4 k[4];  // key rows (lane >> 3) + 8i: 16-byte chunk lane & 7 (dims 16(lane & 7) ..)
@@ -238,9 +137,14 @@ __device__ __forceinline__ int row_a(int m) { return 8 * (m >> 2) + (m & 3); }
 // 2((r >> 3) & 3) + ((r >> 1) & 1), distinct over the eight rows of each
 // parity that one read touches, so the 16-byte operand reads (chunk 4h +
 // (lane >> 4)) and the row writes both take the minimum of four passes.
+// bf16: sixteen chunks a row, chunk c of row r at c ^ t(r) with t(r) =
+// (r & 3) + 4((r >> 3) & 3), distinct over the 16 rows row_a(0..15) (and over
+// those + 4) that one operand read touches, so every 16 lanes of the read hit
+// 16 different 16-byte bank groups; a row write spans all 16 chunks of a row.
 template <int P>
 __device__ __forceinline__ int kidx32(int row, int chunk) {
     if constexpr (P == kFp4) return row * 4 + (chunk ^ ((row >> 3) & 3));
+    else if constexpr (P == kBf16) return row * 16 + (chunk ^ ((row & 3) | (((row >> 3) & 3) << 2)));
     else return row * 8 + (chunk ^ ((((row >> 3) & 3) << 1) | ((row >> 1) & 1)));
 }
 
@@ -254,9 +158,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const char* base, i
 }
 
 // This lane's byte offsets inside a 32-key tile, the same for every tile of a
-// split: K codes (fp8: row lane >> 3, chunk lane & 7; fp4: row lane >> 2,
-// chunk lane & 3), K scales (fp4) of row row_a(lane & 15), V codes of row
-// 8(lane >> 4) at dims 8(lane & 15), V scales (fp4) of row 8(lane >> 4). The
+// split: K (bf16: row lane >> 4, chunk lane & 15; fp8: row lane >> 3, chunk
+// lane & 7; fp4: row lane >> 2, chunk lane & 3), K scales (fp4) of row
+// row_a(lane & 15), V of row 8(lane >> 4) at dims 8(lane & 15), V scales
+// (fp4) of row 8(lane >> 4). The
 // other rows a lane reads are these plus a multiple of the row stride, passed
 // as the loads' scalar offset.
 struct Lanes32 {
@@ -265,7 +170,12 @@ struct Lanes32 {
 template <int P>
 __device__ __forceinline__ Lanes32 lanes32(int ik, int iks, int iv, int ivs, int lane) {
     Lanes32 o;
-    if constexpr (P == kFp4) {
+    if constexpr (P == kBf16) {
+        o.k = (lane >> 4) * ik + 16 * (lane & 15);
+        o.ks = 0;
+        o.v = 8 * (lane >> 4) * iv + 16 * (lane & 15);
+        o.vs = 0;
+    } else if constexpr (P == kFp4) {
         o.k = (lane >> 2) * ik + 16 * (lane & 3);
         o.ks = row_a(lane & 15) * iks;
         o.v = 8 * (lane >> 4) * iv + 4 * (lane & 15);
@@ -289,7 +199,7 @@ __device__ __forceinline__ void load_tile32(Tile32<P>& t, const char* kbase, con
                                             const ScaleRows& sc, int iks, int ivs, const Lanes32& ln, int tok0,
                                             int tlast) {
     const int last = min(tlast - tok0, kTile32 - 1);
-    constexpr int kRow = P == kFp4 ? 64 : 128;  // bytes of codes per row (d = 128)
+    constexpr int kRow = P == kFp4 ? 64 : (P == kFp8 ? 128 : 256);  // bytes of a row (d = 128)
     const __amdgpu_buffer_rsrc_t rk = bytes_rsrc(kbase + (int64_t)tok0 * ik, last * ik + kRow);
     const __amdgpu_buffer_rsrc_t rv = bytes_rsrc(vbase + (int64_t)tok0 * iv, last * iv + kRow);
     if constexpr (P == kFp4) {
@@ -304,6 +214,13 @@ __device__ __forceinline__ void load_tile32(Tile32<P>& t, const char* kbase, con
             t.v[u] = __builtin_amdgcn_raw_buffer_load_b32(rv, ln.v, u * iv, kNonTemporal);
             t.vs[u] = __builtin_amdgcn_raw_buffer_load_b32(rvs, ln.vs, u * ivs, kNonTemporal);
         }
+    } else if constexpr (P == kBf16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            t.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 4 * i * ik, kNonTemporal));
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            t.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.v, u * iv, kNonTemporal));
     } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -320,6 +237,21 @@ template <int P, int SEL>
 __device__ __forceinline__ void pv_pair(const Tile32<P>& t, const float (&sc)[8], const bf16x8& pb, f32x4& acc0,
                                         f32x4& acc1) {
     bf16x8 a0, a1;
+    if constexpr (P == kBf16) {
+        // word SEL of a key's 16 bytes holds dims 2 SEL (low half) and 2 SEL + 1
+        u32x4 w0, w1;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t x = t.v[2 * q][SEL], y = t.v[2 * q + 1][SEL];
+            w0[q] = __builtin_amdgcn_perm(y, x, 0x05040100u);
+            w1[q] = __builtin_amdgcn_perm(y, x, 0x07060302u);
+        }
+        a0 = __builtin_bit_cast(bf16x8, w0);
+        a1 = __builtin_bit_cast(bf16x8, w1);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, pb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, pb, acc1, 0, 0, 0);
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
         f32x2 x;
@@ -339,7 +271,18 @@ __device__ __forceinline__ void tile32(const Tile32<P>& t, u32x4* ks, const floa
                                        f32x4 (&acc)[8]) {
     const int g = lane >> 4, ra = row_a(lane & 15);
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (P == kFp4) {
+    if constexpr (P == kBf16) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ks[kidx32<kBf16>((lane >> 4) + 4 * i, lane & 15)] = t.k[i];
+        // step i: dims 32i + 8g .. +7 (chunk 4i + g), the Q operand's bf16 dim order
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u32x4 a = ks[kidx32<kBf16>(ra, 4 * i + g)];
+            const u32x4 b = ks[kidx32<kBf16>(ra + 4, 4 * i + g)];
+            sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qop[i], sa, 0, 0, 0);
+            sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), qop[i], sb, 0, 0, 0);
+        }
+    } else if constexpr (P == kFp4) {
         ks[kidx32<kFp4>(lane >> 2, lane & 3)] = t.k[0];
         ks[kidx32<kFp4>(16 + (lane >> 2), lane & 3)] = t.k[1];
         const uint32_t* ks32 = reinterpret_cast<const uint32_t*>(ks);
@@ -584,7 +527,7 @@ __device__ __forceinline__ void merge_group_if_last(const DecodeParams& p, int b
 // LDS of one decode workgroup: the per-wave K staging buffers and the
 // cross-wave merge (level 1b).
 struct DecodeLds {
-    u32x4 kstage[kWaves][256];
+    u32x4 kstage[kWaves][512];
     float o[kWaves][4][128];
     float m[kWaves][4];
     float l[kWaves][4];
@@ -651,8 +594,6 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         }
         return;
     }
-    const int ntiles = (t_end - t_begin + kTile - 1) / kTile;
-
     constexpr int esz = P == kBf16 ? 2 : 1;  // bytes per stride unit (fp4 spans carry byte strides)
     const char* kbase = static_cast<const char*>(sp.k) + (b * sp.k_sb + g * sp.k_sh + row0 * sp.k_ss) * esz;
     const char* vbase = static_cast<const char*>(sp.v) + (b * sp.v_sb + g * sp.v_sh + row0 * sp.v_ss) * esz;
@@ -684,7 +625,7 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
     float m_run = kNegInf, l_run = 0.f;
     u32x4* ks = lds.kstage[w];
     int k = w;
-    if constexpr (P == kFp4 || P == kFp8) {
+    {
         // 32-key tiles, both products on the MFMA (tile32); two tiles in flight
         const int ntiles32 = (t_end - t_begin + kTile32 - 1) / kTile32;
         f32x4 acc[8];
@@ -730,63 +671,6 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         }
         if (lane < 4) {
             lds.m[w][lane] = m_run;
-            lds.l[w][lane] = lw;
-        }
-    } else {
-        float o[4][8];
-#pragma unroll
-        for (int h = 0; h < 4; ++h)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-
-        // Tile buffers used in turn: the next tile is in flight while the
-        // current one is computed.
-        if (k < ntiles) {
-            Tile ta, tb;
-            load_tile(ta, kbase, vbase, kss, vss, t_begin + kTile * k, t_end - 1, lane);
-            while (true) {
-                const bool more_b = k + kWaves < ntiles;
-                if (more_b) load_tile(tb, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-                compute_tile(ta, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
-                if (!more_b) break;
-                k += kWaves;
-                const bool more_a = k + kWaves < ntiles;
-                if (more_a) load_tile(ta, kbase, vbase, kss, vss, t_begin + kTile * (k + kWaves), t_end - 1, lane);
-                compute_tile(tb, ks, qop, scale2, t_begin + kTile * k, t_end, lane, m_run, l_run, o);
-                if (!more_a) break;
-                k += kWaves;
-            }
-        }
-
-        // Level 1a: merge the four lane groups (keys 4*(lane>>4)..) of this wave.
-        float M = fmaxf(m_run, __shfl_xor(m_run, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        const float f = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - M);
-        float lw = l_run * f;
-        lw += __shfl_xor(lw, 16);
-        lw += __shfl_xor(lw, 32);
-        {
-            const float fh[4] = {quad_bcast<0>(f), quad_bcast<1>(f), quad_bcast<2>(f), quad_bcast<3>(f)};
-#pragma unroll
-            for (int h = 0; h < 4; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    float x = o[h][e] * fh[h];
-                    x += __shfl_xor(x, 16);
-                    x += __shfl_xor(x, 32);
-                    o[h][e] = x;
-                }
-        }
-
-        // Level 1b, first half: each wave's partial into LDS.
-        if (lane < 16) {
-#pragma unroll
-            for (int h = 0; h < 4; ++h)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) lds.o[w][h][8 * lane + e] = o[h][e];
-        }
-        if (lane < 4) {
-            lds.m[w][lane] = M;
             lds.l[w][lane] = lw;
         }
     }
@@ -843,7 +727,7 @@ __device__ __forceinline__ KvSpan main_span(const DecodeParams& p) {
 }
 
 template <bool FP8, bool FUSED>
-__global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_gqa4_d128(DecodeParams p) {
     __shared__ DecodeLds lds;
     decode_wg<FP8 ? kFp8 : kBf16, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
 }
@@ -852,7 +736,7 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128(DecodeParams p) {
 // and skip keys): splits [0, S0) stream span sp0, the others span sp1; one
 // merge over all splits.
 template <int P0, int P1, bool FUSED>
-__global__ __launch_bounds__(256) void decode_gqa4_d128_two(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_gqa4_d128_two(DecodeParams p) {
     __shared__ DecodeLds lds;  // one copy for both branches
     const int s = blockIdx.x;
     if (s < p.S0) decode_wg<P0, FUSED, true>(p, p.sp0, s, s, lds);
@@ -864,7 +748,7 @@ __global__ __launch_bounds__(256) void decode_gqa4_d128_two(DecodeParams p) {
 // splits. Each workgroup reads one precision, so no wave branches between
 // formats.
 template <int P0, int P1, int P2, bool FUSED>
-__global__ __launch_bounds__(256) void decode_gqa4_d128_three(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_gqa4_d128_three(DecodeParams p) {
     __shared__ DecodeLds lds;
     const int s = blockIdx.x;
     if (s < p.S0) decode_wg<P0, FUSED, true>(p, p.sp0, s, s, lds);

@@ -101,10 +101,12 @@ def test_decode_argument_errors(so):
     assert decode(so, Hq=6, Hkv=2) == UNSUPPORTED  # 3 query heads per KV head
     assert decode(so, k=T(FP8, 2 * 1024 * 128, 1024 * 128, 128), v=T(FP8, 2 * 1024 * 128, 1024 * 128, 128)) == INVALID
     assert decode(so, ks=FAKE, vs=FAKE) == INVALID  # scales with bf16 k/v
-    # fp8 rows are read in 32-row tiles with 32-bit byte offsets
+    # rows are read in 32-row tiles with 32-bit byte offsets on the grouped-query path
     big8 = T(FP8, 2 * 1024 * (1 << 26), 1024 * (1 << 26), 1 << 26)
     assert decode(so, k=big8, v=big8, ks=FAKE, vs=FAKE) == INVALID
     assert "2^26" in lib.load_library().attn_last_error().decode()
+    big16 = T(BF16, 2 * 1024 * (1 << 25), 1024 * (1 << 25), 1 << 25)  # 2^26 bytes a row
+    assert decode(so, k=big16, v=big16) == INVALID
     assert decode(so, k=T(F32, 2 * 1024 * 128, 1024 * 128, 128)) == INVALID  # k and v dtypes differ
     assert decode(so, q=T(BF16, 1024, 128, 128, data=FAKE + 2)) == INVALID  # misaligned
     assert decode(so, k=T(BF16, 2 * 1024 * 129, 1024 * 129, 129)) == INVALID
@@ -287,6 +289,8 @@ def test_pi_decode_argument_errors(so):
     assert pi(so, kv=FP8, ks=FAKE, vs=FAKE, period=1 << 19) == INVALID
     assert "2^26" in lib.load_library().attn_last_error().decode()
     assert pi(so, kv=FP8, ks=FAKE, vs=FAKE, period=(1 << 19) - 1, ws=None) == WORKSPACE  # within the limit
+    assert pi(so, period=1 << 18) == INVALID  # bf16: 256-byte rows
+    assert pi(so, period=(1 << 18) - 1, ws=None) == WORKSPACE
     assert pi(so, d=64) == UNSUPPORTED
     assert pi(so, Hq=16) == UNSUPPORTED
     assert pi(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
