@@ -22,7 +22,7 @@ attn_status fail(attn_status st, const char* fmt, ...) {
     return st;
 }
 
-constexpr int kChunkQuantum = 64;  // keys per workgroup step (4 waves x 16 keys)
+constexpr int kChunkQuantum = 64;  // split chunks are a multiple of this many keys
 constexpr int kPrecBf16 = 0, kPrecFp8 = 1, kPrecFp4 = 2;  // span precisions of launch_decode_mfma_two
 // Split-plan cost per key of an fp8 and of an MX fp4 span, against 2 for
 // bf16 (bytes per element), measured on the two-span decodes at 128K keys,
