@@ -171,10 +171,11 @@ ATTN_API int attn_decode_plan(int L_cap, int num_splits, int* chunk);
  *
  * q, k and v need 16-byte aligned data and strides that are multiples of 16
  * bytes. Supported: d in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
- * bf16 or fp8 KV with Hq/Hkv == 4 and d == 128 (grouped-query decode of
- * Llama-style models) runs on MFMA; everything else on the vector ALUs. On
- * that path rows are read 32 at a time with 32-bit byte offsets, so k/v row
- * strides must be below 2^26 bytes (else ATTN_ERR_INVALID_ARG).
+ * bf16 q with bf16 or fp8 KV and d == 128 (every supported Hq/Hkv) runs on
+ * MFMA; fp32 and d == 64 run on the vector ALUs. On the MFMA path rows are
+ * read 32 at a time with 32-bit byte offsets, so k/v row strides must be
+ * below 2^26 bytes (else ATTN_ERR_INVALID_ARG). The merge is fused into the
+ * decode kernel only for Hq/Hkv == 4.
  */
 ATTN_API attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                                  const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B,

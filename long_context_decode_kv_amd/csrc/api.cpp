@@ -276,7 +276,7 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     p.lse = nullptr;
 
     hipError_t e;
-    const bool mfma = q->dtype == ATTN_BF16 && G == 4 && d == 128;
+    const bool mfma = q->dtype == ATTN_BF16 && d == 128;  // every supported G (1, 2, 4, 8)
     // the MFMA path reads 32-key tiles addressed by 32-bit byte offsets
     if (mfma) {
         const int64_t esz = fp8 ? 1 : 2, lim = int64_t(1) << 26;
@@ -290,7 +290,7 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     // the second kernel won (64 splits: 88.5 against 86.8 us).
     const int cus = device_cu_count();
     const int64_t wgs = (int64_t)B * Hkv * pl->S;
-    if (mfma && fused && (int64_t)B * Hkv <= attn::kMaxCounterGroups && pl->S <= attn::kMaxFusedSplits &&
+    if (mfma && G == 4 && fused && (int64_t)B * Hkv <= attn::kMaxCounterGroups && pl->S <= attn::kMaxFusedSplits &&
         cus > 0 && wgs <= cus) {
         p.counters = fused->counters;
         p.ticket_block = ticket_block_for(pl->S);
@@ -307,7 +307,7 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
             if (e != hipSuccess) return fail(ATTN_ERR_HIP, "clearing the merge counters: %s", hipGetErrorString(e));
         }
     }
-    if (mfma) e = attn::launch_decode_mfma(p, fp8 ? attn::DT_FP8 : attn::DT_BF16, stream);
+    if (mfma) e = attn::launch_decode_mfma(p, fp8 ? attn::DT_FP8 : attn::DT_BF16, G, stream);
     else e = attn::launch_decode_valu(p, q->dtype, k->dtype, G, stream);
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
     return ATTN_OK;

@@ -265,7 +265,7 @@ __device__ __forceinline__ void pv_pair(const Tile32<P>& t, const float (&sc)[8]
 }
 
 // One 32-key tile of a wave: scores, softmax update, P.V (see above).
-template <int P>
+template <int P, int G>
 __device__ __forceinline__ void tile32(const Tile32<P>& t, u32x4* ks, const float* e8m0, const bf16x8 (&qop)[4],
                                        float scale2, int tok0, int tend, int lane, float& m_run, float& l_run,
                                        f32x4 (&acc)[8]) {
@@ -327,11 +327,11 @@ __device__ __forceinline__ void tile32(const Tile32<P>& t, u32x4* ks, const floa
 #pragma unroll
     for (int r = 0; r < 4; ++r) tmax = fmaxf(tmax, fmaxf(s[r], s[4 + r]));
     if (__builtin_amdgcn_ballot_w64(tmax > m_run + kHeadroom) != 0) {
-        // the new running max of each head: over the 16 lanes with its lane & 3
-        float hm = fmaxf(tmax, __shfl_xor(tmax, 4));
-        hm = fmaxf(hm, __shfl_xor(hm, 8));
-        hm = fmaxf(hm, __shfl_xor(hm, 16));
-        hm = fmaxf(hm, __shfl_xor(hm, 32));
+        // the new running max of each head: over the 64 / G lanes with its
+        // lane & (G - 1)
+        float hm = tmax;
+#pragma unroll
+        for (int off = G; off < 64; off <<= 1) hm = fmaxf(hm, __shfl_xor(hm, off));
         const float m_new = fmaxf(m_run, hm);
         const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
         l_run *= alpha;
@@ -526,11 +526,12 @@ __device__ __forceinline__ void merge_group_if_last(const DecodeParams& p, int b
 
 // LDS of one decode workgroup: the per-wave K staging buffers and the
 // cross-wave merge (level 1b).
+constexpr int kMaxG = 8;  // query heads per KV head, at most
 struct DecodeLds {
     u32x4 kstage[kWaves][512];
-    float o[kWaves][4][128];
-    float m[kWaves][4];
-    float l[kWaves][4];
+    float o[kWaves][kMaxG][128];
+    float m[kWaves][kMaxG];
+    float l[kWaves][kMaxG];
     float e8m0[256];  // MX fp4 spans: the value of every E8M0 scale byte
 };
 
@@ -538,10 +539,12 @@ struct DecodeLds {
 // TWO (two-span launches): the span's key geometry and log-prior apply; every
 // split of the launch publishes a partial (an empty one the identity) and
 // takes part in the fused merge, which covers all p.S of them.
-template <int P, bool FUSED, bool TWO>
+template <int P, int G, bool FUSED, bool TWO>
 __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& sp, int s, int s_out,
                                           DecodeLds& lds) {
     constexpr bool FP8 = P == kFp8;
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8, "query heads per KV head");
+    static_assert(G == 4 || !FUSED, "the fused merge takes four heads a group");
     const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile rows and bases in scalar registers
@@ -567,8 +570,8 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
     const int n_merge = TWO ? p.S : (L_b + sp.chunk - 1) / sp.chunk;
     if (t_begin >= t_end) {
         // A split past the end of a shorter sequence: the identity partial.
-        for (int i = tid; i < 4 * 128; i += 256) {
-            const int64_t row = (int64_t)b * p.Hq + g * 4 + i / 128;
+        for (int i = tid; i < G * 128; i += 256) {
+            const int64_t row = (int64_t)b * p.Hq + g * G + i / 128;
             if constexpr (FUSED && TWO) {
                 st_agent(p.o_part + (row * p.S + s_out) * 128 + i % 128, 0.f);
                 if (i % 128 == 0) {
@@ -586,10 +589,10 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         if constexpr (FUSED && TWO) merge_group_if_last(p, b, g, n_merge, tid);
         if (FUSED && !TWO && L_b == 0 && s == 0) {
             // an empty sequence: O = 0, lse = -inf (no workgroup of it merges)
-            for (int i = tid; i < 4 * 128; i += 256) {
-                uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)(g * 4 + i / 128) * p.out_sh;
+            for (int i = tid; i < G * 128; i += 256) {
+                uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.out_sb + (int64_t)(g * G + i / 128) * p.out_sh;
                 orow[i % 128] = 0;
-                if (p.lse && i % 128 == 0) p.lse[(int64_t)b * p.Hq + g * 4 + i / 128] = kNegInf;
+                if (p.lse && i % 128 == 0) p.lse[(int64_t)b * p.Hq + g * G + i / 128] = kNegInf;
             }
         }
         return;
@@ -606,9 +609,11 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         sc.vss = sp.vsc_ss * rmul;
     }
 
-    // Q^T operand: column (lane & 15) is query head 4g + (lane & 3); its k-slots
-    // follow the same dim order as the K operand.
-    const __bf16* qrow = static_cast<const __bf16*>(p.q) + b * p.q_sb + (int64_t)(g * 4 + (lane & 3)) * p.q_sh;
+    // Q^T operand: column (lane & 15) is query head G g + (lane & (G - 1)) (the
+    // G heads repeat across the 16 columns); its k-slots follow the same dim
+    // order as the K operand.
+    const __bf16* qrow =
+        static_cast<const __bf16*>(p.q) + b * p.q_sb + (int64_t)(g * G + (lane & (G - 1))) * p.q_sh;
     bf16x8 qop[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -645,80 +650,86 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
                 const bool more_b = k + kWaves < ntiles32;
                 if (more_b)
                     load_tile32<P>(tb, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * (k + kWaves), t_end - 1);
-                tile32<P>(ta, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
+                tile32<P, G>(ta, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
                 if (!more_b) break;
                 k += kWaves;
                 const bool more_a = k + kWaves < ntiles32;
                 if (more_a)
                     load_tile32<P>(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * (k + kWaves), t_end - 1);
-                tile32<P>(tb, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
+                tile32<P, G>(tb, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
                 if (!more_a) break;
                 k += kWaves;
             }
         }
         // The MFMA summed over every key of the wave, so the wave's partial is
-        // complete: lane l holds head l & 3 at dims 32*(l>>4) + 8r + j (acc[j][r]),
-        // the same in the four lanes with equal l & 3 and l >> 4; l_run counts
-        // the keys of lane group l >> 4 once per lane of a head.
+        // complete: lane l holds head l & (G - 1) at dims 32*(l>>4) + 8r + j
+        // (acc[j][r]), the same in the 16 / G lanes with equal l & (G - 1) and
+        // l >> 4; l_run counts the keys of lane group l >> 4 once per lane of a
+        // head.
         float lw = l_run + __shfl_xor(l_run, 16);
         lw += __shfl_xor(lw, 32);
-        if ((lane & 12) == 0) {
-            float* orow = lds.o[w][lane & 3] + 32 * (lane >> 4);
+        if ((lane & 15) < G) {
+            float* orow = lds.o[w][lane & (G - 1)] + 32 * (lane >> 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
                 for (int j = 0; j < 8; ++j) orow[8 * r + j] = acc[j][r];
         }
-        if (lane < 4) {
+        if (lane < G) {
             lds.m[w][lane] = m_run;
             lds.l[w][lane] = lw;
         }
     }
-    // Level 1b: merge the four waves in LDS.
+    // Level 1b: merge the four waves in LDS; thread pass q takes head h and
+    // columns c, c + 1 (G * 64 column pairs over 256 threads).
     __syncthreads();
-
-    const int h = tid >> 6;
-    const int c = (tid & 63) * 2;
-    float mw[kWaves], fw[kWaves];
-    float Mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) {
-        mw[i] = lds.m[i][h];
-        Mx = fmaxf(Mx, mw[i]);
-    }
+    for (int q0 = 0; q0 < G * 64; q0 += 256) {
+        const int qi = q0 + tid;
+        if (qi >= G * 64) break;
+        const int h = qi >> 6;
+        const int c = (qi & 63) * 2;
+        float mw[kWaves], fw[kWaves];
+        float Mx = kNegInf;
 #pragma unroll
-    for (int i = 0; i < kWaves; ++i) fw[i] = (mw[i] == kNegInf) ? 0.f : fast_exp2(mw[i] - Mx);
-    const float L = (fw[0] * lds.l[0][h] + fw[1] * lds.l[1][h]) + (fw[2] * lds.l[2][h] + fw[3] * lds.l[3][h]);
-    f32x2 out;
+        for (int i = 0; i < kWaves; ++i) {
+            mw[i] = lds.m[i][h];
+            Mx = fmaxf(Mx, mw[i]);
+        }
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
-        const float v = (fw[0] * lds.o[0][h][c + cc] + fw[1] * lds.o[1][h][c + cc]) +
-                        (fw[2] * lds.o[2][h][c + cc] + fw[3] * lds.o[3][h][c + cc]);
-        out[cc] = v * vsc;
-    }
-    const int64_t row = (int64_t)b * p.Hq + g * 4 + h;
-    float m_out = Mx * kLn2;
-    if constexpr (TWO) {
-        // the span's log-prior shifts its partial's max (natural-log units)
-        if (sp.prior && p.alpha) {
-            const float a = fminf(fmaxf(p.alpha[row], 0.f), 1.f);
-            m_out += logf(sp.prior == 1 ? a : 1.f - a);
+        for (int i = 0; i < kWaves; ++i) fw[i] = (mw[i] == kNegInf) ? 0.f : fast_exp2(mw[i] - Mx);
+        const float L = (fw[0] * lds.l[0][h] + fw[1] * lds.l[1][h]) + (fw[2] * lds.l[2][h] + fw[3] * lds.l[3][h]);
+        f32x2 out;
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const float v = (fw[0] * lds.o[0][h][c + cc] + fw[1] * lds.o[1][h][c + cc]) +
+                            (fw[2] * lds.o[2][h][c + cc] + fw[3] * lds.o[3][h][c + cc]);
+            out[cc] = v * vsc;
+        }
+        const int64_t row = (int64_t)b * p.Hq + g * G + h;
+        float m_out = Mx * kLn2;
+        if constexpr (TWO) {
+            // the span's log-prior shifts its partial's max (natural-log units)
+            if (sp.prior && p.alpha) {
+                const float a = fminf(fmaxf(p.alpha[row], 0.f), 1.f);
+                m_out += logf(sp.prior == 1 ? a : 1.f - a);
+            }
+        }
+        if constexpr (FUSED) {
+            st_agent2(p.o_part + (row * p.S + s_out) * 128 + c, out);
+            if ((qi & 63) == 0) {
+                st_agent(p.m_part + row * p.S + s_out, m_out);
+                st_agent(p.l_part + row * p.S + s_out, L);
+            }
+        } else {
+            *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s_out) * 128 + c) = out;
+            if ((qi & 63) == 0) {
+                p.m_part[row * p.S + s_out] = m_out;
+                p.l_part[row * p.S + s_out] = L;
+            }
         }
     }
-    if constexpr (FUSED) {
-        st_agent2(p.o_part + (row * p.S + s_out) * 128 + c, out);
-        if ((tid & 63) == 0) {
-            st_agent(p.m_part + row * p.S + s_out, m_out);
-            st_agent(p.l_part + row * p.S + s_out, L);
-        }
-        merge_group_if_last(p, b, g, n_merge, tid);
-    } else {
-        *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s_out) * 128 + c) = out;
-        if ((tid & 63) == 0) {
-            p.m_part[row * p.S + s_out] = m_out;
-            p.l_part[row * p.S + s_out] = L;
-        }
-    }
+    if constexpr (FUSED) merge_group_if_last(p, b, g, n_merge, tid);
 }
 
 __device__ __forceinline__ KvSpan main_span(const DecodeParams& p) {
@@ -726,10 +737,10 @@ __device__ __forceinline__ KvSpan main_span(const DecodeParams& p) {
                   1,         0,      p.L_cap, p.chunk,   kGeomAll, 0, 1, 0};
 }
 
-template <bool FP8, bool FUSED>
-__global__ __launch_bounds__(256, 2) void decode_gqa4_d128(DecodeParams p) {
+template <int G, bool FP8, bool FUSED>
+__global__ __launch_bounds__(256, 2) void decode_gqa_d128(DecodeParams p) {
     __shared__ DecodeLds lds;
-    decode_wg<FP8 ? kFp8 : kBf16, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
+    decode_wg<FP8 ? kFp8 : kBf16, G, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
 }
 
 // Two spans in one launch (a two-precision cache, or pi-Attention's window
@@ -739,8 +750,8 @@ template <int P0, int P1, bool FUSED>
 __global__ __launch_bounds__(256, 2) void decode_gqa4_d128_two(DecodeParams p) {
     __shared__ DecodeLds lds;  // one copy for both branches
     const int s = blockIdx.x;
-    if (s < p.S0) decode_wg<P0, FUSED, true>(p, p.sp0, s, s, lds);
-    else decode_wg<P1, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
+    if (s < p.S0) decode_wg<P0, 4, FUSED, true>(p, p.sp0, s, s, lds);
+    else decode_wg<P1, 4, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
 }
 
 // Three spans in one launch (a cache kept in bf16, fp8 and MX fp4): splits
@@ -751,24 +762,34 @@ template <int P0, int P1, int P2, bool FUSED>
 __global__ __launch_bounds__(256, 2) void decode_gqa4_d128_three(DecodeParams p) {
     __shared__ DecodeLds lds;
     const int s = blockIdx.x;
-    if (s < p.S0) decode_wg<P0, FUSED, true>(p, p.sp0, s, s, lds);
-    else if (s < p.S1) decode_wg<P1, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
-    else decode_wg<P2, FUSED, true>(p, p.sp2, s - p.S1, s, lds);
+    if (s < p.S0) decode_wg<P0, 4, FUSED, true>(p, p.sp0, s, s, lds);
+    else if (s < p.S1) decode_wg<P1, 4, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
+    else decode_wg<P2, 4, FUSED, true>(p, p.sp2, s - p.S1, s, lds);
 }
 
 }  // namespace
 
-hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream) {
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int G, hipStream_t stream) {
     dim3 grid(p.S, p.Hkv, p.B);
     const bool fused = p.counters != nullptr;
-    if (kv_dtype == DT_FP8) {
-        if (fused) hipLaunchKernelGGL((decode_gqa4_d128<true, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((decode_gqa4_d128<true, false>), grid, dim3(256), 0, stream, p);
-    } else {
-        if (fused) hipLaunchKernelGGL((decode_gqa4_d128<false, true>), grid, dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL((decode_gqa4_d128<false, false>), grid, dim3(256), 0, stream, p);
+    const bool fp8 = kv_dtype == DT_FP8;
+    if (fused && G != 4) return hipErrorInvalidValue;  // the fused merge takes four heads a group
+#define ATTN_ONE(GG, F8)                                                                                 \
+    if (G == GG && fp8 == F8) {                                                                          \
+        if (fused) hipLaunchKernelGGL((decode_gqa_d128<GG, F8, GG == 4>), grid, dim3(256), 0, stream, p); \
+        else hipLaunchKernelGGL((decode_gqa_d128<GG, F8, false>), grid, dim3(256), 0, stream, p);        \
+        return hipGetLastError();                                                                        \
     }
-    return hipGetLastError();
+    ATTN_ONE(4, false)
+    ATTN_ONE(4, true)
+    ATTN_ONE(8, false)
+    ATTN_ONE(8, true)
+    ATTN_ONE(2, false)
+    ATTN_ONE(2, true)
+    ATTN_ONE(1, false)
+    ATTN_ONE(1, true)
+#undef ATTN_ONE
+    return hipErrorInvalidValue;  // no kernel for this head ratio
 }
 
 hipError_t launch_decode_mfma_two(const DecodeParams& p, int prec0, int prec1, hipStream_t stream) {

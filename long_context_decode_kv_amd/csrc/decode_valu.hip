@@ -1,6 +1,5 @@
 // Split-KV decode on the vector ALUs: the general path for shapes the MFMA
-// kernel does not cover (fp32 inputs, head dim 64, 1/2/8 query heads per KV
-// head). Same work split and partial format as decode_mfma.hip: workgroup
+// kernel does not cover (fp32 inputs, head dim 64). Same work split and partial format as decode_mfma.hip: workgroup
 // (s, g, b) owns one chunk of keys of KV head g and emits one partial
 // (o, m, l) per query head of the group (explainer of "Tree Attention:
 // Topology-aware Decoding for Long-Context Attention on GPU Clusters",
@@ -216,7 +215,9 @@ hipError_t launch_g(const DecodeParams& p, int G, hipStream_t stream) {
 template <int QDT, int KVDT>
 hipError_t launch_d(const DecodeParams& p, int G, hipStream_t stream) {
     if (p.d == 64) return launch_g<QDT, KVDT, 64>(p, G, stream);
-    if (p.d == 128) return launch_g<QDT, KVDT, 128>(p, G, stream);
+    // bf16 q with d = 128 runs on the MFMA decode (decode_mfma.hip)
+    if constexpr (QDT == DT_F32)
+        if (p.d == 128) return launch_g<QDT, KVDT, 128>(p, G, stream);
     return hipErrorInvalidValue;
 }
 

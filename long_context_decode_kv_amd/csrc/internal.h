@@ -152,7 +152,7 @@ struct PrefillParams {
     const float* alpha;  // or nullptr: no prior
 };
 
-hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, hipStream_t stream);
+hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int G, hipStream_t stream);
 // Two-span decode: fp8_0 / fp8_1 give the KV dtype of sp0 / sp1 (bf16 or fp8).
 // Span precisions: 0 bf16, 1 fp8-e4m3, 2 MX fp4.
 hipError_t launch_decode_mfma_two(const DecodeParams& p, int prec0, int prec1, hipStream_t stream);

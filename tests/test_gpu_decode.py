@@ -191,10 +191,35 @@ def test_workload5_fp8_1m_full_size():
     del dev
 
 
+# ------------------------------------------------------------ MFMA path, other head ratios
+
+@pytest.mark.parametrize("G,fmt,S", [(1, "bf16", 3), (2, "bf16", 5), (8, "bf16", 7), (8, "e4m3", 4), (1, "e4m3", 2),
+                                     (2, "e4m3", 1)])
+def test_mfma_head_ratios(G, fmt, S):
+    wl = 2 if fmt == "bf16" else 5
+    inp = make_inputs(wl, B=2, Hq=2 * G, Hkv=2, L=1500, seed=70 + G + S)
+    _check(inp, S, fmt, what="mfma G=%d %s" % (G, fmt))
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_mfma_head_ratios_ragged_edges(G):
+    lens = np.array([0, 1, 31, 33, 64, 65, 300, 129], np.int32)
+    inp = make_inputs(3, B=8, Hq=2 * G, Hkv=2, L=300, seed=80 + G)
+    inp["kv_lens"] = lens
+    out, lse = _check(inp, 5, "bf16", causal=True, what="mfma G=%d ragged" % G)
+    assert np.all(from_dev(out)[0] == 0.0) and np.all(np.isneginf(lse.cpu().numpy()[0]))
+
+
+def test_g8_full_size_128k():
+    # 64 query heads over 8 KV heads (eight per group), 128K bf16 keys
+    inp = make_inputs(2, Hq=64, Hkv=8, seed=82)
+    _check(inp, 64, "bf16", what="G=8 128K")
+
+
 # ------------------------------------------------------------ vector-ALU path
 
-@pytest.mark.parametrize("G,d,fmt", [(1, 64, "bf16"), (2, 128, "bf16"), (8, 128, "bf16"), (4, 64, "bf16"),
-                                     (1, 128, "f32"), (8, 64, "f32"), (2, 128, "e4m3"), (4, 64, "e4m3")])
+@pytest.mark.parametrize("G,d,fmt", [(1, 64, "bf16"), (2, 64, "bf16"), (8, 64, "bf16"), (4, 64, "bf16"),
+                                     (1, 128, "f32"), (8, 64, "f32"), (2, 64, "e4m3"), (4, 64, "e4m3")])
 def test_valu_paths(G, d, fmt):
     wl = {"bf16": 2, "f32": 1, "e4m3": 5}[fmt]
     inp = make_inputs(wl, B=2, Hq=2 * G, Hkv=2, d=d, L=1111, seed=50 + G + d)
