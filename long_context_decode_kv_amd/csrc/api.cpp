@@ -399,6 +399,9 @@ attn::KvSpan span_of(const attn_tensor* k, const attn_tensor* v, const int32_t* 
     return sp;
 }
 
+// Query heads per KV head the MFMA decode kernels take.
+bool mfma_head_ratio(int G) { return G == 1 || G == 2 || G == 4 || G == 8; }
+
 // Spans are read in 32-key tiles addressed by 32-bit byte offsets from the
 // tile's first row: the distance between the rows a span visits (the row
 // stride in bytes, times the period of a skip span) must stay below 2^26
@@ -468,8 +471,8 @@ attn_status two_span_launch(attn::DecodeParams& p, int S, int prec0, int prec1, 
     // the same rule as the one-span decode (pi decode, 200 workgroups: fused
     // 12.8 us, two kernels 13.5 us; two-precision, 512: fused 65 us, two
     // kernels 64 us)
-    const bool fused = (int64_t)B * Hkv <= attn::kMaxCounterGroups && S <= attn::kMaxFusedSplits && cus > 0 &&
-                       wgs <= cus;
+    const bool fused = Hq == 4 * Hkv && (int64_t)B * Hkv <= attn::kMaxCounterGroups && S <= attn::kMaxFusedSplits &&
+                       cus > 0 && wgs <= cus;
     if (fused) {
         p.counters = counters;
         p.ticket_block = ticket_block_for(S);
@@ -747,8 +750,9 @@ attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, con
     }
     if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
         return fail(ATTN_ERR_UNSUPPORTED, "mixed decode takes bf16 q and out");
-    if (d != 128 || Hq != 4 * Hkv)
-        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+    if (d != 128 || !mfma_head_ratio(Hq / Hkv))
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv in {1, 2, 4, 8} (got %d, %d)", d,
+                    Hq / Hkv);
 
     int auto_hi = 0, auto_lo = 0;
     if ((!num_splits_hi && L_hi_cap) || (!num_splits_lo && L_lo_cap)) {
@@ -821,8 +825,9 @@ attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tensor* k_hi,
     }
     if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
         return fail(ATTN_ERR_UNSUPPORTED, "mixed decode takes bf16 q and out");
-    if (d != 128 || Hq != 4 * Hkv)
-        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+    if (d != 128 || !mfma_head_ratio(Hq / Hkv))
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv in {1, 2, 4, 8} (got %d, %d)", d,
+                    Hq / Hkv);
 
     int auto_hi = 0, auto_lo = 0;
     if ((!num_splits_hi && L_hi_cap) || (!num_splits_lo && L_lo_cap)) {
@@ -913,8 +918,9 @@ attn_status attn_decode_mixed3(const attn_tensor* q, const attn_tensor* k_hi, co
     }
     if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
         return fail(ATTN_ERR_UNSUPPORTED, "mixed decode takes bf16 q and out");
-    if (d != 128 || Hq != 4 * Hkv)
-        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+    if (d != 128 || !mfma_head_ratio(Hq / Hkv))
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv in {1, 2, 4, 8} (got %d, %d)", d,
+                    Hq / Hkv);
 
     int a[3] = {0, 0, 0};
     if ((!num_splits_hi && L_hi_cap) || (!num_splits_mid && L_mid_cap) || (!num_splits_lo && L_lo_cap)) {
@@ -978,8 +984,9 @@ attn_status attn_decode_pi(const attn_tensor* q, const attn_tensor* k, const att
     if (!fp8 && (k_scale || v_scale)) return fail(ATTN_ERR_INVALID_ARG, "scales are only for fp8 k/v");
     if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16 || (k->dtype != ATTN_BF16 && !fp8))
         return fail(ATTN_ERR_UNSUPPORTED, "pi decode takes bf16 q and out, bf16 or fp8 k/v");
-    if (d != 128 || Hq != 4 * Hkv)
-        return fail(ATTN_ERR_UNSUPPORTED, "pi decode supports d = 128 and Hq/Hkv = 4 (got %d, %d)", d, Hq / Hkv);
+    if (d != 128 || !mfma_head_ratio(Hq / Hkv))
+        return fail(ATTN_ERR_UNSUPPORTED, "pi decode supports d = 128 and Hq/Hkv in {1, 2, 4, 8} (got %d, %d)", d,
+                    Hq / Hkv);
     if (window > L_cap) window = L_cap;  // same keys; keeps window arithmetic in range
 
     const PiCaps c = pi_caps(L_cap, window, period);

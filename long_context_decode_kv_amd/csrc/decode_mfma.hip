@@ -746,25 +746,25 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_d128(DecodeParams p) {
 // Two spans in one launch (a two-precision cache, or pi-Attention's window
 // and skip keys): splits [0, S0) stream span sp0, the others span sp1; one
 // merge over all splits.
-template <int P0, int P1, bool FUSED>
-__global__ __launch_bounds__(256, 2) void decode_gqa4_d128_two(DecodeParams p) {
+template <int G, int P0, int P1, bool FUSED>
+__global__ __launch_bounds__(256, 2) void decode_gqa_d128_two(DecodeParams p) {
     __shared__ DecodeLds lds;  // one copy for both branches
     const int s = blockIdx.x;
-    if (s < p.S0) decode_wg<P0, 4, FUSED, true>(p, p.sp0, s, s, lds);
-    else decode_wg<P1, 4, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
+    if (s < p.S0) decode_wg<P0, G, FUSED, true>(p, p.sp0, s, s, lds);
+    else decode_wg<P1, G, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
 }
 
 // Three spans in one launch (a cache kept in bf16, fp8 and MX fp4): splits
 // [0, S0) stream sp0, [S0, S1) sp1, the others sp2; one merge over all
 // splits. Each workgroup reads one precision, so no wave branches between
 // formats.
-template <int P0, int P1, int P2, bool FUSED>
-__global__ __launch_bounds__(256, 2) void decode_gqa4_d128_three(DecodeParams p) {
+template <int G, int P0, int P1, int P2, bool FUSED>
+__global__ __launch_bounds__(256, 2) void decode_gqa_d128_three(DecodeParams p) {
     __shared__ DecodeLds lds;
     const int s = blockIdx.x;
-    if (s < p.S0) decode_wg<P0, 4, FUSED, true>(p, p.sp0, s, s, lds);
-    else if (s < p.S1) decode_wg<P1, 4, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
-    else decode_wg<P2, 4, FUSED, true>(p, p.sp2, s - p.S1, s, lds);
+    if (s < p.S0) decode_wg<P0, G, FUSED, true>(p, p.sp0, s, s, lds);
+    else if (s < p.S1) decode_wg<P1, G, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
+    else decode_wg<P2, G, FUSED, true>(p, p.sp2, s - p.S1, s, lds);
 }
 
 }  // namespace
@@ -795,26 +795,44 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int G, hipStr
 hipError_t launch_decode_mfma_two(const DecodeParams& p, int prec0, int prec1, hipStream_t stream) {
     dim3 grid(p.S, p.Hkv, p.B);
     const bool f = p.counters != nullptr;
-#define ATTN_TWO(P0, P1)                                                                                  \
-    if (prec0 == P0 && prec1 == P1) {                                                                     \
-        if (f) hipLaunchKernelGGL((decode_gqa4_d128_two<P0, P1, true>), grid, dim3(256), 0, stream, p);  \
-        else hipLaunchKernelGGL((decode_gqa4_d128_two<P0, P1, false>), grid, dim3(256), 0, stream, p);   \
-        return hipGetLastError();                                                                         \
+    const int G = p.Hkv > 0 ? p.Hq / p.Hkv : 0;
+    if (f && G != 4) return hipErrorInvalidValue;  // the fused merge takes four heads a group
+#define ATTN_TWO(GG, P0, P1)                                                                                    \
+    if (G == GG && prec0 == P0 && prec1 == P1) {                                                                \
+        if (f) hipLaunchKernelGGL((decode_gqa_d128_two<GG, P0, P1, GG == 4>), grid, dim3(256), 0, stream, p);  \
+        else hipLaunchKernelGGL((decode_gqa_d128_two<GG, P0, P1, false>), grid, dim3(256), 0, stream, p);      \
+        return hipGetLastError();                                                                               \
     }
-    ATTN_TWO(kBf16, kFp8)
-    ATTN_TWO(kBf16, kBf16)
-    ATTN_TWO(kFp8, kFp8)
-    ATTN_TWO(kBf16, kFp4)
+#define ATTN_TWO_G(P0, P1) ATTN_TWO(4, P0, P1) ATTN_TWO(8, P0, P1) ATTN_TWO(2, P0, P1) ATTN_TWO(1, P0, P1)
+    ATTN_TWO_G(kBf16, kFp8)
+    ATTN_TWO_G(kBf16, kBf16)
+    ATTN_TWO_G(kFp8, kFp8)
+    ATTN_TWO_G(kBf16, kFp4)
+#undef ATTN_TWO_G
 #undef ATTN_TWO
-    return hipErrorInvalidValue;  // no kernel for this pair of precisions
+    return hipErrorInvalidValue;  // no kernel for this pair of precisions or head ratio
 }
 
 hipError_t launch_decode_mfma_three(const DecodeParams& p, int prec0, int prec1, int prec2, hipStream_t stream) {
     if (prec0 != kBf16 || prec1 != kFp8 || prec2 != kFp4) return hipErrorInvalidValue;
     dim3 grid(p.S, p.Hkv, p.B);
-    if (p.counters) hipLaunchKernelGGL((decode_gqa4_d128_three<kBf16, kFp8, kFp4, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((decode_gqa4_d128_three<kBf16, kFp8, kFp4, false>), grid, dim3(256), 0, stream, p);
-    return hipGetLastError();
+    const bool f = p.counters != nullptr;
+    const int G = p.Hkv > 0 ? p.Hq / p.Hkv : 0;
+    if (f && G != 4) return hipErrorInvalidValue;
+#define ATTN_THREE(GG)                                                                                            \
+    if (G == GG) {                                                                                                \
+        if (f) hipLaunchKernelGGL((decode_gqa_d128_three<GG, kBf16, kFp8, kFp4, GG == 4>), grid, dim3(256), 0,   \
+                                  stream, p);                                                                     \
+        else hipLaunchKernelGGL((decode_gqa_d128_three<GG, kBf16, kFp8, kFp4, false>), grid, dim3(256), 0, stream, \
+                                p);                                                                               \
+        return hipGetLastError();                                                                                 \
+    }
+    ATTN_THREE(4)
+    ATTN_THREE(8)
+    ATTN_THREE(2)
+    ATTN_THREE(1)
+#undef ATTN_THREE
+    return hipErrorInvalidValue;
 }
 
 }  // namespace attn

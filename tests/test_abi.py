@@ -215,7 +215,7 @@ def test_mixed_decode_argument_errors(so):
     assert mixed(so, ks=None) == INVALID  # the fp8 span needs its scales
     assert mixed(so, khi=T(FP8, 2 * 256 * 128, 256 * 128, 128)) == UNSUPPORTED  # bf16 span holds fp8
     assert mixed(so, klo=T(BF16, 2 * 1024 * 128, 1024 * 128, 128)) == UNSUPPORTED  # fp8 span holds bf16
-    assert mixed(so, Hq=16, Hkv=2) == UNSUPPORTED  # 8 query heads per KV head
+    assert mixed(so, Hq=6, Hkv=2) == UNSUPPORTED  # 3 query heads per KV head
     assert mixed(so, d=64) == UNSUPPORTED
     assert mixed(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
     assert mixed(so, Hq=6, Hkv=4) == INVALID
@@ -260,7 +260,7 @@ def test_mixed_fp4_decode_argument_errors(so):
     assert mixed_fp4(so, klo=T(MXFP4, 0, 0, 72)) == INVALID  # code rows must be 16-byte multiples
     assert mixed_fp4(so, klo=T(MXFP4, 0, 0, 1 << 26)) == INVALID  # row stride too large for the tile offsets
     assert mixed_fp4(so, d=64) == UNSUPPORTED
-    assert mixed_fp4(so, Hq=16, Hkv=2) == UNSUPPORTED
+    assert mixed_fp4(so, Hq=6, Hkv=2) == UNSUPPORTED
     assert mixed_fp4(so, ws=None) == WORKSPACE
     assert mixed_fp4(so, ws_bytes=lib.attn_decode_workspace_size(1, 8, 128, 6) - 1) == WORKSPACE
     assert "6 splits" in lib.load_library().attn_last_error().decode()
@@ -292,7 +292,7 @@ def test_pi_decode_argument_errors(so):
     assert pi(so, period=1 << 18) == INVALID  # bf16: 256-byte rows
     assert pi(so, period=(1 << 18) - 1, ws=None) == WORKSPACE
     assert pi(so, d=64) == UNSUPPORTED
-    assert pi(so, Hq=16) == UNSUPPORTED
+    assert pi(so, Hq=6) == UNSUPPORTED
     assert pi(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
     assert pi(so, ws=None) == WORKSPACE
     # window 513 keys in 2 splits, (4096 - 2 - 512) // 16 + 1 = 224 skip keys in 2 splits
@@ -378,7 +378,7 @@ def test_mixed3_decode_argument_errors(so):
     assert mixed3(so, ksc=False) == INVALID  # the fp4 span needs its scales
     assert mixed3(so, mid_dtype=BF16) == UNSUPPORTED
     assert mixed3(so, lo_dtype=FP8) == UNSUPPORTED
-    assert mixed3(so, Hq=16) == UNSUPPORTED
+    assert mixed3(so, Hq=6) == UNSUPPORTED
     assert mixed3(so, d=64) == UNSUPPORTED
     assert mixed3(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
     assert mixed3(so, ws=None) == WORKSPACE

@@ -33,6 +33,14 @@ def test_mixed_small(S_hi, S_lo):
     _check(inp, S_hi, S_lo, what="mixed L=3000")
 
 
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_mixed_other_head_ratios(G):
+    # G query heads per KV head; per-head lengths leave a head without bf16 keys
+    inp = make_mixed_inputs(B=2, Hq=2 * G, Hkv=2, L=3000, lens=(0.0, 1.0), seed=66 + G)
+    inp["hi_lens"][0] = 0
+    _check(inp, 3, 7, what="mixed G=%d" % G)
+
+
 def test_mixed_per_head_ragged_lengths_and_empty_spans():
     inp = make_mixed_inputs(B=3, Hq=8, Hkv=2, L=4000, lens=(0.0, 1.0), seed=61)
     inp["hi_lens"][0] = 0  # a head with fp8 keys only

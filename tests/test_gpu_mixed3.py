@@ -49,6 +49,12 @@ def test_mixed3_small(S):
     _check(inp, S, what="mixed3 L=3000")
 
 
+@pytest.mark.parametrize("G", [2, 8])
+def test_mixed3_other_head_ratios(G):
+    inp = make_mixed3_inputs(B=2, Hq=2 * G, Hkv=2, L=3000, seed=104 + G)
+    _check(inp, (2, 2, 4), what="mixed3 G=%d" % G)
+
+
 def test_mixed3_per_head_ragged_lengths_and_empty_spans():
     inp = make_mixed3_inputs(B=3, Hq=8, Hkv=2, L=5000, lens=(0.0, 1.0), seed=101)
     inp["hi_lens"][0] = 0                     # no bf16 key

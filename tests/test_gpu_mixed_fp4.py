@@ -36,6 +36,12 @@ def test_mixed_fp4_small(S_hi, S_lo):
     _check(inp, S_hi, S_lo, what="fp4 L=3000")
 
 
+@pytest.mark.parametrize("G", [1, 8])
+def test_mixed_fp4_other_head_ratios(G):
+    inp = make_mixed_inputs(9, B=2, Hq=2 * G, Hkv=2, L=3000, seed=98 + G)
+    _check(inp, 3, 7, what="mixed fp4 G=%d" % G)
+
+
 def test_mixed_fp4_per_head_ragged_lengths_and_empty_spans():
     inp = make_mixed_inputs(9, B=3, Hq=8, Hkv=2, L=4000, lens=(0.0, 1.0), seed=91)
     inp["hi_lens"][0] = 0  # a head with fp4 keys only

@@ -54,6 +54,12 @@ def test_pi_ragged_lengths_below_and_above_the_window():
     assert np.isneginf(lse.cpu().numpy()[1, 2])
 
 
+@pytest.mark.parametrize("G,kv", [(1, "bf16"), (8, "bf16"), (2, "e4m3")])
+def test_pi_other_head_ratios(G, kv):
+    inp = make_inputs(2 if kv == "bf16" else 5, B=2, Hq=2 * G, Hkv=2, L=3000, seed=78 + G)
+    _check(inp, 256, 16, _alpha(2, 2 * G, 79 + G), what="pi G=%d %s" % (G, kv), kind=kv)
+
+
 def test_pi_fp8_cache():
     inp = make_inputs(5, B=2, Hq=8, Hkv=2, L=6000, seed=76)
     _check(inp, 1024, 32, _alpha(2, 8, 77), what="pi fp8", kind="e4m3")
