@@ -276,7 +276,7 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     p.lse = nullptr;
 
     hipError_t e;
-    const bool mfma = q->dtype == ATTN_BF16 && d == 128;  // every supported G (1, 2, 4, 8)
+    const bool mfma = q->dtype == ATTN_BF16;  // every supported d (64, 128) and G (1, 2, 4, 8)
     // the MFMA path reads 32-key tiles addressed by 32-bit byte offsets
     if (mfma) {
         const int64_t esz = fp8 ? 1 : 2, lim = int64_t(1) << 26;
@@ -290,7 +290,7 @@ attn_status decode_level1(const attn_tensor* q, const attn_tensor* k, const attn
     // the second kernel won (64 splits: 88.5 against 86.8 us).
     const int cus = device_cu_count();
     const int64_t wgs = (int64_t)B * Hkv * pl->S;
-    if (mfma && G == 4 && fused && (int64_t)B * Hkv <= attn::kMaxCounterGroups && pl->S <= attn::kMaxFusedSplits &&
+    if (mfma && G == 4 && d == 128 && fused && (int64_t)B * Hkv <= attn::kMaxCounterGroups && pl->S <= attn::kMaxFusedSplits &&
         cus > 0 && wgs <= cus) {
         p.counters = fused->counters;
         p.ticket_block = ticket_block_for(pl->S);
@@ -471,7 +471,7 @@ attn_status two_span_launch(attn::DecodeParams& p, int S, int prec0, int prec1, 
     // the same rule as the one-span decode (pi decode, 200 workgroups: fused
     // 12.8 us, two kernels 13.5 us; two-precision, 512: fused 65 us, two
     // kernels 64 us)
-    const bool fused = Hq == 4 * Hkv && (int64_t)B * Hkv <= attn::kMaxCounterGroups && S <= attn::kMaxFusedSplits &&
+    const bool fused = Hq == 4 * Hkv && d == 128 && (int64_t)B * Hkv <= attn::kMaxCounterGroups && S <= attn::kMaxFusedSplits &&
                        cus > 0 && wgs <= cus;
     if (fused) {
         p.counters = counters;
@@ -750,9 +750,9 @@ attn_status attn_decode_mixed(const attn_tensor* q, const attn_tensor* k_hi, con
     }
     if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16)
         return fail(ATTN_ERR_UNSUPPORTED, "mixed decode takes bf16 q and out");
-    if (d != 128 || !mfma_head_ratio(Hq / Hkv))
-        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d = 128 and Hq/Hkv in {1, 2, 4, 8} (got %d, %d)", d,
-                    Hq / Hkv);
+    if ((d != 64 && d != 128) || !mfma_head_ratio(Hq / Hkv))
+        return fail(ATTN_ERR_UNSUPPORTED, "mixed decode supports d in {64, 128} and Hq/Hkv in {1, 2, 4, 8} (got %d, %d)",
+                    d, Hq / Hkv);
 
     int auto_hi = 0, auto_lo = 0;
     if ((!num_splits_hi && L_hi_cap) || (!num_splits_lo && L_lo_cap)) {
@@ -984,8 +984,8 @@ attn_status attn_decode_pi(const attn_tensor* q, const attn_tensor* k, const att
     if (!fp8 && (k_scale || v_scale)) return fail(ATTN_ERR_INVALID_ARG, "scales are only for fp8 k/v");
     if (q->dtype != ATTN_BF16 || out->dtype != ATTN_BF16 || (k->dtype != ATTN_BF16 && !fp8))
         return fail(ATTN_ERR_UNSUPPORTED, "pi decode takes bf16 q and out, bf16 or fp8 k/v");
-    if (d != 128 || !mfma_head_ratio(Hq / Hkv))
-        return fail(ATTN_ERR_UNSUPPORTED, "pi decode supports d = 128 and Hq/Hkv in {1, 2, 4, 8} (got %d, %d)", d,
+    if ((d != 64 && d != 128) || !mfma_head_ratio(Hq / Hkv))
+        return fail(ATTN_ERR_UNSUPPORTED, "pi decode supports d in {64, 128} and Hq/Hkv in {1, 2, 4, 8} (got %d, %d)", d,
                     Hq / Hkv);
     if (window > L_cap) window = L_cap;  // same keys; keeps window arithmetic in range
 

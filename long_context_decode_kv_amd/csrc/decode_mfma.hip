@@ -107,20 +107,35 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t w0, uint32_t w1) {
 // fp8's per-head K scale is folded into the score scale and its V scale is
 // applied to the partial; fp4's block scales are applied in the conversion.
 constexpr int kTile32 = 32;
-template <int P>
+
+// Geometry of a span's 32-key tile with head dim D: bytes of a K or V row,
+// 16-byte chunks a K row has, and K loads a lane issues per tile (one 16-byte
+// chunk each: a load instruction covers 64 / kChunks whole rows).
+template <int P, int D>
+struct Geo {
+    static constexpr int kRowBytes = P == kBf16 ? 2 * D : (P == kFp8 ? D : D / 2);
+    static constexpr int kChunks = kRowBytes / 16;
+    static constexpr int kRowsPerLoad = 64 / kChunks;
+    static constexpr int kLoads = kTile32 / kRowsPerLoad;
+    static constexpr int kSteps = D / 32;  // MFMA steps over d for the scores
+    static_assert(kChunks == 4 || kChunks == 8 || kChunks == 16, "tile geometry");
+};
+
+template <int P, int D>
 struct Tile32;
-template <>
-struct Tile32<kBf16> {
-    u32x4 k[8];  // key rows (lane >> 4) + 4i: 16-byte chunk lane & 15 (dims 8(lane & 15) ..)
-    u32x4 v[8];  // key 8*(lane >> 4) + u: its 8 values at dims 8*(lane & 15) .. +7
+template <int D>
+struct Tile32<kBf16, D> {
+    u32x4 k[Geo<kBf16, D>::kLoads];  // key row lane / kChunks + kRowsPerLoad i: chunk lane % kChunks
+    u32x4 v[8];  // key 8*(lane >> 4) + u: its 8 values at dims 8*(lane & (D/8 - 1)) .. +7
 };
-template <>
-struct Tile32<kFp8> {
-    u32x4 k[4];  // key rows (lane >> 3) + 8i: 16-byte chunk lane & 7 (dims 16(lane & 7) ..)
-    u32x2 v[8];  // key 8*(lane >> 4) + u: its 8 codes at dims 8*(lane & 15) .. +7
+template <int D>
+struct Tile32<kFp8, D> {
+    u32x4 k[Geo<kFp8, D>::kLoads];
+    u32x2 v[8];  // key 8*(lane >> 4) + u: its 8 codes at dims 8*(lane & (D/8 - 1)) .. +7
 };
-template <>
-struct Tile32<kFp4> {
+template <int D>
+struct Tile32<kFp4, D> {
+    static_assert(D == 128, "MX fp4 spans take d = 128");
     u32x4 k[2];      // key rows lane >> 2 and 16 + (lane >> 2): 16-byte chunk lane & 3 (32 codes, block lane & 3)
     uint32_t ks[2];  // scale words of key rows row_a(lane & 15) and that + 4 (byte i: block i)
     uint32_t v[8];   // key 8*(lane >> 4) + u: its 8 codes at dims 8*(lane & 15) .. +7
@@ -130,21 +145,23 @@ struct Tile32<kFp4> {
 // The tile row score product a takes as its A row m.
 __device__ __forceinline__ int row_a(int m) { return 8 * (m >> 2) + (m & 3); }
 
-// K stages of a 32-row tile (u32x4 units). fp4: four 16-byte chunks a row,
-// chunk c of row r at c ^ ((r >> 3) & 3); the operand reads (4-byte word
-// lane >> 4 of chunk i of row row_a(lane & 15), or that + 4) hit 64 distinct
-// banks. fp8: eight chunks a row, chunk c of row r at c ^ s(r) with s(r) =
-// 2((r >> 3) & 3) + ((r >> 1) & 1), distinct over the eight rows of each
-// parity that one read touches, so the 16-byte operand reads (chunk 4h +
-// (lane >> 4)) and the row writes both take the minimum of four passes.
-// bf16: sixteen chunks a row, chunk c of row r at c ^ t(r) with t(r) =
-// (r & 3) + 4((r >> 3) & 3), distinct over the 16 rows row_a(0..15) (and over
-// those + 4) that one operand read touches, so every 16 lanes of the read hit
-// 16 different 16-byte bank groups; a row write spans all 16 chunks of a row.
-template <int P>
+// K stages of a 32-row tile (u32x4 units), by chunks a row. Four chunks
+// (fp4 at d = 128, fp8 at d = 64): chunk c of row r at c ^ ((r >> 3) & 3);
+// the operand reads (16 bytes, or for fp4 4-byte word lane >> 4, of chunk
+// lane >> 4 or i of row row_a(lane & 15), or that + 4) hit distinct bank
+// groups. Eight chunks (fp8 at d = 128, bf16 at d = 64): chunk c of row r at
+// c ^ s(r) with s(r) = 2((r >> 3) & 3) + ((r >> 1) & 1), distinct over the
+// eight rows of each parity that one read touches, so the 16-byte operand
+// reads (chunk 4h + (lane >> 4)) and the row writes both take the minimum of
+// four passes. Sixteen chunks (bf16 at d = 128): chunk c of row r at c ^ t(r)
+// with t(r) = (r & 3) + 4((r >> 3) & 3), distinct over the 16 rows
+// row_a(0..15) (and over those + 4) that one operand read touches, so every
+// 16 lanes of the read hit 16 different 16-byte bank groups; a row write
+// spans all 16 chunks of a row.
+template <int CH>
 __device__ __forceinline__ int kidx32(int row, int chunk) {
-    if constexpr (P == kFp4) return row * 4 + (chunk ^ ((row >> 3) & 3));
-    else if constexpr (P == kBf16) return row * 16 + (chunk ^ ((row & 3) | (((row >> 3) & 3) << 2)));
+    if constexpr (CH == 4) return row * 4 + (chunk ^ ((row >> 3) & 3));
+    else if constexpr (CH == 16) return row * 16 + (chunk ^ ((row & 3) | (((row >> 3) & 3) << 2)));
     else return row * 8 + (chunk ^ ((((row >> 3) & 3) << 1) | ((row >> 1) & 1)));
 }
 
@@ -158,32 +175,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t bytes_rsrc(const char* base, i
 }
 
 // This lane's byte offsets inside a 32-key tile, the same for every tile of a
-// split: K (bf16: row lane >> 4, chunk lane & 15; fp8: row lane >> 3, chunk
-// lane & 7; fp4: row lane >> 2, chunk lane & 3), K scales (fp4) of row
-// row_a(lane & 15), V of row 8(lane >> 4) at dims 8(lane & 15), V scales
-// (fp4) of row 8(lane >> 4). The
-// other rows a lane reads are these plus a multiple of the row stride, passed
-// as the loads' scalar offset.
+// split: K (row lane / kChunks, chunk lane % kChunks), K scales (fp4) of row
+// row_a(lane & 15), V of row 8(lane >> 4) at dims 8(lane & (D/8 - 1)) (at
+// d = 64 lanes l and l + 8 of each 16 read the same bytes: the products'
+// rows for dims past 64 are computed and dropped), V scales (fp4) of row
+// 8(lane >> 4). The other rows a lane reads are these plus a multiple of the
+// row stride, passed as the loads' scalar offset.
 struct Lanes32 {
     uint32_t k, ks, v, vs;
 };
-template <int P>
+template <int P, int D>
 __device__ __forceinline__ Lanes32 lanes32(int ik, int iks, int iv, int ivs, int lane) {
+    using Gm = Geo<P, D>;
     Lanes32 o;
-    if constexpr (P == kBf16) {
-        o.k = (lane >> 4) * ik + 16 * (lane & 15);
-        o.ks = 0;
-        o.v = 8 * (lane >> 4) * iv + 16 * (lane & 15);
-        o.vs = 0;
-    } else if constexpr (P == kFp4) {
-        o.k = (lane >> 2) * ik + 16 * (lane & 3);
+    o.k = (lane / Gm::kChunks) * ik + 16 * (lane % Gm::kChunks);
+    constexpr int kVBytes = P == kBf16 ? 16 : (P == kFp8 ? 8 : 4);  // 8 values of a V row
+    o.v = 8 * (lane >> 4) * iv + kVBytes * (lane & (D / 8 - 1));
+    if constexpr (P == kFp4) {
         o.ks = row_a(lane & 15) * iks;
-        o.v = 8 * (lane >> 4) * iv + 4 * (lane & 15);
         o.vs = 8 * (lane >> 4) * ivs;
     } else {
-        o.k = (lane >> 3) * ik + 16 * (lane & 7);
         o.ks = 0;
-        o.v = 8 * (lane >> 4) * iv + 8 * (lane & 15);
         o.vs = 0;
     }
     return o;
@@ -194,19 +206,21 @@ __device__ __forceinline__ Lanes32 lanes32(int ik, int iks, int iv, int ivs, int
 // no clamping (a zero key scores 0 and is masked; a zero value adds nothing),
 // and the lanes' addresses are fixed offsets (the host keeps row strides below
 // 2^26 bytes, so 32 rows fit 32-bit offsets).
-template <int P>
-__device__ __forceinline__ void load_tile32(Tile32<P>& t, const char* kbase, const char* vbase, int ik, int iv,
+template <int P, int D>
+__device__ __forceinline__ void load_tile32(Tile32<P, D>& t, const char* kbase, const char* vbase, int ik, int iv,
                                             const ScaleRows& sc, int iks, int ivs, const Lanes32& ln, int tok0,
                                             int tlast) {
+    using Gm = Geo<P, D>;
     const int last = min(tlast - tok0, kTile32 - 1);
-    constexpr int kRow = P == kFp4 ? 64 : (P == kFp8 ? 128 : 256);  // bytes of a row (d = 128)
-    const __amdgpu_buffer_rsrc_t rk = bytes_rsrc(kbase + (int64_t)tok0 * ik, last * ik + kRow);
-    const __amdgpu_buffer_rsrc_t rv = bytes_rsrc(vbase + (int64_t)tok0 * iv, last * iv + kRow);
+    const __amdgpu_buffer_rsrc_t rk = bytes_rsrc(kbase + (int64_t)tok0 * ik, last * ik + Gm::kRowBytes);
+    const __amdgpu_buffer_rsrc_t rv = bytes_rsrc(vbase + (int64_t)tok0 * iv, last * iv + Gm::kRowBytes);
+#pragma unroll
+    for (int i = 0; i < Gm::kLoads; ++i)
+        t.k[i] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, Gm::kRowsPerLoad * i * ik, kNonTemporal));
     if constexpr (P == kFp4) {
         const __amdgpu_buffer_rsrc_t rks = bytes_rsrc(sc.k + (int64_t)tok0 * iks, last * iks + 4);
         const __amdgpu_buffer_rsrc_t rvs = bytes_rsrc(sc.v + (int64_t)tok0 * ivs, last * ivs + 4);
-        t.k[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 0, kNonTemporal));
-        t.k[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 16 * ik, kNonTemporal));
         t.ks[0] = __builtin_amdgcn_raw_buffer_load_b32(rks, ln.ks, 0, kNonTemporal);
         t.ks[1] = __builtin_amdgcn_raw_buffer_load_b32(rks, ln.ks, 4 * iks, kNonTemporal);
 #pragma unroll
@@ -216,15 +230,9 @@ __device__ __forceinline__ void load_tile32(Tile32<P>& t, const char* kbase, con
         }
     } else if constexpr (P == kBf16) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            t.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 4 * i * ik, kNonTemporal));
-#pragma unroll
         for (int u = 0; u < 8; ++u)
             t.v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, ln.v, u * iv, kNonTemporal));
     } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            t.k[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ln.k, 8 * i * ik, kNonTemporal));
 #pragma unroll
         for (int u = 0; u < 8; ++u)
             t.v[u] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv, ln.v, u * iv, kNonTemporal));
@@ -233,8 +241,8 @@ __device__ __forceinline__ void load_tile32(Tile32<P>& t, const char* kbase, con
 
 // P.V products 2 SEL and 2 SEL + 1: values 2 SEL and 2 SEL + 1 of every key
 // (dims 8m + 2 SEL and 8m + 2 SEL + 1 of A row m).
-template <int P, int SEL>
-__device__ __forceinline__ void pv_pair(const Tile32<P>& t, const float (&sc)[8], const bf16x8& pb, f32x4& acc0,
+template <int P, int D, int SEL>
+__device__ __forceinline__ void pv_pair(const Tile32<P, D>& t, const float (&sc)[8], const bf16x8& pb, f32x4& acc0,
                                         f32x4& acc1) {
     bf16x8 a0, a1;
     if constexpr (P == kBf16) {
@@ -265,44 +273,42 @@ __device__ __forceinline__ void pv_pair(const Tile32<P>& t, const float (&sc)[8]
 }
 
 // One 32-key tile of a wave: scores, softmax update, P.V (see above).
-template <int P, int G>
-__device__ __forceinline__ void tile32(const Tile32<P>& t, u32x4* ks, const float* e8m0, const bf16x8 (&qop)[4],
+template <int P, int D, int G>
+__device__ __forceinline__ void tile32(const Tile32<P, D>& t, u32x4* ks, const float* e8m0, const bf16x8 (&qop)[4],
                                        float scale2, int tok0, int tend, int lane, float& m_run, float& l_run,
                                        f32x4 (&acc)[8]) {
+    using Gm = Geo<P, D>;
+    constexpr int CH = Gm::kChunks;
     const int g = lane >> 4, ra = row_a(lane & 15);
     f32x4 sa = {0.f, 0.f, 0.f, 0.f}, sb = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (P == kBf16) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) ks[kidx32<kBf16>((lane >> 4) + 4 * i, lane & 15)] = t.k[i];
+    for (int i = 0; i < Gm::kLoads; ++i) ks[kidx32<CH>(lane / CH + Gm::kRowsPerLoad * i, lane % CH)] = t.k[i];
+    if constexpr (P == kBf16) {
         // step i: dims 32i + 8g .. +7 (chunk 4i + g), the Q operand's bf16 dim order
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x4 a = ks[kidx32<kBf16>(ra, 4 * i + g)];
-            const u32x4 b = ks[kidx32<kBf16>(ra + 4, 4 * i + g)];
+        for (int i = 0; i < Gm::kSteps; ++i) {
+            const u32x4 a = ks[kidx32<CH>(ra, 4 * i + g)];
+            const u32x4 b = ks[kidx32<CH>(ra + 4, 4 * i + g)];
             sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), qop[i], sa, 0, 0, 0);
             sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, b), qop[i], sb, 0, 0, 0);
         }
     } else if constexpr (P == kFp4) {
-        ks[kidx32<kFp4>(lane >> 2, lane & 3)] = t.k[0];
-        ks[kidx32<kFp4>(16 + (lane >> 2), lane & 3)] = t.k[1];
         const uint32_t* ks32 = reinterpret_cast<const uint32_t*>(ks);
         // step i is scale block i: dims 32i + 8g .. +7 of this lane's rows
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bf16x8 a = fp4x8_to_bf16(ks32[4 * kidx32<kFp4>(ra, i) + g], e8m0[(t.ks[0] >> (8 * i)) & 255u]);
+            const bf16x8 a = fp4x8_to_bf16(ks32[4 * kidx32<CH>(ra, i) + g], e8m0[(t.ks[0] >> (8 * i)) & 255u]);
             sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qop[i], sa, 0, 0, 0);
-            const bf16x8 b = fp4x8_to_bf16(ks32[4 * kidx32<kFp4>(ra + 4, i) + g], e8m0[(t.ks[1] >> (8 * i)) & 255u]);
+            const bf16x8 b = fp4x8_to_bf16(ks32[4 * kidx32<CH>(ra + 4, i) + g], e8m0[(t.ks[1] >> (8 * i)) & 255u]);
             sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, qop[i], sb, 0, 0, 0);
         }
     } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ks[kidx32<kFp8>((lane >> 3) + 8 * i, lane & 7)] = t.k[i];
         // steps 2h and 2h + 1 take the two halves of chunk 4h + g: dims
         // 64h + 16g .. +7 and +8 .. +15 (the Q operand's fp8 dim order)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const u32x4 a = ks[kidx32<kFp8>(ra, 4 * h + g)];
-            const u32x4 b = ks[kidx32<kFp8>(ra + 4, 4 * h + g)];
+        for (int h = 0; h < Gm::kSteps / 2; ++h) {
+            const u32x4 a = ks[kidx32<CH>(ra, 4 * h + g)];
+            const u32x4 b = ks[kidx32<CH>(ra + 4, 4 * h + g)];
             sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[0], a[1]), qop[2 * h], sa, 0, 0, 0);
             sb = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(b[0], b[1]), qop[2 * h], sb, 0, 0, 0);
             sa = __builtin_amdgcn_mfma_f32_16x16x32_bf16(e4m3x8_to_bf16(a[2], a[3]), qop[2 * h + 1], sa, 0, 0, 0);
@@ -357,10 +363,10 @@ __device__ __forceinline__ void tile32(const Tile32<P>& t, u32x4* ks, const floa
 #pragma unroll
         for (int u = 0; u < 8; ++u) sc[u] = e8m0[(t.vs[u] >> sh) & 255u];
     }
-    pv_pair<P, 0>(t, sc, pb, acc[0], acc[1]);
-    pv_pair<P, 1>(t, sc, pb, acc[2], acc[3]);
-    pv_pair<P, 2>(t, sc, pb, acc[4], acc[5]);
-    pv_pair<P, 3>(t, sc, pb, acc[6], acc[7]);
+    pv_pair<P, D, 0>(t, sc, pb, acc[0], acc[1]);
+    pv_pair<P, D, 1>(t, sc, pb, acc[2], acc[3]);
+    pv_pair<P, D, 2>(t, sc, pb, acc[4], acc[5]);
+    pv_pair<P, D, 3>(t, sc, pb, acc[6], acc[7]);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -539,12 +545,13 @@ struct DecodeLds {
 // TWO (two-span launches): the span's key geometry and log-prior apply; every
 // split of the launch publishes a partial (an empty one the identity) and
 // takes part in the fused merge, which covers all p.S of them.
-template <int P, int G, bool FUSED, bool TWO>
+template <int P, int D, int G, bool FUSED, bool TWO>
 __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& sp, int s, int s_out,
                                           DecodeLds& lds) {
     constexpr bool FP8 = P == kFp8;
     static_assert(G == 1 || G == 2 || G == 4 || G == 8, "query heads per KV head");
-    static_assert(G == 4 || !FUSED, "the fused merge takes four heads a group");
+    static_assert((G == 4 && D == 128) || !FUSED, "the fused merge takes four heads of 128 dims a group");
+    static_assert(D == 64 || D == 128, "head dim");
     const int g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile rows and bases in scalar registers
@@ -570,17 +577,17 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
     const int n_merge = TWO ? p.S : (L_b + sp.chunk - 1) / sp.chunk;
     if (t_begin >= t_end) {
         // A split past the end of a shorter sequence: the identity partial.
-        for (int i = tid; i < G * 128; i += 256) {
-            const int64_t row = (int64_t)b * p.Hq + g * G + i / 128;
+        for (int i = tid; i < G * D; i += 256) {
+            const int64_t row = (int64_t)b * p.Hq + g * G + i / D;
             if constexpr (FUSED && TWO) {
-                st_agent(p.o_part + (row * p.S + s_out) * 128 + i % 128, 0.f);
-                if (i % 128 == 0) {
+                st_agent(p.o_part + (row * p.S + s_out) * D + i % D, 0.f);
+                if (i % D == 0) {
                     st_agent(p.m_part + row * p.S + s_out, kNegInf);
                     st_agent(p.l_part + row * p.S + s_out, 0.f);
                 }
             } else {
-                p.o_part[(row * p.S + s_out) * 128 + i % 128] = 0.f;
-                if (i % 128 == 0) {
+                p.o_part[(row * p.S + s_out) * D + i % D] = 0.f;
+                if (i % D == 0) {
                     p.m_part[row * p.S + s_out] = kNegInf;
                     p.l_part[row * p.S + s_out] = 0.f;
                 }
@@ -616,7 +623,7 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         static_cast<const __bf16*>(p.q) + b * p.q_sb + (int64_t)(g * G + (lane & (G - 1))) * p.q_sh;
     bf16x8 qop[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < D / 32; ++i) {
         const int dim = FP8 ? 64 * (i >> 1) + 16 * (lane >> 4) + 8 * (i & 1) : 32 * i + 8 * (lane >> 4);
         qop[i] = *reinterpret_cast<const bf16x8*>(qrow + dim);
     }
@@ -643,20 +650,20 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         }
         if (k < ntiles32) {
             const int ik = (int)kss, iv = (int)vss, iks = (int)sc.kss, ivs = (int)sc.vss;
-            const Lanes32 ln = lanes32<P>(ik, iks, iv, ivs, lane);
-            Tile32<P> ta, tb;
-            load_tile32<P>(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * k, t_end - 1);
+            const Lanes32 ln = lanes32<P, D>(ik, iks, iv, ivs, lane);
+            Tile32<P, D> ta, tb;
+            load_tile32<P, D>(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * k, t_end - 1);
             while (true) {
                 const bool more_b = k + kWaves < ntiles32;
                 if (more_b)
-                    load_tile32<P>(tb, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * (k + kWaves), t_end - 1);
-                tile32<P, G>(ta, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
+                    load_tile32<P, D>(tb, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * (k + kWaves), t_end - 1);
+                tile32<P, D, G>(ta, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
                 if (!more_b) break;
                 k += kWaves;
                 const bool more_a = k + kWaves < ntiles32;
                 if (more_a)
-                    load_tile32<P>(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * (k + kWaves), t_end - 1);
-                tile32<P, G>(tb, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
+                    load_tile32<P, D>(ta, kbase, vbase, ik, iv, sc, iks, ivs, ln, t_begin + kTile32 * (k + kWaves), t_end - 1);
+                tile32<P, D, G>(tb, ks, lds.e8m0, qop, scale2, t_begin + kTile32 * k, t_end, lane, m_run, l_run, acc);
                 if (!more_a) break;
                 k += kWaves;
             }
@@ -668,7 +675,7 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         // head.
         float lw = l_run + __shfl_xor(l_run, 16);
         lw += __shfl_xor(lw, 32);
-        if ((lane & 15) < G) {
+        if ((lane & 15) < G && (lane >> 4) < D / 32) {
             float* orow = lds.o[w][lane & (G - 1)] + 32 * (lane >> 4);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
@@ -681,14 +688,15 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
         }
     }
     // Level 1b: merge the four waves in LDS; thread pass q takes head h and
-    // columns c, c + 1 (G * 64 column pairs over 256 threads).
+    // columns c, c + 1 (G * D / 2 column pairs over 256 threads).
     __syncthreads();
+    constexpr int kPairs = D / 2;
 #pragma unroll
-    for (int q0 = 0; q0 < G * 64; q0 += 256) {
+    for (int q0 = 0; q0 < G * kPairs; q0 += 256) {
         const int qi = q0 + tid;
-        if (qi >= G * 64) break;
-        const int h = qi >> 6;
-        const int c = (qi & 63) * 2;
+        if (qi >= G * kPairs) break;
+        const int h = qi / kPairs;
+        const int c = (qi % kPairs) * 2;
         float mw[kWaves], fw[kWaves];
         float Mx = kNegInf;
 #pragma unroll
@@ -716,14 +724,14 @@ __device__ __forceinline__ void decode_wg(const DecodeParams& p, const KvSpan& s
             }
         }
         if constexpr (FUSED) {
-            st_agent2(p.o_part + (row * p.S + s_out) * 128 + c, out);
-            if ((qi & 63) == 0) {
+            st_agent2(p.o_part + (row * p.S + s_out) * D + c, out);
+            if (qi % kPairs == 0) {
                 st_agent(p.m_part + row * p.S + s_out, m_out);
                 st_agent(p.l_part + row * p.S + s_out, L);
             }
         } else {
-            *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s_out) * 128 + c) = out;
-            if ((qi & 63) == 0) {
+            *reinterpret_cast<f32x2*>(p.o_part + (row * p.S + s_out) * D + c) = out;
+            if (qi % kPairs == 0) {
                 p.m_part[row * p.S + s_out] = m_out;
                 p.l_part[row * p.S + s_out] = L;
             }
@@ -737,21 +745,21 @@ __device__ __forceinline__ KvSpan main_span(const DecodeParams& p) {
                   1,         0,      p.L_cap, p.chunk,   kGeomAll, 0, 1, 0};
 }
 
-template <int G, bool FP8, bool FUSED>
-__global__ __launch_bounds__(256, 2) void decode_gqa_d128(DecodeParams p) {
+template <int D, int G, bool FP8, bool FUSED>
+__global__ __launch_bounds__(256, 2) void decode_gqa(DecodeParams p) {
     __shared__ DecodeLds lds;
-    decode_wg<FP8 ? kFp8 : kBf16, G, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
+    decode_wg<FP8 ? kFp8 : kBf16, D, G, FUSED, false>(p, main_span(p), blockIdx.x, blockIdx.x, lds);
 }
 
 // Two spans in one launch (a two-precision cache, or pi-Attention's window
 // and skip keys): splits [0, S0) stream span sp0, the others span sp1; one
 // merge over all splits.
-template <int G, int P0, int P1, bool FUSED>
-__global__ __launch_bounds__(256, 2) void decode_gqa_d128_two(DecodeParams p) {
+template <int D, int G, int P0, int P1, bool FUSED>
+__global__ __launch_bounds__(256, 2) void decode_gqa_two(DecodeParams p) {
     __shared__ DecodeLds lds;  // one copy for both branches
     const int s = blockIdx.x;
-    if (s < p.S0) decode_wg<P0, G, FUSED, true>(p, p.sp0, s, s, lds);
-    else decode_wg<P1, G, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
+    if (s < p.S0) decode_wg<P0, D, G, FUSED, true>(p, p.sp0, s, s, lds);
+    else decode_wg<P1, D, G, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
 }
 
 // Three spans in one launch (a cache kept in bf16, fp8 and MX fp4): splits
@@ -759,12 +767,12 @@ __global__ __launch_bounds__(256, 2) void decode_gqa_d128_two(DecodeParams p) {
 // splits. Each workgroup reads one precision, so no wave branches between
 // formats.
 template <int G, int P0, int P1, int P2, bool FUSED>
-__global__ __launch_bounds__(256, 2) void decode_gqa_d128_three(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_gqa_three(DecodeParams p) {
     __shared__ DecodeLds lds;
     const int s = blockIdx.x;
-    if (s < p.S0) decode_wg<P0, G, FUSED, true>(p, p.sp0, s, s, lds);
-    else if (s < p.S1) decode_wg<P1, G, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
-    else decode_wg<P2, G, FUSED, true>(p, p.sp2, s - p.S1, s, lds);
+    if (s < p.S0) decode_wg<P0, 128, G, FUSED, true>(p, p.sp0, s, s, lds);
+    else if (s < p.S1) decode_wg<P1, 128, G, FUSED, true>(p, p.sp1, s - p.S0, s, lds);
+    else decode_wg<P2, 128, G, FUSED, true>(p, p.sp2, s - p.S1, s, lds);
 }
 
 }  // namespace
@@ -773,59 +781,63 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int kv_dtype, int G, hipStr
     dim3 grid(p.S, p.Hkv, p.B);
     const bool fused = p.counters != nullptr;
     const bool fp8 = kv_dtype == DT_FP8;
-    if (fused && G != 4) return hipErrorInvalidValue;  // the fused merge takes four heads a group
-#define ATTN_ONE(GG, F8)                                                                                 \
-    if (G == GG && fp8 == F8) {                                                                          \
-        if (fused) hipLaunchKernelGGL((decode_gqa_d128<GG, F8, GG == 4>), grid, dim3(256), 0, stream, p); \
-        else hipLaunchKernelGGL((decode_gqa_d128<GG, F8, false>), grid, dim3(256), 0, stream, p);        \
-        return hipGetLastError();                                                                        \
+    const int D = p.d;
+    if (fused && (G != 4 || D != 128)) return hipErrorInvalidValue;  // the fused merge: four heads of 128 dims
+#define ATTN_ONE(DD, GG, F8)                                                                                       \
+    if (D == DD && G == GG && fp8 == F8) {                                                                         \
+        if (fused) hipLaunchKernelGGL((decode_gqa<DD, GG, F8, GG == 4 && DD == 128>), grid, dim3(256), 0, stream, \
+                                      p);                                                                          \
+        else hipLaunchKernelGGL((decode_gqa<DD, GG, F8, false>), grid, dim3(256), 0, stream, p);                   \
+        return hipGetLastError();                                                                                  \
     }
-    ATTN_ONE(4, false)
-    ATTN_ONE(4, true)
-    ATTN_ONE(8, false)
-    ATTN_ONE(8, true)
-    ATTN_ONE(2, false)
-    ATTN_ONE(2, true)
-    ATTN_ONE(1, false)
-    ATTN_ONE(1, true)
+#define ATTN_ONE_G(DD, F8) ATTN_ONE(DD, 4, F8) ATTN_ONE(DD, 8, F8) ATTN_ONE(DD, 2, F8) ATTN_ONE(DD, 1, F8)
+    ATTN_ONE_G(128, false)
+    ATTN_ONE_G(128, true)
+    ATTN_ONE_G(64, false)
+    ATTN_ONE_G(64, true)
+#undef ATTN_ONE_G
 #undef ATTN_ONE
-    return hipErrorInvalidValue;  // no kernel for this head ratio
+    return hipErrorInvalidValue;  // no kernel for this head dim or head ratio
 }
 
 hipError_t launch_decode_mfma_two(const DecodeParams& p, int prec0, int prec1, hipStream_t stream) {
     dim3 grid(p.S, p.Hkv, p.B);
     const bool f = p.counters != nullptr;
     const int G = p.Hkv > 0 ? p.Hq / p.Hkv : 0;
-    if (f && G != 4) return hipErrorInvalidValue;  // the fused merge takes four heads a group
-#define ATTN_TWO(GG, P0, P1)                                                                                    \
-    if (G == GG && prec0 == P0 && prec1 == P1) {                                                                \
-        if (f) hipLaunchKernelGGL((decode_gqa_d128_two<GG, P0, P1, GG == 4>), grid, dim3(256), 0, stream, p);  \
-        else hipLaunchKernelGGL((decode_gqa_d128_two<GG, P0, P1, false>), grid, dim3(256), 0, stream, p);      \
+    const int D = p.d;
+    if (f && (G != 4 || D != 128)) return hipErrorInvalidValue;  // the fused merge: four heads of 128 dims
+#define ATTN_TWO(DD, GG, P0, P1)                                                                                \
+    if (D == DD && G == GG && prec0 == P0 && prec1 == P1) {                                                     \
+        if (f) hipLaunchKernelGGL((decode_gqa_two<DD, GG, P0, P1, GG == 4 && DD == 128>), grid, dim3(256), 0,  \
+                                  stream, p);                                                                   \
+        else hipLaunchKernelGGL((decode_gqa_two<DD, GG, P0, P1, false>), grid, dim3(256), 0, stream, p);        \
         return hipGetLastError();                                                                               \
     }
-#define ATTN_TWO_G(P0, P1) ATTN_TWO(4, P0, P1) ATTN_TWO(8, P0, P1) ATTN_TWO(2, P0, P1) ATTN_TWO(1, P0, P1)
-    ATTN_TWO_G(kBf16, kFp8)
-    ATTN_TWO_G(kBf16, kBf16)
-    ATTN_TWO_G(kFp8, kFp8)
-    ATTN_TWO_G(kBf16, kFp4)
+#define ATTN_TWO_G(DD, P0, P1) ATTN_TWO(DD, 4, P0, P1) ATTN_TWO(DD, 8, P0, P1) ATTN_TWO(DD, 2, P0, P1) ATTN_TWO(DD, 1, P0, P1)
+    ATTN_TWO_G(128, kBf16, kFp8)
+    ATTN_TWO_G(128, kBf16, kBf16)
+    ATTN_TWO_G(128, kFp8, kFp8)
+    ATTN_TWO_G(128, kBf16, kFp4)
+    ATTN_TWO_G(64, kBf16, kFp8)
+    ATTN_TWO_G(64, kBf16, kBf16)
+    ATTN_TWO_G(64, kFp8, kFp8)
 #undef ATTN_TWO_G
 #undef ATTN_TWO
-    return hipErrorInvalidValue;  // no kernel for this pair of precisions or head ratio
+    return hipErrorInvalidValue;  // no kernel for this pair of precisions, head dim or head ratio
 }
 
 hipError_t launch_decode_mfma_three(const DecodeParams& p, int prec0, int prec1, int prec2, hipStream_t stream) {
-    if (prec0 != kBf16 || prec1 != kFp8 || prec2 != kFp4) return hipErrorInvalidValue;
+    if (prec0 != kBf16 || prec1 != kFp8 || prec2 != kFp4 || p.d != 128) return hipErrorInvalidValue;
     dim3 grid(p.S, p.Hkv, p.B);
     const bool f = p.counters != nullptr;
     const int G = p.Hkv > 0 ? p.Hq / p.Hkv : 0;
     if (f && G != 4) return hipErrorInvalidValue;
-#define ATTN_THREE(GG)                                                                                            \
-    if (G == GG) {                                                                                                \
-        if (f) hipLaunchKernelGGL((decode_gqa_d128_three<GG, kBf16, kFp8, kFp4, GG == 4>), grid, dim3(256), 0,   \
-                                  stream, p);                                                                     \
-        else hipLaunchKernelGGL((decode_gqa_d128_three<GG, kBf16, kFp8, kFp4, false>), grid, dim3(256), 0, stream, \
-                                p);                                                                               \
-        return hipGetLastError();                                                                                 \
+#define ATTN_THREE(GG)                                                                                           \
+    if (G == GG) {                                                                                               \
+        if (f) hipLaunchKernelGGL((decode_gqa_three<GG, kBf16, kFp8, kFp4, GG == 4>), grid, dim3(256), 0, stream, \
+                                  p);                                                                            \
+        else hipLaunchKernelGGL((decode_gqa_three<GG, kBf16, kFp8, kFp4, false>), grid, dim3(256), 0, stream, p); \
+        return hipGetLastError();                                                                                \
     }
     ATTN_THREE(4)
     ATTN_THREE(8)

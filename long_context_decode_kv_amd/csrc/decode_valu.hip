@@ -1,5 +1,6 @@
-// Split-KV decode on the vector ALUs: the general path for shapes the MFMA
-// kernel does not cover (fp32 inputs, head dim 64). Same work split and partial format as decode_mfma.hip: workgroup
+// Split-KV decode on the vector ALUs for fp32 inputs (the MFMA kernel takes
+// bf16 queries; the template is written over the element types, and only the
+// fp32 instances are launched). Same work split and partial format as decode_mfma.hip: workgroup
 // (s, g, b) owns one chunk of keys of KV head g and emits one partial
 // (o, m, l) per query head of the group (explainer of "Tree Attention:
 // Topology-aware Decoding for Long-Context Attention on GPU Clusters",
@@ -215,18 +216,15 @@ hipError_t launch_g(const DecodeParams& p, int G, hipStream_t stream) {
 template <int QDT, int KVDT>
 hipError_t launch_d(const DecodeParams& p, int G, hipStream_t stream) {
     if (p.d == 64) return launch_g<QDT, KVDT, 64>(p, G, stream);
-    // bf16 q with d = 128 runs on the MFMA decode (decode_mfma.hip)
-    if constexpr (QDT == DT_F32)
-        if (p.d == 128) return launch_g<QDT, KVDT, 128>(p, G, stream);
+    if (p.d == 128) return launch_g<QDT, KVDT, 128>(p, G, stream);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_decode_valu(const DecodeParams& p, int q_dtype, int kv_dtype, int G, hipStream_t stream) {
+    // bf16 queries run on the MFMA decode (decode_mfma.hip)
     if (q_dtype == DT_F32 && kv_dtype == DT_F32) return launch_d<DT_F32, DT_F32>(p, G, stream);
-    if (q_dtype == DT_BF16 && kv_dtype == DT_BF16) return launch_d<DT_BF16, DT_BF16>(p, G, stream);
-    if (q_dtype == DT_BF16 && kv_dtype == DT_FP8) return launch_d<DT_BF16, DT_FP8>(p, G, stream);
     return hipErrorInvalidValue;
 }
 

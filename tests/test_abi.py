@@ -216,7 +216,7 @@ def test_mixed_decode_argument_errors(so):
     assert mixed(so, khi=T(FP8, 2 * 256 * 128, 256 * 128, 128)) == UNSUPPORTED  # bf16 span holds fp8
     assert mixed(so, klo=T(BF16, 2 * 1024 * 128, 1024 * 128, 128)) == UNSUPPORTED  # fp8 span holds bf16
     assert mixed(so, Hq=6, Hkv=2) == UNSUPPORTED  # 3 query heads per KV head
-    assert mixed(so, d=64) == UNSUPPORTED
+    assert mixed(so, d=96) == UNSUPPORTED
     assert mixed(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
     assert mixed(so, Hq=6, Hkv=4) == INVALID
     assert mixed(so, klo=T(FP8, 2 * 1024 * (1 << 26), 1024 * (1 << 26), 1 << 26)) == INVALID  # 32-row tile offsets
@@ -291,7 +291,7 @@ def test_pi_decode_argument_errors(so):
     assert pi(so, kv=FP8, ks=FAKE, vs=FAKE, period=(1 << 19) - 1, ws=None) == WORKSPACE  # within the limit
     assert pi(so, period=1 << 18) == INVALID  # bf16: 256-byte rows
     assert pi(so, period=(1 << 18) - 1, ws=None) == WORKSPACE
-    assert pi(so, d=64) == UNSUPPORTED
+    assert pi(so, d=96) == UNSUPPORTED
     assert pi(so, Hq=6) == UNSUPPORTED
     assert pi(so, out=T(F32, 1024, 128, 128)) == UNSUPPORTED
     assert pi(so, ws=None) == WORKSPACE

@@ -210,17 +210,32 @@ def test_mfma_head_ratios_ragged_edges(G):
     assert np.all(from_dev(out)[0] == 0.0) and np.all(np.isneginf(lse.cpu().numpy()[0]))
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "e4m3"])
+def test_d64_ragged_edges(fmt):
+    lens = np.array([0, 1, 31, 32, 33, 65, 300, 129], np.int32)
+    inp = make_inputs(3 if fmt == "bf16" else 5, B=8, Hq=8, Hkv=2, d=64, L=300, seed=84)
+    inp["kv_lens"] = lens
+    out, lse = _check(inp, 5, fmt, causal=True, what="d=64 %s ragged" % fmt)
+    assert np.all(from_dev(out)[0] == 0.0) and np.all(np.isneginf(lse.cpu().numpy()[0]))
+
+
+def test_d64_long_cache():
+    inp = make_inputs(2, B=1, Hq=32, Hkv=8, d=64, L=65536, seed=85)
+    _check(inp, 64, "bf16", what="d=64 64K")
+
+
 def test_g8_full_size_128k():
     # 64 query heads over 8 KV heads (eight per group), 128K bf16 keys
     inp = make_inputs(2, Hq=64, Hkv=8, seed=82)
     _check(inp, 64, "bf16", what="G=8 128K")
 
 
-# ------------------------------------------------------------ vector-ALU path
+# ------------------------------------------------------------ head dim 64 (MFMA) and fp32 (vector ALU)
 
 @pytest.mark.parametrize("G,d,fmt", [(1, 64, "bf16"), (2, 64, "bf16"), (8, 64, "bf16"), (4, 64, "bf16"),
-                                     (1, 128, "f32"), (8, 64, "f32"), (2, 64, "e4m3"), (4, 64, "e4m3")])
-def test_valu_paths(G, d, fmt):
+                                     (1, 128, "f32"), (8, 64, "f32"), (2, 64, "e4m3"), (4, 64, "e4m3"),
+                                     (8, 64, "e4m3")])
+def test_d64_and_fp32_paths(G, d, fmt):
     wl = {"bf16": 2, "f32": 1, "e4m3": 5}[fmt]
     inp = make_inputs(wl, B=2, Hq=2 * G, Hkv=2, d=d, L=1111, seed=50 + G + d)
     kind = "f32" if fmt == "f32" else "bf16"

@@ -41,6 +41,12 @@ def test_mixed_other_head_ratios(G):
     _check(inp, 3, 7, what="mixed G=%d" % G)
 
 
+@pytest.mark.parametrize("G", [4, 8])
+def test_mixed_head_dim_64(G):
+    inp = make_mixed_inputs(B=2, Hq=2 * G, Hkv=2, d=64, L=3000, lens=(0.0, 1.0), seed=69 + G)
+    _check(inp, 3, 7, what="mixed d=64 G=%d" % G)
+
+
 def test_mixed_per_head_ragged_lengths_and_empty_spans():
     inp = make_mixed_inputs(B=3, Hq=8, Hkv=2, L=4000, lens=(0.0, 1.0), seed=61)
     inp["hi_lens"][0] = 0  # a head with fp8 keys only

@@ -60,6 +60,12 @@ def test_pi_other_head_ratios(G, kv):
     _check(inp, 256, 16, _alpha(2, 2 * G, 79 + G), what="pi G=%d %s" % (G, kv), kind=kv)
 
 
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+def test_pi_head_dim_64(kv):
+    inp = make_inputs(2 if kv == "bf16" else 5, B=2, Hq=8, Hkv=2, d=64, L=3000, seed=88)
+    _check(inp, 256, 16, _alpha(2, 8, 89), what="pi d=64 %s" % kv, kind=kv)
+
+
 def test_pi_fp8_cache():
     inp = make_inputs(5, B=2, Hq=8, Hkv=2, L=6000, seed=76)
     _check(inp, 1024, 32, _alpha(2, 8, 77), what="pi fp8", kind="e4m3")
