@@ -171,11 +171,11 @@ ATTN_API int attn_decode_plan(int L_cap, int num_splits, int* chunk);
  *
  * q, k and v need 16-byte aligned data and strides that are multiples of 16
  * bytes. Supported: d in {64, 128}; Hq % Hkv == 0 with Hq/Hkv in {1, 2, 4, 8}.
- * bf16 q with bf16 or fp8 KV and d == 128 (every supported Hq/Hkv) runs on
- * MFMA; fp32 and d == 64 run on the vector ALUs. On the MFMA path rows are
+ * bf16 q with bf16 or fp8 KV (d 64 or 128, every supported Hq/Hkv) runs on
+ * MFMA; fp32 runs on the vector ALUs. On the MFMA path rows are
  * read 32 at a time with 32-bit byte offsets, so k/v row strides must be
  * below 2^26 bytes (else ATTN_ERR_INVALID_ARG). The merge is fused into the
- * decode kernel only for Hq/Hkv == 4.
+ * decode kernel only for Hq/Hkv == 4 and d == 128.
  */
 ATTN_API attn_status attn_decode(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
                                  const float* k_scale, const float* v_scale, const int32_t* kv_lens, int B,
@@ -240,7 +240,7 @@ ATTN_API attn_status attn_decode_partials(const attn_tensor* q, const attn_tenso
  * split partials of both spans go through one log-sum-exp merge (Tree
  * Attention explainer, section 3).
  *
- * q        [B, Hq, 1, d] bf16, d = 128, Hq/Hkv in {1, 2, 4, 8}
+ * q        [B, Hq, 1, d] bf16, d in {64, 128}, Hq/Hkv in {1, 2, 4, 8}
  * k_hi, v_hi  [B, Hkv, L_hi_cap, d] bf16: the high-precision span (may be NULL
  *          when L_hi_cap = 0)
  * hi_lens  device int32 [B, Hkv] (index b*Hkv + g): valid keys of the bf16 span
@@ -334,7 +334,7 @@ ATTN_API int attn_decode_mixed_fp4_splits(int B, int Hkv, int L_hi_cap, int L_lo
  *          the workspace is attn_decode_workspace_size(B, Hq, d, S) bytes,
  *          prepared by attn_decode_workspace_init.
  * q, out, lse, softmax_scale, B, Hq, Hkv, d, stream and errors as
- * attn_decode_mixed (bf16 q and out, d = 128, Hq/Hkv in {1, 2, 4, 8}).
+ * attn_decode_mixed (bf16 q and out, Hq/Hkv in {1, 2, 4, 8}), with d = 128.
  */
 ATTN_API attn_status attn_decode_mixed3(const attn_tensor* q, const attn_tensor* k_hi, const attn_tensor* v_hi,
                                         const int32_t* hi_lens, int L_hi_cap, const attn_tensor* k_mid,
@@ -383,8 +383,8 @@ ATTN_API int attn_decode_mixed_splits(int B, int Hkv, int L_hi_cap, int L_lo_cap
  * the union with those priors.
  *
  * q, k, v, k_scale, v_scale, kv_lens ([B] per sequence), softmax_scale, out,
- * lse, workspace: as attn_decode, with bf16 q/out, bf16 or fp8 k/v, d = 128
- * and Hq/Hkv in {1, 2, 4, 8}.
+ * lse, workspace: as attn_decode, with bf16 q/out, bf16 or fp8 k/v, d in
+ * {64, 128} and Hq/Hkv in {1, 2, 4, 8}.
  * window   >= 0 keys before the query (the query's own key is always local)
  * period   >= 1, or 0 for no skip keys; period times the row stride in bytes
  *          must be below 2^26 (the skip keys are read 32 rows at a time with
