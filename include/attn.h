@@ -429,7 +429,7 @@ ATTN_API int attn_decode_pi_splits(int B, int Hkv, int L_cap, int window, int pe
  * causal with Lq > Lkv is rejected (queries with no visible key).
  * bf16 with d == 128 runs on MFMA; fp32 with d == 64 or 128 and bf16 with
  * d == 64 run on a slower vector-ALU kernel (one wave per query row). Other
- * combinations give ATTN_ERR_UNSUPPORTED, as do k and v row strides
+ * combinations give ATTN_ERR_UNSUPPORTED, as do q, k or v row strides
  * (stride_s) of 2^24 elements or more. Hq % Hkv == 0.
  */
 ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B,
@@ -456,7 +456,7 @@ ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, co
  *
  * q, k, v, out, lse, softmax_scale: as attn_prefill (bf16, d = 128), with
  * Lq = Lkv = L.
- * window   >= 0; period >= 1, or 0 for no skip keys. period * k/v row stride
+ * window   >= 0; period >= 1, or 0 for no skip keys. period * q/k/v row stride
  *          must be below 2^24 elements.
  * alpha    device float [B, Hq, L] contiguous (clamped to [0, 1]) or NULL (no
  *          prior).

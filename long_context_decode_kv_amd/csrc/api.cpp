@@ -536,9 +536,9 @@ attn_status check_prefill(const attn_tensor* q, const attn_tensor* k, const attn
                                                        "(q, k, v and out of one dtype; got d = %d)", d);
         return fail(ATTN_ERR_UNSUPPORTED, "this entry point takes bf16 q/k/v/out with d = 128 (got d = %d)", d);
     }
-    // K/V tiles are read through 32-bit buffer offsets covering 64 key rows
-    if (k->stride_s >= (1 << 24) || v->stride_s >= (1 << 24))
-        return fail(ATTN_ERR_UNSUPPORTED, "prefill k/v row stride must be below 2^24 elements");
+    // K/V tiles (64 rows) and Q blocks (32 rows) are read through 32-bit buffer offsets
+    if (q->stride_s >= (1 << 24) || k->stride_s >= (1 << 24) || v->stride_s >= (1 << 24))
+        return fail(ATTN_ERR_UNSUPPORTED, "prefill q/k/v row stride must be below 2^24 elements");
     return ATTN_OK;
 }
 
@@ -1046,8 +1046,9 @@ attn_status attn_prefill_pi(const attn_tensor* q, const attn_tensor* k, const at
     if (window < 0 || period < 0) return fail(ATTN_ERR_INVALID_ARG, "window and period must be >= 0");
     if (window > L) window = L;  // same keys; keeps window arithmetic in range
     if (!causal && 2LL * window > 0x7fffffff) return fail(ATTN_ERR_UNSUPPORTED, "two-sided window too long");
-    if (period > 0 && ((int64_t)period * k->stride_s >= (1 << 24) || (int64_t)period * v->stride_s >= (1 << 24)))
-        return fail(ATTN_ERR_UNSUPPORTED, "period * k/v row stride must be below 2^24 elements");
+    if (period > 0 && ((int64_t)period * q->stride_s >= (1 << 24) || (int64_t)period * k->stride_s >= (1 << 24) ||
+                       (int64_t)period * v->stride_s >= (1 << 24)))
+        return fail(ATTN_ERR_UNSUPPORTED, "period * q/k/v row stride must be below 2^24 elements");
     const size_t need = attn_prefill_pi_workspace_size(B, Hq, L, d);
     if (!workspace) return fail(ATTN_ERR_WORKSPACE, "workspace is null");
     if (!aligned16(workspace)) return fail(ATTN_ERR_WORKSPACE, "workspace must be 16-byte aligned");

@@ -51,6 +51,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -122,7 +123,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // full attention.
 template <bool BAND>
 __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
-    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes];
+    __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes + kWaves * kRows * 4];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,12 +166,26 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     const int kss = (int)(p.k_ss * 2), vss = (int)(p.v_ss * 2);  // row strides in bytes
 
     // Q^T operand: column `row` is query q0 + row; k-slots are dims 16ks + 8hb + e.
+    // The wave's 32 rows come through LDS (8 KB per wave in ring slots 2 and
+    // 3, which the first tiles leave free): buffer loads with an LDS
+    // destination, 16 lanes per 256-byte row, so the global reads are whole
+    // rows; chunk c of row r lands at position c ^ (r & 15), so the operand
+    // reads (chunk 2ks + hb of rows 0..15 per 16 lanes) hit distinct banks.
+    // Rows past the end of the queries arrive as zeros.
     bf16x8 qop[8];
+    const uint32_t qstage = 2 * kSlotBytes + w * (kRows * kRowBytes);
     {
-        const int qr = min(q0 + row, p.Lq - 1);
-        const __bf16* qrow = static_cast<const __bf16*>(p.q) + b * p.q_sb + h * p.q_sh + (int64_t)qr * p.q_ss;
+        const int qrows = max(0, min(kRows, p.Lq - q0));
+        const int qss = (int)(p.q_ss * 2);
+        const char* qbase = static_cast<const char*>(p.q) + (b * p.q_sb + h * p.q_sh + (int64_t)q0 * p.q_ss) * 2;
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<char*>(qbase), 0, qrows > 0 ? (qrows - 1) * qss + kRowBytes : 0, kRsrcWord3);
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) qop[ks] = *reinterpret_cast<const bf16x8*>(qrow + 16 * ks + 8 * hb);
+        for (int i = 0; i < 8; ++i) {
+            const int rr = 4 * i + (lane >> 4), pc = lane & 15;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char*)lds + qstage + 1024 * i, 16,
+                                                     rr * qss + 16 * (pc ^ (rr & 15)), 0, 0, 0);
+        }
     }
     const float c2 = p.scale_log2;
     const int qabs = q0 + row + off;  // absolute position of this lane's query row
@@ -403,8 +418,13 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         constexpr int GG = decltype(gtag)::value;
         if (ntiles > 0) dma(0, gtag);
         if (ntiles > 1) dma(1, gtag);
-        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tiles 0-1 and the Q loads
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tiles 0-1 and this wave's Q rows
         __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            qop[ks] = *reinterpret_cast<const bf16x8*>(lds + qstage + row * kRowBytes +
+                                                       16 * ((2 * ks + hb) ^ (row & 15)));
+        loop_barrier();  // every wave holds its Q before tile 2 is requested into slot 2
         for (int k = 0; k <= ntiles; ++k) {
             if constexpr (GG == 0) {
                 mstep(k - 1, gtag);
@@ -424,70 +444,91 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     else
         run(std::integral_constant<int, 1>{});
 
-    // epilogue: O = acc / l, lse = m ln2 + ln l
+    // epilogue: O = acc / l, lse = m ln2 + ln l. The rows go out through LDS
+    // (the ring is free after the loop's last barrier): each wave stages its
+    // 32 x 128 fp32 tile (16 KB, chunk c of row r at c ^ (r & 15), so the
+    // writes and the row reads both hit distinct banks), then 16 lanes write
+    // each 128-byte half row, so the global stores (and the reads of the part
+    // already in `out` when merging) are whole lines.
     const float l_tot = pair_sum(l_run);
     const int qr = q0 + row;
-    if (qr < p.Lq) {
-        const bool empty = BAND && !(l_tot > 0.f);  // a banded row that saw no key
-        float inv = empty ? 0.f : 1.0f / l_tot;
-        float lse = empty ? kNegInf : m_run * kLn2 + logf(l_tot);
-        const int64_t li = b * p.lse_sb + h * p.lse_sh + (int64_t)qr * p.lse_ss;
-        uint16_t* orow = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh + (int64_t)qr * p.o_ss;
-        float wprev = 0.f;  // weight of the part already in `out` (merge 1 and 3)
-        if constexpr (BAND) {
-            if (p.merge) {
-                // pi-Attention's log-priors: + ln(alpha) on the window part,
-                // + ln(1 - alpha) on the skip part
-                float bw = 0.f, bs = 0.f;
-                if (p.alpha) {
-                    const float a = fminf(fmaxf(p.alpha[li], 0.f), 1.f);
-                    bw = logf(a);
-                    bs = logf(1.f - a);
-                }
-                if (p.merge == 2) {  // the window alone
-                    lse += bw;
-                    if (lse == kNegInf) inv = 0.f;
-                } else {
-                    // this launch's part is skip keys; the part already in
-                    // out / lse_w is the window (merge 1: its prior still to
-                    // add) or the window and the other skip keys (merge 3:
-                    // priors included)
-                    if (p.merge == 3) bw = 0.f;
-                    const float mw = p.lse_w[li] + bw, ms = lse + bs;
-                    const float M = fmaxf(mw, ms);
-                    const float ww = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * kLog2e);
-                    const float ws = (ms == kNegInf) ? 0.f : fast_exp2((ms - M) * kLog2e);
-                    const float z = ww + ws;
-                    const float iz = (M == kNegInf) ? 0.f : 1.f / z;
-                    wprev = ww * iz;
-                    inv *= ws * iz;
-                    lse = (M == kNegInf) ? kNegInf : M + logf(z);
-                }
+    const bool empty = BAND && !(l_tot > 0.f);  // a banded row that saw no key
+    float inv = empty ? 0.f : 1.0f / l_tot;
+    float lse = empty ? kNegInf : m_run * kLn2 + logf(l_tot);
+    float wprev = 0.f;  // weight of the part already in `out` (merge 1 and 3)
+    const int64_t li = b * p.lse_sb + h * p.lse_sh + (int64_t)qr * p.lse_ss;
+    if constexpr (BAND) {
+        if (p.merge && qr < p.Lq) {
+            // pi-Attention's log-priors: + ln(alpha) on the window part,
+            // + ln(1 - alpha) on the skip part
+            float bw = 0.f, bs = 0.f;
+            if (p.alpha) {
+                const float a = fminf(fmaxf(p.alpha[li], 0.f), 1.f);
+                bw = logf(a);
+                bs = logf(1.f - a);
+            }
+            if (p.merge == 2) {  // the window alone
+                lse += bw;
+                if (lse == kNegInf) inv = 0.f;
+            } else {
+                // this launch's part is skip keys; the part already in
+                // out / lse_w is the window (merge 1: its prior still to
+                // add) or the window and the other skip keys (merge 3:
+                // priors included)
+                if (p.merge == 3) bw = 0.f;
+                const float mw = p.lse_w[li] + bw, ms = lse + bs;
+                const float M = fmaxf(mw, ms);
+                const float ww = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * kLog2e);
+                const float ws = (ms == kNegInf) ? 0.f : fast_exp2((ms - M) * kLog2e);
+                const float z = ww + ws;
+                const float iz = (M == kNegInf) ? 0.f : 1.f / z;
+                wprev = ww * iz;
+                inv *= ws * iz;
+                lse = (M == kNegInf) ? kNegInf : M + logf(z);
             }
         }
+    }
+    if (qr < p.Lq && p.lse && hb == 0) p.lse[li] = lse;
+    const uint32_t ostage = w * (kRows * 512);
+    float* wstage = reinterpret_cast<float*>(lds + kLdsBytes) + w * kRows;
 #pragma unroll
-        for (int dblk = 0; dblk < 4; ++dblk)
+    for (int dblk = 0; dblk < 4; ++dblk)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int d0 = 32 * dblk + 8 * jj + 4 * hb;
-                float o[4];
+        for (int jj = 0; jj < 4; ++jj) {
+            // dims 32 dblk + 8 jj + 4 hb .. +3: 16-byte chunk 8 dblk + 2 jj + hb
+            f32x4 o;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) o[e] = oacc[dblk][4 * jj + e] * inv;
-                if (BAND && (p.merge == 1 || p.merge == 3)) {
-                    const u32x2 prev = *reinterpret_cast<const u32x2*>(orow + d0);
+            for (int e = 0; e < 4; ++e) o[e] = oacc[dblk][4 * jj + e] * inv;
+            *reinterpret_cast<f32x4*>(lds + ostage + row * 512 + 16 * ((8 * dblk + 2 * jj + hb) ^ (row & 15))) = o;
+        }
+    if (hb == 0) wstage[row] = wprev;
+    __syncthreads();
+    const bool merge_prev = BAND && (p.merge == 1 || p.merge == 3);
+    uint16_t* obase = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t w2 = prev[e >> 1];
-                        const float x = __builtin_bit_cast(float, (e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
-                        o[e] = fmaf(wprev, x, o[e]);
-                    }
+    for (int i = 0; i < 8; ++i) {
+        const int r = 4 * i + (lane >> 4);
+        if (q0 + r >= p.Lq) continue;
+        uint16_t* orow = obase + (int64_t)(q0 + r) * p.o_ss;
+        const float wp = merge_prev ? wstage[r] : 0.f;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int c = 16 * hh + (lane & 15);  // dims 4c .. 4c + 3
+            f32x4 o = *reinterpret_cast<const f32x4*>(lds + ostage + r * 512 + 16 * (c ^ (r & 15)));
+            if (merge_prev) {
+                const u32x2 prev = *reinterpret_cast<const u32x2*>(orow + 4 * c);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w2 = prev[e >> 1];
+                    const float x = __builtin_bit_cast(float, (e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+                    o[e] = fmaf(wp, x, o[e]);
                 }
-                u32x2 pk;
-                pk[0] = pack_bf16(o[0], o[1]);
-                pk[1] = pack_bf16(o[2], o[3]);
-                *reinterpret_cast<u32x2*>(orow + d0) = pk;
             }
-        if (p.lse && hb == 0) p.lse[li] = lse;
+            u32x2 pk;
+            pk[0] = pack_bf16(o[0], o[1]);
+            pk[1] = pack_bf16(o[2], o[3]);
+            *reinterpret_cast<u32x2*>(orow + 4 * c) = pk;
+        }
     }
 }
 

@@ -173,8 +173,8 @@ def test_error_message_names_the_problem(so):
     assert "workspace" in msg and "need" in msg
 
 
-def prefill(so, dtype=BF16, d=128, Lq=256, Lkv=256, causal=1, Hq=8, Hkv=2):
-    q = T(dtype, Hq * Lq * d, Lq * d, d)
+def prefill(so, dtype=BF16, d=128, Lq=256, Lkv=256, causal=1, Hq=8, Hkv=2, q_ss=None):
+    q = T(dtype, Hq * Lq * d, Lq * d, q_ss or d)
     k = T(dtype, Hkv * Lkv * d, Lkv * d, d)
     o = T(dtype, Hq * Lq * d, Lq * d, d)
     return so.attn_prefill(ctypes.byref(q), ctypes.byref(k), ctypes.byref(k), 1, Hq, Hkv, d, Lq, Lkv, 0.0, causal,
@@ -187,6 +187,7 @@ def test_prefill_argument_errors(so):
     assert prefill(so, d=96) == UNSUPPORTED
     assert prefill(so, Hq=6, Hkv=4) == INVALID
     assert prefill(so, Lq=0) == INVALID
+    assert prefill(so, q_ss=1 << 24) == UNSUPPORTED  # Q rows are read through 32-bit buffer offsets
 
 
 def test_combine_argument_errors(so):
