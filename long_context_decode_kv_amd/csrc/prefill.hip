@@ -189,6 +189,17 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     }
     const float c2 = p.scale_log2;
     const int qabs = q0 + row + off;  // absolute position of this lane's query row
+    // pi-Attention merge inputs of this lane's row, loaded now so the epilogue
+    // does not wait for them: the prior alpha and the lse of the part already
+    // in `out`
+    const int64_t li = b * p.lse_sb + h * p.lse_sh + (int64_t)(q0 + row) * p.lse_ss;
+    float alpha_row = 1.f, lse_prev = kNegInf;
+    if constexpr (BAND) {
+        if (p.merge && q0 + row < p.Lq) {
+            if (p.alpha) alpha_row = p.alpha[li];
+            if (p.merge != 2) lse_prev = p.lse_w[li];
+        }
+    }
 
     f32x16 oacc[4];
 #pragma unroll
@@ -450,20 +461,35 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // writes and the row reads both hit distinct banks), then 16 lanes write
     // each 128-byte half row, so the global stores (and the reads of the part
     // already in `out` when merging) are whole lines.
+    const bool merge_prev = BAND && (p.merge == 1 || p.merge == 3);
+    uint16_t* obase = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh;
+    // the part already in `out` (merging): rows 4i + (lane >> 4), dims 4c .. 4c + 3
+    // with c = 16 hh + (lane & 15), requested before the staging below
+    u32x2 prev[8][2];
+    if (merge_prev) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int r = 4 * i + (lane >> 4), c = 16 * hh + (lane & 15);
+                prev[i][hh] = q0 + r < p.Lq
+                                  ? *reinterpret_cast<const u32x2*>(obase + (int64_t)(q0 + r) * p.o_ss + 4 * c)
+                                  : u32x2{0u, 0u};
+            }
+    }
     const float l_tot = pair_sum(l_run);
     const int qr = q0 + row;
     const bool empty = BAND && !(l_tot > 0.f);  // a banded row that saw no key
     float inv = empty ? 0.f : 1.0f / l_tot;
     float lse = empty ? kNegInf : m_run * kLn2 + logf(l_tot);
     float wprev = 0.f;  // weight of the part already in `out` (merge 1 and 3)
-    const int64_t li = b * p.lse_sb + h * p.lse_sh + (int64_t)qr * p.lse_ss;
     if constexpr (BAND) {
         if (p.merge && qr < p.Lq) {
             // pi-Attention's log-priors: + ln(alpha) on the window part,
             // + ln(1 - alpha) on the skip part
             float bw = 0.f, bs = 0.f;
             if (p.alpha) {
-                const float a = fminf(fmaxf(p.alpha[li], 0.f), 1.f);
+                const float a = fminf(fmaxf(alpha_row, 0.f), 1.f);
                 bw = logf(a);
                 bs = logf(1.f - a);
             }
@@ -476,7 +502,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
                 // add) or the window and the other skip keys (merge 3:
                 // priors included)
                 if (p.merge == 3) bw = 0.f;
-                const float mw = p.lse_w[li] + bw, ms = lse + bs;
+                const float mw = lse_prev + bw, ms = lse + bs;
                 const float M = fmaxf(mw, ms);
                 const float ww = (mw == kNegInf) ? 0.f : fast_exp2((mw - M) * kLog2e);
                 const float ws = (ms == kNegInf) ? 0.f : fast_exp2((ms - M) * kLog2e);
@@ -502,9 +528,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
             *reinterpret_cast<f32x4*>(lds + ostage + row * 512 + 16 * ((8 * dblk + 2 * jj + hb) ^ (row & 15))) = o;
         }
     if (hb == 0) wstage[row] = wprev;
-    __syncthreads();
-    const bool merge_prev = BAND && (p.merge == 1 || p.merge == 3);
-    uint16_t* obase = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh;
+    loop_barrier();  // LDS writes done; the loads of the part in `out` stay in flight
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = 4 * i + (lane >> 4);
@@ -516,10 +540,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
             const int c = 16 * hh + (lane & 15);  // dims 4c .. 4c + 3
             f32x4 o = *reinterpret_cast<const f32x4*>(lds + ostage + r * 512 + 16 * (c ^ (r & 15)));
             if (merge_prev) {
-                const u32x2 prev = *reinterpret_cast<const u32x2*>(orow + 4 * c);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t w2 = prev[e >> 1];
+                    const uint32_t w2 = prev[i][hh][e >> 1];
                     const float x = __builtin_bit_cast(float, (e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
                     o[e] = fmaf(wp, x, o[e]);
                 }
