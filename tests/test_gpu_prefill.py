@@ -34,6 +34,8 @@ def oracle_rows(inp, causal, rows=None, scale=None):
     (1, 4, 2, 64, 1000, False),
     (1, 16, 2, 513, 513, True),
     (1, 4, 4, 1, 77, True),
+    (1, 4, 2, 257, 300, True),
+    (1, 8, 2, 200, 777, False),
 ])
 def test_prefill_small(B, Hq, Hkv, Lq, Lkv, causal):
     inp = make_inputs(4, B=B, Hq=Hq, Hkv=Hkv, L=Lkv, Lq=Lq, seed=80 + Lq + Lkv)
