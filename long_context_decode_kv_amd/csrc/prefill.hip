@@ -137,14 +137,30 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     const int nqb = (p.Lq + span - 1) / span;
     const int hgroups = G / HW;
 
-    // Workgroup -> (position block, batch, KV head, head group), heaviest first.
+    // Workgroup -> (position block, batch, KV head, head group). Plain:
+    // heaviest (latest) position block first. Banded: batch entry first (a
+    // residue class of a skip launch), then its position blocks, KV head
+    // fastest, so the blocks of one class run together on the XCD of their
+    // KV head (round-robin by workgroup index) and share its K/V tiles in L2.
     const int id = blockIdx.x;
-    const int per_qb = p.B * p.Hkv * hgroups;
-    const int qb = nqb - 1 - id / per_qb;
-    const int rem = id % per_qb;
-    const int hgi = rem % hgroups;
-    const int bg = rem / hgroups;
-    const int b = bg / p.Hkv, g = bg % p.Hkv;
+    int qb, hgi, b, g;
+    if constexpr (BAND) {
+        const int inner = nqb * p.Hkv * hgroups;
+        b = id / inner;
+        const int rem = id % inner;
+        g = rem % p.Hkv;
+        const int r2 = rem / p.Hkv;
+        hgi = r2 % hgroups;
+        qb = nqb - 1 - r2 / hgroups;
+    } else {
+        const int per_qb = p.B * p.Hkv * hgroups;
+        qb = nqb - 1 - id / per_qb;
+        const int rem = id % per_qb;
+        hgi = rem % hgroups;
+        const int bg = rem / hgroups;
+        b = bg / p.Hkv;
+        g = bg % p.Hkv;
+    }
     const int h = g * G + hgi * HW + (w % HW);
 
     const int off = BAND ? p.diag : p.Lkv - p.Lq;  // bottom-right alignment unless banded
