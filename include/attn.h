@@ -304,7 +304,7 @@ ATTN_API attn_status attn_decode_mixed_fp4(const attn_tensor* q, const attn_tens
 
 /*
  * Automatic split plan of attn_decode_mixed_fp4: as attn_decode_mixed_splits,
- * with a cost per key of 2 for bf16 and 1.0 for fp4 (measured: an fp4 key
+ * with a cost per key of 2 for bf16 and 1.1 for fp4 (measured: an fp4 key
  * costs about half a bf16 key, its widening making up for most of its fewer
  * bytes). Returns S_hi + S_lo, 0 on a bad argument or a failed device query.
  */
@@ -349,7 +349,7 @@ ATTN_API attn_status attn_decode_mixed3(const attn_tensor* q, const attn_tensor*
 /*
  * Automatic split plan of attn_decode_mixed3: about two workgroups per compute
  * unit in all, shared among the three spans in proportion to keys times the
- * cost per key of the two-precision plans (2 bf16, 0.95 fp8, 1.0 fp4), no
+ * cost per key of the two-precision plans (2 bf16, 0.95 fp8, 1.1 fp4), no
  * split shorter than 256 keys. Stores each span's splits (host pointers, may
  * be NULL) and returns their sum; 0 on a bad argument or a failed device query.
  */

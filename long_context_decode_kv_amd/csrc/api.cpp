@@ -27,12 +27,16 @@ constexpr int kPrecBf16 = 0, kPrecFp8 = 1, kPrecFp4 = 2;  // span precisions of 
 // Split-plan cost per key of an fp8 and of an MX fp4 span, against 2 for
 // bf16 (bytes per element), measured on the two-span decodes at 128K keys,
 // 20 % bf16, 8 KV heads. fp8: 22 + 42 splits 56.1-56.2 us, 20 + 44 56.5-56.8,
-// 18 + 46 58.6-58.7, 16 + 48 61.1-61.5. fp4: 20 + 44 43.5-44.1 us,
-// 21 + 43 44.3-44.6, 22 + 42 44.4-44.5, 24 + 40 45.4-45.5, 18 + 46 49.6-51.9.
+// 18 + 46 58.6-58.7, 16 + 48 61.1-61.5. fp4 (two boxes, the current body):
+// 19 + 45 41.2-41.5 us, 20 + 44 41.6-41.8, 18 + 46 42.6-42.7, 21 + 43
+// 43.0-43.2, 22 + 42 43.8, 24 + 40 45.2. The three-precision decode (20 %
+// bf16, 20 % fp8, 60 % fp4) takes the same weights: 20 + 10 + 34 45.7-45.8 us,
+// 22 + 10 + 32 46.3-46.5, 20 + 9 + 35 48.7; 1.1 plans 20 + 44 and 20 + 10 +
+// 34 (1.15 and up would give the three spans 20 + 9 + 35).
 // Both bodies run scores and P.V on the MFMA; an fp8 key has twice the bytes
 // of an fp4 key, an fp4 key more conversion work per byte.
 constexpr double kFp8Cost = 0.95;
-constexpr double kFp4Cost = 1.0;
+constexpr double kFp4Cost = 1.1;
 constexpr float kLog2e = 1.44269504088896340736f;
 
 int elem_size(int dt) {
