@@ -387,7 +387,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         // banded rows may have seen no key yet (m_run = -inf): their masked
         // scores must give weight 0, not exp2(-inf + inf)
         const float nm = (BAND && m_run == kNegInf) ? 0.f : -m_run;
-        float ls = 0.f;
+        float ls;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -395,11 +395,21 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
                 float pr[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) pr[e] = fast_exp2(fmaf(sacc[kb][8 * half + e], c2, nm));
-                ls += ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+                const float gs = ((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7]));
+                ls = (kb == 0 && half == 0) ? gs : ls + gs;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) pk[kb][half][e] = pack_bf16(pr[2 * e], pr[2 * e + 1]);
             }
         l_run += ls;
+        // Issue order: one exponential (transcendental, mask 0x400), then
+        // three other vector instructions (mask 0x2), instead of runs of four
+        // exponentials: the partner wave issues its MFMAs between them (same
+        // results; 16K prefill about 0.5 % faster).
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x2, 3, 0);
+        }
     };
 
     // M phase of tile j (P.V of j, scores of j+1) for this wave, if any, after
