@@ -146,3 +146,15 @@ def test_pi_prefill_two_sided_16k_sampled_rows():
     per_head = np.unique(np.concatenate([np.arange(64), np.arange(L - 64, L), np.linspace(0, L - 1, 64).astype(int)]))
     rows = np.concatenate([h * L + per_head for h in (0, 5, 17, 31)])
     _check(inp, 512, 64, alpha, "pi prefill two-sided 16K", rows=rows, causal=False)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_pi_prefill_rising_score_ramp(causal):
+    # keys of 64-key tile t scaled by 2^(t // 2): the banded kernel's running
+    # max passes its lazy headroom on tile after tile, in the window launch
+    # and in the strided skip-class launches
+    from test_gpu_prefill import _scale_key_rows
+    inp = make_inputs(4, B=1, Hq=8, Hkv=2, L=700, seed=142)
+    inp["k"] = _scale_key_rows(inp["k"], (np.arange(700) // 64) // 2)
+    alpha = np.random.default_rng(142).uniform(0.0, 1.0, size=(1, 8, 700)).astype(np.float32)
+    _check(inp, 100, 16, alpha, "pi ramp causal %s" % causal, causal=causal)

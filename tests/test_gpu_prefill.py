@@ -132,3 +132,50 @@ def test_prefill_valu_path(wl, B, Hq, Hkv, d, Lq, Lkv, causal, kind):
     assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 1e-5 if kind == "f32" else 2e-3)
     print("prefill valu %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % ((wl, B, Hq, Hkv, d, Lq, Lkv, causal), *res),
           flush=True)
+
+
+def _scale_key_rows(bits, exponents):
+    """bf16 K rows times 2^e per row (exact: only the exponent changes)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * (2.0 ** exponents).astype(np.float32)[None, None, :, None]
+    return (f.view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("direction", ["rising", "falling"])
+def test_prefill_score_ramp(causal, direction):
+    # keys of 64-key tile t scaled by 2^(t // 2) (rising: the scores' scale
+    # grows up to 32x, so the running max passes the lazy headroom on tile
+    # after tile and the accumulators are rescaled each time) or by
+    # 2^-(t // 2) (falling: the first tile holds the max and the later
+    # weights underflow towards zero)
+    inp = make_inputs(4, B=1, Hq=8, Hkv=2, L=700, seed=140)
+    t = np.arange(700) // 64
+    inp["k"] = _scale_key_rows(inp["k"], (t // 2) if direction == "rising" else -(t // 2))
+    out, lse = prefill_on_gpu(inp, causal)
+    ref, ref_lse = oracle_rows(inp, causal)
+    res = assert_close(from_dev(out).reshape(-1, 128), ref, "bf16", what="prefill ramp %s" % direction)
+    assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 2e-3)
+    print("prefill ramp %s causal %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (direction, causal, *res), flush=True)
+
+
+def test_prefill_sharp_softmax_and_needles():
+    # Q scaled x4 (a sharp softmax), and for a few rows of every head a key
+    # planted along the row's query, at or before the row, so that one key
+    # dominates it
+    inp = make_inputs(4, B=1, Hq=8, Hkv=2, L=600, q_mul=4.0, seed=141)
+    q = (inp["q"].astype(np.uint32) << 16).view(np.float32)
+    k = inp["k"].copy()
+    rng = np.random.default_rng(141)
+    import datagen
+    for g in range(2):
+        for i in rng.choice(600, size=4, replace=False):
+            j = int(rng.integers(0, i + 1))
+            qd = q[0, 4 * g, i]
+            k[0, g, j] = datagen.f32_to_bf16_bits((2.0 * qd / np.linalg.norm(qd) * np.sqrt(128)).astype(np.float32))
+    inp["k"] = k
+    for causal in (True, False):
+        out, lse = prefill_on_gpu(inp, causal)
+        ref, ref_lse = oracle_rows(inp, causal)
+        res = assert_close(from_dev(out).reshape(-1, 128), ref, "bf16", what="prefill sharp/needles")
+        assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 2e-3)
+        print("prefill sharp/needles causal %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (causal, *res), flush=True)
