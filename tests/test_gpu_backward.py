@@ -124,3 +124,20 @@ def test_backward_16k_sampled_rows_and_keys():
     print("16k: dk column sums max %.3g, dv sums rel %.3g" % (dk64.abs().max().item(), rel.item()), flush=True)
     assert rel.item() <= 1e-2
     assert torch.isfinite(dq).all()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_backward_rising_score_ramp(causal):
+    # keys of 64-key tile t scaled by 2^(t // 2) (scores up to 32x their usual
+    # size, so each row's softmax is dominated by the latest tiles it sees):
+    # P recomputed from the forward's lse, dz and the three gradients against
+    # the oracle's backward
+    from test_gpu_prefill import _scale_key_rows
+    inp = make_inputs(4, B=1, Hq=8, Hkv=2, L=600, seed=150)
+    inp["k"] = _scale_key_rows(inp["k"], (np.arange(600) // 64) // 2)
+    (dq, dk, dv), dout_bits, _, _ = _run(inp, causal, seed=151)
+    rq, rk, rv = oracle.backward(oracle.Problem(inp["q"], inp["k"], inp["v"], causal=causal), dout_bits)
+    what = "bwd ramp causal %s" % causal
+    _check(dq, rq, what + " dq")
+    _check(dk, rk, what + " dk")
+    _check(dv, rv, what + " dv")

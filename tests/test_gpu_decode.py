@@ -399,3 +399,15 @@ def test_decode_captured_in_a_graph_matches_eager_on_every_replay():
         torch.cuda.synchronize()
         assert torch.equal(o2.view(torch.int16), ref_out.view(torch.int16))
     assert int(ws[:4 << 20].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("S", [1, 5, 0])
+def test_gqa_bf16_rising_score_ramp(S):
+    # keys of 64-key block t scaled by 2^(t // 8) (up to 32x at 3000 keys): the
+    # running max of each wave moves past its lazy headroom again and again,
+    # and the splits' partials differ in scale by orders of magnitude
+    inp = make_inputs(2, B=2, Hq=8, Hkv=2, L=3000, seed=34)
+    t = np.arange(3000) // 64
+    f = (inp["k"].astype(np.uint32) << 16).view(np.float32) * (2.0 ** (t // 8)).astype(np.float32)[None, None, :, None]
+    inp["k"] = (f.view(np.uint32) >> 16).astype(np.uint16)
+    _check(inp, S, "bf16", what="gqa-bf16 ramp S=%d" % S)
