@@ -427,10 +427,10 @@ ATTN_API int attn_decode_pi_splits(int B, int Hkv, int L_cap, int window, int pe
  * 16-byte aligned data and strides.
  * lse: device float [B, Hq, Lq] (contiguous) or NULL.
  * causal with Lq > Lkv is rejected (queries with no visible key).
- * bf16 with d == 128 runs on MFMA; fp32 with d == 64 or 128 and bf16 with
- * d == 64 run on a slower vector-ALU kernel (one wave per query row). Other
- * combinations give ATTN_ERR_UNSUPPORTED, as do q, k or v row strides
- * (stride_s) of 2^24 elements or more. Hq % Hkv == 0.
+ * bf16 with d == 64 or 128 runs on MFMA; fp32 with d == 64 or 128 runs on a
+ * slower vector-ALU kernel (one wave per query row). Other combinations give
+ * ATTN_ERR_UNSUPPORTED, as do q, k or v row strides (stride_s) of 2^24
+ * elements or more. Hq % Hkv == 0.
  */
 ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_tensor* v, int B,
                                   int Hq, int Hkv, int d, int Lq, int Lkv, float softmax_scale, int causal,
@@ -454,7 +454,7 @@ ATTN_API attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, co
  * each launch's epilogue merging its part into the row by log-sum-exp (Tree
  * Attention explainer, section 3).
  *
- * q, k, v, out, lse, softmax_scale: as attn_prefill (bf16, d = 128), with
+ * q, k, v, out, lse, softmax_scale: as attn_prefill (bf16, d = 64 or 128), with
  * Lq = Lkv = L.
  * window   >= 0; period >= 1, or 0 for no skip keys. period * q/k/v row stride
  *          must be below 2^24 elements.

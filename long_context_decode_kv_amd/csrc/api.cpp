@@ -533,12 +533,12 @@ attn_status check_prefill(const attn_tensor* q, const attn_tensor* k, const attn
     if (causal && Lq > Lkv) return fail(ATTN_ERR_INVALID_ARG, "causal with Lq (%d) > Lkv (%d)", Lq, Lkv);
     if (isnan(softmax_scale) || isinf(softmax_scale)) return fail(ATTN_ERR_INVALID_ARG, "softmax_scale not finite");
     const bool same = q->dtype == k->dtype && q->dtype == v->dtype && q->dtype == out->dtype;
-    const bool mfma = same && q->dtype == ATTN_BF16 && d == 128;
-    const bool valu = same && ((q->dtype == ATTN_F32 && (d == 64 || d == 128)) || (q->dtype == ATTN_BF16 && d == 64));
+    const bool mfma = same && q->dtype == ATTN_BF16 && (d == 128 || d == 64);
+    const bool valu = same && q->dtype == ATTN_F32 && (d == 64 || d == 128);
     if (!mfma && !(general && valu)) {
         if (general) return fail(ATTN_ERR_UNSUPPORTED, "prefill takes bf16 with d = 64 or 128, or fp32 with d = 64 or 128 "
                                                        "(q, k, v and out of one dtype; got d = %d)", d);
-        return fail(ATTN_ERR_UNSUPPORTED, "this entry point takes bf16 q/k/v/out with d = 128 (got d = %d)", d);
+        return fail(ATTN_ERR_UNSUPPORTED, "this entry point takes bf16 q/k/v/out with d = 64 or 128 (got d = %d)", d);
     }
     // K/V tiles (64 rows) and Q blocks (32 rows) are read through 32-bit buffer offsets
     if (q->stride_s >= (1 << 24) || k->stride_s >= (1 << 24) || v->stride_s >= (1 << 24))
@@ -1029,9 +1029,8 @@ attn_status attn_prefill(const attn_tensor* q, const attn_tensor* k, const attn_
     if (st != ATTN_OK) return st;
     attn::PrefillParams p = prefill_params(q, k, v, out, lse, B, Hq, Hkv, d, Lq, Lkv, softmax_scale, causal);
     hipError_t e;
-    if (q->dtype == ATTN_BF16 && d == 128) e = attn::launch_prefill(p, static_cast<hipStream_t>(stream));
-    else e = attn::launch_prefill_valu(p, q->dtype == ATTN_F32 ? attn::DT_F32 : attn::DT_BF16,
-                                       static_cast<hipStream_t>(stream));
+    if (q->dtype == ATTN_BF16) e = attn::launch_prefill(p, static_cast<hipStream_t>(stream));
+    else e = attn::launch_prefill_valu(p, attn::DT_F32, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(ATTN_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
     return ATTN_OK;
 }
@@ -1150,6 +1149,7 @@ attn_status attn_prefill_backward(const attn_tensor* q, const attn_tensor* k, co
     g_last_error[0] = 0;
     attn_status st;
     if ((st = check_prefill(q, k, v, out, B, Hq, Hkv, d, Lq, Lkv, softmax_scale, causal))) return st;
+    if (d != 128) return fail(ATTN_ERR_UNSUPPORTED, "the backward takes d = 128 (got d = %d)", d);
     if ((st = check_tensor(dout, "dout", true)) || (st = check_tensor(dq, "dq", false)) ||
         (st = check_tensor(dk, "dk", false)) || (st = check_tensor(dv, "dv", false)))
         return st;

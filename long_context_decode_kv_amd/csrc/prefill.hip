@@ -1,4 +1,4 @@
-// Fused prefill attention for gfx950 (bf16, head dim 128, causal or not).
+// Fused prefill attention for gfx950 (bf16, head dim 128 or 64, causal or not).
 //
 // The score matrix never leaves the chip: per tile of keys, scores, scaling,
 // the max-subtracted softmax and the product with V all happen in registers
@@ -59,12 +59,50 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kRows = 32;        // query rows per wave
 constexpr int kWaves = 8;        // waves per workgroup
 constexpr int kN = 64;           // keys per tile
-constexpr int kD = 128;          // head dim
-constexpr int kRowBytes = kD * 2;            // one K or V row (256 bytes)
-constexpr int kTileBytes = kN * kRowBytes;    // one K or V tile in LDS (16 KB)
-constexpr int kSlots = 4;                     // LDS ring of tiles
-constexpr int kSlotBytes = 2 * kTileBytes;    // K tile, then V tile
-constexpr int kLdsBytes = kSlots * kSlotBytes;
+constexpr int kSlots = 4;  // LDS ring of tiles
+
+// Sizes that follow the head dim D (128 or 64): a K or V row of 2D bytes in
+// 2D / 16 chunks of 16 bytes, a 64-row tile, a ring slot of one K and one V
+// tile, the ring, the 32 x D fp32 output tile a wave stages (4D bytes a row).
+template <int D>
+struct Geom {
+    static_assert(D == 128 || D == 64, "head dim");
+    static constexpr int kRowBytes = D * 2;
+    static constexpr int kChunks = kRowBytes / 16;
+    static constexpr int kTileBytes = kN * kRowBytes;
+    static constexpr int kSlotBytes = 2 * kTileBytes;
+    static constexpr int kLdsBytes = kSlots * kSlotBytes;
+    static constexpr int kKSteps = D / 16;     // k-steps of the scores over d
+    static constexpr int kDimBlocks = D / 32;  // 32-dim output blocks
+    static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one 1 KB LDS-destination load fills
+    static constexpr int kOutRow = 4 * D;                  // bytes of a staged fp32 output row
+};
+
+// LDS position of 16-byte chunk c of a K (or staged Q) row r, chosen so that
+// the 16 rows one operand read touches per 16 lanes (same chunk) hit 16
+// different 16-byte bank groups: with 256-byte rows c ^ (r & 15); with
+// 128-byte rows two rows share a 256-byte bank window, so the rows of each
+// parity take c ^ ((r >> 1) & 7).
+template <int D>
+__device__ __forceinline__ int kchunk(int r, int c) {
+    if constexpr (D == 128) return c ^ (r & 15);
+    else return c ^ ((r >> 1) & 7);
+}
+// Position of the 64-byte segment sg (32 dims) of V row r: the four rows a
+// transposed read touches per 32 lanes must cover all 64 banks once. 256-byte
+// rows: (sg + r) & 3. 128-byte rows (two segments, rows r and r + 1 in
+// different bank halves): (sg + ((r & 3) >> 1)) & 1.
+template <int D>
+__device__ __forceinline__ int vseg(int r, int sg) {
+    if constexpr (D == 128) return (sg + r) & 3;
+    else return (sg + ((r & 3) >> 1)) & 1;
+}
+// The segment of V row r that position ps holds (the inverse of vseg).
+template <int D>
+__device__ __forceinline__ int vseg_at(int r, int ps) {
+    if constexpr (D == 128) return (ps - r) & 3;
+    else return (ps + ((r & 3) >> 1)) & 1;
+}
 constexpr float kHeadroom = 8.0f;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kLog2e = 1.44269504088896340736f;
@@ -121,8 +159,11 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // gets O = 0 and lse = -inf). Used for pi-Attention's window and its strided
 // skip classes; without BAND the kernel is plain causal (diag = Lkv - Lq) or
 // full attention.
-template <bool BAND>
-__global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
+template <bool BAND, int D>
+__global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
+    using Gm = Geom<D>;
+    constexpr int kRowBytes = Gm::kRowBytes, kTileBytes = Gm::kTileBytes, kSlotBytes = Gm::kSlotBytes;
+    constexpr int kLdsBytes = Gm::kLdsBytes, kKSteps = Gm::kKSteps, kDB = Gm::kDimBlocks;
     __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes + kWaves * kRows * 4];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -188,6 +229,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // rows; chunk c of row r lands at position c ^ (r & 15), so the operand
     // reads (chunk 2ks + hb of rows 0..15 per 16 lanes) hit distinct banks.
     // Rows past the end of the queries arrive as zeros.
+    // Register arrays are sized for d = 128 (only the first kKSteps / kDB
+    // entries are used at d = 64): an array whose size depends on D would make
+    // the builtin calls that take its elements type-dependent, and the host
+    // pass would then emit no launch stub for the kernel.
     bf16x8 qop[8];
     const uint32_t qstage = 2 * kSlotBytes + w * (kRows * kRowBytes);
     {
@@ -197,10 +242,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<char*>(qbase), 0, qrows > 0 ? (qrows - 1) * qss + kRowBytes : 0, kRsrcWord3);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int rr = 4 * i + (lane >> 4), pc = lane & 15;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char*)lds + qstage + 1024 * i, 16,
-                                                     rr * qss + 16 * (pc ^ (rr & 15)), 0, 0, 0);
+        for (int i = 0; i < kRows / Gm::kRowsPerLoad; ++i) {
+            const int rr = Gm::kRowsPerLoad * i + lane / Gm::kChunks, pc = lane % Gm::kChunks;
+            const int goff = rr * qss + 16 * kchunk<D>(rr, pc);  // a plain int: see the arrays above
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char*)lds + qstage + 1024 * i, 16, goff, 0, 0, 0);
         }
     }
     const float c2 = p.scale_log2;
@@ -219,7 +264,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
 
     f32x16 oacc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kDB; ++i)
 #pragma unroll
         for (int j = 0; j < 16; ++j) oacc[i][j] = 0.f;
     float m_run = kNegInf, l_run = 0.f;
@@ -238,15 +283,17 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // 1 KB instructions, lane i writing bytes 16i..16i+15 of each; the global
     // address each lane asks for makes the layout above. Group 0 moves V,
     // group 1 moves K. Rows past the end of the sequence arrive as zeros.
+    constexpr int kLoads = 16 / Gm::kRowsPerLoad;  // 1 KB loads a wave issues per K or V tile
     int soff[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wv + 4 * i + (lane >> 4), q = lane & 15;  // LDS row and 16-byte chunk written
+    for (int i = 0; i < kLoads; ++i) {
+        // LDS row and 16-byte chunk position written
+        const int r = 16 * wv + Gm::kRowsPerLoad * i + lane / Gm::kChunks, q = lane % Gm::kChunks;
         if (grp) {
             const int key = (r & ~31) | perm_row(r & 31);
-            soff[i] = key * kss + 16 * (q ^ (r & 15));
+            soff[i] = key * kss + 16 * kchunk<D>(r, q);  // kchunk is its own inverse
         } else {
-            soff[i] = r * vss + 64 * (((q >> 2) - r) & 3) + 16 * (q & 3);
+            soff[i] = r * vss + 64 * vseg_at<D>(r, q >> 2) + 16 * (q & 3);
         }
     }
     // Requests this group's piece of tile t into LDS slot t % kSlots.
@@ -256,9 +303,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         const int rows = min(kN, p.Lkv - key0);
         const __amdgpu_buffer_rsrc_t r = GG ? rows_rsrc(kbase + (int64_t)key0 * kss, rows, kss)
                                             : rows_rsrc(vbase + (int64_t)key0 * vss, rows, vss);
-        lds_char* dst = (lds_char*)lds + (t % kSlots) * kSlotBytes + (GG ? 0 : kTileBytes) + wv * 4096;
+        lds_char* dst = (lds_char*)lds + (t % kSlots) * kSlotBytes + (GG ? 0 : kTileBytes) + wv * (kTileBytes / 4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * i, 16, soff[i], 0, 0, 0);
+        for (int i = 0; i < kLoads; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * i, 16, soff[i], 0, 0, 0);
     };
 
     // Per-lane read offsets within a slot. K operand (key block kb, d-step
@@ -267,12 +314,12 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // the address of keys kk + (i16 >> 2), dims 32dblk + 16g + 4(i16 & 3).
     uint32_t kofs[8], vofs[4];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kofs[ks] = row * kRowBytes + 16 * ((2 * ks + hb) ^ (row & 15));
+    for (int ks = 0; ks < kKSteps; ++ks) kofs[ks] = row * kRowBytes + 16 * kchunk<D>(row, 2 * ks + hb);
     {
         const int i16 = lane & 15, ga = i16 >> 2, gb = i16 & 3, gg = (lane >> 4) & 1;
 #pragma unroll
-        for (int dblk = 0; dblk < 4; ++dblk)
-            vofs[dblk] = kTileBytes + (8 * hb + ga) * kRowBytes + 64 * ((dblk + ga) & 3) + 32 * gg + 8 * gb;
+        for (int dblk = 0; dblk < kDB; ++dblk)
+            vofs[dblk] = kTileBytes + (8 * hb + ga) * kRowBytes + 64 * vseg<D>(ga, dblk) + 32 * gg + 8 * gb;
     }
 
     f32x16 sacc[2];  // scores of the tile whose softmax is next
@@ -285,10 +332,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
     // S); each tile still sums its steps in the same order.
     constexpr int kAhead = 6;
     auto pv_block = [&](uint32_t slot) __attribute__((always_inline)) {
-        // operand i: key block kb = i >> 3, dim block i & 3, half (i >> 2) & 1:
+        // operand i: key block kb = i / (2 kDB), dim block i % kDB, half (i / kDB) & 1:
         // keys 32kb + 16half + 8hb + (0..7), dim 32dblk + (lane & 31)
         auto rd = [&](int i) __attribute__((always_inline)) {
-            const int kb = i >> 3, dblk = i & 3, half = (i >> 2) & 1;
+            const int kb = i / (2 * kDB), dblk = i % kDB, half = (i / kDB) & 1;
             const uint32_t a0 = slot + vofs[dblk] + (32 * kb + 16 * half) * kRowBytes;
             const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)((lds_char*)lds + a0));
             const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -301,10 +348,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         for (int i = 0; i < kA; ++i) opnd[i] = rd(i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 4 * kDB; ++i) {
             const bf16x8 a = opnd[i % kA];
-            if (i + kA < 16) opnd[i % kA] = rd(i + kA);
-            const int kb = i >> 3, dblk = i & 3, half = (i >> 2) & 1;
+            if (i + kA < 4 * kDB) opnd[i % kA] = rd(i + kA);
+            const int kb = i / (2 * kDB), dblk = i % kDB, half = (i / kDB) & 1;
             oacc[dblk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, pk[kb][half]),
                                                                  oacc[dblk], 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -320,9 +367,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         for (int i = 0; i < kAhead; ++i) opnd[i] = rd(i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < 2 * kKSteps; ++i) {
             const bf16x8 a = opnd[i % kAhead];
-            if (i + kAhead < 16) opnd[i % kAhead] = rd(i + kAhead);
+            if (i + kAhead < 2 * kKSteps) opnd[i % kAhead] = rd(i + kAhead);
             const int kb = i & 1, ks = i >> 1;
             sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qop[ks], ks ? sacc[kb] : (f32x16){}, 0, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
@@ -380,7 +427,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < kDB; ++i)
 #pragma unroll
                 for (int jj = 0; jj < 16; ++jj) oacc[i][jj] *= alpha;
         }
@@ -458,9 +505,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tiles 0-1 and this wave's Q rows
         __syncthreads();
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
+        for (int ks = 0; ks < kKSteps; ++ks)
             qop[ks] = *reinterpret_cast<const bf16x8*>(lds + qstage + row * kRowBytes +
-                                                       16 * ((2 * ks + hb) ^ (row & 15)));
+                                                       16 * kchunk<D>(row, 2 * ks + hb));
         loop_barrier();  // every wave holds its Q before tile 2 is requested into slot 2
         for (int k = 0; k <= ntiles; ++k) {
             if constexpr (GG == 0) {
@@ -483,20 +530,21 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
 
     // epilogue: O = acc / l, lse = m ln2 + ln l. The rows go out through LDS
     // (the ring is free after the loop's last barrier): each wave stages its
-    // 32 x 128 fp32 tile (16 KB, chunk c of row r at c ^ (r & 15), so the
-    // writes and the row reads both hit distinct banks), then 16 lanes write
-    // each 128-byte half row, so the global stores (and the reads of the part
-    // already in `out` when merging) are whole lines.
+    // 32 x D fp32 tile (4D bytes a row, chunk c of row r at c ^ (r & 15), so
+    // the writes and the row reads both hit distinct banks), then 16 lanes
+    // write each 128-byte piece of a bf16 row, so the global stores (and the
+    // reads of the part already in `out` when merging) are whole lines.
     const bool merge_prev = BAND && (p.merge == 1 || p.merge == 3);
     uint16_t* obase = static_cast<uint16_t*>(p.out) + b * p.o_sb + h * p.o_sh;
     // the part already in `out` (merging): rows 4i + (lane >> 4), dims 4c .. 4c + 3
     // with c = 16 hh + (lane & 15), requested before the staging below
+    constexpr int kHH = D / 64;  // 128-byte pieces of a bf16 output row
     u32x2 prev[8][2];
     if (merge_prev) {
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int hh = 0; hh < kHH; ++hh) {
                 const int r = 4 * i + (lane >> 4), c = 16 * hh + (lane & 15);
                 prev[i][hh] = q0 + r < p.Lq
                                   ? *reinterpret_cast<const u32x2*>(obase + (int64_t)(q0 + r) * p.o_ss + 4 * c)
@@ -541,17 +589,17 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         }
     }
     if (qr < p.Lq && p.lse && hb == 0) p.lse[li] = lse;
-    const uint32_t ostage = w * (kRows * 512);
+    const uint32_t ostage = w * (kRows * Gm::kOutRow);
     float* wstage = reinterpret_cast<float*>(lds + kLdsBytes) + w * kRows;
 #pragma unroll
-    for (int dblk = 0; dblk < 4; ++dblk)
+    for (int dblk = 0; dblk < kDB; ++dblk)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
             // dims 32 dblk + 8 jj + 4 hb .. +3: 16-byte chunk 8 dblk + 2 jj + hb
             f32x4 o;
 #pragma unroll
             for (int e = 0; e < 4; ++e) o[e] = oacc[dblk][4 * jj + e] * inv;
-            *reinterpret_cast<f32x4*>(lds + ostage + row * 512 + 16 * ((8 * dblk + 2 * jj + hb) ^ (row & 15))) = o;
+            *reinterpret_cast<f32x4*>(lds + ostage + row * Gm::kOutRow + 16 * ((8 * dblk + 2 * jj + hb) ^ (row & 15))) = o;
         }
     if (hb == 0) wstage[row] = wprev;
     loop_barrier();  // LDS writes done; the loads of the part in `out` stay in flight
@@ -562,9 +610,9 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
         uint16_t* orow = obase + (int64_t)(q0 + r) * p.o_ss;
         const float wp = merge_prev ? wstage[r] : 0.f;
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < kHH; ++hh) {
             const int c = 16 * hh + (lane & 15);  // dims 4c .. 4c + 3
-            f32x4 o = *reinterpret_cast<const f32x4*>(lds + ostage + r * 512 + 16 * (c ^ (r & 15)));
+            f32x4 o = *reinterpret_cast<const f32x4*>(lds + ostage + r * Gm::kOutRow + 16 * (c ^ (r & 15)));
             if (merge_prev) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -584,7 +632,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd_d128(PrefillParams p) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-    if (p.d != kD) return hipErrorInvalidValue;
+    if (p.d != 128 && p.d != 64) return hipErrorInvalidValue;
     const int G = p.Hq / p.Hkv;
     const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
     const int span = kRows * (kWaves / HW);
@@ -592,10 +640,14 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     const int64_t wgs = nqb * p.B * p.Hkv * (G / HW);
     if (wgs > 0x7fffffff) return hipErrorInvalidValue;
     if (wgs == 0) return hipSuccess;
-    if (p.band)
-        hipLaunchKernelGGL(prefill_fwd_d128<true>, dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, p);
-    else
-        hipLaunchKernelGGL(prefill_fwd_d128<false>, dim3((unsigned)wgs), dim3(64 * kWaves), 0, stream, p);
+    const dim3 grid((unsigned)wgs), block(64 * kWaves);
+    if (p.d == 128) {
+        if (p.band) hipLaunchKernelGGL((prefill_fwd<true, 128>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_fwd<false, 128>), grid, block, 0, stream, p);
+    } else {
+        if (p.band) hipLaunchKernelGGL((prefill_fwd<true, 64>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_fwd<false, 64>), grid, block, 0, stream, p);
+    }
     return hipGetLastError();
 }
 

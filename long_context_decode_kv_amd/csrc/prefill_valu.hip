@@ -1,6 +1,5 @@
-// Prefill on the vector ALUs: the general (slow) path for shapes the MFMA
-// kernel does not take -- fp32 inputs (head dim 64 or 128) and bf16 with
-// head dim 64. Same operation as prefill.hip (every query dotted with the keys
+// Prefill on the vector ALUs: the general (slow) path for what the MFMA
+// kernel does not take -- fp32 inputs (head dim 64 or 128). Same operation as prefill.hip (every query dotted with the keys
 // it may see, a max-subtracted softmax, the weighted mean of the values:
 // glossary page "Attention", section on Query/Key/Value; the stability step of
 // the "Attention in SRAM on Tenstorrent Grayskull" explainer, section 3), the
@@ -76,8 +75,6 @@ hipError_t launch_prefill_valu(const PrefillParams& p, int dtype, hipStream_t st
         hipLaunchKernelGGL((prefill_valu_kernel<float, 128>), grid, dim3(256), 0, stream, p);
     else if (dtype == DT_F32 && p.d == 64)
         hipLaunchKernelGGL((prefill_valu_kernel<float, 64>), grid, dim3(256), 0, stream, p);
-    else if (dtype == DT_BF16 && p.d == 64)
-        hipLaunchKernelGGL((prefill_valu_kernel<__bf16, 64>), grid, dim3(256), 0, stream, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

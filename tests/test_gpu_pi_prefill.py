@@ -33,7 +33,7 @@ def oracle_pi_rows(inp, window, period, alpha=None, rows=None, causal=True):
 def _check(inp, window, period, alpha, what, dev=None, rows=None, causal=True):
     out, lse = pi_prefill_on_gpu(inp, window, period, alpha, dev=dev, causal=causal)
     ref, ref_lse = oracle_pi_rows(inp, window, period, alpha, rows=rows, causal=causal)
-    got = from_dev(out).reshape(-1, 128)
+    got = from_dev(out).reshape(-1, inp["q"].shape[-1])
     gl = lse.cpu().numpy().astype(np.float64).ravel()
     if rows is not None:
         got, gl = got[rows], gl[rows]
@@ -158,3 +158,12 @@ def test_pi_prefill_rising_score_ramp(causal):
     inp["k"] = _scale_key_rows(inp["k"], (np.arange(700) // 64) // 2)
     alpha = np.random.default_rng(142).uniform(0.0, 1.0, size=(1, 8, 700)).astype(np.float32)
     _check(inp, 100, 16, alpha, "pi ramp causal %s" % causal, causal=causal)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("window,period", [(128, 16), (37, 5), (0, 1)])
+def test_pi_prefill_d64(window, period, causal):
+    # head dim 64 through the same window and skip-class launches
+    inp = make_inputs(4, B=1, Hq=8, Hkv=2, d=64, L=700, seed=180 + window + period)
+    alpha = np.random.default_rng(180).uniform(0.0, 1.0, size=(1, 8, 700)).astype(np.float32)
+    _check(inp, window, period, alpha, "pi d64 causal %s" % causal, causal=causal)

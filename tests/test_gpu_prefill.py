@@ -114,14 +114,12 @@ def test_prefill_repeats_are_bit_identical():
     assert_lse_close(first_lse.cpu().numpy().astype(np.float64).ravel()[rows], ref_lse, 2e-3)
 
 
-# ------------------------------------------------------------ vector-ALU prefill (fp32, head dim 64)
+# ------------------------------------------------------------ vector-ALU prefill (fp32, head dim 64 or 128)
 
 @pytest.mark.parametrize("wl,B,Hq,Hkv,d,Lq,Lkv,causal,kind", [
     (1, 1, 4, 2, 128, 150, 150, True, "f32"),
     (1, 2, 2, 2, 64, 100, 230, True, "f32"),
     (1, 1, 8, 1, 64, 77, 77, False, "f32"),
-    (4, 1, 8, 2, 64, 300, 300, True, "bf16"),
-    (4, 1, 4, 4, 64, 1, 90, True, "bf16"),
 ])
 def test_prefill_valu_path(wl, B, Hq, Hkv, d, Lq, Lkv, causal, kind):
     inp = make_inputs(wl, B=B, Hq=Hq, Hkv=Hkv, d=d, L=Lkv, Lq=Lq, seed=140 + Lq + d)
@@ -179,3 +177,41 @@ def test_prefill_sharp_softmax_and_needles():
         res = assert_close(from_dev(out).reshape(-1, 128), ref, "bf16", what="prefill sharp/needles")
         assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 2e-3)
         print("prefill sharp/needles causal %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (causal, *res), flush=True)
+
+
+# ------------------------------------------------------------ MFMA prefill at head dim 64
+
+@pytest.mark.parametrize("B,Hq,Hkv,Lq,Lkv,causal", [
+    (1, 8, 2, 300, 300, True),
+    (2, 4, 4, 129, 129, True),
+    (1, 8, 1, 200, 200, False),
+    (1, 8, 2, 130, 400, True),
+    (1, 4, 2, 64, 1000, False),
+    (1, 16, 2, 513, 513, True),
+    (1, 4, 4, 1, 90, True),
+    (1, 6, 3, 257, 300, True),
+])
+def test_prefill_d64(B, Hq, Hkv, Lq, Lkv, causal):
+    # the same kernel with 128-byte K/V rows: its own LDS swizzles, half the
+    # score steps and output blocks, and the 8 KB output staging per wave
+    inp = make_inputs(4, B=B, Hq=Hq, Hkv=Hkv, d=64, L=Lkv, Lq=Lq, seed=160 + Lq + Lkv)
+    out, lse = prefill_on_gpu(inp, causal)
+    ref, ref_lse = oracle_rows(inp, causal)
+    res = assert_close(from_dev(out).reshape(-1, 64), ref, "bf16", what="prefill d64")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 2e-3)
+    print("prefill d64 %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % ((B, Hq, Hkv, Lq, Lkv, causal), *res), flush=True)
+
+
+def test_prefill_d64_4k_sampled_rows_and_repeats():
+    # 4096 tokens, 32 query / 8 KV heads, causal: sampled rows of every head
+    # against the oracle, and a second call bit-identical to the first
+    inp = make_inputs(4, L=4096, d=64, seed=170)
+    dev = {k: to_dev(inp[k]) for k in ("q", "k", "v")}
+    o1, l1 = prefill_on_gpu(inp, True, dev=dev)
+    o2, l2 = prefill_on_gpu(inp, True, dev=dev)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    rows, _ = _sample_rows(32, 4096)
+    ref, ref_lse = oracle_rows(inp, True, rows=rows)
+    res = assert_close(from_dev(o1).reshape(-1, 64)[rows], ref, "bf16", what="prefill d64 4K")
+    assert_lse_close(l1.cpu().numpy().astype(np.float64).ravel()[rows], ref_lse, 2e-3)
+    print("prefill d64 4K max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % res, flush=True)

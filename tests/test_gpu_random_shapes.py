@@ -245,3 +245,27 @@ def test_random_backward(G, Hkv, B, Lq, Lkv, causal, seed):
     check_grad(dq, rq, what + " dq")
     check_grad(dk, rk, what + " dk")
     check_grad(dv, rv, what + " dv")
+
+
+def _prefill_d64_cases(n=12):
+    r = np.random.default_rng(2032)
+    out = []
+    for _ in range(n):
+        G = int(r.choice([1, 2, 4, 8]))
+        Hkv = int(r.integers(1, 3))
+        B = int(r.integers(1, 3))
+        Lkv = int(r.integers(1, 700))
+        causal = bool(r.integers(2))
+        Lq = int(r.integers(1, Lkv + 1)) if causal else int(r.integers(1, 700))
+        out.append((G, Hkv, B, Lq, Lkv, causal, int(r.integers(1 << 30))))
+    return out
+
+
+@pytest.mark.parametrize("G,Hkv,B,Lq,Lkv,causal,seed", _prefill_d64_cases())
+def test_random_prefill_d64(G, Hkv, B, Lq, Lkv, causal, seed):
+    print("prefill d64 G", G, "Hkv", Hkv, "B", B, "Lq", Lq, "Lkv", Lkv, "causal", causal, flush=True)
+    inp = make_inputs(4, B=B, Hq=G * Hkv, Hkv=Hkv, d=64, L=Lkv, Lq=Lq, seed=seed % 100000)
+    out, lse = prefill_on_gpu(inp, causal)
+    ref, ref_lse = oracle_rows(inp, causal)
+    assert_close(from_dev(out).reshape(-1, 64), ref, "bf16", what="random prefill d64")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 2e-3)
