@@ -43,6 +43,7 @@
 // Workgroups are issued heaviest (latest) query block first.
 #include "internal.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace attn {
@@ -57,21 +58,24 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRows = 32;        // query rows per wave
-constexpr int kWaves = 8;        // waves per workgroup
 constexpr int kN = 64;           // keys per tile
-constexpr int kSlots = 4;  // LDS ring of tiles
 
-// Sizes that follow the head dim D (128 or 64): a K or V row of 2D bytes in
-// 2D / 16 chunks of 16 bytes, a 64-row tile, a ring slot of one K and one V
-// tile, the ring, the 32 x D fp32 output tile a wave stages (4D bytes a row).
-template <int D>
+// Sizes that follow the head dim D (128 or 64) and the number of wave groups
+// NG (2: eight waves, a four-tile ring; 1: four waves, a two-tile ring): a K
+// or V row of 2D bytes in 2D / 16 chunks of 16 bytes, a 64-row tile, a ring
+// slot of one K and one V tile, the ring, the 32 x D fp32 output tile a wave
+// stages (4D bytes a row).
+template <int D, int NG>
 struct Geom {
     static_assert(D == 128 || D == 64, "head dim");
+    static_assert(NG == 1 || NG == 2, "wave groups");
+    static constexpr int kWaves = 4 * NG;
+    static constexpr int kSlots = NG == 2 ? 4 : 2;
     static constexpr int kRowBytes = D * 2;
     static constexpr int kChunks = kRowBytes / 16;
     static constexpr int kTileBytes = kN * kRowBytes;
     static constexpr int kSlotBytes = 2 * kTileBytes;
-    static constexpr int kLdsBytes = kSlots * kSlotBytes;
+    static constexpr int kLdsBytes = kSlots * kSlotBytes;  // also holds the Q rows and the output tiles
     static constexpr int kKSteps = D / 16;     // k-steps of the scores over d
     static constexpr int kDimBlocks = D / 32;  // 32-dim output blocks
     static constexpr int kRowsPerLoad = 1024 / kRowBytes;  // rows one 1 KB LDS-destination load fills
@@ -159,11 +163,21 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 // gets O = 0 and lse = -inf). Used for pi-Attention's window and its strided
 // skip classes; without BAND the kernel is plain causal (diag = Lkv - Lq) or
 // full attention.
-template <bool BAND, int D>
-__global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
-    using Gm = Geom<D>;
+//
+// NG = 2 is the two-group workgroup described at the top of the file. NG = 1
+// is a four-wave workgroup (one wave per SIMD) with a two-tile ring, of which
+// two fit on a compute unit, so that one workgroup's loads, barrier waits and
+// stores overlap the other's products (launches whose workgroups walk only a
+// few tiles); each wave runs scores, softmax and P.V of a tile in turn, with
+// one barrier per tile (at the loop). Both compute every row the same way:
+// the same tiles, the same products in the same order, so the outputs are
+// bit-identical.
+template <bool BAND, int D, int NG>
+__global__ __launch_bounds__(256 * NG, 3 - NG) void prefill_fwd(PrefillParams p) {
+    using Gm = Geom<D, NG>;
     constexpr int kRowBytes = Gm::kRowBytes, kTileBytes = Gm::kTileBytes, kSlotBytes = Gm::kSlotBytes;
     constexpr int kLdsBytes = Gm::kLdsBytes, kKSteps = Gm::kKSteps, kDB = Gm::kDimBlocks;
+    constexpr int kWaves = Gm::kWaves, kSlots = Gm::kSlots;
     __shared__ __attribute__((aligned(1024))) char lds[kLdsBytes + kWaves * kRows * 4];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -223,8 +237,8 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
     const int kss = (int)(p.k_ss * 2), vss = (int)(p.v_ss * 2);  // row strides in bytes
 
     // Q^T operand: column `row` is query q0 + row; k-slots are dims 16ks + 8hb + e.
-    // The wave's 32 rows come through LDS (8 KB per wave in ring slots 2 and
-    // 3, which the first tiles leave free): buffer loads with an LDS
+    // The wave's 32 rows come through LDS (8 KB per wave in the last NG ring
+    // slots, which the first tiles leave free): buffer loads with an LDS
     // destination, 16 lanes per 256-byte row, so the global reads are whole
     // rows; chunk c of row r lands at position c ^ (r & 15), so the operand
     // reads (chunk 2ks + hb of rows 0..15 per 16 lanes) hit distinct banks.
@@ -234,7 +248,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
     // the builtin calls that take its elements type-dependent, and the host
     // pass would then emit no launch stub for the kernel.
     bf16x8 qop[8];
-    const uint32_t qstage = 2 * kSlotBytes + w * (kRows * kRowBytes);
+    const uint32_t qstage = (kSlots - NG) * kSlotBytes + w * (kRows * kRowBytes);
     {
         const int qrows = max(0, min(kRows, p.Lq - q0));
         const int qss = (int)(p.q_ss * 2);
@@ -281,22 +295,29 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
     // Tiles go from global memory straight into LDS (buffer loads with an LDS
     // destination, no registers): each wave moves 4 KB per tile with four
     // 1 KB instructions, lane i writing bytes 16i..16i+15 of each; the global
-    // address each lane asks for makes the layout above. Group 0 moves V,
-    // group 1 moves K. Rows past the end of the sequence arrive as zeros.
+    // address each lane asks for makes the layout above. With two groups,
+    // group 0 moves V and group 1 moves K; with one, every wave moves its
+    // rows of both. Rows past the end of the sequence arrive as zeros.
     constexpr int kLoads = 16 / Gm::kRowsPerLoad;  // 1 KB loads a wave issues per K or V tile
+    // NG = 1: soff holds the K offsets; the V rows of load i are those of
+    // load 0 plus kRowsPerLoad * i, in the same segment order (which follows
+    // the row mod 4), so their offset is vsoff0 plus a multiple of the stride.
     int soff[4];
+    int vsoff0 = 0;
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
         // LDS row and 16-byte chunk position written
         const int r = 16 * wv + Gm::kRowsPerLoad * i + lane / Gm::kChunks, q = lane % Gm::kChunks;
-        if (grp) {
+        if (NG == 1 || grp) {
             const int key = (r & ~31) | perm_row(r & 31);
             soff[i] = key * kss + 16 * kchunk<D>(r, q);  // kchunk is its own inverse
         } else {
             soff[i] = r * vss + 64 * vseg_at<D>(r, q >> 2) + 16 * (q & 3);
         }
+        if (NG == 1 && i == 0) vsoff0 = r * vss + 64 * vseg_at<D>(r, q >> 2) + 16 * (q & 3);
     }
-    // Requests this group's piece of tile t into LDS slot t % kSlots.
+    // Requests this wave's piece of K (GG = 1) or V (GG = 0) of tile t into
+    // LDS slot t % kSlots.
     auto dma = [&](int t, auto gtag) __attribute__((always_inline)) {
         constexpr int GG = decltype(gtag)::value;
         const int key0 = (t0 + t) * kN;
@@ -305,7 +326,14 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
                                             : rows_rsrc(vbase + (int64_t)key0 * vss, rows, vss);
         lds_char* dst = (lds_char*)lds + (t % kSlots) * kSlotBytes + (GG ? 0 : kTileBytes) + wv * (kTileBytes / 4);
 #pragma unroll
-        for (int i = 0; i < kLoads; ++i) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * i, 16, soff[i], 0, 0, 0);
+        for (int i = 0; i < kLoads; ++i) {
+            // the whole offset in the vector operand (the bounds check that
+            // zero-fills rows past the end covers only that one), as a plain
+            // int: see the arrays above
+            int off = soff[i];
+            if constexpr (NG == 1 && GG == 0) off = vsoff0 + Gm::kRowsPerLoad * i * vss;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst + 1024 * i, 16, off, 0, 0, 0);
+        }
     };
 
     // Per-lane read offsets within a slot. K operand (key block kb, d-step
@@ -330,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
     // two per operand) or six (K) MFMAs ahead. Consecutive MFMAs accumulate
     // into different tiles (the four dim blocks of O, the two key blocks of
     // S); each tile still sums its steps in the same order.
-    constexpr int kAhead = 6;
+    constexpr int kAhead = NG == 2 ? 6 : 4;
     auto pv_block = [&](uint32_t slot) __attribute__((always_inline)) {
         // operand i: key block kb = i / (2 kDB), dim block i % kDB, half (i / kDB) & 1:
         // keys 32kb + 16half + 8hb + (0..7), dim 32dblk + (lane & 31)
@@ -523,10 +551,47 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
             }
         }
     };
-    if (grp == 0)
-        run(std::integral_constant<int, 0>{});
-    else
-        run(std::integral_constant<int, 1>{});
+    // One group: tile t in slot t % 2. Iteration k: P.V of tile k-1; wait for
+    // this wave's piece of tile k (requested in iteration k-1); barrier (every
+    // piece of tile k is in, every wave is done with slot (k-1) % 2); request
+    // tile k+1 into that slot; scores and softmax of tile k. The request has
+    // the scores and the softmax to land before the P.V reads it. Every wave
+    // passes the same ntiles + 1 barriers.
+    auto run1 = [&]() __attribute__((always_inline)) {
+        const std::integral_constant<int, 1> kt{};
+        const std::integral_constant<int, 0> vt{};
+        if (ntiles > 0) {
+            dma(0, kt);
+            dma(0, vt);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): tile 0 and this wave's Q rows
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < kKSteps; ++ks)
+            qop[ks] = *reinterpret_cast<const bf16x8*>(lds + qstage + row * kRowBytes +
+                                                       16 * kchunk<D>(row, 2 * ks + hb));
+        for (int k = 0; k <= ntiles; ++k) {
+            if (k >= 1 && k - 1 >= jw_lo && k - 1 <= jw_hi) pv_block((uint32_t)(((k - 1) % kSlots) * kSlotBytes));
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's piece of tile k
+            loop_barrier();  // also: every wave holds its Q before tile 1 goes into the Q rows' slot
+            if (k + 1 < ntiles) {
+                dma(k + 1, kt);
+                dma(k + 1, vt);
+            }
+            if (k < ntiles && k >= jw_lo && k <= jw_hi) {
+                qk_block((uint32_t)((k % kSlots) * kSlotBytes));
+                vphase(k);
+            }
+        }
+    };
+    if constexpr (NG == 1) {
+        run1();
+    } else {
+        if (grp == 0)
+            run(std::integral_constant<int, 0>{});
+        else
+            run(std::integral_constant<int, 1>{});
+    }
 
     // epilogue: O = acc / l, lse = m ln2 + ln l. The rows go out through LDS
     // (the ring is free after the loop's last barrier): each wave stages its
@@ -555,7 +620,7 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
     const int qr = q0 + row;
     const bool empty = BAND && !(l_tot > 0.f);  // a banded row that saw no key
     float inv = empty ? 0.f : 1.0f / l_tot;
-    float lse = empty ? kNegInf : m_run * kLn2 + logf(l_tot);
+    float lse = empty ? kNegInf : fmaf(m_run, kLn2, logf(l_tot));  // one rounding in every instantiation
     float wprev = 0.f;  // weight of the part already in `out` (merge 1 and 3)
     if constexpr (BAND) {
         if (p.merge && qr < p.Lq) {
@@ -631,8 +696,10 @@ __global__ __launch_bounds__(512, 1) void prefill_fwd(PrefillParams p) {
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
-    if (p.d != 128 && p.d != 64) return hipErrorInvalidValue;
+namespace {
+template <int NG>
+hipError_t launch_prefill_ng(const PrefillParams& p, hipStream_t stream) {
+    constexpr int kWaves = 4 * NG;
     const int G = p.Hq / p.Hkv;
     const int HW = (G % 4 == 0) ? 4 : (G % 2 == 0 ? 2 : 1);
     const int span = kRows * (kWaves / HW);
@@ -642,13 +709,34 @@ hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
     if (wgs == 0) return hipSuccess;
     const dim3 grid((unsigned)wgs), block(64 * kWaves);
     if (p.d == 128) {
-        if (p.band) hipLaunchKernelGGL((prefill_fwd<true, 128>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((prefill_fwd<false, 128>), grid, block, 0, stream, p);
+        if (p.band) hipLaunchKernelGGL((prefill_fwd<true, 128, NG>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_fwd<false, 128, NG>), grid, block, 0, stream, p);
     } else {
-        if (p.band) hipLaunchKernelGGL((prefill_fwd<true, 64>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((prefill_fwd<false, 64>), grid, block, 0, stream, p);
+        if (p.band) hipLaunchKernelGGL((prefill_fwd<true, 64, NG>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_fwd<false, 64, NG>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
+}
+}  // namespace
+
+// Four-wave workgroups (two per compute unit) when no workgroup walks more
+// than sixteen 64-key tiles: then a workgroup's start, barrier waits and
+// stores weigh about as much as its products, and the second workgroup on the
+// compute unit hides them. Longer walks keep the eight-wave workgroup, whose
+// K/V tiles serve twice the rows. Causal prefills, 32q/8kv, d = 128, eight
+// and four waves: 64 x 256 tokens 0.116 / 0.096 ms, 32 x 512 0.149 / 0.134 ms,
+// 16 x 1024 0.188 / 0.185 ms, 4 x 4096 0.493 / 0.528 ms, 16K 1.81 / 1.98 ms;
+// the 16K pi-Attention prefill (window 512, period 64: a window launch of
+// 576-key walks and skip-class launches of 256 keys) 0.350 / 0.327 ms.
+static bool narrow_prefill(const PrefillParams& p) {
+    int64_t keys = p.Lkv;  // keys one workgroup may walk
+    if (p.band && p.window >= 0) keys = std::min<int64_t>(keys, (int64_t)p.window + 2 * kRows);
+    return keys <= 16 * kN;
+}
+
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+    if (p.d != 128 && p.d != 64) return hipErrorInvalidValue;
+    return narrow_prefill(p) ? launch_prefill_ng<1>(p, stream) : launch_prefill_ng<2>(p, stream);
 }
 
 }  // namespace attn

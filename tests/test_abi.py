@@ -48,6 +48,15 @@ def test_every_declared_symbol_is_exported(so):
     assert {e for e in exported if e.startswith("attn_")} == set(names)
 
 
+def test_no_undefined_library_symbols(so):
+    # Every symbol of the library's own namespace is defined in it: a kernel
+    # template whose host-side launch stub was not emitted would otherwise
+    # link and only fail when the library is loaded (with RTLD_NOW) or launched.
+    nm = subprocess.run(["nm", "-D", "--undefined-only", lib.library_path], capture_output=True, text=True).stdout
+    undefined = [line.split()[-1] for line in nm.splitlines() if line.strip()]
+    assert not [u for u in undefined if "4attn" in u or u.startswith("attn_")], undefined
+
+
 def test_status_strings(so):
     assert [lib.attn_status_string(s) for s in range(5)] == [
         "ATTN_OK", "ATTN_ERR_INVALID_ARG", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_WORKSPACE", "ATTN_ERR_HIP"]

@@ -167,3 +167,15 @@ def test_pi_prefill_d64(window, period, causal):
     inp = make_inputs(4, B=1, Hq=8, Hkv=2, d=64, L=700, seed=180 + window + period)
     alpha = np.random.default_rng(180).uniform(0.0, 1.0, size=(1, 8, 700)).astype(np.float32)
     _check(inp, window, period, alpha, "pi d64 causal %s" % causal, causal=causal)
+
+
+@pytest.mark.parametrize("window,causal", [(960, True), (961, True), (470, False), (500, False)])
+def test_pi_prefill_window_launch_both_workgroup_shapes(window, causal):
+    # The window launch takes four-wave workgroups while a workgroup walks at
+    # most 1024 keys (window + 64 <= 1024 causal; two-sided the band is
+    # 2 window + 1 keys) and eight-wave workgroups past that; the skip-class
+    # launches (94 rows a class here) take four-wave workgroups. Every row.
+    inp = make_inputs(4, B=1, Hq=4, Hkv=2, L=1500, seed=7100 + window)
+    alpha = np.random.default_rng(window).uniform(0.0, 1.0, size=(1, 4, 1500))
+    _check(inp, window, 16, alpha, "pi prefill boundary", causal=causal)
+

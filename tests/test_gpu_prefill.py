@@ -47,6 +47,26 @@ def test_prefill_small(B, Hq, Hkv, Lq, Lkv, causal):
     print("prefill %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % ((B, Hq, Hkv, Lq, Lkv, causal), *res), flush=True)
 
 
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("Lq,Lkv,causal", [
+    (1024, 1024, True),   # every workgroup walks at most 1024 keys: four-wave workgroups
+    (1025, 1025, True),   # one key more: eight-wave workgroups
+    (1000, 1089, True),
+    (300, 1024, False),
+    (300, 1025, False),
+])
+def test_prefill_both_workgroup_shapes(Lq, Lkv, causal, d):
+    # Launches whose workgroups walk at most 1024 keys take four-wave
+    # workgroups (two per compute unit), longer ones eight-wave workgroups:
+    # every row on both sides of the boundary against the oracle.
+    inp = make_inputs(4, B=1, Hq=4, Hkv=2, d=d, L=Lkv, Lq=Lq, seed=7000 + Lq + Lkv + d)
+    out, lse = prefill_on_gpu(inp, causal)
+    ref, ref_lse = oracle_rows(inp, causal)
+    res = assert_close(from_dev(out).reshape(-1, d), ref, "bf16", what="prefill")
+    assert_lse_close(lse.cpu().numpy().astype(np.float64).ravel(), ref_lse, 2e-3)
+    print("prefill d=%d %s max_abs=%.3g mean_abs=%.3g rel_l2=%.3g" % (d, (Lq, Lkv, causal), *res), flush=True)
+
+
 def test_prefill_scale_override_and_determinism():
     inp = make_inputs(4, B=1, Hq=4, Hkv=2, L=700, seed=90)
     dev = {k: to_dev(inp[k]) for k in ("q", "k", "v")}
