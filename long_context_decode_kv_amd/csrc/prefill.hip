@@ -711,9 +711,11 @@ hipError_t launch_prefill_ng(const PrefillParams& p, hipStream_t stream) {
     if (p.d == 128) {
         if (p.band) hipLaunchKernelGGL((prefill_fwd<true, 128, NG>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((prefill_fwd<false, 128, NG>), grid, block, 0, stream, p);
-    } else {
+    } else if constexpr (NG == 1) {  // d = 64 always takes four-wave workgroups
         if (p.band) hipLaunchKernelGGL((prefill_fwd<true, 64, NG>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((prefill_fwd<false, 64, NG>), grid, block, 0, stream, p);
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
@@ -728,7 +730,12 @@ hipError_t launch_prefill_ng(const PrefillParams& p, hipStream_t stream) {
 // 16 x 1024 0.188 / 0.185 ms, 4 x 4096 0.493 / 0.528 ms, 16K 1.81 / 1.98 ms;
 // the 16K pi-Attention prefill (window 512, period 64: a window launch of
 // 576-key walks and skip-class launches of 256 keys) 0.350 / 0.327 ms.
+// At d = 64 a tile's products take half the MFMA time while the softmax work
+// stays, and the four-wave form (139 VGPRs, 32.5 KB of LDS: three workgroups
+// per compute unit) wins at every length: 16K causal 1.159 / 1.087 ms,
+// 4 x 4096 0.315 / 0.288 ms, 16 x 1024 0.114 / 0.092 ms.
 static bool narrow_prefill(const PrefillParams& p) {
+    if (p.d == 64) return true;
     int64_t keys = p.Lkv;  // keys one workgroup may walk
     if (p.band && p.window >= 0) keys = std::min<int64_t>(keys, (int64_t)p.window + 2 * kRows);
     return keys <= 16 * kN;

@@ -56,9 +56,10 @@ def test_prefill_small(B, Hq, Hkv, Lq, Lkv, causal):
     (300, 1025, False),
 ])
 def test_prefill_both_workgroup_shapes(Lq, Lkv, causal, d):
-    # Launches whose workgroups walk at most 1024 keys take four-wave
-    # workgroups (two per compute unit), longer ones eight-wave workgroups:
-    # every row on both sides of the boundary against the oracle.
+    # At d = 128, launches whose workgroups walk at most 1024 keys take
+    # four-wave workgroups (two per compute unit), longer ones eight-wave
+    # workgroups: every row on both sides of the boundary against the oracle
+    # (d = 64 always takes four-wave workgroups).
     inp = make_inputs(4, B=1, Hq=4, Hkv=2, d=d, L=Lkv, Lq=Lq, seed=7000 + Lq + Lkv + d)
     out, lse = prefill_on_gpu(inp, causal)
     ref, ref_lse = oracle_rows(inp, causal)
